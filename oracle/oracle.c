@@ -1,0 +1,429 @@
+/*
+ * CPU oracle for group-wise KV-cache quantization and quantized decode
+ * attention.  TEST INFRASTRUCTURE ONLY: it is loaded by the tests, by the
+ * package's smoke check and by the bench's CPU-baseline leg, never by the
+ * product path.  It shares no source with the HIP library.
+ *
+ * Plain scalar C, built with -O2 -ffp-contract=off (no fast-math), so every
+ * float expression below is one IEEE-754 binary32 operation rounded to
+ * nearest-even; attention is evaluated in binary64.
+ *
+ * Pages cited (titles as published):
+ *  [Oaken]      "大模型KV缓存量化技术：原理、优化与实践" (jsqmd.com)
+ *  [KVQ-Eng]    "大模型推理加速之KV Cache量化压缩原理与工程实现" (yunthe.com)
+ *  [KVO-LLM]    "长上下文LLM推理中的KV Cache优化技术解析" (intelliparadigm.com)
+ *  [Cocktail]   Cocktail chunk-adaptive mixed-precision KV-cache page (peacm.com)
+ *  [TurboQuant] TurboQuant KV-cache page (bhfrc.com)
+ *
+ * Readings where the pages are silent (each one is listed in the design doc):
+ *  - Range widened to include zero: lo = min(0, min x), hi = max(0, max x),
+ *    so the zero-point is an integer code inside [0, 2^b - 1].
+ *  - An all-zero group has scale 0; then zero-point and codes are 0.
+ *  - Rounding is half-to-even everywhere; x / s is a true division.
+ *  - Dequantized values are formed in binary32, attention in binary64.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------------- */
+/* fp16 input                                                               */
+/* ---------------------------------------------------------------------- */
+
+/* Exact binary16 -> binary32 (every half value is representable). */
+float ora_f16_to_f32(uint16_t h) {
+  int sign = h >> 15;
+  int e = (h >> 10) & 31;
+  int m = h & 1023;
+  float v;
+  if (e == 0)
+    v = ldexpf((float)m, -24); /* subnormal (or zero) */
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexpf((float)(1024 + m), e - 25);
+  return sign ? -v : v;
+}
+
+static int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+/* ---------------------------------------------------------------------- */
+/* Group quantizers                                                         */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * Asymmetric b-bit quantization of one group of n elements read with the
+ * given stride.  Scale from the group's range over 2^b - 1 levels
+ * ([Oaken] §2.1, the static-quantization formula); code = round(x / s) + z
+ * with s the scale and z the zero-point ([Cocktail] §3.2.2).
+ * Writes the scale, the zero-point and n codes (contiguous).
+ */
+void ora_quant_group_asym(const uint16_t* x, long n, long stride, int bits, float* s_out,
+                          uint8_t* z_out, uint8_t* q) {
+  int qmax = (1 << bits) - 1;
+  float lo = 0.0f, hi = 0.0f;
+  for (long i = 0; i < n; ++i) {
+    float v = ora_f16_to_f32(x[i * stride]);
+    if (v < lo) lo = v;
+    if (v > hi) hi = v;
+  }
+  float s = (hi - lo) / (float)qmax;
+  *s_out = s;
+  if (s == 0.0f) {
+    *z_out = 0;
+    for (long i = 0; i < n; ++i) q[i] = 0;
+    return;
+  }
+  int z = clampi((int)rintf(-lo / s), 0, qmax);
+  *z_out = (uint8_t)z;
+  for (long i = 0; i < n; ++i) {
+    float v = ora_f16_to_f32(x[i * stride]);
+    q[i] = (uint8_t)clampi((int)rintf(v / s) + z, 0, qmax);
+  }
+}
+
+/*
+ * Symmetric INT8 of one group: scale = amax / 127, code = round(x / scale)
+ * clamped to [-128, 127] ([KVQ-Eng], "INT8逐通道量化" listing).  The page
+ * takes amax along the last axis, i.e. per token and head; here the scale
+ * is formed in binary32 rather than the listing's fp16.
+ */
+void ora_quant_group_sym8(const uint16_t* x, long n, long stride, float* s_out, int8_t* q) {
+  float amax = 0.0f;
+  for (long i = 0; i < n; ++i) {
+    float v = fabsf(ora_f16_to_f32(x[i * stride]));
+    if (v > amax) amax = v;
+  }
+  float s = amax / 127.0f;
+  *s_out = s;
+  for (long i = 0; i < n; ++i) {
+    if (s == 0.0f) {
+      q[i] = 0;
+      continue;
+    }
+    float v = ora_f16_to_f32(x[i * stride]);
+    q[i] = (int8_t)clampi((int)rintf(v / s), -128, 127);
+  }
+}
+
+/*
+ * Token-axis groups: each of `rows` rows of D elements is split into D / g
+ * contiguous groups ([TurboQuant] §2.3, per-group scaling along the head
+ * dimension).  codes: rows x D (one code per byte, int8 for sym),
+ * scale and zero: rows x (D / g).  zero may be NULL when sym.
+ */
+void ora_quant_rows(const uint16_t* x, long rows, int D, int g, int bits, int sym,
+                    uint8_t* codes, float* scale, uint8_t* zero) {
+  int ng = D / g;
+  for (long r = 0; r < rows; ++r)
+    for (int j = 0; j < ng; ++j) {
+      const uint16_t* xg = x + r * D + (long)j * g;
+      uint8_t* qg = codes + r * D + (long)j * g;
+      if (sym)
+        ora_quant_group_sym8(xg, g, 1, &scale[r * ng + j], (int8_t*)qg);
+      else
+        ora_quant_group_asym(xg, g, 1, bits, &scale[r * ng + j], &zero[r * ng + j], qg);
+    }
+}
+
+/*
+ * Channel-axis groups for K ([KVQ-Eng], advice to quantize K per channel):
+ * x is `slices` slices of [T][D]; each channel of each block of gt
+ * consecutive tokens is one group.  codes: slices x T x D,
+ * scale and zero: slices x (T / gt) x D.
+ */
+void ora_quant_channel_blocks(const uint16_t* x, long slices, long T, int D, int gt, int bits,
+                              uint8_t* codes, float* scale, uint8_t* zero) {
+  long nb = T / gt;
+  uint8_t* tmp = (uint8_t*)malloc((size_t)gt);
+  for (long sl = 0; sl < slices; ++sl)
+    for (long k = 0; k < nb; ++k)
+      for (int d = 0; d < D; ++d) {
+        const uint16_t* xg = x + (sl * T + k * gt) * D + d;
+        long m = (sl * nb + k) * D + d;
+        ora_quant_group_asym(xg, gt, D, bits, &scale[m], &zero[m], tmp);
+        for (int j = 0; j < gt; ++j) codes[(sl * T + k * gt + j) * D + d] = tmp[j];
+      }
+  free(tmp);
+}
+
+/* Dequantization: x_hat = (q - z) * s in binary32, or q * s when sym. */
+void ora_dequant_rows(const uint8_t* codes, const float* scale, const uint8_t* zero, long rows,
+                      int D, int g, int sym, float* out) {
+  int ng = D / g;
+  for (long r = 0; r < rows; ++r)
+    for (int d = 0; d < D; ++d) {
+      float s = scale[r * ng + d / g];
+      int c = sym ? (int)(int8_t)codes[r * D + d] : (int)codes[r * D + d] - (int)zero[r * ng + d / g];
+      out[r * D + d] = (float)c * s;
+    }
+}
+
+void ora_dequant_channel_blocks(const uint8_t* codes, const float* scale, const uint8_t* zero,
+                                long slices, long T, int D, int gt, float* out) {
+  long nb = T / gt;
+  for (long sl = 0; sl < slices; ++sl)
+    for (long t = 0; t < T; ++t)
+      for (int d = 0; d < D; ++d) {
+        long m = (sl * nb + t / gt) * D + d;
+        int c = (int)codes[(sl * T + t) * D + d] - (int)zero[m];
+        out[(sl * T + t) * D + d] = (float)c * scale[m];
+      }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Oaken threshold grouping with group-shift outer values                   */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * One row of D elements, groups of g along the row ([Oaken] §3.1 online
+ * stage, §3.2.1 threshold grouping, §3.2.2 group shift).
+ * thr = {T_lo_outer, T_lo_inner, T_hi_inner, T_hi_outer}.
+ *  - Outer: x > T_hi_outer or x < T_lo_outer (strict, §3.2.1).
+ *  - Dense body: asymmetric 4-bit over the group's non-outer elements (inner
+ *    and middle share it); outer positions store the zero-point so their
+ *    dense value is exactly 0.
+ *  - Outer value: shifted delta = x - T_hi_outer (above) or x - T_lo_outer
+ *    (below), quantized with a per-group outer scale max|delta| / 31 to a
+ *    5-bit magnitude plus a side bit; entries are listed in ascending
+ *    channel order as idx | side << 7 | mag << 8.
+ * codes: D, scale/zero/oscale: D / g, entries: up to D, *count set.
+ */
+void ora_oaken_row(const uint16_t* x, int D, int g, const float* thr, uint8_t* codes,
+                   float* scale, uint8_t* zero, float* oscale, uint16_t* entries, int* count) {
+  float t_lo = thr[0], t_hi = thr[3];
+  int ng = D / g;
+  int cnt = 0;
+  for (int j = 0; j < ng; ++j) {
+    float lo = 0.0f, hi = 0.0f, dmax = 0.0f;
+    for (int i = j * g; i < (j + 1) * g; ++i) {
+      float v = ora_f16_to_f32(x[i]);
+      int outer = (v > t_hi) || (v < t_lo);
+      if (outer) {
+        float delta = v > t_hi ? v - t_hi : v - t_lo;
+        if (fabsf(delta) > dmax) dmax = fabsf(delta);
+      } else {
+        if (v < lo) lo = v;
+        if (v > hi) hi = v;
+      }
+    }
+    float s = (hi - lo) / 15.0f;
+    int z = 0;
+    if (s != 0.0f) z = clampi((int)rintf(-lo / s), 0, 15);
+    float so = dmax / 31.0f;
+    scale[j] = s;
+    zero[j] = (uint8_t)z;
+    oscale[j] = so;
+    for (int i = j * g; i < (j + 1) * g; ++i) {
+      float v = ora_f16_to_f32(x[i]);
+      int above = v > t_hi;
+      int outer = above || (v < t_lo);
+      if (outer) {
+        codes[i] = (uint8_t)z;
+        float delta = above ? v - t_hi : v - t_lo;
+        int mag = so == 0.0f ? 0 : clampi((int)rintf(fabsf(delta) / so), 0, 31);
+        entries[cnt++] = (uint16_t)(i | (above << 7) | (mag << 8));
+      } else {
+        codes[i] = s == 0.0f ? 0 : (uint8_t)clampi((int)rintf(v / s) + z, 0, 15);
+      }
+    }
+  }
+  *count = cnt;
+}
+
+void ora_oaken_rows(const uint16_t* x, long rows, int D, int g, const float* thr, uint8_t* codes,
+                    float* scale, uint8_t* zero, float* oscale, uint16_t* entries, int* counts) {
+  int ng = D / g;
+  for (long r = 0; r < rows; ++r)
+    ora_oaken_row(x + r * D, D, g, thr, codes + r * D, scale + r * ng, zero + r * ng,
+                  oscale + r * ng, entries + r * D, &counts[r]);
+}
+
+/* Reconstruction: dense (q - z) * s, outer T_hi + mag * s_out or T_lo - mag * s_out. */
+void ora_oaken_dequant_rows(const uint8_t* codes, const float* scale, const uint8_t* zero,
+                            const float* oscale, const uint16_t* entries, const int* counts,
+                            long rows, int D, int g, const float* thr, float* out) {
+  int ng = D / g;
+  for (long r = 0; r < rows; ++r) {
+    for (int d = 0; d < D; ++d)
+      out[r * D + d] = (float)((int)codes[r * D + d] - (int)zero[r * ng + d / g]) * scale[r * ng + d / g];
+    for (int e = 0; e < counts[r]; ++e) {
+      uint16_t en = entries[r * D + e];
+      int idx = en & 127, above = (en >> 7) & 1, mag = (en >> 8) & 31;
+      float step = (float)mag * oscale[r * ng + idx / g];
+      out[r * D + idx] = above ? thr[3] + step : thr[0] - step;
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Offline calibration: nearest-rank percentiles of fp16 samples           */
+/* ---------------------------------------------------------------------- */
+
+/* Order-preserving key of an fp16 bit pattern (negatives below positives). */
+static unsigned f16_key(uint16_t b) { return (b & 0x8000) ? (0xFFFFu - b) : (b | 0x8000u); }
+static uint16_t f16_from_key(unsigned k) {
+  return (uint16_t)(k >= 0x8000u ? (k & 0x7FFFu) : (0xFFFFu - k));
+}
+
+/* Accumulate a 65536-bin histogram of the values, indexed by ordered key. */
+void ora_hist_f16(const uint16_t* x, long n, uint64_t* hist) {
+  for (long i = 0; i < n; ++i) hist[f16_key(x[i])]++;
+}
+
+/*
+ * Nearest-rank percentile ([Oaken] §3.1 offline stage: thresholds from the
+ * sampled KV distribution).  p is given in basis points (2.5% = 250); the
+ * result is the value of rank ceil(p * N / 10000) (at least 1).
+ */
+float ora_hist_percentile(const uint64_t* hist, long p_bp) {
+  uint64_t n = 0;
+  for (unsigned k = 0; k < 65536u; ++k) n += hist[k];
+  uint64_t rank = (n * (uint64_t)p_bp + 9999u) / 10000u;
+  if (rank < 1) rank = 1;
+  uint64_t acc = 0;
+  for (unsigned k = 0; k < 65536u; ++k) {
+    acc += hist[k];
+    if (acc >= rank) return ora_f16_to_f32(f16_from_key(k));
+  }
+  return NAN;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Cocktail chunk precision search and reorder                              */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * [Cocktail] §3.1.1: cosine similarity of the query embedding with each
+ * chunk embedding; T_low = s_min + (s_max - s_min) * alpha,
+ * T_high = s_max - (s_max - s_min) * beta; sim > T_high -> 16 (FP16),
+ * T_low < sim <= T_high -> 4, sim <= T_low -> 2.
+ */
+void ora_chunk_bits(const double* qe, const double* ce, long n_chunks, int dim, double alpha,
+                    double beta, double* sims, uint8_t* bits) {
+  double qq = 0.0;
+  for (int d = 0; d < dim; ++d) qq += qe[d] * qe[d];
+  double smin = INFINITY, smax = -INFINITY;
+  for (long i = 0; i < n_chunks; ++i) {
+    double dot = 0.0, cc = 0.0;
+    for (int d = 0; d < dim; ++d) {
+      dot += qe[d] * ce[i * dim + d];
+      cc += ce[i * dim + d] * ce[i * dim + d];
+    }
+    double s = dot / (sqrt(qq) * sqrt(cc));
+    sims[i] = s;
+    if (s < smin) smin = s;
+    if (s > smax) smax = s;
+  }
+  double t_low = smin + (smax - smin) * alpha;
+  double t_high = smax - (smax - smin) * beta;
+  for (long i = 0; i < n_chunks; ++i)
+    bits[i] = sims[i] > t_high ? 16 : (sims[i] > t_low ? 4 : 2);
+}
+
+/*
+ * [Cocktail] §3.1.2: chunks of equal bit-width made contiguous.  Class
+ * order FP16, INT4, INT2, stable inside a class.  perm[j] = original chunk
+ * id at slot j; seg = {n_fp16, n_int4, n_int2, n_chunks}.  A bit value other
+ * than 16 or 4 is placed in the INT2 class.
+ */
+void ora_reorder(const uint8_t* bits, long batch, long n_chunks, int32_t* perm, int32_t* seg) {
+  for (long b = 0; b < batch; ++b) {
+    const uint8_t* bb = bits + b * n_chunks;
+    int32_t* pp = perm + b * n_chunks;
+    long j = 0;
+    for (int c = 0; c < 3; ++c) {
+      long cnt = 0;
+      for (long i = 0; i < n_chunks; ++i) {
+        int cls = bb[i] == 16 ? 0 : (bb[i] == 4 ? 1 : 2);
+        if (cls == c) {
+          pp[j++] = (int32_t)i;
+          ++cnt;
+        }
+      }
+      seg[b * 4 + c] = (int32_t)cnt;
+    }
+    seg[b * 4 + 3] = (int32_t)n_chunks;
+  }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Attention                                                                */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * Softmax attention of one query over tokens [t0, t1) of one KV head
+ * (khat, vhat: [S][D] dequantized values).  Scores q.k * sm_scale (the
+ * 1/sqrt(d) scaling in [KVO-LLM] §3.2's score estimate).  Returns the
+ * running max m, the sum l of exp(score - m) and the normalized output o.
+ * An empty range gives m = -inf, l = 0, o = 0.
+ */
+void ora_attention_partial(const uint16_t* q, const float* khat, const float* vhat, long t0,
+                           long t1, int D, double sm_scale, double* m_out, double* l_out,
+                           double* o) {
+  for (int d = 0; d < D; ++d) o[d] = 0.0;
+  if (t1 <= t0) {
+    *m_out = -INFINITY;
+    *l_out = 0.0;
+    return;
+  }
+  long n = t1 - t0;
+  double* sc = (double*)malloc(sizeof(double) * (size_t)n);
+  double m = -INFINITY;
+  for (long t = t0; t < t1; ++t) {
+    double acc = 0.0;
+    for (int d = 0; d < D; ++d) acc += (double)ora_f16_to_f32(q[d]) * (double)khat[t * D + d];
+    sc[t - t0] = acc * sm_scale;
+    if (sc[t - t0] > m) m = sc[t - t0];
+  }
+  double l = 0.0;
+  for (long t = t0; t < t1; ++t) {
+    double p = exp(sc[t - t0] - m);
+    l += p;
+    for (int d = 0; d < D; ++d) o[d] += p * (double)vhat[t * D + d];
+  }
+  for (int d = 0; d < D; ++d) o[d] /= l;
+  *m_out = m;
+  *l_out = l;
+  free(sc);
+}
+
+/*
+ * Decode attention for one sequence: q [Hq][D] fp16, khat/vhat
+ * [Hkv][S][D].  Query head h reads KV head h / (Hq / Hkv) (consecutive query
+ * heads share a KV head under GQA, [KVQ-Eng] cache-size section).
+ * out: [Hq][D] in binary64.
+ */
+void ora_attention(const uint16_t* q, int Hq, int Hkv, int D, const float* khat,
+                   const float* vhat, long S, double sm_scale, double* out) {
+  int grp = Hq / Hkv;
+  for (int h = 0; h < Hq; ++h) {
+    int kv = h / grp;
+    double m, l;
+    ora_attention_partial(q + (long)h * D, khat + (long)kv * S * D, vhat + (long)kv * S * D, 0, S,
+                          D, sm_scale, &m, &l, out + (long)h * D);
+  }
+}
+
+/*
+ * Log-sum-exp merge of per-segment partials ([Cocktail] §3.2.3: attention
+ * computed per block and the block outputs merged):
+ * M = max m_j, L = sum l_j e^(m_j - M), o = sum l_j e^(m_j - M) o_j / L.
+ */
+void ora_lse_merge(int parts, const double* m, const double* l, const double* o, int D,
+                   double* out) {
+  double M = -INFINITY;
+  for (int j = 0; j < parts; ++j)
+    if (m[j] > M) M = m[j];
+  double L = 0.0;
+  for (int d = 0; d < D; ++d) out[d] = 0.0;
+  for (int j = 0; j < parts; ++j) {
+    if (l[j] == 0.0) continue;
+    double w = l[j] * exp(m[j] - M);
+    L += w;
+    for (int d = 0; d < D; ++d) out[d] += w * o[(long)j * D + d];
+  }
+  for (int d = 0; d < D; ++d) out[d] /= L;
+}
