@@ -1,0 +1,233 @@
+/*
+ * kvq — group-wise KV-cache quantization and fused-dequant decode attention
+ * for AMD Instinct MI355X (gfx950).  Plain C ABI: host integers, floats and
+ * device pointers only.
+ *
+ * Pages the operations follow (titles as published):
+ *  [Oaken]      "大模型KV缓存量化技术：原理、优化与实践" (jsqmd.com)
+ *  [KVQ-Eng]    "大模型推理加速之KV Cache量化压缩原理与工程实现" (yunthe.com)
+ *  [Cocktail]   Cocktail chunk-adaptive mixed-precision KV-cache page (peacm.com)
+ *  [TurboQuant] TurboQuant KV-cache page (bhfrc.com)
+ *
+ * Conventions shared by every entry point
+ *  - Layout of K and V follows the cache-size formula of [KVQ-Eng]
+ *    ("KV Cache的显存瓶颈" section): [batch][kv_heads][seq][head_dim], fp16,
+ *    row-major, head_dim == 128.
+ *  - Ownership: the caller allocates and frees every buffer (sizes from
+ *    kvq_cache_bytes / kvq_decode_workspace_bytes).  The library keeps no
+ *    state, never allocates, frees or synchronizes; all work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the default stream) and buffers must
+ *    stay alive until that work has completed.  Pre-allocating the cache is
+ *    the practice [Cocktail] §5.2 recommends.
+ *  - Errors: arguments visible to the host are checked before any HIP call;
+ *    a negative kvq_status is returned and nothing is enqueued.  A failed
+ *    launch returns KVQ_ERR_HIP.  Conditions only the device can see set bits
+ *    in the cache's `status` word (KVQ_FLAG_*), which the caller reads after
+ *    synchronizing; the library never clears it.
+ *  - Pointers: device pointers must be 16-byte aligned, except `status`
+ *    (4-byte) and the byte arrays `zero`/`zero2`/`chunk_bits` (1-byte).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_HEAD_DIM 128
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent field */
+  KVQ_ERR_UNSUPPORTED = -2, /* valid but not implemented (head_dim != 128, ...) */
+  KVQ_ERR_CAPACITY = -3,    /* t_new or max_len larger than the cache holds */
+  KVQ_ERR_ALIGNMENT = -4,   /* a device pointer is not aligned as required */
+  KVQ_ERR_WORKSPACE = -5,   /* decode workspace missing or too small */
+  KVQ_ERR_HIP = -6          /* a HIP launch failed */
+} kvq_status;
+
+/* Cache organisation. */
+enum {
+  KVQ_MODE_UNIFORM = 0,     /* one bit-width per tensor */
+  KVQ_MODE_CHUNK_MIXED = 1, /* Cocktail: FP16 / INT4 / INT2 per 32-token chunk, reordered */
+  KVQ_MODE_OAKEN = 2        /* Oaken: dense INT4 body + sparse shifted outer values */
+};
+
+/* Grouping axis of a tensor. */
+enum {
+  KVQ_AXIS_TOKEN = 0,  /* groups of `group` consecutive channels of one token */
+  KVQ_AXIS_CHANNEL = 1 /* groups of `group` consecutive tokens of one channel (K only) */
+};
+
+/* Device status bits (OR-ed into *status by kernels). */
+#define KVQ_FLAG_POS_RANGE 1u       /* pos[b] + t_new > max_seq, or pos[b] < 0: rows skipped */
+#define KVQ_FLAG_SPARSE_FULL 2u     /* Oaken sparse list full: outer entries dropped */
+#define KVQ_FLAG_LEN_RANGE 4u       /* decode seq_len[b] outside [0, max_len]: clamped */
+#define KVQ_FLAG_BAD_CHUNK_BITS 8u  /* chunk bit-width not in {16, 4, 2}: used as 2 */
+#define KVQ_FLAG_BLOCK_ALIGN 16u    /* channel-axis append not on a block boundary: skipped */
+
+/*
+ * One quantized tensor (K or V) of the cache.
+ *
+ * Quantizer ([Oaken] §2.1 scale formula, [Cocktail] §3.2.2 code formula),
+ * per group of fp16 values x, in IEEE binary32 with round-half-to-even:
+ *   asymmetric: lo = min(0, min x), hi = max(0, max x), s = (hi - lo) / (2^bits - 1),
+ *               z = clamp(rne(-lo / s), 0, 2^bits - 1),
+ *               q = clamp(rne(x / s) + z, 0, 2^bits - 1),  x_hat = (q - z) * s;
+ *               an all-zero group has s = 0, z = 0, q = 0.
+ *   symmetric (bits 8, [KVQ-Eng] INT8 listing): s = max|x| / 127,
+ *               q = clamp(rne(x / s), -128, 127), x_hat = q * s.
+ *
+ * Buffers by mode (B = batch, H = kv_heads, S = max_seq, D = 128,
+ * RB = D * bits / 8 bytes per token row, NG = D / group):
+ *  UNIFORM, TOKEN axis:
+ *    codes  [B][H][S][RB]  packed little-endian: for bits 8 one (u)int8 per
+ *                          channel; bits 4: channel 2i in the low nibble of
+ *                          byte i; bits 2: channel 4i + j in bits 2j..2j+1.
+ *    scale  [B][H][S][NG]  float
+ *    zero   [B][H][S][NG]  uint8 (unused and may be NULL when symmetric)
+ *  UNIFORM, CHANNEL axis (K only, group == 64 tokens; asymmetric):
+ *    codes  [B][H][S][RB]  token rows as above
+ *    scale  [B][H][S/64][D] float, zero [B][H][S/64][D] uint8
+ *  OAKEN (bits 4, TOKEN axis, group 32 or 64; [Oaken] §3.1-3.2):
+ *    codes, scale, zero    the dense body as UNIFORM/TOKEN over the
+ *                          non-outer values; outer positions hold code z
+ *    oscale [B][H][S][NG]  float outer scale max|delta| / 31 per group
+ *    rowptr [B][H][S+1]    uint32: entries of token t are
+ *                          sparse[rowptr[t] .. rowptr[t+1]) of that (b, h)
+ *    sparse [B][H][sparse_cap] uint16 entries idx | side << 7 | mag << 8:
+ *                          idx the channel, side 1 above T_hi_outer,
+ *                          x_hat = T_hi_outer + mag * oscale (side 1) or
+ *                          T_lo_outer - mag * oscale (side 0)
+ *  CHUNK_MIXED ([Cocktail] §3.1.2; C = S / chunk_tokens chunk slots, each
+ *  class pool holds up to C chunks per (b, h) in reordered slot order):
+ *    codes16 [B][H][C][chunk_tokens][D] fp16, the FP16 chunks
+ *    codes/scale/zero   INT4 pool, TOKEN-axis layout with C*chunk_tokens rows
+ *    codes2/scale2/zero2 INT2 pool, same layout
+ */
+typedef struct kvq_tensor {
+  int32_t bits;       /* UNIFORM: 8, 4 or 2.  OAKEN: 4.  CHUNK_MIXED: ignored */
+  int32_t symmetric;  /* 1: symmetric INT8 (bits 8, TOKEN axis) */
+  int32_t axis;       /* KVQ_AXIS_TOKEN or KVQ_AXIS_CHANNEL */
+  int32_t group;      /* TOKEN: 32, 64 or 128 channels.  CHANNEL: 64 tokens */
+  float thr[4];       /* OAKEN: T_lo_outer, T_lo_inner, T_hi_inner, T_hi_outer (inner ones
+                         are informational; [Oaken] §3.2.1) */
+  int64_t sparse_cap; /* OAKEN: capacity of `sparse` per (b, h), in entries */
+  void* codes;
+  float* scale;
+  uint8_t* zero;
+  float* oscale;
+  uint32_t* rowptr;
+  uint16_t* sparse;
+  void* codes16;
+  void* codes2;
+  float* scale2;
+  uint8_t* zero2;
+} kvq_tensor;
+
+typedef struct kvq_cache {
+  int32_t batch;
+  int32_t kv_heads;
+  int32_t max_seq;      /* token capacity per (b, h); CHUNK_MIXED: multiple of chunk_tokens */
+  int32_t head_dim;     /* must be 128 */
+  int32_t mode;         /* KVQ_MODE_* */
+  int32_t chunk_tokens; /* CHUNK_MIXED: tokens per chunk (16, 32 or 64) */
+  kvq_tensor k;
+  kvq_tensor v;
+  int32_t* perm;        /* CHUNK_MIXED: [B][C] original chunk id at each slot */
+  int32_t* seg;         /* CHUNK_MIXED: [B][4] {n_fp16, n_int4, n_int2, n_chunks} */
+  uint32_t* status;     /* device word for KVQ_FLAG_* bits (required) */
+} kvq_cache;
+
+/* Byte sizes of every buffer of one tensor; 0 = buffer not used. */
+typedef struct kvq_tensor_bytes {
+  size_t codes, scale, zero, oscale, rowptr, sparse, codes16, codes2, scale2, zero2;
+} kvq_tensor_bytes;
+
+typedef struct kvq_cache_bytes_t {
+  kvq_tensor_bytes k, v;
+  size_t perm, seg, status;
+} kvq_cache_bytes_t;
+
+/*
+ * Sizes of all buffers the cache described by `c` needs (pointer fields of
+ * `c` are ignored).  Host only, no HIP call.  Returns INVALID_ARG /
+ * UNSUPPORTED for a configuration the other entry points would reject.
+ */
+kvq_status kvq_cache_bytes(const kvq_cache* c, kvq_cache_bytes_t* out);
+
+/*
+ * Quantize t_new new tokens per sequence and write them into the cache
+ * ([Oaken] §3.1 online stage; [Cocktail] §3.2.2 group quantization).
+ *  k_new, v_new: device fp16 [batch][kv_heads][t_new][128].
+ *  pos:          device int32 [batch]; token t of sequence b goes to cache
+ *                position pos[b] + t.
+ *  UNIFORM/TOKEN: any pos, t_new >= 1.
+ *  UNIFORM/CHANNEL: t_new a multiple of 64; pos[b] must be a multiple of 64
+ *                (else the sequence is skipped and KVQ_FLAG_BLOCK_ALIGN set).
+ *  OAKEN:        rowptr[b][h][pos[b]] must already hold the entry count of
+ *                the earlier tokens (0 at pos 0; this call writes
+ *                rowptr[pos[b] + 1 .. pos[b] + t_new]); entries past
+ *                sparse_cap are dropped with KVQ_FLAG_SPARSE_FULL.
+ *  CHUNK_MIXED:  whole-sequence prefill: t_new == max_seq and pos[b] == 0;
+ *                perm/seg from kvq_reorder_chunks select, for every slot,
+ *                the source chunk and its class (FP16 chunks are copied).
+ */
+kvq_status kvq_quant_append(const kvq_cache* c, const void* k_new, const void* v_new,
+                            int32_t t_new, const int32_t* pos, void* stream);
+
+/*
+ * [Cocktail] §3.1.2 reorder: for every sequence, place the chunks in class
+ * order FP16, INT4, INT2, stable within a class, writing c->perm (slot ->
+ * original chunk id) and c->seg ({n_fp16, n_int4, n_int2, n_chunks}).
+ *  chunk_bits: device uint8 [batch][n_chunks], each 16, 4 or 2 (the
+ *              per-chunk precision from the query-chunk similarity search,
+ *              [Cocktail] §3.1.1); other values count as 2 and set
+ *              KVQ_FLAG_BAD_CHUNK_BITS.
+ *  n_chunks:   must equal max_seq / chunk_tokens.  CHUNK_MIXED mode only.
+ */
+kvq_status kvq_reorder_chunks(const kvq_cache* c, const uint8_t* chunk_bits, int32_t n_chunks,
+                              void* stream);
+
+/*
+ * Workspace needed by kvq_decode_attn for the same (c, q_heads, max_len,
+ * num_splits); 0 when the chosen split count is 1.  Host only.
+ */
+kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32_t max_len,
+                                      int32_t num_splits, size_t* bytes);
+
+/*
+ * One decode step of softmax attention over the quantized cache, with the
+ * dequantization fused into the q.K and p.V loops ([TurboQuant] §2.3, end:
+ * dequantization inside the attention product, no separate pass).  The
+ * sequence is split across workgroups and the partial results are merged
+ * with the log-sum-exp rule ([Cocktail] §3.2.3: per-block attention whose
+ * merge equals ordinary attention).
+ *  q:        device fp16 [batch][q_heads][128]; q_heads a multiple of
+ *            kv_heads; query head h reads KV head h / (q_heads / kv_heads).
+ *  seq_len:  device int32 [batch], tokens 0 .. seq_len[b]-1 are attended
+ *            (UNIFORM/OAKEN; values outside [0, max_len] are clamped and set
+ *            KVQ_FLAG_LEN_RANGE).  CHUNK_MIXED attends all chunks counted
+ *            in seg; seq_len may then be NULL.
+ *  max_len:  host bound on seq_len (CHUNK_MIXED: max_seq), sizes the grid.
+ *  sm_scale: score scale, usually 1/sqrt(128).
+ *  out:      device fp32 [batch][q_heads][128]; a sequence with no tokens
+ *            gets zeros.
+ *  num_splits: sequence splits per (b, kv head); 0 picks one from the shape.
+ */
+kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t q_heads,
+                           const int32_t* seq_len, int32_t max_len, float sm_scale, float* out,
+                           void* workspace, size_t workspace_bytes, int32_t num_splits,
+                           void* stream);
+
+/* Static string naming a kvq_status value. */
+const char* kvq_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

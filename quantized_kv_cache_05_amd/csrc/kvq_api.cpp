@@ -1,0 +1,369 @@
+// C-ABI entry points of libkvq: argument validation (host only, before any
+// HIP call), buffer sizing, split planning and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+using kvq::CacheArgs;
+using kvq::TensorArgs;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool is_pow2_group(int g) { return g == 32 || g == 64 || g == 128; }
+
+struct Shape {
+  long long B, H, S;
+};
+
+// Structural checks shared by every entry point (no pointer checks).
+kvq_status check_config(const kvq_cache* c) {
+  if (!c) return KVQ_ERR_INVALID_ARG;
+  if (c->batch < 1 || c->kv_heads < 1 || c->max_seq < 64) return KVQ_ERR_INVALID_ARG;
+  if (c->max_seq % 64) return KVQ_ERR_INVALID_ARG;
+  if (c->head_dim != KVQ_HEAD_DIM) return KVQ_ERR_UNSUPPORTED;
+  const kvq_tensor& k = c->k;
+  const kvq_tensor& v = c->v;
+  switch (c->mode) {
+    case KVQ_MODE_UNIFORM: {
+      for (const kvq_tensor* t : {&k, &v}) {
+        if (t->bits != 8 && t->bits != 4 && t->bits != 2) return KVQ_ERR_INVALID_ARG;
+        if (t->symmetric != 0 && t->symmetric != 1) return KVQ_ERR_INVALID_ARG;
+        if (t->symmetric && t->bits != 8) return KVQ_ERR_UNSUPPORTED;
+        if (t->axis != KVQ_AXIS_TOKEN && t->axis != KVQ_AXIS_CHANNEL) return KVQ_ERR_INVALID_ARG;
+      }
+      if (v.axis != KVQ_AXIS_TOKEN) return KVQ_ERR_UNSUPPORTED;
+      if (!is_pow2_group(v.group)) return KVQ_ERR_INVALID_ARG;
+      if (k.axis == KVQ_AXIS_TOKEN && !is_pow2_group(k.group)) return KVQ_ERR_INVALID_ARG;
+      if (k.axis == KVQ_AXIS_CHANNEL) {
+        if (k.group != 64) return KVQ_ERR_UNSUPPORTED;
+        if (k.symmetric) return KVQ_ERR_UNSUPPORTED;
+      }
+      TensorArgs ka{}, va{};
+      ka.bits = k.bits; ka.sym = k.symmetric; ka.axis = k.axis; ka.group = k.group;
+      va.bits = v.bits; va.sym = v.symmetric; va.axis = v.axis; va.group = v.group;
+      if (!kvq::decode_uniform_supported(ka, va)) return KVQ_ERR_UNSUPPORTED;
+      return KVQ_OK;
+    }
+    case KVQ_MODE_OAKEN: {
+      for (const kvq_tensor* t : {&k, &v}) {
+        if (t->bits != 4 || t->symmetric || t->axis != KVQ_AXIS_TOKEN) return KVQ_ERR_UNSUPPORTED;
+        if (!is_pow2_group(t->group)) return KVQ_ERR_INVALID_ARG;
+        if (!std::isfinite(t->thr[0]) || !std::isfinite(t->thr[3]) || !(t->thr[0] < t->thr[3]))
+          return KVQ_ERR_INVALID_ARG;
+        if (t->sparse_cap < 0 || t->sparse_cap > 0xFFFFFFFFll) return KVQ_ERR_INVALID_ARG;
+      }
+      if (k.group != v.group) return KVQ_ERR_UNSUPPORTED;
+      return KVQ_OK;
+    }
+    case KVQ_MODE_CHUNK_MIXED: {
+      if (c->chunk_tokens != 16 && c->chunk_tokens != 32 && c->chunk_tokens != 64)
+        return KVQ_ERR_INVALID_ARG;
+      if (!is_pow2_group(k.group) || k.group != v.group) return KVQ_ERR_INVALID_ARG;
+      if (k.axis != KVQ_AXIS_TOKEN || v.axis != KVQ_AXIS_TOKEN) return KVQ_ERR_UNSUPPORTED;
+      return KVQ_OK;
+    }
+    default:
+      return KVQ_ERR_INVALID_ARG;
+  }
+}
+
+kvq_tensor_bytes tensor_bytes(const kvq_cache* c, const kvq_tensor& t, bool is_k) {
+  kvq_tensor_bytes r{};
+  const size_t B = (size_t)c->batch, H = (size_t)c->kv_heads, S = (size_t)c->max_seq, D = KVQ_HEAD_DIM;
+  const size_t ng = D / (size_t)t.group;
+  switch (c->mode) {
+    case KVQ_MODE_UNIFORM:
+      r.codes = B * H * S * D * (size_t)t.bits / 8;
+      if (is_k && t.axis == KVQ_AXIS_CHANNEL) {
+        r.scale = B * H * (S / 64) * D * 4;
+        r.zero = B * H * (S / 64) * D;
+      } else {
+        r.scale = B * H * S * ng * 4;
+        r.zero = t.symmetric ? 0 : B * H * S * ng;
+      }
+      break;
+    case KVQ_MODE_OAKEN:
+      r.codes = B * H * S * D / 2;
+      r.scale = B * H * S * ng * 4;
+      r.zero = B * H * S * ng;
+      r.oscale = B * H * S * ng * 4;
+      r.rowptr = B * H * (S + 1) * 4;
+      r.sparse = B * H * (size_t)t.sparse_cap * 2;
+      break;
+    case KVQ_MODE_CHUNK_MIXED:
+      r.codes16 = B * H * S * D * 2;
+      r.codes = B * H * S * D / 2;
+      r.scale = B * H * S * ng * 4;
+      r.zero = B * H * S * ng;
+      r.codes2 = B * H * S * D / 4;
+      r.scale2 = B * H * S * ng * 4;
+      r.zero2 = B * H * S * ng;
+      break;
+  }
+  return r;
+}
+
+// Every buffer the mode needs must be present and 16-byte aligned.
+kvq_status check_buffers(const kvq_cache* c) {
+  if (!c->status || !aligned(c->status, 4)) return c->status ? KVQ_ERR_ALIGNMENT : KVQ_ERR_INVALID_ARG;
+  for (int which = 0; which < 2; ++which) {
+    const kvq_tensor& t = which ? c->v : c->k;
+    const kvq_tensor_bytes nb = tensor_bytes(c, t, which == 0);
+    const void* ptrs[10] = {t.codes, t.scale, t.zero, t.oscale, t.rowptr,
+                            t.sparse, t.codes16, t.codes2, t.scale2, t.zero2};
+    const size_t sizes[10] = {nb.codes, nb.scale, nb.zero, nb.oscale, nb.rowptr,
+                              nb.sparse, nb.codes16, nb.codes2, nb.scale2, nb.zero2};
+    for (int i = 0; i < 10; ++i) {
+      if (!sizes[i]) continue;
+      if (!ptrs[i]) return KVQ_ERR_INVALID_ARG;
+      if (!aligned(ptrs[i], 16)) return KVQ_ERR_ALIGNMENT;
+    }
+  }
+  if (c->mode == KVQ_MODE_CHUNK_MIXED) {
+    if (!c->perm || !c->seg) return KVQ_ERR_INVALID_ARG;
+    if (!aligned(c->perm, 4) || !aligned(c->seg, 16)) return KVQ_ERR_ALIGNMENT;
+  }
+  return KVQ_OK;
+}
+
+TensorArgs tensor_args(const kvq_tensor& t) {
+  TensorArgs a;
+  a.bits = t.bits;
+  a.sym = t.symmetric;
+  a.axis = t.axis;
+  a.group = t.group;
+  a.thr_lo = t.thr[0];
+  a.thr_hi = t.thr[3];
+  a.sparse_cap = t.sparse_cap;
+  a.codes = static_cast<uint8_t*>(t.codes);
+  a.scale = t.scale;
+  a.zero = t.zero;
+  a.oscale = t.oscale;
+  a.rowptr = t.rowptr;
+  a.sparse = t.sparse;
+  a.codes16 = static_cast<uint8_t*>(t.codes16);
+  a.codes2 = static_cast<uint8_t*>(t.codes2);
+  a.scale2 = t.scale2;
+  a.zero2 = t.zero2;
+  return a;
+}
+
+CacheArgs cache_args(const kvq_cache* c) {
+  CacheArgs a;
+  a.B = c->batch;
+  a.H = c->kv_heads;
+  a.S = c->max_seq;
+  a.mode = c->mode;
+  a.chunk_tokens = c->chunk_tokens;
+  a.k = tensor_args(c->k);
+  a.v = tensor_args(c->v);
+  a.perm = c->perm;
+  a.seg = c->seg;
+  a.status = c->status;
+  return a;
+}
+
+kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+// Workgroups to aim for: several per compute unit on a 256-CU part.
+constexpr long long kTargetGroups = 2048;
+
+struct Plan {
+  int G, gtile, qtiles, num_splits, split_len;
+};
+
+kvq_status plan_decode(const kvq_cache* c, int q_heads, int max_len, int num_splits, Plan* p) {
+  if (q_heads < 1 || q_heads % c->kv_heads) return KVQ_ERR_INVALID_ARG;
+  if (num_splits < 0) return KVQ_ERR_INVALID_ARG;
+  p->G = q_heads / c->kv_heads;
+  p->gtile = p->G == 1 ? 1 : 4;
+  p->qtiles = (p->G + p->gtile - 1) / p->gtile;
+  const long long units = (long long)c->batch * c->kv_heads * p->qtiles;
+  long long length, min_piece, align;
+  if (c->mode == KVQ_MODE_CHUNK_MIXED) {
+    length = c->max_seq / c->chunk_tokens;  // chunk slots
+    min_piece = 256 / c->chunk_tokens;
+    align = 1;
+  } else {
+    if (max_len < 0) return KVQ_ERR_INVALID_ARG;
+    if (max_len > c->max_seq) return KVQ_ERR_CAPACITY;
+    length = max_len;
+    min_piece = 256;
+    align = 64;
+  }
+  if (length <= 0) {
+    p->num_splits = 1;
+    p->split_len = (int)align;
+    return KVQ_OK;
+  }
+  long long ns = num_splits;
+  if (ns == 0) {
+    ns = (kTargetGroups + units - 1) / units;
+    const long long most = (length + min_piece - 1) / min_piece;
+    if (ns > most) ns = most;
+  }
+  if (ns < 1) ns = 1;
+  if (ns > length) ns = length;
+  long long piece = (length + ns - 1) / ns;
+  piece = (piece + align - 1) / align * align;
+  ns = (length + piece - 1) / piece;
+  if (ns > 65535) return KVQ_ERR_UNSUPPORTED;
+  p->num_splits = (int)ns;
+  p->split_len = (int)piece;
+  return KVQ_OK;
+}
+
+size_t workspace_for(const kvq_cache* c, int q_heads, const Plan& p) {
+  if (p.num_splits <= 1) return 0;
+  return (size_t)c->batch * (size_t)q_heads * (size_t)p.num_splits * kvq::kPartStride * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_cache_bytes(const kvq_cache* c, kvq_cache_bytes_t* out) {
+  if (!out) return KVQ_ERR_INVALID_ARG;
+  const kvq_status s = check_config(c);
+  if (s != KVQ_OK) return s;
+  *out = kvq_cache_bytes_t{};
+  out->k = tensor_bytes(c, c->k, true);
+  out->v = tensor_bytes(c, c->v, false);
+  if (c->mode == KVQ_MODE_CHUNK_MIXED) {
+    const size_t C = (size_t)(c->max_seq / c->chunk_tokens);
+    out->perm = (size_t)c->batch * C * 4;
+    out->seg = (size_t)c->batch * 4 * 4;
+  }
+  out->status = 4;
+  return KVQ_OK;
+}
+
+kvq_status kvq_quant_append(const kvq_cache* c, const void* k_new, const void* v_new, int32_t t_new,
+                            const int32_t* pos, void* stream) {
+  kvq_status s = check_config(c);
+  if (s != KVQ_OK) return s;
+  if (t_new < 0) return KVQ_ERR_INVALID_ARG;
+  if (t_new > c->max_seq) return KVQ_ERR_CAPACITY;
+  if (t_new == 0) return KVQ_OK;
+  if (!k_new || !v_new || !pos) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos, 4)) return KVQ_ERR_ALIGNMENT;
+  s = check_buffers(c);
+  if (s != KVQ_OK) return s;
+  const CacheArgs a = cache_args(c);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint16_t* kx = static_cast<const uint16_t*>(k_new);
+  const uint16_t* vx = static_cast<const uint16_t*>(v_new);
+  hipError_t e = hipSuccess;
+  switch (c->mode) {
+    case KVQ_MODE_UNIFORM:
+      if (c->k.axis == KVQ_AXIS_CHANNEL) {
+        if (t_new % 64) return KVQ_ERR_INVALID_ARG;
+        e = kvq::launch_quant_channel(a, a.k, kx, t_new, pos, st);
+      } else {
+        e = kvq::launch_quant_token(a, a.k, kx, t_new, pos, st);
+      }
+      if (e == hipSuccess) e = kvq::launch_quant_token(a, a.v, vx, t_new, pos, st);
+      break;
+    case KVQ_MODE_OAKEN:
+      e = kvq::launch_quant_oaken(a, a.k, kx, t_new, pos, st);
+      if (e == hipSuccess) e = kvq::launch_quant_oaken(a, a.v, vx, t_new, pos, st);
+      break;
+    case KVQ_MODE_CHUNK_MIXED:
+      if (t_new != c->max_seq) return KVQ_ERR_INVALID_ARG;
+      e = kvq::launch_quant_mixed(a, a.k, kx, pos, st);
+      if (e == hipSuccess) e = kvq::launch_quant_mixed(a, a.v, vx, pos, st);
+      break;
+  }
+  return from_hip(e);
+}
+
+kvq_status kvq_reorder_chunks(const kvq_cache* c, const uint8_t* chunk_bits, int32_t n_chunks,
+                              void* stream) {
+  kvq_status s = check_config(c);
+  if (s != KVQ_OK) return s;
+  if (c->mode != KVQ_MODE_CHUNK_MIXED) return KVQ_ERR_INVALID_ARG;
+  if (n_chunks != c->max_seq / c->chunk_tokens) return KVQ_ERR_INVALID_ARG;
+  if (!chunk_bits || !c->perm || !c->seg || !c->status) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(c->perm, 4) || !aligned(c->seg, 16) || !aligned(c->status, 4)) return KVQ_ERR_ALIGNMENT;
+  const CacheArgs a = cache_args(c);
+  return from_hip(kvq::launch_reorder(a, chunk_bits, n_chunks, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32_t max_len,
+                                      int32_t num_splits, size_t* bytes) {
+  if (!bytes) return KVQ_ERR_INVALID_ARG;
+  kvq_status s = check_config(c);
+  if (s != KVQ_OK) return s;
+  Plan p;
+  s = plan_decode(c, q_heads, max_len, num_splits, &p);
+  if (s != KVQ_OK) return s;
+  *bytes = workspace_for(c, q_heads, p);
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t q_heads, const int32_t* seq_len,
+                           int32_t max_len, float sm_scale, float* out, void* workspace,
+                           size_t workspace_bytes, int32_t num_splits, void* stream) {
+  kvq_status s = check_config(c);
+  if (s != KVQ_OK) return s;
+  if (!q || !out) return KVQ_ERR_INVALID_ARG;
+  if (c->mode != KVQ_MODE_CHUNK_MIXED && !seq_len) return KVQ_ERR_INVALID_ARG;
+  if (!std::isfinite(sm_scale)) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || (seq_len && !aligned(seq_len, 4)))
+    return KVQ_ERR_ALIGNMENT;
+  Plan p;
+  s = plan_decode(c, q_heads, max_len, num_splits, &p);
+  if (s != KVQ_OK) return s;
+  const size_t need = workspace_for(c, q_heads, p);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return KVQ_ERR_ALIGNMENT;
+  }
+  s = check_buffers(c);
+  if (s != KVQ_OK) return s;
+  const CacheArgs a = cache_args(c);
+  kvq::DecodeLaunch d;
+  d.q = static_cast<const uint16_t*>(q);
+  d.Hq = q_heads;
+  d.G = p.G;
+  d.gtile = p.gtile;
+  d.qtiles = p.qtiles;
+  d.seq_len = seq_len;
+  d.max_len = c->mode == KVQ_MODE_CHUNK_MIXED ? c->max_seq : max_len;
+  d.num_splits = p.num_splits;
+  d.split_len = p.split_len;
+  d.qscale = sm_scale * 1.4426950408889634f;
+  d.out = out;
+  d.ws = static_cast<float*>(need ? workspace : nullptr);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (c->mode) {
+    case KVQ_MODE_UNIFORM: e = kvq::launch_decode_uniform(a, d, st); break;
+    case KVQ_MODE_OAKEN: e = kvq::launch_decode_oaken(a, d, st); break;
+    default: e = kvq::launch_decode_mixed(a, d, st); break;
+  }
+  if (e == hipErrorInvalidValue) return KVQ_ERR_UNSUPPORTED;
+  if (e != hipSuccess) return KVQ_ERR_HIP;
+  if (p.num_splits > 1) e = kvq::launch_merge(d, c->batch, st);
+  return from_hip(e);
+}
+
+const char* kvq_status_string(int32_t status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_CAPACITY: return "exceeds cache capacity";
+    case KVQ_ERR_ALIGNMENT: return "misaligned pointer";
+    case KVQ_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case KVQ_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Device helpers shared by the kvq kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+constexpr unsigned kFlagPosRange = 1u;
+constexpr unsigned kFlagSparseFull = 2u;
+constexpr unsigned kFlagLenRange = 4u;
+constexpr unsigned kFlagBadChunkBits = 8u;
+constexpr unsigned kFlagBlockAlign = 16u;
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// fp16 bit patterns packed two per 32-bit word -> floats.
+__device__ __forceinline__ float lo_h2f(uint32_t w) { return h2f((uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float hi_h2f(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+__device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Sum / max over the lanes that differ only in bits [lo_bit, hi_bit) of the lane id.
+template <int LO, int HI>
+__device__ __forceinline__ float sum_lanes(float v) {
+#pragma unroll
+  for (int m = LO; m < HI; m <<= 1) v += shfl_xor_f(v, m);
+  return v;
+}
+template <int LO, int HI>
+__device__ __forceinline__ float max_lanes(float v) {
+#pragma unroll
+  for (int m = LO; m < HI; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  return v;
+}
+template <int LO, int HI>
+__device__ __forceinline__ float min_lanes(float v) {
+#pragma unroll
+  for (int m = LO; m < HI; m <<= 1) v = fminf(v, shfl_xor_f(v, m));
+  return v;
+}
+
+// Unpack the DPL codes a lane holds (little-endian, see kvq.h) into floats.
+// BITS 8: one code per byte; 4: two per byte, low nibble first; 2: four per
+// byte, lowest bits first.  Each byte is widened with a byte-select convert.
+template <int BITS, int DPL>
+__device__ __forceinline__ void codes_to_float(const uint32_t* w, float* c) {
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int k = 0; k < DPL / 4; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[4 * k + j] = (float)((w[k] >> (8 * j)) & 0xFFu);
+  } else if constexpr (BITS == 4) {
+#pragma unroll
+    for (int k = 0; k < DPL / 8; ++k) {
+      uint32_t ev = w[k] & 0x0F0F0F0Fu;
+      uint32_t od = (w[k] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[8 * k + 2 * j] = (float)((ev >> (8 * j)) & 0xFFu);
+        c[8 * k + 2 * j + 1] = (float)((od >> (8 * j)) & 0xFFu);
+      }
+    }
+  } else if constexpr (BITS == 2) {
+#pragma unroll
+    for (int k = 0; k < DPL / 16; ++k)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint32_t m = (w[k] >> (2 * s)) & 0x03030303u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[16 * k + 4 * j + s] = (float)((m >> (8 * j)) & 0xFFu);
+      }
+  } else {  // 16: raw fp16
+#pragma unroll
+    for (int k = 0; k < DPL / 2; ++k) {
+      c[2 * k] = lo_h2f(w[k]);
+      c[2 * k + 1] = hi_h2f(w[k]);
+    }
+  }
+}
+
+// Load N 32-bit words from a 4*N-byte aligned address (16-byte vector loads
+// where N allows).
+template <int N>
+__device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
+  if constexpr (N == 1) {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (N == 2) {
+    uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+      uint4 v = reinterpret_cast<const uint4*>(p)[k];
+      w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+    }
+  }
+}
+
+__device__ __forceinline__ void set_flag(unsigned* status, unsigned f) { atomicOr(status, f); }
+
+}  // namespace kvq

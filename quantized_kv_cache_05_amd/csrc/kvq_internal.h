@@ -1,0 +1,77 @@
+// Host-side interface between the C-ABI layer (kvq_api.cpp) and the kernel
+// launchers (kvq_quant.hip, kvq_reorder.hip, kvq_decode*.hip).  Plain structs:
+// pointers already offset and validated by the API layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kD = 128;          // head_dim
+constexpr int kPartStride = 132; // floats per split partial: m, l, 2 pad, o[128]
+
+// Device view of one quantized tensor (K or V).
+struct TensorArgs {
+  int bits;       // 8, 4, 2 (UNIFORM), 4 (OAKEN)
+  int sym;        // symmetric INT8
+  int axis;       // 0 token, 1 channel
+  int group;      // channels (token axis) or tokens (channel axis)
+  float thr_lo, thr_hi;  // OAKEN outer thresholds
+  long long sparse_cap;
+  uint8_t* codes;
+  float* scale;
+  uint8_t* zero;
+  float* oscale;
+  uint32_t* rowptr;
+  uint16_t* sparse;
+  uint8_t* codes16;
+  uint8_t* codes2;
+  float* scale2;
+  uint8_t* zero2;
+};
+
+struct CacheArgs {
+  int B, H, S;  // batch, kv heads, max_seq
+  int mode;     // 0 uniform, 1 chunk mixed, 2 oaken
+  int chunk_tokens;
+  TensorArgs k, v;
+  int* perm;
+  int* seg;
+  unsigned* status;
+};
+
+struct DecodeLaunch {
+  const uint16_t* q;
+  int Hq;        // query heads
+  int G;         // query heads per KV head
+  int gtile;     // query heads handled per workgroup (1 or 4)
+  int qtiles;    // ceil(G / gtile)
+  const int* seq_len;
+  int max_len;
+  int num_splits;
+  int split_len; // tokens (UNIFORM/OAKEN) or chunk slots (CHUNK_MIXED) per split
+  float qscale;  // sm_scale * log2(e)
+  float* out;
+  float* ws;     // partials, null when num_splits == 1
+};
+
+hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, const uint16_t* x, int t_new,
+                              const int* pos, hipStream_t st);
+hipError_t launch_quant_channel(const CacheArgs& c, const TensorArgs& t, const uint16_t* x, int t_new,
+                                const int* pos, hipStream_t st);
+hipError_t launch_quant_mixed(const CacheArgs& c, const TensorArgs& t, const uint16_t* x,
+                              const int* pos, hipStream_t st);
+hipError_t launch_quant_oaken(const CacheArgs& c, const TensorArgs& t, const uint16_t* x, int t_new,
+                              const int* pos, hipStream_t st);
+hipError_t launch_reorder(const CacheArgs& c, const uint8_t* bits, int n_chunks, hipStream_t st);
+
+// Returns hipErrorInvalidValue for a combination without a compiled kernel.
+hipError_t launch_decode_uniform(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
+hipError_t launch_decode_oaken(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
+hipError_t launch_decode_mixed(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
+hipError_t launch_merge(const DecodeLaunch& d, int B, hipStream_t st);
+
+// True when a uniform (K, V) pair has a compiled decode kernel.
+bool decode_uniform_supported(const TensorArgs& k, const TensorArgs& v);
+
+}  // namespace kvq

@@ -1,0 +1,442 @@
+// Quantize-append kernels.
+//
+// Quantizer (per group, binary32, round half to even):
+//   asymmetric ([Oaken page "大模型KV缓存量化技术：原理、优化与实践" §2.1 scale
+//   formula; Cocktail page §3.2.2 code = round(x / s) + z]):
+//     lo = min(0, min x), hi = max(0, max x), s = (hi - lo) / (2^b - 1),
+//     z = clamp(rne(-lo / s)), q = clamp(rne(x / s) + z); all-zero group -> 0, 0, 0
+//   symmetric INT8 ([KV-cache quantization engineering page, INT8 listing]):
+//     s = max|x| / 127, q = clamp(rne(x / s), -128, 127)
+// The divisions are true IEEE divisions (the build keeps correctly rounded
+// fp32 division and denormals), so codes, scales and zero-points are
+// bit-identical to any other binary32 evaluation of these formulas.
+//
+// Thread layout of the token-axis kernels: 16 lanes per 128-channel row, each
+// lane holds 8 consecutive channels (one 16-byte load); a group of GE
+// channels is GE / 8 adjacent lanes, reduced with lane shuffles.
+#include "kvq_dev.h"
+
+namespace kvq {
+namespace {
+
+template <int BITS, bool SYM, int GE>
+__device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint32_t& plo,
+                                       uint32_t& phi, float& s, int& z) {
+  constexpr int LG = GE / 8;
+  plo = 0;
+  phi = 0;
+  if constexpr (SYM) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
+    amax = max_lanes<1, LG>(amax);
+    s = amax / 127.0f;
+    z = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      int q = 0;
+      if (s != 0.0f) q = min(max((int)rintf(x[k] / s), -128), 127);
+      uint32_t byte = (uint32_t)(q & 0xFF);
+      if (k < 4) plo |= byte << (8 * k);
+      else phi |= byte << (8 * (k - 4));
+    }
+  } else {
+    constexpr int QMAX = (1 << BITS) - 1;
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if ((valid >> k) & 1u) {
+        lo = fminf(lo, x[k]);
+        hi = fmaxf(hi, x[k]);
+      }
+    lo = min_lanes<1, LG>(lo);
+    hi = max_lanes<1, LG>(hi);
+    s = (hi - lo) / (float)QMAX;
+    z = 0;
+    if (s != 0.0f) z = min(max((int)rintf(-lo / s), 0), QMAX);
+    uint64_t packed = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      int q = z;
+      if (s == 0.0f) q = 0;
+      else if ((valid >> k) & 1u) q = min(max((int)rintf(x[k] / s) + z, 0), QMAX);
+      packed |= (uint64_t)q << (BITS * k);
+    }
+    plo = (uint32_t)packed;
+    phi = (uint32_t)(packed >> 32);
+  }
+}
+
+__device__ __forceinline__ void unpack8(const uint4 raw, float (&v)[8]) {
+  v[0] = lo_h2f(raw.x); v[1] = hi_h2f(raw.x);
+  v[2] = lo_h2f(raw.y); v[3] = hi_h2f(raw.y);
+  v[4] = lo_h2f(raw.z); v[5] = hi_h2f(raw.z);
+  v[6] = lo_h2f(raw.w); v[7] = hi_h2f(raw.w);
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_codes8(uint8_t* row, int li, uint32_t plo, uint32_t phi) {
+  if constexpr (BITS == 8) {
+    *reinterpret_cast<uint2*>(row + li * 8) = make_uint2(plo, phi);
+  } else if constexpr (BITS == 4) {
+    *reinterpret_cast<uint32_t*>(row + li * 4) = plo;
+  } else {
+    *reinterpret_cast<uint16_t*>(row + li * 2) = (uint16_t)plo;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Uniform cache, token-axis groups.  x: [B][H][t_new][128], rows in that order.
+template <int BITS, bool SYM, int GE>
+__global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict__ x, int t_new, int H,
+                                                     int S, const int* __restrict__ pos,
+                                                     long long rows, uint8_t* __restrict__ codes,
+                                                     float* __restrict__ scale,
+                                                     uint8_t* __restrict__ zero,
+                                                     unsigned* __restrict__ status) {
+  constexpr int NG = kD / GE, LG = GE / 8, RB = kD * BITS / 8;
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int li = threadIdx.x & 15;
+  if (row >= rows) return;  // all 16 lanes of a row leave together
+  const int t = (int)(row % t_new);
+  const long long bh = row / t_new;
+  const int b = (int)(bh / H);
+  const int p = pos[b];
+  if (p < 0 || p + t >= S) {
+    if (li == 0) set_flag(status, kFlagPosRange);
+    return;
+  }
+  const long long dst = bh * S + p + t;
+  float v[8];
+  unpack8(*reinterpret_cast<const uint4*>(x + row * kD + li * 8), v);
+  uint32_t plo, phi;
+  float s;
+  int z;
+  quant8<BITS, SYM, GE>(v, 0xFFu, plo, phi, s, z);
+  store_codes8<BITS>(codes + dst * RB, li, plo, phi);
+  if (li % LG == 0) {
+    scale[dst * NG + li / LG] = s;
+    if constexpr (!SYM) zero[dst * NG + li / LG] = (uint8_t)z;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Uniform cache, channel-axis groups of 64 tokens (K per channel, [KV-cache
+// quantization engineering page] advice).  One workgroup per 64-token block.
+template <int BITS>
+__global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restrict__ x, int t_new,
+                                                       int H, int S, const int* __restrict__ pos,
+                                                       uint8_t* __restrict__ codes,
+                                                       float* __restrict__ scale,
+                                                       uint8_t* __restrict__ zero,
+                                                       unsigned* __restrict__ status) {
+  constexpr int QMAX = (1 << BITS) - 1, RB = kD * BITS / 8, PB = 32 * BITS / 8;
+  const int kb = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int b = (int)(bh / H);
+  const int p = pos[b];
+  if (p < 0 || p + t_new > S || (p & 63)) {
+    if (threadIdx.x == 0 && kb == 0)
+      set_flag(status, (p < 0 || p + t_new > S) ? kFlagPosRange : kFlagBlockAlign);
+    return;
+  }
+  __shared__ float tile[64][kD + 1];
+  __shared__ float lo_sh[2][kD], hi_sh[2][kD], s_sh[kD];
+  __shared__ int z_sh[kD];
+  const uint16_t* xb = x + (bh * t_new + (long long)kb * 64) * kD;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int r = pass * 16 + (threadIdx.x >> 4), li = threadIdx.x & 15;
+    float v[8];
+    unpack8(*reinterpret_cast<const uint4*>(xb + r * kD + li * 8), v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) tile[r][li * 8 + k] = v[k];
+  }
+  __syncthreads();
+  {
+    const int c = threadIdx.x & 127, half = threadIdx.x >> 7;
+    float lo = 0.0f, hi = 0.0f;
+    for (int r = half * 32; r < half * 32 + 32; ++r) {
+      const float v = tile[r][c];
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+    }
+    lo_sh[half][c] = lo;
+    hi_sh[half][c] = hi;
+  }
+  __syncthreads();
+  if (threadIdx.x < kD) {
+    const int c = threadIdx.x;
+    const float lo = fminf(lo_sh[0][c], lo_sh[1][c]);
+    const float hi = fmaxf(hi_sh[0][c], hi_sh[1][c]);
+    const float s = (hi - lo) / (float)QMAX;
+    int z = 0;
+    if (s != 0.0f) z = min(max((int)rintf(-lo / s), 0), QMAX);
+    s_sh[c] = s;
+    z_sh[c] = z;
+    const long long m = (bh * (S / 64) + p / 64 + kb) * kD + c;
+    scale[m] = s;
+    zero[m] = (uint8_t)z;
+  }
+  __syncthreads();
+  const int r = threadIdx.x >> 2, pc = threadIdx.x & 3;
+  uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int ch = pc * 32 + k;
+    const float s = s_sh[ch];
+    int q = 0;
+    if (s != 0.0f) q = min(max((int)rintf(tile[r][ch] / s) + z_sh[ch], 0), QMAX);
+    words[(k * BITS) / 32] |= (uint32_t)q << ((k * BITS) % 32);
+  }
+  uint8_t* dst = codes + (bh * S + p + (long long)kb * 64 + r) * RB + pc * PB;
+#pragma unroll
+  for (int k = 0; k < PB / 4; ++k) reinterpret_cast<uint32_t*>(dst)[k] = words[k];
+}
+
+// ---------------------------------------------------------------------------
+// Chunk-mixed cache ([Cocktail page] §3.1.2 reorder, then quantization of the
+// reordered chunks): one workgroup per (slot, b, h); the slot's source chunk
+// is perm[b][slot], its class follows from seg[b].  FP16 chunks are copied.
+template <int GE>
+__global__ __launch_bounds__(256) void k_quant_mixed(
+    const uint16_t* __restrict__ x, int H, int S, int CT, int C, const int* __restrict__ pos,
+    const int* __restrict__ perm, const int* __restrict__ seg, uint8_t* __restrict__ c16,
+    uint8_t* __restrict__ c4, float* __restrict__ s4, uint8_t* __restrict__ z4,
+    uint8_t* __restrict__ c2, float* __restrict__ s2, uint8_t* __restrict__ z2,
+    unsigned* __restrict__ status) {
+  constexpr int NG = kD / GE, LG = GE / 8;
+  const int j = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int b = (int)(bh / H);
+  if (pos[b] != 0) {
+    if (threadIdx.x == 0 && j == 0) set_flag(status, kFlagPosRange);
+    return;
+  }
+  const int n16 = seg[b * 4], n4 = seg[b * 4 + 1], n = seg[b * 4 + 3];
+  if (j >= n || n > C) return;
+  const int src = perm[(long long)b * C + j];
+  if (src < 0 || src >= C) return;
+  const int cls = j < n16 ? 0 : (j < n16 + n4 ? 1 : 2);
+  const int k = cls == 0 ? j : (cls == 1 ? j - n16 : j - n16 - n4);
+  const uint16_t* xs = x + (bh * S + (long long)src * CT) * kD;
+  const long long drow0 = (bh * C + k) * CT;
+  const int li = threadIdx.x & 15;
+  for (int r = threadIdx.x >> 4; r < CT; r += 16) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(xs + (long long)r * kD + li * 8);
+    const long long drow = drow0 + r;
+    if (cls == 0) {
+      *reinterpret_cast<uint4*>(c16 + (drow * kD + li * 8) * 2) = raw;
+      continue;
+    }
+    float v[8];
+    unpack8(raw, v);
+    uint32_t plo, phi;
+    float s;
+    int z;
+    if (cls == 1) {
+      quant8<4, false, GE>(v, 0xFFu, plo, phi, s, z);
+      store_codes8<4>(c4 + drow * 64, li, plo, phi);
+      if (li % LG == 0) {
+        s4[drow * NG + li / LG] = s;
+        z4[drow * NG + li / LG] = (uint8_t)z;
+      }
+    } else {
+      quant8<2, false, GE>(v, 0xFFu, plo, phi, s, z);
+      store_codes8<2>(c2 + drow * 32, li, plo, phi);
+      if (li % LG == 0) {
+        s2[drow * NG + li / LG] = s;
+        z2[drow * NG + li / LG] = (uint8_t)z;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Oaken ([Oaken page] §3.1 online stage, §3.2.1-3.2.2): per row, outer values
+// (x > T_hi_outer or x < T_lo_outer) leave the dense INT4 body (coded z) and
+// go to the row's sparse list as shifted deltas with a per-group 5-bit scale.
+// One workgroup per (b, h) walks the new rows in tiles of 16, keeping the
+// running entry offset so rowptr stays a prefix sum.
+template <int GE>
+__global__ __launch_bounds__(256) void k_quant_oaken(
+    const uint16_t* __restrict__ x, int t_new, int H, int S, const int* __restrict__ pos,
+    float t_lo, float t_hi, long long cap, uint8_t* __restrict__ codes, float* __restrict__ scale,
+    uint8_t* __restrict__ zero, float* __restrict__ oscale, uint32_t* __restrict__ rowptr,
+    uint16_t* __restrict__ sparse, unsigned* __restrict__ status) {
+  constexpr int NG = kD / GE, LG = GE / 8;
+  const long long bh = blockIdx.x;
+  const int b = (int)(bh / H);
+  const int p = pos[b];
+  if (p < 0 || p + t_new > S) {
+    if (threadIdx.x == 0) set_flag(status, kFlagPosRange);
+    return;
+  }
+  uint32_t* rp = rowptr + bh * (S + 1);
+  uint16_t* sp = sparse + bh * cap;
+  __shared__ int row_cnt[16];
+  unsigned long long base = p == 0 ? 0ull : (unsigned long long)rp[p];
+  if (p == 0 && threadIdx.x == 0) rp[0] = 0u;
+  const int rl = threadIdx.x >> 4, li = threadIdx.x & 15;
+  bool dropped = false;
+  for (int t0 = 0; t0 < t_new; t0 += 16) {
+    const int t = t0 + rl;
+    const bool active = t < t_new;
+    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    unsigned outer = 0;
+    if (active) {
+      unpack8(*reinterpret_cast<const uint4*>(x + (bh * t_new + t) * kD + li * 8), v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) outer |= (unsigned)((v[k] > t_hi) || (v[k] < t_lo)) << k;
+    }
+    uint32_t plo, phi;
+    float s;
+    int z;
+    quant8<4, false, GE>(v, ~outer & 0xFFu, plo, phi, s, z);
+    float dmax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if ((outer >> k) & 1u) dmax = fmaxf(dmax, fabsf(v[k] > t_hi ? v[k] - t_hi : v[k] - t_lo));
+    dmax = max_lanes<1, LG>(dmax);
+    const float so = dmax / 31.0f;
+    const int lc = __popc(outer);
+    int incl = lc;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      const int o = __shfl_up(incl, m, 16);
+      if (li >= m) incl += o;
+    }
+    const int rowtot = __shfl(incl, 15, 16);
+    if (li == 0) row_cnt[rl] = active ? rowtot : 0;
+    __syncthreads();
+    unsigned long long rb = base, tile_tot = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < rl) rb += (unsigned)row_cnt[i];
+      tile_tot += (unsigned)row_cnt[i];
+    }
+    if (active) {
+      const long long dst = bh * S + p + t;
+      store_codes8<4>(codes + dst * 64, li, plo, phi);
+      if (li % LG == 0) {
+        scale[dst * NG + li / LG] = s;
+        zero[dst * NG + li / LG] = (uint8_t)z;
+        oscale[dst * NG + li / LG] = so;
+      }
+      unsigned long long e = rb + (unsigned)(incl - lc);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if ((outer >> k) & 1u) {
+          const bool above = v[k] > t_hi;
+          const float delta = above ? v[k] - t_hi : v[k] - t_lo;
+          int mag = 0;
+          if (so != 0.0f) mag = min(max((int)rintf(fabsf(delta) / so), 0), 31);
+          if (e < (unsigned long long)cap)
+            sp[e] = (uint16_t)((li * 8 + k) | ((int)above << 7) | (mag << 8));
+          else
+            dropped = true;
+          ++e;
+        }
+      if (li == 0) {
+        unsigned long long end = rb + (unsigned)rowtot;
+        rp[p + t + 1] = (uint32_t)(end < (unsigned long long)cap ? end : (unsigned long long)cap);
+      }
+    }
+    base += tile_tot;
+    __syncthreads();
+  }
+  if (dropped) set_flag(status, kFlagSparseFull);
+}
+
+constexpr int kThreads = 256;
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers
+
+hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, const uint16_t* x, int t_new,
+                              const int* pos, hipStream_t st) {
+  const long long rows = (long long)c.B * c.H * t_new;
+  const dim3 grid((unsigned)((rows + 15) / 16));
+#define KVQ_TOK(BITS, SYM, GE)                                                                 \
+  hipLaunchKernelGGL((k_quant_token<BITS, SYM, GE>), grid, dim3(kThreads), 0, st, x, t_new, c.H, \
+                     c.S, pos, rows, t.codes, t.scale, t.zero, c.status)
+#define KVQ_TOK_G(BITS, SYM)                  \
+  switch (t.group) {                          \
+    case 32: KVQ_TOK(BITS, SYM, 32); break;   \
+    case 64: KVQ_TOK(BITS, SYM, 64); break;   \
+    case 128: KVQ_TOK(BITS, SYM, 128); break; \
+    default: return hipErrorInvalidValue;     \
+  }
+  if (t.sym) {
+    if (t.bits != 8) return hipErrorInvalidValue;
+    KVQ_TOK_G(8, true);
+  } else if (t.bits == 8) {
+    KVQ_TOK_G(8, false);
+  } else if (t.bits == 4) {
+    KVQ_TOK_G(4, false);
+  } else if (t.bits == 2) {
+    KVQ_TOK_G(2, false);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef KVQ_TOK_G
+#undef KVQ_TOK
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_channel(const CacheArgs& c, const TensorArgs& t, const uint16_t* x, int t_new,
+                                const int* pos, hipStream_t st) {
+  if (t.group != 64 || t_new % 64) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(t_new / 64), (unsigned)(c.B * c.H));
+  if (t.bits == 8)
+    hipLaunchKernelGGL(k_quant_channel<8>, grid, dim3(kThreads), 0, st, x, t_new, c.H, c.S, pos,
+                       t.codes, t.scale, t.zero, c.status);
+  else if (t.bits == 4)
+    hipLaunchKernelGGL(k_quant_channel<4>, grid, dim3(kThreads), 0, st, x, t_new, c.H, c.S, pos,
+                       t.codes, t.scale, t.zero, c.status);
+  else if (t.bits == 2)
+    hipLaunchKernelGGL(k_quant_channel<2>, grid, dim3(kThreads), 0, st, x, t_new, c.H, c.S, pos,
+                       t.codes, t.scale, t.zero, c.status);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mixed(const CacheArgs& c, const TensorArgs& t, const uint16_t* x,
+                              const int* pos, hipStream_t st) {
+  const int C = c.S / c.chunk_tokens;
+  const dim3 grid((unsigned)C, (unsigned)(c.B * c.H));
+#define KVQ_MIX(GE)                                                                              \
+  hipLaunchKernelGGL(k_quant_mixed<GE>, grid, dim3(kThreads), 0, st, x, c.H, c.S, c.chunk_tokens, \
+                     C, pos, c.perm, c.seg, t.codes16, t.codes, t.scale, t.zero, t.codes2,       \
+                     t.scale2, t.zero2, c.status)
+  switch (t.group) {
+    case 32: KVQ_MIX(32); break;
+    case 64: KVQ_MIX(64); break;
+    case 128: KVQ_MIX(128); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef KVQ_MIX
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_oaken(const CacheArgs& c, const TensorArgs& t, const uint16_t* x, int t_new,
+                              const int* pos, hipStream_t st) {
+  const dim3 grid((unsigned)(c.B * c.H));
+#define KVQ_OAK(GE)                                                                              \
+  hipLaunchKernelGGL(k_quant_oaken<GE>, grid, dim3(kThreads), 0, st, x, t_new, c.H, c.S, pos,     \
+                     t.thr_lo, t.thr_hi, t.sparse_cap, t.codes, t.scale, t.zero, t.oscale,        \
+                     t.rowptr, t.sparse, c.status)
+  switch (t.group) {
+    case 32: KVQ_OAK(32); break;
+    case 64: KVQ_OAK(64); break;
+    case 128: KVQ_OAK(128); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef KVQ_OAK
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -50,10 +50,14 @@ static double normal_at(uint64_t key, uint64_t i) {
 }
 
 static double student_t3_at(uint64_t key, uint64_t i) {
-  double z0 = normal_at(key, 4 * i);
-  double z1 = normal_at(key, 4 * i + 1);
-  double z2 = normal_at(key, 4 * i + 2);
-  double z3 = normal_at(key, 4 * i + 3);
+  /* normals 4i .. 4i+3 are the pairs 2i and 2i + 1 */
+  const double two_pi = 6.283185307179586476925286766559;
+  double r0 = sqrt(-2.0 * log(unit_open(key, 4 * i)));
+  double a0 = two_pi * unit_open(key, 4 * i + 1);
+  double r1 = sqrt(-2.0 * log(unit_open(key, 4 * i + 2)));
+  double a1 = two_pi * unit_open(key, 4 * i + 3);
+  double z0 = r0 * cos(a0), z1 = r0 * sin(a0);
+  double z2 = r1 * cos(a1), z3 = r1 * sin(a1);
   return z0 / sqrt((z1 * z1 + z2 * z2 + z3 * z3) / 3.0);
 }
 
@@ -99,10 +103,26 @@ uint16_t synth_f16_from_double(double v) {
 void synth_fill_f16(uint64_t seed, uint64_t stream, int dist, double mult, uint64_t start,
                     uint64_t count, int dim, uint64_t rows_per_head, int heads,
                     const double* chan_scale, uint16_t* out) {
+  const double two_pi = 6.283185307179586476925286766559;
   uint64_t key = synth_stream_key(seed, stream);
+  /* Normals come in Box-Muller pairs; the pair's radius is computed once and
+     each element still takes exactly the cos or sin branch defined above. */
+  double pr = 0.0, pt = 0.0;
+  uint64_t cached = ~0ULL;
   for (uint64_t k = 0; k < count; ++k) {
     uint64_t i = start + k;
-    double v = dist == 1 ? student_t3_at(key, i) : normal_at(key, i);
+    double v;
+    if (dist == 1) {
+      v = student_t3_at(key, i);
+    } else {
+      uint64_t p = i >> 1;
+      if (p != cached) {
+        pr = sqrt(-2.0 * log(unit_open(key, 2 * p)));
+        pt = two_pi * unit_open(key, 2 * p + 1);
+        cached = p;
+      }
+      v = (i & 1) ? pr * sin(pt) : pr * cos(pt);
+    }
     v *= mult;
     if (chan_scale) {
       uint64_t row = i / (uint64_t)dim;

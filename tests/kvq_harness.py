@@ -1,0 +1,69 @@
+"""Test-side helpers: unpack the documented packed layout, move fp16 bits to
+the GPU, and compare attention outputs.  Neither the oracle nor the HIP
+library is imported here; tests combine the three.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Bar for attention outputs: max relative error 2e-3 per (b, query head) row,
+# relative to the row's largest |output| (the per-row infinity norm).
+ATTN_BAR = 2e-3
+# Tighter implementation check, from the arithmetic: binary32 scores with
+# relative error ~1e-6 of |score| <= ~30 (base-2 logits) move each softmax
+# weight by <= ~3e-5; binary32 accumulation of a few hundred terms per wave
+# adds ~1e-6.  1e-4 leaves 3x margin and still catches a dropped or repeated
+# token at the sequence lengths the small tests use (~1/S >= 1e-3).
+ATTN_TIGHT = 1e-4
+
+
+def unpack_codes(packed: np.ndarray, bits: int, signed: bool = False) -> np.ndarray:
+    """Packed token rows [..., 128*bits/8] (uint8) -> one code per channel [..., 128]."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    if bits == 8:
+        return p.view(np.int8) if signed else p
+    if bits == 4:
+        out = np.stack([p & 0x0F, p >> 4], axis=-1)
+    elif bits == 2:
+        out = np.stack([(p >> (2 * j)) & 0x03 for j in range(4)], axis=-1)
+    else:
+        raise ValueError(bits)
+    return out.reshape(p.shape[:-1] + (p.shape[-1] * (8 // bits),))
+
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Inverse of unpack_codes (used only to test the unpacker itself)."""
+    c = np.ascontiguousarray(codes).astype(np.uint8)
+    if bits == 8:
+        return c
+    per = 8 // bits
+    c = c.reshape(c.shape[:-1] + (c.shape[-1] // per, per)).astype(np.uint16)
+    out = np.zeros(c.shape[:-1], np.uint16)
+    for j in range(per):
+        out |= c[..., j] << (bits * j)
+    return out.astype(np.uint8)
+
+
+def rel_err_rows(out: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-row max|out - ref| / max|ref| over the last axis."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    num = np.max(np.abs(out - ref), axis=-1)
+    den = np.maximum(np.max(np.abs(ref), axis=-1), 1e-30)
+    return num / den
+
+
+def to_device(bits: np.ndarray, device="cuda"):
+    """fp16 bit patterns (uint16 numpy) -> torch int16 device tensor (same bytes)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)
+
+
+def i32_device(values, device="cuda"):
+    import torch
+    return torch.tensor(np.asarray(values, dtype=np.int32), dtype=torch.int32, device=device)
+
+
+def host_bytes(t) -> np.ndarray:
+    """A uint8 / int32 device tensor -> numpy (synchronizes)."""
+    return t.cpu().numpy()
