@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--quiet", action="store_true")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="run one plain device copy of this size first (HBM counter calibration)")
     return p.parse_args()
 
 
@@ -142,6 +144,15 @@ def main():
     ws, ws_bytes = cache.workspace(Hq, L, args.num_splits)
     sm = 1.0 / np.sqrt(128.0)
     stream = torch.cuda.current_stream()
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # bulk prefill quantize (also fills the cache)
     for _ in range(2):
