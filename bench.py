@@ -1,24 +1,42 @@
 #!/usr/bin/env python
 """Benchmark of the quantized KV-cache hot path on one MI355X.
 
-Workload: Llama-2-7B-shaped attention layer, batch 16, 32 MHA heads,
-head_dim 128, 4096 cached tokens + 1 appended, fp16 K/V ~ N(0, 1) with 4
-outlier channels per (tensor, head) scaled x15, INT8 symmetric per token and
-head (scale = amax / 127).  One step = quantize-append of 1 token per
-sequence (K and V) followed by one decode query per head over the 4097
-cached tokens (fused-dequant split decode + log-sum-exp merge).
+Workloads (seeded synthetic fp16 K/V, head_dim 128; ``--workload N``):
+  1 tiny      batch 1, 1 head, 1024 tokens, INT4 asymmetric groups of 64
+              along head_dim; step = quantize all 1024 tokens + 1 decode query
+  2 llama2    (default) batch 16, 32 MHA heads, 4096 cached + 1 appended
+              token, INT8 symmetric per token and head; step = append 1 token
+              per sequence + 1 decode query per head over 4097 tokens
+  3 gqa128k   batch 1, 32 query / 8 KV heads, 131072 tokens, INT4, K per
+              channel over 64-token blocks, V groups of 64 along head_dim;
+              step = 1 split-sequence decode query per head (4 cache copies
+              rotate so that the 256 MB last-level cache cannot hold the
+              working set)
+  4 cocktail  batch 8, 40 heads, 32768 tokens in 32-token chunks classed
+              FP16 / INT4 / INT2 (groups of 32) by query-chunk cosine
+              similarity and reordered contiguous by class; step = 1 chunked
+              decode query per head
+  5 oaken     batch 256, 40 heads, 2048 tokens of 0.5 * Student-t(3);
+              thresholds from a 100-sequence calibration set; dense INT4 +
+              sparse shifted outer values; step = append 1 token per
+              sequence + 1 decode query per head
 
-Prints one JSON line: value = algorithmic bytes of the step (packed cache +
-metadata read, q read, output written, appended token read and written) per
-second of step time, in GB/s; roofline = the decode call alone against the
-8 TB/s HBM peak; quantize-append throughput (bulk prefill and per-step
-append) in tokens/s, a token being one sequence position across all KV heads,
-K and V; cpu_baseline = the CPU oracle on a bounded sample of the same work.
+Prints one JSON line.  value = algorithmic bytes of a step (packed cache and
+metadata read by decode, query read, output written, appended tokens read
+and written) per second of step time, in GB/s.  roofline = the decode kernel
+alone: its algorithmic bytes over its average duration (HIP events on the
+stream it runs on) against the 8 TB/s HBM peak.  Quantize throughput is in
+tokens/s, a token being one sequence position over all KV heads, K and V.
+cpu_baseline = the CPU oracle on a bounded sample of the same work, single
+thread and all threads.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -28,6 +46,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn packed-KV GB/s (% of HBM peak) + quantize-append tokens/s"
 HBM_PEAK_GBS = 8000.0
+SM_SCALE = 1.0 / math.sqrt(128.0)
+MALL_BYTES = 256 << 20
 
 
 def parse():
@@ -35,8 +55,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     p.add_argument("--num-splits", type=int, default=0)
-    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--cpu-seconds", type=float, default=16.0,
+                   help="budget of the CPU-oracle leg (half single-threaded, half all threads)")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--quiet", action="store_true")
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -44,106 +66,496 @@ def parse():
     return p.parse_args()
 
 
-def log(args, *a):
-    if not args.quiet:
+ARGS = None
+
+
+def log(*a):
+    if not ARGS.quiet:
         print(*a, file=sys.stderr, flush=True)
 
 
-def decode_bytes(B, H, Hq, L):
-    codes = 2 * B * H * L * 128          # INT8 K and V codes
-    scales = 2 * B * H * L * 4           # fp32 scale per token and head, K and V
-    q = B * Hq * 128 * 2
-    out = B * Hq * 128 * 4
-    return codes + scales + q + out
+# ---------------------------------------------------------------------------
+# inputs
+
+def upload_kv(w, tensor, torch, chunk_bytes=512 << 20):
+    """Device int16 [B][H][T][128] holding the fp16 bits of K (0) or V (1), generated per batch slice."""
+    B, H, T = w.batch, w.kv_heads, w.tokens
+    out = torch.empty((B, H, T, 128), dtype=torch.int16, device="cuda")
+    per = max(1, chunk_bytes // (H * T * 128 * 2))
+    for b0 in range(0, B, per):
+        b1 = min(B, b0 + per)
+        host = w.kv(tensor, b0, b1)
+        out[b0:b1].copy_(torch.from_numpy(host.view("int16")))
+    return out
 
 
-def append_bytes(B, H, t):
-    return 2 * B * H * t * (128 * 2 + 128 + 4)  # fp16 in, int8 codes + fp32 scale out, K and V
+def i32(torch, vals):
+    import numpy as np
+    return torch.tensor(np.asarray(vals, dtype=np.int32), dtype=torch.int32, device="cuda")
 
 
-def cpu_baseline(w, budget_s, args):
-    """The oracle (single thread) on whole (b, h) slices until the time budget is spent."""
+# ---------------------------------------------------------------------------
+# workloads: each sets up device state and exposes prefill(), step(), byte counts
+
+class Workload:
+    rotate = 1
+
+    def __init__(self, w, torch, K):
+        self.w, self.torch, self.K = w, torch, K
+        self.q = None
+        self.out = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float32, device="cuda")
+
+    # decode over cache copy r
+    def decode(self, r):
+        c = self.caches[r]
+        self.K.kvq_decode_attn(c.desc, self.q, self.w.q_heads, self.seq_len, self.max_len, SM_SCALE,
+                               self.out, self.ws[r][0], self.ws[r][1], ARGS.num_splits)
+
+    def make_workspaces(self):
+        self.ws = [c.workspace(self.w.q_heads, self.max_len, ARGS.num_splits) for c in self.caches]
+
+    def append(self, r):
+        pass
+
+    def append_bytes(self):
+        return 0
+
+    def flags(self):
+        return [c.flags() for c in self.caches]
+
+
+class UniformToken(Workload):
+    """Workloads 1 and 2: token-axis groups, optional 1-token append per step."""
+
+    def __init__(self, w, torch, K, bits, sym, group, append):
+        super().__init__(w, torch, K)
+        self.bits, self.sym, self.group, self.app = bits, sym, group, append
+        B, H, T = w.batch, w.kv_heads, w.tokens
+        self.T0 = T - 1 if append else T
+        S = (T + 63) // 64 * 64
+        kx, vx = upload_kv(w, 0, torch), upload_kv(w, 1, torch)
+        self.k_pre = kx[:, :, :self.T0].contiguous()
+        self.v_pre = vx[:, :, :self.T0].contiguous()
+        if append:
+            self.k_new = kx[:, :, self.T0:].contiguous()
+            self.v_new = vx[:, :, self.T0:].contiguous()
+        del kx, vx
+        self.caches = [K.QuantKVCache(B, H, S, K.KVQ_MODE_UNIFORM, k_bits=bits, symmetric=sym,
+                                      k_group=group)]
+        self.q = torch.from_numpy(w.q().view("int16")).cuda()
+        self.pos0 = i32(torch, [0] * B)
+        self.pos_app = i32(torch, [self.T0] * B)
+        self.seq_len = i32(torch, [T] * B)
+        self.max_len = T
+        self.make_workspaces()
+        self.prefill_tokens = B * self.T0
+
+    def prefill(self, r=0):
+        self.K.kvq_quant_append(self.caches[r].desc, self.k_pre, self.v_pre, self.T0, self.pos0)
+
+    def append(self, r):
+        if self.app:
+            self.K.kvq_quant_append(self.caches[r].desc, self.k_new, self.v_new, 1, self.pos_app)
+        else:  # the tiny workload quantizes its whole sequence every step
+            self.prefill(r)
+
+    def row_bytes(self):
+        ng = 128 // self.group
+        return 128 * self.bits // 8 + ng * 4 + (0 if self.sym else ng)
+
+    def decode_bytes(self):
+        w = self.w
+        return (2 * w.batch * w.kv_heads * w.tokens * self.row_bytes()
+                + w.batch * w.q_heads * 128 * (2 + 4))
+
+    def append_bytes(self):
+        w = self.w
+        t = 1 if self.app else self.T0
+        return 2 * w.batch * w.kv_heads * t * (256 + self.row_bytes())
+
+
+class ChannelK(Workload):
+    """Workload 3: K per channel over 64-token blocks, V token groups of 64, GQA."""
+
+    def __init__(self, w, torch, K):
+        super().__init__(w, torch, K)
+        B, H, T = w.batch, w.kv_heads, w.tokens
+        self.kx, self.vx = upload_kv(w, 0, torch), upload_kv(w, 1, torch)
+        one = K.QuantKVCache(B, H, T, K.KVQ_MODE_UNIFORM, k_bits=4, k_axis=K.KVQ_AXIS_CHANNEL,
+                             k_group=64, v_group=64)
+        self.rotate = max(1, min(8, -(-2 * MALL_BYTES // one.total_bytes)))
+        self.caches = [one] + [K.QuantKVCache(B, H, T, K.KVQ_MODE_UNIFORM, k_bits=4,
+                                              k_axis=K.KVQ_AXIS_CHANNEL, k_group=64, v_group=64)
+                               for _ in range(self.rotate - 1)]
+        self.q = torch.from_numpy(w.q().view("int16")).cuda()
+        self.pos0 = i32(torch, [0] * B)
+        self.seq_len = i32(torch, [T] * B)
+        self.max_len = T
+        self.make_workspaces()
+        self.prefill_tokens = B * T
+
+    def prefill(self, r=0):
+        self.K.kvq_quant_append(self.caches[r].desc, self.kx, self.vx, self.w.tokens, self.pos0)
+
+    def decode_bytes(self):
+        w = self.w
+        rows = w.batch * w.kv_heads * w.tokens
+        k = rows * 64 + (rows // 64) * 128 * 5
+        v = rows * (64 + 2 * 5)
+        return k + v + w.batch * w.q_heads * 128 * (2 + 4)
+
+
+class Cocktail(Workload):
+    """Workload 4: chunk precision search, reorder, class pools, chunked decode."""
+
+    def __init__(self, w, torch, K):
+        super().__init__(w, torch, K)
+        import numpy as np
+        B, H, T, CT = w.batch, w.kv_heads, w.tokens, w.chunk_tokens
+        self.C = T // CT
+        embs = [w.chunk_embeddings(b) for b in range(B)]
+        self.q_emb = torch.from_numpy(np.stack([e[0] for e in embs])).cuda()
+        self.c_emb = torch.from_numpy(np.stack([e[1] for e in embs])).cuda()
+        self.bits = torch.zeros((B, self.C), dtype=torch.uint8, device="cuda")
+        self.kx, self.vx = upload_kv(w, 0, torch), upload_kv(w, 1, torch)
+        self.caches = [K.QuantKVCache(B, H, T, K.KVQ_MODE_CHUNK_MIXED, k_group=32, chunk_tokens=CT)]
+        self.q = torch.from_numpy(w.q().view("int16")).cuda()
+        self.pos0 = i32(torch, [0] * B)
+        self.seq_len = None
+        self.max_len = T
+        self.make_workspaces()
+        self.prefill_tokens = B * T
+        self.search()
+        torch.cuda.synchronize()
+
+    def search(self):
+        w = self.w
+        self.K.kvq_chunk_bits(self.q_emb, self.c_emb, w.batch, self.C, w.emb_dim, self.K.COCKTAIL_ALPHA,
+                              self.K.COCKTAIL_BETA, self.bits)
+
+    def prefill(self, r=0):
+        c = self.caches[r]
+        self.K.kvq_reorder_chunks(c.desc, self.bits, self.C)
+        self.K.kvq_quant_append(c.desc, self.kx, self.vx, self.w.tokens, self.pos0)
+
+    def seg(self):
+        return self.caches[0].buf("seg").cpu().numpy().reshape(self.w.batch, 4)
+
+    def decode_bytes(self):
+        w = self.w
+        CT, H = w.chunk_tokens, w.kv_heads
+        ng = 128 // 32
+        total = 0
+        for n16, n4, n2, _ in self.seg():
+            rows16, rows4, rows2 = n16 * CT, n4 * CT, n2 * CT
+            total += 2 * H * (rows16 * 256 + rows4 * (64 + ng * 5) + rows2 * (32 + ng * 5))
+            total += 16  # the sequence's segment counts
+        return total + w.batch * w.q_heads * 128 * (2 + 4)
+
+
+class Oaken(Workload):
+    """Workload 5: calibration, dense INT4 + sparse outer list, 1-token append per step."""
+
+    def __init__(self, w, torch, K):
+        super().__init__(w, torch, K)
+        B, H, T = w.batch, w.kv_heads, w.tokens
+        t = time.perf_counter()
+        self.thr = [self.calibrate(0), self.calibrate(1)]
+        log("calibration (2 x %d sequences) in %.1fs: K %s V %s" % (
+            w.cal_samples, time.perf_counter() - t, self.thr[0], self.thr[1]))
+        self.kx, self.vx = upload_kv(w, 0, torch), upload_kv(w, 1, torch)
+        self.k_new = self.kx[:, :, T - 1:].contiguous()
+        self.v_new = self.vx[:, :, T - 1:].contiguous()
+        cap = int(T * 128 * 0.08)  # outer share is ~5 % by construction of the thresholds
+        self.caches = [K.QuantKVCache(B, H, T, K.KVQ_MODE_OAKEN, k_bits=4, k_group=64, k_thr=self.thr[0],
+                                      v_thr=self.thr[1], sparse_cap=cap)]
+        self.q = torch.from_numpy(w.q().view("int16")).cuda()
+        self.pos0 = i32(torch, [0] * B)
+        self.pos_app = i32(torch, [T - 1] * B)
+        self.seq_len = i32(torch, [T] * B)
+        self.max_len = T
+        self.make_workspaces()
+        self.prefill_tokens = B * T
+
+    def calibrate(self, tensor):
+        torch, K, w = self.torch, self.K, self.w
+        hist = torch.zeros(65536, dtype=torch.int64, device="cuda")
+        for s in range(w.cal_samples):
+            x = w.calibration(tensor, s)
+            K.kvq_hist_f16(torch.from_numpy(x.view("int16")).cuda(), x.size, hist)
+        out = torch.zeros(4, dtype=torch.float32, device="cuda")
+        K.kvq_hist_percentiles(hist, K.OAKEN_PERCENTILES_BP, out)
+        return [float(v) for v in out.cpu()]
+
+    def prefill(self, r=0):
+        self.K.kvq_quant_append(self.caches[r].desc, self.kx, self.vx, self.w.tokens, self.pos0)
+
+    def append(self, r):
+        self.K.kvq_quant_append(self.caches[r].desc, self.k_new, self.v_new, 1, self.pos_app)
+
+    def entries(self):
+        c = self.caches[0]
+        T = self.w.tokens
+        tot = 0
+        for name in ("k", "v"):
+            rp = c.buf(name + ".rowptr").view(self.torch.int32).view(-1, T + 1)[:, T]
+            tot += int(rp.to(self.torch.int64).sum())
+        return tot
+
+    def decode_bytes(self):
+        w = self.w
+        rows = w.batch * w.kv_heads * w.tokens
+        per_row = 64 + 2 * (4 + 1 + 4)  # dense codes, scale, zero-point, outer scale per group
+        rowptr = w.batch * w.kv_heads * (w.tokens + 1) * 4
+        return 2 * (rows * per_row + rowptr) + 2 * self.entries() + w.batch * w.q_heads * 128 * (2 + 4)
+
+    def append_bytes(self):
+        # one token per (b, h) and tensor: fp16 row in; dense codes, group metadata and the row
+        # pointer out, plus that row's share of the sparse entries (measured mean)
+        w = self.w
+        rows = w.batch * w.kv_heads
+        per_row_entries = self.entries() / (2 * rows * w.tokens)
+        return int(2 * rows * (256 + 64 + 2 * 9 + 4 + 2 * per_row_entries))
+
+
+def build_workload(idx, torch, K, synth):
+    w = synth.WORKLOADS[idx]
+    if idx == 1:
+        return UniformToken(w, torch, K, bits=4, sym=False, group=64, append=False)
+    if idx == 2:
+        return UniformToken(w, torch, K, bits=8, sym=True, group=128, append=True)
+    if idx == 3:
+        return ChannelK(w, torch, K)
+    if idx == 4:
+        return Cocktail(w, torch, K)
+    return Oaken(w, torch, K)
+
+
+WORKLOAD_TEXT = {
+    1: "tiny: batch 1, 1 KV head, head_dim 128, 1024 tokens N(0,1) with channels 7 and 93 x20; "
+       "INT4 asymmetric groups of 64 along head_dim; step = quantize 1024 tokens + 1 decode query",
+    2: "llama2-7b-layer-int8: batch 16, 32 MHA heads, head_dim 128, 4096 cached + 1 appended token, "
+       "N(0,1) with 4 outlier channels x15 per head; INT8 symmetric per token and head; "
+       "step = append 1 token per sequence + 1 decode query per head",
+    3: "llama3-8b-gqa-128k-int4: batch 1, 32 query / 8 KV heads, head_dim 128, 131072 tokens, "
+       "N(0,1) with 3 outlier channels x20 per head; INT4 asymmetric, K per channel over 64-token "
+       "blocks, V groups of 64; step = 1 split-sequence decode query per head",
+    4: "cocktail-13b-mixed: batch 8, 40 heads, head_dim 128, 32768 tokens in 32-token chunks classed "
+       "FP16/INT4/INT2 (groups of 32) by 768-d query-chunk cosine similarity (alpha 0.6, beta 0.1), "
+       "reordered by class; step = 1 chunked decode query per head",
+    5: "oaken-13b-threshold: batch 256, 40 heads, head_dim 128, 2048 tokens of 0.5*t(3); thresholds at "
+       "2.5/15/85/97.5 % of a 100-sequence calibration set; dense INT4 groups of 64 + sparse 6-bit "
+       "shifted outer values; step = append 1 token per sequence + 1 decode query per head",
+}
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle leg
+
+def oracle_slice(w, idx, b, h, thr=None):
+    """Oracle quantize + dequantize + attention of one (batch, kv head) slice.
+    Returns (quantize seconds, decode seconds, decode algorithmic bytes, input generation seconds)."""
     import numpy as np
     import oracle
+    tg = time.perf_counter()
+    G = w.q_heads // w.kv_heads
+    k = w.kv(0, b, b + 1, h, h + 1)[0, 0]
+    v = w.kv(1, b, b + 1, h, h + 1)[0, 0]
+    q = w.q(b, b + 1)[0, h * G:(h + 1) * G]
+    T = w.tokens
+    t0 = time.perf_counter()
+    if idx in (1, 2):
+        bits, sym, g = (4, False, 64) if idx == 1 else (8, True, 128)
+        kc, ks, kz = oracle.quant_rows(k, g, bits, sym)
+        vc, vs, vz = oracle.quant_rows(v, g, bits, sym)
+        t1 = time.perf_counter()
+        kh = oracle.dequant_rows(kc, ks, kz, g, sym)
+        vh = oracle.dequant_rows(vc, vs, vz, g, sym)
+        ng = 128 // g
+        nbytes = 2 * T * (128 * bits // 8 + ng * 4 + (0 if sym else ng))
+    elif idx == 3:
+        kc, ks, kz = oracle.quant_channel_blocks(k, 64, 4)
+        vc, vs, vz = oracle.quant_rows(v, 64, 4)
+        t1 = time.perf_counter()
+        kh = oracle.dequant_channel_blocks(kc, ks, kz, 64)
+        vh = oracle.dequant_rows(vc, vs, vz, 64)
+        nbytes = T * 64 + (T // 64) * 128 * 5 + T * 74
+    elif idx == 4:
+        CT = w.chunk_tokens
+        bits_c, _ = oracle.chunk_bits(*w.chunk_embeddings(b))
+        perm, seg = oracle.reorder(bits_c[None])
+        kh = np.zeros((T, 128), np.float32)
+        vh = np.zeros((T, 128), np.float32)
+        nbytes = 0
+        for x, xh in ((k, kh), (v, vh)):
+            for c in perm[0]:
+                rows = x[c * CT:(c + 1) * CT]
+                if bits_c[c] == 16:
+                    xh[c * CT:(c + 1) * CT] = rows.view(np.float16).astype(np.float32)
+                    nbytes += CT * 256
+                else:
+                    nb = 4 if bits_c[c] == 4 else 2
+                    oc, os_, oz = oracle.quant_rows(rows, 32, nb)
+                    xh[c * CT:(c + 1) * CT] = oracle.dequant_rows(oc, os_, oz, 32)
+                    nbytes += CT * (128 * nb // 8 + 4 * 5)
+        t1 = time.perf_counter()
+    else:
+        res = []
+        for x, tt in ((k, thr[0]), (v, thr[1])):
+            res.append(oracle.oaken_rows(x, tt, 64))
+        t1 = time.perf_counter()
+        kh = oracle.oaken_dequant_rows(*res[0], thr[0], 64)
+        vh = oracle.oaken_dequant_rows(*res[1], thr[1], 64)
+        nbytes = 2 * (T * (64 + 18) + (T + 1) * 4) + 2 * int(res[0][5].sum() + res[1][5].sum())
+    oracle.attention(q, kh[None], vh[None], SM_SCALE)
+    t2 = time.perf_counter()
+    nbytes += G * 128 * (2 + 4)
+    return t1 - t0, t2 - t1, nbytes, t0 - tg
 
-    t_quant = t_dec = 0.0
-    slices = 0
-    qall = w.q()
-    L = w.seq
-    sm = 1.0 / np.sqrt(128.0)
-    start = time.perf_counter()
-    for b in range(w.batch):
-        for h in range(w.kv_heads):
-            k = w.kv(0, b, b + 1, h, h + 1)
-            v = w.kv(1, b, b + 1, h, h + 1)
-            t0 = time.perf_counter()
-            kc, ks, _ = oracle.quant_rows(k, 128, 8, True)
-            vc, vs, _ = oracle.quant_rows(v, 128, 8, True)
-            t1 = time.perf_counter()
-            kh = oracle.dequant_rows(kc, ks, None, 128, True)[0]
-            vh = oracle.dequant_rows(vc, vs, None, 128, True)[0]
-            oracle.attention(qall[b, h:h + 1], kh, vh, sm)
-            t2 = time.perf_counter()
-            t_quant += t1 - t0
-            t_dec += t2 - t1
-            slices += 1
-            if time.perf_counter() - start > budget_s:
-                break
-        else:
-            continue
-        break
-    dec_bytes = slices * 2 * L * (128 + 4) + slices * (128 * 2 + 128 * 4)
-    log(args, "cpu oracle: %d slices, quant %.2fs, decode %.2fs" % (slices, t_quant, t_dec))
+
+def _oracle_job(idx, b, h, thr):
+    import synth
+    return oracle_slice(synth.WORKLOADS[idx], idx, b, h, thr=thr)
+
+
+def cpu_baseline(w, idx, budget_s):
+    """The oracle on (batch, kv head) slices: half the budget on one thread, half on worker
+    processes (one per available core, at most 16).  Runs before the GPU is initialised."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor, wait, FIRST_COMPLETED
+
+    import numpy as np
+    import oracle
+    thr = None
+    cal_note = ""
+    if idx == 5:
+        # thresholds from a reduced calibration set (offline stage, not timed)
+        thr = []
+        for tensor in (0, 1):
+            hist = np.zeros(65536, np.uint64)
+            for s in range(2):
+                oracle.hist_f16(w.calibration(tensor, s), hist)
+            thr.append(oracle.thresholds_from_hist(hist))
+        cal_note = "; thresholds from 2 of the 100 calibration sequences"
+    slices = [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
+    rng = np.random.default_rng(0)
+    order = [slices[i] for i in rng.permutation(len(slices))]
+    # single thread
+    tq = td = 0.0
+    nb = n1 = 0
+    t_start = time.perf_counter()
+    while n1 < len(order) and time.perf_counter() - t_start < budget_s / 2:
+        a, d, n, _ = oracle_slice(w, idx, *order[n1], thr=thr)
+        tq, td, nb, n1 = tq + a, td + d, nb + n, n1 + 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    workers = max(1, min(avail, 16))
+    # all cores: worker processes take slices until half the budget has passed
+    done = []
+    with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn")) as ex:
+        ex.submit(int, 0).result()  # pay the interpreter start-up before the clock starts
+        list(ex.map(int, range(workers)))
+        t0 = time.perf_counter()
+        pending = set()
+        nxt = 0
+        while nxt < len(order) and len(pending) < 2 * workers:
+            pending.add(ex.submit(_oracle_job, idx, *order[nxt], thr))
+            nxt += 1
+        while pending:
+            fin, pending = wait(pending, return_when=FIRST_COMPLETED)
+            done.extend(f.result() for f in fin)
+            if time.perf_counter() - t0 < budget_s / 2:
+                while nxt < len(order) and len(pending) < 2 * workers:
+                    pending.add(ex.submit(_oracle_job, idx, *order[nxt], thr))
+                    nxt += 1
+        wall = time.perf_counter() - t0
+    tq_m = sum(r[0] for r in done)
+    td_m = sum(r[1] for r in done)
+    nb_m = sum(r[2] for r in done)
+    tg_m = sum(r[3] for r in done)
+    # the wall time is split between input generation, quantize and attention in proportion to
+    # their summed per-slice times; generation is not part of the oracle's rate
+    wall_dec = wall * td_m / (tq_m + td_m + tg_m)
+    wall_q = wall * tq_m / (tq_m + td_m + tg_m)
     return {
-        "value": dec_bytes / t_dec / 1e9,
+        "value": round(nb_m / wall_dec / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": "%d of %d (batch, kv-head) slices, %d tokens each: INT8 quantize + dequant + "
-                  "binary64 attention, single thread" % (slices, w.batch * w.kv_heads, L),
-        "quant_tokens_per_s": slices * L / w.kv_heads / t_quant,
+        "sample": "%d of %d (batch, kv-head) slices of %d tokens on %d worker processes, %d slices on "
+                  "one thread: oracle quantize + dequantize + binary64 attention%s" % (
+                      len(done), len(slices), w.tokens, workers, n1, cal_note),
+        "single_thread_value": round(nb / td / 1e9, 4),
+        "quant_tokens_per_s": round(len(done) * w.tokens / w.kv_heads / wall_q, 1),
+        "single_thread_quant_tokens_per_s": round(n1 * w.tokens / w.kv_heads / tq, 1),
     }
 
 
+# ---------------------------------------------------------------------------
+# stored HBM counters of the decode kernel (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "quantized_kv_cache_05_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(idx):
+    """HBM bytes per decode launch from profiles/decode_traffic_w<idx>.txt, if it was taken on the
+    current kernel sources; None otherwise."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic_w%d.txt" % idx)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != source_hash():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+
 def main():
-    args = parse()
+    global ARGS
+    ARGS = args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only (--gpus 1); multi-GPU runs are not part of this build",
-              file=sys.stderr)
+        print("bench.py measures one GPU (--gpus 1); runs on several GPUs are not part of this "
+              "library's scope", file=sys.stderr)
         sys.exit(2)
     import numpy as np
-    import torch
 
     import synth
+
+    cpu = None
+    if not args.no_cpu:
+        t = time.perf_counter()
+        cpu = cpu_baseline(synth.WORKLOADS[args.workload], args.workload, args.cpu_seconds)
+        log("cpu oracle leg %.1fs: %s" % (time.perf_counter() - t, cpu))
+
+    import torch
+
     import quantized_kv_cache_05_amd as K
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from kvq_harness import i32_device, to_device
 
     torch.cuda.set_device(0)
-    w = synth.WORKLOADS[2]
-    B, H, Hq, L = w.batch, w.kv_heads, w.q_heads, w.seq  # L = 4097
-    T0 = L - 1
-    S = (L + 63) // 64 * 64
-    log(args, "generating inputs ...")
-    t = time.perf_counter()
-    k = w.kv(0)
-    v = w.kv(1)
-    q = w.q()
-    log(args, "inputs ready in %.1fs" % (time.perf_counter() - t))
-    k_bulk = to_device(np.ascontiguousarray(k[:, :, :T0]))
-    v_bulk = to_device(np.ascontiguousarray(v[:, :, :T0]))
-    k_new = to_device(np.ascontiguousarray(k[:, :, T0:]))
-    v_new = to_device(np.ascontiguousarray(v[:, :, T0:]))
-    q_dev = to_device(q)
-    del k, v
-    cache = K.QuantKVCache(B, H, S, K.KVQ_MODE_UNIFORM, k_bits=8, symmetric=True, k_group=128)
-    pos0 = i32_device([0] * B)
-    pos_app = i32_device([T0] * B)
-    seq_len = i32_device([L] * B)
-    out = torch.empty(B, Hq, 128, dtype=torch.float32, device="cuda")
-    ws, ws_bytes = cache.workspace(Hq, L, args.num_splits)
-    sm = 1.0 / np.sqrt(128.0)
     stream = torch.cuda.current_stream()
+    idx = args.workload
+    t = time.perf_counter()
+    wl = build_workload(idx, torch, K, synth)
+    torch.cuda.synchronize()
+    log("workload %d set up in %.1fs (%d cache cop%s)" % (idx, time.perf_counter() - t, wl.rotate,
+                                                        "y" if wl.rotate == 1 else "ies"))
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
@@ -154,56 +566,59 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # bulk prefill quantize (also fills the cache)
-    for _ in range(2):
-        K.kvq_quant_append(cache.desc, k_bulk, v_bulk, T0, pos0)
+    # bulk prefill (quantize-append of the whole prompt); fills every cache copy
+    for r in range(wl.rotate):
+        wl.prefill(r)
     torch.cuda.synchronize()
-    reps = 10
+    reps = 5
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(reps):
-        K.kvq_quant_append(cache.desc, k_bulk, v_bulk, T0, pos0)
+    for i in range(reps):
+        wl.prefill(i % wl.rotate)
     e1.record(stream)
     torch.cuda.synchronize()
     bulk_ms = e0.elapsed_time(e1) / reps
-    bulk_tok_s = B * T0 / (bulk_ms / 1e3)
-    log(args, "bulk quantize %d x %d tokens: %.3f ms, %.3e tok/s" % (B, T0, bulk_ms, bulk_tok_s))
+    bulk_tok_s = wl.prefill_tokens / (bulk_ms / 1e3)
+    log("prefill quantize %d tokens: %.3f ms, %.3e tok/s" % (wl.prefill_tokens, bulk_ms, bulk_tok_s))
 
-    def step(ev_a=None, ev_b=None):
-        K.kvq_quant_append(cache.desc, k_new, v_new, 1, pos_app)
+    def step(i, ev_a=None, ev_b=None):
+        r = i % wl.rotate
+        wl.append(r)
         if ev_a is not None:
             ev_a.record(stream)
-        K.kvq_decode_attn(cache.desc, q_dev, Hq, seq_len, L, sm, out, ws, ws_bytes, args.num_splits)
+        wl.decode(r)
         if ev_b is not None:
             ev_b.record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
-    assert cache.flags() == 0, "device status flags %#x" % cache.flags()
+    flags = wl.flags()
+    assert not any(flags), "device status flags %s" % flags
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     s0.record(stream)
-    for a, b in evs:
-        step(a, b)
+    for i, (a, b) in enumerate(evs):
+        step(i, a, b)
     s1.record(stream)
     torch.cuda.synchronize()
     step_ms = s0.elapsed_time(s1) / args.steps
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    dbytes = decode_bytes(B, H, Hq, L)
-    abytes = append_bytes(B, H, 1)
+    dec_times = [a.elapsed_time(b) for a, b in evs]
+    dec_ms = float(np.mean(dec_times))
+    dbytes = wl.decode_bytes()
+    abytes = wl.append_bytes()
     value = (dbytes + abytes) / (step_ms / 1e3) / 1e9
     achieved = dbytes / (dec_ms / 1e3) / 1e9
-    append_tok_s = B / ((step_ms - dec_ms) / 1e3) if step_ms > dec_ms else None
-    log(args, "step %.4f ms, decode %.4f ms -> %.1f GB/s (%.1f%% of peak)"
-        % (step_ms, dec_ms, achieved, 100 * achieved / HBM_PEAK_GBS))
+    app_ms = step_ms - dec_ms
+    w = wl.w
+    app_tokens = w.batch * (1 if idx != 1 else w.tokens)
+    append_tok_s = app_tokens / (app_ms / 1e3) if (idx in (1, 2, 5) and app_ms > 0) else None
+    log("step %.4f ms, decode %.4f ms (median %.4f) -> %.1f GB/s (%.1f%% of peak)"
+        % (step_ms, dec_ms, float(np.median(dec_times)), achieved, 100 * achieved / HBM_PEAK_GBS))
 
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(w, args.cpu_seconds, args)
-
+    traffic = stored_traffic(idx)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -218,16 +633,16 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "llama2-7b-layer-int8: batch 16, 32 MHA heads, head_dim 128, 4096 cached + 1 "
-                        "appended token, INT8 symmetric per token and head; step = append 1 token per "
-                        "sequence + 1 decode query per head",
-            "batch": B, "kv_heads": H, "q_heads": Hq, "seq_len": L, "num_splits": args.num_splits,
+            "workload": WORKLOAD_TEXT[idx],
+            "batch": w.batch, "kv_heads": w.kv_heads, "q_heads": w.q_heads, "seq_len": w.tokens,
+            "num_splits": args.num_splits, "cache_copies": wl.rotate,
         },
         "decode_ms": round(dec_ms, 5),
+        "decode_bytes": int(dbytes),
         "decode_gbs": round(achieved, 1),
         "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
-        "quant_bulk_tokens_per_s": round(bulk_tok_s, 1),
-        "quant_bulk_ms": round(bulk_ms, 4),
+        "quant_prefill_tokens_per_s": round(bulk_tok_s, 1),
+        "quant_prefill_ms": round(bulk_ms, 4),
         "quant_append_tokens_per_s": round(append_tok_s, 1) if append_tok_s else None,
         "roofline": {
             "bound": "hbm",
@@ -235,7 +650,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
         },
         "cpu_baseline": cpu,
     }

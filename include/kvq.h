@@ -223,6 +223,48 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t q_heads,
                            void* workspace, size_t workspace_bytes, int32_t num_splits,
                            void* stream);
 
+/*
+ * [Cocktail] §3.1.1 chunk precision search: for every sequence b, the
+ * cosine similarity sim_i = q.c_i / (|q| |c_i|) of its query embedding with
+ * each chunk embedding, T_low = s_min + (s_max - s_min) * alpha,
+ * T_high = s_max - (s_max - s_min) * beta, and bits_i = 16 if sim_i > T_high,
+ * 4 if T_low < sim_i <= T_high, else 2 (the page recommends alpha = 0.6,
+ * beta = 0.1, §4.3.2).  Every similarity is a sequential binary64 sum over
+ * d = 0 .. dim-1 with one rounding per operation, so results are
+ * reproducible bit for bit by any such evaluation.
+ *  q_emb:     device double [batch][dim], 8-byte aligned.
+ *  chunk_emb: device double [batch][n_chunks][dim], 8-byte aligned.
+ *  sims:      optional device double [batch][n_chunks] (NULL: not written).
+ *  bits:      device uint8 [batch][n_chunks], the input of kvq_reorder_chunks.
+ * alpha and beta must lie in [0, 1]; batch <= 65535.
+ */
+kvq_status kvq_chunk_bits(const double* q_emb, const double* chunk_emb, int32_t batch,
+                          int32_t n_chunks, int32_t dim, double alpha, double beta, double* sims,
+                          uint8_t* bits, void* stream);
+
+/*
+ * [Oaken] §3.1 offline stage, the distribution of sampled K or V values:
+ * adds, for each of the n fp16 values of x, one count to hist[key], where
+ * key orders fp16 bit patterns by value (h | 0x8000 for a positive sign
+ * bit, 0xFFFF - h for a negative one, so -0 sorts just below +0).
+ *  x:    device fp16 [n], 16-byte aligned; n <= 2^40.
+ *  hist: device uint64 [65536], 8-byte aligned, accumulated into (the
+ *        caller zeroes it before the first call of a calibration).
+ */
+kvq_status kvq_hist_f16(const void* x, int64_t n, uint64_t* hist, void* stream);
+
+/*
+ * Nearest-rank percentiles of a kvq_hist_f16 histogram of N values: for
+ * each p_bp[i] (basis points, 0 .. 10000; e.g. 250 = 2.5 %), the value of
+ * rank max(1, ceil(p * N / 10000)) in ascending order, as float.  These are
+ * the Oaken thresholds (T_lo_outer, T_lo_inner, T_hi_inner, T_hi_outer at
+ * 250, 1500, 8500, 9750 for the 5 % / 25 % / 70 % regions of §3.2.1).
+ *  p_bp: host int32 [count], count <= 8.   out: device float [count]
+ *  (NaN when the histogram is empty).
+ */
+kvq_status kvq_hist_percentiles(const uint64_t* hist, int32_t count, const int32_t* p_bp, float* out,
+                                void* stream);
+
 /* Static string naming a kvq_status value. */
 const char* kvq_status_string(int32_t status);
 

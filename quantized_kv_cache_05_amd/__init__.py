@@ -75,7 +75,8 @@ class KVQError(RuntimeError):
 _lib = None
 
 EXPORTS = ("kvq_cache_bytes", "kvq_quant_append", "kvq_reorder_chunks", "kvq_decode_workspace_bytes",
-           "kvq_decode_attn", "kvq_status_string")
+           "kvq_decode_attn", "kvq_chunk_bits", "kvq_hist_f16", "kvq_hist_percentiles",
+           "kvq_status_string")
 
 
 def lib():
@@ -91,9 +92,15 @@ def lib():
         L.kvq_reorder_chunks.argtypes = [P(kvq_cache), _vp, _i32, _vp]
         L.kvq_decode_workspace_bytes.argtypes = [P(kvq_cache), _i32, _i32, _i32, P(_sz)]
         L.kvq_decode_attn.argtypes = [P(kvq_cache), _vp, _i32, _vp, _i32, _f32, _vp, _vp, _sz, _i32, _vp]
+        L.kvq_chunk_bits.argtypes = [_vp, _vp, _i32, _i32, _i32, ctypes.c_double, ctypes.c_double, _vp,
+                                     _vp, _vp]
+        L.kvq_hist_f16.argtypes = [_vp, _i64, _vp, _vp]
+        L.kvq_hist_percentiles.argtypes = [_vp, _i32, _vp, _vp, _vp]
         L.kvq_status_string.argtypes = [_i32]
         L.kvq_status_string.restype = ctypes.c_char_p
-        for n in EXPORTS[:-1]:
+        for n in EXPORTS:
+            if n == "kvq_status_string":
+                continue
             getattr(L, n).restype = _i32
         _lib = L
     return _lib
@@ -156,6 +163,30 @@ def kvq_decode_attn(cache: kvq_cache, q, q_heads: int, seq_len, max_len: int, sm
                                         int(max_len), float(sm_scale), _ptr(out), _ptr(workspace),
                                         int(workspace_bytes), int(num_splits), _stream(stream)),
                   "kvq_decode_attn")
+
+
+def kvq_chunk_bits(q_emb, chunk_emb, batch: int, n_chunks: int, dim: int, alpha: float, beta: float,
+                   bits, sims=None, stream=None) -> int:
+    return _check(lib().kvq_chunk_bits(_ptr(q_emb), _ptr(chunk_emb), int(batch), int(n_chunks), int(dim),
+                                       float(alpha), float(beta), _ptr(sims), _ptr(bits), _stream(stream)),
+                  "kvq_chunk_bits")
+
+
+def kvq_hist_f16(x, n: int, hist, stream=None) -> int:
+    return _check(lib().kvq_hist_f16(_ptr(x), int(n), _ptr(hist), _stream(stream)), "kvq_hist_f16")
+
+
+def kvq_hist_percentiles(hist, p_bp, out, stream=None) -> int:
+    arr = (_i32 * len(p_bp))(*[int(p) for p in p_bp])
+    return _check(lib().kvq_hist_percentiles(_ptr(hist), len(p_bp), arr, _ptr(out), _stream(stream)),
+                  "kvq_hist_percentiles")
+
+
+# Oaken threshold percentiles in basis points: T_lo_outer, T_lo_inner, T_hi_inner, T_hi_outer.
+OAKEN_PERCENTILES_BP = (250, 1500, 8500, 9750)
+# Cocktail similarity thresholds recommended by the page (alpha for T_low, beta for T_high).
+COCKTAIL_ALPHA = 0.6
+COCKTAIL_BETA = 0.1
 
 
 from .cache import QuantKVCache  # noqa: E402  (allocation helper over the binding)

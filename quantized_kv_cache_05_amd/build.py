@@ -16,6 +16,7 @@ SOURCES = [
     "kvq_api.cpp",
     "kvq_quant.hip",
     "kvq_reorder.hip",
+    "kvq_prep.hip",
     "kvq_decode_uniform.hip",
     "kvq_decode_oaken.hip",
     "kvq_decode_mixed.hip",

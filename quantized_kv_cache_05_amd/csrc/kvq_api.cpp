@@ -353,6 +353,46 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t q_heads, c
   return from_hip(e);
 }
 
+kvq_status kvq_chunk_bits(const double* q_emb, const double* chunk_emb, int32_t batch,
+                          int32_t n_chunks, int32_t dim, double alpha, double beta, double* sims,
+                          uint8_t* bits, void* stream) {
+  if (batch < 0 || n_chunks < 0 || dim < 1) return KVQ_ERR_INVALID_ARG;
+  if (!(alpha >= 0.0 && alpha <= 1.0 && beta >= 0.0 && beta <= 1.0)) return KVQ_ERR_INVALID_ARG;
+  if (batch == 0 || n_chunks == 0) return KVQ_OK;
+  if (batch > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (!q_emb || !chunk_emb || !bits) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(q_emb, 8) || !aligned(chunk_emb, 8) || (sims && !aligned(sims, 8)))
+    return KVQ_ERR_ALIGNMENT;
+  return from_hip(kvq::launch_chunk_bits(q_emb, chunk_emb, batch, n_chunks, dim, alpha, beta, sims,
+                                         bits, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_hist_f16(const void* x, int64_t n, uint64_t* hist, void* stream) {
+  if (n < 0 || n > (int64_t(1) << 40)) return KVQ_ERR_INVALID_ARG;
+  if (n == 0) return KVQ_OK;
+  if (!x || !hist) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(hist, 8)) return KVQ_ERR_ALIGNMENT;
+  return from_hip(kvq::launch_hist_f16(static_cast<const uint16_t*>(x), (long long)n,
+                                       reinterpret_cast<unsigned long long*>(hist),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_hist_percentiles(const uint64_t* hist, int32_t count, const int32_t* p_bp, float* out,
+                                void* stream) {
+  if (count < 0 || count > kvq::kMaxPercentiles) return KVQ_ERR_INVALID_ARG;
+  if (count == 0) return KVQ_OK;
+  if (!hist || !p_bp || !out) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(hist, 8) || !aligned(out, 4)) return KVQ_ERR_ALIGNMENT;
+  kvq::PercentileList pl{};
+  pl.count = count;
+  for (int i = 0; i < count; ++i) {
+    if (p_bp[i] < 0 || p_bp[i] > 10000) return KVQ_ERR_INVALID_ARG;
+    pl.p_bp[i] = p_bp[i];
+  }
+  return from_hip(kvq::launch_percentiles(reinterpret_cast<const unsigned long long*>(hist), pl, out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 const char* kvq_status_string(int32_t status) {
   switch (status) {
     case KVQ_OK: return "ok";

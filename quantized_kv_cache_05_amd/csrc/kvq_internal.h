@@ -65,6 +65,18 @@ hipError_t launch_quant_oaken(const CacheArgs& c, const TensorArgs& t, const uin
                               const int* pos, hipStream_t st);
 hipError_t launch_reorder(const CacheArgs& c, const uint8_t* bits, int n_chunks, hipStream_t st);
 
+// Cocktail chunk precision search and Oaken calibration histogram.
+constexpr int kMaxPercentiles = 8;
+struct PercentileList {
+  int count;
+  int p_bp[kMaxPercentiles];  // basis points, 0..10000
+};
+hipError_t launch_chunk_bits(const double* q_emb, const double* c_emb, int batch, int n, int dim,
+                             double alpha, double beta, double* sims, uint8_t* bits, hipStream_t st);
+hipError_t launch_hist_f16(const uint16_t* x, long long n, unsigned long long* hist, hipStream_t st);
+hipError_t launch_percentiles(const unsigned long long* hist, const PercentileList& pl, float* out,
+                              hipStream_t st);
+
 // Returns hipErrorInvalidValue for a combination without a compiled kernel.
 hipError_t launch_decode_uniform(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
 hipError_t launch_decode_oaken(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);

@@ -181,3 +181,54 @@ def test_unpacker_hand_examples():
     for bits in (2, 4, 8):
         codes = rng.integers(0, 1 << bits, size=(5, 128)).astype(np.uint8)
         assert np.array_equal(unpack_codes(pack_codes(codes, bits), bits), codes)
+
+
+def test_prep_entry_points_validate_before_launch():
+    # chunk precision search
+    assert status_of(K.kvq_chunk_bits, 8, 8, -1, 4, 16, 0.6, 0.1, 16) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_chunk_bits, 8, 8, 1, 4, 0, 0.6, 0.1, 16) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_chunk_bits, 8, 8, 1, 4, 16, 1.5, 0.1, 16) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_chunk_bits, 8, 8, 1, 4, 16, 0.6, float("nan"), 16) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_chunk_bits, 8, 8, 0, 4, 16, 0.6, 0.1, 16) == K.KVQ_OK  # nothing to do
+    assert status_of(K.kvq_chunk_bits, None, 8, 1, 4, 16, 0.6, 0.1, 16) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_chunk_bits, 8, 12, 1, 4, 16, 0.6, 0.1, 16) == K.KVQ_ERR_ALIGNMENT
+    assert status_of(K.kvq_chunk_bits, 8, 8, 70000, 4, 16, 0.6, 0.1, 16) == K.KVQ_ERR_UNSUPPORTED
+    # calibration histogram and percentiles
+    assert status_of(K.kvq_hist_f16, 16, -1, 16) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_hist_f16, 16, 0, 16) == K.KVQ_OK
+    assert status_of(K.kvq_hist_f16, None, 5, 16) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_hist_f16, 8, 5, 16) == K.KVQ_ERR_ALIGNMENT
+    assert status_of(K.kvq_hist_f16, 16, 5, 12) == K.KVQ_ERR_ALIGNMENT
+    assert status_of(K.kvq_hist_percentiles, 16, [250] * 9, 16) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_hist_percentiles, 16, [10001], 16) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_hist_percentiles, 16, [-1], 16) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_hist_percentiles, 16, [], 16) == K.KVQ_OK
+    assert status_of(K.kvq_hist_percentiles, None, [250], 16) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_hist_percentiles, 12, [250], 16) == K.KVQ_ERR_ALIGNMENT
+
+
+def test_cache_bytes_reproduce_page_arithmetic():
+    """Byte accounting against the pages' worked numbers.
+
+    The engineering page's cache formula is 2 * layers * kv_heads * head_dim *
+    seq * batch * bytes; the TurboQuant page (§1.2) evaluates it for an 8B
+    model (32 layers, 32 heads, head_dim 128) at 131072 tokens: 34,359,738,368
+    elements, about 68.7 GB in fp16.  An INT4 cache with 64-wide groups stores
+    half a byte per element plus 5 bytes of scale and zero-point per group,
+    and an INT8 symmetric one a byte per element plus 4 bytes per token row.
+    """
+    layers, H, D, S, B = 32, 32, 128, 131072, 1
+    elements = 2 * layers * H * D * S * B
+    assert elements == 34_359_738_368
+    assert abs(elements * 2 / 1e9 - 68.7) < 0.05
+    c = make_desc(B=B, H=H, S=S, bits=4, group=64)
+    b = K.kvq_cache_bytes(c)
+    per_layer = sum(getattr(t, f) for t in (b.k, b.v) for f in K.TENSOR_BUFFERS)
+    assert per_layer * layers == elements // 2 + (elements // 64) * 5
+    c8 = make_desc(B=B, H=H, S=S, bits=8, sym=1, group=128)
+    b8 = K.kvq_cache_bytes(c8)
+    per_layer8 = sum(getattr(t, f) for t in (b8.k, b8.v) for f in K.TENSOR_BUFFERS)
+    assert per_layer8 * layers == elements + (elements // 128) * 4
+    # KVO-LLM page: 2 x 4096 hidden x 4 bytes = 32 KB per token and layer in fp32; the
+    # fp16 cache of the same model (32 heads of 128) is half of it per token
+    assert 2 * 32 * 128 * 2 == 32 * 1024 // 2
