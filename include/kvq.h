@@ -84,9 +84,7 @@ enum {
  * Buffers by mode (B = batch, H = kv_heads, S = max_seq, D = 128,
  * RB = D * bits / 8 bytes per token row, NG = D / group):
  *  UNIFORM, TOKEN axis:
- *    codes  [B][H][S][RB]  packed little-endian: for bits 8 one (u)int8 per
- *                          channel; bits 4: channel 2i in the low nibble of
- *                          byte i; bits 2: channel 4i + j in bits 2j..2j+1.
+ *    codes  [B][H][S][RB]  one packed row per token (row layouts below)
  *    scale  [B][H][S][NG]  float
  *    zero   [B][H][S][NG]  uint8 (unused and may be NULL when symmetric)
  *  UNIFORM, CHANNEL axis (K only, group == 64 tokens; asymmetric):
@@ -107,6 +105,18 @@ enum {
  *    codes16 [B][H][C][chunk_tokens][D] fp16, the FP16 chunks
  *    codes/scale/zero   INT4 pool, TOKEN-axis layout with C*chunk_tokens rows
  *    codes2/scale2/zero2 INT2 pool, same layout
+ *
+ * Packed rows.  A row holds the 128 codes of one token in 16 words of 8
+ * codes (a word is 8 * bits / 8 bytes; inside a word, code e sits at bits
+ * e*bits .. e*bits + bits - 1 counted from the least significant bit of the
+ * little-endian word; 8-bit symmetric codes are two's complement).  The
+ * channel order differs between K and V so that the decode kernel can feed
+ * rows straight into the matrix cores:
+ *    K rows: word 4 q + s holds channels 32 s + 8 q + e    (q, s in 0..3)
+ *    V rows: word n holds channels n + 16 e                (n in 0..15)
+ * fp16 rows of the CHUNK_MIXED FP16 pool use the same word positions (16-byte
+ * words); inside a K word the 8 halves hold channel offsets
+ * 0, 4, 1, 5, 2, 6, 3, 7, inside a V word channels n + 16 e in order e.
  */
 typedef struct kvq_tensor {
   int32_t bits;       /* UNIFORM: 8, 4 or 2.  OAKEN: 4.  CHUNK_MIXED: ignored */
@@ -195,6 +205,11 @@ kvq_status kvq_reorder_chunks(const kvq_cache* c, const uint8_t* chunk_bits, int
 /*
  * Workspace needed by kvq_decode_attn for the same (c, q_heads, max_len,
  * num_splits); 0 when the chosen split count is 1.  Host only.
+ * The workspace holds the split partials followed by one uint32 arrival
+ * counter per (batch, kv head, query tile).  The counters must be zero when
+ * a call is enqueued; every completed call leaves them zero again, so
+ * zero-fill a workspace once after allocating it.  One workspace serves one
+ * call at a time (calls on different streams need their own).
  */
 kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32_t max_len,
                                       int32_t num_splits, size_t* bytes);
@@ -205,7 +220,8 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32
  * dequantization inside the attention product, no separate pass).  The
  * sequence is split across workgroups and the partial results are merged
  * with the log-sum-exp rule ([Cocktail] §3.2.3: per-block attention whose
- * merge equals ordinary attention).
+ * merge equals ordinary attention) by the last workgroup of each
+ * (batch, kv head, query tile) to finish, inside the same kernel launch.
  *  q:        device fp16 [batch][q_heads][128]; q_heads a multiple of
  *            kv_heads; query head h reads KV head h / (q_heads / kv_heads).
  *  seq_len:  device int32 [batch], tokens 0 .. seq_len[b]-1 are attended

@@ -174,15 +174,15 @@ kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HI
 constexpr long long kTargetGroups = 2048;
 
 struct Plan {
-  int G, gtile, qtiles, num_splits, split_len;
+  int G, qr, qtiles, num_splits, split_len;
 };
 
 kvq_status plan_decode(const kvq_cache* c, int q_heads, int max_len, int num_splits, Plan* p) {
   if (q_heads < 1 || q_heads % c->kv_heads) return KVQ_ERR_INVALID_ARG;
   if (num_splits < 0) return KVQ_ERR_INVALID_ARG;
   p->G = q_heads / c->kv_heads;
-  p->gtile = p->G == 1 ? 1 : 4;
-  p->qtiles = (p->G + p->gtile - 1) / p->gtile;
+  p->qr = p->G == 1 ? 1 : (p->G <= 4 ? 4 : kvq::kMaxQR);
+  p->qtiles = (p->G + p->qr - 1) / p->qr;
   const long long units = (long long)c->batch * c->kv_heads * p->qtiles;
   long long length, min_piece, align;
   if (c->mode == KVQ_MODE_CHUNK_MIXED) {
@@ -218,9 +218,15 @@ kvq_status plan_decode(const kvq_cache* c, int q_heads, int max_len, int num_spl
   return KVQ_OK;
 }
 
+// Split partials, then the arrival counters (256-byte aligned).
+size_t partials_bytes(const kvq_cache* c, int q_heads, const Plan& p) {
+  const size_t n = (size_t)c->batch * (size_t)q_heads * (size_t)p.num_splits * kvq::kPartStride * 4;
+  return (n + 255) / 256 * 256;
+}
+
 size_t workspace_for(const kvq_cache* c, int q_heads, const Plan& p) {
   if (p.num_splits <= 1) return 0;
-  return (size_t)c->batch * (size_t)q_heads * (size_t)p.num_splits * kvq::kPartStride * sizeof(float);
+  return partials_bytes(c, q_heads, p) + (size_t)c->batch * c->kv_heads * p.qtiles * 4;
 }
 
 }  // namespace
@@ -265,18 +271,18 @@ kvq_status kvq_quant_append(const kvq_cache* c, const void* k_new, const void* v
         if (t_new % 64) return KVQ_ERR_INVALID_ARG;
         e = kvq::launch_quant_channel(a, a.k, kx, t_new, pos, st);
       } else {
-        e = kvq::launch_quant_token(a, a.k, kx, t_new, pos, st);
+        e = kvq::launch_quant_token(a, a.k, false, kx, t_new, pos, st);
       }
-      if (e == hipSuccess) e = kvq::launch_quant_token(a, a.v, vx, t_new, pos, st);
+      if (e == hipSuccess) e = kvq::launch_quant_token(a, a.v, true, vx, t_new, pos, st);
       break;
     case KVQ_MODE_OAKEN:
-      e = kvq::launch_quant_oaken(a, a.k, kx, t_new, pos, st);
-      if (e == hipSuccess) e = kvq::launch_quant_oaken(a, a.v, vx, t_new, pos, st);
+      e = kvq::launch_quant_oaken(a, a.k, false, kx, t_new, pos, st);
+      if (e == hipSuccess) e = kvq::launch_quant_oaken(a, a.v, true, vx, t_new, pos, st);
       break;
     case KVQ_MODE_CHUNK_MIXED:
       if (t_new != c->max_seq) return KVQ_ERR_INVALID_ARG;
-      e = kvq::launch_quant_mixed(a, a.k, kx, pos, st);
-      if (e == hipSuccess) e = kvq::launch_quant_mixed(a, a.v, vx, pos, st);
+      e = kvq::launch_quant_mixed(a, a.k, false, kx, pos, st);
+      if (e == hipSuccess) e = kvq::launch_quant_mixed(a, a.v, true, vx, pos, st);
       break;
   }
   return from_hip(e);
@@ -331,7 +337,7 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t q_heads, c
   d.q = static_cast<const uint16_t*>(q);
   d.Hq = q_heads;
   d.G = p.G;
-  d.gtile = p.gtile;
+  d.qr = p.qr;
   d.qtiles = p.qtiles;
   d.seq_len = seq_len;
   d.max_len = c->mode == KVQ_MODE_CHUNK_MIXED ? c->max_seq : max_len;
@@ -340,6 +346,9 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t q_heads, c
   d.qscale = sm_scale * 1.4426950408889634f;
   d.out = out;
   d.ws = static_cast<float*>(need ? workspace : nullptr);
+  d.counters = need ? reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
+                                                   partials_bytes(c, q_heads, p))
+                    : nullptr;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (c->mode) {
@@ -348,8 +357,6 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t q_heads, c
     default: e = kvq::launch_decode_mixed(a, d, st); break;
   }
   if (e == hipErrorInvalidValue) return KVQ_ERR_UNSUPPORTED;
-  if (e != hipSuccess) return KVQ_ERR_HIP;
-  if (p.num_splits > 1) e = kvq::launch_merge(d, c->batch, st);
   return from_hip(e);
 }
 

@@ -1,0 +1,316 @@
+// Split-sequence decode attention on the matrix cores (gfx950, wave64), with
+// the dequantization fused into both products: the TurboQuant page (§2.3,
+// end) puts dequantization inside the attention product instead of a
+// separate pass; the Cocktail page (§3.2.3) computes attention per block and
+// merges the block results.
+//
+// A wave consumes tiles of 32 cached tokens.  For each tile:
+//   scores  S[m][t] = sum_d q[m][d] k_hat[t][d]   v_mfma_f32_16x16x32_f16,
+//           A = the query tile (16 rows: up to 16 query heads sharing this KV
+//           head), B = K codes (16 tokens per column block), 4 k-steps of 32
+//           channels, two column blocks per tile;
+//   output  O[m][c] += sum_t w[m][t] v_hat[t][c]  same instruction, A = the
+//           softmax weights (binary32 split into two fp16 halves, hi + lo),
+//           B = V codes, one k-step of 32 tokens, 8 column blocks of 16
+//           channels.
+// Codes enter the matrix cores as exact small fp16 integers OFF + c, built
+// with a magic-exponent OR (OFF = 16 for 4-bit, 4 for 2-bit, 256 / 384 for
+// 8-bit codes).  Group scales and zero-points stay in binary32 outside the
+// products: per token t and channel group g
+//   score = sum_g s[t][g] * (C_g[t] - (OFF + z[t][g]) * Q_g),  Q_g = sum_{d in g} q_d,
+//   O[c]  = sum_t (p_t s[t][g(c)]) (OFF + c_t) - sum_t p_t s[t][g(c)] (OFF + z[t][g(c)]),
+// which equals sum_t p_t s (c_t - z) exactly up to binary32 rounding.
+// The layouts of packed rows (kvq.h) are chosen for these operands: a
+// K row is 16 slots of 8 channels, slot 4q + s holding channels
+// 32 s + 8 q + v, so every k-step (32 channels) lies in one quantization
+// group; a V row is 16 column words, word n holding channels n + 16 j, so a
+// lane forms the B operand of column block j from its 8 token rows.
+//
+// Lane roles: l = lane, n16 = l & 15, q4 = l >> 4.
+//  K-MFMA  A: row n16 = query, k-slots of lane group q4;
+//          B: column n16 = token (nb*16 + n16), same k-slots;
+//          C: column n16 = token, rows 4*q4 + i = queries (i < 4).
+//  V-MFMA  A: row n16 = query, k-slots = tokens 8*q4 .. 8*q4+7 of the tile;
+//          B: column n16 = channel 16 j + n16, same token slots;
+//          C: column = channel 16 j + n16, rows 4*q4 + i = queries.
+// Softmax state (running max, sum, V bias) lives with the C rows: lane
+// (q4, n16) owns queries 4*q4 + i for its token column and its channels.
+#pragma once
+#include "kvq_dev.h"
+
+namespace kvq {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kNW = 4;    // waves per workgroup
+constexpr int kTile = 32; // tokens per tile
+
+__device__ __forceinline__ f4_t mfma(u4_t a, u4_t b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a),
+                                                __builtin_bit_cast(h8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ unsigned perm(unsigned hi, unsigned lo, unsigned sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// perm selector placing byte `a` of lo at bits 0-7 and byte `a` of hi at bits 16-23
+__host__ __device__ constexpr unsigned sel_bytes(int a) {
+  return (0x0Cu << 24) | ((4u + a) << 16) | (0x0Cu << 8) | (unsigned)a;
+}
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float f16lo(unsigned w) { return (float)__builtin_bit_cast(h2_t, w)[0]; }
+__device__ __forceinline__ float f16hi(unsigned w) { return (float)__builtin_bit_cast(h2_t, w)[1]; }
+
+// Two binary32 values -> (hi, lo) fp16 pairs with a + b == hi + lo to ~2^-22.
+__device__ __forceinline__ void split_pair(float a, float b, unsigned& hi, unsigned& lo) {
+  const h2_t h = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+  hi = __builtin_bit_cast(unsigned, h);
+  lo = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a - (float)h[0], b - (float)h[1]));
+}
+
+// ---------------------------------------------------------------------------
+// K codecs: load a token row's 4 slices for lane group q4, and form k-step s
+// as 4 fp16 pairs (channels v, v + 4 of the slice), value OFF + code.
+
+struct KI4 {
+  static constexpr int RB = 64, OFF = 16, BITS = 4;
+  static constexpr bool SYM = false, F16 = false;
+  u4_t r;
+  __device__ __forceinline__ void load(const uint8_t* row, int q4) {
+    r = *reinterpret_cast<const u4_t*>(row + q4 * 16);
+  }
+  __device__ __forceinline__ u4_t slice(int s) const {
+    const unsigned w = r[s];
+    u4_t o;
+    o[0] = ((w << 6) & 0x03C003C0u) | 0x4C004C00u;
+    o[1] = ((w << 2) & 0x03C003C0u) | 0x4C004C00u;
+    o[2] = ((w >> 2) & 0x03C003C0u) | 0x4C004C00u;
+    o[3] = ((w >> 6) & 0x03C003C0u) | 0x4C004C00u;
+    return o;
+  }
+};
+
+struct KI2 {
+  static constexpr int RB = 32, OFF = 4, BITS = 2;
+  static constexpr bool SYM = false, F16 = false;
+  u2_t r;
+  __device__ __forceinline__ void load(const uint8_t* row, int q4) {
+    r = *reinterpret_cast<const u2_t*>(row + q4 * 8);
+  }
+  __device__ __forceinline__ u4_t slice(int s) const {
+    const unsigned d = r[s >> 1];
+    // byte 0 of the slice (channels 0-3) to the low half, byte 1 (4-7) to the high half
+    const unsigned x = (s & 1) ? perm(0u, d, 0x0C030C02u) : perm(0u, d, 0x0C010C00u);
+    u4_t o;
+    o[0] = ((x << 8) & 0x03000300u) | 0x44004400u;
+    o[1] = ((x << 6) & 0x03000300u) | 0x44004400u;
+    o[2] = ((x << 4) & 0x03000300u) | 0x44004400u;
+    o[3] = ((x << 2) & 0x03000300u) | 0x44004400u;
+    return o;
+  }
+};
+
+template <bool SYM_>
+struct KI8 {
+  static constexpr int RB = 128, OFF = SYM_ ? 384 : 256, BITS = 8;
+  static constexpr bool SYM = SYM_, F16 = false;
+  u4_t a, b;
+  __device__ __forceinline__ void load(const uint8_t* row, int q4) {
+    const u4_t* p = reinterpret_cast<const u4_t*>(row + q4 * 32);
+    a = p[0];
+    b = p[1];
+  }
+  __device__ __forceinline__ u4_t slice(int s) const {
+    unsigned lo = s < 2 ? a[2 * s] : b[2 * s - 4];
+    unsigned hi = s < 2 ? a[2 * s + 1] : b[2 * s - 3];
+    if constexpr (SYM) {
+      lo ^= 0x80808080u;
+      hi ^= 0x80808080u;
+    }
+    u4_t o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (perm(hi, lo, sel_bytes(i)) << 2) | 0x5C005C00u;
+    return o;
+  }
+};
+
+struct KF16 {
+  static constexpr int RB = 256, OFF = 0, BITS = 16;
+  static constexpr bool SYM = false, F16 = true;
+  u4_t r[4];
+  __device__ __forceinline__ void load(const uint8_t* row, int q4) {
+    const u4_t* p = reinterpret_cast<const u4_t*>(row + q4 * 64);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) r[s] = p[s];
+  }
+  __device__ __forceinline__ u4_t slice(int s) const { return r[s]; }
+};
+
+// ---------------------------------------------------------------------------
+// V codecs: load the lane's column word n16 of 8 token rows and form the B
+// operand of column block j: 4 fp16 pairs (rows 2r, 2r + 1), value OFF + code
+// (8-bit codes: code - z exactly, see pair_sub).
+
+struct VI4 {
+  static constexpr int RB = 64, OFF = 16, BITS = 4;
+  static constexpr bool SYM = false, F16 = false, EXACT = false;
+  unsigned r[8];
+  __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r[k] = *reinterpret_cast<const unsigned*>(row0 + k * RB + n16 * 4);
+  }
+  __device__ __forceinline__ void zero_row(int k) { r[k] = 0u; }
+  __device__ __forceinline__ u4_t block(int j) const {
+    u4_t o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const unsigned x = perm(r[2 * p + 1], r[2 * p], sel_bytes(j >> 1));
+      o[p] = ((j & 1) ? ((x << 2) & 0x03C003C0u) : ((x << 6) & 0x03C003C0u)) | 0x4C004C00u;
+    }
+    return o;
+  }
+};
+
+struct VI2 {
+  static constexpr int RB = 32, OFF = 4, BITS = 2;
+  static constexpr bool SYM = false, F16 = false, EXACT = false;
+  unsigned x[4];  // rows 2p (low half) and 2p + 1 (high half)
+  __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
+    unsigned r[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r[k] = *reinterpret_cast<const uint16_t*>(row0 + k * RB + n16 * 2);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) x[p] = perm(r[2 * p + 1], r[2 * p], 0x05040100u);
+  }
+  __device__ __forceinline__ void zero_row(int k) {
+    x[k >> 1] &= (k & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+  }
+  __device__ __forceinline__ u4_t block(int j) const {
+    u4_t o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const unsigned y = j <= 4 ? (x[p] << (8 - 2 * j)) : (x[p] >> (2 * j - 8));
+      o[p] = (y & 0x03000300u) | 0x44004400u;
+    }
+    return o;
+  }
+};
+
+template <bool SYM_>
+struct VI8 {
+  static constexpr int RB = 128, OFF = 0, BITS = 8;
+  static constexpr bool SYM = SYM_, F16 = false, EXACT = true;
+  unsigned w0[8], w1[8];  // codes 0-3 and 4-7 of the column word, per row
+  __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint2 v = *reinterpret_cast<const uint2*>(row0 + k * RB + n16 * 8);
+      w0[k] = SYM ? (v.x ^ 0x80808080u) : v.x;
+      w1[k] = SYM ? (v.y ^ 0x80808080u) : v.y;
+    }
+  }
+  __device__ __forceinline__ void zero_row(int k) {}
+  // 1024 + code (+128 when symmetric) per pair; the caller subtracts (1024 + z) exactly
+  __device__ __forceinline__ u4_t block(int j) const {
+    const unsigned* w = (j >> 2) ? w1 : w0;
+    u4_t o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) o[p] = perm(w[2 * p + 1], w[2 * p], sel_bytes(j & 3)) | 0x64006400u;
+    return o;
+  }
+};
+
+struct VF16 {
+  static constexpr int RB = 256, OFF = 0, BITS = 16;
+  static constexpr bool SYM = false, F16 = true, EXACT = false;
+  u4_t r[8];
+  __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r[k] = *reinterpret_cast<const u4_t*>(row0 + k * RB + n16 * 16);
+  }
+  __device__ __forceinline__ void zero_row(int k) { r[k] = u4_t{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ u4_t block(int j) const {
+    u4_t o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      o[p] = perm(r[2 * p + 1][j >> 1], r[2 * p][j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
+    return o;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Per-call parameters and per-(b, kv head) views.
+
+struct AttnParams {
+  int B, H, S, Hq, G, qtiles, max_len, num_splits, split_len, chunk_tokens;
+  float qscale;  // sm_scale * log2(e)
+  const uint16_t* q;
+  const int* seq_len;
+  float* out;
+  float* ws;           // split partials [B][Hq][num_splits][kPartStride]
+  unsigned* counters;  // [B][H][qtiles] arrival counters (zero between calls)
+  const int* seg;
+  unsigned* status;
+  TensorArgs k, v;
+};
+
+// One tensor's view for a (b, kv head): code rows and token-axis metadata.
+struct TokView {
+  const uint8_t* codes;  // row 0 of this (b, h)
+  const float* scale;    // [rows][ng]
+  const uint8_t* zero;   // [rows][ng] (null when symmetric)
+};
+
+// Channel-axis K metadata: per 64-token block, per channel.
+struct ChanView {
+  const float* scale;   // [S/64][128]
+  const uint8_t* zero;  // [S/64][128]
+};
+
+// Oaken sparse side list of one tensor for a (b, kv head).
+struct SparseView {
+  const float* oscale;    // [rows][ng]
+  const uint32_t* rowptr; // [S + 1]
+  const uint16_t* sparse; // [cap]
+  unsigned cap;
+  float t_lo, t_hi;
+};
+
+// Per-wave LDS scratch.
+template <int NGV, bool OAK>
+struct WaveLds {
+  unsigned short w[NGV][2][16][kTile];  // softmax weights per V group: hi / lo, [query][token]
+  float sp_sc[OAK ? 16 : 1][kTile];     // sparse K score additions [query][token]
+  float sp_p[OAK ? 16 : 1][kTile];      // probabilities for the sparse V side
+  float sp_o[OAK ? 16 : 1][128];        // sparse V accumulators [query][channel]
+  unsigned sp_rp[OAK ? kTile + 1 : 1];  // tile row pointers
+};
+
+// Running softmax state of a wave (lane-held, see the header comment).
+template <int GI>
+struct SoftState {
+  float m[GI], l[GI];
+  f4_t o[8];  // [column block j] rows 4*q4 + i
+  float vb[GI][4];  // V bias per query row and V group (partial over this lane's tokens)
+};
+
+template <int GI>
+__device__ __forceinline__ void soft_init(SoftState<GI>& st) {
+#pragma unroll
+  for (int i = 0; i < GI; ++i) {
+    st.m[i] = -INFINITY;
+    st.l[i] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) st.vb[i][g] = 0.0f;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+}  // namespace kvq

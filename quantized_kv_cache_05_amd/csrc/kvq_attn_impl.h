@@ -1,0 +1,543 @@
+// The tile loop and epilogue of the matrix-core decode (see kvq_attn.h for the
+// operand layouts).  Kernels in kvq_decode_*.hip instantiate attend_wave for
+// their codecs and finish with finish_split.
+#pragma once
+#include "kvq_attn.h"
+
+namespace kvq {
+
+// QR = query rows a workgroup serves (1, 4 or 16 query heads of one KV
+// head); GI = query rows per lane row group in the C layouts (1 or 4).
+template <int QR>
+struct QRows {
+  static constexpr int R = QR;
+  static constexpr int GI = QR == 1 ? 1 : 4;
+};
+
+// Workgroup-shared LDS: the query tile, per-group query sums, and a per-wave
+// scratch area that the epilogue reuses for the wave records.
+template <int QR, int NGV, bool OAK>
+struct AttnLds {
+  static constexpr int R = QR;
+  float q[R][128];       // query tile (fp16 values in binary32)
+  float qg[R][4];        // sum of the query over each K channel group
+  struct __attribute__((aligned(16))) Wave {
+    unsigned short w[NGV][2][R][kTile];  // softmax weights hi / lo, [V group][query][token]
+    float sp_sc[OAK ? R : 1][kTile];
+    float sp_p[OAK ? R : 1][kTile];
+    float sp_o[OAK ? R : 1][128];
+    float sp_alpha[OAK ? R : 1];
+    unsigned sp_rp[OAK ? kTile + 1 : 1];
+  };
+  struct Rec {
+    float o[R][128 + 2];  // per query: output sum, then m, l
+  };
+  union __attribute__((aligned(16))) {
+    Wave wave[kNW];
+    Rec rec[kNW];
+  } u;
+  int last;
+};
+
+// Meta of the two tokens of a lane's score column (token nb*16 + n16).
+template <int NG, bool SYM>
+__device__ __forceinline__ void load_tok_meta(const TokView& v, int row, float (&s)[NG], float (&z)[NG],
+                                              bool valid) {
+  if constexpr (NG == 1) {
+    s[0] = v.scale[row];
+  } else if constexpr (NG == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(v.scale + (long long)row * 2);
+    s[0] = t.x; s[1] = t.y;
+  } else {
+    const float4 t = *reinterpret_cast<const float4*>(v.scale + (long long)row * 4);
+    s[0] = t.x; s[1] = t.y; s[2] = t.z; s[3] = t.w;
+  }
+  if constexpr (SYM) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) z[g] = 0.0f;
+  } else {
+    unsigned zw;
+    if constexpr (NG == 1) zw = v.zero[row];
+    else if constexpr (NG == 2) zw = *reinterpret_cast<const uint16_t*>(v.zero + (long long)row * 2);
+    else zw = *reinterpret_cast<const unsigned*>(v.zero + (long long)row * 4);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) z[g] = (float)((zw >> (8 * g)) & 0xFFu);
+  }
+  if (!valid) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) { s[g] = 0.0f; z[g] = 0.0f; }
+  }
+}
+
+// Sum / max over the 16 lanes of a row group (lanes differing in bits 0-3).
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ __forceinline__ float max16(float v) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// Oaken sparse entries of tile rows [ra, rb) (relative to the tile start
+// `tile`): calls f(entry lane's row r in the tile, channel idx, x_hat) for
+// every entry, 64 entries per pass; rows come from a binary search over the
+// tile's row pointers staged in LDS.
+template <class F>
+__device__ __forceinline__ void for_tile_entries(const SparseView& sv, int ng, long long tile, int ra,
+                                                 int rb, unsigned* sp_rp, int lane, F&& f) {
+  if (lane <= kTile) sp_rp[lane] = sv.rowptr[tile + lane];
+  wave_lds_sync();
+  const unsigned e0 = sp_rp[ra], e1 = min(sp_rp[rb], sv.cap);
+  for (unsigned base = e0; base < e1; base += 64) {
+    const unsigned e = base + lane;
+    if (e < e1) {
+      // last row r in [ra, rb) with rp[r] <= e
+      int lo = ra, hi = rb - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sp_rp[mid] <= e) lo = mid; else hi = mid - 1;
+      }
+      const unsigned en = sv.sparse[e];
+      const int idx = (int)(en & 127u);
+      const float mag = (float)((en >> 8) & 31u);
+      const float so = sv.oscale[(tile + lo) * ng + idx / (128 / ng)];
+      const float xh = ((en >> 7) & 1u) ? sv.t_hi + mag * so : sv.t_lo - mag * so;
+      f(lo, idx, xh);
+    }
+  }
+  wave_lds_sync();
+}
+
+// ---------------------------------------------------------------------------
+// One wave's share of a token range [t0, t1) of one (b, kv head): tiles of 32
+// tokens starting at tile-aligned offsets, taken round robin by the waves in
+// steps of TPS tiles.
+//
+//  KC / VC: codecs.  NGK / NGV: channel groups of K / V (token axis).
+//  CHANK: K has channel-axis groups of 64 tokens (scale folded into the query).
+//  OAK: Oaken sparse side lists for K and V.
+template <int QR, int NGK, int NGV, class KC, class VC, bool CHANK, bool OAK, int TPS, class LDS>
+__device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
+                                            SoftState<QRows<QR>::GI>& st, const TokView& kv,
+                                            const TokView& vv, const ChanView& kc,
+                                            const SparseView& ks, const SparseView& vs, int nq,
+                                            int t0, int t1, int wave, const u4_t (&qop)[4]) {
+  constexpr int R = QR, GI = QRows<QR>::GI;
+  static_assert(LDS::R == QR, "LDS tables sized for QR query rows");
+  const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
+  // table row of the A-operand row n16 and of C-layout row 4*q4 + i (rows past QR
+  // are padding and repeat the last table row)
+  auto arow = [&](int x) { return GI == 1 ? 0 : min(x, R - 1); };
+  auto& W = L.u.wave[wave];
+  const int tb = t0 & ~(kTile * TPS - 1);
+  for (int step = tb + wave * kTile * TPS; step < t1; step += kNW * kTile * TPS) {
+    // ---- channel-axis K: fold the block's scales into the query ----
+    u4_t qh[4], ql[4];
+    float cbias[GI];
+    if constexpr (CHANK) {
+      const int blk = step >> 6;
+      const float* sp = kc.scale + (long long)blk * 128;
+      const uint8_t* zp = kc.zero + (long long)blk * 128;
+      const int m = arow(n16);
+      float part = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int c0 = 32 * s + 8 * q4;
+        const float4 sa = *reinterpret_cast<const float4*>(sp + c0);
+        const float4 sb = *reinterpret_cast<const float4*>(sp + c0 + 4);
+        const u2_t zz = *reinterpret_cast<const u2_t*>(zp + c0);
+        const float sc[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float a = L.q[m][c0 + v] * sc[v], b = L.q[m][c0 + v + 4] * sc[v + 4];
+          unsigned hi, lo;
+          split_pair(a, b, hi, lo);
+          qh[s][v] = hi;
+          ql[s][v] = lo;
+          const float za = (float)((zz[0] >> (8 * v)) & 0xFFu) + (float)KC::OFF;
+          const float zb = (float)((zz[1] >> (8 * v)) & 0xFFu) + (float)KC::OFF;
+          part = fmaf(a, za, part);
+          part = fmaf(b, zb, part);
+        }
+      }
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      // part now holds the bias of query n16; rows of this lane are 4*q4 + i
+#pragma unroll
+      for (int i = 0; i < GI; ++i) cbias[i] = __shfl(part, GI == 1 ? 0 : 4 * q4 + i, 64);
+    }
+#pragma unroll
+    for (int tt = 0; tt < TPS; ++tt) {
+      const int tile = step + tt * kTile;
+      if (tile >= t1) break;
+      if (tile + kTile <= t0) continue;
+      // ---- loads ----
+      KC kr[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) kr[nb].load(kv.codes + (long long)(tile + nb * 16 + n16) * KC::RB, q4);
+      VC vr;
+      vr.load(vv.codes + (long long)(tile + 8 * q4) * VC::RB, n16);
+      float sk[2][NGK], zk[2][NGK], sv[2][NGV], zv[2][NGV];
+      bool ok[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int t = tile + nb * 16 + n16;
+        ok[nb] = t >= t0 && t < t1;
+        if constexpr (!CHANK && !KC::F16) load_tok_meta<NGK, KC::SYM>(kv, t, sk[nb], zk[nb], ok[nb]);
+        if constexpr (!VC::F16) load_tok_meta<NGV, VC::SYM>(vv, t, sv[nb], zv[nb], ok[nb]);
+      }
+      if constexpr (VC::F16) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int t = tile + 8 * q4 + k;
+          if (t < t0 || t >= t1) vr.zero_row(k);
+        }
+      }
+      // V zero-points of the B operand rows (8-bit V codes subtract them exactly)
+      u4_t zsub[NGV];
+      if constexpr (VC::EXACT) {
+#pragma unroll
+        for (int g = 0; g < NGV; ++g) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            float za = VC::SYM ? 128.0f : 0.0f, zb = za;
+            if constexpr (!VC::SYM) {
+              za = (float)vv.zero[(long long)(tile + 8 * q4 + 2 * p) * NGV + g];
+              zb = (float)vv.zero[(long long)(tile + 8 * q4 + 2 * p + 1) * NGV + g];
+            }
+            const h2_t zz = {(_Float16)(-1024.0f - za), (_Float16)(-1024.0f - zb)};
+            zsub[g][p] = __builtin_bit_cast(unsigned, zz);
+          }
+        }
+      }
+      // ---- scores ----
+      float sc[2][GI];
+      if constexpr (CHANK) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          f4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const u4_t kb = kr[nb].slice(s);
+            c = mfma(qh[s], kb, c);
+            c = mfma(ql[s], kb, c);
+          }
+#pragma unroll
+          for (int i = 0; i < GI; ++i) sc[nb][i] = (c[i] - cbias[i]) * P.qscale;
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          f4_t c[NGK];
+#pragma unroll
+          for (int g = 0; g < NGK; ++g) c[g] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) c[s / (4 / NGK)] = mfma(qop[s], kr[nb].slice(s), c[s / (4 / NGK)]);
+#pragma unroll
+          for (int i = 0; i < GI; ++i) {
+            const int m = arow(4 * q4 + i);
+            float a;
+            if constexpr (KC::F16) {
+              a = c[0][i];
+            } else {
+              a = 0.0f;
+#pragma unroll
+              for (int g = 0; g < NGK; ++g)
+                a = fmaf(sk[nb][g], fmaf(-(zk[nb][g] + (float)KC::OFF), L.qg[m][g], c[g][i]), a);
+            }
+            sc[nb][i] = a * P.qscale;
+          }
+        }
+      }
+      // ---- Oaken: outer K values add q[idx] * x_hat to their token's score ----
+      if constexpr (OAK) {
+        const int ra = max(t0 - tile, 0), rb = min(t1 - tile, kTile);
+        for_tile_entries(ks, NGK, tile, ra, rb, W.sp_rp, lane, [&](int r, int idx, float xh) {
+          for (int m = 0; m < nq; ++m) atomicAdd(&W.sp_sc[m][r], L.q[m][idx] * xh);
+        });
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int i = 0; i < GI; ++i) {
+            const int m = GI == 1 ? 0 : 4 * q4 + i;
+            if (m < nq) sc[nb][i] = fmaf(W.sp_sc[m][nb * 16 + n16], P.qscale, sc[nb][i]);
+          }
+        wave_lds_sync();
+        for (int idx = lane; idx < R * kTile; idx += 64) (&W.sp_sc[0][0])[idx] = 0.0f;
+      }
+      // ---- online softmax (base 2) ----
+      float alpha[GI];
+      bool grow = false;
+#pragma unroll
+      for (int i = 0; i < GI; ++i) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          if (!ok[nb]) sc[nb][i] = -INFINITY;
+        const float tm = max16(fmaxf(sc[0][i], sc[1][i]));
+        const float mn = fmaxf(st.m[i], tm);
+        alpha[i] = mn == -INFINITY ? 1.0f : fexp2(st.m[i] - mn);
+        grow |= mn > st.m[i];
+        st.m[i] = mn;
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int i = 0; i < GI; ++i) {
+          const float a = alpha[i];
+          st.l[i] *= a;
+#pragma unroll
+          for (int g = 0; g < NGV; ++g) st.vb[i][g] *= a;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) st.o[j][i] *= a;
+        }
+        if constexpr (OAK) {
+          if (n16 == 0) {
+#pragma unroll
+            for (int i = 0; i < GI; ++i) {
+              const int m = GI == 1 ? 0 : 4 * q4 + i;
+              if (m < R) W.sp_alpha[m] = alpha[i];
+            }
+          }
+          wave_lds_sync();
+          for (int idx = lane; idx < nq * 128; idx += 64) (&W.sp_o[0][0])[idx] *= W.sp_alpha[idx >> 7];
+        }
+      }
+      float p[2][GI];
+#pragma unroll
+      for (int i = 0; i < GI; ++i)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          p[nb][i] = ok[nb] ? fexp2(sc[nb][i] - st.m[i]) : 0.0f;
+          st.l[i] += p[nb][i];
+        }
+      // ---- Oaken: outer V values add p * x_hat to their channel ----
+      if constexpr (OAK) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int i = 0; i < GI; ++i) {
+            const int m = GI == 1 ? 0 : 4 * q4 + i;
+            if ((GI != 1 || q4 == 0) && m < R) W.sp_p[m][nb * 16 + n16] = p[nb][i];
+          }
+        wave_lds_sync();
+        const int ra = max(t0 - tile, 0), rb = min(t1 - tile, kTile);
+        for_tile_entries(vs, NGV, tile, ra, rb, W.sp_rp, lane, [&](int r, int idx, float xh) {
+          for (int m = 0; m < nq; ++m) atomicAdd(&W.sp_o[m][idx], W.sp_p[m][r] * xh);
+        });
+      }
+      // ---- weights p * s_v (binary32) -> fp16 hi / lo in LDS, V bias ----
+#pragma unroll
+      for (int i = 0; i < GI; ++i) {
+        const int m = GI == 1 ? 0 : 4 * q4 + i;
+        const bool wr = (GI != 1 || q4 == 0) && m < R;
+#pragma unroll
+        for (int g = 0; g < NGV; ++g) {
+          float w0, w1;
+          if constexpr (VC::F16) {
+            w0 = p[0][i];
+            w1 = p[1][i];
+          } else {
+            w0 = p[0][i] * sv[0][g];
+            w1 = p[1][i] * sv[1][g];
+            if constexpr (!VC::EXACT) {
+              st.vb[i][g] = fmaf(w0, zv[0][g] + (float)VC::OFF, st.vb[i][g]);
+              st.vb[i][g] = fmaf(w1, zv[1][g] + (float)VC::OFF, st.vb[i][g]);
+            }
+          }
+          unsigned hi, lo;
+          split_pair(w0, w1, hi, lo);
+          if (wr) {
+            W.w[g][0][m][n16] = (unsigned short)(hi & 0xFFFFu);
+            W.w[g][0][m][16 + n16] = (unsigned short)(hi >> 16);
+            W.w[g][1][m][n16] = (unsigned short)(lo & 0xFFFFu);
+            W.w[g][1][m][16 + n16] = (unsigned short)(lo >> 16);
+          }
+        }
+      }
+      wave_lds_sync();
+      // ---- O += W V ----
+      u4_t wa[NGV][2];
+      const int mr = arow(n16);
+#pragma unroll
+      for (int g = 0; g < NGV; ++g)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) wa[g][h] = *reinterpret_cast<const u4_t*>(&W.w[g][h][mr][8 * q4]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        constexpr int JPG = 8 / NGV;
+        u4_t b = vr.block(j);
+        if constexpr (VC::EXACT) {
+#pragma unroll
+          for (int p2 = 0; p2 < 4; ++p2) {
+            // copy vector elements to scalars before bit casts: clang miscompiles a bit cast
+            // applied directly to an ext-vector element
+            const unsigned bv = b[p2], zv = zsub[j / JPG][p2];
+            const h2_t x = __builtin_bit_cast(h2_t, bv) + __builtin_bit_cast(h2_t, zv);
+            b[p2] = __builtin_bit_cast(unsigned, x);
+          }
+        }
+        st.o[j] = mfma(wa[j / JPG][0], b, st.o[j]);
+        st.o[j] = mfma(wa[j / JPG][1], b, st.o[j]);
+      }
+      wave_lds_sync();
+    }
+  }
+}
+
+// Fold the wave's state into its record (sum over the 16 token columns,
+// V bias and sparse V values applied).  Caller: all waves, after a barrier.
+template <int QR, int NGV, bool OAK, class LDS>
+__device__ __forceinline__ void wave_record(LDS& L, SoftState<QRows<QR>::GI>& st, int wave, int nq) {
+  constexpr int GI = QRows<QR>::GI;
+  const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
+  float lt[GI], vbt[GI][NGV];
+#pragma unroll
+  for (int i = 0; i < GI; ++i) {
+    lt[i] = sum16(st.l[i]);
+#pragma unroll
+    for (int g = 0; g < NGV; ++g) vbt[i][g] = sum16(st.vb[i][g]);
+  }
+  float spo[GI][8];
+  if constexpr (OAK) {
+    // copy the sparse V accumulators out before the records overwrite them
+#pragma unroll
+    for (int i = 0; i < GI; ++i) {
+      const int m = GI == 1 ? 0 : 4 * q4 + i;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) spo[i][j] = m < nq ? L.u.wave[wave].sp_o[m][16 * j + n16] : 0.0f;
+    }
+  }
+  __syncthreads();
+  auto& rec = L.u.rec[wave];
+#pragma unroll
+  for (int i = 0; i < GI; ++i) {
+    const int m = GI == 1 ? 0 : 4 * q4 + i;
+    if (GI == 1 && q4 != 0) continue;
+    if (m >= nq) continue;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float o = st.o[j][i] - vbt[i][j / (8 / NGV)];
+      if constexpr (OAK) o += spo[i][j];
+      rec.o[m][16 * j + n16] = o;
+    }
+    if (n16 == 0) {
+      rec.o[m][128] = st.m[i];
+      rec.o[m][129] = lt[i];
+    }
+  }
+}
+
+// Merge the four wave records of each query; write the output (one split)
+// or the split partial, and let the last-arriving workgroup of the
+// (b, kv head, query tile) merge all partials (log-sum-exp rule).
+template <class LDS>
+__device__ __forceinline__ void finish_split(const AttnParams& P, LDS& L, int b, int kvh, int qt,
+                                             int split, int nq) {
+  __syncthreads();
+  const long long hq0 = (long long)kvh * P.G + (long long)qt * 16;
+  for (int idx = threadIdx.x; idx < nq * 128; idx += blockDim.x) {
+    const int m = idx >> 7, d = idx & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) M = fmaxf(M, L.u.rec[w].o[m][128]);
+    float Ls = 0.0f, O = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) {
+        const float mw = L.u.rec[w].o[m][128];
+        if (mw != -INFINITY) {
+          const float f = fexp2(mw - M);
+          Ls = fmaf(f, L.u.rec[w].o[m][129], Ls);
+          O = fmaf(f, L.u.rec[w].o[m][d], O);
+        }
+      }
+    }
+    const long long hq = hq0 + m;
+    if (P.num_splits == 1) {
+      P.out[((long long)b * P.Hq + hq) * 128 + d] = Ls > 0.0f ? O / Ls : 0.0f;
+    } else {
+      float* r = P.ws + (((long long)b * P.Hq + hq) * P.num_splits + split) * kPartStride;
+      r[4 + d] = O;
+      if (d == 0) {
+        r[0] = M;
+        r[1] = Ls;
+      }
+    }
+  }
+  if (P.num_splits == 1) return;
+  __threadfence();
+  __syncthreads();
+  unsigned* cnt = P.counters + ((long long)b * P.H + kvh) * P.qtiles + qt;
+  if (threadIdx.x == 0) L.last = atomicAdd(cnt, 1u) == (unsigned)(P.num_splits - 1);
+  __syncthreads();
+  if (!L.last) return;
+  __threadfence();
+  for (int idx = threadIdx.x; idx < nq * 128; idx += blockDim.x) {
+    const int m = idx >> 7, d = idx & 127;
+    const float* r0 = P.ws + (((long long)b * P.Hq + hq0 + m) * P.num_splits) * kPartStride;
+    float M = -INFINITY;
+    for (int s = 0; s < P.num_splits; ++s) M = fmaxf(M, r0[(long long)s * kPartStride]);
+    float Ls = 0.0f, O = 0.0f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < P.num_splits; ++s) {
+        const float* r = r0 + (long long)s * kPartStride;
+        const float ms = r[0];
+        if (ms != -INFINITY) {
+          const float f = fexp2(ms - M);
+          Ls = fmaf(f, r[1], Ls);
+          O = fmaf(f, r[4 + d], O);
+        }
+      }
+    }
+    P.out[((long long)b * P.Hq + hq0 + m) * 128 + d] = Ls > 0.0f ? O / Ls : 0.0f;
+  }
+  if (threadIdx.x == 0) *cnt = 0u;
+}
+
+// Workgroup prologue: the query tile in LDS, per-group query sums, the K
+// A-operand of each k-step, and reset wave state.  Ends with a barrier.
+template <int QR, int NGK, class LDS>
+__device__ __forceinline__ void attn_prologue(const AttnParams& P, LDS& L, int b, int kvh, int qt,
+                                              int nq, u4_t (&qop)[4]) {
+  constexpr int R = QR, GI = QRows<QR>::GI;
+  for (int idx = threadIdx.x; idx < R * 128; idx += blockDim.x) {
+    const int m = idx >> 7, d = idx & 127;
+    float v = 0.0f;
+    if (m < nq) v = h2f(P.q[((long long)b * P.Hq + (long long)kvh * P.G + (long long)qt * 16 + m) * 128 + d]);
+    L.q[m][d] = v;
+  }
+  for (int idx = threadIdx.x; idx < (int)(sizeof(L.u) / 4); idx += blockDim.x)
+    reinterpret_cast<float*>(&L.u)[idx] = 0.0f;
+  __syncthreads();
+  if (threadIdx.x < R * NGK) {
+    const int m = threadIdx.x / NGK, g = threadIdx.x % NGK, w = 128 / NGK;
+    float s = 0.0f;
+    for (int d = g * w; d < (g + 1) * w; ++d) s += L.q[m][d];
+    L.qg[m][g] = s;
+  }
+  const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
+  const int m = GI == 1 ? 0 : min(n16, R - 1);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c0 = 32 * s + 8 * q4;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const h2_t h = {(_Float16)L.q[m][c0 + v], (_Float16)L.q[m][c0 + v + 4]};
+      qop[s][v] = __builtin_bit_cast(unsigned, h);
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ int clamp_seq_len(const AttnParams& P, int b, bool report) {
+  int len = P.seq_len[b];
+  if (len < 0 || len > P.max_len) {
+    if (report) set_flag(P.status, kFlagLenRange);
+    len = len < 0 ? 0 : P.max_len;
+  }
+  return len;
+}
+
+}  // namespace kvq

@@ -1,52 +1,20 @@
-// Decode kernels for the uniform cache (token-axis K and V, or channel-axis
-// K with token-axis V) and the split merge.
-#include "kvq_decode_impl.h"
+// Decode kernels for the uniform cache: token-axis K and V groups, or K with
+// channel-axis groups of 64 tokens and token-axis V (see kvq_attn.h).
+#include "kvq_attn_impl.h"
 
 namespace kvq {
 namespace {
 
-template <class C>
-struct Maker;
-template <int BITS, bool SYM, int NG>
-struct Maker<TokCodec<BITS, SYM, NG>> {
-  using T = TokCodec<BITS, SYM, NG>;
-  static __device__ __forceinline__ T make(const TensorArgs& t, long long bh, int S) {
-    T c;
-    c.codes = t.codes + bh * S * T::RB;
-    c.scale = t.scale + bh * S * NG;
-    c.zero = SYM ? nullptr : t.zero + bh * S * NG;
-    return c;
-  }
-};
-template <int BITS>
-struct Maker<ChanCodec<BITS>> {
-  using T = ChanCodec<BITS>;
-  static __device__ __forceinline__ T make(const TensorArgs& t, long long bh, int S) {
-    T c;
-    c.codes = t.codes + bh * S * T::RB;
-    c.scale = t.scale + bh * (S / 64) * kD;
-    c.zero = t.zero + bh * (S / 64) * kD;
-    return c;
-  }
-};
-
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
-
-template <int GT, class KC, class VC>
-struct Layout {
-  static constexpr int LPR = cmax(cmax(KC::MIN_LPR, VC::MIN_LPR), GT > 1 ? 8 : 1);
-};
-
-template <int GT, class KC, class VC>
-__global__ __launch_bounds__(256) void k_decode_uniform(DecodeParams P) {
-  constexpr int LPR = Layout<GT, KC, VC>::LPR;
-  __shared__ float q_lds[GT * kD];
-  __shared__ float canon[kNW * GT * (kD + 2)];
+template <int QR, class KC, class VC, int NGK, int NGV, bool CHANK>
+__global__ __launch_bounds__(256) void k_attn_uniform(AttnParams P) {
+  __shared__ AttnLds<QR, NGV, false> L;
   const int split = blockIdx.x, qt = blockIdx.y % P.qtiles, kvh = blockIdx.y / P.qtiles, b = blockIdx.z;
   const int wave = threadIdx.x >> 6;
-  decode_prologue<GT, false>(P, b, kvh, qt, q_lds, canon, nullptr);
-  int len = clamp_len(P, b, split == 0 && blockIdx.y == 0 && threadIdx.x == 0);
-  if constexpr (KC::kind == kChan) {
+  const int nq = min(QR, P.G - qt * QR);
+  u4_t qop[4];
+  attn_prologue<QR, NGK>(P, L, b, kvh, qt, nq, qop);
+  int len = clamp_seq_len(P, b, split == 0 && blockIdx.y == 0 && threadIdx.x == 0);
+  if constexpr (CHANK) {
     if (len & 63) {
       if (split == 0 && blockIdx.y == 0 && threadIdx.x == 0) set_flag(P.status, kFlagLenRange);
       len &= ~63;
@@ -54,88 +22,80 @@ __global__ __launch_bounds__(256) void k_decode_uniform(DecodeParams P) {
   }
   const int t0 = split * P.split_len;
   const int t1 = min(len, t0 + P.split_len);
-  const long long bh = (long long)b * P.H + kvh;
+  SoftState<QRows<QR>::GI> st;
+  soft_init(st);
   if (t0 < t1) {
-    const KC kc = Maker<KC>::make(P.k, bh, P.S);
-    const VC vc = Maker<VC>::make(P.v, bh, P.S);
-    attend_segment<LPR, GT, 64>(kc, vc, t0, t1, wave, q_lds, nullptr, canon + wave * GT * (kD + 2));
-  }
-  decode_epilogue<GT>(P, b, kvh, qt, split, canon);
-}
-
-// kvq merge: one workgroup of 128 threads per (b, query head).
-__global__ __launch_bounds__(128) void k_merge(const float* __restrict__ ws, int NS,
-                                              float* __restrict__ out) {
-  const long long bq = blockIdx.x;
-  const int d = threadIdx.x;
-  const float* rec0 = ws + bq * NS * kPartStride;
-  float M = -INFINITY;
-  for (int s = 0; s < NS; ++s) M = fmaxf(M, rec0[(long long)s * kPartStride]);
-  float L = 0.0f, O = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < NS; ++s) {
-      const float* rec = rec0 + (long long)s * kPartStride;
-      if (rec[0] != -INFINITY) {
-        const float f = fexp2(rec[0] - M);
-        L = fmaf(f, rec[1], L);
-        O = fmaf(f, rec[4 + d], O);
-      }
+    const long long bh = (long long)b * P.H + kvh;
+    const long long S = P.S;
+    TokView kv{P.k.codes + bh * S * KC::RB, nullptr, nullptr};
+    ChanView kc{nullptr, nullptr};
+    if constexpr (CHANK) {
+      kc.scale = P.k.scale + bh * (S / 64) * 128;
+      kc.zero = P.k.zero + bh * (S / 64) * 128;
+    } else {
+      kv.scale = P.k.scale + bh * S * NGK;
+      kv.zero = KC::SYM ? nullptr : P.k.zero + bh * S * NGK;
     }
+    const TokView vv{P.v.codes + bh * S * VC::RB, P.v.scale + bh * S * NGV,
+                     VC::SYM ? nullptr : P.v.zero + bh * S * NGV};
+    const SparseView none{};
+    attend_wave<QR, NGK, NGV, KC, VC, CHANK, false, 2>(P, L, st, kv, vv, kc, none, none, nq, t0, t1,
+                                                        wave, qop);
   }
-  out[bq * kD + d] = L > 0.0f ? O / L : 0.0f;
+  wave_record<QR, NGV, false>(L, st, wave, nq);
+  finish_split(P, L, b, kvh, qt, split, nq);
 }
 
-DecodeParams make_params(const CacheArgs& c, const DecodeLaunch& d) {
-  DecodeParams P;
-  P.B = c.B; P.H = c.H; P.S = c.S; P.Hq = d.Hq; P.G = d.G; P.qtiles = d.qtiles;
-  P.max_len = d.max_len; P.num_splits = d.num_splits; P.split_len = d.split_len;
-  P.chunk_tokens = c.chunk_tokens; P.qscale = d.qscale; P.q = d.q; P.seq_len = d.seq_len;
-  P.out = d.out; P.ws = d.ws; P.seg = c.seg; P.status = c.status; P.k = c.k; P.v = c.v;
-  return P;
-}
-
-template <int GT, class KC, class VC>
-hipError_t go(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st) {
-  const dim3 grid((unsigned)d.num_splits, (unsigned)(c.H * d.qtiles), (unsigned)c.B);
-  hipLaunchKernelGGL((k_decode_uniform<GT, KC, VC>), grid, dim3(kNW * 64), 0, st, make_params(c, d));
+template <int QR, class KC, class VC, int NGK, int NGV, bool CHANK>
+hipError_t go(const AttnParams& P, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_attn_uniform<QR, KC, VC, NGK, NGV, CHANK>), grid, dim3(kNW * 64), 0, st, P);
   return hipGetLastError();
 }
 
-template <int GT, int BITS, bool SYM>
-hipError_t go_ng(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st) {
-  const int ng = kD / c.v.group;
-  if (c.k.axis == 1) {
-    if constexpr (SYM || BITS == 2) {
-      return hipErrorInvalidValue;
-    } else {
-      switch (ng) {
-        case 1: return go<GT, ChanCodec<BITS>, TokCodec<BITS, false, 1>>(c, d, st);
-        case 2: return go<GT, ChanCodec<BITS>, TokCodec<BITS, false, 2>>(c, d, st);
-        case 4: return go<GT, ChanCodec<BITS>, TokCodec<BITS, false, 4>>(c, d, st);
-        default: return hipErrorInvalidValue;
-      }
+template <int QR, class KC, class VC>
+hipError_t go_ng(const AttnParams& P, dim3 grid, bool chank, int ng, hipStream_t st) {
+  if (chank) {
+    switch (ng) {
+      case 1: return go<QR, KC, VC, 1, 1, true>(P, grid, st);
+      case 2: return go<QR, KC, VC, 1, 2, true>(P, grid, st);
+      case 4: return go<QR, KC, VC, 1, 4, true>(P, grid, st);
     }
+    return hipErrorInvalidValue;
   }
   switch (ng) {
-    case 1: return go<GT, TokCodec<BITS, SYM, 1>, TokCodec<BITS, SYM, 1>>(c, d, st);
-    case 2: return go<GT, TokCodec<BITS, SYM, 2>, TokCodec<BITS, SYM, 2>>(c, d, st);
-    case 4: return go<GT, TokCodec<BITS, SYM, 4>, TokCodec<BITS, SYM, 4>>(c, d, st);
-    default: return hipErrorInvalidValue;
+    case 1: return go<QR, KC, VC, 1, 1, false>(P, grid, st);
+    case 2: return go<QR, KC, VC, 2, 2, false>(P, grid, st);
+    case 4: return go<QR, KC, VC, 4, 4, false>(P, grid, st);
   }
+  return hipErrorInvalidValue;
 }
 
-template <int GT>
-hipError_t go_bits(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st) {
-  if (c.v.sym) return go_ng<GT, 8, true>(c, d, st);
-  switch (c.v.bits) {
-    case 8: return go_ng<GT, 8, false>(c, d, st);
-    case 4: return go_ng<GT, 4, false>(c, d, st);
-    case 2: return go_ng<GT, 2, false>(c, d, st);
-    default: return hipErrorInvalidValue;
+template <int QR>
+hipError_t go_codec(const AttnParams& P, dim3 grid, hipStream_t st) {
+  const bool chank = P.k.axis == 1;
+  const int ng = kD / P.v.group;
+  if (P.v.sym) return go_ng<QR, KI8<true>, VI8<true>>(P, grid, false, ng, st);
+  switch (P.v.bits) {
+    case 8: return go_ng<QR, KI8<false>, VI8<false>>(P, grid, chank, ng, st);
+    case 4: return go_ng<QR, KI4, VI4>(P, grid, chank, ng, st);
+    case 2:
+      if (chank) return hipErrorInvalidValue;
+      return go_ng<QR, KI2, VI2>(P, grid, false, ng, st);
   }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
+
+AttnParams make_attn_params(const CacheArgs& c, const DecodeLaunch& d) {
+  AttnParams P;
+  P.B = c.B; P.H = c.H; P.S = c.S; P.Hq = d.Hq; P.G = d.G; P.qtiles = d.qtiles;
+  P.max_len = d.max_len; P.num_splits = d.num_splits; P.split_len = d.split_len;
+  P.chunk_tokens = c.chunk_tokens; P.qscale = d.qscale; P.q = d.q; P.seq_len = d.seq_len;
+  P.out = d.out; P.ws = d.ws; P.counters = d.counters; P.seg = c.seg; P.status = c.status;
+  P.k = c.k; P.v = c.v;
+  return P;
+}
 
 bool decode_uniform_supported(const TensorArgs& k, const TensorArgs& v) {
   if (v.axis != 0) return false;
@@ -150,14 +110,14 @@ bool decode_uniform_supported(const TensorArgs& k, const TensorArgs& v) {
 
 hipError_t launch_decode_uniform(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st) {
   if (!decode_uniform_supported(c.k, c.v)) return hipErrorInvalidValue;
-  if (d.gtile == 1) return go_bits<1>(c, d, st);
-  if (d.gtile == 4) return go_bits<4>(c, d, st);
+  const AttnParams P = make_attn_params(c, d);
+  const dim3 grid((unsigned)d.num_splits, (unsigned)(c.H * d.qtiles), (unsigned)c.B);
+  switch (d.qr) {
+    case 1: return go_codec<1>(P, grid, st);
+    case 4: return go_codec<4>(P, grid, st);
+    case 16: return go_codec<16>(P, grid, st);
+  }
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_merge(const DecodeLaunch& d, int B, hipStream_t st) {
-  hipLaunchKernelGGL(k_merge, dim3((unsigned)(B * d.Hq)), dim3(kD), 0, st, d.ws, d.num_splits, d.out);
-  return hipGetLastError();
 }
 
 }  // namespace kvq

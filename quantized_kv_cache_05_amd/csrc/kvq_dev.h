@@ -103,4 +103,12 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
 
 __device__ __forceinline__ void set_flag(unsigned* status, unsigned f) { atomicOr(status, f); }
 
+// Wave-local ordering of LDS traffic: the wave's earlier LDS writes are
+// complete and visible to its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 }  // namespace kvq

@@ -9,6 +9,7 @@ namespace kvq {
 
 constexpr int kD = 128;          // head_dim
 constexpr int kPartStride = 132; // floats per split partial: m, l, 2 pad, o[128]
+constexpr int kMaxQR = 16;       // query heads one decode workgroup serves
 
 // Device view of one quantized tensor (K or V).
 struct TensorArgs {
@@ -44,25 +45,27 @@ struct DecodeLaunch {
   const uint16_t* q;
   int Hq;        // query heads
   int G;         // query heads per KV head
-  int gtile;     // query heads handled per workgroup (1 or 4)
-  int qtiles;    // ceil(G / gtile)
+  int qr;        // query heads per workgroup: 1, 4 or 16
+  int qtiles;    // ceil(G / qr)
   const int* seq_len;
   int max_len;
   int num_splits;
   int split_len; // tokens (UNIFORM/OAKEN) or chunk slots (CHUNK_MIXED) per split
   float qscale;  // sm_scale * log2(e)
   float* out;
-  float* ws;     // partials, null when num_splits == 1
+  float* ws;           // split partials, null when num_splits == 1
+  unsigned* counters;  // arrival counters [B][H][qtiles], null when num_splits == 1
 };
 
-hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, const uint16_t* x, int t_new,
-                              const int* pos, hipStream_t st);
+// vl: write the V row layout (else the K row layout), see kvq.h.
+hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
+                              int t_new, const int* pos, hipStream_t st);
 hipError_t launch_quant_channel(const CacheArgs& c, const TensorArgs& t, const uint16_t* x, int t_new,
                                 const int* pos, hipStream_t st);
-hipError_t launch_quant_mixed(const CacheArgs& c, const TensorArgs& t, const uint16_t* x,
+hipError_t launch_quant_mixed(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
                               const int* pos, hipStream_t st);
-hipError_t launch_quant_oaken(const CacheArgs& c, const TensorArgs& t, const uint16_t* x, int t_new,
-                              const int* pos, hipStream_t st);
+hipError_t launch_quant_oaken(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
+                              int t_new, const int* pos, hipStream_t st);
 hipError_t launch_reorder(const CacheArgs& c, const uint8_t* bits, int n_chunks, hipStream_t st);
 
 // Cocktail chunk precision search and Oaken calibration histogram.
@@ -81,9 +84,11 @@ hipError_t launch_percentiles(const unsigned long long* hist, const PercentileLi
 hipError_t launch_decode_uniform(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
 hipError_t launch_decode_oaken(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
 hipError_t launch_decode_mixed(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
-hipError_t launch_merge(const DecodeLaunch& d, int B, hipStream_t st);
 
 // True when a uniform (K, V) pair has a compiled decode kernel.
 bool decode_uniform_supported(const TensorArgs& k, const TensorArgs& v);
+
+struct AttnParams;
+AttnParams make_attn_params(const CacheArgs& c, const DecodeLaunch& d);
 
 }  // namespace kvq

@@ -75,19 +75,78 @@ __device__ __forceinline__ void unpack8(const uint4 raw, float (&v)[8]) {
 }
 
 template <int BITS>
-__device__ __forceinline__ void store_codes8(uint8_t* row, int li, uint32_t plo, uint32_t phi) {
+__device__ __forceinline__ void store_codes8(uint8_t* row, int slot, uint32_t plo, uint32_t phi) {
   if constexpr (BITS == 8) {
-    *reinterpret_cast<uint2*>(row + li * 8) = make_uint2(plo, phi);
+    *reinterpret_cast<uint2*>(row + slot * 8) = make_uint2(plo, phi);
   } else if constexpr (BITS == 4) {
-    *reinterpret_cast<uint32_t*>(row + li * 4) = plo;
+    *reinterpret_cast<uint32_t*>(row + slot * 4) = plo;
   } else {
-    *reinterpret_cast<uint16_t*>(row + li * 2) = (uint16_t)plo;
+    *reinterpret_cast<uint16_t*>(row + slot * 2) = (uint16_t)plo;
+  }
+}
+
+// Code v (0..7) of a lane's naturally packed codes.
+template <int BITS>
+__device__ __forceinline__ unsigned code_at(uint32_t plo, uint32_t phi, int v) {
+  if constexpr (BITS == 8) return ((v < 4 ? plo : phi) >> (8 * (v & 3))) & 0xFFu;
+  else return (plo >> (BITS * v)) & ((1u << BITS) - 1u);
+}
+
+// Slot of the K row that holds the 8 channels 8 li .. 8 li + 7 (kvq.h: slot
+// 4 q + s holds channels 32 s + 8 q + v).
+__device__ __forceinline__ int k_slot(int li) { return 4 * (li & 3) + (li >> 2); }
+
+// Store a lane's 8 codes (channels 8 li + v) into a packed row.
+//  K layout: the lane's codes form one slot.
+//  V layout: column word n holds channels n + 16 j; the row's 16 lanes
+//  exchange codes through `lrow` (128 entries of this row, wave-local).
+template <int BITS, bool VL>
+__device__ __forceinline__ void store_row_codes(uint8_t* row, int li, uint32_t plo, uint32_t phi,
+                                                uint16_t* lrow) {
+  if constexpr (!VL) {
+    store_codes8<BITS>(row, k_slot(li), plo, phi);
+  } else {
+#pragma unroll
+    for (int v = 0; v < 8; ++v) lrow[8 * li + v] = (uint16_t)code_at<BITS>(plo, phi, v);
+    wave_lds_sync();
+    uint64_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w |= (uint64_t)lrow[li + 16 * j] << (BITS * j);
+    wave_lds_sync();
+    store_codes8<BITS>(row, li, (uint32_t)w, (uint32_t)(w >> 32));
+  }
+}
+
+// fp16 rows of the chunk-mixed FP16 pool.  K layout: slot 4 q + s (16 bytes)
+// holds channels 32 s + 8 q + (0, 4, 1, 5, 2, 6, 3, 7); V layout: word n (16
+// bytes) holds channels n + 16 j.
+template <bool VL>
+__device__ __forceinline__ void store_row_f16(uint8_t* row, int li, uint4 raw, uint16_t* lrow) {
+  if constexpr (!VL) {
+    uint4 o;
+    o.x = __builtin_amdgcn_perm(raw.z, raw.x, 0x05040100u);
+    o.y = __builtin_amdgcn_perm(raw.z, raw.x, 0x07060302u);
+    o.z = __builtin_amdgcn_perm(raw.w, raw.y, 0x05040100u);
+    o.w = __builtin_amdgcn_perm(raw.w, raw.y, 0x07060302u);
+    *reinterpret_cast<uint4*>(row + k_slot(li) * 16) = o;
+  } else {
+    const uint32_t d[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int v = 0; v < 8; ++v) lrow[8 * li + v] = (uint16_t)(d[v >> 1] >> (16 * (v & 1)));
+    wave_lds_sync();
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (uint32_t)lrow[li + 32 * k] | ((uint32_t)lrow[li + 32 * k + 16] << 16);
+    wave_lds_sync();
+    *reinterpret_cast<uint4*>(row + li * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Uniform cache, token-axis groups.  x: [B][H][t_new][128], rows in that order.
-template <int BITS, bool SYM, int GE>
+// VL selects the V row layout.
+template <int BITS, bool SYM, int GE, bool VL>
 __global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict__ x, int t_new, int H,
                                                      int S, const int* __restrict__ pos,
                                                      long long rows, uint8_t* __restrict__ codes,
@@ -95,6 +154,7 @@ __global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict_
                                                      uint8_t* __restrict__ zero,
                                                      unsigned* __restrict__ status) {
   constexpr int NG = kD / GE, LG = GE / 8, RB = kD * BITS / 8;
+  __shared__ uint16_t lrows[VL ? 16 : 1][128];
   const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int li = threadIdx.x & 15;
   if (row >= rows) return;  // all 16 lanes of a row leave together
@@ -113,7 +173,7 @@ __global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict_
   float s;
   int z;
   quant8<BITS, SYM, GE>(v, 0xFFu, plo, phi, s, z);
-  store_codes8<BITS>(codes + dst * RB, li, plo, phi);
+  store_row_codes<BITS, VL>(codes + dst * RB, li, plo, phi, lrows[VL ? (threadIdx.x >> 4) : 0]);
   if (li % LG == 0) {
     scale[dst * NG + li / LG] = s;
     if constexpr (!SYM) zero[dst * NG + li / LG] = (uint8_t)z;
@@ -121,8 +181,9 @@ __global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Uniform cache, channel-axis groups of 64 tokens (K per channel, [KV-cache
-// quantization engineering page] advice).  One workgroup per 64-token block.
+// Uniform cache, channel-axis groups of 64 tokens (K per channel, the KV-cache
+// quantization engineering page's advice).  One workgroup per 64-token block;
+// codes in the K row layout.
 template <int BITS>
 __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restrict__ x, int t_new,
                                                        int H, int S, const int* __restrict__ pos,
@@ -130,7 +191,7 @@ __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restric
                                                        float* __restrict__ scale,
                                                        uint8_t* __restrict__ zero,
                                                        unsigned* __restrict__ status) {
-  constexpr int QMAX = (1 << BITS) - 1, RB = kD * BITS / 8, PB = 32 * BITS / 8;
+  constexpr int QMAX = (1 << BITS) - 1, RB = kD * BITS / 8;
   const int kb = blockIdx.x;
   const long long bh = blockIdx.y;
   const int b = (int)(bh / H);
@@ -179,26 +240,30 @@ __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restric
     zero[m] = (uint8_t)z;
   }
   __syncthreads();
+  // thread (row r, 32-channel block pc): slices q = 0..3 of k-step pc
   const int r = threadIdx.x >> 2, pc = threadIdx.x & 3;
-  uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  uint8_t* dst = codes + (bh * S + p + (long long)kb * 64 + r) * RB;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const int ch = pc * 32 + k;
-    const float s = s_sh[ch];
-    int q = 0;
-    if (s != 0.0f) q = min(max((int)rintf(tile[r][ch] / s) + z_sh[ch], 0), QMAX);
-    words[(k * BITS) / 32] |= (uint32_t)q << ((k * BITS) % 32);
+  for (int q = 0; q < 4; ++q) {
+    uint64_t w = 0;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int ch = pc * 32 + q * 8 + v;
+      const float s = s_sh[ch];
+      int c = 0;
+      if (s != 0.0f) c = min(max((int)rintf(tile[r][ch] / s) + z_sh[ch], 0), QMAX);
+      w |= (uint64_t)c << (BITS * v);
+    }
+    store_codes8<BITS>(dst, 4 * q + pc, (uint32_t)w, (uint32_t)(w >> 32));
   }
-  uint8_t* dst = codes + (bh * S + p + (long long)kb * 64 + r) * RB + pc * PB;
-#pragma unroll
-  for (int k = 0; k < PB / 4; ++k) reinterpret_cast<uint32_t*>(dst)[k] = words[k];
 }
 
 // ---------------------------------------------------------------------------
-// Chunk-mixed cache ([Cocktail page] §3.1.2 reorder, then quantization of the
-// reordered chunks): one workgroup per (slot, b, h); the slot's source chunk
-// is perm[b][slot], its class follows from seg[b].  FP16 chunks are copied.
-template <int GE>
+// Chunk-mixed cache (the Cocktail page's reorder, §3.1.2, then quantization
+// of the reordered chunks): one workgroup per (slot, b, h); the slot's source
+// chunk is perm[b][slot], its class follows from seg[b].  FP16 chunks are
+// copied (in the row layout of the FP16 pool).
+template <int GE, bool VL>
 __global__ __launch_bounds__(256) void k_quant_mixed(
     const uint16_t* __restrict__ x, int H, int S, int CT, int C, const int* __restrict__ pos,
     const int* __restrict__ perm, const int* __restrict__ seg, uint8_t* __restrict__ c16,
@@ -206,6 +271,7 @@ __global__ __launch_bounds__(256) void k_quant_mixed(
     uint8_t* __restrict__ c2, float* __restrict__ s2, uint8_t* __restrict__ z2,
     unsigned* __restrict__ status) {
   constexpr int NG = kD / GE, LG = GE / 8;
+  __shared__ uint16_t lrows[VL ? 16 : 1][128];
   const int j = blockIdx.x;
   const long long bh = blockIdx.y;
   const int b = (int)(bh / H);
@@ -222,11 +288,12 @@ __global__ __launch_bounds__(256) void k_quant_mixed(
   const uint16_t* xs = x + (bh * S + (long long)src * CT) * kD;
   const long long drow0 = (bh * C + k) * CT;
   const int li = threadIdx.x & 15;
+  uint16_t* lrow = lrows[VL ? (threadIdx.x >> 4) : 0];
   for (int r = threadIdx.x >> 4; r < CT; r += 16) {
     const uint4 raw = *reinterpret_cast<const uint4*>(xs + (long long)r * kD + li * 8);
     const long long drow = drow0 + r;
     if (cls == 0) {
-      *reinterpret_cast<uint4*>(c16 + (drow * kD + li * 8) * 2) = raw;
+      store_row_f16<VL>(c16 + drow * kD * 2, li, raw, lrow);
       continue;
     }
     float v[8];
@@ -236,14 +303,14 @@ __global__ __launch_bounds__(256) void k_quant_mixed(
     int z;
     if (cls == 1) {
       quant8<4, false, GE>(v, 0xFFu, plo, phi, s, z);
-      store_codes8<4>(c4 + drow * 64, li, plo, phi);
+      store_row_codes<4, VL>(c4 + drow * 64, li, plo, phi, lrow);
       if (li % LG == 0) {
         s4[drow * NG + li / LG] = s;
         z4[drow * NG + li / LG] = (uint8_t)z;
       }
     } else {
       quant8<2, false, GE>(v, 0xFFu, plo, phi, s, z);
-      store_codes8<2>(c2 + drow * 32, li, plo, phi);
+      store_row_codes<2, VL>(c2 + drow * 32, li, plo, phi, lrow);
       if (li % LG == 0) {
         s2[drow * NG + li / LG] = s;
         z2[drow * NG + li / LG] = (uint8_t)z;
@@ -253,18 +320,19 @@ __global__ __launch_bounds__(256) void k_quant_mixed(
 }
 
 // ---------------------------------------------------------------------------
-// Oaken ([Oaken page] §3.1 online stage, §3.2.1-3.2.2): per row, outer values
-// (x > T_hi_outer or x < T_lo_outer) leave the dense INT4 body (coded z) and
-// go to the row's sparse list as shifted deltas with a per-group 5-bit scale.
-// One workgroup per (b, h) walks the new rows in tiles of 16, keeping the
-// running entry offset so rowptr stays a prefix sum.
-template <int GE>
+// Oaken (the Oaken page, §3.1 online stage, §3.2.1-3.2.2): per row, outer
+// values (x > T_hi_outer or x < T_lo_outer) leave the dense INT4 body (coded
+// z) and go to the row's sparse list as shifted deltas with a per-group
+// 5-bit scale.  One workgroup per (b, h) walks the new rows in tiles of 16,
+// keeping the running entry offset so rowptr stays a prefix sum.
+template <int GE, bool VL>
 __global__ __launch_bounds__(256) void k_quant_oaken(
     const uint16_t* __restrict__ x, int t_new, int H, int S, const int* __restrict__ pos,
     float t_lo, float t_hi, long long cap, uint8_t* __restrict__ codes, float* __restrict__ scale,
     uint8_t* __restrict__ zero, float* __restrict__ oscale, uint32_t* __restrict__ rowptr,
     uint16_t* __restrict__ sparse, unsigned* __restrict__ status) {
   constexpr int NG = kD / GE, LG = GE / 8;
+  __shared__ uint16_t lrows[VL ? 16 : 1][128];
   const long long bh = blockIdx.x;
   const int b = (int)(bh / H);
   const int p = pos[b];
@@ -278,6 +346,7 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
   unsigned long long base = p == 0 ? 0ull : (unsigned long long)rp[p];
   if (p == 0 && threadIdx.x == 0) rp[0] = 0u;
   const int rl = threadIdx.x >> 4, li = threadIdx.x & 15;
+  uint16_t* lrow = lrows[VL ? rl : 0];
   bool dropped = false;
   for (int t0 = 0; t0 < t_new; t0 += 16) {
     const int t = t0 + rl;
@@ -317,7 +386,7 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
     }
     if (active) {
       const long long dst = bh * S + p + t;
-      store_codes8<4>(codes + dst * 64, li, plo, phi);
+      store_row_codes<4, VL>(codes + dst * 64, li, plo, phi, lrow);
       if (li % LG == 0) {
         scale[dst * NG + li / LG] = s;
         zero[dst * NG + li / LG] = (uint8_t)z;
@@ -355,13 +424,19 @@ constexpr int kThreads = 256;
 // ---------------------------------------------------------------------------
 // Launchers
 
-hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, const uint16_t* x, int t_new,
-                              const int* pos, hipStream_t st) {
+hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
+                              int t_new, const int* pos, hipStream_t st) {
   const long long rows = (long long)c.B * c.H * t_new;
   const dim3 grid((unsigned)((rows + 15) / 16));
-#define KVQ_TOK(BITS, SYM, GE)                                                                 \
-  hipLaunchKernelGGL((k_quant_token<BITS, SYM, GE>), grid, dim3(kThreads), 0, st, x, t_new, c.H, \
-                     c.S, pos, rows, t.codes, t.scale, t.zero, c.status)
+#define KVQ_TOK(BITS, SYM, GE)                                                                      \
+  do {                                                                                              \
+    if (vl)                                                                                         \
+      hipLaunchKernelGGL((k_quant_token<BITS, SYM, GE, true>), grid, dim3(kThreads), 0, st, x,      \
+                         t_new, c.H, c.S, pos, rows, t.codes, t.scale, t.zero, c.status);           \
+    else                                                                                            \
+      hipLaunchKernelGGL((k_quant_token<BITS, SYM, GE, false>), grid, dim3(kThreads), 0, st, x,     \
+                         t_new, c.H, c.S, pos, rows, t.codes, t.scale, t.zero, c.status);           \
+  } while (0)
 #define KVQ_TOK_G(BITS, SYM)                  \
   switch (t.group) {                          \
     case 32: KVQ_TOK(BITS, SYM, 32); break;   \
@@ -404,14 +479,21 @@ hipError_t launch_quant_channel(const CacheArgs& c, const TensorArgs& t, const u
   return hipGetLastError();
 }
 
-hipError_t launch_quant_mixed(const CacheArgs& c, const TensorArgs& t, const uint16_t* x,
+hipError_t launch_quant_mixed(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
                               const int* pos, hipStream_t st) {
   const int C = c.S / c.chunk_tokens;
   const dim3 grid((unsigned)C, (unsigned)(c.B * c.H));
-#define KVQ_MIX(GE)                                                                              \
-  hipLaunchKernelGGL(k_quant_mixed<GE>, grid, dim3(kThreads), 0, st, x, c.H, c.S, c.chunk_tokens, \
-                     C, pos, c.perm, c.seg, t.codes16, t.codes, t.scale, t.zero, t.codes2,       \
-                     t.scale2, t.zero2, c.status)
+#define KVQ_MIX(GE)                                                                                \
+  do {                                                                                             \
+    if (vl)                                                                                        \
+      hipLaunchKernelGGL((k_quant_mixed<GE, true>), grid, dim3(kThreads), 0, st, x, c.H, c.S,      \
+                         c.chunk_tokens, C, pos, c.perm, c.seg, t.codes16, t.codes, t.scale,       \
+                         t.zero, t.codes2, t.scale2, t.zero2, c.status);                           \
+    else                                                                                           \
+      hipLaunchKernelGGL((k_quant_mixed<GE, false>), grid, dim3(kThreads), 0, st, x, c.H, c.S,     \
+                         c.chunk_tokens, C, pos, c.perm, c.seg, t.codes16, t.codes, t.scale,       \
+                         t.zero, t.codes2, t.scale2, t.zero2, c.status);                           \
+  } while (0)
   switch (t.group) {
     case 32: KVQ_MIX(32); break;
     case 64: KVQ_MIX(64); break;
@@ -422,13 +504,20 @@ hipError_t launch_quant_mixed(const CacheArgs& c, const TensorArgs& t, const uin
   return hipGetLastError();
 }
 
-hipError_t launch_quant_oaken(const CacheArgs& c, const TensorArgs& t, const uint16_t* x, int t_new,
-                              const int* pos, hipStream_t st) {
+hipError_t launch_quant_oaken(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
+                              int t_new, const int* pos, hipStream_t st) {
   const dim3 grid((unsigned)(c.B * c.H));
-#define KVQ_OAK(GE)                                                                              \
-  hipLaunchKernelGGL(k_quant_oaken<GE>, grid, dim3(kThreads), 0, st, x, t_new, c.H, c.S, pos,     \
-                     t.thr_lo, t.thr_hi, t.sparse_cap, t.codes, t.scale, t.zero, t.oscale,        \
-                     t.rowptr, t.sparse, c.status)
+#define KVQ_OAK(GE)                                                                               \
+  do {                                                                                            \
+    if (vl)                                                                                       \
+      hipLaunchKernelGGL((k_quant_oaken<GE, true>), grid, dim3(kThreads), 0, st, x, t_new, c.H,    \
+                         c.S, pos, t.thr_lo, t.thr_hi, t.sparse_cap, t.codes, t.scale, t.zero,    \
+                         t.oscale, t.rowptr, t.sparse, c.status);                                 \
+    else                                                                                          \
+      hipLaunchKernelGGL((k_quant_oaken<GE, false>), grid, dim3(kThreads), 0, st, x, t_new, c.H,   \
+                         c.S, pos, t.thr_lo, t.thr_hi, t.sparse_cap, t.codes, t.scale, t.zero,    \
+                         t.oscale, t.rowptr, t.sparse, c.status);                                 \
+  } while (0)
   switch (t.group) {
     case 32: KVQ_OAK(32); break;
     case 64: KVQ_OAK(64); break;

@@ -31,6 +31,37 @@ def unpack_codes(packed: np.ndarray, bits: int, signed: bool = False) -> np.ndar
     return out.reshape(p.shape[:-1] + (p.shape[-1] * (8 // bits),))
 
 
+# Channel order of packed rows (kvq.h).  Unpacking a row naively gives 128
+# elements e[0..127]; e[PERM[c]] is the element of channel c.
+#  K rows: slot 4q + s (elements 8 (4q + s) + v) holds channels 32 s + 8 q + v.
+#  V rows: column word n (elements 8 n + j) holds channels n + 16 j.
+#  fp16 K rows of the chunk-mixed FP16 pool: slot order (0, 4, 1, 5, 2, 6, 3, 7)
+#  inside each slot.
+def _k_perm(order=(0, 1, 2, 3, 4, 5, 6, 7)):
+    perm = np.zeros(128, np.int64)
+    for q in range(4):
+        for s in range(4):
+            for k, v in enumerate(order):
+                perm[32 * s + 8 * q + v] = 8 * (4 * q + s) + k
+    return perm
+
+
+K_PERM = _k_perm()
+K16_PERM = _k_perm((0, 4, 1, 5, 2, 6, 3, 7))
+V_PERM = np.array([8 * (c % 16) + c // 16 for c in range(128)], np.int64)
+
+
+def unpack_layout(packed: np.ndarray, bits: int, layout: str, signed: bool = False) -> np.ndarray:
+    """Packed K or V rows [..., 16 * bits] -> codes in channel order [..., 128]."""
+    e = unpack_codes(packed, bits, signed)
+    return e[..., K_PERM if layout == "K" else V_PERM]
+
+
+def f16_layout(rows_u16: np.ndarray, layout: str) -> np.ndarray:
+    """fp16 rows of the FP16 pool [..., 128] (uint16 bits) -> channel order."""
+    return rows_u16[..., K16_PERM if layout == "K" else V_PERM]
+
+
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     """Inverse of unpack_codes (used only to test the unpacker itself)."""
     c = np.ascontiguousarray(codes).astype(np.uint8)

@@ -148,17 +148,30 @@ def test_entry_point_validation_before_any_launch():
     assert status_of(K.kvq_decode_attn, c, 16, 6, 16, 256, 0.1, 16, None, need, 4, 0) == K.KVQ_ERR_WORKSPACE
 
 
+def workspace_formula(B, Hq, H, qtiles, ns):
+    """Split partials (132 floats per (b, query head, split), 256-byte aligned), then one
+    arrival counter per (b, kv head, query tile)."""
+    part = B * Hq * ns * K.PART_STRIDE * 4
+    return (part + 255) // 256 * 256 + B * H * qtiles * 4
+
+
 def test_workspace_plan():
     c = make_desc(B=16, H=32, S=4160, bits=8, sym=1, group=128)
     for ns in (1, 2, 3, 4, 8, 17):
         n = K.kvq_decode_workspace_bytes(c, 32, 4097, ns)
-        per = 16 * 32 * K.PART_STRIDE * 4
-        assert n % per == 0
-        assert (n // per == 0) if ns == 1 else (1 <= n // per <= ns)
+        if ns == 1:
+            assert n == 0
+            continue
+        assert any(n == workspace_formula(16, 32, 32, 1, s) for s in range(2, ns + 1)), (ns, n)
     assert K.kvq_decode_workspace_bytes(c, 32, 0, 0) == 0
     g = make_desc(B=1, H=8, S=131072, bits=4, k_axis=1, group=64)
     n = K.kvq_decode_workspace_bytes(g, 32, 131072, 0)
-    assert n // (32 * K.PART_STRIDE * 4) >= 64  # long single sequence is split many ways
+    splits = [s for s in range(1, 4097) if n == workspace_formula(1, 32, 8, 1, s)]
+    assert splits and splits[0] >= 64  # long single sequence is split many ways
+    # 16 query heads per kv head -> query tiles of 16
+    g2 = make_desc(B=2, H=2, S=1024, bits=4, group=64)
+    n2 = K.kvq_decode_workspace_bytes(g2, 64, 1024, 3)
+    assert n2 == workspace_formula(2, 64, 2, 2, 3)
 
 
 def test_status_strings():
@@ -232,3 +245,20 @@ def test_cache_bytes_reproduce_page_arithmetic():
     # KVO-LLM page: 2 x 4096 hidden x 4 bytes = 32 KB per token and layer in fp32; the
     # fp16 cache of the same model (32 heads of 128) is half of it per token
     assert 2 * 32 * 128 * 2 == 32 * 1024 // 2
+
+
+def test_row_layout_maps_hand_examples():
+    """Channel -> element index of packed rows, worked by hand from kvq.h."""
+    from kvq_harness import K16_PERM, K_PERM, V_PERM
+    # K: channel 32 s + 8 q + e sits in word 4 q + s, element e
+    assert K_PERM[0] == 0                   # s0 q0 e0 -> word 0
+    assert K_PERM[9] == 8 * 4 + 1           # s0 q1 e1 -> word 4
+    assert K_PERM[40] == 8 * 5 + 0          # s1 q1 e0 -> word 5
+    assert K_PERM[127] == 8 * 15 + 7        # s3 q3 e7 -> word 15
+    assert K_PERM[32] == 8 * 1              # s1 q0 -> word 1
+    # V: channel n + 16 e sits in word n, element e
+    assert V_PERM[17] == 8 * 1 + 1 and V_PERM[15] == 8 * 15 and V_PERM[112] == 7
+    # fp16 K words hold offsets 0, 4, 1, 5, 2, 6, 3, 7
+    assert K16_PERM[4] == 1 and K16_PERM[1] == 2 and K16_PERM[7] == 7
+    for p in (K_PERM, V_PERM, K16_PERM):
+        assert sorted(p) == list(range(128))

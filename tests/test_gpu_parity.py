@@ -11,8 +11,10 @@ import pytest
 
 import oracle
 import synth
-from kvq_harness import (ATTN_BAR, ATTN_TIGHT, host_bytes, i32_device, rel_err_rows, to_device,
-                         unpack_codes)
+from kvq_harness import (ATTN_BAR, ATTN_TIGHT, f16_layout, host_bytes, i32_device, rel_err_rows,
+                         to_device, unpack_layout)
+
+LAYOUT = {"k": "K", "v": "V"}
 
 pytestmark = pytest.mark.gpu
 
@@ -84,7 +86,8 @@ def test_uniform_token(bits, sym, group, G):
     deq = {}
     for name, x in (("k", k), ("v", v)):
         oc, os_, oz = oracle.quant_rows(x, group, bits, bool(sym))
-        got = unpack_codes(dev_u8(cache.buf(name + ".codes"), (B, H, S, RB))[:, :, :T], bits, bool(sym))
+        got = unpack_layout(dev_u8(cache.buf(name + ".codes"), (B, H, S, RB))[:, :, :T], bits, LAYOUT[name],
+                            bool(sym))
         assert np.array_equal(got, oc), name + " codes"
         gs = dev_f32(cache.buf(name + ".scale"), (B, H, S, NG))[:, :, :T]
         assert np.array_equal(f32bits(gs), f32bits(os_)), name + " scales"
@@ -121,7 +124,7 @@ def test_uniform_append_positions():
         expect[1, :, :200] = x[1, :, :200]
         expect[1, :, 100:103] = x[1, :, 200:203]
         oc, os_, oz = oracle.quant_rows(expect, 64, 4)
-        got = unpack_codes(dev_u8(cache.buf(name + ".codes"), (B, H, S, 64)), 4)
+        got = unpack_layout(dev_u8(cache.buf(name + ".codes"), (B, H, S, 64)), 4, LAYOUT[name])
         gs = dev_f32(cache.buf(name + ".scale"), (B, H, S, 2))
         for b, L in enumerate(lens):
             assert np.array_equal(got[b, :, :L], oc[b, :, :L])
@@ -150,13 +153,13 @@ def test_channel_k(bits, G):
     assert cache.flags() == 0
     RB = 128 * bits // 8
     kc, ks, kz = oracle.quant_channel_blocks(k, 64, bits)
-    got = unpack_codes(dev_u8(cache.buf("k.codes"), (B, H, S, RB))[:, :, :T], bits)
+    got = unpack_layout(dev_u8(cache.buf("k.codes"), (B, H, S, RB))[:, :, :T], bits, "K")
     assert np.array_equal(got, kc)
     gs = dev_f32(cache.buf("k.scale"), (B, H, S // 64, 128))[:, :, :T // 64]
     gz = dev_u8(cache.buf("k.zero"), (B, H, S // 64, 128))[:, :, :T // 64]
     assert np.array_equal(f32bits(gs), f32bits(ks)) and np.array_equal(gz, kz)
     vc, vs, vz = oracle.quant_rows(v, 64, bits)
-    gotv = unpack_codes(dev_u8(cache.buf("v.codes"), (B, H, S, RB))[:, :, :T], bits)
+    gotv = unpack_layout(dev_u8(cache.buf("v.codes"), (B, H, S, RB))[:, :, :T], bits, "V")
     assert np.array_equal(gotv, vc)
     kh = oracle.dequant_channel_blocks(kc, ks, kz, 64)
     vh = oracle.dequant_rows(vc, vs, vz, 64)
@@ -211,11 +214,12 @@ def test_chunk_mixed(G, source):
     assert cache.flags() == 0
     # pools: slot j of class c holds the source chunk perm[b][j]
     for name, x in (("k", k), ("v", v)):
-        p16 = host_bytes(cache.buf(name + ".codes16")).view(np.uint16).reshape(B, H, C, CT, 128)
-        p4 = unpack_codes(dev_u8(cache.buf(name + ".codes"), (B, H, C, CT, 64)), 4)
+        p16 = f16_layout(host_bytes(cache.buf(name + ".codes16")).view(np.uint16).reshape(B, H, C, CT, 128),
+                         LAYOUT[name])
+        p4 = unpack_layout(dev_u8(cache.buf(name + ".codes"), (B, H, C, CT, 64)), 4, LAYOUT[name])
         s4 = dev_f32(cache.buf(name + ".scale"), (B, H, C, CT, 4))
         z4 = dev_u8(cache.buf(name + ".zero"), (B, H, C, CT, 4))
-        p2 = unpack_codes(dev_u8(cache.buf(name + ".codes2"), (B, H, C, CT, 32)), 2)
+        p2 = unpack_layout(dev_u8(cache.buf(name + ".codes2"), (B, H, C, CT, 32)), 2, LAYOUT[name])
         s2 = dev_f32(cache.buf(name + ".scale2"), (B, H, C, CT, 4))
         z2 = dev_u8(cache.buf(name + ".zero2"), (B, H, C, CT, 4))
         for b in range(B):
@@ -265,7 +269,7 @@ def oaken_thresholds(w, tensor, samples):
 def check_oaken_tensor(cache, name, x, thr, B, H, S, lens, group=64):
     NG = 128 // group
     oc, os_, oz, oo, oe, on = oracle.oaken_rows(x, thr, group)
-    codes = unpack_codes(dev_u8(cache.buf(name + ".codes"), (B, H, S, 64)), 4)
+    codes = unpack_layout(dev_u8(cache.buf(name + ".codes"), (B, H, S, 64)), 4, LAYOUT[name])
     sc = dev_f32(cache.buf(name + ".scale"), (B, H, S, NG))
     zr = dev_u8(cache.buf(name + ".zero"), (B, H, S, NG))
     osc = dev_f32(cache.buf(name + ".oscale"), (B, H, S, NG))
@@ -359,7 +363,7 @@ def test_edges_empty_single_and_flags():
     K.kvq_quant_append(cache.desc, to_device(k[:, :, :2]), to_device(v[:, :, :2]), 2, i32_device([S - 1] * B))
     torch.cuda.synchronize()
     assert cache.flags() & K.KVQ_FLAG_POS_RANGE
-    got = dev_u8(cache.buf("k.codes"), (B, H, S, 128)).view(np.int8)
+    got = unpack_layout(dev_u8(cache.buf("k.codes"), (B, H, S, 128)), 8, "K", signed=True)
     assert np.array_equal(got[:, :, S - 1], oc_k[:, :, 0])
 
 
