@@ -204,12 +204,9 @@ kvq_status kvq_reorder_chunks(const kvq_cache* c, const uint8_t* chunk_bits, int
 
 /*
  * Workspace needed by kvq_decode_attn for the same (c, q_heads, max_len,
- * num_splits); 0 when the chosen split count is 1.  Host only.
- * The workspace holds the split partials followed by one uint32 arrival
- * counter per (batch, kv head, query tile).  The counters must be zero when
- * a call is enqueued; every completed call leaves them zero again, so
- * zero-fill a workspace once after allocating it.  One workspace serves one
- * call at a time (calls on different streams need their own).
+ * num_splits); 0 when the chosen split count is 1.  Host only.  The
+ * workspace holds the split partials (m, l, unnormalized output per batch,
+ * query head and split); one workspace serves one call at a time.
  */
 kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32_t max_len,
                                       int32_t num_splits, size_t* bytes);
@@ -220,8 +217,7 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32
  * dequantization inside the attention product, no separate pass).  The
  * sequence is split across workgroups and the partial results are merged
  * with the log-sum-exp rule ([Cocktail] §3.2.3: per-block attention whose
- * merge equals ordinary attention) by the last workgroup of each
- * (batch, kv head, query tile) to finish, inside the same kernel launch.
+ * merge equals ordinary attention) by a second, small kernel.
  *  q:        device fp16 [batch][q_heads][128]; q_heads a multiple of
  *            kv_heads; query head h reads KV head h / (q_heads / kv_heads).
  *  seq_len:  device int32 [batch], tokens 0 .. seq_len[b]-1 are attended

@@ -59,8 +59,7 @@ class QuantKVCache:
 
     def workspace(self, q_heads: int, max_len: int, num_splits: int = 0):
         n = kvq_decode_workspace_bytes(self.desc, q_heads, max_len, num_splits)
-        # zero-filled: the arrival counters at the end of the workspace start at zero
-        ws = self.torch.zeros(max(n, 16), dtype=self.torch.uint8, device=self.status.device)
+        ws = self.torch.empty(max(n, 16), dtype=self.torch.uint8, device=self.status.device)
         return ws, n
 
     def flags(self) -> int:

@@ -170,8 +170,12 @@ CacheArgs cache_args(const kvq_cache* c) {
 
 kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
-// Workgroups to aim for: several per compute unit on a 256-CU part.
-constexpr long long kTargetGroups = 2048;
+// Split planning.  One workgroup (4 waves) per (b, kv head, query tile)
+// already fills the GPU when there are at least kWideUnits of them; fewer
+// units are split along the sequence towards kTargetGroups workgroups, and
+// the partials merged by a second kernel.
+constexpr long long kWideUnits = 384;
+constexpr long long kTargetGroups = 1024;
 
 struct Plan {
   int G, qr, qtiles, num_splits, split_len;
@@ -203,7 +207,7 @@ kvq_status plan_decode(const kvq_cache* c, int q_heads, int max_len, int num_spl
   }
   long long ns = num_splits;
   if (ns == 0) {
-    ns = (kTargetGroups + units - 1) / units;
+    ns = units >= kWideUnits ? 1 : (kTargetGroups + units - 1) / units;
     const long long most = (length + min_piece - 1) / min_piece;
     if (ns > most) ns = most;
   }
@@ -218,15 +222,9 @@ kvq_status plan_decode(const kvq_cache* c, int q_heads, int max_len, int num_spl
   return KVQ_OK;
 }
 
-// Split partials, then the arrival counters (256-byte aligned).
-size_t partials_bytes(const kvq_cache* c, int q_heads, const Plan& p) {
-  const size_t n = (size_t)c->batch * (size_t)q_heads * (size_t)p.num_splits * kvq::kPartStride * 4;
-  return (n + 255) / 256 * 256;
-}
-
 size_t workspace_for(const kvq_cache* c, int q_heads, const Plan& p) {
   if (p.num_splits <= 1) return 0;
-  return partials_bytes(c, q_heads, p) + (size_t)c->batch * c->kv_heads * p.qtiles * 4;
+  return (size_t)c->batch * (size_t)q_heads * (size_t)p.num_splits * kvq::kPartStride * sizeof(float);
 }
 
 }  // namespace
@@ -346,9 +344,6 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t q_heads, c
   d.qscale = sm_scale * 1.4426950408889634f;
   d.out = out;
   d.ws = static_cast<float*>(need ? workspace : nullptr);
-  d.counters = need ? reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
-                                                   partials_bytes(c, q_heads, p))
-                    : nullptr;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (c->mode) {
@@ -357,6 +352,8 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t q_heads, c
     default: e = kvq::launch_decode_mixed(a, d, st); break;
   }
   if (e == hipErrorInvalidValue) return KVQ_ERR_UNSUPPORTED;
+  if (e != hipSuccess) return KVQ_ERR_HIP;
+  if (p.num_splits > 1) e = kvq::launch_merge(d, c->batch, st);
   return from_hip(e);
 }
 

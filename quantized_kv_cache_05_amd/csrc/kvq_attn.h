@@ -254,7 +254,6 @@ struct AttnParams {
   const int* seq_len;
   float* out;
   float* ws;           // split partials [B][Hq][num_splits][kPartStride]
-  unsigned* counters;  // [B][H][qtiles] arrival counters (zero between calls)
   const int* seg;
   unsigned* status;
   TensorArgs k, v;

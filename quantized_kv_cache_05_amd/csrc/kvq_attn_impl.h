@@ -36,7 +36,6 @@ struct AttnLds {
     Wave wave[kNW];
     Rec rec[kNW];
   } u;
-  int last;
 };
 
 // Meta of the two tokens of a lane's score column (token nb*16 + n16).
@@ -429,14 +428,13 @@ __device__ __forceinline__ void wave_record(LDS& L, SoftState<QRows<QR>::GI>& st
   }
 }
 
-// Merge the four wave records of each query; write the output (one split)
-// or the split partial, and let the last-arriving workgroup of the
-// (b, kv head, query tile) merge all partials (log-sum-exp rule).
+// Merge the four wave records of each query and write the output (one
+// split) or the split partial (m, l, unnormalized output) for k_merge.
 template <class LDS>
 __device__ __forceinline__ void finish_split(const AttnParams& P, LDS& L, int b, int kvh, int qt,
                                              int split, int nq) {
   __syncthreads();
-  const long long hq0 = (long long)kvh * P.G + (long long)qt * 16;
+  const long long hq0 = (long long)kvh * P.G + (long long)qt * LDS::R;
   for (int idx = threadIdx.x; idx < nq * 128; idx += blockDim.x) {
     const int m = idx >> 7, d = idx & 127;
     float M = -INFINITY;
@@ -466,34 +464,6 @@ __device__ __forceinline__ void finish_split(const AttnParams& P, LDS& L, int b,
       }
     }
   }
-  if (P.num_splits == 1) return;
-  __threadfence();
-  __syncthreads();
-  unsigned* cnt = P.counters + ((long long)b * P.H + kvh) * P.qtiles + qt;
-  if (threadIdx.x == 0) L.last = atomicAdd(cnt, 1u) == (unsigned)(P.num_splits - 1);
-  __syncthreads();
-  if (!L.last) return;
-  __threadfence();
-  for (int idx = threadIdx.x; idx < nq * 128; idx += blockDim.x) {
-    const int m = idx >> 7, d = idx & 127;
-    const float* r0 = P.ws + (((long long)b * P.Hq + hq0 + m) * P.num_splits) * kPartStride;
-    float M = -INFINITY;
-    for (int s = 0; s < P.num_splits; ++s) M = fmaxf(M, r0[(long long)s * kPartStride]);
-    float Ls = 0.0f, O = 0.0f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < P.num_splits; ++s) {
-        const float* r = r0 + (long long)s * kPartStride;
-        const float ms = r[0];
-        if (ms != -INFINITY) {
-          const float f = fexp2(ms - M);
-          Ls = fmaf(f, r[1], Ls);
-          O = fmaf(f, r[4 + d], O);
-        }
-      }
-    }
-    P.out[((long long)b * P.Hq + hq0 + m) * 128 + d] = Ls > 0.0f ? O / Ls : 0.0f;
-  }
-  if (threadIdx.x == 0) *cnt = 0u;
 }
 
 // Workgroup prologue: the query tile in LDS, per-group query sums, the K
@@ -505,7 +475,7 @@ __device__ __forceinline__ void attn_prologue(const AttnParams& P, LDS& L, int b
   for (int idx = threadIdx.x; idx < R * 128; idx += blockDim.x) {
     const int m = idx >> 7, d = idx & 127;
     float v = 0.0f;
-    if (m < nq) v = h2f(P.q[((long long)b * P.Hq + (long long)kvh * P.G + (long long)qt * 16 + m) * 128 + d]);
+    if (m < nq) v = h2f(P.q[((long long)b * P.Hq + (long long)kvh * P.G + (long long)qt * QR + m) * 128 + d]);
     L.q[m][d] = v;
   }
   for (int idx = threadIdx.x; idx < (int)(sizeof(L.u) / 4); idx += blockDim.x)

@@ -92,7 +92,7 @@ AttnParams make_attn_params(const CacheArgs& c, const DecodeLaunch& d) {
   P.B = c.B; P.H = c.H; P.S = c.S; P.Hq = d.Hq; P.G = d.G; P.qtiles = d.qtiles;
   P.max_len = d.max_len; P.num_splits = d.num_splits; P.split_len = d.split_len;
   P.chunk_tokens = c.chunk_tokens; P.qscale = d.qscale; P.q = d.q; P.seq_len = d.seq_len;
-  P.out = d.out; P.ws = d.ws; P.counters = d.counters; P.seg = c.seg; P.status = c.status;
+  P.out = d.out; P.ws = d.ws; P.seg = c.seg; P.status = c.status;
   P.k = c.k; P.v = c.v;
   return P;
 }
@@ -106,6 +106,34 @@ bool decode_uniform_supported(const TensorArgs& k, const TensorArgs& v) {
   if (k.axis == 0) return k.group == v.group;
   if (k.axis == 1) return k.group == 64 && !k.sym && (k.bits == 8 || k.bits == 4);
   return false;
+}
+
+// Log-sum-exp merge of split partials: one workgroup of 128 threads per
+// (b, query head): M = max m_j, L = sum l_j 2^(m_j - M), out = sum 2^(m_j - M) o_j / L.
+__global__ __launch_bounds__(128) void k_merge(const float* __restrict__ ws, int NS,
+                                              float* __restrict__ out) {
+  const long long bq = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* rec0 = ws + bq * NS * kPartStride;
+  float M = -INFINITY;
+  for (int s = 0; s < NS; ++s) M = fmaxf(M, rec0[(long long)s * kPartStride]);
+  float L = 0.0f, O = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < NS; ++s) {
+      const float* rec = rec0 + (long long)s * kPartStride;
+      if (rec[0] != -INFINITY) {
+        const float f = fexp2(rec[0] - M);
+        L = fmaf(f, rec[1], L);
+        O = fmaf(f, rec[4 + d], O);
+      }
+    }
+  }
+  out[bq * kD + d] = L > 0.0f ? O / L : 0.0f;
+}
+
+hipError_t launch_merge(const DecodeLaunch& d, int B, hipStream_t st) {
+  hipLaunchKernelGGL(k_merge, dim3((unsigned)(B * d.Hq)), dim3(kD), 0, st, d.ws, d.num_splits, d.out);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_uniform(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st) {

@@ -53,8 +53,7 @@ struct DecodeLaunch {
   int split_len; // tokens (UNIFORM/OAKEN) or chunk slots (CHUNK_MIXED) per split
   float qscale;  // sm_scale * log2(e)
   float* out;
-  float* ws;           // split partials, null when num_splits == 1
-  unsigned* counters;  // arrival counters [B][H][qtiles], null when num_splits == 1
+  float* ws;     // split partials, null when num_splits == 1
 };
 
 // vl: write the V row layout (else the K row layout), see kvq.h.
@@ -84,6 +83,8 @@ hipError_t launch_percentiles(const unsigned long long* hist, const PercentileLi
 hipError_t launch_decode_uniform(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
 hipError_t launch_decode_oaken(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
 hipError_t launch_decode_mixed(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
+// log-sum-exp merge of the split partials into the output
+hipError_t launch_merge(const DecodeLaunch& d, int B, hipStream_t st);
 
 // True when a uniform (K, V) pair has a compiled decode kernel.
 bool decode_uniform_supported(const TensorArgs& k, const TensorArgs& v);
