@@ -215,6 +215,11 @@ kvq_status plan_decode(const kvq_cache* c, int q_heads, int max_len, int num_spl
   if (ns > length) ns = length;
   long long piece = (length + ns - 1) / ns;
   piece = (piece + align - 1) / align * align;
+  if (c->mode == KVQ_MODE_OAKEN) {
+    // the Oaken kernel keeps one score slot per (query, token) of a split in LDS
+    const long long most = kvq::oaken_max_split(p->qr);
+    if (piece > most) piece = most;
+  }
   ns = (length + piece - 1) / piece;
   if (ns > 65535) return KVQ_ERR_UNSUPPORTED;
   p->num_splits = (int)ns;

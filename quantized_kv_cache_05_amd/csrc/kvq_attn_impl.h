@@ -16,18 +16,13 @@ struct QRows {
 
 // Workgroup-shared LDS: the query tile, per-group query sums, and a per-wave
 // scratch area that the epilogue reuses for the wave records.
-template <int QR, int NGV, bool OAK>
+template <int QR, int NGV>
 struct AttnLds {
   static constexpr int R = QR;
   float q[R][128];       // query tile (fp16 values in binary32)
   float qg[R][4];        // sum of the query over each K channel group
   struct __attribute__((aligned(16))) Wave {
     unsigned short w[NGV][2][R][kTile];  // softmax weights hi / lo, [V group][query][token]
-    float sp_sc[OAK ? R : 1][kTile];
-    float sp_p[OAK ? R : 1][kTile];
-    float sp_o[OAK ? R : 1][128];
-    float sp_alpha[OAK ? R : 1];
-    unsigned sp_rp[OAK ? kTile + 1 : 1];
   };
   struct Rec {
     float o[R][128 + 2];  // per query: output sum, then m, l
@@ -80,36 +75,6 @@ __device__ __forceinline__ float max16(float v) {
   return v;
 }
 
-// Oaken sparse entries of tile rows [ra, rb) (relative to the tile start
-// `tile`): calls f(entry lane's row r in the tile, channel idx, x_hat) for
-// every entry, 64 entries per pass; rows come from a binary search over the
-// tile's row pointers staged in LDS.
-template <class F>
-__device__ __forceinline__ void for_tile_entries(const SparseView& sv, int ng, long long tile, int ra,
-                                                 int rb, unsigned* sp_rp, int lane, F&& f) {
-  if (lane <= kTile) sp_rp[lane] = sv.rowptr[tile + lane];
-  wave_lds_sync();
-  const unsigned e0 = sp_rp[ra], e1 = min(sp_rp[rb], sv.cap);
-  for (unsigned base = e0; base < e1; base += 64) {
-    const unsigned e = base + lane;
-    if (e < e1) {
-      // last row r in [ra, rb) with rp[r] <= e
-      int lo = ra, hi = rb - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (sp_rp[mid] <= e) lo = mid; else hi = mid - 1;
-      }
-      const unsigned en = sv.sparse[e];
-      const int idx = (int)(en & 127u);
-      const float mag = (float)((en >> 8) & 31u);
-      const float so = sv.oscale[(tile + lo) * ng + idx / (128 / ng)];
-      const float xh = ((en >> 7) & 1u) ? sv.t_hi + mag * so : sv.t_lo - mag * so;
-      f(lo, idx, xh);
-    }
-  }
-  wave_lds_sync();
-}
-
 // ---------------------------------------------------------------------------
 // One wave's share of a token range [t0, t1) of one (b, kv head): tiles of 32
 // tokens starting at tile-aligned offsets, taken round robin by the waves in
@@ -117,13 +82,15 @@ __device__ __forceinline__ void for_tile_entries(const SparseView& sv, int ng, l
 //
 //  KC / VC: codecs.  NGK / NGV: channel groups of K / V (token axis).
 //  CHANK: K has channel-axis groups of 64 tokens (scale folded into the query).
-//  OAK: Oaken sparse side lists for K and V.
+//  OAK: Oaken; oak_sc[m * oak_span + (t - t0)] holds the sparse outer-value
+//       part of query m's score for token t on entry and receives the final
+//       base-2 score (the V outer values are added after the loop).
 template <int QR, int NGK, int NGV, class KC, class VC, bool CHANK, bool OAK, int TPS, class LDS>
 __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
                                             SoftState<QRows<QR>::GI>& st, const TokView& kv,
-                                            const TokView& vv, const ChanView& kc,
-                                            const SparseView& ks, const SparseView& vs, int nq,
-                                            int t0, int t1, int wave, const u4_t (&qop)[4]) {
+                                            const TokView& vv, const ChanView& kc, float* oak_sc,
+                                            int oak_span, int nq, int t0, int t1, int wave,
+                                            const u4_t (&qop)[4]) {
   constexpr int R = QR, GI = QRows<QR>::GI;
   static_assert(LDS::R == QR, "LDS tables sized for QR query rows");
   const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
@@ -251,21 +218,16 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
           }
         }
       }
-      // ---- Oaken: outer K values add q[idx] * x_hat to their token's score ----
+      // ---- Oaken: the outer K values' share of the score (pre-pass) ----
       if constexpr (OAK) {
-        const int ra = max(t0 - tile, 0), rb = min(t1 - tile, kTile);
-        for_tile_entries(ks, NGK, tile, ra, rb, W.sp_rp, lane, [&](int r, int idx, float xh) {
-          for (int m = 0; m < nq; ++m) atomicAdd(&W.sp_sc[m][r], L.q[m][idx] * xh);
-        });
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
           for (int i = 0; i < GI; ++i) {
             const int m = GI == 1 ? 0 : 4 * q4 + i;
-            if (m < nq) sc[nb][i] = fmaf(W.sp_sc[m][nb * 16 + n16], P.qscale, sc[nb][i]);
+            const int t = tile + nb * 16 + n16;
+            if (ok[nb] && m < nq) sc[nb][i] = fmaf(oak_sc[m * oak_span + (t - t0)], P.qscale, sc[nb][i]);
           }
-        wave_lds_sync();
-        for (int idx = lane; idx < R * kTile; idx += 64) (&W.sp_sc[0][0])[idx] = 0.0f;
       }
       // ---- online softmax (base 2) ----
       float alpha[GI];
@@ -291,17 +253,6 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
 #pragma unroll
           for (int j = 0; j < 8; ++j) st.o[j][i] *= a;
         }
-        if constexpr (OAK) {
-          if (n16 == 0) {
-#pragma unroll
-            for (int i = 0; i < GI; ++i) {
-              const int m = GI == 1 ? 0 : 4 * q4 + i;
-              if (m < R) W.sp_alpha[m] = alpha[i];
-            }
-          }
-          wave_lds_sync();
-          for (int idx = lane; idx < nq * 128; idx += 64) (&W.sp_o[0][0])[idx] *= W.sp_alpha[idx >> 7];
-        }
       }
       float p[2][GI];
 #pragma unroll
@@ -311,20 +262,16 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
           p[nb][i] = ok[nb] ? fexp2(sc[nb][i] - st.m[i]) : 0.0f;
           st.l[i] += p[nb][i];
         }
-      // ---- Oaken: outer V values add p * x_hat to their channel ----
+      // ---- Oaken: keep the final scores for the V outer values (post-pass) ----
       if constexpr (OAK) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
           for (int i = 0; i < GI; ++i) {
             const int m = GI == 1 ? 0 : 4 * q4 + i;
-            if ((GI != 1 || q4 == 0) && m < R) W.sp_p[m][nb * 16 + n16] = p[nb][i];
+            const int t = tile + nb * 16 + n16;
+            if (ok[nb] && m < nq && (GI != 1 || q4 == 0)) oak_sc[m * oak_span + (t - t0)] = sc[nb][i];
           }
-        wave_lds_sync();
-        const int ra = max(t0 - tile, 0), rb = min(t1 - tile, kTile);
-        for_tile_entries(vs, NGV, tile, ra, rb, W.sp_rp, lane, [&](int r, int idx, float xh) {
-          for (int m = 0; m < nq; ++m) atomicAdd(&W.sp_o[m][idx], W.sp_p[m][r] * xh);
-        });
       }
       // ---- weights p * s_v (binary32) -> fp16 hi / lo in LDS, V bias ----
 #pragma unroll
@@ -387,7 +334,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
 
 // Fold the wave's state into its record (sum over the 16 token columns,
 // V bias and sparse V values applied).  Caller: all waves, after a barrier.
-template <int QR, int NGV, bool OAK, class LDS>
+template <int QR, int NGV, class LDS>
 __device__ __forceinline__ void wave_record(LDS& L, SoftState<QRows<QR>::GI>& st, int wave, int nq) {
   constexpr int GI = QRows<QR>::GI;
   const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
@@ -398,16 +345,6 @@ __device__ __forceinline__ void wave_record(LDS& L, SoftState<QRows<QR>::GI>& st
 #pragma unroll
     for (int g = 0; g < NGV; ++g) vbt[i][g] = sum16(st.vb[i][g]);
   }
-  float spo[GI][8];
-  if constexpr (OAK) {
-    // copy the sparse V accumulators out before the records overwrite them
-#pragma unroll
-    for (int i = 0; i < GI; ++i) {
-      const int m = GI == 1 ? 0 : 4 * q4 + i;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) spo[i][j] = m < nq ? L.u.wave[wave].sp_o[m][16 * j + n16] : 0.0f;
-    }
-  }
   __syncthreads();
   auto& rec = L.u.rec[wave];
 #pragma unroll
@@ -417,9 +354,7 @@ __device__ __forceinline__ void wave_record(LDS& L, SoftState<QRows<QR>::GI>& st
     if (m >= nq) continue;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float o = st.o[j][i] - vbt[i][j / (8 / NGV)];
-      if constexpr (OAK) o += spo[i][j];
-      rec.o[m][16 * j + n16] = o;
+      rec.o[m][16 * j + n16] = st.o[j][i] - vbt[i][j / (8 / NGV)];
     }
     if (n16 == 0) {
       rec.o[m][128] = st.m[i];
@@ -430,16 +365,16 @@ __device__ __forceinline__ void wave_record(LDS& L, SoftState<QRows<QR>::GI>& st
 
 // Merge the four wave records of each query and write the output (one
 // split) or the split partial (m, l, unnormalized output) for k_merge.
-template <class LDS>
+// extra(m, d, M) may add a term to the unnormalized output of query m,
+// channel d, in the frame of the workgroup maximum M.
+template <class LDS, class Extra>
 __device__ __forceinline__ void finish_split(const AttnParams& P, LDS& L, int b, int kvh, int qt,
-                                             int split, int nq) {
+                                             int split, int nq, Extra&& extra) {
   __syncthreads();
   const long long hq0 = (long long)kvh * P.G + (long long)qt * LDS::R;
   for (int idx = threadIdx.x; idx < nq * 128; idx += blockDim.x) {
     const int m = idx >> 7, d = idx & 127;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) M = fmaxf(M, L.u.rec[w].o[m][128]);
+    const float M = wg_max(L, m);
     float Ls = 0.0f, O = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
@@ -451,6 +386,7 @@ __device__ __forceinline__ void finish_split(const AttnParams& P, LDS& L, int b,
           O = fmaf(f, L.u.rec[w].o[m][d], O);
         }
       }
+      O += extra(m, d, M);
     }
     const long long hq = hq0 + m;
     if (P.num_splits == 1) {
@@ -464,6 +400,21 @@ __device__ __forceinline__ void finish_split(const AttnParams& P, LDS& L, int b,
       }
     }
   }
+}
+
+template <class LDS>
+__device__ __forceinline__ void finish_split(const AttnParams& P, LDS& L, int b, int kvh, int qt,
+                                             int split, int nq) {
+  finish_split(P, L, b, kvh, qt, split, nq, [](int, int, float) { return 0.0f; });
+}
+
+// Maximum of query m's running maxima over the four wave records.
+template <class LDS>
+__device__ __forceinline__ float wg_max(const LDS& L, int m) {
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) M = fmaxf(M, L.u.rec[w].o[m][128]);
+  return M;
 }
 
 // Workgroup prologue: the query tile in LDS, per-group query sums, the K

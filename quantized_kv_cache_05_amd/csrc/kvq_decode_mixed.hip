@@ -10,7 +10,7 @@ namespace {
 
 template <int QR, int NG>
 __global__ __launch_bounds__(256) void k_attn_mixed(AttnParams P) {
-  __shared__ AttnLds<QR, NG, false> L;
+  __shared__ AttnLds<QR, NG> L;
   const int split = blockIdx.x, qt = blockIdx.y % P.qtiles, kvh = blockIdx.y / P.qtiles, b = blockIdx.z;
   const int wave = threadIdx.x >> 6;
   const int nq = min(QR, P.G - qt * QR);
@@ -28,13 +28,12 @@ __global__ __launch_bounds__(256) void k_attn_mixed(AttnParams P) {
   SoftState<QRows<QR>::GI> st;
   soft_init(st);
   const ChanView nc{nullptr, nullptr};
-  const SparseView none{};
   {
     const int a = max(j0, 0), e = min(j1, n16);
     if (a < e) {
       const TokView k16{P.k.codes16 + bh * S * KF16::RB, nullptr, nullptr};
       const TokView v16{P.v.codes16 + bh * S * VF16::RB, nullptr, nullptr};
-      attend_wave<QR, 1, 1, KF16, VF16, false, false, 1>(P, L, st, k16, v16, nc, none, none, nq,
+      attend_wave<QR, 1, 1, KF16, VF16, false, false, 1>(P, L, st, k16, v16, nc, nullptr, 0, nq,
                                                           a * CT, e * CT, wave, qop);
     }
   }
@@ -43,7 +42,7 @@ __global__ __launch_bounds__(256) void k_attn_mixed(AttnParams P) {
     if (a < e) {
       const TokView k4{P.k.codes + bh * S * KI4::RB, P.k.scale + bh * S * NG, P.k.zero + bh * S * NG};
       const TokView v4{P.v.codes + bh * S * VI4::RB, P.v.scale + bh * S * NG, P.v.zero + bh * S * NG};
-      attend_wave<QR, NG, NG, KI4, VI4, false, false, 1>(P, L, st, k4, v4, nc, none, none, nq,
+      attend_wave<QR, NG, NG, KI4, VI4, false, false, 1>(P, L, st, k4, v4, nc, nullptr, 0, nq,
                                                           (a - n16) * CT, (e - n16) * CT, wave, qop);
     }
   }
@@ -52,12 +51,12 @@ __global__ __launch_bounds__(256) void k_attn_mixed(AttnParams P) {
     if (a < e) {
       const TokView k2{P.k.codes2 + bh * S * KI2::RB, P.k.scale2 + bh * S * NG, P.k.zero2 + bh * S * NG};
       const TokView v2{P.v.codes2 + bh * S * VI2::RB, P.v.scale2 + bh * S * NG, P.v.zero2 + bh * S * NG};
-      attend_wave<QR, NG, NG, KI2, VI2, false, false, 1>(P, L, st, k2, v2, nc, none, none, nq,
+      attend_wave<QR, NG, NG, KI2, VI2, false, false, 1>(P, L, st, k2, v2, nc, nullptr, 0, nq,
                                                           (a - n16 - n4) * CT, (e - n16 - n4) * CT,
                                                           wave, qop);
     }
   }
-  wave_record<QR, NG, false>(L, st, wave, nq);
+  wave_record<QR, NG>(L, st, wave, nq);
   finish_split(P, L, b, kvh, qt, split, nq);
 }
 

@@ -1,13 +1,21 @@
-// Decode kernels for the Oaken cache: the dense INT4 body goes through the
-// matrix cores like any token-axis group; each row's sparse outer entries add
-// q[idx] * x_hat to the row's score and p * x_hat to output channel idx (LDS
-// accumulators rescaled with the running maximum).  Reconstruction follows
-// the Oaken page, §3.2.2: x_hat = T_hi + mag * s_out above, T_lo - mag * s_out
-// below; the dense value at an outer position is exactly 0.
+// Decode kernels for the Oaken cache.  The dense INT4 body goes through the
+// matrix-core tile loop like any token-axis group; the sparse outer values
+// are handled in bulk around it (reconstruction from the Oaken page, §3.2.2:
+// x_hat = T_hi + mag * s_out above the upper outer threshold, T_lo - mag *
+// s_out below the lower one; the dense value at an outer position is 0):
+//  - K pre-pass: every outer K entry of the split adds q[m][idx] * x_hat to
+//    query m's score slot of its token (LDS);
+//  - tile loop: the slot is added to the dense score and replaced by the
+//    final base-2 score;
+//  - V post-pass: with the workgroup maximum M known, every outer V entry
+//    adds 2^(score - M) * x_hat to output channel idx of query m (LDS).
+// One lane per row walks the row's entries (row pointers staged in LDS).
 #include "kvq_attn_impl.h"
 
 namespace kvq {
 namespace {
+
+constexpr int kOakSpan = 2048;  // query x token score slots per workgroup
 
 __device__ __forceinline__ SparseView make_sparse(const TensorArgs& t, long long bh, long long S, int ng) {
   SparseView v;
@@ -20,9 +28,80 @@ __device__ __forceinline__ SparseView make_sparse(const TensorArgs& t, long long
   return v;
 }
 
+struct OakLds {
+  unsigned rp[kOakSpan + 1];  // row pointers of the split's rows (K, then V)
+  float sc[kOakSpan];         // [query][token] score slots
+};
+
+// Stage the row pointers of rows t0 .. t0 + n of one tensor; ends with a barrier.
+__device__ __forceinline__ void stage_rowptr(const SparseView& sv, int t0, int n, unsigned* rp) {
+  for (int i = threadIdx.x; i <= n; i += blockDim.x) rp[i] = sv.rowptr[t0 + i];
+  __syncthreads();
+}
+
+// The outer scales of one row (one per channel group).
+template <int NG>
+__device__ __forceinline__ void row_oscale(const SparseView& sv, long long row, float (&so)[NG]) {
+  if constexpr (NG == 1) {
+    so[0] = sv.oscale[row];
+  } else if constexpr (NG == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(sv.oscale + row * 2);
+    so[0] = v.x; so[1] = v.y;
+  } else {
+    const float4 v = *reinterpret_cast<const float4*>(sv.oscale + row * 4);
+    so[0] = v.x; so[1] = v.y; so[2] = v.z; so[3] = v.w;
+  }
+}
+
+// One lane per row of the split: f(lane's row r, channel idx, x_hat) for each
+// of its entries, four entry loads in flight at a time.  begin(r) is called
+// first for each valid row (and the wave), end(r) after its entries.
+template <int NG, class B, class F, class E>
+__device__ __forceinline__ void for_row_entries(const SparseView& sv, int t0, int n,
+                                                const unsigned* rp, B&& begin, F&& f, E&& end) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r0 = wave * 64; r0 < n; r0 += kNW * 64) {
+    const int r = r0 + lane;
+    const bool valid = r < n;
+    unsigned a = 0, c = 0;
+    float so[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) so[g] = 0.0f;
+    if (valid) {
+      a = min(rp[r], sv.cap);
+      c = min(rp[r + 1], sv.cap) - a;
+      row_oscale<NG>(sv, t0 + r, so);
+      begin(r);
+    }
+    for (unsigned j = 0; __any(j < c); j += 4) {
+      unsigned en[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) en[k] = j + k < c ? (unsigned)sv.sparse[a + j + k] : 0u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (j + k < c) {
+          const int idx = (int)(en[k] & 127u);
+          const float mag = (float)((en[k] >> 8) & 31u);
+          float s = so[0];
+#pragma unroll
+          for (int g = 1; g < NG; ++g)
+            if (idx >= g * (128 / NG)) s = so[g];
+          const float xh = ((en[k] >> 7) & 1u) ? sv.t_hi + mag * s : sv.t_lo - mag * s;
+          f(r, idx, xh);
+        }
+      }
+    }
+    if (valid) end(r);
+  }
+}
+
 template <int QR, int NG>
 __global__ __launch_bounds__(256) void k_attn_oaken(AttnParams P) {
-  __shared__ AttnLds<QR, NG, true> L;
+  __shared__ AttnLds<QR, NG> L;
+  __shared__ OakLds OL;
+  __shared__ float osp[QR][128];
+  __shared__ float mwg[QR];
+  constexpr int span = kOakSpan / QR;
   const int split = blockIdx.x, qt = blockIdx.y % P.qtiles, kvh = blockIdx.y / P.qtiles, b = blockIdx.z;
   const int wave = threadIdx.x >> 6;
   const int nq = min(QR, P.G - qt * QR);
@@ -31,20 +110,66 @@ __global__ __launch_bounds__(256) void k_attn_oaken(AttnParams P) {
   const int len = clamp_seq_len(P, b, split == 0 && blockIdx.y == 0 && threadIdx.x == 0);
   const int t0 = split * P.split_len;
   const int t1 = min(len, t0 + P.split_len);
+  const int n = t1 - t0;  // <= span (split planning)
+  const long long bh = (long long)b * P.H + kvh;
+  const long long S = P.S;
+  const SparseView ks = make_sparse(P.k, bh, S, NG), vs = make_sparse(P.v, bh, S, NG);
   SoftState<QRows<QR>::GI> st;
   soft_init(st);
-  if (t0 < t1) {
-    const long long bh = (long long)b * P.H + kvh;
-    const long long S = P.S;
+  if (n > 0) {
+    // K pre-pass: each lane sums its row's outer K contributions per query
+    stage_rowptr(ks, t0, n, OL.rp);
+    {
+      float acc[QR];
+      for_row_entries<NG>(
+          ks, t0, n, OL.rp,
+          [&](int) {
+#pragma unroll
+            for (int m = 0; m < QR; ++m) acc[m] = 0.0f;
+          },
+          [&](int, int idx, float xh) {
+#pragma unroll
+            for (int m = 0; m < QR; ++m)
+              if (m < nq) acc[m] = fmaf(L.q[m][idx], xh, acc[m]);
+          },
+          [&](int r) {
+#pragma unroll
+            for (int m = 0; m < QR; ++m)
+              if (m < nq) OL.sc[m * span + r] = acc[m];
+          });
+    }
+    __syncthreads();
     const TokView kv{P.k.codes + bh * S * KI4::RB, P.k.scale + bh * S * NG, P.k.zero + bh * S * NG};
     const TokView vv{P.v.codes + bh * S * VI4::RB, P.v.scale + bh * S * NG, P.v.zero + bh * S * NG};
     const ChanView nc{nullptr, nullptr};
-    const SparseView ks = make_sparse(P.k, bh, S, NG), vs = make_sparse(P.v, bh, S, NG);
-    attend_wave<QR, NG, NG, KI4, VI4, false, true, 2>(P, L, st, kv, vv, nc, ks, vs, nq, t0, t1, wave,
-                                                       qop);
+    attend_wave<QR, NG, NG, KI4, VI4, false, true, 2>(P, L, st, kv, vv, nc, OL.sc, span, nq, t0, t1,
+                                                       wave, qop);
   }
-  wave_record<QR, NG, true>(L, st, wave, nq);
-  finish_split(P, L, b, kvh, qt, split, nq);
+  wave_record<QR, NG>(L, st, wave, nq);
+  __syncthreads();
+  // V post-pass in the frame of the workgroup maximum
+  for (int i = threadIdx.x; i < QR * 128; i += blockDim.x) (&osp[0][0])[i] = 0.0f;
+  if (threadIdx.x < nq) mwg[threadIdx.x] = wg_max(L, threadIdx.x);
+  if (n > 0) {
+    stage_rowptr(vs, t0, n, OL.rp);  // (barrier inside)
+    float pr[QR];
+    for_row_entries<NG>(
+        vs, t0, n, OL.rp,
+        [&](int r) {
+#pragma unroll
+          for (int m = 0; m < QR; ++m) {
+            const float s = m < nq ? OL.sc[m * span + r] : -INFINITY;
+            pr[m] = s == -INFINITY ? 0.0f : fexp2(s - mwg[m]);
+          }
+        },
+        [&](int, int idx, float xh) {
+#pragma unroll
+          for (int m = 0; m < QR; ++m)
+            if (m < nq) atomicAdd(&osp[m][idx], pr[m] * xh);
+        },
+        [&](int) {});
+  }
+  finish_split(P, L, b, kvh, qt, split, nq, [&](int m, int d, float) { return osp[m][d]; });
 }
 
 template <int QR>
@@ -60,8 +185,11 @@ hipError_t go(const AttnParams& P, int ng, dim3 grid, hipStream_t st) {
 
 }  // namespace
 
+int oaken_max_split(int qr) { return kOakSpan / qr; }
+
 hipError_t launch_decode_oaken(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st) {
   if (c.k.group != c.v.group) return hipErrorInvalidValue;
+  if (d.split_len > kOakSpan / d.qr) return hipErrorInvalidValue;
   const AttnParams P = make_attn_params(c, d);
   const dim3 grid((unsigned)d.num_splits, (unsigned)(c.H * d.qtiles), (unsigned)c.B);
   const int ng = kD / c.v.group;

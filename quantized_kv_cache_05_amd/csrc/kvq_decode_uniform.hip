@@ -7,7 +7,7 @@ namespace {
 
 template <int QR, class KC, class VC, int NGK, int NGV, bool CHANK>
 __global__ __launch_bounds__(256) void k_attn_uniform(AttnParams P) {
-  __shared__ AttnLds<QR, NGV, false> L;
+  __shared__ AttnLds<QR, NGV> L;
   const int split = blockIdx.x, qt = blockIdx.y % P.qtiles, kvh = blockIdx.y / P.qtiles, b = blockIdx.z;
   const int wave = threadIdx.x >> 6;
   const int nq = min(QR, P.G - qt * QR);
@@ -38,11 +38,10 @@ __global__ __launch_bounds__(256) void k_attn_uniform(AttnParams P) {
     }
     const TokView vv{P.v.codes + bh * S * VC::RB, P.v.scale + bh * S * NGV,
                      VC::SYM ? nullptr : P.v.zero + bh * S * NGV};
-    const SparseView none{};
-    attend_wave<QR, NGK, NGV, KC, VC, CHANK, false, 2>(P, L, st, kv, vv, kc, none, none, nq, t0, t1,
+    attend_wave<QR, NGK, NGV, KC, VC, CHANK, false, 2>(P, L, st, kv, vv, kc, nullptr, 0, nq, t0, t1,
                                                         wave, qop);
   }
-  wave_record<QR, NGV, false>(L, st, wave, nq);
+  wave_record<QR, NGV>(L, st, wave, nq);
   finish_split(P, L, b, kvh, qt, split, nq);
 }
 
@@ -110,24 +109,58 @@ bool decode_uniform_supported(const TensorArgs& k, const TensorArgs& v) {
 
 // Log-sum-exp merge of split partials: one workgroup of 128 threads per
 // (b, query head): M = max m_j, L = sum l_j 2^(m_j - M), out = sum 2^(m_j - M) o_j / L.
+// Split weights are formed cooperatively in LDS, chunk by chunk, so each
+// thread's loads of its output channel are independent of one another.
 __global__ __launch_bounds__(128) void k_merge(const float* __restrict__ ws, int NS,
                                               float* __restrict__ out) {
+  constexpr int CH = 512;  // splits per LDS chunk
+  __shared__ float wgt[CH];
+  __shared__ float red[128];
   const long long bq = blockIdx.x;
   const int d = threadIdx.x;
   const float* rec0 = ws + bq * NS * kPartStride;
   float M = -INFINITY;
-  for (int s = 0; s < NS; ++s) M = fmaxf(M, rec0[(long long)s * kPartStride]);
-  float L = 0.0f, O = 0.0f;
+  for (int s = d; s < NS; s += 128) M = fmaxf(M, rec0[(long long)s * kPartStride]);
+  red[d] = M;
+  __syncthreads();
+  for (int w = 64; w > 0; w >>= 1) {
+    if (d < w) red[d] = fmaxf(red[d], red[d + w]);
+    __syncthreads();
+  }
+  M = red[0];
+  __syncthreads();
+  float Lp = 0.0f, O = 0.0f;
   if (M != -INFINITY) {
-    for (int s = 0; s < NS; ++s) {
-      const float* rec = rec0 + (long long)s * kPartStride;
-      if (rec[0] != -INFINITY) {
-        const float f = fexp2(rec[0] - M);
-        L = fmaf(f, rec[1], L);
-        O = fmaf(f, rec[4 + d], O);
+    for (int c0 = 0; c0 < NS; c0 += CH) {
+      const int n = min(CH, NS - c0);
+      for (int s = d; s < n; s += 128) {
+        const float* r = rec0 + (long long)(c0 + s) * kPartStride;
+        const float ms = r[0];
+        const float f = ms == -INFINITY ? 0.0f : fexp2(ms - M);
+        wgt[s] = f;
+        Lp = fmaf(f, r[1], Lp);
       }
+      __syncthreads();
+      const float* r = rec0 + (long long)c0 * kPartStride + 4 + d;
+      int s = 0;
+      for (; s + 8 <= n; s += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = r[(long long)(s + k) * kPartStride];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) O = fmaf(wgt[s + k], v[k], O);
+      }
+      for (; s < n; ++s) O = fmaf(wgt[s], r[(long long)s * kPartStride], O);
+      __syncthreads();
     }
   }
+  red[d] = Lp;
+  __syncthreads();
+  for (int w = 64; w > 0; w >>= 1) {
+    if (d < w) red[d] += red[d + w];
+    __syncthreads();
+  }
+  const float L = red[0];
   out[bq * kD + d] = L > 0.0f ? O / L : 0.0f;
 }
 

@@ -72,7 +72,7 @@ UNIFORM_CASES = [(8, 1, 128), (8, 1, 64), (8, 0, 128), (8, 0, 32), (4, 0, 64), (
 
 
 @pytest.mark.parametrize("bits,sym,group", UNIFORM_CASES)
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 4, 16])
 def test_uniform_token(bits, sym, group, G):
     B, H, T, S = 2, 3, 333, 384
     print("case uniform bits=%d sym=%d group=%d G=%d" % (bits, sym, group, G), flush=True)
@@ -140,7 +140,7 @@ def test_uniform_append_positions():
 # channel-axis K (per channel over 64-token blocks), token-axis V, GQA
 
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 4, 16])
 def test_channel_k(bits, G):
     B, H, T, S = 1, 2, 640, 704
     print("case channel bits=%d G=%d" % (bits, G), flush=True)
@@ -290,7 +290,7 @@ def check_oaken_tensor(cache, name, x, thr, B, H, S, lens, group=64):
     return oracle.oaken_dequant_rows(oc, os_, oz, oo, oe, on, thr, group)
 
 
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 4, 16])
 def test_oaken(G):
     B, H, T, S = 2, 3, 333, 384
     print("case oaken G=%d" % G, flush=True)
