@@ -63,6 +63,13 @@ def parse():
     p.add_argument("--quiet", action="store_true")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run one plain device copy of this size first (HBM counter calibration)")
+    p.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "BENCH_LOG"),
+                   help="no GPU work: turn the counter CSVs of two rocprofv3 --pmc runs of this "
+                        "script (FETCH_SIZE, then WRITE_SIZE, both with --copy-probe-mib) and the "
+                        "bench line printed by one of them into a traffic summary on stdout")
+    p.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "BENCH_LOG"),
+                   help="no GPU work: summarize a rocprofv3 --kernel-trace --stats run of this "
+                        "script (its kernel_stats.csv and the output it printed) on stdout")
     return p.parse_args()
 
 
@@ -525,11 +532,113 @@ def stored_traffic(idx):
         return None
 
 
+def summarize_pmc(fetch_csv, write_csv, bench_log, copy_mib):
+    """Per-launch HBM bytes of the attention kernel from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch).  Each counter is scaled by what it reads for the plain copy of copy_mib MiB that
+    the same run made (the largest copy dispatch): bytes moved / counter KiB."""
+    import csv
+
+    def per_dispatch(path):
+        out = []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                out.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+        return out
+
+    copy_bytes = copy_mib << 20
+    res = {}
+    for name, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = per_dispatch(path)
+        copies = [r for r in rows if "copyBuffer" in r[0]]
+        if not copies:
+            raise SystemExit("%s: no copy dispatch; run with --copy-probe-mib" % path)
+        probe = max(copies, key=lambda r: r[1])
+        attn = [r for r in rows if "k_attn_" in r[0]]
+        if not attn:
+            raise SystemExit("%s: no attention kernel dispatch" % path)
+        kib = sum(r[2] for r in attn) / len(attn)
+        factor = copy_bytes / (probe[2] * 1024.0)
+        res[name] = (kib, probe[2], factor, len(attn), attn[0][0])
+    bench = None
+    with open(bench_log) as fh:
+        for line in fh:
+            if line.startswith("{"):
+                bench = json.loads(line)
+    hbm = sum(kib * 1024.0 * f for kib, _, f, _, _ in res.values())
+    lines = [
+        "kernel: %s" % res["fetch"][4],
+        "workload: %s" % (bench["config"]["workload"] if bench else "?"),
+        "dispatches: %d (FETCH_SIZE run), %d (WRITE_SIZE run)" % (res["fetch"][3], res["write"][3]),
+        "copy_probe_bytes: %d" % copy_bytes,
+        "copy_probe_fetch_kib: %.1f" % res["fetch"][1],
+        "copy_probe_write_kib: %.1f" % res["write"][1],
+        "fetch_factor: %.5f" % res["fetch"][2],
+        "write_factor: %.5f" % res["write"][2],
+        "fetch_kib_per_launch: %.1f" % res["fetch"][0],
+        "write_kib_per_launch: %.1f" % res["write"][0],
+        "hbm_bytes_per_launch: %d" % round(hbm),
+    ]
+    if bench:
+        lines += ["algorithmic_bytes_per_launch: %d" % bench["decode_bytes"],
+                  "traffic_over_algorithmic: %.4f" % (hbm / bench["decode_bytes"])]
+    lines.append("source_hash: %s" % source_hash())
+    print("\n".join(lines))
+
+
+def short_kernel_name(name):
+    name = name.replace("kvq::(anonymous namespace)::", "").replace("kvq::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    if name.startswith("at::native::"):
+        return name.split("<")[0] + "<...>"
+    cut = name.find("(")
+    return name[:cut] if cut > 0 else name
+
+
+def summarize_stats(stats_csv, bench_log):
+    """Per-kernel durations of one profiled bench run, next to the bench's own event timing."""
+    import csv
+    with open(stats_csv) as fh:
+        rows = list(csv.DictReader(fh))
+    bench = None
+    with open(bench_log) as fh:
+        for line in fh:
+            if line.startswith("{"):
+                bench = json.loads(line)
+    lines = []
+    if bench:
+        lines += ["workload: %s" % bench["config"]["workload"],
+                  "bench decode_ms (HIP events, mean over steps): %.4f" % bench["decode_ms"],
+                  "bench decode_bytes: %d" % bench["decode_bytes"],
+                  "bench decode GB/s: %.1f (%.2f%% of 8 TB/s)" % (bench["decode_gbs"], bench["pct_hbm_peak"]),
+                  "bench quant_prefill_tokens_per_s: %.4g" % bench["quant_prefill_tokens_per_s"],
+                  ""]
+    lines.append("%-58s %6s %12s %12s %12s %7s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "pct"))
+    for r in rows:
+        lines.append("%-58s %6s %12.2f %12.2f %12.2f %7.2f" % (
+            short_kernel_name(r["Name"])[:58], r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    attn = [r for r in rows if "k_attn_" in r["Name"]]
+    if attn and bench:
+        a = attn[0]
+        lines += ["", "attention kernel: %s" % short_kernel_name(a["Name"]),
+                  "attention avg_us: %.2f -> %.1f GB/s on the decode algorithmic bytes" % (
+                      float(a["AverageNs"]) / 1e3, bench["decode_bytes"] / float(a["AverageNs"]))]
+    lines.append("source_hash: %s" % source_hash())
+    print("\n".join(lines))
+
+
 # ---------------------------------------------------------------------------
 
 def main():
     global ARGS
     ARGS = args = parse()
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.copy_probe_mib or 1024)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU (--gpus 1); runs on several GPUs are not part of this "
               "library's scope", file=sys.stderr)

@@ -15,7 +15,7 @@
  *  [Cocktail]   Cocktail chunk-adaptive mixed-precision KV-cache page (peacm.com)
  *  [TurboQuant] TurboQuant KV-cache page (bhfrc.com)
  *
- * Readings where the pages are silent (each one is listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - Range widened to include zero: lo = min(0, min x), hi = max(0, max x),
  *    so the zero-point is an integer code inside [0, 2^b - 1].
  *  - An all-zero group has scale 0; then zero-point and codes are 0.

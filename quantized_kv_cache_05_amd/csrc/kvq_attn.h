@@ -18,8 +18,11 @@
 // 8-bit codes).  Group scales and zero-points stay in binary32 outside the
 // products: per token t and channel group g
 //   score = sum_g s[t][g] * (C_g[t] - (OFF + z[t][g]) * Q_g),  Q_g = sum_{d in g} q_d,
-//   O[c]  = sum_t (p_t s[t][g(c)]) (OFF + c_t) - sum_t p_t s[t][g(c)] (OFF + z[t][g(c)]),
-// which equals sum_t p_t s (c_t - z) exactly up to binary32 rounding.
+// which equals sum_d q_d s (c_td - z) up to binary32 rounding.  On the V side
+// a packed fp16 add of -(OFF + z) turns each B element into c - z exactly
+// before the product, so
+//   O[c]  = sum_t (p_t s[t][g(c)]) (c_t - z[t][g(c)])
+// carries no large offset that would cancel in binary32.
 // The layouts of packed rows (kvq.h) are chosen for these operands: a
 // K row is 16 slots of 8 channels, slot 4q + s holding channels
 // 32 s + 8 q + v, so every k-step (32 channels) lies in one quantization
@@ -154,12 +157,16 @@ struct KF16 {
 
 // ---------------------------------------------------------------------------
 // V codecs: load the lane's column word n16 of 8 token rows and form the B
-// operand of column block j: 4 fp16 pairs (rows 2r, 2r + 1), value OFF + code
-// (8-bit codes: code - z exactly, see pair_sub).
+// operand of column block j: 4 fp16 pairs (rows 2r, 2r + 1), value OFF + code.
+// The tile loop then adds the packed fp16 pair -(OFF + z) of the two rows,
+// which leaves code - z exactly (small integers are exact in fp16).
 
 struct VI4 {
   static constexpr int RB = 64, OFF = 16, BITS = 4;
-  static constexpr bool SYM = false, F16 = false, EXACT = false;
+  static constexpr bool SYM = false, F16 = false;
+  // -(16 + z) as fp16: sign, the exponent of 16, z in mantissa bits 6-9
+  static constexpr unsigned ZMAGIC = 0xCC00CC00u, ZMASK = 0x03C003C0u;
+  static constexpr int ZSH = 6;
   unsigned r[8];
   __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
 #pragma unroll
@@ -179,7 +186,10 @@ struct VI4 {
 
 struct VI2 {
   static constexpr int RB = 32, OFF = 4, BITS = 2;
-  static constexpr bool SYM = false, F16 = false, EXACT = false;
+  static constexpr bool SYM = false, F16 = false;
+  // -(4 + z) as fp16: sign, the exponent of 4, z in mantissa bits 8-9
+  static constexpr unsigned ZMAGIC = 0xC400C400u, ZMASK = 0x03000300u;
+  static constexpr int ZSH = 8;
   unsigned x[4];  // rows 2p (low half) and 2p + 1 (high half)
   __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
     unsigned r[8];
@@ -204,8 +214,11 @@ struct VI2 {
 
 template <bool SYM_>
 struct VI8 {
-  static constexpr int RB = 128, OFF = 0, BITS = 8;
-  static constexpr bool SYM = SYM_, F16 = false, EXACT = true;
+  static constexpr int RB = 128, OFF = 1024, BITS = 8;
+  static constexpr bool SYM = SYM_, F16 = false;
+  // -(1024 + z) as fp16: sign, the exponent of 1024, z in mantissa bits 0-7
+  static constexpr unsigned ZMAGIC = 0xE400E400u, ZMASK = 0x00FF00FFu;
+  static constexpr int ZSH = 0;
   unsigned w0[8], w1[8];  // codes 0-3 and 4-7 of the column word, per row
   __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
 #pragma unroll
@@ -216,7 +229,7 @@ struct VI8 {
     }
   }
   __device__ __forceinline__ void zero_row(int k) {}
-  // 1024 + code (+128 when symmetric) per pair; the caller subtracts (1024 + z) exactly
+  // 1024 + code (+128 when symmetric) per pair
   __device__ __forceinline__ u4_t block(int j) const {
     const unsigned* w = (j >> 2) ? w1 : w0;
     u4_t o;
@@ -228,7 +241,7 @@ struct VI8 {
 
 struct VF16 {
   static constexpr int RB = 256, OFF = 0, BITS = 16;
-  static constexpr bool SYM = false, F16 = true, EXACT = false;
+  static constexpr bool SYM = false, F16 = true;
   u4_t r[8];
   __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
 #pragma unroll
@@ -281,22 +294,11 @@ struct SparseView {
   float t_lo, t_hi;
 };
 
-// Per-wave LDS scratch.
-template <int NGV, bool OAK>
-struct WaveLds {
-  unsigned short w[NGV][2][16][kTile];  // softmax weights per V group: hi / lo, [query][token]
-  float sp_sc[OAK ? 16 : 1][kTile];     // sparse K score additions [query][token]
-  float sp_p[OAK ? 16 : 1][kTile];      // probabilities for the sparse V side
-  float sp_o[OAK ? 16 : 1][128];        // sparse V accumulators [query][channel]
-  unsigned sp_rp[OAK ? kTile + 1 : 1];  // tile row pointers
-};
-
 // Running softmax state of a wave (lane-held, see the header comment).
 template <int GI>
 struct SoftState {
   float m[GI], l[GI];
   f4_t o[8];  // [column block j] rows 4*q4 + i
-  float vb[GI][4];  // V bias per query row and V group (partial over this lane's tokens)
 };
 
 template <int GI>
@@ -305,8 +307,6 @@ __device__ __forceinline__ void soft_init(SoftState<GI>& st) {
   for (int i = 0; i < GI; ++i) {
     st.m[i] = -INFINITY;
     st.l[i] = 0.0f;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) st.vb[i][g] = 0.0f;
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) st.o[j] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};

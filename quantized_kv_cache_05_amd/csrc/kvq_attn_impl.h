@@ -63,6 +63,47 @@ __device__ __forceinline__ void load_tok_meta(const TokView& v, int row, float (
   }
 }
 
+// -(OFF + z) as packed fp16 pairs for the B operand of the V product: lane
+// rows r0 .. r0 + 7 (pairs 2p, 2p + 1), one set per V group.  The zero-point
+// bytes of the 8 rows are contiguous (NGV per row); the row offset is a
+// multiple of 8, so the loads are aligned.  Codes of rows past the valid
+// range multiply zero weights; the mask keeps their (arbitrary) zero-point
+// bytes inside the mantissa so the pair stays finite.
+template <class VC, int NGV>
+__device__ __forceinline__ void load_zsub(const TokView& vv, int r0, u4_t (&zsub)[NGV]) {
+  if constexpr (VC::SYM) {
+#pragma unroll
+    for (int g = 0; g < NGV; ++g)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) zsub[g][p] = VC::ZMAGIC | 0x00800080u;  // z = 128
+  } else {
+    unsigned zw[2 * NGV];
+    const uint8_t* zp = vv.zero + (long long)r0 * NGV;
+    if constexpr (NGV == 1) {
+      const u2_t t = *reinterpret_cast<const u2_t*>(zp);
+      zw[0] = t[0];
+      zw[1] = t[1];
+    } else {
+#pragma unroll
+      for (int k = 0; k < NGV / 2; ++k) {
+        const u4_t t = *reinterpret_cast<const u4_t*>(zp + 16 * k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zw[4 * k + e] = t[e];
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < NGV; ++g)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int ia = 2 * p * NGV + g, ib = (2 * p + 1) * NGV + g;
+        // byte ia of the row bytes -> bits 0-7, byte ib -> bits 16-23
+        const unsigned sel = (0x0Cu << 24) | ((4u + (ib & 3)) << 16) | (0x0Cu << 8) | (unsigned)(ia & 3);
+        const unsigned x = perm(zw[ib >> 2], zw[ia >> 2], sel);
+        zsub[g][p] = ((x << VC::ZSH) & VC::ZMASK) | VC::ZMAGIC;
+      }
+  }
+}
+
 // Sum / max over the 16 lanes of a row group (lanes differing in bits 0-3).
 __device__ __forceinline__ float sum16(float v) {
 #pragma unroll
@@ -153,7 +194,8 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
         const int t = tile + nb * 16 + n16;
         ok[nb] = t >= t0 && t < t1;
         if constexpr (!CHANK && !KC::F16) load_tok_meta<NGK, KC::SYM>(kv, t, sk[nb], zk[nb], ok[nb]);
-        if constexpr (!VC::F16) load_tok_meta<NGV, VC::SYM>(vv, t, sv[nb], zv[nb], ok[nb]);
+        // V zero-points enter through zsub below; only the scales are needed here
+        if constexpr (!VC::F16) load_tok_meta<NGV, true>(vv, t, sv[nb], zv[nb], ok[nb]);
       }
       if constexpr (VC::F16) {
 #pragma unroll
@@ -162,23 +204,9 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
           if (t < t0 || t >= t1) vr.zero_row(k);
         }
       }
-      // V zero-points of the B operand rows (8-bit V codes subtract them exactly)
+      // -(OFF + z) of the B-operand rows as packed fp16 pairs, per V group
       u4_t zsub[NGV];
-      if constexpr (VC::EXACT) {
-#pragma unroll
-        for (int g = 0; g < NGV; ++g) {
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            float za = VC::SYM ? 128.0f : 0.0f, zb = za;
-            if constexpr (!VC::SYM) {
-              za = (float)vv.zero[(long long)(tile + 8 * q4 + 2 * p) * NGV + g];
-              zb = (float)vv.zero[(long long)(tile + 8 * q4 + 2 * p + 1) * NGV + g];
-            }
-            const h2_t zz = {(_Float16)(-1024.0f - za), (_Float16)(-1024.0f - zb)};
-            zsub[g][p] = __builtin_bit_cast(unsigned, zz);
-          }
-        }
-      }
+      if constexpr (!VC::F16) load_zsub<VC, NGV>(vv, tile + 8 * q4, zsub);
       // ---- scores ----
       float sc[2][GI];
       if constexpr (CHANK) {
@@ -249,8 +277,6 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
           const float a = alpha[i];
           st.l[i] *= a;
 #pragma unroll
-          for (int g = 0; g < NGV; ++g) st.vb[i][g] *= a;
-#pragma unroll
           for (int j = 0; j < 8; ++j) st.o[j][i] *= a;
         }
       }
@@ -273,7 +299,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
             if (ok[nb] && m < nq && (GI != 1 || q4 == 0)) oak_sc[m * oak_span + (t - t0)] = sc[nb][i];
           }
       }
-      // ---- weights p * s_v (binary32) -> fp16 hi / lo in LDS, V bias ----
+      // ---- weights p * s_v (binary32) -> fp16 hi / lo in LDS ----
 #pragma unroll
       for (int i = 0; i < GI; ++i) {
         const int m = GI == 1 ? 0 : 4 * q4 + i;
@@ -287,10 +313,6 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
           } else {
             w0 = p[0][i] * sv[0][g];
             w1 = p[1][i] * sv[1][g];
-            if constexpr (!VC::EXACT) {
-              st.vb[i][g] = fmaf(w0, zv[0][g] + (float)VC::OFF, st.vb[i][g]);
-              st.vb[i][g] = fmaf(w1, zv[1][g] + (float)VC::OFF, st.vb[i][g]);
-            }
           }
           unsigned hi, lo;
           split_pair(w0, w1, hi, lo);
@@ -314,7 +336,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       for (int j = 0; j < 8; ++j) {
         constexpr int JPG = 8 / NGV;
         u4_t b = vr.block(j);
-        if constexpr (VC::EXACT) {
+        if constexpr (!VC::F16) {
 #pragma unroll
           for (int p2 = 0; p2 < 4; ++p2) {
             // copy vector elements to scalars before bit casts: clang miscompiles a bit cast
@@ -332,19 +354,15 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
   }
 }
 
-// Fold the wave's state into its record (sum over the 16 token columns,
-// V bias and sparse V values applied).  Caller: all waves, after a barrier.
+// Fold the wave's state into its record (sum of l over the 16 token
+// columns).  Caller: all waves, after a barrier.
 template <int QR, int NGV, class LDS>
 __device__ __forceinline__ void wave_record(LDS& L, SoftState<QRows<QR>::GI>& st, int wave, int nq) {
   constexpr int GI = QRows<QR>::GI;
   const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
-  float lt[GI], vbt[GI][NGV];
+  float lt[GI];
 #pragma unroll
-  for (int i = 0; i < GI; ++i) {
-    lt[i] = sum16(st.l[i]);
-#pragma unroll
-    for (int g = 0; g < NGV; ++g) vbt[i][g] = sum16(st.vb[i][g]);
-  }
+  for (int i = 0; i < GI; ++i) lt[i] = sum16(st.l[i]);
   __syncthreads();
   auto& rec = L.u.rec[wave];
 #pragma unroll
@@ -354,7 +372,7 @@ __device__ __forceinline__ void wave_record(LDS& L, SoftState<QRows<QR>::GI>& st
     if (m >= nq) continue;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      rec.o[m][16 * j + n16] = st.o[j][i] - vbt[i][j / (8 / NGV)];
+      rec.o[m][16 * j + n16] = st.o[j][i];
     }
     if (n16 == 0) {
       rec.o[m][128] = st.m[i];

@@ -9,7 +9,7 @@ namespace kvq {
 namespace {
 
 template <int QR, int NG>
-__global__ __launch_bounds__(256) void k_attn_mixed(AttnParams P) {
+__global__ __launch_bounds__(256, 2) void k_attn_mixed(AttnParams P) {
   __shared__ AttnLds<QR, NG> L;
   const int split = blockIdx.x, qt = blockIdx.y % P.qtiles, kvh = blockIdx.y / P.qtiles, b = blockIdx.z;
   const int wave = threadIdx.x >> 6;

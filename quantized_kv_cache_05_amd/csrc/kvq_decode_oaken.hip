@@ -96,7 +96,7 @@ __device__ __forceinline__ void for_row_entries(const SparseView& sv, int t0, in
 }
 
 template <int QR, int NG>
-__global__ __launch_bounds__(256) void k_attn_oaken(AttnParams P) {
+__global__ __launch_bounds__(256, 2) void k_attn_oaken(AttnParams P) {
   __shared__ AttnLds<QR, NG> L;
   __shared__ OakLds OL;
   __shared__ float osp[QR][128];

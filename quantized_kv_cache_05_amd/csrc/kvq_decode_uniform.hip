@@ -6,7 +6,7 @@ namespace kvq {
 namespace {
 
 template <int QR, class KC, class VC, int NGK, int NGV, bool CHANK>
-__global__ __launch_bounds__(256) void k_attn_uniform(AttnParams P) {
+__global__ __launch_bounds__(256, 2) void k_attn_uniform(AttnParams P) {
   __shared__ AttnLds<QR, NGV> L;
   const int split = blockIdx.x, qt = blockIdx.y % P.qtiles, kvh = blockIdx.y / P.qtiles, b = blockIdx.z;
   const int wave = threadIdx.x >> 6;

@@ -1,0 +1,211 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+bench times (its own workload builders, automatic split count).
+
+The whole cache is built and decoded on the GPU; the oracle then recomputes
+a few sampled (batch, KV head) slices one by one from the same seeded
+inputs: codes, scales, zero-points, sparse entries, row pointers, perm and
+seg of the slice bit for bit, and the decode output rows of that slice's
+query heads within the attention bar.  Inputs of the oracle are regenerated
+on the host and never read back from the GPU (the Oaken thresholds are
+recomputed by the oracle from the calibration set and must equal the
+device's).
+"""
+import argparse
+
+import numpy as np
+import pytest
+
+import bench
+import oracle
+import synth
+from kvq_harness import ATTN_BAR, ATTN_TIGHT, f16_layout, rel_err_rows, unpack_layout
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+K = pytest.importorskip("quantized_kv_cache_05_amd")
+
+SM = bench.SM_SCALE
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    K.lib()
+    bench.ARGS = argparse.Namespace(num_splits=0, quiet=True)
+    yield
+
+
+def bh(t, B, H, b, h, dtype=np.uint8):
+    """Bytes of slice (b, h) of a [B][H][...] device buffer -> numpy of dtype."""
+    return t.view(torch.uint8).view(B, H, -1)[b, h].cpu().numpy().view(dtype)
+
+
+def f32bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def sampled_slices(B, H, seed):
+    rng = np.random.default_rng(seed)
+    picks = {(0, 0), (B - 1, H - 1), (int(rng.integers(B)), int(rng.integers(H)))}
+    return sorted(picks)
+
+
+def run_bench_step(idx):
+    """Build workload idx as the bench does, prefill, append (if the workload
+    appends) and decode once on cache copy 0."""
+    print("case full-size workload %d" % idx, flush=True)
+    wl = bench.build_workload(idx, torch, K, synth)
+    wl.prefill(0)
+    wl.append(0)
+    wl.out.fill_(float("nan"))
+    wl.decode(0)
+    torch.cuda.synchronize()
+    assert not any(wl.flags())
+    return wl, wl.out.cpu().numpy()
+
+
+def check_rows(out, b, h, G, q, kh, vh, label):
+    ref = oracle.attention(q[h * G:(h + 1) * G], kh[None], vh[None], SM)
+    err = float(rel_err_rows(out[b, h * G:(h + 1) * G], ref).max())
+    print("%s b%d h%d: max rel err %.3e" % (label, b, h, err), flush=True)
+    assert err <= ATTN_BAR and err <= ATTN_TIGHT, (label, b, h, err)
+
+
+@pytest.mark.parametrize("idx", [1, 2])
+def test_uniform_token_full(idx):
+    wl, out = run_bench_step(idx)
+    w = wl.w
+    B, H, T, G = w.batch, w.kv_heads, w.tokens, w.q_heads // w.kv_heads
+    bits, sym, g = wl.bits, bool(wl.sym), wl.group
+    c = wl.caches[0]
+    S, RB, NG = c.desc.max_seq, 128 * bits // 8, 128 // g
+    for b, h in sampled_slices(B, H, 100 + idx):
+        deq = {}
+        for name, tensor in (("k", 0), ("v", 1)):
+            x = w.kv(tensor, b, b + 1, h, h + 1)[0, 0]
+            oc, os_, oz = oracle.quant_rows(x, g, bits, sym)
+            got = unpack_layout(bh(c.buf(name + ".codes"), B, H, b, h).reshape(S, RB)[:T], bits,
+                                name.upper(), sym)
+            assert np.array_equal(got, oc), (name, b, h)
+            gs = bh(c.buf(name + ".scale"), B, H, b, h, np.float32).reshape(S, NG)[:T]
+            assert np.array_equal(f32bits(gs), f32bits(os_)), (name, b, h)
+            if not sym:
+                gz = bh(c.buf(name + ".zero"), B, H, b, h).reshape(S, NG)[:T]
+                assert np.array_equal(gz, oz), (name, b, h)
+            deq[name] = oracle.dequant_rows(oc, os_, oz, g, sym)
+        q = w.q(b, b + 1)[0]
+        check_rows(out, b, h, G, q, deq["k"], deq["v"], "workload %d" % idx)
+
+
+def test_channel_k_gqa_full():
+    wl, out = run_bench_step(3)
+    w = wl.w
+    B, H, T, G = w.batch, w.kv_heads, w.tokens, w.q_heads // w.kv_heads
+    c = wl.caches[0]
+    S = c.desc.max_seq
+    for b, h in sampled_slices(B, H, 103):
+        k = w.kv(0, b, b + 1, h, h + 1)[0, 0]
+        v = w.kv(1, b, b + 1, h, h + 1)[0, 0]
+        kc, ks, kz = oracle.quant_channel_blocks(k, 64, 4)
+        got = unpack_layout(bh(c.buf("k.codes"), B, H, b, h).reshape(S, 64)[:T], 4, "K")
+        assert np.array_equal(got, kc), (b, h)
+        gs = bh(c.buf("k.scale"), B, H, b, h, np.float32).reshape(S // 64, 128)[:T // 64]
+        gz = bh(c.buf("k.zero"), B, H, b, h).reshape(S // 64, 128)[:T // 64]
+        assert np.array_equal(f32bits(gs), f32bits(ks)) and np.array_equal(gz, kz), (b, h)
+        vc, vs, vz = oracle.quant_rows(v, 64, 4)
+        gotv = unpack_layout(bh(c.buf("v.codes"), B, H, b, h).reshape(S, 64)[:T], 4, "V")
+        assert np.array_equal(gotv, vc), (b, h)
+        gvs = bh(c.buf("v.scale"), B, H, b, h, np.float32).reshape(S, 2)[:T]
+        gvz = bh(c.buf("v.zero"), B, H, b, h).reshape(S, 2)[:T]
+        assert np.array_equal(f32bits(gvs), f32bits(vs)) and np.array_equal(gvz, vz), (b, h)
+        kh = oracle.dequant_channel_blocks(kc, ks, kz, 64)
+        vh = oracle.dequant_rows(vc, vs, vz, 64)
+        q = w.q(b, b + 1)[0]
+        check_rows(out, b, h, G, q, kh, vh, "workload 3")
+
+
+def test_chunk_mixed_full():
+    wl, out = run_bench_step(4)
+    w = wl.w
+    B, H, T, G, CT = w.batch, w.kv_heads, w.tokens, w.q_heads // w.kv_heads, w.chunk_tokens
+    C = T // CT
+    c = wl.caches[0]
+    dev_bits = wl.bits.cpu().numpy()
+    dev_perm = c.buf("perm").view(torch.int32).view(B, C).cpu().numpy()
+    dev_seg = c.buf("seg").view(torch.int32).view(B, 4).cpu().numpy()
+    checked = set()
+    for b, h in sampled_slices(B, H, 104):
+        bits_c, _ = oracle.chunk_bits(*w.chunk_embeddings(b))
+        if b not in checked:
+            assert np.array_equal(dev_bits[b], bits_c), b
+            checked.add(b)
+        perm_o, seg_o = oracle.reorder(bits_c[None])
+        assert np.array_equal(dev_perm[b], perm_o[0]) and np.array_equal(dev_seg[b], seg_o[0]), b
+        n16, n4, n2, n = seg_o[0]
+        deq = {}
+        for name, tensor in (("k", 0), ("v", 1)):
+            x = w.kv(tensor, b, b + 1, h, h + 1)[0, 0]
+            lay = name.upper()
+            p16 = f16_layout(bh(c.buf(name + ".codes16"), B, H, b, h, np.uint16).reshape(C, CT, 128), lay)
+            p4 = unpack_layout(bh(c.buf(name + ".codes"), B, H, b, h).reshape(C, CT, 64), 4, lay)
+            s4 = bh(c.buf(name + ".scale"), B, H, b, h, np.float32).reshape(C, CT, 4)
+            z4 = bh(c.buf(name + ".zero"), B, H, b, h).reshape(C, CT, 4)
+            p2 = unpack_layout(bh(c.buf(name + ".codes2"), B, H, b, h).reshape(C, CT, 32), 2, lay)
+            s2 = bh(c.buf(name + ".scale2"), B, H, b, h, np.float32).reshape(C, CT, 4)
+            z2 = bh(c.buf(name + ".zero2"), B, H, b, h).reshape(C, CT, 4)
+            xh = np.zeros((T, 128), np.float32)
+            for j in range(n):
+                src = perm_o[0, j]
+                rows = x[src * CT:(src + 1) * CT]
+                if j < n16:
+                    assert np.array_equal(p16[j], rows), (name, b, h, j)
+                    xh[src * CT:(src + 1) * CT] = rows.view(np.float16).astype(np.float32)
+                    continue
+                nb, kk = (4, j - n16) if j < n16 + n4 else (2, j - n16 - n4)
+                oc, os_, oz = oracle.quant_rows(rows, 32, nb)
+                pc, ps, pz = (p4, s4, z4) if nb == 4 else (p2, s2, z2)
+                assert np.array_equal(pc[kk], oc), (name, b, h, j)
+                assert np.array_equal(f32bits(ps[kk]), f32bits(os_)), (name, b, h, j)
+                assert np.array_equal(pz[kk], oz), (name, b, h, j)
+                xh[src * CT:(src + 1) * CT] = oracle.dequant_rows(oc, os_, oz, 32)
+            deq[name] = xh
+        q = w.q(b, b + 1)[0]
+        check_rows(out, b, h, G, q, deq["k"], deq["v"], "workload 4")
+
+
+def test_oaken_full():
+    wl, out = run_bench_step(5)
+    w = wl.w
+    B, H, T, G = w.batch, w.kv_heads, w.tokens, w.q_heads // w.kv_heads
+    c = wl.caches[0]
+    S, cap = c.desc.max_seq, c.desc.k.sparse_cap
+    thr = []
+    for tensor in (0, 1):
+        hist = np.zeros(65536, np.uint64)
+        for s in range(w.cal_samples):
+            oracle.hist_f16(w.calibration(tensor, s), hist)
+        thr.append(oracle.thresholds_from_hist(hist))
+        assert np.array_equal(f32bits(thr[-1]), f32bits(np.array(wl.thr[tensor], np.float32))), tensor
+    for b, h in sampled_slices(B, H, 105):
+        deq = {}
+        for name, tensor in (("k", 0), ("v", 1)):
+            x = w.kv(tensor, b, b + 1, h, h + 1)[0, 0]
+            t = thr[tensor]
+            oc, os_, oz, oo, oe, on = oracle.oaken_rows(x, t, 64)
+            got = unpack_layout(bh(c.buf(name + ".codes"), B, H, b, h).reshape(S, 64)[:T], 4, name.upper())
+            assert np.array_equal(got, oc), (name, b, h)
+            for buf, ref, dt in (("scale", os_, np.float32), ("oscale", oo, np.float32)):
+                g = bh(c.buf(name + "." + buf), B, H, b, h, dt).reshape(S, 2)[:T]
+                assert np.array_equal(f32bits(g), f32bits(ref)), (name, buf, b, h)
+            gz = bh(c.buf(name + ".zero"), B, H, b, h).reshape(S, 2)[:T]
+            assert np.array_equal(gz, oz), (name, b, h)
+            rp = bh(c.buf(name + ".rowptr"), B, H, b, h, np.uint32)[:T + 1].astype(np.int64)
+            assert rp[0] == 0 and np.array_equal(np.diff(rp), on), (name, b, h)
+            sp = bh(c.buf(name + ".sparse"), B, H, b, h, np.uint16)[:cap]
+            flat = np.concatenate([oe[i, :on[i]] for i in range(T)])
+            assert np.array_equal(sp[:rp[T]], flat), (name, b, h)
+            deq[name] = oracle.oaken_dequant_rows(oc, os_, oz, oo, oe, on, t, 64)
+        q = w.q(b, b + 1)[0]
+        check_rows(out, b, h, G, q, deq["k"], deq["v"], "workload 5")
