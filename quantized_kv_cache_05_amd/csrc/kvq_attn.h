@@ -67,6 +67,20 @@ __host__ __device__ constexpr unsigned sel_bytes(int a) {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// (x & m) | c as one v_and_or_b32.  VOP3 encodings take no literal
+// constants on this target, so with literal m and c the compiler emits an AND
+// and an OR; passing m and c through an empty asm hides their values, so they
+// are kept in registers (the asm has no side effects and is hoisted out of
+// loops) and the selector fuses the pair.  The instruction itself stays
+// compiler-generated, so its hazards against the matrix cores are tracked.
+__device__ __forceinline__ unsigned opaque(unsigned v) {
+  asm("" : "+v"(v));
+  return v;
+}
+__device__ __forceinline__ unsigned and_or(unsigned x, unsigned m, unsigned c) {
+  return (x & opaque(m)) | opaque(c);
+}
+
 __device__ __forceinline__ float f16lo(unsigned w) { return (float)__builtin_bit_cast(h2_t, w)[0]; }
 __device__ __forceinline__ float f16hi(unsigned w) { return (float)__builtin_bit_cast(h2_t, w)[1]; }
 
@@ -91,10 +105,10 @@ struct KI4 {
   __device__ __forceinline__ u4_t slice(int s) const {
     const unsigned w = r[s];
     u4_t o;
-    o[0] = ((w << 6) & 0x03C003C0u) | 0x4C004C00u;
-    o[1] = ((w << 2) & 0x03C003C0u) | 0x4C004C00u;
-    o[2] = ((w >> 2) & 0x03C003C0u) | 0x4C004C00u;
-    o[3] = ((w >> 6) & 0x03C003C0u) | 0x4C004C00u;
+    o[0] = and_or(w << 6, 0x03C003C0u, 0x4C004C00u);
+    o[1] = and_or(w << 2, 0x03C003C0u, 0x4C004C00u);
+    o[2] = and_or(w >> 2, 0x03C003C0u, 0x4C004C00u);
+    o[3] = and_or(w >> 6, 0x03C003C0u, 0x4C004C00u);
     return o;
   }
 };
@@ -111,10 +125,10 @@ struct KI2 {
     // byte 0 of the slice (channels 0-3) to the low half, byte 1 (4-7) to the high half
     const unsigned x = (s & 1) ? perm(0u, d, 0x0C030C02u) : perm(0u, d, 0x0C010C00u);
     u4_t o;
-    o[0] = ((x << 8) & 0x03000300u) | 0x44004400u;
-    o[1] = ((x << 6) & 0x03000300u) | 0x44004400u;
-    o[2] = ((x << 4) & 0x03000300u) | 0x44004400u;
-    o[3] = ((x << 2) & 0x03000300u) | 0x44004400u;
+    o[0] = and_or(x << 8, 0x03000300u, 0x44004400u);
+    o[1] = and_or(x << 6, 0x03000300u, 0x44004400u);
+    o[2] = and_or(x << 4, 0x03000300u, 0x44004400u);
+    o[3] = and_or(x << 2, 0x03000300u, 0x44004400u);
     return o;
   }
 };
@@ -157,16 +171,22 @@ struct KF16 {
 
 // ---------------------------------------------------------------------------
 // V codecs: load the lane's column word n16 of 8 token rows and form the B
-// operand of column block j: 4 fp16 pairs (rows 2r, 2r + 1), value OFF + code.
-// The tile loop then adds the packed fp16 pair -(OFF + z) of the two rows,
-// which leaves code - z exactly (small integers are exact in fp16).
+// operand of column block j: 4 fp16 pairs (rows 2r, 2r + 1), each the fp16
+// integer 1024 + f * code (the code masked in place under the exponent of
+// 1024, whose ulp is 1; f = 16 when the code sits 4 bits up, odd blocks of
+// 4-bit codes).  The tile loop adds the packed pair -(1024 + f * z) of the
+// two rows, leaving f * (code - z) exactly; the output block then carries the
+// factor f, removed when the wave's state leaves the loop.  Zero-point pairs
+// are built from the rows' z bytes as ((z << ZSH[par]) & ZMASK[par]) | ZMAGIC,
+// par = 1 for odd blocks when ZODD.
 
 struct VI4 {
-  static constexpr int RB = 64, OFF = 16, BITS = 4;
-  static constexpr bool SYM = false, F16 = false;
-  // -(16 + z) as fp16: sign, the exponent of 16, z in mantissa bits 6-9
-  static constexpr unsigned ZMAGIC = 0xCC00CC00u, ZMASK = 0x03C003C0u;
-  static constexpr int ZSH = 6;
+  static constexpr int RB = 64, BITS = 4;
+  static constexpr bool SYM = false, F16 = false, ZODD = true;
+  static constexpr unsigned ZMAGIC = 0xE400E400u;
+  static constexpr unsigned ZMASK[2] = {0x000F000Fu, 0x00F000F0u};
+  static constexpr int ZSH[2] = {0, 4};
+  static constexpr float fac(int j) { return (j & 1) ? 16.0f : 1.0f; }
   unsigned r[8];
   __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
 #pragma unroll
@@ -176,20 +196,19 @@ struct VI4 {
   __device__ __forceinline__ u4_t block(int j) const {
     u4_t o;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const unsigned x = perm(r[2 * p + 1], r[2 * p], sel_bytes(j >> 1));
-      o[p] = ((j & 1) ? ((x << 2) & 0x03C003C0u) : ((x << 6) & 0x03C003C0u)) | 0x4C004C00u;
-    }
+    for (int p = 0; p < 4; ++p)
+      o[p] = and_or(perm(r[2 * p + 1], r[2 * p], sel_bytes(j >> 1)), ZMASK[j & 1], 0x64006400u);
     return o;
   }
 };
 
 struct VI2 {
-  static constexpr int RB = 32, OFF = 4, BITS = 2;
-  static constexpr bool SYM = false, F16 = false;
-  // -(4 + z) as fp16: sign, the exponent of 4, z in mantissa bits 8-9
-  static constexpr unsigned ZMAGIC = 0xC400C400u, ZMASK = 0x03000300u;
-  static constexpr int ZSH = 8;
+  static constexpr int RB = 32, BITS = 2;
+  static constexpr bool SYM = false, F16 = false, ZODD = false;
+  static constexpr unsigned ZMAGIC = 0xE400E400u;
+  static constexpr unsigned ZMASK[2] = {0x00030003u, 0x00030003u};
+  static constexpr int ZSH[2] = {0, 0};
+  static constexpr float fac(int) { return 1.0f; }
   unsigned x[4];  // rows 2p (low half) and 2p + 1 (high half)
   __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
     unsigned r[8];
@@ -204,22 +223,20 @@ struct VI2 {
   __device__ __forceinline__ u4_t block(int j) const {
     u4_t o;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const unsigned y = j <= 4 ? (x[p] << (8 - 2 * j)) : (x[p] >> (2 * j - 8));
-      o[p] = (y & 0x03000300u) | 0x44004400u;
-    }
+    for (int p = 0; p < 4; ++p) o[p] = and_or(x[p] >> (2 * j), 0x00030003u, 0x64006400u);
     return o;
   }
 };
 
 template <bool SYM_>
 struct VI8 {
-  static constexpr int RB = 128, OFF = 1024, BITS = 8;
-  static constexpr bool SYM = SYM_, F16 = false;
-  // -(1024 + z) as fp16: sign, the exponent of 1024, z in mantissa bits 0-7
-  static constexpr unsigned ZMAGIC = 0xE400E400u, ZMASK = 0x00FF00FFu;
-  static constexpr int ZSH = 0;
-  unsigned w0[8], w1[8];  // codes 0-3 and 4-7 of the column word, per row
+  static constexpr int RB = 128, BITS = 8;
+  static constexpr bool SYM = SYM_, F16 = false, ZODD = false;
+  static constexpr unsigned ZMAGIC = 0xE400E400u;
+  static constexpr unsigned ZMASK[2] = {0x00FF00FFu, 0x00FF00FFu};
+  static constexpr int ZSH[2] = {0, 0};
+  static constexpr float fac(int) { return 1.0f; }
+  unsigned w0[8], w1[8];  // codes 0-3 and 4-7 of the column word, per row (offset binary)
   __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -229,7 +246,6 @@ struct VI8 {
     }
   }
   __device__ __forceinline__ void zero_row(int k) {}
-  // 1024 + code (+128 when symmetric) per pair
   __device__ __forceinline__ u4_t block(int j) const {
     const unsigned* w = (j >> 2) ? w1 : w0;
     u4_t o;
@@ -240,8 +256,9 @@ struct VI8 {
 };
 
 struct VF16 {
-  static constexpr int RB = 256, OFF = 0, BITS = 16;
-  static constexpr bool SYM = false, F16 = true;
+  static constexpr int RB = 256, BITS = 16;
+  static constexpr bool SYM = false, F16 = true, ZODD = false;
+  static constexpr float fac(int) { return 1.0f; }
   u4_t r[8];
   __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
 #pragma unroll

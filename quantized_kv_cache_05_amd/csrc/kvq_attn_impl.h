@@ -63,19 +63,20 @@ __device__ __forceinline__ void load_tok_meta(const TokView& v, int row, float (
   }
 }
 
-// -(OFF + z) as packed fp16 pairs for the B operand of the V product: lane
-// rows r0 .. r0 + 7 (pairs 2p, 2p + 1), one set per V group.  The zero-point
-// bytes of the 8 rows are contiguous (NGV per row); the row offset is a
-// multiple of 8, so the loads are aligned.  Codes of rows past the valid
-// range multiply zero weights; the mask keeps their (arbitrary) zero-point
-// bytes inside the mantissa so the pair stays finite.
+// -(1024 + f z) as packed fp16 pairs for the B operand of the V product:
+// lane rows r0 .. r0 + 7 (pairs 2p, 2p + 1), one set per V group and block
+// parity (see the V codecs).  The zero-point bytes of the 8 rows are
+// contiguous (NGV per row); the row offset is a multiple of 8, so the loads
+// are aligned.  Rows past the valid range multiply zero weights; the mask
+// keeps their (arbitrary) bytes inside the mantissa, so the pairs stay finite.
 template <class VC, int NGV>
-__device__ __forceinline__ void load_zsub(const TokView& vv, int r0, u4_t (&zsub)[NGV]) {
+__device__ __forceinline__ void load_zsub(const TokView& vv, int r0, u4_t (&zsub)[2][NGV]) {
+  constexpr int NP = VC::ZODD ? 2 : 1;
   if constexpr (VC::SYM) {
 #pragma unroll
     for (int g = 0; g < NGV; ++g)
 #pragma unroll
-      for (int p = 0; p < 4; ++p) zsub[g][p] = VC::ZMAGIC | 0x00800080u;  // z = 128
+      for (int p = 0; p < 4; ++p) zsub[0][g][p] = VC::ZMAGIC | 0x00800080u;  // z = 128
   } else {
     unsigned zw[2 * NGV];
     const uint8_t* zp = vv.zero + (long long)r0 * NGV;
@@ -99,7 +100,9 @@ __device__ __forceinline__ void load_zsub(const TokView& vv, int r0, u4_t (&zsub
         // byte ia of the row bytes -> bits 0-7, byte ib -> bits 16-23
         const unsigned sel = (0x0Cu << 24) | ((4u + (ib & 3)) << 16) | (0x0Cu << 8) | (unsigned)(ia & 3);
         const unsigned x = perm(zw[ib >> 2], zw[ia >> 2], sel);
-        zsub[g][p] = ((x << VC::ZSH) & VC::ZMASK) | VC::ZMAGIC;
+#pragma unroll
+        for (int par = 0; par < NP; ++par)
+          zsub[par][g][p] = and_or(x << VC::ZSH[par], VC::ZMASK[par], VC::ZMAGIC);
       }
   }
 }
@@ -140,6 +143,11 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
   auto arow = [&](int x) { return GI == 1 ? 0 : min(x, R - 1); };
   auto& W = L.u.wave[wave];
   const int tb = t0 & ~(kTile * TPS - 1);
+  // the running output is held in natural units between calls; inside, block
+  // j accumulates with the codec's factor fac(j)
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (VC::fac(j) != 1.0f) st.o[j] *= VC::fac(j);
   for (int step = tb + wave * kTile * TPS; step < t1; step += kNW * kTile * TPS) {
     // ---- channel-axis K: fold the block's scales into the query ----
     u4_t qh[4], ql[4];
@@ -205,7 +213,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
         }
       }
       // -(OFF + z) of the B-operand rows as packed fp16 pairs, per V group
-      u4_t zsub[NGV];
+      u4_t zsub[2][NGV];
       if constexpr (!VC::F16) load_zsub<VC, NGV>(vv, tile + 8 * q4, zsub);
       // ---- scores ----
       float sc[2][GI];
@@ -341,7 +349,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
           for (int p2 = 0; p2 < 4; ++p2) {
             // copy vector elements to scalars before bit casts: clang miscompiles a bit cast
             // applied directly to an ext-vector element
-            const unsigned bv = b[p2], zv = zsub[j / JPG][p2];
+            const unsigned bv = b[p2], zv = zsub[VC::ZODD ? (j & 1) : 0][j / JPG][p2];
             const h2_t x = __builtin_bit_cast(h2_t, bv) + __builtin_bit_cast(h2_t, zv);
             b[p2] = __builtin_bit_cast(unsigned, x);
           }
@@ -352,6 +360,9 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       wave_lds_sync();
     }
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (VC::fac(j) != 1.0f) st.o[j] *= 1.0f / VC::fac(j);
 }
 
 // Fold the wave's state into its record (sum of l over the 16 token
@@ -452,9 +463,9 @@ __device__ __forceinline__ void attn_prologue(const AttnParams& P, LDS& L, int b
   __syncthreads();
   if (threadIdx.x < R * NGK) {
     const int m = threadIdx.x / NGK, g = threadIdx.x % NGK, w = 128 / NGK;
-    float s = 0.0f;
-    for (int d = g * w; d < (g + 1) * w; ++d) s += L.q[m][d];
-    L.qg[m][g] = s;
+    double s = 0.0;  // exact for up to 128 fp16 terms: one rounding to binary32
+    for (int d = g * w; d < (g + 1) * w; ++d) s += (double)L.q[m][d];
+    L.qg[m][g] = (float)s;
   }
   const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
   const int m = GI == 1 ? 0 : min(n16, R - 1);
