@@ -33,10 +33,12 @@ struct AttnLds {
   } u;
 };
 
-// Meta of the two tokens of a lane's score column (token nb*16 + n16).
+// Meta of the token of a lane's score column (token nb*16 + n16).  Rows past
+// the valid range are read too (they lie inside the allocation); callers mask
+// what they produce (scores to -inf, weights to 0), so no branch and no early
+// wait on the loads is needed here.
 template <int NG, bool SYM>
-__device__ __forceinline__ void load_tok_meta(const TokView& v, int row, float (&s)[NG], float (&z)[NG],
-                                              bool valid) {
+__device__ __forceinline__ void load_tok_meta(const TokView& v, int row, float (&s)[NG], float (&z)[NG]) {
   if constexpr (NG == 1) {
     s[0] = v.scale[row];
   } else if constexpr (NG == 2) {
@@ -56,10 +58,6 @@ __device__ __forceinline__ void load_tok_meta(const TokView& v, int row, float (
     else zw = *reinterpret_cast<const unsigned*>(v.zero + (long long)row * 4);
 #pragma unroll
     for (int g = 0; g < NG; ++g) z[g] = (float)((zw >> (8 * g)) & 0xFFu);
-  }
-  if (!valid) {
-#pragma unroll
-    for (int g = 0; g < NG; ++g) { s[g] = 0.0f; z[g] = 0.0f; }
   }
 }
 
@@ -201,9 +199,9 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       for (int nb = 0; nb < 2; ++nb) {
         const int t = tile + nb * 16 + n16;
         ok[nb] = t >= t0 && t < t1;
-        if constexpr (!CHANK && !KC::F16) load_tok_meta<NGK, KC::SYM>(kv, t, sk[nb], zk[nb], ok[nb]);
+        if constexpr (!CHANK && !KC::F16) load_tok_meta<NGK, KC::SYM>(kv, t, sk[nb], zk[nb]);
         // V zero-points enter through zsub below; only the scales are needed here
-        if constexpr (!VC::F16) load_tok_meta<NGV, true>(vv, t, sv[nb], zv[nb], ok[nb]);
+        if constexpr (!VC::F16) load_tok_meta<NGV, true>(vv, t, sv[nb], zv[nb]);
       }
       if constexpr (VC::F16) {
 #pragma unroll
@@ -319,8 +317,8 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
             w0 = p[0][i];
             w1 = p[1][i];
           } else {
-            w0 = p[0][i] * sv[0][g];
-            w1 = p[1][i] * sv[1][g];
+            w0 = ok[0] ? p[0][i] * sv[0][g] : 0.0f;
+            w1 = ok[1] ? p[1][i] * sv[1][g] : 0.0f;
           }
           unsigned hi, lo;
           split_pair(w0, w1, hi, lo);
