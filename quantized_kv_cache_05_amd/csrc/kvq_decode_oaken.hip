@@ -53,45 +53,73 @@ __device__ __forceinline__ void row_oscale(const SparseView& sv, long long row, 
   }
 }
 
-// One lane per row of the split: f(lane's row r, channel idx, x_hat) for each
-// of its entries, four entry loads in flight at a time.  begin(r) is called
-// first for each valid row (and the wave), end(r) after its entries.
+// One lane per row of the split: begin(r), then f(r, channel idx, x_hat) for
+// each of row r's entries, then end(r), for every row r of the lane.  A lane
+// takes kRowsInFlight rows at a time and issues, before any use, the loads of
+// their outer scales and of the first kEntriesAhead entries of each row
+// (clamped to a valid address, masked at use), so a batch of rows costs one
+// memory round trip; the rare rows with more entries finish with a tail loop.
+constexpr int kRowsInFlight = 4, kEntriesAhead = 8;
+
+template <int NG>
+__device__ __forceinline__ float entry_value(const SparseView& sv, unsigned en, const float (&so)[NG],
+                                             int& idx) {
+  idx = (int)(en & 127u);
+  const float mag = (float)((en >> 8) & 31u);
+  float s = so[0];
+#pragma unroll
+  for (int g = 1; g < NG; ++g)
+    if (idx >= g * (128 / NG)) s = so[g];
+  return ((en >> 7) & 1u) ? sv.t_hi + mag * s : sv.t_lo - mag * s;
+}
+
 template <int NG, class B, class F, class E>
 __device__ __forceinline__ void for_row_entries(const SparseView& sv, int t0, int n,
                                                 const unsigned* rp, B&& begin, F&& f, E&& end) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int r0 = wave * 64; r0 < n; r0 += kNW * 64) {
-    const int r = r0 + lane;
-    const bool valid = r < n;
-    unsigned a = 0, c = 0;
-    float so[NG];
+  constexpr int kStride = kNW * 64;
+  if (sv.cap == 0) return;  // no list: every entry was dropped at append time
+  const unsigned last = sv.cap - 1;
+  for (int r0 = wave * 64; r0 < n; r0 += kRowsInFlight * kStride) {
+    unsigned a[kRowsInFlight], c[kRowsInFlight], en[kRowsInFlight][kEntriesAhead];
+    float so[kRowsInFlight][NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) so[g] = 0.0f;
-    if (valid) {
-      a = min(rp[r], sv.cap);
-      c = min(rp[r + 1], sv.cap) - a;
-      row_oscale<NG>(sv, t0 + r, so);
-      begin(r);
+    for (int k = 0; k < kRowsInFlight; ++k) {
+      const int r = r0 + k * kStride + lane;
+      const int rc = min(r, n - 1);
+      a[k] = min(rp[rc], sv.cap);
+      c[k] = r < n ? min(rp[rc + 1], sv.cap) - a[k] : 0u;
+      row_oscale<NG>(sv, t0 + rc, so[k]);
+#pragma unroll
+      for (int j = 0; j < kEntriesAhead; ++j) en[k][j] = sv.sparse[min(a[k] + j, last)];
     }
-    for (unsigned j = 0; __any(j < c); j += 4) {
-      unsigned en[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) en[k] = j + k < c ? (unsigned)sv.sparse[a + j + k] : 0u;
+    for (int k = 0; k < kRowsInFlight; ++k) {
+      const int r = r0 + k * kStride + lane;
+      if (r < n) begin(r);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (j + k < c) {
-          const int idx = (int)(en[k] & 127u);
-          const float mag = (float)((en[k] >> 8) & 31u);
-          float s = so[0];
-#pragma unroll
-          for (int g = 1; g < NG; ++g)
-            if (idx >= g * (128 / NG)) s = so[g];
-          const float xh = ((en[k] >> 7) & 1u) ? sv.t_hi + mag * s : sv.t_lo - mag * s;
+      for (int j = 0; j < kEntriesAhead; ++j) {
+        if (j < (int)c[k]) {
+          int idx;
+          const float xh = entry_value<NG>(sv, en[k][j], so[k], idx);
           f(r, idx, xh);
         }
       }
+      for (unsigned j = kEntriesAhead; __any(j < c[k]); j += 4) {
+        unsigned e4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) e4[q] = sv.sparse[min(a[k] + j + q, last)];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (j + q < c[k]) {
+            int idx;
+            const float xh = entry_value<NG>(sv, e4[q], so[k], idx);
+            f(r, idx, xh);
+          }
+        }
+      }
+      if (r < n) end(r);
     }
-    if (valid) end(r);
   }
 }
 
