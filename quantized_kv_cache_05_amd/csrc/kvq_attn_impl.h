@@ -7,11 +7,29 @@
 namespace kvq {
 
 // QR = query rows a workgroup serves (1, 4 or 16 query heads of one KV
-// head); GI = query rows per lane row group in the C layouts (1 or 4).
+// head).  Query rows sit in the A operands as follows:
+//  QR 1:  every A row holds query 0; a lane uses C element 0;
+//  QR 4:  A row 4m holds query m, the other rows are zero ("diagonal"): lane
+//         group q4 then finds query q4 in C element 0, so every lane keeps one
+//         softmax row, as for QR 1, instead of four mostly redundant ones;
+//  QR 16: A row r holds query r; a lane keeps the four C rows 4*q4 + i.
+// GI = softmax rows a lane keeps (1 or 4).
 template <int QR>
 struct QRows {
   static constexpr int R = QR;
-  static constexpr int GI = QR == 1 ? 1 : 4;
+  static constexpr bool DIAG = QR == 4;
+  static constexpr int GI = QR == 16 ? 4 : 1;
+  // query held by A-operand row r (-1: a zero row)
+  __device__ static int arow_query(int r) {
+    if constexpr (QR == 1) return 0;
+    else if constexpr (DIAG) return (r & 3) ? -1 : (r >> 2);
+    else return min(r, R - 1);
+  }
+  // query of softmax slot i of a lane in row group q4, and its C element
+  __device__ static int slot_query(int q4, int i) { return QR == 1 ? 0 : (DIAG ? q4 : 4 * q4 + i); }
+  static constexpr int slot_elem(int i) { return DIAG ? 0 : i; }
+  // whether the lane owns (writes) slot i: one lane group for QR 1
+  __device__ static bool slot_owner(int q4) { return QR != 1 || q4 == 0; }
 };
 
 // Workgroup-shared LDS: the query tile, per-group query sums, and a per-wave
@@ -133,12 +151,11 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
                                             const TokView& vv, const ChanView& kc, float* oak_sc,
                                             int oak_span, int nq, int t0, int t1, int wave,
                                             const u4_t (&qop)[4]) {
-  constexpr int R = QR, GI = QRows<QR>::GI;
+  using QRW = QRows<QR>;
+  constexpr int R = QR, GI = QRW::GI;
   static_assert(LDS::R == QR, "LDS tables sized for QR query rows");
   const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
-  // table row of the A-operand row n16 and of C-layout row 4*q4 + i (rows past QR
-  // are padding and repeat the last table row)
-  auto arow = [&](int x) { return GI == 1 ? 0 : min(x, R - 1); };
+  const int aq = QRW::arow_query(n16);  // query of this lane's A-operand row (-1: zero row)
   auto& W = L.u.wave[wave];
   const int tb = t0 & ~(kTile * TPS - 1);
   // the running output is held in natural units between calls; inside, block
@@ -154,7 +171,8 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       const int blk = step >> 6;
       const float* sp = kc.scale + (long long)blk * 128;
       const uint8_t* zp = kc.zero + (long long)blk * 128;
-      const int m = arow(n16);
+      const int m = max(aq, 0);
+      const float az = aq < 0 ? 0.0f : 1.0f;
       float part = 0.0f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -165,7 +183,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
         const float sc[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float a = L.q[m][c0 + v] * sc[v], b = L.q[m][c0 + v + 4] * sc[v + 4];
+          const float a = az * L.q[m][c0 + v] * sc[v], b = az * L.q[m][c0 + v + 4] * sc[v + 4];
           unsigned hi, lo;
           split_pair(a, b, hi, lo);
           qh[s][v] = hi;
@@ -178,9 +196,9 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       }
       part += __shfl_xor(part, 16, 64);
       part += __shfl_xor(part, 32, 64);
-      // part now holds the bias of query n16; rows of this lane are 4*q4 + i
+      // part now holds the bias of A row n16; slot i of this lane reads C row 4*q4 + elem(i)
 #pragma unroll
-      for (int i = 0; i < GI; ++i) cbias[i] = __shfl(part, GI == 1 ? 0 : 4 * q4 + i, 64);
+      for (int i = 0; i < GI; ++i) cbias[i] = __shfl(part, QR == 1 ? 0 : 4 * q4 + QRW::slot_elem(i), 64);
     }
 #pragma unroll
     for (int tt = 0; tt < TPS; ++tt) {
@@ -226,7 +244,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
             c = mfma(ql[s], kb, c);
           }
 #pragma unroll
-          for (int i = 0; i < GI; ++i) sc[nb][i] = (c[i] - cbias[i]) * P.qscale;
+          for (int i = 0; i < GI; ++i) sc[nb][i] = (c[QRW::slot_elem(i)] - cbias[i]) * P.qscale;
         }
       } else {
 #pragma unroll
@@ -238,15 +256,16 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
           for (int s = 0; s < 4; ++s) c[s / (4 / NGK)] = mfma(qop[s], kr[nb].slice(s), c[s / (4 / NGK)]);
 #pragma unroll
           for (int i = 0; i < GI; ++i) {
-            const int m = arow(4 * q4 + i);
+            const int m = min(QRW::slot_query(q4, i), R - 1);
+            const int e = QRW::slot_elem(i);
             float a;
             if constexpr (KC::F16) {
-              a = c[0][i];
+              a = c[0][e];
             } else {
               a = 0.0f;
 #pragma unroll
               for (int g = 0; g < NGK; ++g)
-                a = fmaf(sk[nb][g], fmaf(-(zk[nb][g] + (float)KC::OFF), L.qg[m][g], c[g][i]), a);
+                a = fmaf(sk[nb][g], fmaf(-(zk[nb][g] + (float)KC::OFF), L.qg[m][g], c[g][e]), a);
             }
             sc[nb][i] = a * P.qscale;
           }
@@ -258,7 +277,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
           for (int i = 0; i < GI; ++i) {
-            const int m = GI == 1 ? 0 : 4 * q4 + i;
+            const int m = QRW::slot_query(q4, i);
             const int t = tile + nb * 16 + n16;
             if (ok[nb] && m < nq) sc[nb][i] = fmaf(oak_sc[m * oak_span + (t - t0)], P.qscale, sc[nb][i]);
           }
@@ -283,7 +302,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
           const float a = alpha[i];
           st.l[i] *= a;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) st.o[j][i] *= a;
+          for (int j = 0; j < 8; ++j) st.o[j][QRW::slot_elem(i)] *= a;
         }
       }
       float p[2][GI];
@@ -300,16 +319,16 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
           for (int i = 0; i < GI; ++i) {
-            const int m = GI == 1 ? 0 : 4 * q4 + i;
+            const int m = QRW::slot_query(q4, i);
             const int t = tile + nb * 16 + n16;
-            if (ok[nb] && m < nq && (GI != 1 || q4 == 0)) oak_sc[m * oak_span + (t - t0)] = sc[nb][i];
+            if (ok[nb] && m < nq && QRW::slot_owner(q4)) oak_sc[m * oak_span + (t - t0)] = sc[nb][i];
           }
       }
       // ---- weights p * s_v (binary32) -> fp16 hi / lo in LDS ----
 #pragma unroll
       for (int i = 0; i < GI; ++i) {
-        const int m = GI == 1 ? 0 : 4 * q4 + i;
-        const bool wr = (GI != 1 || q4 == 0) && m < R;
+        const int m = QRW::slot_query(q4, i);
+        const bool wr = QRW::slot_owner(q4) && m < R;
 #pragma unroll
         for (int g = 0; g < NGV; ++g) {
           float w0, w1;
@@ -333,11 +352,14 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       wave_lds_sync();
       // ---- O += W V ----
       u4_t wa[NGV][2];
-      const int mr = arow(n16);
+      const int mr = max(aq, 0);
 #pragma unroll
       for (int g = 0; g < NGV; ++g)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) wa[g][h] = *reinterpret_cast<const u4_t*>(&W.w[g][h][mr][8 * q4]);
+        for (int h = 0; h < 2; ++h) {
+          wa[g][h] = *reinterpret_cast<const u4_t*>(&W.w[g][h][mr][8 * q4]);
+          if (aq < 0) wa[g][h] = u4_t{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         constexpr int JPG = 8 / NGV;
@@ -374,14 +396,15 @@ __device__ __forceinline__ void wave_record(LDS& L, SoftState<QRows<QR>::GI>& st
   for (int i = 0; i < GI; ++i) lt[i] = sum16(st.l[i]);
   __syncthreads();
   auto& rec = L.u.rec[wave];
+  using QRW = QRows<QR>;
 #pragma unroll
   for (int i = 0; i < GI; ++i) {
-    const int m = GI == 1 ? 0 : 4 * q4 + i;
-    if (GI == 1 && q4 != 0) continue;
+    const int m = QRW::slot_query(q4, i);
+    if (!QRW::slot_owner(q4)) continue;
     if (m >= nq) continue;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      rec.o[m][16 * j + n16] = st.o[j][i];
+      rec.o[m][16 * j + n16] = st.o[j][QRW::slot_elem(i)];
     }
     if (n16 == 0) {
       rec.o[m][128] = st.m[i];
@@ -466,14 +489,15 @@ __device__ __forceinline__ void attn_prologue(const AttnParams& P, LDS& L, int b
     L.qg[m][g] = (float)s;
   }
   const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
-  const int m = GI == 1 ? 0 : min(n16, R - 1);
+  const int aq = QRows<QR>::arow_query(n16);
+  const int m = max(aq, 0);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int c0 = 32 * s + 8 * q4;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const h2_t h = {(_Float16)L.q[m][c0 + v], (_Float16)L.q[m][c0 + v + 4]};
-      qop[s][v] = __builtin_bit_cast(unsigned, h);
+      qop[s][v] = aq < 0 ? 0u : __builtin_bit_cast(unsigned, h);
     }
   }
   __syncthreads();
