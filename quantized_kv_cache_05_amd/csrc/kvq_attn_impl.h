@@ -58,22 +58,27 @@ struct AttnLds {
 template <int NG, bool SYM>
 __device__ __forceinline__ void load_tok_meta(const TokView& v, int row, float (&s)[NG], float (&z)[NG]) {
   if constexpr (NG == 1) {
-    s[0] = v.scale[row];
+    s[0] = ld_nt<float>(v.scale + row);
   } else if constexpr (NG == 2) {
-    const float2 t = *reinterpret_cast<const float2*>(v.scale + (long long)row * 2);
-    s[0] = t.x; s[1] = t.y;
+    const u2_t t = ld_nt<u2_t>(v.scale + (long long)row * 2);
+    const unsigned t0 = t[0], t1 = t[1];
+    s[0] = __builtin_bit_cast(float, t0); s[1] = __builtin_bit_cast(float, t1);
   } else {
-    const float4 t = *reinterpret_cast<const float4*>(v.scale + (long long)row * 4);
-    s[0] = t.x; s[1] = t.y; s[2] = t.z; s[3] = t.w;
+    const u4_t t = ld_nt<u4_t>(v.scale + (long long)row * 4);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const unsigned tg = t[g];  // scalar copy before the bit cast (see the V product)
+      s[g] = __builtin_bit_cast(float, tg);
+    }
   }
   if constexpr (SYM) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) z[g] = 0.0f;
   } else {
     unsigned zw;
-    if constexpr (NG == 1) zw = v.zero[row];
-    else if constexpr (NG == 2) zw = *reinterpret_cast<const uint16_t*>(v.zero + (long long)row * 2);
-    else zw = *reinterpret_cast<const unsigned*>(v.zero + (long long)row * 4);
+    if constexpr (NG == 1) zw = ld_nt<uint8_t>(v.zero + row);
+    else if constexpr (NG == 2) zw = ld_nt<uint16_t>(v.zero + (long long)row * 2);
+    else zw = ld_nt<unsigned>(v.zero + (long long)row * 4);
 #pragma unroll
     for (int g = 0; g < NG; ++g) z[g] = (float)((zw >> (8 * g)) & 0xFFu);
   }
@@ -97,13 +102,13 @@ __device__ __forceinline__ void load_zsub(const TokView& vv, int r0, u4_t (&zsub
     unsigned zw[2 * NGV];
     const uint8_t* zp = vv.zero + (long long)r0 * NGV;
     if constexpr (NGV == 1) {
-      const u2_t t = *reinterpret_cast<const u2_t*>(zp);
+      const u2_t t = ld_nt<u2_t>(zp);
       zw[0] = t[0];
       zw[1] = t[1];
     } else {
 #pragma unroll
       for (int k = 0; k < NGV / 2; ++k) {
-        const u4_t t = *reinterpret_cast<const u4_t*>(zp + 16 * k);
+        const u4_t t = ld_nt<u4_t>(zp + 16 * k);
 #pragma unroll
         for (int e = 0; e < 4; ++e) zw[4 * k + e] = t[e];
       }
