@@ -67,14 +67,6 @@ __host__ __device__ constexpr unsigned sel_bytes(int a) {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Streaming load of packed cache data: every byte is read once per decode
-// step, so the loads carry the non-temporal hint (they do not displace
-// reusable lines in the caches), which measurably raises the achieved HBM
-// bandwidth of the decode loop.
-template <class T>
-__device__ __forceinline__ T ld_nt(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
-}
 
 // (x & m) | c as one v_and_or_b32.  VOP3 encodings take no literal
 // constants on this target, so with literal m and c the compiler emits an AND

@@ -67,6 +67,17 @@ __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint
   }
 }
 
+typedef unsigned u4q_t __attribute__((ext_vector_type(4)));
+typedef unsigned u2q_t __attribute__((ext_vector_type(2)));
+
+// 16 bytes of input (8 fp16 values), streamed
+__device__ __forceinline__ uint4 ld_row8(const uint16_t* p) {
+  const u4q_t t = ld_nt<u4q_t>(p);
+  const unsigned a = t[0], b = t[1], c = t[2], d = t[3];
+  return make_uint4(a, b, c, d);
+}
+__device__ __forceinline__ void st_u4(uint8_t* p, uint4 v) { st_nt<u4q_t>(p, u4q_t{v.x, v.y, v.z, v.w}); }
+
 __device__ __forceinline__ void unpack8(const uint4 raw, float (&v)[8]) {
   v[0] = lo_h2f(raw.x); v[1] = hi_h2f(raw.x);
   v[2] = lo_h2f(raw.y); v[3] = hi_h2f(raw.y);
@@ -77,11 +88,11 @@ __device__ __forceinline__ void unpack8(const uint4 raw, float (&v)[8]) {
 template <int BITS>
 __device__ __forceinline__ void store_codes8(uint8_t* row, int slot, uint32_t plo, uint32_t phi) {
   if constexpr (BITS == 8) {
-    *reinterpret_cast<uint2*>(row + slot * 8) = make_uint2(plo, phi);
+    st_nt<u2q_t>(row + slot * 8, u2q_t{plo, phi});
   } else if constexpr (BITS == 4) {
-    *reinterpret_cast<uint32_t*>(row + slot * 4) = plo;
+    st_nt<uint32_t>(row + slot * 4, plo);
   } else {
-    *reinterpret_cast<uint16_t*>(row + slot * 2) = (uint16_t)plo;
+    st_nt<uint16_t>(row + slot * 2, (uint16_t)plo);
   }
 }
 
@@ -128,7 +139,7 @@ __device__ __forceinline__ void store_row_f16(uint8_t* row, int li, uint4 raw, u
     o.y = __builtin_amdgcn_perm(raw.z, raw.x, 0x07060302u);
     o.z = __builtin_amdgcn_perm(raw.w, raw.y, 0x05040100u);
     o.w = __builtin_amdgcn_perm(raw.w, raw.y, 0x07060302u);
-    *reinterpret_cast<uint4*>(row + k_slot(li) * 16) = o;
+    st_u4(row + k_slot(li) * 16, o);
   } else {
     const uint32_t d[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -139,7 +150,7 @@ __device__ __forceinline__ void store_row_f16(uint8_t* row, int li, uint4 raw, u
     for (int k = 0; k < 4; ++k)
       w[k] = (uint32_t)lrow[li + 32 * k] | ((uint32_t)lrow[li + 32 * k + 16] << 16);
     wave_lds_sync();
-    *reinterpret_cast<uint4*>(row + li * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    st_u4(row + li * 16, make_uint4(w[0], w[1], w[2], w[3]));
   }
 }
 
@@ -168,7 +179,7 @@ __global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict_
   }
   const long long dst = bh * S + p + t;
   float v[8];
-  unpack8(*reinterpret_cast<const uint4*>(x + row * kD + li * 8), v);
+  unpack8(ld_row8(x + row * kD + li * 8), v);
   uint32_t plo, phi;
   float s;
   int z;
@@ -209,7 +220,7 @@ __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restric
   for (int pass = 0; pass < 4; ++pass) {
     const int r = pass * 16 + (threadIdx.x >> 4), li = threadIdx.x & 15;
     float v[8];
-    unpack8(*reinterpret_cast<const uint4*>(xb + r * kD + li * 8), v);
+    unpack8(ld_row8(xb + r * kD + li * 8), v);
 #pragma unroll
     for (int k = 0; k < 8; ++k) tile[r][li * 8 + k] = v[k];
   }
@@ -290,7 +301,7 @@ __global__ __launch_bounds__(256) void k_quant_mixed(
   const int li = threadIdx.x & 15;
   uint16_t* lrow = lrows[VL ? (threadIdx.x >> 4) : 0];
   for (int r = threadIdx.x >> 4; r < CT; r += 16) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(xs + (long long)r * kD + li * 8);
+    const uint4 raw = ld_row8(xs + (long long)r * kD + li * 8);
     const long long drow = drow0 + r;
     if (cls == 0) {
       store_row_f16<VL>(c16 + drow * kD * 2, li, raw, lrow);
@@ -354,7 +365,7 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
     float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     unsigned outer = 0;
     if (active) {
-      unpack8(*reinterpret_cast<const uint4*>(x + (bh * t_new + t) * kD + li * 8), v);
+      unpack8(ld_row8(x + (bh * t_new + t) * kD + li * 8), v);
 #pragma unroll
       for (int k = 0; k < 8; ++k) outer |= (unsigned)((v[k] > t_hi) || (v[k] < t_lo)) << k;
     }
