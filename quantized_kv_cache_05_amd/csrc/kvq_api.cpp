@@ -172,10 +172,12 @@ kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HI
 
 // Split planning.  One workgroup (4 waves) per (b, kv head, query tile)
 // already fills the GPU when there are at least kWideUnits of them; fewer
-// units are split along the sequence towards kTargetGroups workgroups, and
-// the partials merged by a second kernel.
+// units are split along the sequence towards one round of resident
+// workgroups (256 CUs x the workgroups a CU holds at the kernel's register
+// use: 4 for one query row, 3 for four, 2 for sixteen), and the partials
+// merged by a second kernel.
 constexpr long long kWideUnits = 384;
-constexpr long long kTargetGroups = 1024;
+long long target_groups(int qr) { return qr == 1 ? 1024 : (qr == 4 ? 768 : 512); }
 
 struct Plan {
   int G, qr, qtiles, num_splits, split_len;
@@ -207,7 +209,8 @@ kvq_status plan_decode(const kvq_cache* c, int q_heads, int max_len, int num_spl
   }
   long long ns = num_splits;
   if (ns == 0) {
-    ns = units >= kWideUnits ? 1 : (kTargetGroups + units - 1) / units;
+    const long long groups = target_groups(p->qr);
+    ns = units >= kWideUnits ? 1 : (groups + units - 1) / units;
     const long long most = (length + min_piece - 1) / min_piece;
     if (ns > most) ns = most;
   }

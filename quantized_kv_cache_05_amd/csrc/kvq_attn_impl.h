@@ -2,6 +2,8 @@
 // operand layouts).  Kernels in kvq_decode_*.hip instantiate attend_wave for
 // their codecs and finish with finish_split.
 #pragma once
+#include <type_traits>
+
 #include "kvq_attn.h"
 
 namespace kvq {
@@ -34,11 +36,19 @@ struct QRows {
 
 // Workgroup-shared LDS: the query tile, per-group query sums, and a per-wave
 // scratch area that the epilogue reuses for the wave records.
-template <int QR, int NGV>
+template <int QR, int NGV, bool CHANK_ = false>
 struct AttnLds {
   static constexpr int R = QR;
   float q[R][128];       // query tile (fp16 values in binary32)
   float qg[R][4];        // sum of the query over each K channel group
+  // channel-axis K: per wave, the block's scaled query as MFMA A-operand
+  // entries [hi / lo][k-step s][query m][lane group q4] (see attend_wave)
+  struct __attribute__((aligned(16))) QTab {
+    u4_t e[2][4][R][4];
+  };
+  // (a placeholder of one entry's alignment when K has token-axis groups)
+  struct Empty {};
+  typename std::conditional<CHANK_, QTab[kNW], Empty>::type qtab;
   struct __attribute__((aligned(16))) Wave {
     unsigned short w[NGV][2][R][kTile];  // softmax weights hi / lo, [V group][query][token]
   };
@@ -170,40 +180,61 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
     if (VC::fac(j) != 1.0f) st.o[j] *= VC::fac(j);
   for (int step = tb + wave * kTile * TPS; step < t1; step += kNW * kTile * TPS) {
     // ---- channel-axis K: fold the block's scales into the query ----
-    u4_t qh[4], ql[4];
+    // The R x 128 products q[m][d] * s[d] are spread over the wave: entry
+    // (s, m, q4e) covers channels 32 s + 8 q4e + (v, v + 4), v < 4; it is
+    // split into fp16 hi + lo pairs and stored in the wave's LDS table, from
+    // which the tile loop's A-operand lanes read it.  Each query's bias
+    // sum_d q[m][d] s[d] (OFF + z[d]) is reduced over its entries.
     float cbias[GI];
     if constexpr (CHANK) {
       const int blk = step >> 6;
       const float* sp = kc.scale + (long long)blk * 128;
       const uint8_t* zp = kc.zero + (long long)blk * 128;
-      const int m = max(aq, 0);
-      const float az = aq < 0 ? 0.0f : 1.0f;
+      auto& T = L.qtab[wave];
+      constexpr int NE = 16 * R, PER = (NE + 63) / 64;
       float part = 0.0f;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int c0 = 32 * s + 8 * q4;
-        const float4 sa = *reinterpret_cast<const float4*>(sp + c0);
-        const float4 sb = *reinterpret_cast<const float4*>(sp + c0 + 4);
-        const u2_t zz = *reinterpret_cast<const u2_t*>(zp + c0);
-        const float sc[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+      for (int k = 0; k < PER; ++k) {
+        const int e = lane + 64 * k;
+        if (e < NE) {
+          const int sl = e / (4 * R), m = (e >> 2) % R, qe = e & 3;
+          const int c0 = 32 * sl + 8 * qe;
+          const float4 sa = *reinterpret_cast<const float4*>(sp + c0);
+          const float4 sb = *reinterpret_cast<const float4*>(sp + c0 + 4);
+          const u2_t zz = *reinterpret_cast<const u2_t*>(zp + c0);
+          const float sc[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+          u4_t hi4, lo4;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float a = az * L.q[m][c0 + v] * sc[v], b = az * L.q[m][c0 + v + 4] * sc[v + 4];
-          unsigned hi, lo;
-          split_pair(a, b, hi, lo);
-          qh[s][v] = hi;
-          ql[s][v] = lo;
-          const float za = (float)((zz[0] >> (8 * v)) & 0xFFu) + (float)KC::OFF;
-          const float zb = (float)((zz[1] >> (8 * v)) & 0xFFu) + (float)KC::OFF;
-          part = fmaf(a, za, part);
-          part = fmaf(b, zb, part);
+          for (int v = 0; v < 4; ++v) {
+            const float a = L.q[m][c0 + v] * sc[v], b = L.q[m][c0 + v + 4] * sc[v + 4];
+            unsigned hi, lo;
+            split_pair(a, b, hi, lo);
+            hi4[v] = hi;
+            lo4[v] = lo;
+            const float za = (float)((zz[0] >> (8 * v)) & 0xFFu) + (float)KC::OFF;
+            const float zb = (float)((zz[1] >> (8 * v)) & 0xFFu) + (float)KC::OFF;
+            part = fmaf(a, za, part);
+            part = fmaf(b, zb, part);
+          }
+          T.e[0][sl][m][qe] = hi4;
+          T.e[1][sl][m][qe] = lo4;
         }
       }
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
-      // part now holds the bias of A row n16; slot i of this lane reads C row 4*q4 + elem(i)
+      // sum the entries of each query: lanes of query m differ in q4e (bits 0-1)
+      // and, for R <= 4, in the k-step (the bits above the query's)
+      part += __shfl_xor(part, 1, 64);
+      part += __shfl_xor(part, 2, 64);
+      if constexpr (R == 1) {
+        part += __shfl_xor(part, 4, 64);
+        part += __shfl_xor(part, 8, 64);
+      } else if constexpr (R == 4) {
+        part += __shfl_xor(part, 16, 64);
+        part += __shfl_xor(part, 32, 64);
+      }
+      // the sum of query m sits in lane 4 m (R > 1) or lane 0 (R == 1)
 #pragma unroll
-      for (int i = 0; i < GI; ++i) cbias[i] = __shfl(part, QR == 1 ? 0 : 4 * q4 + QRW::slot_elem(i), 64);
+      for (int i = 0; i < GI; ++i) cbias[i] = __shfl(part, R == 1 ? 0 : 4 * QRW::slot_query(q4, i), 64);
+      wave_lds_sync();
     }
 #pragma unroll
     for (int tt = 0; tt < TPS; ++tt) {
@@ -242,11 +273,14 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           f4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+          const auto& T = L.qtab[wave];
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             const u4_t kb = kr[nb].slice(s);
-            c = mfma(qh[s], kb, c);
-            c = mfma(ql[s], kb, c);
+            u4_t qh = T.e[0][s][max(aq, 0)][q4], ql = T.e[1][s][max(aq, 0)][q4];
+            if (aq < 0) qh = ql = u4_t{0u, 0u, 0u, 0u};
+            c = mfma(qh, kb, c);
+            c = mfma(ql, kb, c);
           }
 #pragma unroll
           for (int i = 0; i < GI; ++i) sc[nb][i] = (c[QRW::slot_elem(i)] - cbias[i]) * P.qscale;

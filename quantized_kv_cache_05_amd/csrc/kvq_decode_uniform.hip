@@ -5,9 +5,16 @@
 namespace kvq {
 namespace {
 
+// Occupancy target (waves per SIMD): two in general; four for the 4-query
+// per-channel-K kernels with 4- or 2-bit codes and two V groups, which fit
+// in 128 registers without spilling.
+template <int QR, class KC, int NGV, bool CHANK>
+constexpr int kUniformWaves = (CHANK && QR == 4 && NGV == 2 && KC::BITS <= 4) ? 4 : 2;
+
 template <int QR, class KC, class VC, int NGK, int NGV, bool CHANK>
-__global__ __launch_bounds__(256, 2) void k_attn_uniform(AttnParams P) {
-  __shared__ AttnLds<QR, NGV> L;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kUniformWaves<QR, KC, NGV, CHANK>)))
+void k_attn_uniform(AttnParams P) {
+  __shared__ AttnLds<QR, NGV, CHANK> L;
   const int split = blockIdx.x, qt = blockIdx.y % P.qtiles, kvh = blockIdx.y / P.qtiles, b = blockIdx.z;
   const int wave = threadIdx.x >> 6;
   const int nq = min(QR, P.G - qt * QR);
