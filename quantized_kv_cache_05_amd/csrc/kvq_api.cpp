@@ -276,10 +276,13 @@ kvq_status kvq_quant_append(const kvq_cache* c, const void* k_new, const void* v
       if (c->k.axis == KVQ_AXIS_CHANNEL) {
         if (t_new % 64) return KVQ_ERR_INVALID_ARG;
         e = kvq::launch_quant_channel(a, a.k, kx, t_new, pos, st);
+        if (e == hipSuccess) e = kvq::launch_quant_token(a, a.v, true, vx, t_new, pos, st);
+      } else if (a.k.bits == a.v.bits && a.k.sym == a.v.sym && a.k.group == a.v.group) {
+        e = kvq::launch_quant_token_kv(a, kx, vx, t_new, pos, st);
       } else {
         e = kvq::launch_quant_token(a, a.k, false, kx, t_new, pos, st);
+        if (e == hipSuccess) e = kvq::launch_quant_token(a, a.v, true, vx, t_new, pos, st);
       }
-      if (e == hipSuccess) e = kvq::launch_quant_token(a, a.v, true, vx, t_new, pos, st);
       break;
     case KVQ_MODE_OAKEN:
       e = kvq::launch_quant_oaken(a, a.k, false, kx, t_new, pos, st);

@@ -57,6 +57,9 @@ struct DecodeLaunch {
 };
 
 // vl: write the V row layout (else the K row layout), see kvq.h.
+// K and V in one launch; both tensors token-axis with equal bits, sym and group.
+hipError_t launch_quant_token_kv(const CacheArgs& c, const uint16_t* xk, const uint16_t* xv, int t_new,
+                                 const int* pos, hipStream_t st);
 hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
                               int t_new, const int* pos, hipStream_t st);
 hipError_t launch_quant_channel(const CacheArgs& c, const TensorArgs& t, const uint16_t* x, int t_new,

@@ -157,15 +157,14 @@ __device__ __forceinline__ void store_row_f16(uint8_t* row, int li, uint4 raw, u
 // ---------------------------------------------------------------------------
 // Uniform cache, token-axis groups.  x: [B][H][t_new][128], rows in that order.
 // VL selects the V row layout.
+// One token row per 16 lanes; lrow: the row's wave-local exchange area (V).
 template <int BITS, bool SYM, int GE, bool VL>
-__global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict__ x, int t_new, int H,
-                                                     int S, const int* __restrict__ pos,
-                                                     long long rows, uint8_t* __restrict__ codes,
-                                                     float* __restrict__ scale,
-                                                     uint8_t* __restrict__ zero,
-                                                     unsigned* __restrict__ status) {
+__device__ __forceinline__ void quant_token_row(const uint16_t* __restrict__ x, int t_new, int H, int S,
+                                                const int* __restrict__ pos, long long rows,
+                                                uint8_t* __restrict__ codes, float* __restrict__ scale,
+                                                uint8_t* __restrict__ zero, unsigned* __restrict__ status,
+                                                uint16_t* lrow) {
   constexpr int NG = kD / GE, LG = GE / 8, RB = kD * BITS / 8;
-  __shared__ uint16_t lrows[VL ? 16 : 1][128];
   const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int li = threadIdx.x & 15;
   if (row >= rows) return;  // all 16 lanes of a row leave together
@@ -184,11 +183,40 @@ __global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict_
   float s;
   int z;
   quant8<BITS, SYM, GE>(v, 0xFFu, plo, phi, s, z);
-  store_row_codes<BITS, VL>(codes + dst * RB, li, plo, phi, lrows[VL ? (threadIdx.x >> 4) : 0]);
+  store_row_codes<BITS, VL>(codes + dst * RB, li, plo, phi, lrow);
   if (li % LG == 0) {
     scale[dst * NG + li / LG] = s;
     if constexpr (!SYM) zero[dst * NG + li / LG] = (uint8_t)z;
   }
+}
+
+template <int BITS, bool SYM, int GE, bool VL>
+__global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict__ x, int t_new, int H,
+                                                     int S, const int* __restrict__ pos,
+                                                     long long rows, uint8_t* __restrict__ codes,
+                                                     float* __restrict__ scale,
+                                                     uint8_t* __restrict__ zero,
+                                                     unsigned* __restrict__ status) {
+  __shared__ uint16_t lrows[VL ? 16 : 1][128];
+  quant_token_row<BITS, SYM, GE, VL>(x, t_new, H, S, pos, rows, codes, scale, zero, status,
+                                     lrows[VL ? (threadIdx.x >> 4) : 0]);
+}
+
+// K and V of the same token-axis format in one launch: blockIdx.y selects the
+// tensor (0: K rows, 1: V rows), so a decode-step append costs one launch.
+template <int BITS, bool SYM, int GE>
+__global__ __launch_bounds__(256) void k_quant_token_kv(const uint16_t* __restrict__ xk,
+                                                        const uint16_t* __restrict__ xv, int t_new, int H,
+                                                        int S, const int* __restrict__ pos, long long rows,
+                                                        TensorArgs tk, TensorArgs tv,
+                                                        unsigned* __restrict__ status) {
+  __shared__ uint16_t lrows[16][128];
+  if (blockIdx.y == 0)
+    quant_token_row<BITS, SYM, GE, false>(xk, t_new, H, S, pos, rows, tk.codes, tk.scale, tk.zero, status,
+                                          lrows[0]);
+  else
+    quant_token_row<BITS, SYM, GE, true>(xv, t_new, H, S, pos, rows, tv.codes, tv.scale, tv.zero, status,
+                                         lrows[threadIdx.x >> 4]);
 }
 
 // ---------------------------------------------------------------------------
@@ -434,6 +462,38 @@ constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------------------
 // Launchers
+
+hipError_t launch_quant_token_kv(const CacheArgs& c, const uint16_t* xk, const uint16_t* xv, int t_new,
+                                 const int* pos, hipStream_t st) {
+  const TensorArgs& t = c.k;
+  const long long rows = (long long)c.B * c.H * t_new;
+  const dim3 grid((unsigned)((rows + 15) / 16), 2);
+#define KVQ_TOK(BITS, SYM, GE)                                                                       \
+  hipLaunchKernelGGL((k_quant_token_kv<BITS, SYM, GE>), grid, dim3(kThreads), 0, st, xk, xv, t_new, \
+                     c.H, c.S, pos, rows, c.k, c.v, c.status)
+#define KVQ_TOK_G(BITS, SYM)                  \
+  switch (t.group) {                          \
+    case 32: KVQ_TOK(BITS, SYM, 32); break;   \
+    case 64: KVQ_TOK(BITS, SYM, 64); break;   \
+    case 128: KVQ_TOK(BITS, SYM, 128); break; \
+    default: return hipErrorInvalidValue;     \
+  }
+  if (t.sym) {
+    if (t.bits != 8) return hipErrorInvalidValue;
+    KVQ_TOK_G(8, true);
+  } else if (t.bits == 8) {
+    KVQ_TOK_G(8, false);
+  } else if (t.bits == 4) {
+    KVQ_TOK_G(4, false);
+  } else if (t.bits == 2) {
+    KVQ_TOK_G(2, false);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef KVQ_TOK_G
+#undef KVQ_TOK
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
                               int t_new, const int* pos, hipStream_t st) {
