@@ -285,8 +285,12 @@ kvq_status kvq_quant_append(const kvq_cache* c, const void* k_new, const void* v
       }
       break;
     case KVQ_MODE_OAKEN:
-      e = kvq::launch_quant_oaken(a, a.k, false, kx, t_new, pos, st);
-      if (e == hipSuccess) e = kvq::launch_quant_oaken(a, a.v, true, vx, t_new, pos, st);
+      if (t_new == 1 && a.k.group == a.v.group) {
+        e = kvq::launch_quant_oaken_one(a, kx, vx, pos, st);
+      } else {
+        e = kvq::launch_quant_oaken(a, a.k, false, kx, t_new, pos, st);
+        if (e == hipSuccess) e = kvq::launch_quant_oaken(a, a.v, true, vx, t_new, pos, st);
+      }
       break;
     case KVQ_MODE_CHUNK_MIXED:
       if (t_new != c->max_seq) return KVQ_ERR_INVALID_ARG;

@@ -60,6 +60,9 @@ struct DecodeLaunch {
 // K and V in one launch; both tensors token-axis with equal bits, sym and group.
 hipError_t launch_quant_token_kv(const CacheArgs& c, const uint16_t* xk, const uint16_t* xv, int t_new,
                                  const int* pos, hipStream_t st);
+// Oaken append of one token per sequence, K and V in one launch (equal groups).
+hipError_t launch_quant_oaken_one(const CacheArgs& c, const uint16_t* xk, const uint16_t* xv,
+                                 const int* pos, hipStream_t st);
 hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
                               int t_new, const int* pos, hipStream_t st);
 hipError_t launch_quant_channel(const CacheArgs& c, const TensorArgs& t, const uint16_t* x, int t_new,

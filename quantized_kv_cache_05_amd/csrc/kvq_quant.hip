@@ -456,6 +456,86 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
   if (dropped) set_flag(status, kFlagSparseFull);
 }
 
+// Oaken append of one token per sequence, K and V in one launch
+// (blockIdx.y: 0 K rows, 1 V rows): 16 lanes per (b, h) row, 16 rows per
+// workgroup.  With one new token the rows are independent: each continues its
+// own (b, h) list at rowptr[pos].
+template <int GE>
+__global__ __launch_bounds__(256) void k_quant_oaken_one(const uint16_t* __restrict__ xk,
+                                                         const uint16_t* __restrict__ xv, int BH, int H,
+                                                         int S, const int* __restrict__ pos,
+                                                         TensorArgs tk, TensorArgs tv,
+                                                         unsigned* __restrict__ status) {
+  constexpr int NG = kD / GE, LG = GE / 8;
+  __shared__ uint16_t lrows[16][128];
+  const bool vl = blockIdx.y != 0;
+  const TensorArgs& t = vl ? tv : tk;
+  const uint16_t* x = vl ? xv : xk;
+  const int rl = threadIdx.x >> 4, li = threadIdx.x & 15;
+  const long long bh = (long long)blockIdx.x * 16 + rl;
+  if (bh >= BH) return;  // all 16 lanes of a row leave together
+  const int b = (int)(bh / H);
+  const int p = pos[b];
+  if (p < 0 || p + 1 > S) {
+    if (li == 0) set_flag(status, kFlagPosRange);
+    return;
+  }
+  uint32_t* rp = t.rowptr + bh * (S + 1);
+  uint16_t* sp = t.sparse + bh * t.sparse_cap;
+  const unsigned long long base = p == 0 ? 0ull : (unsigned long long)rp[p];
+  if (p == 0 && li == 0) rp[0] = 0u;
+  float v[8];
+  unpack8(ld_row8(x + bh * kD + li * 8), v);
+  unsigned outer = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) outer |= (unsigned)((v[k] > t.thr_hi) || (v[k] < t.thr_lo)) << k;
+  uint32_t plo, phi;
+  float s;
+  int z;
+  quant8<4, false, GE>(v, ~outer & 0xFFu, plo, phi, s, z);
+  float dmax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if ((outer >> k) & 1u) dmax = fmaxf(dmax, fabsf(v[k] > t.thr_hi ? v[k] - t.thr_hi : v[k] - t.thr_lo));
+  dmax = max_lanes<1, LG>(dmax);
+  const float so = dmax / 31.0f;
+  const int lc = __popc(outer);
+  int incl = lc;
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    const int o = __shfl_up(incl, m, 16);
+    if (li >= m) incl += o;
+  }
+  const int rowtot = __shfl(incl, 15, 16);
+  const long long dst = bh * S + p;
+  if (vl) store_row_codes<4, true>(t.codes + dst * 64, li, plo, phi, lrows[rl]);
+  else store_row_codes<4, false>(t.codes + dst * 64, li, plo, phi, lrows[rl]);
+  if (li % LG == 0) {
+    t.scale[dst * NG + li / LG] = s;
+    t.zero[dst * NG + li / LG] = (uint8_t)z;
+    t.oscale[dst * NG + li / LG] = so;
+  }
+  const unsigned long long cap = (unsigned long long)t.sparse_cap;
+  unsigned long long e = base + (unsigned)(incl - lc);
+  bool dropped = false;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if ((outer >> k) & 1u) {
+      const bool above = v[k] > t.thr_hi;
+      const float delta = above ? v[k] - t.thr_hi : v[k] - t.thr_lo;
+      int mag = 0;
+      if (so != 0.0f) mag = min(max((int)rintf(fabsf(delta) / so), 0), 31);
+      if (e < cap) sp[e] = (uint16_t)((li * 8 + k) | ((int)above << 7) | (mag << 8));
+      else dropped = true;
+      ++e;
+    }
+  if (li == 0) {
+    const unsigned long long end = base + (unsigned)rowtot;
+    rp[p + 1] = (uint32_t)(end < cap ? end : cap);
+  }
+  if (dropped) set_flag(status, kFlagSparseFull);
+}
+
 constexpr int kThreads = 256;
 
 }  // namespace
@@ -596,6 +676,19 @@ hipError_t launch_quant_oaken(const CacheArgs& c, const TensorArgs& t, bool vl, 
     default: return hipErrorInvalidValue;
   }
 #undef KVQ_OAK
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_oaken_one(const CacheArgs& c, const uint16_t* xk, const uint16_t* xv,
+                                 const int* pos, hipStream_t st) {
+  const int BH = c.B * c.H;
+  const dim3 grid((unsigned)((BH + 15) / 16), 2);
+  switch (c.k.group) {
+    case 32: hipLaunchKernelGGL((k_quant_oaken_one<32>), grid, dim3(kThreads), 0, st, xk, xv, BH, c.H, c.S, pos, c.k, c.v, c.status); break;
+    case 64: hipLaunchKernelGGL((k_quant_oaken_one<64>), grid, dim3(kThreads), 0, st, xk, xv, BH, c.H, c.S, pos, c.k, c.v, c.status); break;
+    case 128: hipLaunchKernelGGL((k_quant_oaken_one<128>), grid, dim3(kThreads), 0, st, xk, xv, BH, c.H, c.S, pos, c.k, c.v, c.status); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
