@@ -14,6 +14,8 @@
 // Thread layout of the token-axis kernels: 16 lanes per 128-channel row, each
 // lane holds 8 consecutive channels (one 16-byte load); a group of GE
 // channels is GE / 8 adjacent lanes, reduced with lane shuffles.
+#include <algorithm>
+
 #include "kvq_dev.h"
 
 namespace kvq {
@@ -159,13 +161,12 @@ __device__ __forceinline__ void store_row_f16(uint8_t* row, int li, uint4 raw, u
 // VL selects the V row layout.
 // One token row per 16 lanes; lrow: the row's wave-local exchange area (V).
 template <int BITS, bool SYM, int GE, bool VL>
-__device__ __forceinline__ void quant_token_row(const uint16_t* __restrict__ x, int t_new, int H, int S,
-                                                const int* __restrict__ pos, long long rows,
+__device__ __forceinline__ void quant_token_row(long long row, const uint16_t* __restrict__ x, int t_new,
+                                                int H, int S, const int* __restrict__ pos, long long rows,
                                                 uint8_t* __restrict__ codes, float* __restrict__ scale,
                                                 uint8_t* __restrict__ zero, unsigned* __restrict__ status,
                                                 uint16_t* lrow) {
   constexpr int NG = kD / GE, LG = GE / 8, RB = kD * BITS / 8;
-  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int li = threadIdx.x & 15;
   if (row >= rows) return;  // all 16 lanes of a row leave together
   const int t = (int)(row % t_new);
@@ -198,8 +199,10 @@ __global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict_
                                                      uint8_t* __restrict__ zero,
                                                      unsigned* __restrict__ status) {
   __shared__ uint16_t lrows[VL ? 16 : 1][128];
-  quant_token_row<BITS, SYM, GE, VL>(x, t_new, H, S, pos, rows, codes, scale, zero, status,
-                                     lrows[VL ? (threadIdx.x >> 4) : 0]);
+  // blocks of 16 rows, grid-strided: a bounded grid keeps the dispatch cost low
+  for (long long r0 = (long long)blockIdx.x * 16; r0 < rows; r0 += (long long)gridDim.x * 16)
+    quant_token_row<BITS, SYM, GE, VL>(r0 + (threadIdx.x >> 4), x, t_new, H, S, pos, rows, codes, scale,
+                                       zero, status, lrows[VL ? (threadIdx.x >> 4) : 0]);
 }
 
 // K and V of the same token-axis format in one launch: blockIdx.y selects the
@@ -211,12 +214,15 @@ __global__ __launch_bounds__(256) void k_quant_token_kv(const uint16_t* __restri
                                                         TensorArgs tk, TensorArgs tv,
                                                         unsigned* __restrict__ status) {
   __shared__ uint16_t lrows[16][128];
-  if (blockIdx.y == 0)
-    quant_token_row<BITS, SYM, GE, false>(xk, t_new, H, S, pos, rows, tk.codes, tk.scale, tk.zero, status,
-                                          lrows[0]);
-  else
-    quant_token_row<BITS, SYM, GE, true>(xv, t_new, H, S, pos, rows, tv.codes, tv.scale, tv.zero, status,
-                                         lrows[threadIdx.x >> 4]);
+  for (long long r0 = (long long)blockIdx.x * 16; r0 < rows; r0 += (long long)gridDim.x * 16) {
+    const long long row = r0 + (threadIdx.x >> 4);
+    if (blockIdx.y == 0)
+      quant_token_row<BITS, SYM, GE, false>(row, xk, t_new, H, S, pos, rows, tk.codes, tk.scale, tk.zero,
+                                            status, lrows[0]);
+    else
+      quant_token_row<BITS, SYM, GE, true>(row, xv, t_new, H, S, pos, rows, tv.codes, tv.scale, tv.zero,
+                                           status, lrows[threadIdx.x >> 4]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -537,6 +543,7 @@ __global__ __launch_bounds__(256) void k_quant_oaken_one(const uint16_t* __restr
 }
 
 constexpr int kThreads = 256;
+constexpr long long kRowBlocks = 4096;  // grid bound of the row kernels (blocks of 16 rows)
 
 }  // namespace
 
@@ -547,7 +554,7 @@ hipError_t launch_quant_token_kv(const CacheArgs& c, const uint16_t* xk, const u
                                  const int* pos, hipStream_t st) {
   const TensorArgs& t = c.k;
   const long long rows = (long long)c.B * c.H * t_new;
-  const dim3 grid((unsigned)((rows + 15) / 16), 2);
+  const dim3 grid((unsigned)std::min<long long>((rows + 15) / 16, kRowBlocks), 2);
 #define KVQ_TOK(BITS, SYM, GE)                                                                       \
   hipLaunchKernelGGL((k_quant_token_kv<BITS, SYM, GE>), grid, dim3(kThreads), 0, st, xk, xv, t_new, \
                      c.H, c.S, pos, rows, c.k, c.v, c.status)
@@ -578,7 +585,7 @@ hipError_t launch_quant_token_kv(const CacheArgs& c, const uint16_t* xk, const u
 hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
                               int t_new, const int* pos, hipStream_t st) {
   const long long rows = (long long)c.B * c.H * t_new;
-  const dim3 grid((unsigned)((rows + 15) / 16));
+  const dim3 grid((unsigned)std::min<long long>((rows + 15) / 16, kRowBlocks));
 #define KVQ_TOK(BITS, SYM, GE)                                                                      \
   do {                                                                                              \
     if (vl)                                                                                         \
