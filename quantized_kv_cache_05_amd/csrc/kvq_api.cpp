@@ -174,10 +174,16 @@ kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HI
 // already fills the GPU when there are at least kWideUnits of them; fewer
 // units are split along the sequence towards one round of resident
 // workgroups (256 CUs x the workgroups a CU holds at the kernel's register
-// use: 4 for one query row, 3 for four, 2 for sixteen), and the partials
-// merged by a second kernel.
+// use: 4 for one query row, 3 for four, 2 for sixteen; 4 for four rows with
+// channel-axis K of at most 4 bits and two V groups, whose kernel is built
+// for four waves per SIMD), and the partials merged by a second kernel.
 constexpr long long kWideUnits = 384;
-long long target_groups(int qr) { return qr == 1 ? 1024 : (qr == 4 ? 768 : 512); }
+long long target_groups(const kvq_cache* c, int qr) {
+  if (qr == 4 && c->mode == KVQ_MODE_UNIFORM && c->k.axis == KVQ_AXIS_CHANNEL && c->k.bits <= 4 &&
+      c->v.group == 64)
+    return 1024;
+  return qr == 1 ? 1024 : (qr == 4 ? 768 : 512);
+}
 
 struct Plan {
   int G, qr, qtiles, num_splits, split_len;
@@ -209,7 +215,7 @@ kvq_status plan_decode(const kvq_cache* c, int q_heads, int max_len, int num_spl
   }
   long long ns = num_splits;
   if (ns == 0) {
-    const long long groups = target_groups(p->qr);
+    const long long groups = target_groups(c, p->qr);
     ns = units >= kWideUnits ? 1 : (groups + units - 1) / units;
     const long long most = (length + min_piece - 1) / min_piece;
     if (ns > most) ns = most;
