@@ -45,6 +45,10 @@ def lib():
                 "ora_quant_group_sym8": ([vp, lg, lg, vp, vp], None),
                 "ora_quant_rows": ([vp, lg, i32, i32, i32, i32, vp, vp, vp], None),
                 "ora_quant_channel_blocks": ([vp, lg, lg, i32, i32, i32, vp, vp, vp], None),
+                "ora_e4m3_value": ([ctypes.c_uint8], dbl),
+                "ora_e4m3_encode": ([ctypes.c_float], ctypes.c_uint8),
+                "ora_quant_rows_e4m3": ([vp, lg, i32, i32, vp, vp], None),
+                "ora_dequant_rows_e4m3": ([vp, vp, lg, i32, i32, vp], None),
                 "ora_dequant_rows": ([vp, vp, vp, lg, i32, i32, i32, vp], None),
                 "ora_dequant_channel_blocks": ([vp, vp, vp, lg, lg, i32, i32, vp], None),
                 "ora_oaken_rows": ([vp, lg, i32, i32, vp, vp, vp, vp, vp, vp, vp], None),
@@ -106,6 +110,40 @@ def quant_rows(x_bits, g, bits, sym=False):
     lib().ora_quant_rows(px, rows, D, g, bits, int(sym), codes.ctypes.data, scale.ctypes.data,
                          zero.ctypes.data)
     return codes, scale, zero
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """binary64 values of E4M3 codes (any shape)."""
+    L = lib()
+    flat = np.asarray(codes, dtype=np.uint8).reshape(-1)
+    return np.array([L.ora_e4m3_value(int(c)) for c in flat], dtype=np.float64).reshape(np.shape(codes))
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """E4M3 codes of binary32 values (any shape)."""
+    L = lib()
+    flat = np.asarray(y, dtype=np.float32).reshape(-1)
+    return np.array([L.ora_e4m3_encode(float(v)) for v in flat], dtype=np.uint8).reshape(np.shape(y))
+
+
+def quant_rows_e4m3(x_bits, g):
+    """x [..., D] fp16 bits -> E4M3 codes [..., D] (uint8), scale [..., D/g]."""
+    x, px = _c(x_bits, np.uint16)
+    D = x.shape[-1]
+    rows = x.size // D
+    codes = np.zeros(x.shape, np.uint8)
+    scale = np.zeros(x.shape[:-1] + (D // g,), np.float32)
+    lib().ora_quant_rows_e4m3(px, rows, D, g, codes.ctypes.data, scale.ctypes.data)
+    return codes, scale
+
+
+def dequant_rows_e4m3(codes, scale, g):
+    c, pc = _c(codes, np.uint8)
+    s, ps = _c(scale, np.float32)
+    D = c.shape[-1]
+    out = np.zeros(c.shape, np.float32)
+    lib().ora_dequant_rows_e4m3(pc, ps, c.size // D, D, g, out.ctypes.data)
+    return out
 
 
 def quant_channel_blocks(x_bits, gt, bits):

@@ -128,6 +128,90 @@ void ora_quant_rows(const uint16_t* x, long rows, int D, int g, int bits, int sy
     }
 }
 
+/* ---------------------------------------------------------------------- */
+/* FP8 E4M3 codes                                                           */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * [KVQ-Eng] §"主流KV Cache量化方案对比", item 1 (FP8): the cache is converted
+ * from fp16 to 8-bit floating point, E4M3 or E5M2.  The E4M3 format used is
+ * the OCP 8-bit one without infinities: 1 sign bit, 4 exponent bits with bias
+ * 7, 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9, and
+ * the all-ones pattern S.1111.111 is NaN, so the largest finite magnitude
+ * is 1.75 * 2^8 = 448.
+ *
+ * Readings (the page names the formats only):
+ *  - Scale: dynamic, one binary32 scale per token group (the page's practice
+ *    section prefers dynamic per-vector scales), s = max|x| / 448, so the
+ *    group's largest magnitude lands on the largest finite code.
+ *  - Code: the E4M3 value nearest to the binary32 quotient x / s, ties to
+ *    the code with an even mantissa; magnitudes beyond 448 saturate to 448;
+ *    the code's sign bit is the quotient's sign bit.
+ *  - An all-zero group has scale 0 and codes 0.
+ *  - Dequantized value: E4M3 value * s in binary32 (exact product rounded once).
+ */
+
+/* Value of an E4M3 code, from the format definition (binary64, exact). */
+double ora_e4m3_value(uint8_t c) {
+  int e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp((double)(8 + m), e - 10);
+  return (c & 0x80) ? -v : v;
+}
+
+/* E4M3 code of a binary32 value: the nearest of the 127 finite non-negative
+ * magnitudes (codes 0x00 .. 0x7E, increasing with the code), found by a
+ * plain search; on a tie the even code wins; 448 and beyond give 448. */
+uint8_t ora_e4m3_encode(float y) {
+  uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  double a = fabs((double)y);
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double d = fabs(ora_e4m3_value((uint8_t)c) - a);
+    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+      bd = d;
+      best = c;
+    }
+  }
+  if (a >= 448.0) best = 0x7E; /* saturation (distances lose all precision far above 448) */
+  return (uint8_t)(sign | best);
+}
+
+/* One group of n elements: s = amax / 448, codes E4M3(x / s). */
+void ora_quant_group_e4m3(const uint16_t* x, long n, float* s_out, uint8_t* q) {
+  float amax = 0.0f;
+  for (long i = 0; i < n; ++i) {
+    float v = fabsf(ora_f16_to_f32(x[i]));
+    if (v > amax) amax = v;
+  }
+  float s = amax / 448.0f;
+  *s_out = s;
+  for (long i = 0; i < n; ++i) q[i] = s == 0.0f ? 0 : ora_e4m3_encode(ora_f16_to_f32(x[i]) / s);
+}
+
+/* Token-axis groups of g channels, E4M3 codes: codes rows x D, scale rows x (D / g). */
+void ora_quant_rows_e4m3(const uint16_t* x, long rows, int D, int g, uint8_t* codes, float* scale) {
+  int ng = D / g;
+  for (long r = 0; r < rows; ++r)
+    for (int j = 0; j < ng; ++j)
+      ora_quant_group_e4m3(x + r * D + (long)j * g, g, &scale[r * ng + j], codes + r * D + (long)j * g);
+}
+
+/* x_hat = value(code) * s in binary32. */
+void ora_dequant_rows_e4m3(const uint8_t* codes, const float* scale, long rows, int D, int g,
+                           float* out) {
+  int ng = D / g;
+  for (long r = 0; r < rows; ++r)
+    for (int d = 0; d < D; ++d)
+      out[r * D + d] = (float)ora_e4m3_value(codes[r * D + d]) * scale[r * ng + d / g];
+}
+
 /*
  * Channel-axis groups for K ([KVQ-Eng], advice to quantize K per channel):
  * x is `slices` slices of [T][D]; each channel of each block of gt
