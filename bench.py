@@ -20,6 +20,8 @@ Workloads (seeded synthetic fp16 K/V, head_dim 128; ``--workload N``):
               thresholds from a 100-sequence calibration set; dense INT4 +
               sparse shifted outer values; step = append 1 token per
               sequence + 1 decode query per head
+  6 e4m3      workload 2's shapes and inputs with FP8 E4M3 codes, one scale
+              (max|x| / 448) per token and head
 
 Prints one JSON line.  value = algorithmic bytes of a step (packed cache and
 metadata read by decode, query read, output written, appended tokens read
@@ -55,7 +57,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     p.add_argument("--num-splits", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=16.0,
                    help="budget of the CPU-oracle leg (half single-threaded, half all threads)")
@@ -132,11 +134,11 @@ class Workload:
 
 
 class UniformToken(Workload):
-    """Workloads 1 and 2: token-axis groups, optional 1-token append per step."""
+    """Workloads 1, 2 and 6: token-axis groups, optional 1-token append per step."""
 
-    def __init__(self, w, torch, K, bits, sym, group, append):
+    def __init__(self, w, torch, K, bits, sym, group, append, fmt=0):
         super().__init__(w, torch, K)
-        self.bits, self.sym, self.group, self.app = bits, sym, group, append
+        self.bits, self.sym, self.group, self.app, self.fmt = bits, sym, group, append, fmt
         B, H, T = w.batch, w.kv_heads, w.tokens
         self.T0 = T - 1 if append else T
         S = (T + 63) // 64 * 64
@@ -148,7 +150,7 @@ class UniformToken(Workload):
             self.v_new = vx[:, :, self.T0:].contiguous()
         del kx, vx
         self.caches = [K.QuantKVCache(B, H, S, K.KVQ_MODE_UNIFORM, k_bits=bits, symmetric=sym,
-                                      k_group=group)]
+                                      k_group=group, fmt=fmt)]
         self.q = torch.from_numpy(w.q().view("int16")).cuda()
         self.pos0 = i32(torch, [0] * B)
         self.pos_app = i32(torch, [self.T0] * B)
@@ -168,7 +170,7 @@ class UniformToken(Workload):
 
     def row_bytes(self):
         ng = 128 // self.group
-        return 128 * self.bits // 8 + ng * 4 + (0 if self.sym else ng)
+        return 128 * self.bits // 8 + ng * 4 + (0 if (self.sym or self.fmt) else ng)
 
     def decode_bytes(self):
         w = self.w
@@ -331,6 +333,8 @@ def build_workload(idx, torch, K, synth):
         return UniformToken(w, torch, K, bits=4, sym=False, group=64, append=False)
     if idx == 2:
         return UniformToken(w, torch, K, bits=8, sym=True, group=128, append=True)
+    if idx == 6:
+        return UniformToken(w, torch, K, bits=8, sym=False, group=128, append=True, fmt=K.KVQ_FMT_E4M3)
     if idx == 3:
         return ChannelK(w, torch, K)
     if idx == 4:
@@ -353,6 +357,9 @@ WORKLOAD_TEXT = {
     5: "oaken-13b-threshold: batch 256, 40 heads, head_dim 128, 2048 tokens of 0.5*t(3); thresholds at "
        "2.5/15/85/97.5 % of a 100-sequence calibration set; dense INT4 groups of 64 + sparse 6-bit "
        "shifted outer values; step = append 1 token per sequence + 1 decode query per head",
+    6: "llama2-7b-layer-e4m3: batch 16, 32 MHA heads, head_dim 128, 4096 cached + 1 appended token, "
+       "N(0,1) with 4 outlier channels x15 per head; FP8 E4M3 with one scale (max|x| / 448) per token "
+       "and head; step = append 1 token per sequence + 1 decode query per head",
 }
 
 
@@ -371,7 +378,14 @@ def oracle_slice(w, idx, b, h, thr=None):
     q = w.q(b, b + 1)[0, h * G:(h + 1) * G]
     T = w.tokens
     t0 = time.perf_counter()
-    if idx in (1, 2):
+    if idx == 6:
+        kc, ks = oracle.quant_rows_e4m3(k, 128)
+        vc, vs = oracle.quant_rows_e4m3(v, 128)
+        t1 = time.perf_counter()
+        kh = oracle.dequant_rows_e4m3(kc, ks, 128)
+        vh = oracle.dequant_rows_e4m3(vc, vs, 128)
+        nbytes = 2 * T * (128 + 4)
+    elif idx in (1, 2):
         bits, sym, g = (4, False, 64) if idx == 1 else (8, True, 128)
         kc, ks, kz = oracle.quant_rows(k, g, bits, sym)
         vc, vs, vz = oracle.quant_rows(v, g, bits, sym)
@@ -723,7 +737,7 @@ def main():
     app_ms = step_ms - dec_ms
     w = wl.w
     app_tokens = w.batch * (1 if idx != 1 else w.tokens)
-    append_tok_s = app_tokens / (app_ms / 1e3) if (idx in (1, 2, 5) and app_ms > 0) else None
+    append_tok_s = app_tokens / (app_ms / 1e3) if (idx in (1, 2, 5, 6) and app_ms > 0) else None
     log("step %.4f ms, decode %.4f ms (median %.4f) -> %.1f GB/s (%.1f%% of peak)"
         % (step_ms, dec_ms, float(np.median(dec_times)), achieved, 100 * achieved / HBM_PEAK_GBS))
 

@@ -62,6 +62,13 @@ enum {
   KVQ_AXIS_CHANNEL = 1 /* groups of `group` consecutive tokens of one channel (K only) */
 };
 
+/* Code format of a tensor. */
+enum {
+  KVQ_FMT_INT = 0, /* integer codes as described below */
+  KVQ_FMT_E4M3 = 1 /* FP8 E4M3 codes ([KVQ-Eng] §"主流KV Cache量化方案对比", FP8 item);
+                      UNIFORM mode, bits 8, TOKEN axis, symmetric 0, K and V alike */
+};
+
 /* Device status bits (OR-ed into *status by kernels). */
 #define KVQ_FLAG_POS_RANGE 1u       /* pos[b] + t_new > max_seq, or pos[b] < 0: rows skipped */
 #define KVQ_FLAG_SPARSE_FULL 2u     /* Oaken sparse list full: outer entries dropped */
@@ -80,6 +87,12 @@ enum {
  *               an all-zero group has s = 0, z = 0, q = 0.
  *   symmetric (bits 8, [KVQ-Eng] INT8 listing): s = max|x| / 127,
  *               q = clamp(rne(x / s), -128, 127), x_hat = q * s.
+ *   E4M3 (format KVQ_FMT_E4M3): s = max|x| / 448, q = the OCP E4M3 value
+ *               (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ *               infinities, largest finite 448) nearest to x / s, ties to
+ *               the even mantissa, saturating at 448, sign bit of x / s;
+ *               x_hat = value(q) * s.  Stored like symmetric INT8 (one
+ *               byte per code, no zero buffer).
  *
  * Buffers by mode (B = batch, H = kv_heads, S = max_seq, D = 128,
  * RB = D * bits / 8 bytes per token row, NG = D / group):
@@ -123,6 +136,7 @@ typedef struct kvq_tensor {
   int32_t symmetric;  /* 1: symmetric INT8 (bits 8, TOKEN axis) */
   int32_t axis;       /* KVQ_AXIS_TOKEN or KVQ_AXIS_CHANNEL */
   int32_t group;      /* TOKEN: 32, 64 or 128 channels.  CHANNEL: 64 tokens */
+  int32_t format;     /* KVQ_FMT_INT or KVQ_FMT_E4M3 */
   float thr[4];       /* OAKEN: T_lo_outer, T_lo_inner, T_hi_inner, T_hi_outer (inner ones
                          are informational; [Oaken] §3.2.1) */
   int64_t sparse_cap; /* OAKEN: capacity of `sparse` per (b, h), in entries */

@@ -31,6 +31,8 @@ KVQ_MODE_CHUNK_MIXED = 1
 KVQ_MODE_OAKEN = 2
 KVQ_AXIS_TOKEN = 0
 KVQ_AXIS_CHANNEL = 1
+KVQ_FMT_INT = 0
+KVQ_FMT_E4M3 = 1
 
 KVQ_FLAG_POS_RANGE = 1
 KVQ_FLAG_SPARSE_FULL = 2
@@ -48,7 +50,7 @@ TENSOR_BUFFERS = ("codes", "scale", "zero", "oscale", "rowptr", "sparse", "codes
 
 class kvq_tensor(ctypes.Structure):
     _fields_ = [("bits", _i32), ("symmetric", _i32), ("axis", _i32), ("group", _i32),
-                ("thr", _f32 * 4), ("sparse_cap", _i64)] + [(n, _vp) for n in TENSOR_BUFFERS]
+                ("format", _i32), ("thr", _f32 * 4), ("sparse_cap", _i64)] + [(n, _vp) for n in TENSOR_BUFFERS]
 
 
 class kvq_cache(ctypes.Structure):

@@ -18,7 +18,7 @@ class QuantKVCache:
                  k_bits: int = 4, v_bits: int | None = None, symmetric: bool = False,
                  k_axis: int = KVQ_AXIS_TOKEN, k_group: int = 64, v_group: int | None = None,
                  chunk_tokens: int = 32, k_thr=None, v_thr=None, sparse_cap: int = 0,
-                 device="cuda", zero_fill: bool = False):
+                 device="cuda", zero_fill: bool = False, fmt: int = 0):
         import torch
         self.torch = torch
         c = kvq_cache()
@@ -29,7 +29,7 @@ class QuantKVCache:
         v_group = k_group if v_group is None and k_axis == KVQ_AXIS_TOKEN else (v_group or 64)
         for t, bits, axis, group, thr in ((c.k, k_bits, k_axis, k_group, k_thr),
                                           (c.v, v_bits, KVQ_AXIS_TOKEN, v_group, v_thr)):
-            t.bits, t.symmetric, t.axis, t.group = bits, int(symmetric), axis, group
+            t.bits, t.symmetric, t.axis, t.group, t.format = bits, int(symmetric), axis, group, fmt
             if thr is not None:
                 for i in range(4):
                     t.thr[i] = float(thr[i])

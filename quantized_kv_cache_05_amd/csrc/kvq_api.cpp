@@ -33,6 +33,9 @@ kvq_status check_config(const kvq_cache* c) {
       for (const kvq_tensor* t : {&k, &v}) {
         if (t->bits != 8 && t->bits != 4 && t->bits != 2) return KVQ_ERR_INVALID_ARG;
         if (t->symmetric != 0 && t->symmetric != 1) return KVQ_ERR_INVALID_ARG;
+        if (t->format != KVQ_FMT_INT && t->format != KVQ_FMT_E4M3) return KVQ_ERR_INVALID_ARG;
+        if (t->format == KVQ_FMT_E4M3 && (t->bits != 8 || t->symmetric || t->axis != KVQ_AXIS_TOKEN))
+          return KVQ_ERR_UNSUPPORTED;
         if (t->symmetric && t->bits != 8) return KVQ_ERR_UNSUPPORTED;
         if (t->axis != KVQ_AXIS_TOKEN && t->axis != KVQ_AXIS_CHANNEL) return KVQ_ERR_INVALID_ARG;
       }
@@ -44,14 +47,15 @@ kvq_status check_config(const kvq_cache* c) {
         if (k.symmetric) return KVQ_ERR_UNSUPPORTED;
       }
       TensorArgs ka{}, va{};
-      ka.bits = k.bits; ka.sym = k.symmetric; ka.axis = k.axis; ka.group = k.group;
-      va.bits = v.bits; va.sym = v.symmetric; va.axis = v.axis; va.group = v.group;
+      ka.bits = k.bits; ka.sym = k.symmetric; ka.fmt = k.format; ka.axis = k.axis; ka.group = k.group;
+      va.bits = v.bits; va.sym = v.symmetric; va.fmt = v.format; va.axis = v.axis; va.group = v.group;
       if (!kvq::decode_uniform_supported(ka, va)) return KVQ_ERR_UNSUPPORTED;
       return KVQ_OK;
     }
     case KVQ_MODE_OAKEN: {
       for (const kvq_tensor* t : {&k, &v}) {
-        if (t->bits != 4 || t->symmetric || t->axis != KVQ_AXIS_TOKEN) return KVQ_ERR_UNSUPPORTED;
+        if (t->bits != 4 || t->symmetric || t->axis != KVQ_AXIS_TOKEN || t->format != KVQ_FMT_INT)
+          return KVQ_ERR_UNSUPPORTED;
         if (!is_pow2_group(t->group)) return KVQ_ERR_INVALID_ARG;
         if (!std::isfinite(t->thr[0]) || !std::isfinite(t->thr[3]) || !(t->thr[0] < t->thr[3]))
           return KVQ_ERR_INVALID_ARG;
@@ -65,6 +69,7 @@ kvq_status check_config(const kvq_cache* c) {
         return KVQ_ERR_INVALID_ARG;
       if (!is_pow2_group(k.group) || k.group != v.group) return KVQ_ERR_INVALID_ARG;
       if (k.axis != KVQ_AXIS_TOKEN || v.axis != KVQ_AXIS_TOKEN) return KVQ_ERR_UNSUPPORTED;
+      if (k.format != KVQ_FMT_INT || v.format != KVQ_FMT_INT) return KVQ_ERR_UNSUPPORTED;
       return KVQ_OK;
     }
     default:
@@ -84,7 +89,7 @@ kvq_tensor_bytes tensor_bytes(const kvq_cache* c, const kvq_tensor& t, bool is_k
         r.zero = B * H * (S / 64) * D;
       } else {
         r.scale = B * H * S * ng * 4;
-        r.zero = t.symmetric ? 0 : B * H * S * ng;
+        r.zero = (t.symmetric || t.format == KVQ_FMT_E4M3) ? 0 : B * H * S * ng;
       }
       break;
     case KVQ_MODE_OAKEN:
@@ -135,6 +140,7 @@ TensorArgs tensor_args(const kvq_tensor& t) {
   TensorArgs a;
   a.bits = t.bits;
   a.sym = t.symmetric;
+  a.fmt = t.format;
   a.axis = t.axis;
   a.group = t.group;
   a.thr_lo = t.thr[0];
@@ -283,7 +289,8 @@ kvq_status kvq_quant_append(const kvq_cache* c, const void* k_new, const void* v
         if (t_new % 64) return KVQ_ERR_INVALID_ARG;
         e = kvq::launch_quant_channel(a, a.k, kx, t_new, pos, st);
         if (e == hipSuccess) e = kvq::launch_quant_token(a, a.v, true, vx, t_new, pos, st);
-      } else if (a.k.bits == a.v.bits && a.k.sym == a.v.sym && a.k.group == a.v.group) {
+      } else if (a.k.bits == a.v.bits && a.k.sym == a.v.sym && a.k.fmt == a.v.fmt &&
+                 a.k.group == a.v.group) {
         e = kvq::launch_quant_token_kv(a, kx, vx, t_new, pos, st);
       } else {
         e = kvq::launch_quant_token(a, a.k, false, kx, t_new, pos, st);

@@ -157,6 +157,42 @@ struct KI8 {
   }
 };
 
+// FP8 E4M3 codes ([KVQ-Eng] FP8 item): every E4M3 value is a normal fp16
+// number (the smallest, 2^-9, is above fp16's normal range limit 2^-14), so
+// the hardware's scaled conversion with scale 1 widens a pair of codes to
+// an exact fp16 pair.  Bytes i and i + 1 of the slot's two words are
+// gathered into one word (lo.i, hi.i, lo.i+1, hi.i+1) whose halves convert
+// to the pairs of slots i and i + 1 (channel offsets i and i + 4, as INT8).
+template <bool UPPER>
+__device__ __forceinline__ unsigned e4m3_pair(unsigned x) {
+  const h2_t h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, UPPER);
+  return __builtin_bit_cast(unsigned, h);
+}
+__host__ __device__ constexpr unsigned sel_pairs(int i) {  // i even
+  return ((5u + i) << 24) | ((unsigned)(i + 1) << 16) | ((4u + i) << 8) | (unsigned)i;
+}
+
+struct KE4 {
+  static constexpr int RB = 128, OFF = 0, BITS = 8;
+  static constexpr bool SYM = true, F16 = false;
+  u4_t a, b;
+  __device__ __forceinline__ void load(const uint8_t* row, int q4) {
+    a = ld_nt<u4_t>(row + q4 * 32);
+    b = ld_nt<u4_t>(row + q4 * 32 + 16);
+  }
+  __device__ __forceinline__ u4_t slice(int s) const {
+    const unsigned lo = s < 2 ? a[2 * s] : b[2 * s - 4];
+    const unsigned hi = s < 2 ? a[2 * s + 1] : b[2 * s - 3];
+    const unsigned x0 = perm(hi, lo, sel_pairs(0)), x2 = perm(hi, lo, sel_pairs(2));
+    u4_t o;
+    o[0] = e4m3_pair<false>(x0);
+    o[1] = e4m3_pair<true>(x0);
+    o[2] = e4m3_pair<false>(x2);
+    o[3] = e4m3_pair<true>(x2);
+    return o;
+  }
+};
+
 struct KF16 {
   static constexpr int RB = 256, OFF = 0, BITS = 16;
   static constexpr bool SYM = false, F16 = true;
@@ -181,7 +217,7 @@ struct KF16 {
 
 struct VI4 {
   static constexpr int RB = 64, BITS = 4;
-  static constexpr bool SYM = false, F16 = false, ZODD = true;
+  static constexpr bool SYM = false, F16 = false, ZODD = true, ZP = true, MASK_ROWS = false;
   static constexpr unsigned ZMAGIC = 0xE400E400u;
   static constexpr unsigned ZMASK[2] = {0x000F000Fu, 0x00F000F0u};
   static constexpr int ZSH[2] = {0, 4};
@@ -203,7 +239,7 @@ struct VI4 {
 
 struct VI2 {
   static constexpr int RB = 32, BITS = 2;
-  static constexpr bool SYM = false, F16 = false, ZODD = false;
+  static constexpr bool SYM = false, F16 = false, ZODD = false, ZP = true, MASK_ROWS = false;
   static constexpr unsigned ZMAGIC = 0xE400E400u;
   static constexpr unsigned ZMASK[2] = {0x00030003u, 0x00030003u};
   static constexpr int ZSH[2] = {0, 0};
@@ -230,7 +266,7 @@ struct VI2 {
 template <bool SYM_>
 struct VI8 {
   static constexpr int RB = 128, BITS = 8;
-  static constexpr bool SYM = SYM_, F16 = false, ZODD = false;
+  static constexpr bool SYM = SYM_, F16 = false, ZODD = false, ZP = true, MASK_ROWS = false;
   static constexpr unsigned ZMAGIC = 0xE400E400u;
   static constexpr unsigned ZMASK[2] = {0x00FF00FFu, 0x00FF00FFu};
   static constexpr int ZSH[2] = {0, 0};
@@ -255,9 +291,42 @@ struct VI8 {
   }
 };
 
+// E4M3 V codes: the B operand pairs (rows 2p, 2p + 1) of column blocks j and
+// j + 1 come from one gathered word, converted half by half (see KE4).  No
+// zero-point; rows past the valid range are cleared (a stray byte could be
+// the NaN pattern, and 0 * NaN would poison the product).
+struct VE4 {
+  static constexpr int RB = 128, BITS = 8;
+  static constexpr bool SYM = true, F16 = false, ZODD = false, ZP = false, MASK_ROWS = true;
+  static constexpr float fac(int) { return 1.0f; }
+  unsigned w0[8], w1[8];  // codes of channels n16 + 16 e, e = 0-3 and 4-7, per row
+  __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const u2_t v = ld_nt<u2_t>(row0 + k * RB + n16 * 8);
+      w0[k] = v[0];
+      w1[k] = v[1];
+    }
+  }
+  __device__ __forceinline__ void zero_row(int k) {
+    w0[k] = 0u;
+    w1[k] = 0u;
+  }
+  __device__ __forceinline__ u4_t block(int j) const {
+    const unsigned* w = (j >> 2) ? w1 : w0;
+    u4_t o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const unsigned x = perm(w[2 * p + 1], w[2 * p], sel_pairs(j & 2));
+      o[p] = (j & 1) ? e4m3_pair<true>(x) : e4m3_pair<false>(x);
+    }
+    return o;
+  }
+};
+
 struct VF16 {
   static constexpr int RB = 256, BITS = 16;
-  static constexpr bool SYM = false, F16 = true, ZODD = false;
+  static constexpr bool SYM = false, F16 = true, ZODD = false, ZP = false, MASK_ROWS = true;
   static constexpr float fac(int) { return 1.0f; }
   u4_t r[8];
   __device__ __forceinline__ void load(const uint8_t* row0, int n16) {

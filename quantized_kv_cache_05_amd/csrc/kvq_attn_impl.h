@@ -257,7 +257,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
         // V zero-points enter through zsub below; only the scales are needed here
         if constexpr (!VC::F16) load_tok_meta<NGV, true>(vv, t, sv[nb], zv[nb]);
       }
-      if constexpr (VC::F16) {
+      if constexpr (VC::MASK_ROWS) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int t = tile + 8 * q4 + k;
@@ -266,7 +266,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       }
       // -(OFF + z) of the B-operand rows as packed fp16 pairs, per V group
       u4_t zsub[2][NGV];
-      if constexpr (!VC::F16) load_zsub<VC, NGV>(vv, tile + 8 * q4, zsub);
+      if constexpr (VC::ZP) load_zsub<VC, NGV>(vv, tile + 8 * q4, zsub);
       // ---- scores ----
       float sc[2][GI];
       if constexpr (CHANK) {
@@ -403,7 +403,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       for (int j = 0; j < 8; ++j) {
         constexpr int JPG = 8 / NGV;
         u4_t b = vr.block(j);
-        if constexpr (!VC::F16) {
+        if constexpr (VC::ZP) {
 #pragma unroll
           for (int p2 = 0; p2 < 4; ++p2) {
             // copy vector elements to scalars before bit casts: clang miscompiles a bit cast

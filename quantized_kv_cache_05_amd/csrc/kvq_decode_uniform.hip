@@ -58,9 +58,11 @@ hipError_t go(const AttnParams& P, dim3 grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int QR, class KC, class VC>
+template <int QR, class KC, class VC, bool CHANK_OK = true>
 hipError_t go_ng(const AttnParams& P, dim3 grid, bool chank, int ng, hipStream_t st) {
-  if (chank) {
+  if constexpr (!CHANK_OK) {
+    if (chank) return hipErrorInvalidValue;
+  } else if (chank) {
     switch (ng) {
       case 1: return go<QR, KC, VC, 1, 1, true>(P, grid, st);
       case 2: return go<QR, KC, VC, 1, 2, true>(P, grid, st);
@@ -80,13 +82,12 @@ template <int QR>
 hipError_t go_codec(const AttnParams& P, dim3 grid, hipStream_t st) {
   const bool chank = P.k.axis == 1;
   const int ng = kD / P.v.group;
-  if (P.v.sym) return go_ng<QR, KI8<true>, VI8<true>>(P, grid, false, ng, st);
+  if (P.v.fmt == 1) return go_ng<QR, KE4, VE4, false>(P, grid, chank, ng, st);
+  if (P.v.sym) return go_ng<QR, KI8<true>, VI8<true>, false>(P, grid, chank, ng, st);
   switch (P.v.bits) {
     case 8: return go_ng<QR, KI8<false>, VI8<false>>(P, grid, chank, ng, st);
     case 4: return go_ng<QR, KI4, VI4>(P, grid, chank, ng, st);
-    case 2:
-      if (chank) return hipErrorInvalidValue;
-      return go_ng<QR, KI2, VI2>(P, grid, false, ng, st);
+    case 2: return go_ng<QR, KI2, VI2, false>(P, grid, chank, ng, st);
   }
   return hipErrorInvalidValue;
 }
@@ -106,7 +107,8 @@ AttnParams make_attn_params(const CacheArgs& c, const DecodeLaunch& d) {
 bool decode_uniform_supported(const TensorArgs& k, const TensorArgs& v) {
   if (v.axis != 0) return false;
   if (v.group != 32 && v.group != 64 && v.group != 128) return false;
-  if (k.bits != v.bits || k.sym != v.sym) return false;
+  if (k.bits != v.bits || k.sym != v.sym || k.fmt != v.fmt) return false;
+  if (v.fmt == 1) return v.bits == 8 && !v.sym && k.axis == 0 && k.group == v.group;
   if (v.sym && v.bits != 8) return false;
   if (v.bits != 8 && v.bits != 4 && v.bits != 2) return false;
   if (k.axis == 0) return k.group == v.group;

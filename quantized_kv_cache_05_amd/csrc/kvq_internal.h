@@ -15,6 +15,7 @@ constexpr int kMaxQR = 16;       // query heads one decode workgroup serves
 struct TensorArgs {
   int bits;       // 8, 4, 2 (UNIFORM), 4 (OAKEN)
   int sym;        // symmetric INT8
+  int fmt;        // 0 integer codes, 1 FP8 E4M3 (bits 8, scale only)
   int axis;       // 0 token, 1 channel
   int group;      // channels (token axis) or tokens (channel axis)
   float thr_lo, thr_hi;  // OAKEN outer thresholds

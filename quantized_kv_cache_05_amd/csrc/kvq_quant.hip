@@ -7,6 +7,8 @@
 //     z = clamp(rne(-lo / s)), q = clamp(rne(x / s) + z); all-zero group -> 0, 0, 0
 //   symmetric INT8 ([KV-cache quantization engineering page, INT8 listing]):
 //     s = max|x| / 127, q = clamp(rne(x / s), -128, 127)
+//   FP8 E4M3 (the same page's FP8 item): s = max|x| / 448, q = E4M3 code of
+//     x / s (nearest, ties to even, saturating at 448; see e4m3_code)
 // The divisions are true IEEE divisions (the build keeps correctly rounded
 // fp32 division and denormals), so codes, scales and zero-points are
 // bit-identical to any other binary32 evaluation of these formulas.
@@ -21,13 +23,46 @@
 namespace kvq {
 namespace {
 
-template <int BITS, bool SYM, int GE>
+// OCP E4M3 code (no infinities, largest finite 1.75 * 2^8 = 448) of a
+// binary32 value, from its bits: the nearest finite value, ties to the even
+// mantissa, magnitudes from 448 up give 448; the sign bit is kept.
+//  |y| < 2^-6: the subnormal codes m * 2^-9, m = rne(|y| * 2^9) (exact
+//              scaling; m = 8 is the smallest normal, code 0x08);
+//  otherwise : exponent and mantissa bits rounded half to even at bit 20
+//              (a carry out of the mantissa steps the exponent), then the
+//              exponent rebiased from 127 to 7.
+// All three candidates are formed and one selected, so a wave never splits.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  const uint32_t normal = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  const uint32_t sub = (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+  const uint32_t mag = a >= 0x43E00000u ? 0x7Eu : (a < 0x3C800000u ? sub : normal);
+  return sign | mag;
+}
+
+template <int BITS, bool SYM, int GE, bool F8 = false>
 __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint32_t& plo,
                                        uint32_t& phi, float& s, int& z) {
   constexpr int LG = GE / 8;
   plo = 0;
   phi = 0;
-  if constexpr (SYM) {
+  if constexpr (F8) {
+    static_assert(BITS == 8, "E4M3 codes are bytes");
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
+    amax = max_lanes<1, LG>(amax);
+    s = amax / 448.0f;
+    z = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t byte = s != 0.0f ? e4m3_code(x[k] / s) : 0u;
+      if (k < 4) plo |= byte << (8 * k);
+      else phi |= byte << (8 * (k - 4));
+    }
+  } else if constexpr (SYM) {
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
@@ -160,7 +195,7 @@ __device__ __forceinline__ void store_row_f16(uint8_t* row, int li, uint4 raw, u
 // Uniform cache, token-axis groups.  x: [B][H][t_new][128], rows in that order.
 // VL selects the V row layout.
 // One token row per 16 lanes; lrow: the row's wave-local exchange area (V).
-template <int BITS, bool SYM, int GE, bool VL>
+template <int BITS, bool SYM, int GE, bool VL, bool F8 = false>
 __device__ __forceinline__ void quant_token_row(long long row, const uint16_t* __restrict__ x, int t_new,
                                                 int H, int S, const int* __restrict__ pos, long long rows,
                                                 uint8_t* __restrict__ codes, float* __restrict__ scale,
@@ -183,15 +218,15 @@ __device__ __forceinline__ void quant_token_row(long long row, const uint16_t* _
   uint32_t plo, phi;
   float s;
   int z;
-  quant8<BITS, SYM, GE>(v, 0xFFu, plo, phi, s, z);
+  quant8<BITS, SYM, GE, F8>(v, 0xFFu, plo, phi, s, z);
   store_row_codes<BITS, VL>(codes + dst * RB, li, plo, phi, lrow);
   if (li % LG == 0) {
     scale[dst * NG + li / LG] = s;
-    if constexpr (!SYM) zero[dst * NG + li / LG] = (uint8_t)z;
+    if constexpr (!SYM && !F8) zero[dst * NG + li / LG] = (uint8_t)z;
   }
 }
 
-template <int BITS, bool SYM, int GE, bool VL>
+template <int BITS, bool SYM, int GE, bool VL, bool F8>
 __global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict__ x, int t_new, int H,
                                                      int S, const int* __restrict__ pos,
                                                      long long rows, uint8_t* __restrict__ codes,
@@ -201,13 +236,13 @@ __global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict_
   __shared__ uint16_t lrows[VL ? 16 : 1][128];
   // blocks of 16 rows, grid-strided: a bounded grid keeps the dispatch cost low
   for (long long r0 = (long long)blockIdx.x * 16; r0 < rows; r0 += (long long)gridDim.x * 16)
-    quant_token_row<BITS, SYM, GE, VL>(r0 + (threadIdx.x >> 4), x, t_new, H, S, pos, rows, codes, scale,
-                                       zero, status, lrows[VL ? (threadIdx.x >> 4) : 0]);
+    quant_token_row<BITS, SYM, GE, VL, F8>(r0 + (threadIdx.x >> 4), x, t_new, H, S, pos, rows, codes,
+                                           scale, zero, status, lrows[VL ? (threadIdx.x >> 4) : 0]);
 }
 
 // K and V of the same token-axis format in one launch: blockIdx.y selects the
 // tensor (0: K rows, 1: V rows), so a decode-step append costs one launch.
-template <int BITS, bool SYM, int GE>
+template <int BITS, bool SYM, int GE, bool F8>
 __global__ __launch_bounds__(256) void k_quant_token_kv(const uint16_t* __restrict__ xk,
                                                         const uint16_t* __restrict__ xv, int t_new, int H,
                                                         int S, const int* __restrict__ pos, long long rows,
@@ -217,11 +252,11 @@ __global__ __launch_bounds__(256) void k_quant_token_kv(const uint16_t* __restri
   for (long long r0 = (long long)blockIdx.x * 16; r0 < rows; r0 += (long long)gridDim.x * 16) {
     const long long row = r0 + (threadIdx.x >> 4);
     if (blockIdx.y == 0)
-      quant_token_row<BITS, SYM, GE, false>(row, xk, t_new, H, S, pos, rows, tk.codes, tk.scale, tk.zero,
-                                            status, lrows[0]);
+      quant_token_row<BITS, SYM, GE, false, F8>(row, xk, t_new, H, S, pos, rows, tk.codes, tk.scale,
+                                                tk.zero, status, lrows[0]);
     else
-      quant_token_row<BITS, SYM, GE, true>(row, xv, t_new, H, S, pos, rows, tv.codes, tv.scale, tv.zero,
-                                           status, lrows[threadIdx.x >> 4]);
+      quant_token_row<BITS, SYM, GE, true, F8>(row, xv, t_new, H, S, pos, rows, tv.codes, tv.scale,
+                                               tv.zero, status, lrows[threadIdx.x >> 4]);
   }
 }
 
@@ -555,25 +590,28 @@ hipError_t launch_quant_token_kv(const CacheArgs& c, const uint16_t* xk, const u
   const TensorArgs& t = c.k;
   const long long rows = (long long)c.B * c.H * t_new;
   const dim3 grid((unsigned)std::min<long long>((rows + 15) / 16, kRowBlocks), 2);
-#define KVQ_TOK(BITS, SYM, GE)                                                                       \
-  hipLaunchKernelGGL((k_quant_token_kv<BITS, SYM, GE>), grid, dim3(kThreads), 0, st, xk, xv, t_new, \
+#define KVQ_TOK(BITS, SYM, GE, F8)                                                                      \
+  hipLaunchKernelGGL((k_quant_token_kv<BITS, SYM, GE, F8>), grid, dim3(kThreads), 0, st, xk, xv, t_new, \
                      c.H, c.S, pos, rows, c.k, c.v, c.status)
-#define KVQ_TOK_G(BITS, SYM)                  \
-  switch (t.group) {                          \
-    case 32: KVQ_TOK(BITS, SYM, 32); break;   \
-    case 64: KVQ_TOK(BITS, SYM, 64); break;   \
-    case 128: KVQ_TOK(BITS, SYM, 128); break; \
-    default: return hipErrorInvalidValue;     \
+#define KVQ_TOK_G(BITS, SYM, F8)                  \
+  switch (t.group) {                              \
+    case 32: KVQ_TOK(BITS, SYM, 32, F8); break;   \
+    case 64: KVQ_TOK(BITS, SYM, 64, F8); break;   \
+    case 128: KVQ_TOK(BITS, SYM, 128, F8); break; \
+    default: return hipErrorInvalidValue;         \
   }
-  if (t.sym) {
+  if (t.fmt == 1) {
+    if (t.bits != 8 || t.sym) return hipErrorInvalidValue;
+    KVQ_TOK_G(8, false, true);
+  } else if (t.sym) {
     if (t.bits != 8) return hipErrorInvalidValue;
-    KVQ_TOK_G(8, true);
+    KVQ_TOK_G(8, true, false);
   } else if (t.bits == 8) {
-    KVQ_TOK_G(8, false);
+    KVQ_TOK_G(8, false, false);
   } else if (t.bits == 4) {
-    KVQ_TOK_G(4, false);
+    KVQ_TOK_G(4, false, false);
   } else if (t.bits == 2) {
-    KVQ_TOK_G(2, false);
+    KVQ_TOK_G(2, false, false);
   } else {
     return hipErrorInvalidValue;
   }
@@ -586,31 +624,34 @@ hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, bool vl, 
                               int t_new, const int* pos, hipStream_t st) {
   const long long rows = (long long)c.B * c.H * t_new;
   const dim3 grid((unsigned)std::min<long long>((rows + 15) / 16, kRowBlocks));
-#define KVQ_TOK(BITS, SYM, GE)                                                                      \
+#define KVQ_TOK(BITS, SYM, GE, F8)                                                                  \
   do {                                                                                              \
     if (vl)                                                                                         \
-      hipLaunchKernelGGL((k_quant_token<BITS, SYM, GE, true>), grid, dim3(kThreads), 0, st, x,      \
+      hipLaunchKernelGGL((k_quant_token<BITS, SYM, GE, true, F8>), grid, dim3(kThreads), 0, st, x,  \
                          t_new, c.H, c.S, pos, rows, t.codes, t.scale, t.zero, c.status);           \
     else                                                                                            \
-      hipLaunchKernelGGL((k_quant_token<BITS, SYM, GE, false>), grid, dim3(kThreads), 0, st, x,     \
+      hipLaunchKernelGGL((k_quant_token<BITS, SYM, GE, false, F8>), grid, dim3(kThreads), 0, st, x, \
                          t_new, c.H, c.S, pos, rows, t.codes, t.scale, t.zero, c.status);           \
   } while (0)
-#define KVQ_TOK_G(BITS, SYM)                  \
-  switch (t.group) {                          \
-    case 32: KVQ_TOK(BITS, SYM, 32); break;   \
-    case 64: KVQ_TOK(BITS, SYM, 64); break;   \
-    case 128: KVQ_TOK(BITS, SYM, 128); break; \
-    default: return hipErrorInvalidValue;     \
+#define KVQ_TOK_G(BITS, SYM, F8)                  \
+  switch (t.group) {                              \
+    case 32: KVQ_TOK(BITS, SYM, 32, F8); break;   \
+    case 64: KVQ_TOK(BITS, SYM, 64, F8); break;   \
+    case 128: KVQ_TOK(BITS, SYM, 128, F8); break; \
+    default: return hipErrorInvalidValue;         \
   }
-  if (t.sym) {
+  if (t.fmt == 1) {
+    if (t.bits != 8 || t.sym) return hipErrorInvalidValue;
+    KVQ_TOK_G(8, false, true);
+  } else if (t.sym) {
     if (t.bits != 8) return hipErrorInvalidValue;
-    KVQ_TOK_G(8, true);
+    KVQ_TOK_G(8, true, false);
   } else if (t.bits == 8) {
-    KVQ_TOK_G(8, false);
+    KVQ_TOK_G(8, false, false);
   } else if (t.bits == 4) {
-    KVQ_TOK_G(4, false);
+    KVQ_TOK_G(4, false, false);
   } else if (t.bits == 2) {
-    KVQ_TOK_G(2, false);
+    KVQ_TOK_G(2, false, false);
   } else {
     return hipErrorInvalidValue;
   }

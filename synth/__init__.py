@@ -199,6 +199,8 @@ WORKLOADS = {
                 chunk_tokens=32, emb_dim=768),
     5: Workload(5, "oaken-13b-threshold", batch=256, kv_heads=40, q_heads=40, seq=2048, tokens=2048,
                 dist=DIST_T3, mult=0.5, cal_samples=100),
+    6: Workload(6, "llama2-7b-e4m3", batch=16, kv_heads=32, q_heads=32, seq=4097, tokens=4097,
+                outlier_mult=15.0, outlier_count=4),
 }
 
 

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_struct_layout_matches_header(tmp_path):
-    fields_t = ["bits", "symmetric", "axis", "group", "thr", "sparse_cap"] + list(K.TENSOR_BUFFERS)
+    fields_t = ["bits", "symmetric", "axis", "group", "format", "thr", "sparse_cap"] + list(K.TENSOR_BUFFERS)
     fields_c = ["batch", "kv_heads", "max_seq", "head_dim", "mode", "chunk_tokens", "k", "v", "perm",
                 "seg", "status"]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "kvq.h"', "int main(void){"]
@@ -113,6 +113,29 @@ def test_config_validation(mutate, expect):
     c = make_desc()
     mutate(c)
     assert status_of(K.kvq_cache_bytes, c) == expect
+
+
+def test_e4m3_format_validation_and_sizes():
+    B, H, S = 2, 3, 256
+
+    def e4m3(**kw):
+        c = make_desc(**kw)
+        c.k.format = c.v.format = K.KVQ_FMT_E4M3
+        return c
+
+    b = K.kvq_cache_bytes(e4m3(bits=8, group=64))
+    assert (b.k.codes, b.k.scale, b.k.zero) == (B * H * S * 128, B * H * S * 2 * 4, 0)
+    assert (b.v.codes, b.v.scale, b.v.zero) == (B * H * S * 128, B * H * S * 2 * 4, 0)
+    assert status_of(K.kvq_cache_bytes, e4m3(bits=4)) == K.KVQ_ERR_UNSUPPORTED
+    assert status_of(K.kvq_cache_bytes, e4m3(bits=8, sym=1)) == K.KVQ_ERR_UNSUPPORTED
+    assert status_of(K.kvq_cache_bytes, e4m3(bits=8, k_axis=1)) == K.KVQ_ERR_UNSUPPORTED
+    assert status_of(K.kvq_cache_bytes, e4m3(mode=K.KVQ_MODE_OAKEN)) == K.KVQ_ERR_UNSUPPORTED
+    assert status_of(K.kvq_cache_bytes, e4m3(mode=K.KVQ_MODE_CHUNK_MIXED, group=32)) == K.KVQ_ERR_UNSUPPORTED
+    c = make_desc(bits=8)
+    c.k.format = K.KVQ_FMT_E4M3  # K and V formats must agree
+    assert status_of(K.kvq_cache_bytes, c) == K.KVQ_ERR_UNSUPPORTED
+    c.k.format = 2
+    assert status_of(K.kvq_cache_bytes, c) == K.KVQ_ERR_INVALID_ARG
 
 
 def test_oaken_and_mixed_validation():

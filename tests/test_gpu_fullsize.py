@@ -73,6 +73,26 @@ def check_rows(out, b, h, G, q, kh, vh, label):
     assert err <= ATTN_BAR and err <= ATTN_TIGHT, (label, b, h, err)
 
 
+def test_e4m3_full():
+    wl, out = run_bench_step(6)
+    w = wl.w
+    B, H, T, G = w.batch, w.kv_heads, w.tokens, w.q_heads // w.kv_heads
+    c = wl.caches[0]
+    S = c.desc.max_seq
+    for b, h in sampled_slices(B, H, 106):
+        deq = {}
+        for name, tensor in (("k", 0), ("v", 1)):
+            x = w.kv(tensor, b, b + 1, h, h + 1)[0, 0]
+            oc, os_ = oracle.quant_rows_e4m3(x, 128)
+            got = unpack_layout(bh(c.buf(name + ".codes"), B, H, b, h).reshape(S, 128)[:T], 8, name.upper())
+            assert np.array_equal(got, oc), (name, b, h)
+            gs = bh(c.buf(name + ".scale"), B, H, b, h, np.float32).reshape(S, 1)[:T]
+            assert np.array_equal(f32bits(gs), f32bits(os_)), (name, b, h)
+            deq[name] = oracle.dequant_rows_e4m3(oc, os_, 128)
+        q = w.q(b, b + 1)[0]
+        check_rows(out, b, h, G, q, deq["k"], deq["v"], "workload 6")
+
+
 @pytest.mark.parametrize("idx", [1, 2])
 def test_uniform_token_full(idx):
     wl, out = run_bench_step(idx)
