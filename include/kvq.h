@@ -74,7 +74,6 @@ enum {
 #define KVQ_FLAG_SPARSE_FULL 2u     /* Oaken sparse list full: outer entries dropped */
 #define KVQ_FLAG_LEN_RANGE 4u       /* decode seq_len[b] outside [0, max_len]: clamped */
 #define KVQ_FLAG_BAD_CHUNK_BITS 8u  /* chunk bit-width not in {16, 4, 2}: used as 2 */
-#define KVQ_FLAG_BLOCK_ALIGN 16u    /* channel-axis append not on a block boundary: skipped */
 
 /*
  * One quantized tensor (K or V) of the cache.
@@ -101,8 +100,12 @@ enum {
  *    scale  [B][H][S][NG]  float
  *    zero   [B][H][S][NG]  uint8 (unused and may be NULL when symmetric)
  *  UNIFORM, CHANNEL axis (K only, group == 64 tokens; asymmetric):
- *    codes  [B][H][S][RB]  token rows as above
+ *    codes  [B][H][S][RB]  token rows as above, for complete 64-token blocks
  *    scale  [B][H][S/64][D] float, zero [B][H][S/64][D] uint8
+ *    codes16 [B][H][64][D] fp16 residual tail: the tokens of the block not
+ *                          yet complete, row t - 64 floor(t / 64) for token
+ *                          t, in the fp16 K row layout of the CHUNK_MIXED
+ *                          FP16 pool (below)
  *  OAKEN (bits 4, TOKEN axis, group 32 or 64; [Oaken] §3.1-3.2):
  *    codes, scale, zero    the dense body as UNIFORM/TOKEN over the
  *                          non-outer values; outer positions hold code z
@@ -190,8 +193,12 @@ kvq_status kvq_cache_bytes(const kvq_cache* c, kvq_cache_bytes_t* out);
  *  pos:          device int32 [batch]; token t of sequence b goes to cache
  *                position pos[b] + t.
  *  UNIFORM/TOKEN: any pos, t_new >= 1.
- *  UNIFORM/CHANNEL: t_new a multiple of 64; pos[b] must be a multiple of 64
- *                (else the sequence is skipped and KVQ_FLAG_BLOCK_ALIGN set).
+ *  UNIFORM/CHANNEL: any t_new >= 1, appended as a stream: pos[b] must be
+ *                the sequence's current length.  K blocks of 64 tokens that
+ *                are complete after the call are quantized (their earlier
+ *                tokens read from the fp16 tail); the new tokens of a block
+ *                left incomplete are stored in the tail.  V rows are
+ *                quantized per token as for the TOKEN axis.
  *  OAKEN:        rowptr[b][h][pos[b]] must already hold the entry count of
  *                the earlier tokens (0 at pos 0; this call writes
  *                rowptr[pos[b] + 1 .. pos[b] + t_new]); entries past
@@ -236,8 +243,11 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32
  *            kv_heads; query head h reads KV head h / (q_heads / kv_heads).
  *  seq_len:  device int32 [batch], tokens 0 .. seq_len[b]-1 are attended
  *            (UNIFORM/OAKEN; values outside [0, max_len] are clamped and set
- *            KVQ_FLAG_LEN_RANGE).  CHUNK_MIXED attends all chunks counted
- *            in seg; seq_len may then be NULL.
+ *            KVQ_FLAG_LEN_RANGE).  UNIFORM/CHANNEL reads K of the tokens
+ *            from 64 floor(seq_len[b] / 64) on from the fp16 tail, so
+ *            seq_len[b] is the appended length or a multiple of 64 not above
+ *            it.  CHUNK_MIXED attends all chunks counted in seg; seq_len may
+ *            then be NULL.
  *  max_len:  host bound on seq_len (CHUNK_MIXED: max_seq), sizes the grid.
  *  sm_scale: score scale, usually 1/sqrt(128).
  *  out:      device fp32 [batch][q_heads][128]; a sequence with no tokens

@@ -150,11 +150,13 @@ def quant_channel_blocks(x_bits, gt, bits):
     """x [..., T, D] -> codes [..., T, D], scale/zero [..., T/gt, D]."""
     x, px = _c(x_bits, np.uint16)
     T, D = x.shape[-2], x.shape[-1]
-    slices = x.size // (T * D)
     lead = x.shape[:-2]
+    slices = int(np.prod(lead, dtype=np.int64))
     codes = np.zeros(x.shape, np.uint8)
     scale = np.zeros(lead + (T // gt, D), np.float32)
     zero = np.zeros(lead + (T // gt, D), np.uint8)
+    if x.size == 0:
+        return codes, scale, zero
     lib().ora_quant_channel_blocks(px, slices, T, D, gt, bits, codes.ctypes.data, scale.ctypes.data,
                                    zero.ctypes.data)
     return codes, scale, zero
@@ -176,6 +178,8 @@ def dequant_channel_blocks(codes, scale, zero, gt):
     z, pz = _c(zero, np.uint8)
     T, D = c.shape[-2], c.shape[-1]
     out = np.zeros(c.shape, np.float32)
+    if c.size == 0:
+        return out
     lib().ora_dequant_channel_blocks(pc, ps, pz, c.size // (T * D), T, D, gt, out.ctypes.data)
     return out
 

@@ -38,7 +38,6 @@ KVQ_FLAG_POS_RANGE = 1
 KVQ_FLAG_SPARSE_FULL = 2
 KVQ_FLAG_LEN_RANGE = 4
 KVQ_FLAG_BAD_CHUNK_BITS = 8
-KVQ_FLAG_BLOCK_ALIGN = 16
 
 PART_STRIDE = 132  # floats per split partial in the decode workspace
 

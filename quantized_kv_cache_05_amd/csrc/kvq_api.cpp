@@ -87,6 +87,7 @@ kvq_tensor_bytes tensor_bytes(const kvq_cache* c, const kvq_tensor& t, bool is_k
       if (is_k && t.axis == KVQ_AXIS_CHANNEL) {
         r.scale = B * H * (S / 64) * D * 4;
         r.zero = B * H * (S / 64) * D;
+        r.codes16 = B * H * 64 * D * 2;  // fp16 residual tail: the incomplete 64-token block
       } else {
         r.scale = B * H * S * ng * 4;
         r.zero = (t.symmetric || t.format == KVQ_FMT_E4M3) ? 0 : B * H * S * ng;
@@ -286,7 +287,6 @@ kvq_status kvq_quant_append(const kvq_cache* c, const void* k_new, const void* v
   switch (c->mode) {
     case KVQ_MODE_UNIFORM:
       if (c->k.axis == KVQ_AXIS_CHANNEL) {
-        if (t_new % 64) return KVQ_ERR_INVALID_ARG;
         e = kvq::launch_quant_channel(a, a.k, kx, t_new, pos, st);
         if (e == hipSuccess) e = kvq::launch_quant_token(a, a.v, true, vx, t_new, pos, st);
       } else if (a.k.bits == a.v.bits && a.k.sym == a.v.sym && a.k.fmt == a.v.fmt &&

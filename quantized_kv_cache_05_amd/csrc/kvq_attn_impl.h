@@ -508,6 +508,25 @@ __device__ __forceinline__ float wg_max(const LDS& L, int m) {
 
 // Workgroup prologue: the query tile in LDS, per-group query sums, the K
 // A-operand of each k-step, and reset wave state.  Ends with a barrier.
+// The K-product A operand of a lane from the query tile in LDS: k-step s
+// holds fp16 pairs of channels (c0 + v, c0 + v + 4), c0 = 32 s + 8 q4, of the
+// query on the lane's A row (zero rows stay zero).
+template <int QR, class LDS>
+__device__ __forceinline__ void build_qop(const LDS& L, u4_t (&qop)[4]) {
+  const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
+  const int aq = QRows<QR>::arow_query(n16);
+  const int m = max(aq, 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c0 = 32 * s + 8 * q4;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const h2_t h = {(_Float16)L.q[m][c0 + v], (_Float16)L.q[m][c0 + v + 4]};
+      qop[s][v] = aq < 0 ? 0u : __builtin_bit_cast(unsigned, h);
+    }
+  }
+}
+
 template <int QR, int NGK, class LDS>
 __device__ __forceinline__ void attn_prologue(const AttnParams& P, LDS& L, int b, int kvh, int qt,
                                               int nq, u4_t (&qop)[4]) {
@@ -527,18 +546,7 @@ __device__ __forceinline__ void attn_prologue(const AttnParams& P, LDS& L, int b
     for (int d = g * w; d < (g + 1) * w; ++d) s += (double)L.q[m][d];
     L.qg[m][g] = (float)s;
   }
-  const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
-  const int aq = QRows<QR>::arow_query(n16);
-  const int m = max(aq, 0);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int c0 = 32 * s + 8 * q4;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const h2_t h = {(_Float16)L.q[m][c0 + v], (_Float16)L.q[m][c0 + v + 4]};
-      qop[s][v] = aq < 0 ? 0u : __builtin_bit_cast(unsigned, h);
-    }
-  }
+  build_qop<QR>(L, qop);
   __syncthreads();
 }
 

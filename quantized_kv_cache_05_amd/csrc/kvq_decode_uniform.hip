@@ -20,18 +20,16 @@ void k_attn_uniform(AttnParams P) {
   const int nq = min(QR, P.G - qt * QR);
   u4_t qop[4];
   attn_prologue<QR, NGK>(P, L, b, kvh, qt, nq, qop);
-  int len = clamp_seq_len(P, b, split == 0 && blockIdx.y == 0 && threadIdx.x == 0);
-  if constexpr (CHANK) {
-    if (len & 63) {
-      if (split == 0 && blockIdx.y == 0 && threadIdx.x == 0) set_flag(P.status, kFlagLenRange);
-      len &= ~63;
-    }
-  }
+  const int len = clamp_seq_len(P, b, split == 0 && blockIdx.y == 0 && threadIdx.x == 0);
   const int t0 = split * P.split_len;
   const int t1 = min(len, t0 + P.split_len);
+  // channel-axis K: tokens from lq on (the block not yet complete) are read
+  // from the fp16 residual tail; splits are 64-token aligned, so one split
+  // holds them all
+  const int lq = CHANK ? (len & ~63) : len;
   SoftState<QRows<QR>::GI> st;
   soft_init(st);
-  if (t0 < t1) {
+  if (t0 < min(t1, lq)) {
     const long long bh = (long long)b * P.H + kvh;
     const long long S = P.S;
     TokView kv{P.k.codes + bh * S * KC::RB, nullptr, nullptr};
@@ -45,8 +43,24 @@ void k_attn_uniform(AttnParams P) {
     }
     const TokView vv{P.v.codes + bh * S * VC::RB, P.v.scale + bh * S * NGV,
                      VC::SYM ? nullptr : P.v.zero + bh * S * NGV};
-    attend_wave<QR, NGK, NGV, KC, VC, CHANK, false, 2>(P, L, st, kv, vv, kc, nullptr, 0, nq, t0, t1,
-                                                        wave, qop);
+    attend_wave<QR, NGK, NGV, KC, VC, CHANK, false, 2>(P, L, st, kv, vv, kc, nullptr, 0, nq, t0,
+                                                        min(t1, lq), wave, qop);
+  }
+  if constexpr (CHANK) {
+    if (max(t0, lq) < t1) {
+      const long long bh = (long long)b * P.H + kvh;
+      const long long S = P.S;
+      // row t of the view is tail row t - lq
+      const TokView kt{P.k.codes16 + (bh * 64 - lq) * KF16::RB, nullptr, nullptr};
+      const TokView vv{P.v.codes + bh * S * VC::RB, P.v.scale + bh * S * NGV,
+                       VC::SYM ? nullptr : P.v.zero + bh * S * NGV};
+      const ChanView nc{nullptr, nullptr};
+      // the query operand is rebuilt here rather than kept live through the main loop
+      u4_t qop16[4];
+      build_qop<QR>(L, qop16);
+      attend_wave<QR, 1, NGV, KF16, VC, false, false, 1>(P, L, st, kt, vv, nc, nullptr, 0, nq,
+                                                         max(t0, lq), t1, wave, qop16);
+    }
   }
   wave_record<QR, NGV>(L, st, wave, nq);
   finish_split(P, L, b, kvh, qt, split, nq);

@@ -262,34 +262,61 @@ __global__ __launch_bounds__(256) void k_quant_token_kv(const uint16_t* __restri
 
 // ---------------------------------------------------------------------------
 // Uniform cache, channel-axis groups of 64 tokens (K per channel, the KV-cache
-// quantization engineering page's advice).  One workgroup per 64-token block;
-// codes in the K row layout.
+// quantization engineering page's advice), appended as a stream: a block of
+// 64 tokens is quantized once all its tokens are present; until then its
+// tokens wait in the fp16 residual tail (one block per (b, h), rows in the
+// fp16 K layout of store_row_f16).  An append of tokens [p, p + t_new) of a
+// sequence therefore continues that sequence (p = its current length): the
+// tail holds its tokens 64 floor(p / 64) .. p - 1.
+//
+// k_quant_channel: one workgroup per (block touched by the append, b h);
+// block k0 = 64 floor(p / 64) + 64 blockIdx.x is quantized when it is
+// complete after the append, its rows below p read from the tail, the others
+// from the input.  Codes in the K row layout.  k_channel_tail (launched after
+// it on the same stream, so the tail is read before it is overwritten) then
+// moves the new tokens of the block left incomplete into the tail.
+
+// 8 channels 8 li .. 8 li + 7 of an fp16 K-layout row, in channel order
+// (inverse of store_row_f16's K permutation).
+__device__ __forceinline__ uint4 ld_row8_k16(const uint8_t* row, int li) {
+  const uint4 t = ld_row8(reinterpret_cast<const uint16_t*>(row + k_slot(li) * 16));
+  uint4 o;
+  o.x = __builtin_amdgcn_perm(t.y, t.x, 0x05040100u);
+  o.y = __builtin_amdgcn_perm(t.w, t.z, 0x05040100u);
+  o.z = __builtin_amdgcn_perm(t.y, t.x, 0x07060302u);
+  o.w = __builtin_amdgcn_perm(t.w, t.z, 0x07060302u);
+  return o;
+}
+
 template <int BITS>
 __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restrict__ x, int t_new,
                                                        int H, int S, const int* __restrict__ pos,
                                                        uint8_t* __restrict__ codes,
                                                        float* __restrict__ scale,
                                                        uint8_t* __restrict__ zero,
+                                                       const uint8_t* __restrict__ tail,
                                                        unsigned* __restrict__ status) {
   constexpr int QMAX = (1 << BITS) - 1, RB = kD * BITS / 8;
-  const int kb = blockIdx.x;
   const long long bh = blockIdx.y;
   const int b = (int)(bh / H);
   const int p = pos[b];
-  if (p < 0 || p + t_new > S || (p & 63)) {
-    if (threadIdx.x == 0 && kb == 0)
-      set_flag(status, (p < 0 || p + t_new > S) ? kFlagPosRange : kFlagBlockAlign);
+  if (p < 0 || p + t_new > S) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) set_flag(status, kFlagPosRange);
     return;
   }
+  const int k0 = (p & ~63) + 64 * (int)blockIdx.x;
+  if (k0 + 64 > p + t_new) return;  // incomplete after this append (or past it)
   __shared__ float tile[64][kD + 1];
   __shared__ float lo_sh[2][kD], hi_sh[2][kD], s_sh[kD];
   __shared__ int z_sh[kD];
-  const uint16_t* xb = x + (bh * t_new + (long long)kb * 64) * kD;
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int r = pass * 16 + (threadIdx.x >> 4), li = threadIdx.x & 15;
+    const int t = k0 + r;
+    const uint4 raw = t < p ? ld_row8_k16(tail + (bh * 64 + r) * 256, li)
+                            : ld_row8(x + (bh * t_new + (t - p)) * kD + li * 8);
     float v[8];
-    unpack8(ld_row8(xb + r * kD + li * 8), v);
+    unpack8(raw, v);
 #pragma unroll
     for (int k = 0; k < 8; ++k) tile[r][li * 8 + k] = v[k];
   }
@@ -315,14 +342,14 @@ __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restric
     if (s != 0.0f) z = min(max((int)rintf(-lo / s), 0), QMAX);
     s_sh[c] = s;
     z_sh[c] = z;
-    const long long m = (bh * (S / 64) + p / 64 + kb) * kD + c;
+    const long long m = (bh * (S / 64) + k0 / 64) * kD + c;
     scale[m] = s;
     zero[m] = (uint8_t)z;
   }
   __syncthreads();
   // thread (row r, 32-channel block pc): slices q = 0..3 of k-step pc
   const int r = threadIdx.x >> 2, pc = threadIdx.x & 3;
-  uint8_t* dst = codes + (bh * S + p + (long long)kb * 64 + r) * RB;
+  uint8_t* dst = codes + (bh * S + k0 + r) * RB;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     uint64_t w = 0;
@@ -335,6 +362,25 @@ __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restric
       w |= (uint64_t)c << (BITS * v);
     }
     store_codes8<BITS>(dst, 4 * q + pc, (uint32_t)w, (uint32_t)(w >> 32));
+  }
+}
+
+// One workgroup per b h: the appended tokens of the block that stays
+// incomplete (tokens 64 floor(e / 64) .. e - 1, e = p + t_new, those at or
+// after p) go to the tail as fp16 K-layout rows.
+__global__ __launch_bounds__(256) void k_channel_tail(const uint16_t* __restrict__ x, int t_new, int H,
+                                                      int S, const int* __restrict__ pos,
+                                                      uint8_t* __restrict__ tail) {
+  const long long bh = blockIdx.x;
+  const int b = (int)(bh / H);
+  const int p = pos[b];
+  if (p < 0 || p + t_new > S) return;  // flagged by k_quant_channel
+  const int e = p + t_new, k0 = e & ~63;
+  const int r0 = max(p, k0) - k0, r1 = e - k0;
+  const int li = threadIdx.x & 15;
+  for (int r = r0 + (threadIdx.x >> 4); r < r1; r += 16) {
+    const uint4 raw = ld_row8(x + (bh * t_new + (k0 + r - p)) * kD + li * 8);
+    store_row_f16<false>(tail + (bh * 64 + r) * 256, li, raw, nullptr);
   }
 }
 
@@ -662,19 +708,24 @@ hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, bool vl, 
 
 hipError_t launch_quant_channel(const CacheArgs& c, const TensorArgs& t, const uint16_t* x, int t_new,
                                 const int* pos, hipStream_t st) {
-  if (t.group != 64 || t_new % 64) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(t_new / 64), (unsigned)(c.B * c.H));
+  if (t.group != 64 || t_new < 1) return hipErrorInvalidValue;
+  // blocks an append of t_new tokens can complete: floor((p mod 64 + t_new) / 64) <= (t_new + 63) / 64
+  const dim3 grid((unsigned)((t_new + 63) / 64), (unsigned)(c.B * c.H));
   if (t.bits == 8)
     hipLaunchKernelGGL(k_quant_channel<8>, grid, dim3(kThreads), 0, st, x, t_new, c.H, c.S, pos,
-                       t.codes, t.scale, t.zero, c.status);
+                       t.codes, t.scale, t.zero, t.codes16, c.status);
   else if (t.bits == 4)
     hipLaunchKernelGGL(k_quant_channel<4>, grid, dim3(kThreads), 0, st, x, t_new, c.H, c.S, pos,
-                       t.codes, t.scale, t.zero, c.status);
+                       t.codes, t.scale, t.zero, t.codes16, c.status);
   else if (t.bits == 2)
     hipLaunchKernelGGL(k_quant_channel<2>, grid, dim3(kThreads), 0, st, x, t_new, c.H, c.S, pos,
-                       t.codes, t.scale, t.zero, c.status);
+                       t.codes, t.scale, t.zero, t.codes16, c.status);
   else
     return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_channel_tail, dim3((unsigned)(c.B * c.H)), dim3(kThreads), 0, st, x, t_new, c.H,
+                     c.S, pos, t.codes16);
   return hipGetLastError();
 }
 

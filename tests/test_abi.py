@@ -89,7 +89,8 @@ def test_cache_bytes_per_mode():
     assert (b.v.codes, b.v.scale, b.v.zero) == (B * H * S * 32, B * H * S * 4 * 4, B * H * S * 4)
     b = K.kvq_cache_bytes(make_desc(bits=4, k_axis=1, group=64))
     assert (b.k.codes, b.k.scale, b.k.zero) == (B * H * S * 64, B * H * (S // 64) * 128 * 4, B * H * (S // 64) * 128)
-    assert (b.v.scale, b.v.zero) == (B * H * S * 2 * 4, B * H * S * 2)
+    assert b.k.codes16 == B * H * 64 * 128 * 2  # fp16 residual tail of the incomplete block
+    assert (b.v.scale, b.v.zero, b.v.codes16) == (B * H * S * 2 * 4, B * H * S * 2, 0)
     b = K.kvq_cache_bytes(make_desc(mode=K.KVQ_MODE_OAKEN, cap=1000))
     assert (b.k.oscale, b.k.rowptr, b.k.sparse) == (B * H * S * 2 * 4, B * H * (S + 1) * 4, B * H * 1000 * 2)
     b = K.kvq_cache_bytes(make_desc(mode=K.KVQ_MODE_CHUNK_MIXED, group=32))

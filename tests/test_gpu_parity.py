@@ -170,6 +170,59 @@ def test_channel_k(bits, G):
             check_attention(out, refs, "channel b%d G%d L%d ns%d" % (bits, G, L, ns))
 
 
+def k16_rows(raw_u16):
+    """fp16 K-layout rows [..., 128] (uint16 bits) -> channel order."""
+    from kvq_harness import f16_layout
+    return f16_layout(raw_u16, "K")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("G", [1, 4])
+def test_channel_k_streaming(bits, G):
+    """Appends of any size continue each sequence; complete 64-token K blocks are quantized,
+    the incomplete one waits in the fp16 tail; decode reads both."""
+    B, H, S = 2, 2, 320
+    steps = [37, 1, 1, 25, 1, 64, 70, 5, 1, 90]  # 295 tokens, crossing blocks in every way
+    T = sum(steps)
+    print("case channel streaming bits=%d G=%d" % (bits, G), flush=True)
+    w = synth.scaled(synth.WORKLOADS[3], batch=B, kv_heads=H, q_heads=H * G, seq=T, tokens=T)
+    k, v, q = w.kv(0), w.kv(1), w.q()
+    cache = K.QuantKVCache(B, H, S, K.KVQ_MODE_UNIFORM, k_bits=bits, k_axis=K.KVQ_AXIS_CHANNEL,
+                           k_group=64, v_group=64)
+    RB = 128 * bits // 8
+    vc, vs, vz = oracle.quant_rows(v, 64, bits)
+    vh = oracle.dequant_rows(vc, vs, vz, 64)
+    n = 0
+    for step in steps:
+        K.kvq_quant_append(cache.desc, to_device(k[:, :, n:n + step]), to_device(v[:, :, n:n + step]), step,
+                           i32_device([n] * B))
+        n += step
+        torch.cuda.synchronize()
+        assert cache.flags() == 0
+        nq = n // 64 * 64
+        # complete blocks: bit-exact against the oracle's per-channel blocks of the prefix
+        kc, ks, kz = oracle.quant_channel_blocks(k[:, :, :nq], 64, bits)
+        got = unpack_layout(dev_u8(cache.buf("k.codes"), (B, H, S, RB))[:, :, :nq], bits, "K")
+        assert np.array_equal(got, kc), ("codes", n)
+        gs = dev_f32(cache.buf("k.scale"), (B, H, S // 64, 128))[:, :, :nq // 64]
+        gz = dev_u8(cache.buf("k.zero"), (B, H, S // 64, 128))[:, :, :nq // 64]
+        assert np.array_equal(f32bits(gs), f32bits(ks)) and np.array_equal(gz, kz), ("meta", n)
+        # the tail holds the fp16 tokens of the incomplete block, bit for bit
+        tail = k16_rows(host_bytes(cache.buf("k.codes16")).view(np.uint16).reshape(B, H, 64, 128))
+        assert np.array_equal(tail[:, :, :n - nq], k[:, :, nq:n]), ("tail", n)
+        gotv = unpack_layout(dev_u8(cache.buf("v.codes"), (B, H, S, RB))[:, :, :n], bits, "V")
+        assert np.array_equal(gotv, vc[:, :, :n]), ("v codes", n)
+        if step in (1, 5, 70, 90):
+            kh = np.concatenate([oracle.dequant_channel_blocks(kc, ks, kz, 64),
+                                 k[:, :, nq:n].view(np.float16).astype(np.float32)], axis=2)
+            lens = [n, nq or n]  # the appended length, and the block boundary below it
+            for ns in (0, 1, 3):
+                out = run_decode(cache, q, H * G, lens, n, ns)
+                refs = np.stack([oracle.attention(q[b], kh[b][:, :L], vh[b][:, :L], SM)
+                                 for b, L in enumerate(lens)])
+                check_attention(out, refs, "stream b%d G%d n%d ns%d" % (bits, G, n, ns))
+
+
 # ---------------------------------------------------------------------------
 # chunk-mixed (Cocktail)
 
