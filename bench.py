@@ -22,6 +22,8 @@ Workloads (seeded synthetic fp16 K/V, head_dim 128; ``--workload N``):
               sequence + 1 decode query per head
   6 e4m3      workload 2's shapes and inputs with FP8 E4M3 codes, one scale
               (max|x| / 448) per token and head
+  7 paged     workload 2 in a paged cache: pages of 64 tokens handed out in a
+              seeded random order from one pool, read through a block table
 
 Prints one JSON line.  value = algorithmic bytes of a step (packed cache and
 metadata read by decode, query read, output written, appended tokens read
@@ -57,7 +59,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     p.add_argument("--num-splits", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=16.0,
                    help="budget of the CPU-oracle leg (half single-threaded, half all threads)")
@@ -134,14 +136,24 @@ class Workload:
 
 
 class UniformToken(Workload):
-    """Workloads 1, 2 and 6: token-axis groups, optional 1-token append per step."""
+    """Workloads 1, 2, 6 and 7: token-axis groups, optional 1-token append per step."""
 
-    def __init__(self, w, torch, K, bits, sym, group, append, fmt=0):
+    def __init__(self, w, torch, K, bits, sym, group, append, fmt=0, page=0):
         super().__init__(w, torch, K)
         self.bits, self.sym, self.group, self.app, self.fmt = bits, sym, group, append, fmt
         B, H, T = w.batch, w.kv_heads, w.tokens
         self.T0 = T - 1 if append else T
         S = (T + 63) // 64 * 64
+        paging = {}
+        self.table_bytes = 0
+        if page:
+            import numpy as np
+            S = (T + page - 1) // page * page
+            n = S // page
+            order = np.random.default_rng(w.seed).permutation(B * n).astype(np.int32)
+            paging = dict(page_tokens=page, num_pages=B * n,
+                          block_table=torch.from_numpy(order.reshape(B, n)).cuda())
+            self.table_bytes = B * H * (-(-T // page)) * 4  # entries read by the decode workgroups
         kx, vx = upload_kv(w, 0, torch), upload_kv(w, 1, torch)
         self.k_pre = kx[:, :, :self.T0].contiguous()
         self.v_pre = vx[:, :, :self.T0].contiguous()
@@ -150,7 +162,7 @@ class UniformToken(Workload):
             self.v_new = vx[:, :, self.T0:].contiguous()
         del kx, vx
         self.caches = [K.QuantKVCache(B, H, S, K.KVQ_MODE_UNIFORM, k_bits=bits, symmetric=sym,
-                                      k_group=group, fmt=fmt)]
+                                      k_group=group, fmt=fmt, **paging)]
         self.q = torch.from_numpy(w.q().view("int16")).cuda()
         self.pos0 = i32(torch, [0] * B)
         self.pos_app = i32(torch, [self.T0] * B)
@@ -175,7 +187,7 @@ class UniformToken(Workload):
     def decode_bytes(self):
         w = self.w
         return (2 * w.batch * w.kv_heads * w.tokens * self.row_bytes()
-                + w.batch * w.q_heads * 128 * (2 + 4))
+                + w.batch * w.q_heads * 128 * (2 + 4) + self.table_bytes)
 
     def append_bytes(self):
         w = self.w
@@ -335,6 +347,8 @@ def build_workload(idx, torch, K, synth):
         return UniformToken(w, torch, K, bits=8, sym=True, group=128, append=True)
     if idx == 6:
         return UniformToken(w, torch, K, bits=8, sym=False, group=128, append=True, fmt=K.KVQ_FMT_E4M3)
+    if idx == 7:
+        return UniformToken(w, torch, K, bits=8, sym=True, group=128, append=True, page=64)
     if idx == 3:
         return ChannelK(w, torch, K)
     if idx == 4:
@@ -360,6 +374,9 @@ WORKLOAD_TEXT = {
     6: "llama2-7b-layer-e4m3: batch 16, 32 MHA heads, head_dim 128, 4096 cached + 1 appended token, "
        "N(0,1) with 4 outlier channels x15 per head; FP8 E4M3 with one scale (max|x| / 448) per token "
        "and head; step = append 1 token per sequence + 1 decode query per head",
+    7: "llama2-7b-layer-int8-paged: workload 2 (batch 16, 32 MHA heads, 4096 cached + 1 appended "
+       "token, INT8 symmetric per token and head) in a paged cache, 64-token pages in a seeded random "
+       "order, block table read by decode; step = append 1 token per sequence + 1 decode query per head",
 }
 
 
@@ -385,7 +402,7 @@ def oracle_slice(w, idx, b, h, thr=None):
         kh = oracle.dequant_rows_e4m3(kc, ks, 128)
         vh = oracle.dequant_rows_e4m3(vc, vs, 128)
         nbytes = 2 * T * (128 + 4)
-    elif idx in (1, 2):
+    elif idx in (1, 2, 7):
         bits, sym, g = (4, False, 64) if idx == 1 else (8, True, 128)
         kc, ks, kz = oracle.quant_rows(k, g, bits, sym)
         vc, vs, vz = oracle.quant_rows(v, g, bits, sym)
@@ -737,7 +754,7 @@ def main():
     app_ms = step_ms - dec_ms
     w = wl.w
     app_tokens = w.batch * (1 if idx != 1 else w.tokens)
-    append_tok_s = app_tokens / (app_ms / 1e3) if (idx in (1, 2, 5, 6) and app_ms > 0) else None
+    append_tok_s = app_tokens / (app_ms / 1e3) if (idx in (1, 2, 5, 6, 7) and app_ms > 0) else None
     log("step %.4f ms, decode %.4f ms (median %.4f) -> %.1f GB/s (%.1f%% of peak)"
         % (step_ms, dec_ms, float(np.median(dec_times)), achieved, 100 * achieved / HBM_PEAK_GBS))
 

@@ -74,6 +74,8 @@ enum {
 #define KVQ_FLAG_SPARSE_FULL 2u     /* Oaken sparse list full: outer entries dropped */
 #define KVQ_FLAG_LEN_RANGE 4u       /* decode seq_len[b] outside [0, max_len]: clamped */
 #define KVQ_FLAG_BAD_CHUNK_BITS 8u  /* chunk bit-width not in {16, 4, 2}: used as 2 */
+#define KVQ_FLAG_PAGE_RANGE 16u     /* paged cache: block-table entry outside [0, num_pages):
+                                       append rows skipped, decode reads page 0 instead */
 
 /*
  * One quantized tensor (K or V) of the cache.
@@ -167,6 +169,16 @@ typedef struct kvq_cache {
   int32_t* perm;        /* CHUNK_MIXED: [B][C] original chunk id at each slot */
   int32_t* seg;         /* CHUNK_MIXED: [B][4] {n_fp16, n_int4, n_int2, n_chunks} */
   uint32_t* status;     /* device word for KVQ_FLAG_* bits (required) */
+  /* Paged layout (UNIFORM mode with TOKEN-axis K and V only; page_tokens 0 =
+   * contiguous).  Every per-token buffer (codes, scale, zero) is then a pool
+   * of num_pages pages [num_pages][H][page_tokens][row], and token t of
+   * sequence b lives in page block_table[b][t / page_tokens], row
+   * t % page_tokens of its head.  Pages are owned by the caller, who may map
+   * any page to any (b, logical page); a page shared by two sequences is
+   * written by both. */
+  int32_t page_tokens;          /* 0, 64, 128 or 256; max_seq a multiple of it */
+  int32_t num_pages;            /* pages in each pool (paged: >= 1) */
+  const int32_t* block_table;   /* paged: device int32 [batch][max_seq / page_tokens] */
 } kvq_cache;
 
 /* Byte sizes of every buffer of one tensor; 0 = buffer not used. */

@@ -38,6 +38,7 @@ KVQ_FLAG_POS_RANGE = 1
 KVQ_FLAG_SPARSE_FULL = 2
 KVQ_FLAG_LEN_RANGE = 4
 KVQ_FLAG_BAD_CHUNK_BITS = 8
+KVQ_FLAG_PAGE_RANGE = 16
 
 PART_STRIDE = 132  # floats per split partial in the decode workspace
 
@@ -55,7 +56,8 @@ class kvq_tensor(ctypes.Structure):
 class kvq_cache(ctypes.Structure):
     _fields_ = [("batch", _i32), ("kv_heads", _i32), ("max_seq", _i32), ("head_dim", _i32),
                 ("mode", _i32), ("chunk_tokens", _i32), ("k", kvq_tensor), ("v", kvq_tensor),
-                ("perm", _vp), ("seg", _vp), ("status", _vp)]
+                ("perm", _vp), ("seg", _vp), ("status", _vp), ("page_tokens", _i32), ("num_pages", _i32),
+                ("block_table", _vp)]
 
 
 class kvq_tensor_bytes(ctypes.Structure):

@@ -18,7 +18,8 @@ class QuantKVCache:
                  k_bits: int = 4, v_bits: int | None = None, symmetric: bool = False,
                  k_axis: int = KVQ_AXIS_TOKEN, k_group: int = 64, v_group: int | None = None,
                  chunk_tokens: int = 32, k_thr=None, v_thr=None, sparse_cap: int = 0,
-                 device="cuda", zero_fill: bool = False, fmt: int = 0):
+                 device="cuda", zero_fill: bool = False, fmt: int = 0, page_tokens: int = 0,
+                 num_pages: int = 0, block_table=None):
         import torch
         self.torch = torch
         c = kvq_cache()
@@ -34,6 +35,10 @@ class QuantKVCache:
                 for i in range(4):
                     t.thr[i] = float(thr[i])
             t.sparse_cap = sparse_cap
+        c.page_tokens, c.num_pages = page_tokens, num_pages
+        if block_table is not None:
+            self.block_table = block_table  # device int32 [batch][max_seq / page_tokens], kept alive here
+            c.block_table = block_table.data_ptr()
         self.desc = c
         self.sizes = kvq_cache_bytes(c)
         self.buffers = {}

@@ -28,6 +28,11 @@ kvq_status check_config(const kvq_cache* c) {
   if (c->head_dim != KVQ_HEAD_DIM) return KVQ_ERR_UNSUPPORTED;
   const kvq_tensor& k = c->k;
   const kvq_tensor& v = c->v;
+  if (c->page_tokens != 0) {
+    if (c->page_tokens != 64 && c->page_tokens != 128 && c->page_tokens != 256) return KVQ_ERR_INVALID_ARG;
+    if (c->max_seq % c->page_tokens || c->num_pages < 1) return KVQ_ERR_INVALID_ARG;
+    if (c->mode != KVQ_MODE_UNIFORM || k.axis != KVQ_AXIS_TOKEN) return KVQ_ERR_UNSUPPORTED;
+  }
   switch (c->mode) {
     case KVQ_MODE_UNIFORM: {
       for (const kvq_tensor* t : {&k, &v}) {
@@ -79,7 +84,12 @@ kvq_status check_config(const kvq_cache* c) {
 
 kvq_tensor_bytes tensor_bytes(const kvq_cache* c, const kvq_tensor& t, bool is_k) {
   kvq_tensor_bytes r{};
-  const size_t B = (size_t)c->batch, H = (size_t)c->kv_heads, S = (size_t)c->max_seq, D = KVQ_HEAD_DIM;
+  size_t B = (size_t)c->batch, S = (size_t)c->max_seq;
+  const size_t H = (size_t)c->kv_heads, D = KVQ_HEAD_DIM;
+  if (c->page_tokens) {  // pools of pages: (B, S) rows become (num_pages, page_tokens)
+    B = (size_t)c->num_pages;
+    S = (size_t)c->page_tokens;
+  }
   const size_t ng = D / (size_t)t.group;
   switch (c->mode) {
     case KVQ_MODE_UNIFORM:
@@ -134,6 +144,10 @@ kvq_status check_buffers(const kvq_cache* c) {
     if (!c->perm || !c->seg) return KVQ_ERR_INVALID_ARG;
     if (!aligned(c->perm, 4) || !aligned(c->seg, 16)) return KVQ_ERR_ALIGNMENT;
   }
+  if (c->page_tokens) {
+    if (!c->block_table) return KVQ_ERR_INVALID_ARG;
+    if (!aligned(c->block_table, 4)) return KVQ_ERR_ALIGNMENT;
+  }
   return KVQ_OK;
 }
 
@@ -172,6 +186,9 @@ CacheArgs cache_args(const kvq_cache* c) {
   a.perm = c->perm;
   a.seg = c->seg;
   a.status = c->status;
+  a.pages = c->page_tokens ? c->block_table : nullptr;
+  a.ptok = c->page_tokens;
+  a.npages = c->num_pages;
   return a;
 }
 

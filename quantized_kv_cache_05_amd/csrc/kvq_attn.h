@@ -356,14 +356,48 @@ struct AttnParams {
   const int* seg;
   unsigned* status;
   TensorArgs k, v;
+  const int* pages;  // paged layout: block table [B][S / ptok]; null when contiguous
+  int pshift;        // log2 tokens per page
+  int npages;
 };
 
 // One tensor's view for a (b, kv head): code rows and token-axis metadata.
+// Contiguous: row t of the (b, h) is token t.  Paged: the pointers are the
+// pool bases and token t sits in row (pages[t >> pshift] H + h) 2^pshift +
+// (t mod 2^pshift); at_tile rebases a view for the 32-token tile holding t
+// (a tile never straddles a page) so that row t addresses it directly.
 struct TokView {
-  const uint8_t* codes;  // row 0 of this (b, h)
+  const uint8_t* codes;  // row 0 of this (b, h), or the pool base when paged
   const float* scale;    // [rows][ng]
   const uint8_t* zero;   // [rows][ng] (null when symmetric)
+  const int* pages;      // paged: this sequence's block-table row (else null)
+  int pshift;            // log2 tokens per page
+  int hrow;              // this head's first row in a page: h << pshift
+  int prow;              // rows of a page over all heads: H << pshift
+  int npages;
+  unsigned* status;
 };
+
+// Row offset that maps the tokens t of the page-aligned range starting at
+// `tok` (within one page) to their pool rows: row = t + offset.  pg is the
+// block-table entry of that page; one outside the pool reads page 0 and
+// raises the flag.
+__device__ __forceinline__ long long page_row_offset(const TokView& v, int pg, int tok) {
+  if (pg < 0 || pg >= v.npages) {
+    if ((threadIdx.x & 63) == 0) set_flag(v.status, kFlagPageRange);
+    pg = 0;
+  }
+  return (long long)pg * v.prow + v.hrow + (tok & ((1 << v.pshift) - 1)) - tok;
+}
+
+template <int RB, int NG>
+__device__ __forceinline__ TokView at_rows(const TokView& v, long long off) {
+  TokView r = v;
+  r.codes = v.codes + off * RB;
+  r.scale = v.scale + off * NG;
+  if (v.zero) r.zero = v.zero + off * NG;
+  return r;
+}
 
 // Channel-axis K metadata: per 64-token block, per channel.
 struct ChanView {

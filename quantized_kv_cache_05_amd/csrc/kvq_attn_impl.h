@@ -66,7 +66,7 @@ struct AttnLds {
 // what they produce (scores to -inf, weights to 0), so no branch and no early
 // wait on the loads is needed here.
 template <int NG, bool SYM>
-__device__ __forceinline__ void load_tok_meta(const TokView& v, int row, float (&s)[NG], float (&z)[NG]) {
+__device__ __forceinline__ void load_tok_meta(const TokView& v, long long row, float (&s)[NG], float (&z)[NG]) {
   if constexpr (NG == 1) {
     s[0] = ld_nt<float>(v.scale + row);
   } else if constexpr (NG == 2) {
@@ -101,7 +101,7 @@ __device__ __forceinline__ void load_tok_meta(const TokView& v, int row, float (
 // are aligned.  Rows past the valid range multiply zero weights; the mask
 // keeps their (arbitrary) bytes inside the mantissa, so the pairs stay finite.
 template <class VC, int NGV>
-__device__ __forceinline__ void load_zsub(const TokView& vv, int r0, u4_t (&zsub)[2][NGV]) {
+__device__ __forceinline__ void load_zsub(const TokView& vv, long long r0, u4_t (&zsub)[2][NGV]) {
   constexpr int NP = VC::ZODD ? 2 : 1;
   if constexpr (VC::SYM) {
 #pragma unroll
@@ -157,13 +157,15 @@ __device__ __forceinline__ float max16(float v) {
 //
 //  KC / VC: codecs.  NGK / NGV: channel groups of K / V (token axis).
 //  CHANK: K has channel-axis groups of 64 tokens (scale folded into the query).
+//  PAGED: the views are paged (TokView), rebased for every tile.
 //  OAK: Oaken; oak_sc[m * oak_span + (t - t0)] holds the sparse outer-value
 //       part of query m's score for token t on entry and receives the final
 //       base-2 score (the V outer values are added after the loop).
-template <int QR, int NGK, int NGV, class KC, class VC, bool CHANK, bool OAK, int TPS, class LDS>
+template <int QR, int NGK, int NGV, class KC, class VC, bool CHANK, bool OAK, int TPS, bool PAGED = false,
+          class LDS>
 __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
-                                            SoftState<QRows<QR>::GI>& st, const TokView& kv,
-                                            const TokView& vv, const ChanView& kc, float* oak_sc,
+                                            SoftState<QRows<QR>::GI>& st, const TokView& kv_,
+                                            const TokView& vv_, const ChanView& kc, float* oak_sc,
                                             int oak_span, int nq, int t0, int t1, int wave,
                                             const u4_t (&qop)[4]) {
   using QRW = QRows<QR>;
@@ -178,7 +180,20 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     if (VC::fac(j) != 1.0f) st.o[j] *= VC::fac(j);
+  // paged: the block-table entry of the next step is loaded one step ahead
+  // (a step of kTile * TPS <= 64 tokens lies in one page: pages hold a
+  // multiple of 64 tokens and steps start 64-aligned)
+  static_assert(!PAGED || kTile * TPS <= 64, "a step must stay inside one page");
+  int pg_next = 0;
+  if constexpr (PAGED) pg_next = kv_.pages[min(tb + wave * kTile * TPS, t1 - 1) >> kv_.pshift];
   for (int step = tb + wave * kTile * TPS; step < t1; step += kNW * kTile * TPS) {
+    TokView kv = kv_, vv = vv_;
+    if constexpr (PAGED) {
+      const long long ro = page_row_offset(kv_, pg_next, step);
+      kv = at_rows<KC::RB, NGK>(kv_, ro);
+      vv = at_rows<VC::RB, NGV>(vv_, ro);
+      pg_next = kv_.pages[min(step + kNW * kTile * TPS, t1 - 1) >> kv_.pshift];
+    }
     // ---- channel-axis K: fold the block's scales into the query ----
     // The R x 128 products q[m][d] * s[d] are spread over the wave: entry
     // (s, m, q4e) covers channels 32 s + 8 q4e + (v, v + 4), v < 4; it is

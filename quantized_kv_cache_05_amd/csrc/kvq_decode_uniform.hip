@@ -6,13 +6,18 @@ namespace kvq {
 namespace {
 
 // Occupancy target (waves per SIMD): two in general; four for the 4-query
-// per-channel-K kernels with 4- or 2-bit codes and two V groups, which fit
-// in 128 registers without spilling.
-template <int QR, class KC, int NGV, bool CHANK>
-constexpr int kUniformWaves = (CHANK && QR == 4 && NGV == 2 && KC::BITS <= 4) ? 4 : 2;
+// per-channel-K kernels with 4- or 2-bit codes and two V groups, and for the
+// paged one-query kernels with at most two groups other than asymmetric
+// INT8, which fit in 128 registers without spilling (the contiguous
+// one-query kernels land there by themselves).
+template <int QR, class KC, int NGV, bool CHANK, bool PAGED>
+constexpr int kUniformWaves = ((CHANK && QR == 4 && NGV == 2 && KC::BITS <= 4) ||
+                               (PAGED && QR == 1 && NGV <= 2 && !(KC::BITS == 8 && !KC::SYM)))
+                                  ? 4
+                                  : 2;
 
-template <int QR, class KC, class VC, int NGK, int NGV, bool CHANK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kUniformWaves<QR, KC, NGV, CHANK>)))
+template <int QR, class KC, class VC, int NGK, int NGV, bool CHANK, bool PAGED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kUniformWaves<QR, KC, NGV, CHANK, PAGED>)))
 void k_attn_uniform(AttnParams P) {
   __shared__ AttnLds<QR, NGV, CHANK> L;
   const int split = blockIdx.x, qt = blockIdx.y % P.qtiles, kvh = blockIdx.y / P.qtiles, b = blockIdx.z;
@@ -41,10 +46,18 @@ void k_attn_uniform(AttnParams P) {
       kv.scale = P.k.scale + bh * S * NGK;
       kv.zero = KC::SYM ? nullptr : P.k.zero + bh * S * NGK;
     }
-    const TokView vv{P.v.codes + bh * S * VC::RB, P.v.scale + bh * S * NGV,
-                     VC::SYM ? nullptr : P.v.zero + bh * S * NGV};
-    attend_wave<QR, NGK, NGV, KC, VC, CHANK, false, 2>(P, L, st, kv, vv, kc, nullptr, 0, nq, t0,
-                                                        min(t1, lq), wave, qop);
+    TokView vv{P.v.codes + bh * S * VC::RB, P.v.scale + bh * S * NGV,
+               VC::SYM ? nullptr : P.v.zero + bh * S * NGV};
+    if constexpr (PAGED) {  // pools of pages: the views start at the pool bases
+      const int pshift = P.pshift;
+      kv = TokView{P.k.codes, P.k.scale, KC::SYM ? nullptr : P.k.zero,
+                   P.pages + (long long)b * (S >> pshift), pshift, kvh << pshift, P.H << pshift,
+                   P.npages, P.status};
+      vv = TokView{P.v.codes, P.v.scale, VC::SYM ? nullptr : P.v.zero, kv.pages, pshift, kv.hrow, kv.prow,
+                   P.npages, P.status};
+    }
+    attend_wave<QR, NGK, NGV, KC, VC, CHANK, false, 2, PAGED>(P, L, st, kv, vv, kc, nullptr, 0, nq, t0,
+                                                               min(t1, lq), wave, qop);
   }
   if constexpr (CHANK) {
     if (max(t0, lq) < t1) {
@@ -68,7 +81,13 @@ void k_attn_uniform(AttnParams P) {
 
 template <int QR, class KC, class VC, int NGK, int NGV, bool CHANK>
 hipError_t go(const AttnParams& P, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_uniform<QR, KC, VC, NGK, NGV, CHANK>), grid, dim3(kNW * 64), 0, st, P);
+  if constexpr (!CHANK) {
+    if (P.pages) {
+      hipLaunchKernelGGL((k_attn_uniform<QR, KC, VC, NGK, NGV, false, true>), grid, dim3(kNW * 64), 0, st, P);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((k_attn_uniform<QR, KC, VC, NGK, NGV, CHANK, false>), grid, dim3(kNW * 64), 0, st, P);
   return hipGetLastError();
 }
 
@@ -115,6 +134,9 @@ AttnParams make_attn_params(const CacheArgs& c, const DecodeLaunch& d) {
   P.chunk_tokens = c.chunk_tokens; P.qscale = d.qscale; P.q = d.q; P.seq_len = d.seq_len;
   P.out = d.out; P.ws = d.ws; P.seg = c.seg; P.status = c.status;
   P.k = c.k; P.v = c.v;
+  P.pages = c.pages;
+  P.pshift = c.ptok ? __builtin_ctz((unsigned)c.ptok) : 0;
+  P.npages = c.npages;
   return P;
 }
 

@@ -11,6 +11,7 @@ constexpr unsigned kFlagPosRange = 1u;
 constexpr unsigned kFlagSparseFull = 2u;
 constexpr unsigned kFlagLenRange = 4u;
 constexpr unsigned kFlagBadChunkBits = 8u;
+constexpr unsigned kFlagPageRange = 16u;
 
 __device__ __forceinline__ float h2f(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);

@@ -40,6 +40,9 @@ struct CacheArgs {
   int* perm;
   int* seg;
   unsigned* status;
+  const int* pages;  // paged: block table [B][S / ptok]; null when contiguous
+  int ptok;          // tokens per page
+  int npages;        // pages per pool
 };
 
 struct DecodeLaunch {

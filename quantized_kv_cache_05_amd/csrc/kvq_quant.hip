@@ -195,12 +195,19 @@ __device__ __forceinline__ void store_row_f16(uint8_t* row, int li, uint4 raw, u
 // Uniform cache, token-axis groups.  x: [B][H][t_new][128], rows in that order.
 // VL selects the V row layout.
 // One token row per 16 lanes; lrow: the row's wave-local exchange area (V).
+// Where token rows live: contiguous [B][H][S] rows, or pages of ptok rows per
+// head, [npages][H][ptok], token t of sequence b in page pages[b][t / ptok].
+struct PageMap {
+  const int* pages;  // null: contiguous
+  int ptok, npages;
+};
+
 template <int BITS, bool SYM, int GE, bool VL, bool F8 = false>
 __device__ __forceinline__ void quant_token_row(long long row, const uint16_t* __restrict__ x, int t_new,
                                                 int H, int S, const int* __restrict__ pos, long long rows,
                                                 uint8_t* __restrict__ codes, float* __restrict__ scale,
                                                 uint8_t* __restrict__ zero, unsigned* __restrict__ status,
-                                                uint16_t* lrow) {
+                                                uint16_t* lrow, const PageMap& pm) {
   constexpr int NG = kD / GE, LG = GE / 8, RB = kD * BITS / 8;
   const int li = threadIdx.x & 15;
   if (row >= rows) return;  // all 16 lanes of a row leave together
@@ -212,7 +219,16 @@ __device__ __forceinline__ void quant_token_row(long long row, const uint16_t* _
     if (li == 0) set_flag(status, kFlagPosRange);
     return;
   }
-  const long long dst = bh * S + p + t;
+  long long dst = bh * S + p + t;
+  if (pm.pages) {
+    const int tok = p + t;
+    const int pg = pm.pages[(long long)b * (S / pm.ptok) + tok / pm.ptok];
+    if (pg < 0 || pg >= pm.npages) {
+      if (li == 0) set_flag(status, kFlagPageRange);
+      return;
+    }
+    dst = ((long long)pg * H + bh % H) * pm.ptok + tok % pm.ptok;
+  }
   float v[8];
   unpack8(ld_row8(x + row * kD + li * 8), v);
   uint32_t plo, phi;
@@ -232,12 +248,12 @@ __global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict_
                                                      long long rows, uint8_t* __restrict__ codes,
                                                      float* __restrict__ scale,
                                                      uint8_t* __restrict__ zero,
-                                                     unsigned* __restrict__ status) {
+                                                     unsigned* __restrict__ status, PageMap pm) {
   __shared__ uint16_t lrows[VL ? 16 : 1][128];
   // blocks of 16 rows, grid-strided: a bounded grid keeps the dispatch cost low
   for (long long r0 = (long long)blockIdx.x * 16; r0 < rows; r0 += (long long)gridDim.x * 16)
     quant_token_row<BITS, SYM, GE, VL, F8>(r0 + (threadIdx.x >> 4), x, t_new, H, S, pos, rows, codes,
-                                           scale, zero, status, lrows[VL ? (threadIdx.x >> 4) : 0]);
+                                           scale, zero, status, lrows[VL ? (threadIdx.x >> 4) : 0], pm);
 }
 
 // K and V of the same token-axis format in one launch: blockIdx.y selects the
@@ -247,16 +263,16 @@ __global__ __launch_bounds__(256) void k_quant_token_kv(const uint16_t* __restri
                                                         const uint16_t* __restrict__ xv, int t_new, int H,
                                                         int S, const int* __restrict__ pos, long long rows,
                                                         TensorArgs tk, TensorArgs tv,
-                                                        unsigned* __restrict__ status) {
+                                                        unsigned* __restrict__ status, PageMap pm) {
   __shared__ uint16_t lrows[16][128];
   for (long long r0 = (long long)blockIdx.x * 16; r0 < rows; r0 += (long long)gridDim.x * 16) {
     const long long row = r0 + (threadIdx.x >> 4);
     if (blockIdx.y == 0)
       quant_token_row<BITS, SYM, GE, false, F8>(row, xk, t_new, H, S, pos, rows, tk.codes, tk.scale,
-                                                tk.zero, status, lrows[0]);
+                                                tk.zero, status, lrows[0], pm);
     else
       quant_token_row<BITS, SYM, GE, true, F8>(row, xv, t_new, H, S, pos, rows, tv.codes, tv.scale,
-                                               tv.zero, status, lrows[threadIdx.x >> 4]);
+                                               tv.zero, status, lrows[threadIdx.x >> 4], pm);
   }
 }
 
@@ -634,11 +650,12 @@ constexpr long long kRowBlocks = 4096;  // grid bound of the row kernels (blocks
 hipError_t launch_quant_token_kv(const CacheArgs& c, const uint16_t* xk, const uint16_t* xv, int t_new,
                                  const int* pos, hipStream_t st) {
   const TensorArgs& t = c.k;
+  const PageMap pm{c.pages, c.ptok, c.npages};
   const long long rows = (long long)c.B * c.H * t_new;
   const dim3 grid((unsigned)std::min<long long>((rows + 15) / 16, kRowBlocks), 2);
 #define KVQ_TOK(BITS, SYM, GE, F8)                                                                      \
   hipLaunchKernelGGL((k_quant_token_kv<BITS, SYM, GE, F8>), grid, dim3(kThreads), 0, st, xk, xv, t_new, \
-                     c.H, c.S, pos, rows, c.k, c.v, c.status)
+                     c.H, c.S, pos, rows, c.k, c.v, c.status, pm)
 #define KVQ_TOK_G(BITS, SYM, F8)                  \
   switch (t.group) {                              \
     case 32: KVQ_TOK(BITS, SYM, 32, F8); break;   \
@@ -668,16 +685,17 @@ hipError_t launch_quant_token_kv(const CacheArgs& c, const uint16_t* xk, const u
 
 hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
                               int t_new, const int* pos, hipStream_t st) {
+  const PageMap pm{c.pages, c.ptok, c.npages};
   const long long rows = (long long)c.B * c.H * t_new;
   const dim3 grid((unsigned)std::min<long long>((rows + 15) / 16, kRowBlocks));
 #define KVQ_TOK(BITS, SYM, GE, F8)                                                                  \
   do {                                                                                              \
     if (vl)                                                                                         \
       hipLaunchKernelGGL((k_quant_token<BITS, SYM, GE, true, F8>), grid, dim3(kThreads), 0, st, x,  \
-                         t_new, c.H, c.S, pos, rows, t.codes, t.scale, t.zero, c.status);           \
+                         t_new, c.H, c.S, pos, rows, t.codes, t.scale, t.zero, c.status, pm);       \
     else                                                                                            \
       hipLaunchKernelGGL((k_quant_token<BITS, SYM, GE, false, F8>), grid, dim3(kThreads), 0, st, x, \
-                         t_new, c.H, c.S, pos, rows, t.codes, t.scale, t.zero, c.status);           \
+                         t_new, c.H, c.S, pos, rows, t.codes, t.scale, t.zero, c.status, pm);       \
   } while (0)
 #define KVQ_TOK_G(BITS, SYM, F8)                  \
   switch (t.group) {                              \

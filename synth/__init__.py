@@ -201,6 +201,8 @@ WORKLOADS = {
                 dist=DIST_T3, mult=0.5, cal_samples=100),
     6: Workload(6, "llama2-7b-e4m3", batch=16, kv_heads=32, q_heads=32, seq=4097, tokens=4097,
                 outlier_mult=15.0, outlier_count=4),
+    7: Workload(7, "llama2-7b-int8-paged", batch=16, kv_heads=32, q_heads=32, seq=4097, tokens=4097,
+                outlier_mult=15.0, outlier_count=4),
 }
 
 

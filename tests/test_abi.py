@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 def test_struct_layout_matches_header(tmp_path):
     fields_t = ["bits", "symmetric", "axis", "group", "format", "thr", "sparse_cap"] + list(K.TENSOR_BUFFERS)
     fields_c = ["batch", "kv_heads", "max_seq", "head_dim", "mode", "chunk_tokens", "k", "v", "perm",
-                "seg", "status"]
+                "seg", "status", "page_tokens", "num_pages", "block_table"]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "kvq.h"', "int main(void){"]
     lines.append('printf("kvq_tensor %zu\\n", sizeof(kvq_tensor));')
     lines.append('printf("kvq_cache %zu\\n", sizeof(kvq_cache));')
@@ -137,6 +137,26 @@ def test_e4m3_format_validation_and_sizes():
     assert status_of(K.kvq_cache_bytes, c) == K.KVQ_ERR_UNSUPPORTED
     c.k.format = 2
     assert status_of(K.kvq_cache_bytes, c) == K.KVQ_ERR_INVALID_ARG
+
+
+def test_paged_validation_and_sizes():
+    H = 3
+
+    def paged(P=64, pages=10, **kw):
+        c = make_desc(**kw)
+        c.page_tokens, c.num_pages = P, pages
+        return c
+
+    b = K.kvq_cache_bytes(paged(bits=4, group=64))
+    assert (b.k.codes, b.k.scale, b.k.zero) == (10 * H * 64 * 64, 10 * H * 64 * 2 * 4, 10 * H * 64 * 2)
+    b = K.kvq_cache_bytes(paged(P=256, pages=3, bits=8, sym=1, group=128))
+    assert (b.v.codes, b.v.scale, b.v.zero) == (3 * H * 256 * 128, 3 * H * 256 * 4, 0)
+    assert status_of(K.kvq_cache_bytes, paged(P=32)) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_cache_bytes, paged(P=128, S=320)) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_cache_bytes, paged(pages=0)) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_cache_bytes, paged(k_axis=1)) == K.KVQ_ERR_UNSUPPORTED
+    assert status_of(K.kvq_cache_bytes, paged(mode=K.KVQ_MODE_OAKEN)) == K.KVQ_ERR_UNSUPPORTED
+    assert status_of(K.kvq_cache_bytes, paged(mode=K.KVQ_MODE_CHUNK_MIXED, group=32)) == K.KVQ_ERR_UNSUPPORTED
 
 
 def test_oaken_and_mixed_validation():

@@ -73,6 +73,32 @@ def check_rows(out, b, h, G, q, kh, vh, label):
     assert err <= ATTN_BAR and err <= ATTN_TIGHT, (label, b, h, err)
 
 
+def test_paged_full():
+    wl, out = run_bench_step(7)
+    w = wl.w
+    B, H, T, G = w.batch, w.kv_heads, w.tokens, w.q_heads // w.kv_heads
+    c = wl.caches[0]
+    P, pool = c.desc.page_tokens, c.desc.num_pages
+    table = c.block_table.cpu().numpy()
+    codes = c.buf("k.codes")
+    for b, h in sampled_slices(B, H, 107):
+        t = np.arange(T)
+        pg, r = table[b, t // P], t % P
+        deq = {}
+        for name, tensor in (("k", 0), ("v", 1)):
+            x = w.kv(tensor, b, b + 1, h, h + 1)[0, 0]
+            oc, os_, oz = oracle.quant_rows(x, 128, 8, True)
+            allc = c.buf(name + ".codes").view(torch.uint8).view(pool, H, P, 128)[:, h].cpu().numpy()
+            got = unpack_layout(allc[pg, r], 8, name.upper(), True)
+            assert np.array_equal(got, oc), (name, b, h)
+            alls = c.buf(name + ".scale").view(torch.uint8).view(pool, H, P, 4)[:, h].cpu().numpy()
+            assert np.array_equal(alls[pg, r].view(np.uint32)[:, 0], f32bits(os_)[:, 0]), (name, b, h)
+            deq[name] = oracle.dequant_rows(oc, os_, oz, 128, True)
+        q = w.q(b, b + 1)[0]
+        check_rows(out, b, h, G, q, deq["k"], deq["v"], "workload 7")
+    assert codes.numel() == pool * H * P * 128
+
+
 def test_e4m3_full():
     wl, out = run_bench_step(6)
     w = wl.w

@@ -1,0 +1,135 @@
+"""GPU parity of the paged cache layout (uniform mode, token-axis groups).
+
+Pages are handed out in a seeded random order from a pool larger than the
+sequences need.  Codes and scales gathered through the block table must equal
+the oracle's bit for bit; decode must equal, bit for bit, the decode of a
+contiguous cache holding the same data (same arithmetic in the same order),
+and meet the attention bar against the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from kvq_harness import ATTN_BAR, ATTN_TIGHT, host_bytes, i32_device, rel_err_rows, to_device, unpack_layout
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+K = pytest.importorskip("quantized_kv_cache_05_amd")
+
+SM = 1.0 / np.sqrt(128.0)
+LAYOUT = {"k": "K", "v": "V"}
+
+# (bits, symmetric, group, format)
+CODECS = [(8, True, 128, 0), (4, False, 64, 0), (2, False, 32, 0), (8, False, 128, 1)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    K.lib()
+    yield
+
+
+def f32bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def make(B, H, S, codec, P=0, pages=0, table=None):
+    bits, sym, group, fmt = codec
+    return K.QuantKVCache(B, H, S, K.KVQ_MODE_UNIFORM, k_bits=bits, symmetric=sym, k_group=group, fmt=fmt,
+                          page_tokens=P, num_pages=pages,
+                          block_table=None if table is None else i32_device(table.reshape(-1)))
+
+
+def decode(cache, q, Hq, lens, max_len, ns):
+    B = q.shape[0]
+    out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ws, n = cache.workspace(Hq, max_len, ns)
+    K.kvq_decode_attn(cache.desc, to_device(q), Hq, i32_device(lens), max_len, SM, out, ws, n, ns)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle_rows(x, codec):
+    bits, sym, group, fmt = codec
+    if fmt:
+        c, s = oracle.quant_rows_e4m3(x, group)
+        return c, s, None, oracle.dequant_rows_e4m3(c, s, group)
+    c, s, z = oracle.quant_rows(x, group, bits, sym)
+    return c, s, z, oracle.dequant_rows(c, s, z, group, sym)
+
+
+@pytest.mark.parametrize("codec", CODECS)
+@pytest.mark.parametrize("P", [64, 256])
+@pytest.mark.parametrize("G", [1, 4])
+def test_paged_matches_contiguous(codec, P, G):
+    bits, sym, group, fmt = codec
+    B, H, S, T = 3, 2, 512, 333
+    print("case paged codec=%s P=%d G=%d" % (codec, P, G), flush=True)
+    w = synth.scaled(synth.WORKLOADS[1], batch=B, kv_heads=H, q_heads=H * G, seq=T + 1, tokens=T + 1)
+    k, v, q = w.kv(0), w.kv(1), w.q()
+    per_seq = S // P
+    used = -(-(T + 1) // P)  # pages each sequence touches
+    pool = B * used + 3  # a few pages never handed out
+    rng = np.random.default_rng(1000 + P + bits)
+    ids = rng.permutation(pool)[:B * used].reshape(B, used)
+    table = np.full((B, per_seq), -1, np.int32)
+    table[:, :used] = ids
+    paged = make(B, H, S, codec, P, pool, table)
+    flat = make(B, H, S, codec)
+    app = np.array([T, 200, 100])  # single-token appends at different positions
+    for cache in (paged, flat):
+        K.kvq_quant_append(cache.desc, to_device(k[:, :, :T]), to_device(v[:, :, :T]), T, i32_device([0] * B))
+        K.kvq_quant_append(cache.desc, to_device(k[:, :, T:T + 1]), to_device(v[:, :, T:T + 1]), 1,
+                           i32_device(app))
+    torch.cuda.synchronize()
+    assert paged.flags() == 0 and flat.flags() == 0
+    RB, NG = 128 * bits // 8, 128 // group
+    lens = [T + 1, 201, 101]
+    deq = {}
+    for name, x in (("k", k), ("v", v)):
+        logical = x[:, :, :T + 1].copy()
+        for b in range(B):
+            logical[b, :, app[b]] = x[b, :, T]
+        oc, os_, oz, xh = oracle_rows(logical, codec)
+        deq[name] = xh
+        codes = host_bytes(paged.buf(name + ".codes")).reshape(pool, H, P, RB)
+        scale = host_bytes(paged.buf(name + ".scale")).view(np.float32).reshape(pool, H, P, NG)
+        zero = None if (sym or fmt) else host_bytes(paged.buf(name + ".zero")).reshape(pool, H, P, NG)
+        for b, L in enumerate(lens):
+            t = np.arange(L)
+            pg, r = table[b, t // P], t % P
+            got = unpack_layout(codes[pg, :, r].transpose(1, 0, 2), bits, LAYOUT[name], sym)
+            assert np.array_equal(got, oc[b, :, :L]), (name, b)
+            assert np.array_equal(f32bits(scale[pg, :, r].transpose(1, 0, 2)), f32bits(os_[b, :, :L])), (name, b)
+            if zero is not None:
+                assert np.array_equal(zero[pg, :, r].transpose(1, 0, 2), oz[b, :, :L]), (name, b)
+    for ns in (0, 1, 3):
+        out_p = decode(paged, q, H * G, lens, T + 1, ns)
+        out_f = decode(flat, q, H * G, lens, T + 1, ns)
+        assert np.array_equal(out_p.view(np.uint32), out_f.view(np.uint32)), ns
+        refs = np.stack([oracle.attention(q[b], deq["k"][b][:, :L], deq["v"][b][:, :L], SM)
+                         for b, L in enumerate(lens)])
+        err = float(rel_err_rows(out_p, refs).max())
+        print("paged %s P%d G%d ns%d: max rel err %.3e" % (codec, P, G, ns, err), flush=True)
+        assert err <= ATTN_BAR and err <= ATTN_TIGHT
+
+
+def test_paged_bad_page_is_flagged():
+    codec = (4, False, 64, 0)
+    B, H, S, P = 2, 2, 256, 64
+    w = synth.scaled(synth.WORKLOADS[1], batch=B, kv_heads=H, q_heads=H, seq=128, tokens=128)
+    k, v, q = w.kv(0), w.kv(1), w.q()
+    table = np.array([[0, 1, -1, -1], [2, 9, -1, -1]], np.int32)  # page 9 is outside a 4-page pool
+    cache = make(B, H, S, codec, P, 4, table)
+    K.kvq_quant_append(cache.desc, to_device(k), to_device(v), 128, i32_device([0, 0]))
+    torch.cuda.synchronize()
+    assert cache.flags() & K.KVQ_FLAG_PAGE_RANGE
+    cache.status.zero_()
+    out = decode(cache, q, H, [128, 64], 128, 0)  # sequence 1 stops before the bad page
+    assert cache.flags() == 0 and np.all(np.isfinite(out))
+    decode(cache, q, H, [128, 128], 128, 0)  # now it reads through it: page 0 instead, flagged
+    assert cache.flags() & K.KVQ_FLAG_PAGE_RANGE
