@@ -120,7 +120,10 @@ enum {
  *                          T_lo_outer - mag * oscale (side 0)
  *  CHUNK_MIXED ([Cocktail] §3.1.2; C = S / chunk_tokens chunk slots, each
  *  class pool holds up to C chunks per (b, h) in reordered slot order):
- *    codes16 [B][H][C][chunk_tokens][D] fp16, the FP16 chunks
+ *    codes16 [B][H][C][chunk_tokens][D] fp16, the FP16 chunks, plus 64
+ *                          spare rows at the end; chunk C - 1 of a (b, h)
+ *                          holds the waiting tokens of kvq_append_chunks
+ *                          until the sequence's final chunk
  *    codes/scale/zero   INT4 pool, TOKEN-axis layout with C*chunk_tokens rows
  *    codes2/scale2/zero2 INT2 pool, same layout
  *
@@ -236,6 +239,31 @@ kvq_status kvq_reorder_chunks(const kvq_cache* c, const uint8_t* chunk_bits, int
                               void* stream);
 
 /*
+ * Cocktail streaming append ([Cocktail] §3.1.2: chunks kept contiguous by
+ * class; §3.2.2 group quantization): t_new new tokens per sequence continue
+ * it at pos[b], its current length, which must satisfy pos[b] /
+ * chunk_tokens == seg[b][3] (the chunks complete so far; a new cache has
+ * zeroed seg).  Tokens of the chunk not yet complete wait as fp16 in the
+ * last chunk of the FP16 pool (chunk max_seq / chunk_tokens - 1, free until
+ * the sequence's final chunk).  The i-th chunk this call completes in
+ * sequence b takes the bit-width new_bits[b * n_new + i] (16, 4 or 2; other
+ * values count as 2 and set KVQ_FLAG_BAD_CHUNK_BITS) and is copied (16) or
+ * quantized (groups of `group` channels) into the next chunk of its class
+ * pool; perm and seg are updated so that they, and the pools, equal what
+ * kvq_reorder_chunks and a whole-sequence append would give for the
+ * complete chunks.
+ *  k_new, v_new: device fp16 [batch][kv_heads][t_new][128].
+ *  new_bits:     device uint8 [batch][n_new]; n_new at least
+ *                (t_new + chunk_tokens - 1) / chunk_tokens.
+ *  A sequence whose pos[b] does not match seg, or which would pass max_seq,
+ *  is skipped and sets KVQ_FLAG_POS_RANGE.  CHUNK_MIXED mode only.
+ *  Decode attends the complete chunks and, when seq_len is given, the
+ *  waiting tokens seg[b][3] * chunk_tokens .. seq_len[b] - 1.
+ */
+kvq_status kvq_append_chunks(const kvq_cache* c, const void* k_new, const void* v_new, int32_t t_new,
+                             const int32_t* pos, const uint8_t* new_bits, int32_t n_new, void* stream);
+
+/*
  * Workspace needed by kvq_decode_attn for the same (c, q_heads, max_len,
  * num_splits); 0 when the chosen split count is 1.  Host only.  The
  * workspace holds the split partials (m, l, unnormalized output per batch,
@@ -258,8 +286,10 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32
  *            KVQ_FLAG_LEN_RANGE).  UNIFORM/CHANNEL reads K of the tokens
  *            from 64 floor(seq_len[b] / 64) on from the fp16 tail, so
  *            seq_len[b] is the appended length or a multiple of 64 not above
- *            it.  CHUNK_MIXED attends all chunks counted in seg; seq_len may
- *            then be NULL.
+ *            it.  CHUNK_MIXED attends all chunks counted in seg, and with
+ *            seq_len the tokens from seg[b][3] * chunk_tokens up to seq_len[b]
+ *            waiting in the FP16 pool's last chunk (kvq_append_chunks; at
+ *            most chunk_tokens - 1 of them); seq_len may be NULL.
  *  max_len:  host bound on seq_len (CHUNK_MIXED: max_seq), sizes the grid.
  *  sm_scale: score scale, usually 1/sqrt(128).
  *  out:      device fp32 [batch][q_heads][128]; a sequence with no tokens

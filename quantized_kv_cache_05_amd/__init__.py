@@ -77,7 +77,8 @@ class KVQError(RuntimeError):
 
 _lib = None
 
-EXPORTS = ("kvq_cache_bytes", "kvq_quant_append", "kvq_reorder_chunks", "kvq_decode_workspace_bytes",
+EXPORTS = ("kvq_cache_bytes", "kvq_quant_append", "kvq_reorder_chunks", "kvq_append_chunks",
+           "kvq_decode_workspace_bytes",
            "kvq_decode_attn", "kvq_chunk_bits", "kvq_hist_f16", "kvq_hist_percentiles",
            "kvq_status_string")
 
@@ -93,6 +94,7 @@ def lib():
         L.kvq_cache_bytes.argtypes = [P(kvq_cache), P(kvq_cache_bytes_t)]
         L.kvq_quant_append.argtypes = [P(kvq_cache), _vp, _vp, _i32, _vp, _vp]
         L.kvq_reorder_chunks.argtypes = [P(kvq_cache), _vp, _i32, _vp]
+        L.kvq_append_chunks.argtypes = [P(kvq_cache), _vp, _vp, _i32, _vp, _vp, _i32, _vp]
         L.kvq_decode_workspace_bytes.argtypes = [P(kvq_cache), _i32, _i32, _i32, P(_sz)]
         L.kvq_decode_attn.argtypes = [P(kvq_cache), _vp, _i32, _vp, _i32, _f32, _vp, _vp, _sz, _i32, _vp]
         L.kvq_chunk_bits.argtypes = [_vp, _vp, _i32, _i32, _i32, ctypes.c_double, ctypes.c_double, _vp,
@@ -150,6 +152,13 @@ def kvq_quant_append(cache: kvq_cache, k_new, v_new, t_new: int, pos, stream=Non
 def kvq_reorder_chunks(cache: kvq_cache, chunk_bits, n_chunks: int, stream=None) -> int:
     return _check(lib().kvq_reorder_chunks(ctypes.byref(cache), _ptr(chunk_bits), int(n_chunks),
                                            _stream(stream)), "kvq_reorder_chunks")
+
+
+def kvq_append_chunks(cache: kvq_cache, k_new, v_new, t_new: int, pos, new_bits, n_new: int,
+                      stream=None) -> int:
+    return _check(lib().kvq_append_chunks(ctypes.byref(cache), _ptr(k_new), _ptr(v_new), int(t_new),
+                                          _ptr(pos), _ptr(new_bits), int(n_new), _stream(stream)),
+                  "kvq_append_chunks")
 
 
 def kvq_decode_workspace_bytes(cache: kvq_cache, q_heads: int, max_len: int, num_splits: int = 0) -> int:

@@ -112,7 +112,9 @@ kvq_tensor_bytes tensor_bytes(const kvq_cache* c, const kvq_tensor& t, bool is_k
       r.sparse = B * H * (size_t)t.sparse_cap * 2;
       break;
     case KVQ_MODE_CHUNK_MIXED:
-      r.codes16 = B * H * S * D * 2;
+      // 64 spare rows: decode tiles of 32 tokens over the waiting chunk of the
+      // last (b, h) may reach up to 16 rows past it when chunks hold 16 tokens
+      r.codes16 = (B * H * S + 64) * D * 2;
       r.codes = B * H * S * D / 2;
       r.scale = B * H * S * ng * 4;
       r.zero = B * H * S * ng;
@@ -341,6 +343,27 @@ kvq_status kvq_reorder_chunks(const kvq_cache* c, const uint8_t* chunk_bits, int
   if (!aligned(c->perm, 4) || !aligned(c->seg, 16) || !aligned(c->status, 4)) return KVQ_ERR_ALIGNMENT;
   const CacheArgs a = cache_args(c);
   return from_hip(kvq::launch_reorder(a, chunk_bits, n_chunks, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_append_chunks(const kvq_cache* c, const void* k_new, const void* v_new, int32_t t_new,
+                             const int32_t* pos, const uint8_t* new_bits, int32_t n_new, void* stream) {
+  kvq_status s = check_config(c);
+  if (s != KVQ_OK) return s;
+  if (c->mode != KVQ_MODE_CHUNK_MIXED) return KVQ_ERR_INVALID_ARG;
+  if (t_new < 0) return KVQ_ERR_INVALID_ARG;
+  if (t_new > c->max_seq) return KVQ_ERR_CAPACITY;
+  if (t_new == 0) return KVQ_OK;
+  if (n_new < (t_new + c->chunk_tokens - 1) / c->chunk_tokens) return KVQ_ERR_INVALID_ARG;
+  if (!k_new || !v_new || !pos || !new_bits) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos, 4)) return KVQ_ERR_ALIGNMENT;
+  s = check_buffers(c);
+  if (s != KVQ_OK) return s;
+  const CacheArgs a = cache_args(c);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = kvq::launch_append_chunks(a, static_cast<const uint16_t*>(k_new),
+                                           static_cast<const uint16_t*>(v_new), t_new, pos, new_bits,
+                                           n_new, st);
+  return from_hip(e);
 }
 
 kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32_t max_len,

@@ -3,6 +3,7 @@
 // reordered chunk slots; its part in each class (FP16, INT4, INT2) is a
 // contiguous row range of that class's pool, attended with that class's
 // codecs into the same running softmax state, so the split emits one partial.
+// The tokens of a chunk still being appended are attended by the last split.
 #include "kvq_attn_impl.h"
 
 namespace kvq {
@@ -54,6 +55,20 @@ __global__ __launch_bounds__(256, 2) void k_attn_mixed(AttnParams P) {
       attend_wave<QR, NG, NG, KI2, VI2, false, false, 2>(P, L, st, k2, v2, nc, nullptr, 0, nq,
                                                           (a - n16 - n4) * CT, (e - n16 - n4) * CT,
                                                           wave, qop);
+    }
+  }
+  // tokens of the chunk not yet complete (streaming appends) wait as fp16 in
+  // the FP16 pool's last chunk: the last split attends seg[b][3] * CT ..
+  // seq_len[b] - 1 of them
+  if (P.seq_len && split == P.num_splits - 1 && n < C) {
+    const int len = clamp_seq_len(P, b, blockIdx.y == 0 && threadIdx.x == 0);
+    const int w0 = n * CT, w1 = min(len, w0 + CT - 1);
+    if (w0 < w1) {
+      const long long wr = bh * S + (long long)(C - 1) * CT - w0;  // row of token t: wr + t
+      const TokView kw{P.k.codes16 + wr * KF16::RB, nullptr, nullptr};
+      const TokView vw{P.v.codes16 + wr * VF16::RB, nullptr, nullptr};
+      attend_wave<QR, 1, 1, KF16, VF16, false, false, 1>(P, L, st, kw, vw, nc, nullptr, 0, nq, w0, w1, wave,
+                                                          qop);
     }
   }
   wave_record<QR, NG>(L, st, wave, nq);

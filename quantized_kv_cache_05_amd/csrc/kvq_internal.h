@@ -76,6 +76,17 @@ hipError_t launch_quant_mixed(const CacheArgs& c, const TensorArgs& t, bool vl, 
 hipError_t launch_quant_oaken(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
                               int t_new, const int* pos, hipStream_t st);
 hipError_t launch_reorder(const CacheArgs& c, const uint8_t* bits, int n_chunks, hipStream_t st);
+// Cocktail streaming append of one tensor: complete chunks into their class
+// pools, the rest into the FP16 pool's last chunk (perm / seg untouched).
+hipError_t launch_chunk_append(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
+                               int t_new, const int* pos, const uint8_t* bits, int n_new, hipStream_t st);
+// perm / seg after a streaming append (runs after launch_chunk_append of K and V).
+hipError_t launch_chunk_seg(const CacheArgs& c, int t_new, const int* pos, const uint8_t* bits, int n_new,
+                            hipStream_t st);
+// Cocktail streaming append: complete chunks into their class pools, the
+// rest into the FP16 pool's last chunk, then perm / seg.
+hipError_t launch_append_chunks(const CacheArgs& c, const uint16_t* xk, const uint16_t* xv, int t_new,
+                                const int* pos, const uint8_t* bits, int n_new, hipStream_t st);
 
 // Cocktail chunk precision search and Oaken calibration histogram.
 constexpr int kMaxPercentiles = 8;

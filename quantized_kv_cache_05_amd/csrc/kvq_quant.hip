@@ -462,6 +462,128 @@ __global__ __launch_bounds__(256) void k_quant_mixed(
 }
 
 // ---------------------------------------------------------------------------
+// Chunk-mixed streaming append.  Tokens of the chunk not yet complete wait as
+// fp16 rows in the FP16 pool's last chunk (the "waiting chunk"); a chunk
+// completed by an append is read from there (its tokens below pos) and from
+// the input, and copied or quantized into the next chunk of its class pool.
+
+__device__ __forceinline__ int chunk_cls(unsigned v) { return v == 16u ? 0 : (v == 4u ? 1 : 2); }
+
+// 8 channels 8 li .. 8 li + 7 of token row r of a chunk being completed, in
+// channel order: from the waiting chunk (fp16 pool layout VL) when `waiting`,
+// else from the input row xrow.  The V layout is transposed through lrow.
+template <bool VL>
+__device__ __forceinline__ uint4 chunk_row8(bool waiting, const uint8_t* wrow, const uint16_t* xrow,
+                                            int li, uint16_t* lrow) {
+  if constexpr (!VL) {
+    return waiting ? ld_row8_k16(wrow, li) : ld_row8(xrow + li * 8);
+  } else {
+    // V pool word li holds channels li + 16 e; an input lane holds 8 li + e
+    const uint4 w = waiting ? ld_row8(reinterpret_cast<const uint16_t*>(wrow + li * 16)) : ld_row8(xrow + li * 8);
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      lrow[waiting ? li + 16 * e : 8 * li + e] = (uint16_t)(d[e >> 1] >> (16 * (e & 1)));
+    wave_lds_sync();
+    uint4 o;
+    o.x = (uint32_t)lrow[8 * li + 0] | ((uint32_t)lrow[8 * li + 1] << 16);
+    o.y = (uint32_t)lrow[8 * li + 2] | ((uint32_t)lrow[8 * li + 3] << 16);
+    o.z = (uint32_t)lrow[8 * li + 4] | ((uint32_t)lrow[8 * li + 5] << 16);
+    o.w = (uint32_t)lrow[8 * li + 6] | ((uint32_t)lrow[8 * li + 7] << 16);
+    wave_lds_sync();
+    return o;
+  }
+}
+
+// One workgroup per (i, b h), i = i0 + blockIdx.x: the i-th chunk this append
+// completes in sequence b (original chunk id n + i, n = seg[b][3] = pos[b] /
+// CT), with the bit-width bits[b][i]; its class-local index is that class's
+// count plus the earlier chunks of the same class in this append.  Only chunk
+// 0 reads waiting tokens, and only the sequence's final chunk can land in the
+// waiting chunk's place (an all-FP16 sequence), so chunk 0 runs in a launch
+// of its own before the others.
+template <int GE, bool VL>
+__global__ __launch_bounds__(256) void k_chunk_append(
+    int i0, const uint16_t* __restrict__ x, int t_new, int H, int S, int CT, int C, const int* __restrict__ pos,
+    const uint8_t* __restrict__ bits, int n_new, const int* __restrict__ seg, uint8_t* __restrict__ c16,
+    uint8_t* __restrict__ c4, float* __restrict__ s4, uint8_t* __restrict__ z4, uint8_t* __restrict__ c2,
+    float* __restrict__ s2, uint8_t* __restrict__ z2, unsigned* __restrict__ status) {
+  constexpr int NG = kD / GE, LG = GE / 8;
+  __shared__ uint16_t lrows[VL ? 16 : 1][128];
+  const int i = i0 + (int)blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int b = (int)(bh / H);
+  const int p = pos[b], n = seg[b * 4 + 3];
+  if (p < 0 || p + t_new > S || p / CT != n) {
+    if (threadIdx.x == 0 && i == 0 && bh % H == 0) set_flag(status, kFlagPosRange);
+    return;
+  }
+  const int j = n + i;
+  if ((j + 1) * CT > p + t_new) return;  // not completed by this append
+  const uint8_t* bb = bits + (long long)b * n_new;
+  const int cls = chunk_cls(bb[i]);
+  int k = seg[b * 4 + cls];
+  for (int i2 = 0; i2 < i; ++i2) k += chunk_cls(bb[i2]) == cls;
+  if (k >= C) return;
+  const long long wrow0 = (bh * C + (C - 1)) * CT;  // waiting chunk
+  const long long drow0 = (bh * C + k) * CT;
+  const int li = threadIdx.x & 15;
+  uint16_t* lrow = lrows[VL ? (threadIdx.x >> 4) : 0];
+  for (int r = threadIdx.x >> 4; r < CT; r += 16) {
+    const int t = j * CT + r;
+    const bool waiting = t < p;
+    const uint4 raw = chunk_row8<VL>(waiting, c16 + (wrow0 + r) * kD * 2,
+                                     x + (bh * t_new + (waiting ? 0 : t - p)) * kD, li, lrow);
+    const long long drow = drow0 + r;
+    if (cls == 0) {
+      store_row_f16<VL>(c16 + drow * kD * 2, li, raw, lrow);
+      continue;
+    }
+    float v[8];
+    unpack8(raw, v);
+    uint32_t plo, phi;
+    float sc;
+    int z;
+    if (cls == 1) {
+      quant8<4, false, GE>(v, 0xFFu, plo, phi, sc, z);
+      store_row_codes<4, VL>(c4 + drow * 64, li, plo, phi, lrow);
+      if (li % LG == 0) {
+        s4[drow * NG + li / LG] = sc;
+        z4[drow * NG + li / LG] = (uint8_t)z;
+      }
+    } else {
+      quant8<2, false, GE>(v, 0xFFu, plo, phi, sc, z);
+      store_row_codes<2, VL>(c2 + drow * 32, li, plo, phi, lrow);
+      if (li % LG == 0) {
+        s2[drow * NG + li / LG] = sc;
+        z2[drow * NG + li / LG] = (uint8_t)z;
+      }
+    }
+  }
+}
+
+// One workgroup per b h, after k_chunk_append (which reads the waiting chunk
+// first): the appended tokens of the chunk left incomplete wait as fp16.
+template <bool VL>
+__global__ __launch_bounds__(256) void k_chunk_wait(const uint16_t* __restrict__ x, int t_new, int H, int S,
+                                                    int CT, int C, const int* __restrict__ pos,
+                                                    const int* __restrict__ seg, uint8_t* __restrict__ c16) {
+  __shared__ uint16_t lrows[VL ? 16 : 1][128];
+  const long long bh = blockIdx.x;
+  const int b = (int)(bh / H);
+  const int p = pos[b];
+  if (p < 0 || p + t_new > S || p / CT != seg[b * 4 + 3]) return;  // flagged by k_chunk_append
+  const int e = p + t_new, j0 = (e / CT) * CT;
+  const int r0 = max(p, j0) - j0, r1 = e - j0;
+  const int li = threadIdx.x & 15;
+  uint16_t* lrow = lrows[VL ? (threadIdx.x >> 4) : 0];
+  for (int r = r0 + (threadIdx.x >> 4); r < r1; r += 16) {
+    const uint4 raw = ld_row8(x + (bh * t_new + (j0 + r - p)) * kD + li * 8);
+    store_row_f16<VL>(c16 + ((bh * C + (C - 1)) * CT + r) * kD * 2, li, raw, lrow);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Oaken (the Oaken page, §3.1 online stage, §3.2.1-3.2.2): per row, outer
 // values (x > T_hi_outer or x < T_lo_outer) leave the dense INT4 body (coded
 // z) and go to the row's sparse list as shifted deltas with a per-group
@@ -769,6 +891,45 @@ hipError_t launch_quant_mixed(const CacheArgs& c, const TensorArgs& t, bool vl, 
     default: return hipErrorInvalidValue;
   }
 #undef KVQ_MIX
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_append(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
+                               int t_new, const int* pos, const uint8_t* bits, int n_new, hipStream_t st) {
+  const int C = c.S / c.chunk_tokens, CT = c.chunk_tokens;
+  hipError_t e = hipSuccess;
+  // chunk 0 first, then the others (see k_chunk_append)
+  for (int part = 0; part < 2 && e == hipSuccess; ++part) {
+    const int i0 = part, cnt = part ? n_new - 1 : 1;
+    if (cnt <= 0) break;
+    const dim3 grid((unsigned)cnt, (unsigned)(c.B * c.H));
+#define KVQ_CA(GE)                                                                                   \
+  do {                                                                                               \
+    if (vl)                                                                                          \
+      hipLaunchKernelGGL((k_chunk_append<GE, true>), grid, dim3(kThreads), 0, st, i0, x, t_new, c.H, \
+                         c.S, CT, C, pos, bits, n_new, c.seg, t.codes16, t.codes, t.scale, t.zero,   \
+                         t.codes2, t.scale2, t.zero2, c.status);                                    \
+    else                                                                                             \
+      hipLaunchKernelGGL((k_chunk_append<GE, false>), grid, dim3(kThreads), 0, st, i0, x, t_new,     \
+                         c.H, c.S, CT, C, pos, bits, n_new, c.seg, t.codes16, t.codes, t.scale,      \
+                         t.zero, t.codes2, t.scale2, t.zero2, c.status);                            \
+  } while (0)
+    switch (t.group) {
+      case 32: KVQ_CA(32); break;
+      case 64: KVQ_CA(64); break;
+      case 128: KVQ_CA(128); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef KVQ_CA
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  if (vl)
+    hipLaunchKernelGGL((k_chunk_wait<true>), dim3((unsigned)(c.B * c.H)), dim3(kThreads), 0, st, x, t_new,
+                       c.H, c.S, CT, C, pos, c.seg, t.codes16);
+  else
+    hipLaunchKernelGGL((k_chunk_wait<false>), dim3((unsigned)(c.B * c.H)), dim3(kThreads), 0, st, x,
+                       t_new, c.H, c.S, CT, C, pos, c.seg, t.codes16);
   return hipGetLastError();
 }
 

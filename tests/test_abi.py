@@ -94,7 +94,7 @@ def test_cache_bytes_per_mode():
     b = K.kvq_cache_bytes(make_desc(mode=K.KVQ_MODE_OAKEN, cap=1000))
     assert (b.k.oscale, b.k.rowptr, b.k.sparse) == (B * H * S * 2 * 4, B * H * (S + 1) * 4, B * H * 1000 * 2)
     b = K.kvq_cache_bytes(make_desc(mode=K.KVQ_MODE_CHUNK_MIXED, group=32))
-    assert (b.k.codes16, b.k.codes, b.k.codes2) == (B * H * S * 256, B * H * S * 64, B * H * S * 32)
+    assert (b.k.codes16, b.k.codes, b.k.codes2) == ((B * H * S + 64) * 256, B * H * S * 64, B * H * S * 32)
     assert (b.perm, b.seg, b.status) == (B * (S // 32) * 4, B * 16, 4)
 
 

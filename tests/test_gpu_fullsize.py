@@ -37,9 +37,13 @@ def _gpu():
     yield
 
 
-def bh(t, B, H, b, h, dtype=np.uint8):
-    """Bytes of slice (b, h) of a [B][H][...] device buffer -> numpy of dtype."""
-    return t.view(torch.uint8).view(B, H, -1)[b, h].cpu().numpy().view(dtype)
+def bh(t, B, H, b, h, dtype=np.uint8, per=None):
+    """Bytes of slice (b, h) of a [B][H][...] device buffer -> numpy of dtype (per: bytes per
+    slice, for buffers with spare bytes at the end)."""
+    flat = t.view(torch.uint8)
+    if per is not None:
+        flat = flat[:B * H * per]
+    return flat.view(B, H, -1)[b, h].cpu().numpy().view(dtype)
 
 
 def f32bits(a):
@@ -194,7 +198,8 @@ def test_chunk_mixed_full():
         for name, tensor in (("k", 0), ("v", 1)):
             x = w.kv(tensor, b, b + 1, h, h + 1)[0, 0]
             lay = name.upper()
-            p16 = f16_layout(bh(c.buf(name + ".codes16"), B, H, b, h, np.uint16).reshape(C, CT, 128), lay)
+            p16 = f16_layout(bh(c.buf(name + ".codes16"), B, H, b, h, np.uint16, per=C * CT * 256)
+                             .reshape(C, CT, 128), lay)
             p4 = unpack_layout(bh(c.buf(name + ".codes"), B, H, b, h).reshape(C, CT, 64), 4, lay)
             s4 = bh(c.buf(name + ".scale"), B, H, b, h, np.float32).reshape(C, CT, 4)
             z4 = bh(c.buf(name + ".zero"), B, H, b, h).reshape(C, CT, 4)

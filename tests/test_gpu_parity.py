@@ -267,7 +267,8 @@ def test_chunk_mixed(G, source):
     assert cache.flags() == 0
     # pools: slot j of class c holds the source chunk perm[b][j]
     for name, x in (("k", k), ("v", v)):
-        p16 = f16_layout(host_bytes(cache.buf(name + ".codes16")).view(np.uint16).reshape(B, H, C, CT, 128),
+        p16 = f16_layout(host_bytes(cache.buf(name + ".codes16"))[:B * H * C * CT * 256].view(np.uint16)
+                         .reshape(B, H, C, CT, 128),
                          LAYOUT[name])
         p4 = unpack_layout(dev_u8(cache.buf(name + ".codes"), (B, H, C, CT, 64)), 4, LAYOUT[name])
         s4 = dev_f32(cache.buf(name + ".scale"), (B, H, C, CT, 4))
@@ -295,6 +296,113 @@ def test_chunk_mixed(G, source):
     for ns in (0, 1, 7):
         out = run_decode(cache, q, H * G, None, S, ns)
         check_attention(out, refs, "mixed G%d %s ns%d" % (G, source, ns))
+
+
+def chunk_pools(cache, name, B, H, C, CT, group):
+    lay = LAYOUT[name]
+    ng = 128 // group
+    return dict(
+        p16=f16_layout(host_bytes(cache.buf(name + ".codes16"))[:B * H * C * CT * 256].view(np.uint16)
+                       .reshape(B, H, C, CT, 128), lay),
+        p4=unpack_layout(dev_u8(cache.buf(name + ".codes"), (B, H, C, CT, 64)), 4, lay),
+        s4=dev_f32(cache.buf(name + ".scale"), (B, H, C, CT, ng)),
+        z4=dev_u8(cache.buf(name + ".zero"), (B, H, C, CT, ng)),
+        p2=unpack_layout(dev_u8(cache.buf(name + ".codes2"), (B, H, C, CT, 32)), 2, lay),
+        s2=dev_f32(cache.buf(name + ".scale2"), (B, H, C, CT, ng)),
+        z2=dev_u8(cache.buf(name + ".zero2"), (B, H, C, CT, ng)))
+
+
+@pytest.mark.parametrize("CT,steps,mix", [
+    (32, [45, 1, 1, 30, 64, 5, 100, 1, 70, 195], "random"),
+    (16, [45, 1, 1, 30, 64, 5, 100, 1, 70, 195], "random"),
+    (32, [40, 88, 130, 254], "all16"),
+])
+@pytest.mark.parametrize("G", [1, 4])
+def test_chunk_streaming(CT, steps, mix, G):
+    """Appends of any size continue each sequence; every chunk an append completes takes its
+    bit-width and joins its class pool, the rest waits as fp16; perm, seg and the pools equal the
+    oracle's reorder of the complete chunks, and in the end the bulk path's result."""
+    B, H, S, group = 2, 2, 512, 32
+    C = S // CT
+    assert sum(steps) == S
+    print("case chunk streaming CT=%d %s G=%d" % (CT, mix, G), flush=True)
+    w = synth.scaled(synth.WORKLOADS[4], batch=B, kv_heads=H, q_heads=H * G, seq=S, tokens=S, emb_dim=64)
+    k, v, q = w.kv(0), w.kv(1), w.q()
+    rng = np.random.default_rng(7 + CT)
+    if mix == "all16":
+        bits = np.full((B, C), 16, np.uint8)
+    else:
+        bits = rng.choice(np.array([16, 4, 2], np.uint8), size=(B, C), p=[0.2, 0.35, 0.45])
+    cache = K.QuantKVCache(B, H, S, K.KVQ_MODE_CHUNK_MIXED, k_group=group, chunk_tokens=CT, zero_fill=True)
+    L = 0
+    for step in steps:
+        done0 = L // CT
+        n_new = -(-step // CT) + 1
+        nb = np.full((B, n_new), 16, np.uint8)
+        m = (L + step) // CT - done0
+        nb[:, :m] = bits[:, done0:done0 + m]
+        K.kvq_append_chunks(cache.desc, to_device(k[:, :, L:L + step]), to_device(v[:, :, L:L + step]), step,
+                            i32_device([L] * B), torch.from_numpy(nb).cuda(), n_new)
+        L += step
+        torch.cuda.synchronize()
+        assert cache.flags() == 0
+        n = L // CT
+        if n:
+            perm_o, seg_o = oracle.reorder(bits[:, :n])
+            assert np.array_equal(host_bytes(cache.buf("perm")).reshape(B, C)[:, :n], perm_o), L
+            assert np.array_equal(host_bytes(cache.buf("seg")).reshape(B, 4), seg_o), L
+        xh = {}
+        for name, x in (("k", k), ("v", v)):
+            pools = chunk_pools(cache, name, B, H, C, CT, group)
+            ref = np.zeros((B, H, L, 128), np.float32)
+            for b in range(B):
+                n16, n4 = (seg_o[b, 0], seg_o[b, 1]) if n else (0, 0)
+                for j in range(n):
+                    src = perm_o[b, j]
+                    rows = x[b, :, src * CT:(src + 1) * CT]
+                    if j < n16:
+                        assert np.array_equal(pools["p16"][b, :, j], rows), (name, L, b, j)
+                        ref[b, :, src * CT:(src + 1) * CT] = rows.view(np.float16).astype(np.float32)
+                        continue
+                    nbits, kk = (4, j - n16) if j < n16 + n4 else (2, j - n16 - n4)
+                    oc, os_, oz = oracle.quant_rows(rows, group, nbits)
+                    pc, ps, pz = (pools["p4"], pools["s4"], pools["z4"]) if nbits == 4 else \
+                        (pools["p2"], pools["s2"], pools["z2"])
+                    assert np.array_equal(pc[b, :, kk], oc), (name, L, b, j)
+                    assert np.array_equal(f32bits(ps[b, :, kk]), f32bits(os_)), (name, L, b, j)
+                    assert np.array_equal(pz[b, :, kk], oz), (name, L, b, j)
+                    ref[b, :, src * CT:(src + 1) * CT] = oracle.dequant_rows(oc, os_, oz, group)
+                wait = x[b, :, n * CT:L]
+                if wait.shape[1]:
+                    assert np.array_equal(pools["p16"][b, :, C - 1, :wait.shape[1]], wait), (name, L, b)
+                    ref[b, :, n * CT:L] = wait.view(np.float16).astype(np.float32)
+            xh[name] = ref
+        if step in (1, 5, 70, 195, 130, 254):
+            for ns in (0, 1, 3):
+                out = run_decode(cache, q, H * G, [L] * B, S, ns)
+                refs = np.stack([oracle.attention(q[b], xh["k"][b], xh["v"][b], SM) for b in range(B)])
+                check_attention(out, refs, "stream CT%d %s G%d L%d ns%d" % (CT, mix, G, L, ns))
+            if n:  # without seq_len only the complete chunks count
+                out = run_decode(cache, q, H * G, None, S, 0)
+                refs = np.stack([oracle.attention(q[b], xh["k"][b][:, :n * CT], xh["v"][b][:, :n * CT], SM)
+                                 for b in range(B)])
+                check_attention(out, refs, "stream CT%d %s G%d complete-only" % (CT, mix, G))
+    # the finished stream equals the bulk path
+    bulk = K.QuantKVCache(B, H, S, K.KVQ_MODE_CHUNK_MIXED, k_group=group, chunk_tokens=CT, zero_fill=True)
+    K.kvq_reorder_chunks(bulk.desc, torch.from_numpy(bits).cuda(), C)
+    K.kvq_quant_append(bulk.desc, to_device(k), to_device(v), S, i32_device([0] * B))
+    torch.cuda.synchronize()
+    for buf in ("perm", "seg", "k.codes", "k.scale", "k.zero", "k.codes2", "k.scale2", "k.zero2", "v.codes",
+                "v.scale", "v.zero", "v.codes2", "v.scale2", "v.zero2"):
+        assert np.array_equal(host_bytes(cache.buf(buf)), host_bytes(bulk.buf(buf))), buf
+    for name in ("k", "v"):
+        nbytes = B * H * C * CT * 256
+        seg_b = host_bytes(bulk.buf("seg")).reshape(B, 4)
+        a = host_bytes(cache.buf(name + ".codes16"))[:nbytes].reshape(B, H, C * CT * 256)
+        c = host_bytes(bulk.buf(name + ".codes16"))[:nbytes].reshape(B, H, C * CT * 256)
+        for b in range(B):  # the FP16 pool is defined up to its class count
+            used = seg_b[b, 0] * CT * 256
+            assert np.array_equal(a[b, :, :used], c[b, :, :used]), (name, b)
 
 
 def test_reorder_flags_bad_bits():
