@@ -60,6 +60,8 @@ def lib():
                 "ora_attention_partial": ([vp, vp, vp, lg, lg, i32, dbl, vp, vp, vp], None),
                 "ora_attention": ([vp, i32, i32, i32, vp, vp, lg, dbl, vp], None),
                 "ora_lse_merge": ([i32, vp, vp, vp, i32, vp], None),
+                "ora_dsq_group": ([vp, vp, vp, i32, i32, i32, i32] + [vp] * 12, None),
+                "ora_dsq_dequant_group": ([ctypes.c_uint64, i32, i32, i32] + [vp] * 13, None),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -290,3 +292,52 @@ def lse_merge(m, l, o):
     out = np.zeros(D)
     lib().ora_lse_merge(parts, pm, pl, po, D, out.ctypes.data)
     return out
+
+
+DSQ_GROUP = 64  # tokens per DSQ group
+
+
+def dsq_quant(k_bits, v_bits, score, n_sig=13, g2=32):
+    """DSQ of one (b, kv head): k/v [T][D] fp16 bits, score [T] float32, T a multiple of 64.
+
+    Returns a dict of per-group arrays (G = T / 64, n = 64 - n_sig):
+    mask [G] uint64; ksig/vsig [G][n_sig][D] int8; kscale/vscale/base [G][D];
+    kc2/vc2 [G][n][D] uint8; ks2/vs2 [G][n][D/g2] float32; kz2/vz2 [G][n][D/g2] uint8.
+    """
+    k, pk = _c(k_bits, np.uint16)
+    v, pv = _c(v_bits, np.uint16)
+    sc, _ = _c(score, np.float32)
+    T, D = k.shape
+    G, n, ng = T // DSQ_GROUP, DSQ_GROUP - n_sig, D // g2
+    r = {
+        "mask": np.zeros(G, np.uint64),
+        "ksig": np.zeros((G, n_sig, D), np.int8), "vsig": np.zeros((G, n_sig, D), np.int8),
+        "kscale": np.zeros((G, D), np.float32), "vscale": np.zeros((G, D), np.float32),
+        "base": np.zeros((G, D), np.float32),
+        "kc2": np.zeros((G, n, D), np.uint8), "vc2": np.zeros((G, n, D), np.uint8),
+        "ks2": np.zeros((G, n, ng), np.float32), "vs2": np.zeros((G, n, ng), np.float32),
+        "kz2": np.zeros((G, n, ng), np.uint8), "vz2": np.zeros((G, n, ng), np.uint8),
+    }
+    L = lib()
+    for g in range(G):
+        o = g * DSQ_GROUP
+        L.ora_dsq_group(pk + o * D * 2, pv + o * D * 2, sc.ctypes.data + o * 4, DSQ_GROUP, D, n_sig, g2,
+                        r["mask"][g:].ctypes.data, r["ksig"][g].ctypes.data, r["kscale"][g].ctypes.data,
+                        r["vsig"][g].ctypes.data, r["vscale"][g].ctypes.data, r["base"][g].ctypes.data,
+                        r["kc2"][g].ctypes.data, r["ks2"][g].ctypes.data, r["kz2"][g].ctypes.data,
+                        r["vc2"][g].ctypes.data, r["vs2"][g].ctypes.data, r["vz2"][g].ctypes.data)
+    return r
+
+
+def dsq_dequant(r, g2=32):
+    """Dequantized K and V [T][D] float32 in token order from a dsq_quant result."""
+    G, D = r["kscale"].shape
+    khat = np.zeros((G * DSQ_GROUP, D), np.float32)
+    vhat = np.zeros((G * DSQ_GROUP, D), np.float32)
+    L = lib()
+    for g in range(G):
+        a = [np.ascontiguousarray(r[x][g]) for x in
+             ("ksig", "kscale", "vsig", "vscale", "base", "kc2", "ks2", "kz2", "vc2", "vs2", "vz2")]
+        L.ora_dsq_dequant_group(int(r["mask"][g]), DSQ_GROUP, D, g2, *[x.ctypes.data for x in a],
+                                khat[g * DSQ_GROUP:].ctypes.data, vhat[g * DSQ_GROUP:].ctypes.data)
+    return khat, vhat

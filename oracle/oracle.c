@@ -511,3 +511,154 @@ void ora_lse_merge(int parts, const double* m, const double* l, const double* o,
   }
   for (int d = 0; d < D; ++d) out[d] /= L;
 }
+
+/* ---------------------------------------------------------------------- */
+/* KVO-LLM differential significant-token quantization (DSQ)               */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * [KVO-LLM] §3.1 (DSQ): tokens are grouped 64 at a time and the top 20 % of
+ * each group by attention statistics are the significant tokens, marked in a
+ * 1-bit mask; significant ("base") tokens are stored as INT8 with per-channel
+ * scales, K of the other tokens as an INT2 difference from the base, V of the
+ * other tokens as group-wise INT2.  The page's learnable scale compensation
+ * is left out.
+ *
+ * Readings (the page gives the steps, not the arithmetic):
+ *  - The statistic is an input: one binary32 importance score per token.
+ *    Significant = the n_sig largest scores of the group (the page's 20 % of
+ *    64 is 12.8; callers use n_sig = 13).  Scores are ordered by their bit
+ *    patterns as a total order (-0 below +0, NaNs at the ends by sign), ties
+ *    by the lower token index, so exactly n_sig tokens are chosen.
+ *  - Significant K and V: symmetric INT8 per channel over the group's
+ *    significant tokens, s_d = max|x| / 127, code = clamp(rne(x / s_d),
+ *    -128, 127) (the INT8 listing's quantizer, applied per channel).
+ *  - K base: one row per group, the mean of the dequantized significant K
+ *    rows, base_d = fl(fl(sum_i fl(s_d * c_id)) / n_sig), summed in token
+ *    order, so that the page's "difference from the base" has one base.
+ *  - K difference of a non-significant token: delta = fl(k - base) in
+ *    binary32, quantized as asymmetric INT2 in groups of g2 channels (the
+ *    page fixes INT2, not its scale), exactly like a V group.
+ *  - Rows are kept in token order within each class (slot i of a class is
+ *    its i-th token); the mask restores positions.
+ */
+static unsigned dsq_key(float x) {
+  uint32_t b;
+  memcpy(&b, &x, 4);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+/* Asymmetric b-bit quantization of n binary32 values (same rule as
+ * ora_quant_group_asym, for inputs that are not fp16). */
+static void quant_group_asym_f32(const float* x, long n, int bits, float* s_out, uint8_t* z_out,
+                                 uint8_t* q) {
+  int qmax = (1 << bits) - 1;
+  float lo = 0.0f, hi = 0.0f;
+  for (long i = 0; i < n; ++i) {
+    if (x[i] < lo) lo = x[i];
+    if (x[i] > hi) hi = x[i];
+  }
+  float s = (hi - lo) / (float)qmax;
+  *s_out = s;
+  if (s == 0.0f) {
+    *z_out = 0;
+    for (long i = 0; i < n; ++i) q[i] = 0;
+    return;
+  }
+  int z = clampi((int)rintf(-lo / s), 0, qmax);
+  *z_out = (uint8_t)z;
+  for (long i = 0; i < n; ++i) q[i] = (uint8_t)clampi((int)rintf(x[i] / s) + z, 0, qmax);
+}
+
+/*
+ * One group of T = 64 tokens (k, v: [T][D] fp16; score: [T]).
+ * Outputs (n_ns = T - n_sig):
+ *   mask:   bit t set when token t is significant
+ *   ksig, vsig [n_sig][D] int8 codes, kscale, vscale [D] channel scales
+ *   base   [D] the K base row
+ *   kc2, vc2 [n_ns][D] INT2 codes (one per byte), ks2, vs2 [n_ns][D/g2]
+ *   scales, kz2, vz2 [n_ns][D/g2] zero-points.
+ */
+void ora_dsq_group(const uint16_t* k, const uint16_t* v, const float* score, int T, int D, int n_sig,
+                   int g2, uint64_t* mask, int8_t* ksig, float* kscale, int8_t* vsig, float* vscale,
+                   float* base, uint8_t* kc2, float* ks2, uint8_t* kz2, uint8_t* vc2, float* vs2,
+                   uint8_t* vz2) {
+  /* 1. significant tokens: rank by score, ties to the lower index */
+  int sig_tok[64], ns_tok[64], n_s = 0, n_n = 0;
+  uint64_t m = 0;
+  for (int t = 0; t < T; ++t) {
+    int rank = 0;
+    for (int u = 0; u < T; ++u) {
+      unsigned ku = dsq_key(score[u]), kt = dsq_key(score[t]);
+      if (ku > kt || (ku == kt && u < t)) ++rank;
+    }
+    if (rank < n_sig) m |= (uint64_t)1 << t;
+  }
+  for (int t = 0; t < T; ++t) {
+    if ((m >> t) & 1u) sig_tok[n_s++] = t;
+    else ns_tok[n_n++] = t;
+  }
+  *mask = m;
+  /* 2. significant K and V: INT8 per channel over the significant tokens */
+  uint16_t col[64];
+  int8_t qc[64];
+  for (int d = 0; d < D; ++d) {
+    for (int i = 0; i < n_s; ++i) col[i] = k[(long)sig_tok[i] * D + d];
+    ora_quant_group_sym8(col, n_s, 1, &kscale[d], qc);
+    for (int i = 0; i < n_s; ++i) ksig[(long)i * D + d] = qc[i];
+    for (int i = 0; i < n_s; ++i) col[i] = v[(long)sig_tok[i] * D + d];
+    ora_quant_group_sym8(col, n_s, 1, &vscale[d], qc);
+    for (int i = 0; i < n_s; ++i) vsig[(long)i * D + d] = qc[i];
+  }
+  /* 3. K base: mean of the dequantized significant rows */
+  for (int d = 0; d < D; ++d) {
+    float acc = 0.0f;
+    for (int i = 0; i < n_s; ++i) acc = acc + kscale[d] * (float)ksig[(long)i * D + d];
+    base[d] = acc / (float)n_s;
+  }
+  /* 4. the other tokens: K difference and V, INT2 groups of g2 channels */
+  int ng = D / g2;
+  float dx[128];
+  for (int j = 0; j < n_n; ++j) {
+    const uint16_t* kr = k + (long)ns_tok[j] * D;
+    const uint16_t* vr = v + (long)ns_tok[j] * D;
+    for (int d = 0; d < D; ++d) dx[d] = ora_f16_to_f32(kr[d]) - base[d];
+    for (int gi = 0; gi < ng; ++gi) {
+      quant_group_asym_f32(dx + (long)gi * g2, g2, 2, &ks2[(long)j * ng + gi], &kz2[(long)j * ng + gi],
+                           kc2 + (long)j * D + (long)gi * g2);
+      ora_quant_group_asym(vr + (long)gi * g2, g2, 1, 2, &vs2[(long)j * ng + gi], &vz2[(long)j * ng + gi],
+                           vc2 + (long)j * D + (long)gi * g2);
+    }
+  }
+}
+
+/*
+ * Dequantized rows of one DSQ group in token order (khat, vhat: [T][D]):
+ * significant tokens s_d * c, others base + (c - z) * s (K) and (c - z) * s
+ * (V), each one binary32 operation per step.
+ */
+void ora_dsq_dequant_group(uint64_t mask, int T, int D, int g2, const int8_t* ksig, const float* kscale,
+                           const int8_t* vsig, const float* vscale, const float* base,
+                           const uint8_t* kc2, const float* ks2, const uint8_t* kz2, const uint8_t* vc2,
+                           const float* vs2, const uint8_t* vz2, float* khat, float* vhat) {
+  int ng = D / g2, i = 0, j = 0;
+  for (int t = 0; t < T; ++t) {
+    float* kr = khat + (long)t * D;
+    float* vr = vhat + (long)t * D;
+    if ((mask >> t) & 1u) {
+      for (int d = 0; d < D; ++d) {
+        kr[d] = kscale[d] * (float)ksig[(long)i * D + d];
+        vr[d] = vscale[d] * (float)vsig[(long)i * D + d];
+      }
+      ++i;
+    } else {
+      for (int d = 0; d < D; ++d) {
+        int gi = d / g2;
+        float kd = (float)((int)kc2[(long)j * D + d] - (int)kz2[(long)j * ng + gi]) * ks2[(long)j * ng + gi];
+        kr[d] = base[d] + kd;
+        vr[d] = (float)((int)vc2[(long)j * D + d] - (int)vz2[(long)j * ng + gi]) * vs2[(long)j * ng + gi];
+      }
+      ++j;
+    }
+  }
+}
