@@ -24,6 +24,12 @@ Workloads (seeded synthetic fp16 K/V, head_dim 128; ``--workload N``):
               (max|x| / 448) per token and head
   7 paged     workload 2 in a paged cache: pages of 64 tokens handed out in a
               seeded random order from one pool, read through a block table
+  8 dsq       batch 16, 32 MHA heads, 4096 tokens (workload 2's distribution)
+              in KVO-LLM's differential significant-token cache: per 64-token
+              group the 13 tokens with the largest seeded scores (exp N(0,1))
+              INT8 per channel, the other 51 INT2 in groups of 32 (K as the
+              difference from the significant mean); step = 1 decode query
+              per head
 
 Prints one JSON line.  value = algorithmic bytes of a step (packed cache and
 metadata read by decode, query read, output written, appended tokens read
@@ -59,7 +65,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
     p.add_argument("--num-splits", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=16.0,
                    help="budget of the CPU-oracle leg (half single-threaded, half all threads)")
@@ -339,6 +345,41 @@ class Oaken(Workload):
         return int(2 * rows * (256 + 64 + 2 * 9 + 4 + 2 * per_row_entries))
 
 
+DSQ_SIG = 13  # significant tokens per 64-token group (20 % of 64, rounded up)
+
+
+def dsq_group_bytes(n_sig=DSQ_SIG):
+    """Bytes decode reads per 64-token DSQ group and tensor: significant int8 rows, their channel
+    scales, the other INT2 rows and their (scale, zero) per 32 channels."""
+    n = 64 - n_sig
+    return n_sig * 128 + 128 * 4 + n * 32 + n * 4 * 5
+
+
+class Dsq(Workload):
+    """Workload 8: KVO-LLM differential significant-token quantization, decode only per step."""
+
+    def __init__(self, w, torch, K):
+        super().__init__(w, torch, K)
+        B, H, T = w.batch, w.kv_heads, w.tokens
+        self.kx, self.vx = upload_kv(w, 0, torch), upload_kv(w, 1, torch)
+        self.sc = torch.from_numpy(w.scores()).cuda()
+        self.caches = [K.QuantKVCache(B, H, T, K.KVQ_MODE_DSQ, k_group=32, v_group=32, dsq_sig=DSQ_SIG)]
+        self.q = torch.from_numpy(w.q().view("int16")).cuda()
+        self.pos0 = i32(torch, [0] * B)
+        self.seq_len = i32(torch, [T] * B)
+        self.max_len = T
+        self.make_workspaces()
+        self.prefill_tokens = B * T
+
+    def prefill(self, r=0):
+        self.K.kvq_dsq_append(self.caches[r].desc, self.kx, self.vx, self.sc, self.w.tokens, self.pos0)
+
+    def decode_bytes(self):
+        w = self.w
+        groups = w.batch * w.kv_heads * (w.tokens // 64)
+        return 2 * groups * dsq_group_bytes() + w.batch * w.q_heads * 128 * (2 + 4)
+
+
 def build_workload(idx, torch, K, synth):
     w = synth.WORKLOADS[idx]
     if idx == 1:
@@ -353,6 +394,8 @@ def build_workload(idx, torch, K, synth):
         return ChannelK(w, torch, K)
     if idx == 4:
         return Cocktail(w, torch, K)
+    if idx == 8:
+        return Dsq(w, torch, K)
     return Oaken(w, torch, K)
 
 
@@ -377,6 +420,11 @@ WORKLOAD_TEXT = {
     7: "llama2-7b-layer-int8-paged: workload 2 (batch 16, 32 MHA heads, 4096 cached + 1 appended "
        "token, INT8 symmetric per token and head) in a paged cache, 64-token pages in a seeded random "
        "order, block table read by decode; step = append 1 token per sequence + 1 decode query per head",
+    8: "llama2-7b-layer-dsq: batch 16, 32 MHA heads, head_dim 128, 4096 tokens N(0,1) with 4 outlier "
+       "channels x15 per head, seeded exp(N(0,1)) token scores; KVO-LLM differential significant-token "
+       "quantization: per 64-token group the 13 top-scored tokens INT8 per channel, the other 51 INT2 "
+       "in groups of 32 (K as the difference from the significant mean), 1-bit mask; "
+       "step = 1 decode query per head",
 }
 
 
@@ -418,6 +466,12 @@ def oracle_slice(w, idx, b, h, thr=None):
         kh = oracle.dequant_channel_blocks(kc, ks, kz, 64)
         vh = oracle.dequant_rows(vc, vs, vz, 64)
         nbytes = T * 64 + (T // 64) * 128 * 5 + T * 74
+    elif idx == 8:
+        sc = w.scores(b, b + 1)[0, h]
+        r = oracle.dsq_quant(k, v, sc, n_sig=DSQ_SIG)
+        t1 = time.perf_counter()
+        kh, vh = oracle.dsq_dequant(r)
+        nbytes = 2 * (T // 64) * dsq_group_bytes()
     elif idx == 4:
         CT = w.chunk_tokens
         bits_c, _ = oracle.chunk_bits(*w.chunk_embeddings(b))

@@ -8,6 +8,7 @@
  *  [KVQ-Eng]    "大模型推理加速之KV Cache量化压缩原理与工程实现" (yunthe.com)
  *  [Cocktail]   Cocktail chunk-adaptive mixed-precision KV-cache page (peacm.com)
  *  [TurboQuant] TurboQuant KV-cache page (bhfrc.com)
+ *  [KVO-LLM]    "长上下文LLM推理中的KV Cache优化技术解析" (intelliparadigm.com)
  *
  * Conventions shared by every entry point
  *  - Layout of K and V follows the cache-size formula of [KVQ-Eng]
@@ -53,7 +54,8 @@ typedef enum kvq_status {
 enum {
   KVQ_MODE_UNIFORM = 0,     /* one bit-width per tensor */
   KVQ_MODE_CHUNK_MIXED = 1, /* Cocktail: FP16 / INT4 / INT2 per 32-token chunk, reordered */
-  KVQ_MODE_OAKEN = 2        /* Oaken: dense INT4 body + sparse shifted outer values */
+  KVQ_MODE_OAKEN = 2,       /* Oaken: dense INT4 body + sparse shifted outer values */
+  KVQ_MODE_DSQ = 3          /* KVO-LLM DSQ: significant tokens INT8, the others INT2 */
 };
 
 /* Grouping axis of a tensor. */
@@ -126,6 +128,27 @@ enum {
  *                          until the sequence's final chunk
  *    codes/scale/zero   INT4 pool, TOKEN-axis layout with C*chunk_tokens rows
  *    codes2/scale2/zero2 INT2 pool, same layout
+ *  DSQ ([KVO-LLM] §3.1; Q = S / 64 token groups per (b, h), n = dsq_sig
+ *  significant tokens per group, group = 32 for both tensors, bits and
+ *  symmetric ignored):
+ *    codes  [B][H][Q][16][D]  int8 rows of the significant tokens, slot i =
+ *                          the group's i-th significant token in token order;
+ *                          code = clamp(rne(x / s_d), -128, 127) with the
+ *                          channel scale s_d = max|x| / 127 over the group's
+ *                          significant tokens; slots n .. 15 hold zeros
+ *    scale  [B][H][Q][D]   float channel scales s_d
+ *    codes2 [B][H][Q][64][D/4] INT2 rows of the other tokens, slot j = the
+ *                          group's j-th other token in token order; slots
+ *                          64 - n .. 63 hold zeros
+ *    scale2, zero2 [B][H][Q][64][D/32] float / uint8, asymmetric groups of
+ *                          32 channels (quantizer above, bits 2).  V rows
+ *                          quantize v; K rows quantize the difference
+ *                          delta = fl(k - base_d) from the group's base row
+ *                          base_d = fl(fl(sum_i fl(s_d * c_id)) / n), the mean
+ *                          of its dequantized significant K rows summed in
+ *                          slot order, so k_hat = base + (c - z) * s
+ *    dsq_mask (cache) [B][H][Q] uint64, bit t set when token t of the group
+ *                          is significant
  *
  * Packed rows.  A row holds the 128 codes of one token in 16 words of 8
  * codes (a word is 8 * bits / 8 bytes; inside a word, code e sits at bits
@@ -182,6 +205,10 @@ typedef struct kvq_cache {
   int32_t page_tokens;          /* 0, 64, 128 or 256; max_seq a multiple of it */
   int32_t num_pages;            /* pages in each pool (paged: >= 1) */
   const int32_t* block_table;   /* paged: device int32 [batch][max_seq / page_tokens] */
+  /* DSQ mode ([KVO-LLM] §3.1): significant tokens per 64-token group (1 .. 16;
+   * the page's top 20 % of 64 is 12.8, so 13) and the significance mask. */
+  int32_t dsq_sig;
+  uint64_t* dsq_mask;           /* device [batch][kv_heads][max_seq / 64], 8-byte aligned */
 } kvq_cache;
 
 /* Byte sizes of every buffer of one tensor; 0 = buffer not used. */
@@ -192,6 +219,7 @@ typedef struct kvq_tensor_bytes {
 typedef struct kvq_cache_bytes_t {
   kvq_tensor_bytes k, v;
   size_t perm, seg, status;
+  size_t dsq_mask;
 } kvq_cache_bytes_t;
 
 /*
@@ -221,6 +249,8 @@ kvq_status kvq_cache_bytes(const kvq_cache* c, kvq_cache_bytes_t* out);
  *  CHUNK_MIXED:  whole-sequence prefill: t_new == max_seq and pos[b] == 0;
  *                perm/seg from kvq_reorder_chunks select, for every slot,
  *                the source chunk and its class (FP16 chunks are copied).
+ *  DSQ:          not accepted (INVALID_ARG): use kvq_dsq_append, which
+ *                takes the token scores the selection needs.
  */
 kvq_status kvq_quant_append(const kvq_cache* c, const void* k_new, const void* v_new,
                             int32_t t_new, const int32_t* pos, void* stream);
@@ -262,6 +292,30 @@ kvq_status kvq_reorder_chunks(const kvq_cache* c, const uint8_t* chunk_bits, int
  */
 kvq_status kvq_append_chunks(const kvq_cache* c, const void* k_new, const void* v_new, int32_t t_new,
                              const int32_t* pos, const uint8_t* new_bits, int32_t n_new, void* stream);
+
+/*
+ * [KVO-LLM] §3.1 differential significant-token quantization of t_new new
+ * tokens per sequence, in whole groups of 64 (DSQ mode only; layout and
+ * arithmetic in the DSQ buffer description above).  In each group the
+ * dsq_sig tokens with the largest scores are significant: scores are
+ * ordered by their binary32 bit patterns as a total order (-0 below +0,
+ * NaNs at the ends by sign), ties to the lower token index, so exactly
+ * dsq_sig tokens are chosen.
+ *  k_new, v_new: device fp16 [batch][kv_heads][t_new][128].
+ *  score:        device float [batch][kv_heads][t_new], the per-token
+ *                attention statistic of the page (e.g. attention mass over a
+ *                recent window), 4-byte aligned.
+ *  t_new:        a multiple of 64 (else INVALID_ARG).
+ *  pos:          device int32 [batch]; the tokens go to positions pos[b] ..
+ *                pos[b] + t_new - 1, pos[b] a multiple of 64; a sequence
+ *                whose pos[b] is negative, not a multiple of 64 or past
+ *                max_seq - t_new is skipped and sets KVQ_FLAG_POS_RANGE.
+ * Decode (kvq_decode_attn) attends the complete groups of seq_len[b]; a
+ * seq_len[b] that is not a multiple of 64 attends floor(seq_len[b] / 64)
+ * groups and sets KVQ_FLAG_LEN_RANGE.
+ */
+kvq_status kvq_dsq_append(const kvq_cache* c, const void* k_new, const void* v_new, const float* score,
+                          int32_t t_new, const int32_t* pos, void* stream);
 
 /*
  * Workspace needed by kvq_decode_attn for the same (c, q_heads, max_len,

@@ -29,6 +29,7 @@ KVQ_ERR_HIP = -6
 KVQ_MODE_UNIFORM = 0
 KVQ_MODE_CHUNK_MIXED = 1
 KVQ_MODE_OAKEN = 2
+KVQ_MODE_DSQ = 3
 KVQ_AXIS_TOKEN = 0
 KVQ_AXIS_CHANNEL = 1
 KVQ_FMT_INT = 0
@@ -57,7 +58,7 @@ class kvq_cache(ctypes.Structure):
     _fields_ = [("batch", _i32), ("kv_heads", _i32), ("max_seq", _i32), ("head_dim", _i32),
                 ("mode", _i32), ("chunk_tokens", _i32), ("k", kvq_tensor), ("v", kvq_tensor),
                 ("perm", _vp), ("seg", _vp), ("status", _vp), ("page_tokens", _i32), ("num_pages", _i32),
-                ("block_table", _vp)]
+                ("block_table", _vp), ("dsq_sig", _i32), ("dsq_mask", _vp)]
 
 
 class kvq_tensor_bytes(ctypes.Structure):
@@ -66,7 +67,7 @@ class kvq_tensor_bytes(ctypes.Structure):
 
 class kvq_cache_bytes_t(ctypes.Structure):
     _fields_ = [("k", kvq_tensor_bytes), ("v", kvq_tensor_bytes), ("perm", _sz), ("seg", _sz),
-                ("status", _sz)]
+                ("status", _sz), ("dsq_mask", _sz)]
 
 
 class KVQError(RuntimeError):
@@ -78,7 +79,7 @@ class KVQError(RuntimeError):
 _lib = None
 
 EXPORTS = ("kvq_cache_bytes", "kvq_quant_append", "kvq_reorder_chunks", "kvq_append_chunks",
-           "kvq_decode_workspace_bytes",
+           "kvq_dsq_append", "kvq_decode_workspace_bytes",
            "kvq_decode_attn", "kvq_chunk_bits", "kvq_hist_f16", "kvq_hist_percentiles",
            "kvq_status_string")
 
@@ -95,6 +96,7 @@ def lib():
         L.kvq_quant_append.argtypes = [P(kvq_cache), _vp, _vp, _i32, _vp, _vp]
         L.kvq_reorder_chunks.argtypes = [P(kvq_cache), _vp, _i32, _vp]
         L.kvq_append_chunks.argtypes = [P(kvq_cache), _vp, _vp, _i32, _vp, _vp, _i32, _vp]
+        L.kvq_dsq_append.argtypes = [P(kvq_cache), _vp, _vp, _vp, _i32, _vp, _vp]
         L.kvq_decode_workspace_bytes.argtypes = [P(kvq_cache), _i32, _i32, _i32, P(_sz)]
         L.kvq_decode_attn.argtypes = [P(kvq_cache), _vp, _i32, _vp, _i32, _f32, _vp, _vp, _sz, _i32, _vp]
         L.kvq_chunk_bits.argtypes = [_vp, _vp, _i32, _i32, _i32, ctypes.c_double, ctypes.c_double, _vp,
@@ -159,6 +161,11 @@ def kvq_append_chunks(cache: kvq_cache, k_new, v_new, t_new: int, pos, new_bits,
     return _check(lib().kvq_append_chunks(ctypes.byref(cache), _ptr(k_new), _ptr(v_new), int(t_new),
                                           _ptr(pos), _ptr(new_bits), int(n_new), _stream(stream)),
                   "kvq_append_chunks")
+
+
+def kvq_dsq_append(cache: kvq_cache, k_new, v_new, score, t_new: int, pos, stream=None) -> int:
+    return _check(lib().kvq_dsq_append(ctypes.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(score), int(t_new),
+                                       _ptr(pos), _stream(stream)), "kvq_dsq_append")
 
 
 def kvq_decode_workspace_bytes(cache: kvq_cache, q_heads: int, max_len: int, num_splits: int = 0) -> int:

@@ -20,6 +20,7 @@ SOURCES = [
     "kvq_decode_uniform.hip",
     "kvq_decode_oaken.hip",
     "kvq_decode_mixed.hip",
+    "kvq_decode_dsq.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

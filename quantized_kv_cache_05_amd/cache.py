@@ -19,7 +19,7 @@ class QuantKVCache:
                  k_axis: int = KVQ_AXIS_TOKEN, k_group: int = 64, v_group: int | None = None,
                  chunk_tokens: int = 32, k_thr=None, v_thr=None, sparse_cap: int = 0,
                  device="cuda", zero_fill: bool = False, fmt: int = 0, page_tokens: int = 0,
-                 num_pages: int = 0, block_table=None):
+                 num_pages: int = 0, block_table=None, dsq_sig: int = 13):
         import torch
         self.torch = torch
         c = kvq_cache()
@@ -36,6 +36,7 @@ class QuantKVCache:
                     t.thr[i] = float(thr[i])
             t.sparse_cap = sparse_cap
         c.page_tokens, c.num_pages = page_tokens, num_pages
+        c.dsq_sig = dsq_sig
         if block_table is not None:
             self.block_table = block_table  # device int32 [batch][max_seq / page_tokens], kept alive here
             c.block_table = block_table.data_ptr()
@@ -56,6 +57,10 @@ class QuantKVCache:
                 buf = torch.zeros(n // 4, dtype=torch.int32, device=device)
                 self.buffers[field] = buf
                 setattr(c, field, buf.data_ptr())
+        if self.sizes.dsq_mask:
+            buf = torch.zeros(self.sizes.dsq_mask // 8, dtype=torch.int64, device=device)
+            self.buffers["dsq_mask"] = buf
+            c.dsq_mask = buf.data_ptr()
         self.status = torch.zeros(1, dtype=torch.int32, device=device)
         c.status = self.status.data_ptr()
 

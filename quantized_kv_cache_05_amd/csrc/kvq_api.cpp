@@ -77,6 +77,13 @@ kvq_status check_config(const kvq_cache* c) {
       if (k.format != KVQ_FMT_INT || v.format != KVQ_FMT_INT) return KVQ_ERR_UNSUPPORTED;
       return KVQ_OK;
     }
+    case KVQ_MODE_DSQ: {
+      if (c->dsq_sig < 1 || c->dsq_sig > 16) return KVQ_ERR_INVALID_ARG;
+      if (k.group != 32 || v.group != 32) return KVQ_ERR_UNSUPPORTED;
+      if (k.axis != KVQ_AXIS_TOKEN || v.axis != KVQ_AXIS_TOKEN) return KVQ_ERR_UNSUPPORTED;
+      if (k.format != KVQ_FMT_INT || v.format != KVQ_FMT_INT) return KVQ_ERR_UNSUPPORTED;
+      return KVQ_OK;
+    }
     default:
       return KVQ_ERR_INVALID_ARG;
   }
@@ -122,6 +129,17 @@ kvq_tensor_bytes tensor_bytes(const kvq_cache* c, const kvq_tensor& t, bool is_k
       r.scale2 = B * H * S * ng * 4;
       r.zero2 = B * H * S * ng;
       break;
+    case KVQ_MODE_DSQ: {
+      // per 64-token group: 16 significant-row slots (int8, channel scales)
+      // and 64 other-row slots (INT2, groups of 32 channels)
+      const size_t Q = S / 64;
+      r.codes = B * H * Q * 16 * D;
+      r.scale = B * H * Q * D * 4;
+      r.codes2 = B * H * Q * 64 * D / 4;
+      r.scale2 = B * H * Q * 64 * (D / 32) * 4;
+      r.zero2 = B * H * Q * 64 * (D / 32);
+      break;
+    }
   }
   return r;
 }
@@ -149,6 +167,10 @@ kvq_status check_buffers(const kvq_cache* c) {
   if (c->page_tokens) {
     if (!c->block_table) return KVQ_ERR_INVALID_ARG;
     if (!aligned(c->block_table, 4)) return KVQ_ERR_ALIGNMENT;
+  }
+  if (c->mode == KVQ_MODE_DSQ) {
+    if (!c->dsq_mask) return KVQ_ERR_INVALID_ARG;
+    if (!aligned(c->dsq_mask, 8)) return KVQ_ERR_ALIGNMENT;
   }
   return KVQ_OK;
 }
@@ -191,6 +213,8 @@ CacheArgs cache_args(const kvq_cache* c) {
   a.pages = c->page_tokens ? c->block_table : nullptr;
   a.ptok = c->page_tokens;
   a.npages = c->num_pages;
+  a.dsq_sig = c->mode == KVQ_MODE_DSQ ? c->dsq_sig : 0;
+  a.dsq_mask = reinterpret_cast<unsigned long long*>(c->mode == KVQ_MODE_DSQ ? c->dsq_mask : nullptr);
   return a;
 }
 
@@ -283,6 +307,8 @@ kvq_status kvq_cache_bytes(const kvq_cache* c, kvq_cache_bytes_t* out) {
     out->perm = (size_t)c->batch * C * 4;
     out->seg = (size_t)c->batch * 4 * 4;
   }
+  if (c->mode == KVQ_MODE_DSQ)
+    out->dsq_mask = (size_t)c->batch * (size_t)c->kv_heads * (size_t)(c->max_seq / 64) * 8;
   out->status = 4;
   return KVQ_OK;
 }
@@ -329,8 +355,30 @@ kvq_status kvq_quant_append(const kvq_cache* c, const void* k_new, const void* v
       e = kvq::launch_quant_mixed(a, a.k, false, kx, pos, st);
       if (e == hipSuccess) e = kvq::launch_quant_mixed(a, a.v, true, vx, pos, st);
       break;
+    default:  // DSQ needs token scores: kvq_dsq_append
+      return KVQ_ERR_INVALID_ARG;
   }
   return from_hip(e);
+}
+
+kvq_status kvq_dsq_append(const kvq_cache* c, const void* k_new, const void* v_new, const float* score,
+                          int32_t t_new, const int32_t* pos, void* stream) {
+  kvq_status s = check_config(c);
+  if (s != KVQ_OK) return s;
+  if (c->mode != KVQ_MODE_DSQ) return KVQ_ERR_INVALID_ARG;
+  if (t_new < 0 || t_new % 64) return KVQ_ERR_INVALID_ARG;
+  if (t_new > c->max_seq) return KVQ_ERR_CAPACITY;
+  if (t_new == 0) return KVQ_OK;
+  if ((long long)c->batch * c->kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (!k_new || !v_new || !score || !pos) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(score, 4) || !aligned(pos, 4))
+    return KVQ_ERR_ALIGNMENT;
+  s = check_buffers(c);
+  if (s != KVQ_OK) return s;
+  const CacheArgs a = cache_args(c);
+  return from_hip(kvq::launch_quant_dsq(a, static_cast<const uint16_t*>(k_new),
+                                        static_cast<const uint16_t*>(v_new), score, t_new, pos,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 kvq_status kvq_reorder_chunks(const kvq_cache* c, const uint8_t* chunk_bits, int32_t n_chunks,
@@ -417,6 +465,7 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t q_heads, c
   switch (c->mode) {
     case KVQ_MODE_UNIFORM: e = kvq::launch_decode_uniform(a, d, st); break;
     case KVQ_MODE_OAKEN: e = kvq::launch_decode_oaken(a, d, st); break;
+    case KVQ_MODE_DSQ: e = kvq::launch_decode_dsq(a, d, st); break;
     default: e = kvq::launch_decode_mixed(a, d, st); break;
   }
   if (e == hipErrorInvalidValue) return KVQ_ERR_UNSUPPORTED;

@@ -359,6 +359,7 @@ struct AttnParams {
   const int* pages;  // paged layout: block table [B][S / ptok]; null when contiguous
   int pshift;        // log2 tokens per page
   int npages;
+  int dsq_sig;       // DSQ: significant tokens per 64-token group
 };
 
 // One tensor's view for a (b, kv head): code rows and token-axis metadata.

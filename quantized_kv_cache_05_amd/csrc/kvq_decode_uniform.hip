@@ -137,6 +137,7 @@ AttnParams make_attn_params(const CacheArgs& c, const DecodeLaunch& d) {
   P.pages = c.pages;
   P.pshift = c.ptok ? __builtin_ctz((unsigned)c.ptok) : 0;
   P.npages = c.npages;
+  P.dsq_sig = c.dsq_sig;
   return P;
 }
 

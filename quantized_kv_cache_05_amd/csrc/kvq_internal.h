@@ -43,6 +43,8 @@ struct CacheArgs {
   const int* pages;  // paged: block table [B][S / ptok]; null when contiguous
   int ptok;          // tokens per page
   int npages;        // pages per pool
+  int dsq_sig;                 // DSQ: significant tokens per 64-token group
+  unsigned long long* dsq_mask;  // DSQ: [B][H][S / 64] significance masks
 };
 
 struct DecodeLaunch {
@@ -88,6 +90,10 @@ hipError_t launch_chunk_seg(const CacheArgs& c, int t_new, const int* pos, const
 hipError_t launch_append_chunks(const CacheArgs& c, const uint16_t* xk, const uint16_t* xv, int t_new,
                                 const int* pos, const uint8_t* bits, int n_new, hipStream_t st);
 
+// KVO-LLM DSQ: whole 64-token groups, K and V in one launch.
+hipError_t launch_quant_dsq(const CacheArgs& c, const uint16_t* xk, const uint16_t* xv, const float* score,
+                            int t_new, const int* pos, hipStream_t st);
+
 // Cocktail chunk precision search and Oaken calibration histogram.
 constexpr int kMaxPercentiles = 8;
 struct PercentileList {
@@ -104,6 +110,7 @@ hipError_t launch_percentiles(const unsigned long long* hist, const PercentileLi
 hipError_t launch_decode_uniform(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
 hipError_t launch_decode_oaken(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
 hipError_t launch_decode_mixed(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
+hipError_t launch_decode_dsq(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
 // longest split (tokens) the Oaken decode kernel takes for qr query heads
 int oaken_max_split(int qr);
 // log-sum-exp merge of the split partials into the output

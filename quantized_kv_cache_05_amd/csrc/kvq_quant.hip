@@ -761,6 +761,135 @@ __global__ __launch_bounds__(256) void k_quant_oaken_one(const uint16_t* __restr
   if (dropped) set_flag(status, kFlagSparseFull);
 }
 
+// ---------------------------------------------------------------------------
+// KVO-LLM differential significant-token quantization (the KVO-LLM page,
+// §3.1): per group of 64 tokens of one (b, h), the dsq_sig tokens with the
+// largest scores are significant (1-bit mask); their K and V rows become
+// INT8 with per-channel scales over the significant tokens; the other
+// tokens become INT2 rows in groups of 32 channels, V directly and K as the
+// difference from the base row, the mean of the dequantized significant K
+// rows.  Class slots follow token order.  One workgroup per (group, b h).
+
+// Scores ordered by bit pattern: a total order (-0 below +0, NaNs at the ends)
+__device__ __forceinline__ unsigned dsq_key(float x) {
+  const unsigned b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+constexpr int kDsqSigSlots = 16;  // significant-row slots per group
+constexpr int kDsqOthSlots = 64;  // other-row slots per group
+
+__global__ __launch_bounds__(256) void k_quant_dsq(const uint16_t* __restrict__ xk,
+                                                   const uint16_t* __restrict__ xv,
+                                                   const float* __restrict__ score, int t_new, int H, int S,
+                                                   int n_sig, const int* __restrict__ pos, TensorArgs kt,
+                                                   TensorArgs vt, unsigned long long* __restrict__ mask_out,
+                                                   unsigned* __restrict__ status) {
+  __shared__ int s_tok[kDsqSigSlots];
+  __shared__ int o_tok[kDsqOthSlots];
+  __shared__ int8_t sig[2][kDsqSigSlots][kD];
+  __shared__ float base[kD];
+  __shared__ uint16_t lrows[16][kD];
+  const int gi = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int b = (int)(bh / H);
+  const int p = pos[b];
+  if (p < 0 || (p & 63) || p > S - t_new) {
+    if (gi == 0 && threadIdx.x == 0) set_flag(status, kFlagPosRange);
+    return;
+  }
+  const long long Q = S / 64;
+  const long long gb = bh * Q + (p >> 6) + gi;      // destination group
+  const long long src = bh * t_new + (long long)gi * 64;  // first input row
+  const int n_oth = 64 - n_sig;
+  // 1. significant tokens: rank of each token's score, ties to the lower index
+  if (threadIdx.x < 64) {
+    const int t = threadIdx.x;
+    const unsigned key = dsq_key(score[src + t]);
+    int rank = 0;
+    for (int u = 0; u < 64; ++u) {
+      const unsigned ku = (unsigned)__shfl((int)key, u, 64);
+      rank += (ku > key || (ku == key && u < t)) ? 1 : 0;
+    }
+    const bool is_sig = rank < n_sig;
+    const unsigned long long m = __ballot(is_sig);
+    const int below = __popcll(m & ((1ull << t) - 1ull));
+    if (is_sig) s_tok[below] = t;
+    else o_tok[t - below] = t;
+    if (t == 0) mask_out[gb] = m;
+  }
+  __syncthreads();
+  // 2. significant rows: INT8 per channel; thread = (tensor, channel)
+  {
+    // the base sum rounds each product and each sum (no fused multiply-add)
+#pragma clang fp contract(off)
+    const int tsr = threadIdx.x >> 7, d = threadIdx.x & 127;
+    const uint16_t* x = (tsr ? xv : xk) + src * kD + d;
+    float xs[kDsqSigSlots];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kDsqSigSlots; ++i) {
+      const int tk = i < n_sig ? s_tok[i] : 0;
+      xs[i] = i < n_sig ? h2f(x[(long long)tk * kD]) : 0.0f;
+      amax = fmaxf(amax, fabsf(xs[i]));
+    }
+    const float s = amax / 127.0f;
+    float acc = 0.0f;  // K base: sum in slot order, one rounding per operation
+#pragma unroll
+    for (int i = 0; i < kDsqSigSlots; ++i) {
+      int q = 0;
+      if (i < n_sig && s != 0.0f) q = min(max((int)rintf(xs[i] / s), -128), 127);
+      sig[tsr][i][d] = (int8_t)q;
+      if (i < n_sig) acc = acc + s * (float)q;
+    }
+    (tsr ? vt : kt).scale[gb * kD + d] = s;
+    if (tsr == 0) base[d] = acc / (float)n_sig;
+  }
+  __syncthreads();
+  // 3. pack the significant rows: job = (tensor, slot, 8-byte word)
+  for (int j = threadIdx.x; j < 2 * kDsqSigSlots * 16; j += blockDim.x) {
+    const int tsr = j >> 8, row = (j >> 4) & 15, w = j & 15;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // K: word 4 q + s holds channels 32 s + 8 q + e; V: word n holds channels n + 16 e
+      const int ch = tsr ? (w + 16 * e) : (32 * (w & 3) + 8 * (w >> 2) + e);
+      const uint32_t byte = (uint8_t)sig[tsr][row][ch];
+      if (e < 4) lo |= byte << (8 * e);
+      else hi |= byte << (8 * (e - 4));
+    }
+    st_nt<u2q_t>((tsr ? vt : kt).codes + (gb * kDsqSigSlots + row) * kD + w * 8, u2q_t{lo, hi});
+  }
+  // 4. the other tokens: INT2 rows in groups of 32 channels; 16 lanes per row
+  const int li = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  uint16_t* lrow = lrows[rg];
+#pragma unroll
+  for (int tsr = 0; tsr < 2; ++tsr) {
+    const TensorArgs& t = tsr ? vt : kt;
+    for (int slot = rg; slot < kDsqOthSlots; slot += 16) {
+      const long long dst = gb * kDsqOthSlots + slot;
+      uint32_t plo = 0, phi = 0;
+      float s = 0.0f;
+      int z = 0;
+      if (slot < n_oth) {
+        float v[8];
+        unpack8(ld_row8((tsr ? xv : xk) + (src + o_tok[slot]) * kD + li * 8), v);
+        if (tsr == 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = v[e] - base[li * 8 + e];  // difference from the base
+        }
+        quant8<2, false, 32>(v, 0xFFu, plo, phi, s, z);
+      }
+      if (tsr) store_row_codes<2, true>(t.codes2 + dst * 32, li, plo, phi, lrow);
+      else store_row_codes<2, false>(t.codes2 + dst * 32, li, plo, phi, lrow);
+      if ((li & 3) == 0) {
+        t.scale2[dst * 4 + (li >> 2)] = s;
+        t.zero2[dst * 4 + (li >> 2)] = (uint8_t)z;
+      }
+    }
+  }
+}
+
 constexpr int kThreads = 256;
 constexpr long long kRowBlocks = 4096;  // grid bound of the row kernels (blocks of 16 rows)
 
@@ -967,6 +1096,14 @@ hipError_t launch_quant_oaken_one(const CacheArgs& c, const uint16_t* xk, const 
     case 128: hipLaunchKernelGGL((k_quant_oaken_one<128>), grid, dim3(kThreads), 0, st, xk, xv, BH, c.H, c.S, pos, c.k, c.v, c.status); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_dsq(const CacheArgs& c, const uint16_t* xk, const uint16_t* xv, const float* score,
+                            int t_new, const int* pos, hipStream_t st) {
+  const dim3 grid((unsigned)(t_new / 64), (unsigned)(c.B * c.H));
+  hipLaunchKernelGGL(k_quant_dsq, grid, dim3(kThreads), 0, st, xk, xv, score, t_new, c.H, c.S, c.dsq_sig, pos,
+                     c.k, c.v, c.dsq_mask, c.status);
   return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@ flat index) (counter-based SplitMix64 + Box-Muller, see ``synth.c``), so any
 same bytes.
 
 Streams: K = 0, V = 1, Q = 2, outlier channels = 3, chunk embeddings = 4,
-calibration K = 5, calibration V = 6.  Seed of workload i (1-based) is
+calibration K = 5, calibration V = 6, token scores = 7.  Seed of workload i (1-based) is
 20261200 + i.
 """
 from __future__ import annotations
@@ -27,7 +27,7 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 _lock = threading.Lock()
 _lib = None
 
-STREAM_K, STREAM_V, STREAM_Q, STREAM_OUTLIER, STREAM_CHUNK_EMB, STREAM_CAL_K, STREAM_CAL_V = range(7)
+STREAM_K, STREAM_V, STREAM_Q, STREAM_OUTLIER, STREAM_CHUNK_EMB, STREAM_CAL_K, STREAM_CAL_V, STREAM_SCORE = range(8)
 DIST_NORMAL, DIST_T3 = 0, 1
 
 
@@ -181,6 +181,14 @@ class Workload:
         flat = fill_f64_normal(self.seed, STREAM_CHUNK_EMB, b * per_seq, per_seq)
         return flat[: self.emb_dim], flat[self.emb_dim:].reshape(n_chunks, self.emb_dim)
 
+    def scores(self, b0=0, b1=None) -> np.ndarray:
+        """float32 [b1-b0][kv_heads][tokens] per-token importance scores, exp(N(0, 1)): positive and
+        heavy-tailed like accumulated attention mass."""
+        b1 = self.batch if b1 is None else b1
+        n = self.kv_heads * self.tokens
+        flat = fill_f64_normal(self.seed, STREAM_SCORE, b0 * n, (b1 - b0) * n)
+        return np.exp(flat).astype(np.float32).reshape(b1 - b0, self.kv_heads, self.tokens)
+
     def calibration(self, tensor: int, sample: int) -> np.ndarray:
         """fp16 bits of calibration sequence `sample`: [kv_heads][seq][head_dim]."""
         n = self.kv_heads * self.seq * self.head_dim
@@ -202,6 +210,8 @@ WORKLOADS = {
     6: Workload(6, "llama2-7b-e4m3", batch=16, kv_heads=32, q_heads=32, seq=4097, tokens=4097,
                 outlier_mult=15.0, outlier_count=4),
     7: Workload(7, "llama2-7b-int8-paged", batch=16, kv_heads=32, q_heads=32, seq=4097, tokens=4097,
+                outlier_mult=15.0, outlier_count=4),
+    8: Workload(8, "llama2-7b-dsq", batch=16, kv_heads=32, q_heads=32, seq=4096, tokens=4096,
                 outlier_mult=15.0, outlier_count=4),
 }
 

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 def test_struct_layout_matches_header(tmp_path):
     fields_t = ["bits", "symmetric", "axis", "group", "format", "thr", "sparse_cap"] + list(K.TENSOR_BUFFERS)
     fields_c = ["batch", "kv_heads", "max_seq", "head_dim", "mode", "chunk_tokens", "k", "v", "perm",
-                "seg", "status", "page_tokens", "num_pages", "block_table"]
+                "seg", "status", "page_tokens", "num_pages", "block_table", "dsq_sig", "dsq_mask"]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "kvq.h"', "int main(void){"]
     lines.append('printf("kvq_tensor %zu\\n", sizeof(kvq_tensor));')
     lines.append('printf("kvq_cache %zu\\n", sizeof(kvq_cache));')
@@ -298,3 +298,70 @@ def test_row_layout_maps_hand_examples():
     assert K16_PERM[4] == 1 and K16_PERM[1] == 2 and K16_PERM[7] == 7
     for p in (K_PERM, V_PERM, K16_PERM):
         assert sorted(p) == list(range(128))
+
+
+def _dsq_desc(B=2, H=3, S=256, sig=13, group=32):
+    c = make_desc(mode=K.KVQ_MODE_DSQ, B=B, H=H, S=S, group=group)
+    c.dsq_sig = sig
+    return c
+
+
+def test_dsq_cache_bytes():
+    B, H, S = 2, 3, 256
+    Q = S // 64
+    b = K.kvq_cache_bytes(_dsq_desc(B, H, S))
+    for t in (b.k, b.v):
+        assert (t.codes, t.scale) == (B * H * Q * 16 * 128, B * H * Q * 128 * 4)
+        assert (t.codes2, t.scale2, t.zero2) == (B * H * Q * 64 * 32, B * H * Q * 64 * 4 * 4, B * H * Q * 64 * 4)
+        assert (t.zero, t.codes16, t.oscale) == (0, 0, 0)
+    assert b.dsq_mask == B * H * Q * 8
+    assert K.kvq_cache_bytes(make_desc()).dsq_mask == 0
+
+
+@pytest.mark.parametrize("sig,group,expect", [(0, 32, K.KVQ_ERR_INVALID_ARG), (17, 32, K.KVQ_ERR_INVALID_ARG),
+                                              (13, 64, K.KVQ_ERR_UNSUPPORTED), (1, 32, K.KVQ_OK),
+                                              (16, 32, K.KVQ_OK)])
+def test_dsq_config_validation(sig, group, expect):
+    assert status_of(K.kvq_cache_bytes, _dsq_desc(sig=sig, group=group)) == expect
+
+
+def _fake_buffers(c):
+    """Aligned non-null host addresses for every buffer: validation passes, nothing is launched
+    because every call below fails a later host check."""
+    sizes = K.kvq_cache_bytes(c)
+    addr = 1 << 20
+    for t, tb in ((c.k, sizes.k), (c.v, sizes.v)):
+        for f in K.TENSOR_BUFFERS:
+            if getattr(tb, f):
+                setattr(t, f, addr)
+                addr += 1 << 20
+    c.status = addr
+    c.dsq_mask = addr + 256
+
+
+def test_dsq_append_host_validation():
+    c = _dsq_desc()
+    _fake_buffers(c)
+    p = 1 << 30
+    # whole groups only
+    assert status_of(K.kvq_dsq_append, c, p, p, p, 65, p, 0) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_dsq_append, c, p, p, p, 320, p, 0) == K.KVQ_ERR_CAPACITY
+    assert status_of(K.kvq_dsq_append, c, p, p, None, 64, p, 0) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_dsq_append, c, p, p, p + 2, 64, p, 0) == K.KVQ_ERR_ALIGNMENT
+    assert status_of(K.kvq_dsq_append, c, p, p, p, 0, p, 0) == K.KVQ_OK
+    # the score-less append is refused in DSQ mode; DSQ append refused in other modes
+    assert status_of(K.kvq_quant_append, c, p, p, 64, p, 0) == K.KVQ_ERR_INVALID_ARG
+    u = make_desc()
+    assert status_of(K.kvq_dsq_append, u, p, p, p, 64, p, 0) == K.KVQ_ERR_INVALID_ARG
+    # a missing or misaligned mask
+    c.dsq_mask = None
+    assert status_of(K.kvq_dsq_append, c, p, p, p, 64, p, 0) == K.KVQ_ERR_INVALID_ARG
+    c.dsq_mask = p + 4
+    assert status_of(K.kvq_dsq_append, c, p, p, p, 64, p, 0) == K.KVQ_ERR_ALIGNMENT
+
+
+def test_dsq_decode_workspace_plan():
+    c = _dsq_desc(B=1, H=2, S=4096)
+    # few (b, head) units: the sequence is split in 64-token multiples, partials need a workspace
+    n = K.kvq_decode_workspace_bytes(c, 2, 4096)
+    assert n > 0 and n % (K.PART_STRIDE * 4 * 2) == 0
