@@ -139,7 +139,12 @@ enum {
  *    scale  [B][H][Q][D]   float channel scales s_d
  *    codes2 [B][H][Q][64][D/4] INT2 rows of the other tokens, slot j = the
  *                          group's j-th other token in token order; slots
- *                          64 - n .. 63 hold zeros
+ *                          64 - n .. 63 hold zeros.  K rows as usual; V rows
+ *                          blocked: the 2-byte column word n (V word order)
+ *                          of slot j sits at byte ((j / 8) * 16 + n) * 16 +
+ *                          (j % 8) * 2 of the group's 2048 bytes, so the
+ *                          words of 8 consecutive slots of one column are
+ *                          one 16-byte run
  *    scale2, zero2 [B][H][Q][64][D/32] float / uint8, asymmetric groups of
  *                          32 channels (quantizer above, bits 2).  V rows
  *                          quantize v; K rows quantize the difference

@@ -34,13 +34,25 @@ template <int QR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_dsq(AttnParams P) {
   using QRW = QRows<QR>;
   constexpr int R = QR, GI = QRW::GI;
-  __shared__ AttnLds<QR, 4> L;
+  __shared__ AttnLds<QR, 4, true> L;
+  __shared__ float vscl[kNW][kD];  // per wave: the group's significant-V channel scales
   const int split = blockIdx.x, qt = blockIdx.y % P.qtiles, kvh = blockIdx.y / P.qtiles, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a wave-uniform value: group indices and group base
+  // addresses then live in scalar registers, and loads take a scalar base
+  // plus a 32-bit lane offset instead of a 64-bit address per lane
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
   const int nq = min(QR, P.G - qt * QR);
   u4_t qop[4];
   attn_prologue<QR, 4>(P, L, b, kvh, qt, nq, qop);
+  // One query (QR 1): every A row holds the query, so row r may carry it on
+  // k-step r mod 4 only; the four 32-channel group sums of a token then land
+  // in the four C elements of one accumulator (rows 4 q4 + g).
+  if constexpr (QR == 1) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if ((threadIdx.x & 3) != s) qop[s] = u4_t{0u, 0u, 0u, 0u};
+  }
   const bool reporter = split == 0 && blockIdx.y == 0 && threadIdx.x == 0;
   const int len = clamp_seq_len(P, b, reporter);
   if ((len & 63) && reporter) set_flag(P.status, kFlagLenRange);
@@ -56,90 +68,154 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const long long bh = (long long)b * P.H + kvh;
   const long long Q = P.S / 64;
   const f4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int grp = g0 + wave; grp < g1; grp += kNW) {
-    const long long gb = bh * Q + grp;
-    const uint8_t* ksig = P.k.codes + gb * kSigSlots * kD;
-    const uint8_t* vsig = P.v.codes + gb * kSigSlots * kD;
-    const float* kss = P.k.scale + gb * kD;
-    const float* vss = P.v.scale + gb * kD;
-    const TokView ko{P.k.codes2 + gb * kOthSlots * 32, P.k.scale2 + gb * kOthSlots * 4,
-                     P.k.zero2 + gb * kOthSlots * 4};
-    const TokView vo{P.v.codes2 + gb * kOthSlots * 32, P.v.scale2 + gb * kOthSlots * 4,
-                     P.v.zero2 + gb * kOthSlots * 4};
-    // ---- loads (slots past the class counts are not read) ----
-    const bool okS = n16 < nsig;
+  // Loads are branch-free: a lane whose slot lies past its class count reads
+  // a slot the wave reads anyway (no extra HBM bytes); its score is masked to
+  // -inf and its weight is 0, and what it reads is finite.  A branch around a
+  // load would make the compiler wait for it inside the branch.
+  //
+  // Two-stage pipeline: the K-side data of a group (significant and other K
+  // rows, their metadata, the channel scales of the scaled-query table) is
+  // loaded during the previous group's V products, into the registers its K
+  // products have just released; the V-side data of a group is loaded when
+  // its K products start.
+  constexpr int NE = 16 * R, PER = (NE + 63) / 64;
+  static_assert((NE & (NE - 1)) == 0, "entry count is a power of two");
+  const bool okS = n16 < nsig;
+  bool okO[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) okO[cb] = 16 * cb + n16 < noth;
+  struct KSide {
+    float4 tsa[PER], tsb[PER];  // table channel scales, loaded first
     KI8<true> kS;
-    kS.a = u4_t{0u, 0u, 0u, 0u};
-    kS.b = kS.a;
-    if (okS) kS.load(ksig + n16 * kD, q4);
     KI2 kO[4];
-    float sk[4][4], zk[4][4], sv[4][4], zd[4][4];
-    bool okO[4];
+    u4_t skr[4];      // scales of the slot's 4 channel groups (binary32 bits)
+    unsigned zkr[4];  // zero-points of the slot's 4 groups (bytes)
+  };
+  auto load_k = [&](int grp, KSide& d) {
+    const long long gb = bh * Q + grp;
+    const float* kss = P.k.scale + gb * kD;
+    // lane l builds table entry (l + 64 k) mod NE (NE = 16, 64 or 256): with
+    // one query four lanes build each entry and store the same values, which
+    // keeps the build free of branches
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = (lane + 64 * k) & (NE - 1);
+      const int c0 = 32 * (e / (4 * R)) + 8 * (e & 3);
+      d.tsa[k] = *reinterpret_cast<const float4*>(kss + c0);
+      d.tsb[k] = *reinterpret_cast<const float4*>(kss + c0 + 4);
+    }
+    d.kS.load(P.k.codes + (gb * kSigSlots + (okS ? n16 : 0)) * kD, q4);
+    const uint8_t* kc = P.k.codes2 + gb * kOthSlots * 32;
+    const float* ks = P.k.scale2 + gb * kOthSlots * 4;
+    const uint8_t* kz = P.k.zero2 + gb * kOthSlots * 4;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      const int slot = 16 * cb + n16;
-      okO[cb] = slot < noth;
-      kO[cb].r = u2_t{0u, 0u};
-#pragma unroll
-      for (int g = 0; g < 4; ++g) sk[cb][g] = zk[cb][g] = sv[cb][g] = 0.0f;
-      if (okO[cb]) {
-        kO[cb].load(ko.codes + slot * KI2::RB, q4);
-        load_tok_meta<4, false>(ko, slot, sk[cb], zk[cb]);
-        load_tok_meta<4, true>(vo, slot, sv[cb], zd[cb]);
-      }
+      // at most 16 significant tokens, so slots 0-47 always exist: only the
+      // last column block needs the substitute slot
+      const int rs = (cb < 3 || okO[cb]) ? 16 * cb + n16 : 0;
+      d.kO[cb].load(kc + rs * KI2::RB, q4);
+      d.skr[cb] = ld_nt<u4_t>(ks + rs * 4);
+      d.zkr[cb] = ld_nt<unsigned>(kz + rs * 4);
     }
-    float4 ksc[4][2];
+  };
+  KSide kd;
+  if (g0 + wave < g1) load_k(g0 + wave, kd);
+  for (int grp = g0 + wave; grp < g1; grp += kNW) {
+    const long long gb = bh * Q + grp;
+    const uint8_t* vsig = P.v.codes + gb * kSigSlots * kD;
+    const float* vss = P.v.scale + gb * kD;
+    const TokView vo{P.v.codes2 + gb * kOthSlots * 32, P.v.scale2 + gb * kOthSlots * 4,
+                     P.v.zero2 + gb * kOthSlots * 4};
+    // ---- V-side loads of this group ----
+    u4_t svr[4];  // V scales of the score column's slot, 4 channel groups
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c0 = 32 * s + 8 * q4;
-      ksc[s][0] = *reinterpret_cast<const float4*>(kss + c0);
-      ksc[s][1] = *reinterpret_cast<const float4*>(kss + c0 + 4);
+    for (int cb = 0; cb < 4; ++cb) {
+      const int rs = (cb < 3 || okO[cb]) ? 16 * cb + n16 : 0;
+      svr[cb] = ld_nt<u4_t>(vo.scale + rs * 4);
     }
+    // significant V rows 8 q4 + k; rows past the count (all of them for
+    // q4 >= 2: the product's k-slots 16-31 carry zero weights) read row 0
     VI8<true> vS;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int r = 8 * q4 + k;
-      vS.w0[k] = vS.w1[k] = 0x80808080u;  // code 0
-      if (r < nsig) {
-        const u2_t x = ld_nt<u2_t>(vsig + r * kD + n16 * 8);
-        const unsigned x0 = x[0], x1 = x[1];
-        vS.w0[k] = x0 ^ 0x80808080u;
-        vS.w1[k] = x1 ^ 0x80808080u;
-      }
+      const u2_t x = ld_nt<u2_t>(vsig + (r < nsig ? r : 0) * kD + n16 * 8);
+      const unsigned x0 = x[0], x1 = x[1];
+      vS.w0[k] = x0 ^ 0x80808080u;
+      vS.w1[k] = x1 ^ 0x80808080u;
     }
-    float vsc[8];
+    const float2 vs2 = *reinterpret_cast<const float2*>(vss + 2 * lane);
+    // other V, both tiles: blocked rows (the lane's 8 column words of rows
+    // r0 .. r0 + 7 are one 16-byte run; rows 2p, 2p + 1 form word p; a run
+    // wholly past the count reads run 0, whose weights are 0) and the rows'
+    // zero-point bytes
+    VI2 vO[2];
+    u4_t zr[2][2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vsc[j] = vss[16 * j + n16];
-    // ---- significant K: scaled query (hi + lo) and its channel sum ----
-    u4_t qh[4], ql[4];
+    for (int tau = 0; tau < 2; ++tau) {
+      const int run = 4 * tau + q4;
+      const u4_t x = ld_nt<u4_t>(vo.codes + (((8 * run < noth) ? run : 0) * 16 + n16) * 16);
+#pragma unroll
+      for (int p2 = 0; p2 < 4; ++p2) vO[tau].x[p2] = x[p2];
+      zr[tau][0] = ld_nt<u4_t>(vo.zero + run * 32);
+      zr[tau][1] = ld_nt<u4_t>(vo.zero + run * 32 + 16);
+    }
+    // ---- significant K: the group's scaled query, built once per wave ----
+    // Entry (s, m, qe) of the wave's LDS table holds the A-operand pairs of
+    // query m, k-step s, lane group qe: channels c0 + v, c0 + v + 4 (v < 4,
+    // c0 = 32 s + 8 qe) times their channel scales, split into fp16 hi + lo.
+    // Each query's scaled sum sum_d q_d s_d is reduced over its entries.
+    auto& T = L.qtab[wave];
     float part = 0.0f;
+    {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c0 = 32 * s + 8 * q4;
-      const float sc[8] = {ksc[s][0].x, ksc[s][0].y, ksc[s][0].z, ksc[s][0].w,
-                           ksc[s][1].x, ksc[s][1].y, ksc[s][1].z, ksc[s][1].w};
+      for (int k = 0; k < PER; ++k) {
+        const int e = (lane + 64 * k) & (NE - 1);
+        {
+          const int sl = e / (4 * R), m = (e >> 2) % R, qe = e & 3;
+          const int c0 = 32 * sl + 8 * qe;
+          const float4 sa = kd.tsa[k], sb = kd.tsb[k];
+          const float sc[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+          u4_t hi4, lo4;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float a = L.q[mr][c0 + v] * sc[v], bq = L.q[mr][c0 + v + 4] * sc[v + 4];
-        unsigned hi, lo;
-        split_pair(a, bq, hi, lo);
-        qh[s][v] = aq < 0 ? 0u : hi;
-        ql[s][v] = aq < 0 ? 0u : lo;
-        part += a + bq;
+          for (int v = 0; v < 4; ++v) {
+            const float a = L.q[m][c0 + v] * sc[v], bq = L.q[m][c0 + v + 4] * sc[v + 4];
+            unsigned hi, lo;
+            split_pair(a, bq, hi, lo);
+            hi4[v] = hi;
+            lo4[v] = lo;
+            part += a + bq;
+          }
+          T.e[0][sl][m][qe] = hi4;
+          T.e[1][sl][m][qe] = lo4;
+        }
+      }
+      // the entries of query m differ in qe (bits 0-1) and, for R <= 4, in the
+      // k-step (the bits above the query's); its sum ends in lane 4 m (lane 0
+      // when R == 1)
+      part += __shfl_xor(part, 1, 64);
+      part += __shfl_xor(part, 2, 64);
+      if constexpr (R == 1) {
+        part += __shfl_xor(part, 4, 64);
+        part += __shfl_xor(part, 8, 64);
+      } else if constexpr (R == 4) {
+        part += __shfl_xor(part, 16, 64);
+        part += __shfl_xor(part, 32, 64);
       }
     }
-    // lanes of one A row differ in q4: their sum covers the row's 128 channels
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
     float qs[GI];
 #pragma unroll
-    for (int i = 0; i < GI; ++i) qs[i] = __shfl(part, arow_of_query<QR>(QRW::slot_query(q4, i)), 64);
+    for (int i = 0; i < GI; ++i) qs[i] = __shfl(part, R == 1 ? 0 : 4 * QRW::slot_query(q4, i), 64);
+    *reinterpret_cast<float2*>(&vscl[wave][2 * lane]) = vs2;
+    wave_lds_sync();
     f4_t c = zero4;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const u4_t kb = kS.slice(s);
-      c = mfma(qh[s], kb, c);
-      c = mfma(ql[s], kb, c);
+      const u4_t kb = kd.kS.slice(s);
+      u4_t qh = T.e[0][s][mr][q4], ql = T.e[1][s][mr][q4];
+      if (aq < 0) qh = ql = u4_t{0u, 0u, 0u, 0u};
+      c = mfma(qh, kb, c);
+      c = mfma(ql, kb, c);
     }
     float rawS[GI], mu[GI];
 #pragma unroll
@@ -151,18 +227,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     float rawO[4][GI];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      f4_t cc[4];
+      if constexpr (QR == 1) {
+        f4_t cc = zero4;  // element g: group g's sum (see the prologue)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) cc[g] = mfma(qop[g], kO[cb].slice(g), zero4);
+        for (int g = 0; g < 4; ++g) cc = mfma(qop[g], kd.kO[cb].slice(g), cc);
+        float a = mu[0];
 #pragma unroll
-      for (int i = 0; i < GI; ++i) {
-        const int m = min(QRW::slot_query(q4, i), R - 1);
-        const int e = QRW::slot_elem(i);
-        float a = mu[i];
+        for (int g = 0; g < 4; ++g) {
+          const unsigned sbits = kd.skr[cb][g];  // scalar copy before the bit cast
+          const float zf = (float)((kd.zkr[cb] >> (8 * g)) & 0xFFu);
+          a = fmaf(__builtin_bit_cast(float, sbits), fmaf(-(zf + (float)KI2::OFF), L.qg[0][g], cc[g]), a);
+        }
+        rawO[cb][0] = a;
+      } else {
+        f4_t cc[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          a = fmaf(sk[cb][g], fmaf(-(zk[cb][g] + (float)KI2::OFF), L.qg[m][g], cc[g][e]), a);
-        rawO[cb][i] = a;
+        for (int g = 0; g < 4; ++g) cc[g] = mfma(qop[g], kd.kO[cb].slice(g), zero4);
+#pragma unroll
+        for (int i = 0; i < GI; ++i) {
+          const int m = min(QRW::slot_query(q4, i), R - 1);
+          const int e = QRW::slot_elem(i);
+          float a = mu[i];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const unsigned sbits = kd.skr[cb][g];
+            const float zf = (float)((kd.zkr[cb] >> (8 * g)) & 0xFFu);
+            a = fmaf(__builtin_bit_cast(float, sbits), fmaf(-(zf + (float)KI2::OFF), L.qg[m][g], cc[g][e]), a);
+          }
+          rawO[cb][i] = a;
+        }
       }
     }
     // ---- online softmax (base 2), one update for the group ----
@@ -232,10 +325,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
         f4_t t = mfma(wh, bb, zero4);
         t = mfma(wl, bb, t);
-        st.o[j] += vsc[j] * t;
+        st.o[j] += vscl[wave][16 * j + n16] * t;
       }
     }
     wave_lds_sync();
+    // ---- K-side loads of this wave's next group (its last group reloads
+    // itself: lines still in cache, and no branch) ----
+    load_k(grp + kNW < g1 ? grp + kNW : grp, kd);
     // ---- other V: two tiles of 32 slots ----
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
@@ -246,7 +342,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           unsigned hi, lo;
-          split_pair(pO[2 * tau][i] * sv[2 * tau][g], pO[2 * tau + 1][i] * sv[2 * tau + 1][g], hi, lo);
+          const unsigned s0 = svr[2 * tau][g], s1 = svr[2 * tau + 1][g];
+          split_pair(pO[2 * tau][i] * __builtin_bit_cast(float, s0),
+                     pO[2 * tau + 1][i] * __builtin_bit_cast(float, s1), hi, lo);
           if (wr) {
             W.w[g][0][m][n16] = (unsigned short)(hi & 0xFFFFu);
             W.w[g][0][m][16 + n16] = (unsigned short)(hi >> 16);
@@ -255,40 +353,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           }
         }
       }
-      VI2 vO;
+      // -(1024 + z) pairs of rows (2p, 2p + 1) per V group, from the bytes
+      // loaded above (row r's 4 group bytes at 4 r)
+      u4_t zsub[4];
       {
-        unsigned rr[8];
+        unsigned zw[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int r = 32 * tau + 8 * q4 + k;
-          rr[k] = 0u;
-          if (r < noth) rr[k] = ld_nt<uint16_t>(vo.codes + r * VI2::RB + n16 * 2);
+        for (int e = 0; e < 4; ++e) {
+          zw[e] = zr[tau][0][e];
+          zw[4 + e] = zr[tau][1][e];
         }
 #pragma unroll
-        for (int p2 = 0; p2 < 4; ++p2) vO.x[p2] = perm(rr[2 * p2 + 1], rr[2 * p2], 0x05040100u);
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int p2 = 0; p2 < 4; ++p2) {
+            const int ia = 8 * p2 + g, ib = 8 * p2 + 4 + g;  // bytes of rows 2p, 2p + 1
+            const unsigned sel = (0x0Cu << 24) | ((4u + (ib & 3)) << 16) | (0x0Cu << 8) | (unsigned)(ia & 3);
+            const unsigned x = perm(zw[ib >> 2], zw[ia >> 2], sel);
+            zsub[g][p2] = and_or(x, VI2::ZMASK[0], VI2::ZMAGIC);
+          }
       }
-      u4_t zsub[2][4];
-      load_zsub<VI2, 4>(vo, 32 * tau + 8 * q4, zsub);
       wave_lds_sync();
-      u4_t wa[4][2];
+      // column blocks 2g, 2g + 1 use the weights of V group g
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g) {
+        u4_t wh = *reinterpret_cast<const u4_t*>(&W.w[g][0][mr][8 * q4]);
+        u4_t wl = *reinterpret_cast<const u4_t*>(&W.w[g][1][mr][8 * q4]);
+        if (aq < 0) wh = wl = u4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          wa[g][h] = *reinterpret_cast<const u4_t*>(&W.w[g][h][mr][8 * q4]);
-          if (aq < 0) wa[g][h] = u4_t{0u, 0u, 0u, 0u};
+        for (int j = 2 * g; j < 2 * g + 2; ++j) {
+          u4_t bb = vO[tau].block(j);
+#pragma unroll
+          for (int p2 = 0; p2 < 4; ++p2) {
+            const unsigned bv = bb[p2], zv = zsub[g][p2];
+            const h2_t x = __builtin_bit_cast(h2_t, bv) + __builtin_bit_cast(h2_t, zv);
+            bb[p2] = __builtin_bit_cast(unsigned, x);
+          }
+          st.o[j] = mfma(wh, bb, st.o[j]);
+          st.o[j] = mfma(wl, bb, st.o[j]);
         }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        u4_t bb = vO.block(j);
-#pragma unroll
-        for (int p2 = 0; p2 < 4; ++p2) {
-          const unsigned bv = bb[p2], zv = zsub[0][j >> 1][p2];
-          const h2_t x = __builtin_bit_cast(h2_t, bv) + __builtin_bit_cast(h2_t, zv);
-          bb[p2] = __builtin_bit_cast(unsigned, x);
-        }
-        st.o[j] = mfma(wa[j >> 1][0], bb, st.o[j]);
-        st.o[j] = mfma(wa[j >> 1][1], bb, st.o[j]);
       }
       wave_lds_sync();
     }

@@ -880,8 +880,21 @@ __global__ __launch_bounds__(256) void k_quant_dsq(const uint16_t* __restrict__ 
         }
         quant8<2, false, 32>(v, 0xFFu, plo, phi, s, z);
       }
-      if (tsr) store_row_codes<2, true>(t.codes2 + dst * 32, li, plo, phi, lrow);
-      else store_row_codes<2, false>(t.codes2 + dst * 32, li, plo, phi, lrow);
+      if (tsr) {
+        // V: column word li of slot `slot` in the blocked order (the 8 words
+        // of rows 8i .. 8i + 7 of one column are contiguous)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) lrow[8 * li + v] = (uint16_t)code_at<2>(plo, phi, v);
+        wave_lds_sync();
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w |= (uint32_t)lrow[li + 16 * j] << (2 * j);
+        wave_lds_sync();
+        st_nt<uint16_t>(t.codes2 + gb * (kDsqOthSlots * 32) + (((slot >> 3) * 16 + li) * 16 + (slot & 7) * 2),
+                        (uint16_t)w);
+      } else {
+        store_row_codes<2, false>(t.codes2 + dst * 32, li, plo, phi, lrow);
+      }
       if ((li & 3) == 0) {
         t.scale2[dst * 4 + (li >> 2)] = s;
         t.zero2[dst * 4 + (li >> 2)] = (uint8_t)z;

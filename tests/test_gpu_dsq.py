@@ -49,7 +49,9 @@ def _device_groups(cache, B, H, Q, n_sig):
         "vsig": unpack_layout(u8("v.codes", (B, H, Q, 16, 128)), 8, "V", signed=True),
         "kscale": f32("k.scale", (B, H, Q, 128)), "vscale": f32("v.scale", (B, H, Q, 128)),
         "kc2": unpack_layout(u8("k.codes2", (B, H, Q, 64, 32)), 2, "K"),
-        "vc2": unpack_layout(u8("v.codes2", (B, H, Q, 64, 32)), 2, "V"),
+        # V rows are blocked: the column words of rows 8i .. 8i + 7 are contiguous
+        "vc2": unpack_layout(u8("v.codes2", (B, H, Q, 8, 16, 8, 2)).transpose(0, 1, 2, 3, 5, 4, 6)
+                             .reshape(B, H, Q, 64, 32), 2, "V"),
         "ks2": f32("k.scale2", (B, H, Q, 64, 4)), "vs2": f32("v.scale2", (B, H, Q, 64, 4)),
         "kz2": u8("k.zero2", (B, H, Q, 64, 4)), "vz2": u8("v.zero2", (B, H, Q, 64, 4)),
     }
