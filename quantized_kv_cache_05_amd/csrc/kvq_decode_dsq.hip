@@ -65,6 +65,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   auto& W = L.u.wave[wave];
   SoftState<GI> st;
   soft_init(st);
+  // other-V zero-point bias of the lane's token columns, per softmax slot and
+  // V group: sum of w (4 + z), in the running softmax frame (see below)
+  float vb[GI][4];
+#pragma unroll
+  for (int i = 0; i < GI; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) vb[i][g] = 0.0f;
   const long long bh = (long long)b * P.H + kvh;
   const long long Q = P.S / 64;
   const f4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -127,11 +134,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const TokView vo{P.v.codes2 + gb * kOthSlots * 32, P.v.scale2 + gb * kOthSlots * 4,
                      P.v.zero2 + gb * kOthSlots * 4};
     // ---- V-side loads of this group ----
-    u4_t svr[4];  // V scales of the score column's slot, 4 channel groups
+    u4_t svr[4];       // V scales of the score column's slot, 4 channel groups
+    unsigned zvr[4];   // and its 4 zero-point bytes
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int rs = (cb < 3 || okO[cb]) ? 16 * cb + n16 : 0;
       svr[cb] = ld_nt<u4_t>(vo.scale + rs * 4);
+      zvr[cb] = ld_nt<unsigned>(vo.zero + rs * 4);
     }
     // significant V rows 8 q4 + k; rows past the count (all of them for
     // q4 >= 2: the product's k-slots 16-31 carry zero weights) read row 0
@@ -147,18 +156,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const float2 vs2 = *reinterpret_cast<const float2*>(vss + 2 * lane);
     // other V, both tiles: blocked rows (the lane's 8 column words of rows
     // r0 .. r0 + 7 are one 16-byte run; rows 2p, 2p + 1 form word p; a run
-    // wholly past the count reads run 0, whose weights are 0) and the rows'
-    // zero-point bytes
-    VI2 vO[2];
-    u4_t zr[2][2];
+    // wholly past the count reads run 0, whose weights are 0)
+    u4_t vO[2];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const int run = 4 * tau + q4;
-      const u4_t x = ld_nt<u4_t>(vo.codes + (((8 * run < noth) ? run : 0) * 16 + n16) * 16);
-#pragma unroll
-      for (int p2 = 0; p2 < 4; ++p2) vO[tau].x[p2] = x[p2];
-      zr[tau][0] = ld_nt<u4_t>(vo.zero + run * 32);
-      zr[tau][1] = ld_nt<u4_t>(vo.zero + run * 32 + 16);
+      vO[tau] = ld_nt<u4_t>(vo.codes + (((8 * run < noth) ? run : 0) * 16 + n16) * 16);
     }
     // ---- significant K: the group's scaled query, built once per wave ----
     // Entry (s, m, qe) of the wave's LDS table holds the A-operand pairs of
@@ -292,6 +295,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         st.l[i] *= alpha[i];
 #pragma unroll
         for (int j = 0; j < 8; ++j) st.o[j][QRW::slot_elem(i)] *= alpha[i];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) vb[i][g] *= alpha[i];
       }
     }
 #pragma unroll
@@ -343,8 +348,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         for (int g = 0; g < 4; ++g) {
           unsigned hi, lo;
           const unsigned s0 = svr[2 * tau][g], s1 = svr[2 * tau + 1][g];
-          split_pair(pO[2 * tau][i] * __builtin_bit_cast(float, s0),
-                     pO[2 * tau + 1][i] * __builtin_bit_cast(float, s1), hi, lo);
+          const float w0 = pO[2 * tau][i] * __builtin_bit_cast(float, s0);
+          const float w1 = pO[2 * tau + 1][i] * __builtin_bit_cast(float, s1);
+          const float z0 = (float)((zvr[2 * tau] >> (8 * g)) & 0xFFu);
+          const float z1 = (float)((zvr[2 * tau + 1] >> (8 * g)) & 0xFFu);
+          vb[i][g] = fmaf(w0, z0 + (float)KI2::OFF, fmaf(w1, z1 + (float)KI2::OFF, vb[i][g]));
+          split_pair(w0, w1, hi, lo);
           if (wr) {
             W.w[g][0][m][n16] = (unsigned short)(hi & 0xFFFFu);
             W.w[g][0][m][16 + n16] = (unsigned short)(hi >> 16);
@@ -352,26 +361,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             W.w[g][1][m][16 + n16] = (unsigned short)(lo >> 16);
           }
         }
-      }
-      // -(1024 + z) pairs of rows (2p, 2p + 1) per V group, from the bytes
-      // loaded above (row r's 4 group bytes at 4 r)
-      u4_t zsub[4];
-      {
-        unsigned zw[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          zw[e] = zr[tau][0][e];
-          zw[4 + e] = zr[tau][1][e];
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int p2 = 0; p2 < 4; ++p2) {
-            const int ia = 8 * p2 + g, ib = 8 * p2 + 4 + g;  // bytes of rows 2p, 2p + 1
-            const unsigned sel = (0x0Cu << 24) | ((4u + (ib & 3)) << 16) | (0x0Cu << 8) | (unsigned)(ia & 3);
-            const unsigned x = perm(zw[ib >> 2], zw[ia >> 2], sel);
-            zsub[g][p2] = and_or(x, VI2::ZMASK[0], VI2::ZMAGIC);
-          }
       }
       wave_lds_sync();
       // column blocks 2g, 2g + 1 use the weights of V group g
@@ -382,12 +371,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         if (aq < 0) wh = wl = u4_t{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 2 * g; j < 2 * g + 2; ++j) {
-          u4_t bb = vO[tau].block(j);
+          // 4 + code as fp16 (codes of block j at bits 2j of each half,
+          // moved to mantissa bits 8-9 under the exponent of 4)
+          u4_t bb;
 #pragma unroll
           for (int p2 = 0; p2 < 4; ++p2) {
-            const unsigned bv = bb[p2], zv = zsub[g][p2];
-            const h2_t x = __builtin_bit_cast(h2_t, bv) + __builtin_bit_cast(h2_t, zv);
-            bb[p2] = __builtin_bit_cast(unsigned, x);
+            const unsigned x = vO[tau][p2];
+            const unsigned y = j < 4 ? (x << (8 - 2 * j)) : (x >> (2 * j - 8));
+            bb[p2] = and_or(y, 0x03000300u, 0x44004400u);
           }
           st.o[j] = mfma(wh, bb, st.o[j]);
           st.o[j] = mfma(wl, bb, st.o[j]);
@@ -396,6 +387,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       wave_lds_sync();
     }
   }
+  // other V entered the products as 4 + c: subtract each query's
+  // sum of w (4 + z) over its token columns (16 lanes of a row group), per
+  // V group (column blocks 2g, 2g + 1)
+#pragma unroll
+  for (int i = 0; i < GI; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float t = sum16(vb[i][g]);
+      st.o[2 * g][QRW::slot_elem(i)] -= t;
+      st.o[2 * g + 1][QRW::slot_elem(i)] -= t;
+    }
   wave_record<QR, 4>(L, st, wave, nq);
   finish_split(P, L, b, kvh, qt, split, nq);
 }
