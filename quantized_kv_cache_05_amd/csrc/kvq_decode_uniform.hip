@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kUniformWav
 void k_attn_uniform(AttnParams P) {
   __shared__ AttnLds<QR, NGV, CHANK> L;
   const int split = blockIdx.x, qt = blockIdx.y % P.qtiles, kvh = blockIdx.y / P.qtiles, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar addressing
   const int nq = min(QR, P.G - qt * QR);
   u4_t qop[4];
   attn_prologue<QR, NGK>(P, L, b, kvh, qt, nq, qop);
