@@ -153,33 +153,47 @@ bool decode_uniform_supported(const TensorArgs& k, const TensorArgs& v) {
   return false;
 }
 
-// Log-sum-exp merge of split partials: one workgroup of 128 threads per
+// Log-sum-exp merge of split partials: one workgroup of 1024 threads per
 // (b, query head): M = max m_j, L = sum l_j 2^(m_j - M), out = sum 2^(m_j - M) o_j / L.
-// Split weights are formed cooperatively in LDS, chunk by chunk, so each
-// thread's loads of its output channel are independent of one another.
-__global__ __launch_bounds__(128) void k_merge(const float* __restrict__ ws, int NS,
-                                              float* __restrict__ out) {
-  constexpr int CH = 512;  // splits per LDS chunk
+// Split weights are formed cooperatively in LDS, a chunk of splits at a time;
+// thread t owns output channel t mod 128 and the splits j = t / 128 (mod 8) of
+// the chunk, so each channel has eight threads with independent loads in
+// flight (a merge of 128 splits takes two rounds of loads per thread).
+constexpr int kMergeThreads = 1024;
+
+__device__ __forceinline__ float merge_block_reduce(float v, bool is_max, float* red) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const float o = __shfl_xor(v, m, 64);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < kMergeThreads / 64; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+  return r;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void k_merge(const float* __restrict__ ws, int NS,
+                                                        float* __restrict__ out) {
+  constexpr int NP = kMergeThreads / kD;  // threads per output channel
+  constexpr int CH = 2048;                // splits per LDS chunk
   __shared__ float wgt[CH];
-  __shared__ float red[128];
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ float po[NP][kD];
   const long long bq = blockIdx.x;
-  const int d = threadIdx.x;
+  const int t = threadIdx.x, d = t & (kD - 1), part = t / kD;
   const float* rec0 = ws + bq * NS * kPartStride;
   float M = -INFINITY;
-  for (int s = d; s < NS; s += 128) M = fmaxf(M, rec0[(long long)s * kPartStride]);
-  red[d] = M;
-  __syncthreads();
-  for (int w = 64; w > 0; w >>= 1) {
-    if (d < w) red[d] = fmaxf(red[d], red[d + w]);
-    __syncthreads();
-  }
-  M = red[0];
-  __syncthreads();
+  for (int s = t; s < NS; s += kMergeThreads) M = fmaxf(M, rec0[(long long)s * kPartStride]);
+  M = merge_block_reduce(M, true, red);
   float Lp = 0.0f, O = 0.0f;
   if (M != -INFINITY) {
     for (int c0 = 0; c0 < NS; c0 += CH) {
       const int n = min(CH, NS - c0);
-      for (int s = d; s < n; s += 128) {
+      for (int s = t; s < n; s += kMergeThreads) {
         const float* r = rec0 + (long long)(c0 + s) * kPartStride;
         const float ms = r[0];
         const float f = ms == -INFINITY ? 0.0f : fexp2(ms - M);
@@ -188,30 +202,32 @@ __global__ __launch_bounds__(128) void k_merge(const float* __restrict__ ws, int
       }
       __syncthreads();
       const float* r = rec0 + (long long)c0 * kPartStride + 4 + d;
-      int s = 0;
-      for (; s + 8 <= n; s += 8) {
+      int s = part;
+      for (; s + 7 * NP < n; s += 8 * NP) {
         float v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = r[(long long)(s + k) * kPartStride];
+        for (int k = 0; k < 8; ++k) v[k] = r[(long long)(s + k * NP) * kPartStride];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) O = fmaf(wgt[s + k], v[k], O);
+        for (int k = 0; k < 8; ++k) O = fmaf(wgt[s + k * NP], v[k], O);
       }
-      for (; s < n; ++s) O = fmaf(wgt[s], r[(long long)s * kPartStride], O);
+      for (; s < n; s += NP) O = fmaf(wgt[s], r[(long long)s * kPartStride], O);
       __syncthreads();
     }
   }
-  red[d] = Lp;
+  const float L = merge_block_reduce(Lp, false, red);
+  po[part][d] = O;
   __syncthreads();
-  for (int w = 64; w > 0; w >>= 1) {
-    if (d < w) red[d] += red[d + w];
-    __syncthreads();
+  if (t < kD) {
+    float o = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) o += po[p][t];
+    out[bq * kD + t] = L > 0.0f ? o / L : 0.0f;
   }
-  const float L = red[0];
-  out[bq * kD + d] = L > 0.0f ? O / L : 0.0f;
 }
 
 hipError_t launch_merge(const DecodeLaunch& d, int B, hipStream_t st) {
-  hipLaunchKernelGGL(k_merge, dim3((unsigned)(B * d.Hq)), dim3(kD), 0, st, d.ws, d.num_splits, d.out);
+  hipLaunchKernelGGL(k_merge, dim3((unsigned)(B * d.Hq)), dim3(kMergeThreads), 0, st, d.ws, d.num_splits,
+                     d.out);
   return hipGetLastError();
 }
 
