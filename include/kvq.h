@@ -152,6 +152,11 @@ enum {
  *                          base_d = fl(fl(sum_i fl(s_d * c_id)) / n), the mean
  *                          of its dequantized significant K rows summed in
  *                          slot order, so k_hat = base + (c - z) * s
+ *    codes16 [B][H][64][D] fp16 tail: the tokens of the group not yet
+ *                          complete, row t - 64 floor(t / 64) for token t, K
+ *                          rows in the K row layout and V rows in the V row
+ *                          layout of the CHUNK_MIXED FP16 pool
+ *    oscale (K only) [B][H][64] float: the scores of the tail's tokens
  *    dsq_mask (cache) [B][H][Q] uint64, bit t set when token t of the group
  *                          is significant
  *
@@ -300,24 +305,26 @@ kvq_status kvq_append_chunks(const kvq_cache* c, const void* k_new, const void* 
 
 /*
  * [KVO-LLM] §3.1 differential significant-token quantization of t_new new
- * tokens per sequence, in whole groups of 64 (DSQ mode only; layout and
- * arithmetic in the DSQ buffer description above).  In each group the
- * dsq_sig tokens with the largest scores are significant: scores are
- * ordered by their binary32 bit patterns as a total order (-0 below +0,
- * NaNs at the ends by sign), ties to the lower token index, so exactly
- * dsq_sig tokens are chosen.
+ * tokens per sequence (DSQ mode only; layout and arithmetic in the DSQ
+ * buffer description above), appended as a stream: pos[b] must be the
+ * sequence's current length.  Every 64-token group that is complete after
+ * the call is quantized (its tokens below pos[b] read from the tails); the
+ * new tokens of the group left incomplete are stored in the tails with
+ * their scores.  In each group the dsq_sig tokens with the largest scores
+ * are significant: scores are ordered by their binary32 bit patterns as a
+ * total order (-0 below +0, NaNs at the ends by sign), ties to the lower
+ * token index, so exactly dsq_sig tokens are chosen.
  *  k_new, v_new: device fp16 [batch][kv_heads][t_new][128].
  *  score:        device float [batch][kv_heads][t_new], the per-token
  *                attention statistic of the page (e.g. attention mass over a
  *                recent window), 4-byte aligned.
- *  t_new:        a multiple of 64 (else INVALID_ARG).
- *  pos:          device int32 [batch]; the tokens go to positions pos[b] ..
- *                pos[b] + t_new - 1, pos[b] a multiple of 64; a sequence
- *                whose pos[b] is negative, not a multiple of 64 or past
- *                max_seq - t_new is skipped and sets KVQ_FLAG_POS_RANGE.
- * Decode (kvq_decode_attn) attends the complete groups of seq_len[b]; a
- * seq_len[b] that is not a multiple of 64 attends floor(seq_len[b] / 64)
- * groups and sets KVQ_FLAG_LEN_RANGE.
+ *  t_new:        >= 0 (0: nothing is enqueued).
+ *  pos:          device int32 [batch]; a sequence whose pos[b] is negative
+ *                or past max_seq - t_new is skipped and sets
+ *                KVQ_FLAG_POS_RANGE.
+ * Decode (kvq_decode_attn) attends the complete groups below seq_len[b] and
+ * reads the tokens from 64 floor(seq_len[b] / 64) on from the tails, so
+ * seq_len[b] is the appended length or a multiple of 64 not above it.
  */
 kvq_status kvq_dsq_append(const kvq_cache* c, const void* k_new, const void* v_new, const float* score,
                           int32_t t_new, const int32_t* pos, void* stream);

@@ -138,6 +138,9 @@ kvq_tensor_bytes tensor_bytes(const kvq_cache* c, const kvq_tensor& t, bool is_k
       r.codes2 = B * H * Q * 64 * D / 4;
       r.scale2 = B * H * Q * 64 * (D / 32) * 4;
       r.zero2 = B * H * Q * 64 * (D / 32);
+      // the group being appended: fp16 rows, and (K) the tokens' scores
+      r.codes16 = B * H * 64 * D * 2;
+      if (is_k) r.oscale = B * H * 64 * 4;
       break;
     }
   }
@@ -366,7 +369,7 @@ kvq_status kvq_dsq_append(const kvq_cache* c, const void* k_new, const void* v_n
   kvq_status s = check_config(c);
   if (s != KVQ_OK) return s;
   if (c->mode != KVQ_MODE_DSQ) return KVQ_ERR_INVALID_ARG;
-  if (t_new < 0 || t_new % 64) return KVQ_ERR_INVALID_ARG;
+  if (t_new < 0) return KVQ_ERR_INVALID_ARG;
   if (t_new > c->max_seq) return KVQ_ERR_CAPACITY;
   if (t_new == 0) return KVQ_OK;
   if ((long long)c->batch * c->kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;

@@ -55,7 +55,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
   const bool reporter = split == 0 && blockIdx.y == 0 && threadIdx.x == 0;
   const int len = clamp_seq_len(P, b, reporter);
-  if ((len & 63) && reporter) set_flag(P.status, kFlagLenRange);
   const int g0 = (split * P.split_len) >> 6;  // split_len is a multiple of 64
   const int g1 = min(len >> 6, g0 + (P.split_len >> 6));
   const int nsig = P.dsq_sig, noth = kOthSlots - nsig;
@@ -398,6 +397,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       st.o[2 * g][QRW::slot_elem(i)] -= t;
       st.o[2 * g + 1][QRW::slot_elem(i)] -= t;
     }
+  // tokens of the group not yet complete (streaming appends) wait as fp16
+  // rows in the tails; the split holding token 64 floor(len / 64) attends
+  // them (splits are 64-token aligned), with the plain fp16 codecs
+  {
+    const int lq = len & ~63;
+    const int t0 = split * P.split_len, t1 = min(len, t0 + P.split_len);
+    if (max(t0, lq) < t1) {
+      const TokView kt{P.k.codes16 + (bh * 64 - lq) * KF16::RB, nullptr, nullptr};  // row t: tail row t - lq
+      const TokView vt{P.v.codes16 + (bh * 64 - lq) * VF16::RB, nullptr, nullptr};
+      const ChanView nc{nullptr, nullptr};
+      u4_t qop16[4];  // the plain query operand (qop was specialised above)
+      build_qop<QR>(L, qop16);
+      attend_wave<QR, 1, 1, KF16, VF16, false, false, 1>(P, L, st, kt, vt, nc, nullptr, 0, nq, max(t0, lq), t1,
+                                                         wave, qop16);
+    }
+  }
   wave_record<QR, 4>(L, st, wave, nq);
   finish_split(P, L, b, kvh, qt, split, nq);
 }

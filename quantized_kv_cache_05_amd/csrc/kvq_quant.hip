@@ -768,7 +768,15 @@ __global__ __launch_bounds__(256) void k_quant_oaken_one(const uint16_t* __restr
 // INT8 with per-channel scales over the significant tokens; the other
 // tokens become INT2 rows in groups of 32 channels, V directly and K as the
 // difference from the base row, the mean of the dequantized significant K
-// rows.  Class slots follow token order.  One workgroup per (group, b h).
+// rows.  Class slots follow token order.
+//
+// Appends are a stream: the tokens of the group not yet complete wait in
+// per-(b, h) fp16 tails (K rows in the K word order, V rows in the V word
+// order of the fp16 pool layout) with their scores; k_quant_dsq takes one
+// workgroup per group an append completes and gathers its 64 rows, those
+// below pos from the tails and the rest from the input; k_dsq_tail (next on
+// the stream, so the tails are read before they are rewritten) stores the
+// new tokens of the group left incomplete.
 
 // Scores ordered by bit pattern: a total order (-0 below +0, NaNs at the ends)
 __device__ __forceinline__ unsigned dsq_key(float x) {
@@ -779,12 +787,26 @@ __device__ __forceinline__ unsigned dsq_key(float x) {
 constexpr int kDsqSigSlots = 16;  // significant-row slots per group
 constexpr int kDsqOthSlots = 64;  // other-row slots per group
 
+// 8 channels 8 li .. 8 li + 7 of an fp16 V-layout row (word n holds
+// channels n + 16 j), in channel order (inverse of store_row_f16's V order).
+__device__ __forceinline__ uint4 ld_row8_v16(const uint8_t* row, int li) {
+  const uint16_t* h = reinterpret_cast<const uint16_t*>(row);
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c0 = 8 * li + 2 * k, c1 = c0 + 1;
+    w[k] = (uint32_t)h[(c0 & 15) * 8 + (c0 >> 4)] | ((uint32_t)h[(c1 & 15) * 8 + (c1 >> 4)] << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 __global__ __launch_bounds__(256) void k_quant_dsq(const uint16_t* __restrict__ xk,
                                                    const uint16_t* __restrict__ xv,
                                                    const float* __restrict__ score, int t_new, int H, int S,
                                                    int n_sig, const int* __restrict__ pos, TensorArgs kt,
                                                    TensorArgs vt, unsigned long long* __restrict__ mask_out,
                                                    unsigned* __restrict__ status) {
+  __shared__ float gsc[64];  // the group's scores
   __shared__ int s_tok[kDsqSigSlots];
   __shared__ int o_tok[kDsqOthSlots];
   __shared__ int8_t sig[2][kDsqSigSlots][kD];
@@ -794,18 +816,25 @@ __global__ __launch_bounds__(256) void k_quant_dsq(const uint16_t* __restrict__ 
   const long long bh = blockIdx.y;
   const int b = (int)(bh / H);
   const int p = pos[b];
-  if (p < 0 || (p & 63) || p > S - t_new) {
+  if (p < 0 || p > S - t_new) {
     if (gi == 0 && threadIdx.x == 0) set_flag(status, kFlagPosRange);
     return;
   }
+  const int k0 = (p & ~63) + 64 * gi;  // first token of the group
+  if (k0 + 64 > p + t_new) return;     // still incomplete after this append
   const long long Q = S / 64;
-  const long long gb = bh * Q + (p >> 6) + gi;      // destination group
-  const long long src = bh * t_new + (long long)gi * 64;  // first input row
+  const long long gb = bh * Q + (k0 >> 6);  // destination group
   const int n_oth = 64 - n_sig;
+  // the group's tokens below p are read from the tails, the others from the input
+  if (threadIdx.x < 64) {
+    const int tok = k0 + threadIdx.x;
+    gsc[threadIdx.x] = tok < p ? kt.oscale[bh * 64 + threadIdx.x] : score[bh * t_new + (tok - p)];
+  }
+  __syncthreads();
   // 1. significant tokens: rank of each token's score, ties to the lower index
   if (threadIdx.x < 64) {
     const int t = threadIdx.x;
-    const unsigned key = dsq_key(score[src + t]);
+    const unsigned key = dsq_key(gsc[t]);
     int rank = 0;
     for (int u = 0; u < 64; ++u) {
       const unsigned ku = (unsigned)__shfl((int)key, u, 64);
@@ -824,21 +853,28 @@ __global__ __launch_bounds__(256) void k_quant_dsq(const uint16_t* __restrict__ 
     // the base sum rounds each product and each sum (no fused multiply-add)
 #pragma clang fp contract(off)
     const int tsr = threadIdx.x >> 7, d = threadIdx.x & 127;
-    const uint16_t* x = (tsr ? xv : xk) + src * kD + d;
-    float xs[kDsqSigSlots];
+    const uint16_t* x = (tsr ? xv : xk) + (bh * t_new - p) * kD + d;  // token t at x[t * kD]
+    const uint16_t* tail = reinterpret_cast<const uint16_t*>((tsr ? vt : kt).codes16) + bh * 64 * kD;
+    // channel d's half within an fp16 tail row: K word order (slot 4 q + s,
+    // halves 0, 4, 1, 5, 2, 6, 3, 7) or V word order (word n, half j)
+    const int toff = tsr ? ((d & 15) * 8 + (d >> 4))
+                         : ((4 * ((d >> 3) & 3) + (d >> 5)) * 8 + (d & 3) * 2 + ((d >> 2) & 1));
+    float xv_[kDsqSigSlots];
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < kDsqSigSlots; ++i) {
-      const int tk = i < n_sig ? s_tok[i] : 0;
-      xs[i] = i < n_sig ? h2f(x[(long long)tk * kD]) : 0.0f;
-      amax = fmaxf(amax, fabsf(xs[i]));
+      const int tok = k0 + (i < n_sig ? s_tok[i] : 0);
+      // both addresses stay valid whichever side is taken (input row >= p, tail row < 64)
+      const uint16_t h = tok < p ? tail[(tok - k0) * kD + toff] : x[(long long)max(tok, p) * kD];
+      xv_[i] = i < n_sig ? h2f(h) : 0.0f;
+      amax = fmaxf(amax, fabsf(xv_[i]));
     }
     const float s = amax / 127.0f;
     float acc = 0.0f;  // K base: sum in slot order, one rounding per operation
 #pragma unroll
     for (int i = 0; i < kDsqSigSlots; ++i) {
       int q = 0;
-      if (i < n_sig && s != 0.0f) q = min(max((int)rintf(xs[i] / s), -128), 127);
+      if (i < n_sig && s != 0.0f) q = min(max((int)rintf(xv_[i] / s), -128), 127);
       sig[tsr][i][d] = (int8_t)q;
       if (i < n_sig) acc = acc + s * (float)q;
     }
@@ -873,7 +909,15 @@ __global__ __launch_bounds__(256) void k_quant_dsq(const uint16_t* __restrict__ 
       int z = 0;
       if (slot < n_oth) {
         float v[8];
-        unpack8(ld_row8((tsr ? xv : xk) + (src + o_tok[slot]) * kD + li * 8), v);
+        const int tok = k0 + o_tok[slot];
+        uint4 raw;
+        if (tok < p) {
+          const uint8_t* trow = (tsr ? vt : kt).codes16 + (bh * 64 + (tok - k0)) * 256;
+          raw = tsr ? ld_row8_v16(trow, li) : ld_row8_k16(trow, li);
+        } else {
+          raw = ld_row8((tsr ? xv : xk) + (bh * t_new + (tok - p)) * kD + li * 8);
+        }
+        unpack8(raw, v);
         if (tsr == 0) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = v[e] - base[li * 8 + e];  // difference from the base
@@ -899,6 +943,34 @@ __global__ __launch_bounds__(256) void k_quant_dsq(const uint16_t* __restrict__ 
         t.scale2[dst * 4 + (li >> 2)] = s;
         t.zero2[dst * 4 + (li >> 2)] = (uint8_t)z;
       }
+    }
+  }
+}
+
+// One workgroup per b h: the appended tokens of the group that stays
+// incomplete (tokens 64 floor(e / 64) .. e - 1, e = p + t_new, those at or
+// after p) go to the tails (K and V fp16 rows, scores).
+__global__ __launch_bounds__(256) void k_dsq_tail(const uint16_t* __restrict__ xk,
+                                                  const uint16_t* __restrict__ xv,
+                                                  const float* __restrict__ score, int t_new, int H, int S,
+                                                  const int* __restrict__ pos, TensorArgs kt, TensorArgs vt) {
+  __shared__ uint16_t lrows[16][kD];
+  const long long bh = blockIdx.x;
+  const int b = (int)(bh / H);
+  const int p = pos[b];
+  if (p < 0 || p > S - t_new) return;  // flagged by k_quant_dsq
+  const int e = p + t_new, k0 = e & ~63;
+  const int r0 = max(p, k0) - k0, r1 = e - k0;
+  const int li = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  // rows r0 .. r1 - 1 in passes of 16; every lane of a 16-lane row group
+  // takes the same branch, and the V exchange is wave-local
+  for (int rb = r0; rb < r1; rb += 16) {
+    const int r = rb + rg;
+    if (r < r1) {
+      const long long src = (bh * t_new + (k0 + r - p)) * kD + li * 8;
+      store_row_f16<false>(kt.codes16 + (bh * 64 + r) * 256, li, ld_row8(xk + src), nullptr);
+      store_row_f16<true>(vt.codes16 + (bh * 64 + r) * 256, li, ld_row8(xv + src), lrows[rg]);
+      if (li == 0) kt.oscale[bh * 64 + r] = score[bh * t_new + (k0 + r - p)];
     }
   }
 }
@@ -1114,9 +1186,14 @@ hipError_t launch_quant_oaken_one(const CacheArgs& c, const uint16_t* xk, const 
 
 hipError_t launch_quant_dsq(const CacheArgs& c, const uint16_t* xk, const uint16_t* xv, const float* score,
                             int t_new, const int* pos, hipStream_t st) {
-  const dim3 grid((unsigned)(t_new / 64), (unsigned)(c.B * c.H));
+  // groups an append of t_new tokens can complete: floor((p mod 64 + t_new) / 64) <= (t_new + 63) / 64
+  const dim3 grid((unsigned)((t_new + 63) / 64), (unsigned)(c.B * c.H));
   hipLaunchKernelGGL(k_quant_dsq, grid, dim3(kThreads), 0, st, xk, xv, score, t_new, c.H, c.S, c.dsq_sig, pos,
                      c.k, c.v, c.dsq_mask, c.status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_dsq_tail, dim3((unsigned)(c.B * c.H)), dim3(kThreads), 0, st, xk, xv, score, t_new, c.H,
+                     c.S, pos, c.k, c.v);
   return hipGetLastError();
 }
 

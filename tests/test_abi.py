@@ -313,7 +313,9 @@ def test_dsq_cache_bytes():
     for t in (b.k, b.v):
         assert (t.codes, t.scale) == (B * H * Q * 16 * 128, B * H * Q * 128 * 4)
         assert (t.codes2, t.scale2, t.zero2) == (B * H * Q * 64 * 32, B * H * Q * 64 * 4 * 4, B * H * Q * 64 * 4)
-        assert (t.zero, t.codes16, t.oscale) == (0, 0, 0)
+        assert t.zero == 0
+        assert t.codes16 == B * H * 64 * 128 * 2  # fp16 tail of the group being appended
+    assert (b.k.oscale, b.v.oscale) == (B * H * 64 * 4, 0)  # scores of the tail's tokens
     assert b.dsq_mask == B * H * Q * 8
     assert K.kvq_cache_bytes(make_desc()).dsq_mask == 0
 
@@ -343,8 +345,7 @@ def test_dsq_append_host_validation():
     c = _dsq_desc()
     _fake_buffers(c)
     p = 1 << 30
-    # whole groups only
-    assert status_of(K.kvq_dsq_append, c, p, p, p, 65, p, 0) == K.KVQ_ERR_INVALID_ARG
+    assert status_of(K.kvq_dsq_append, c, p, p, p, -1, p, 0) == K.KVQ_ERR_INVALID_ARG
     assert status_of(K.kvq_dsq_append, c, p, p, p, 320, p, 0) == K.KVQ_ERR_CAPACITY
     assert status_of(K.kvq_dsq_append, c, p, p, None, 64, p, 0) == K.KVQ_ERR_INVALID_ARG
     assert status_of(K.kvq_dsq_append, c, p, p, p + 2, 64, p, 0) == K.KVQ_ERR_ALIGNMENT

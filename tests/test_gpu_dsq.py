@@ -119,31 +119,110 @@ def test_dsq_append_and_decode(n_sig, G, num_splits):
 
 
 def test_dsq_flags():
-    """pos not a multiple of 64 skips the append (POS_RANGE); a seq_len that ends inside a group
-    attends the complete groups (LEN_RANGE)."""
+    """An append past the capacity is skipped and flagged (POS_RANGE); a seq_len above max_len is
+    clamped and flagged (LEN_RANGE)."""
     B, H, T, S = 1, 2, 192, 256
     w = _workload(B, H, 1, T)
     k, v, q, sc = w.kv(0), w.kv(1), w.q(), w.scores()
     cache = K.QuantKVCache(B, H, S, K.KVQ_MODE_DSQ, k_group=32, v_group=32, dsq_sig=13, zero_fill=True)
-    _append(cache, k, v, sc, 0, 64, [32])
+    _append(cache, k, v, sc, 0, 64, [S - 32])
     torch.cuda.synchronize()
     assert cache.flags() == K.KVQ_FLAG_POS_RANGE
     assert not host_bytes(cache.buf("dsq_mask")).any()
+    assert not host_bytes(cache.buf("k.codes16")).any()
     cache.status.zero_()
     _append(cache, k, v, sc, 0, T, [0])
     torch.cuda.synchronize()
     assert cache.flags() == 0
     out = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
     ws, nb = cache.workspace(H, T, 0)
-    K.kvq_decode_attn(cache.desc, to_device(q), H, i32_device([150]), T, SM, out, ws, nb, 0)
+    K.kvq_decode_attn(cache.desc, to_device(q), H, i32_device([T + 10]), T, SM, out, ws, nb, 0)
     torch.cuda.synchronize()
     assert cache.flags() == K.KVQ_FLAG_LEN_RANGE
     kh = np.zeros((H, T, 128), np.float32)
     vh = np.zeros((H, T, 128), np.float32)
     for h in range(H):
         kh[h], vh[h] = oracle.dsq_dequant(oracle.dsq_quant(k[0, h], v[0, h], sc[0, h]))
-    refo = oracle.attention(q[0], kh[:, :128], vh[:, :128], SM)
+    refo = oracle.attention(q[0], kh, vh, SM)
     assert float(rel_err_rows(out.cpu().numpy()[0], refo).max()) <= ATTN_TIGHT
+
+
+def _ref_rows(k, v, sc, b, h, L, n_sig):
+    """Oracle view of a stream of L tokens: complete groups quantized, the rest exact fp16."""
+    n = L & ~63
+    kh = np.zeros((L, 128), np.float32)
+    vh = np.zeros((L, 128), np.float32)
+    ref = None
+    if n:
+        ref = oracle.dsq_quant(k[b, h, :n], v[b, h, :n], sc[b, h, :n], n_sig=n_sig)
+        kh[:n], vh[:n] = oracle.dsq_dequant(ref)
+    kh[n:] = k[b, h, n:L].view(np.float16).astype(np.float32)
+    vh[n:] = v[b, h, n:L].view(np.float16).astype(np.float32)
+    return ref, kh, vh
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_dsq_streaming(G):
+    """Appends of 1 to 129 tokens continue the sequence: after each, the complete groups equal the
+    oracle's, the tails hold the waiting tokens and their scores, decode at the appended length and
+    at the group boundary below it meets the bar; the finished stream equals a bulk append."""
+    from kvq_harness import f16_layout
+    B, H, S = 2, 2, 512
+    sizes = [1, 5, 58, 64, 1, 70, 3, 129, 19, 33]
+    T = sum(sizes)
+    print("case dsq streaming G=%d T=%d" % (G, T), flush=True)
+    w = _workload(B, H, G, T)
+    k, v, q, sc = w.kv(0), w.kv(1), w.q(), w.scores()
+    cache = K.QuantKVCache(B, H, S, K.KVQ_MODE_DSQ, k_group=32, v_group=32, dsq_sig=13)
+    L = 0
+    worst = 0.0
+    for step, n in enumerate(sizes):
+        _append(cache, k, v, sc, L, L + n, [L] * B)
+        L += n
+        torch.cuda.synchronize()
+        assert cache.flags() == 0
+        dev = _device_groups(cache, B, H, S // 64, 13)
+        k16 = host_bytes(cache.buf("k.codes16")).view(np.uint16).reshape(B, H, 64, 128)
+        v16 = host_bytes(cache.buf("v.codes16")).view(np.uint16).reshape(B, H, 64, 128)
+        tsc = host_bytes(cache.buf("k.oscale")).view(np.float32).reshape(B, H, 64)
+        n0 = L & ~63
+        for b in range(B):
+            for h in range(H):
+                ref, _, _ = _ref_rows(k, v, sc, b, h, L, 13)
+                if ref is not None:
+                    _compare_groups(dev, ref, b, h, 0, n0 // 64, 13)
+                m = L - n0
+                assert np.array_equal(f16_layout(k16[b, h, :m], "K"), k[b, h, n0:L]), "K tail"
+                assert np.array_equal(f16_layout(v16[b, h, :m], "V"), v[b, h, n0:L]), "V tail"
+                assert np.array_equal(tsc[b, h, :m].view(np.uint32), sc[b, h, n0:L].view(np.uint32)), "scores"
+        for ln in sorted({L, n0} - {0}):
+            for ns in (0, 3):
+                out = torch.full((B, H * G, 128), float("nan"), dtype=torch.float32, device="cuda")
+                ws, nb = cache.workspace(H * G, ln, ns)
+                K.kvq_decode_attn(cache.desc, to_device(q), H * G, i32_device([ln] * B), ln, SM, out, ws, nb, ns)
+                torch.cuda.synchronize()
+                assert cache.flags() == 0
+                got = out.cpu().numpy()
+                for b in range(B):
+                    kh = np.zeros((H, ln, 128), np.float32)
+                    vh = np.zeros((H, ln, 128), np.float32)
+                    for h in range(H):
+                        _, kh[h], vh[h] = _ref_rows(k, v, sc, b, h, ln, 13)
+                    worst = max(worst, float(rel_err_rows(got[b], oracle.attention(q[b], kh, vh, SM)).max()))
+    print("dsq streaming max rel err %.3e" % worst, flush=True)
+    assert worst <= ATTN_BAR and worst <= ATTN_TIGHT
+    # the complete groups of the stream equal a bulk append of the same tokens
+    bulk = K.QuantKVCache(B, H, S, K.KVQ_MODE_DSQ, k_group=32, v_group=32, dsq_sig=13)
+    n0 = L & ~63
+    _append(bulk, k, v, sc, 0, n0, [0] * B)
+    torch.cuda.synchronize()
+    Q0 = n0 // 64
+    for name, per in (("k.codes", 2048), ("v.codes", 2048), ("k.scale", 512), ("v.scale", 512),
+                      ("k.codes2", 2048), ("v.codes2", 2048), ("k.scale2", 1024), ("v.scale2", 1024),
+                      ("k.zero2", 256), ("v.zero2", 256), ("dsq_mask", 8)):
+        a = host_bytes(cache.buf(name)).view(np.uint8).reshape(B, H, S // 64, per)[:, :, :Q0]
+        c = host_bytes(bulk.buf(name)).view(np.uint8).reshape(B, H, S // 64, per)[:, :, :Q0]
+        assert np.array_equal(a, c), name
 
 
 def test_dsq_full_size_sampled():
