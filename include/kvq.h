@@ -205,11 +205,14 @@ typedef struct kvq_cache {
   int32_t* perm;        /* CHUNK_MIXED: [B][C] original chunk id at each slot */
   int32_t* seg;         /* CHUNK_MIXED: [B][4] {n_fp16, n_int4, n_int2, n_chunks} */
   uint32_t* status;     /* device word for KVQ_FLAG_* bits (required) */
-  /* Paged layout (UNIFORM mode with TOKEN-axis K and V only; page_tokens 0 =
-   * contiguous).  Every per-token buffer (codes, scale, zero) is then a pool
-   * of num_pages pages [num_pages][H][page_tokens][row], and token t of
-   * sequence b lives in page block_table[b][t / page_tokens], row
-   * t % page_tokens of its head.  Pages are owned by the caller, who may map
+  /* Paged layout (UNIFORM mode with TOKEN-axis K and V, and OAKEN;
+   * page_tokens 0 = contiguous).  Every per-token buffer (codes, scale, zero,
+   * and Oaken's oscale) is then a pool of num_pages pages
+   * [num_pages][H][page_tokens][row], and token t of sequence b lives in page
+   * block_table[b][t / page_tokens], row t % page_tokens of its head.  Oaken's
+   * sparse lists (rowptr, sparse) stay per (sequence, head) as without pages:
+   * a dense page table plus per-sequence sparse lists, after the dual
+   * dense / sparse page management of [Oaken] §3.2.3.  Pages are owned by the caller, who may map
    * any page to any (b, logical page); a page shared by two sequences is
    * written by both. */
   int32_t page_tokens;          /* 0, 64, 128 or 256; max_seq a multiple of it */

@@ -31,7 +31,9 @@ kvq_status check_config(const kvq_cache* c) {
   if (c->page_tokens != 0) {
     if (c->page_tokens != 64 && c->page_tokens != 128 && c->page_tokens != 256) return KVQ_ERR_INVALID_ARG;
     if (c->max_seq % c->page_tokens || c->num_pages < 1) return KVQ_ERR_INVALID_ARG;
-    if (c->mode != KVQ_MODE_UNIFORM || k.axis != KVQ_AXIS_TOKEN) return KVQ_ERR_UNSUPPORTED;
+    // uniform token-axis caches, and Oaken's dense body (its sparse lists stay per sequence)
+    if (!((c->mode == KVQ_MODE_UNIFORM && k.axis == KVQ_AXIS_TOKEN) || c->mode == KVQ_MODE_OAKEN))
+      return KVQ_ERR_UNSUPPORTED;
   }
   switch (c->mode) {
     case KVQ_MODE_UNIFORM: {
@@ -92,6 +94,7 @@ kvq_status check_config(const kvq_cache* c) {
 kvq_tensor_bytes tensor_bytes(const kvq_cache* c, const kvq_tensor& t, bool is_k) {
   kvq_tensor_bytes r{};
   size_t B = (size_t)c->batch, S = (size_t)c->max_seq;
+  const size_t B_seq = B, S_seq = S;  // per-sequence buffers keep these when paged
   const size_t H = (size_t)c->kv_heads, D = KVQ_HEAD_DIM;
   if (c->page_tokens) {  // pools of pages: (B, S) rows become (num_pages, page_tokens)
     B = (size_t)c->num_pages;
@@ -115,8 +118,9 @@ kvq_tensor_bytes tensor_bytes(const kvq_cache* c, const kvq_tensor& t, bool is_k
       r.scale = B * H * S * ng * 4;
       r.zero = B * H * S * ng;
       r.oscale = B * H * S * ng * 4;
-      r.rowptr = B * H * (S + 1) * 4;
-      r.sparse = B * H * (size_t)t.sparse_cap * 2;
+      // the sparse lists are per (sequence, head) CSR, paged or not
+      r.rowptr = B_seq * H * (S_seq + 1) * 4;
+      r.sparse = B_seq * H * (size_t)t.sparse_cap * 2;
       break;
     case KVQ_MODE_CHUNK_MIXED:
       // 64 spare rows: decode tiles of 32 tokens over the waiting chunk of the

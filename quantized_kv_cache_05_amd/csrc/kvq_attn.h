@@ -406,13 +406,18 @@ struct ChanView {
   const uint8_t* zero;  // [S/64][128]
 };
 
-// Oaken sparse side list of one tensor for a (b, kv head).
+// Oaken sparse side list of one tensor for a (b, kv head).  The outer scales
+// are per token row of the dense body: contiguous rows of this (b, h), or,
+// paged, the pool base with token t in row
+// pages[t >> pshift] * prow + hrow + (t mod 2^pshift).
 struct SparseView {
   const float* oscale;    // [rows][ng]
   const uint32_t* rowptr; // [S + 1]
   const uint16_t* sparse; // [cap]
   unsigned cap;
   float t_lo, t_hi;
+  const int* pages = nullptr;  // paged: this sequence's block-table row
+  int pshift = 0, hrow = 0, prow = 0, npages = 0;
 };
 
 // Running softmax state of a wave (lane-held, see the header comment).

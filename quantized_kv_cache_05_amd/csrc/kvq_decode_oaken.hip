@@ -39,9 +39,17 @@ __device__ __forceinline__ void stage_rowptr(const SparseView& sv, int t0, int n
   __syncthreads();
 }
 
-// The outer scales of one row (one per channel group).
+// The outer scales of token t's row (one per channel group); paged rows go
+// through the block table (an entry outside the pool reads page 0, as the
+// dense body does, which flags it).
 template <int NG>
-__device__ __forceinline__ void row_oscale(const SparseView& sv, long long row, float (&so)[NG]) {
+__device__ __forceinline__ void row_oscale(const SparseView& sv, long long t, float (&so)[NG]) {
+  long long row = t;
+  if (sv.pages) {
+    int pg = sv.pages[t >> sv.pshift];
+    if (pg < 0 || pg >= sv.npages) pg = 0;
+    row = (long long)pg * sv.prow + sv.hrow + (t & ((1 << sv.pshift) - 1));
+  }
   if constexpr (NG == 1) {
     so[0] = sv.oscale[row];
   } else if constexpr (NG == 2) {
@@ -126,7 +134,7 @@ __device__ __forceinline__ void for_row_entries(const SparseView& sv, int t0, in
   }
 }
 
-template <int QR, int NG>
+template <int QR, int NG, bool PAGED>
 __global__ __launch_bounds__(256, 2) void k_attn_oaken(AttnParams P) {
   __shared__ AttnLds<QR, NG> L;
   __shared__ OakLds OL;
@@ -144,7 +152,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_oaken(AttnParams P) {
   const int n = t1 - t0;  // <= span (split planning)
   const long long bh = (long long)b * P.H + kvh;
   const long long S = P.S;
-  const SparseView ks = make_sparse(P.k, bh, S, NG), vs = make_sparse(P.v, bh, S, NG);
+  SparseView ks = make_sparse(P.k, bh, S, NG), vs = make_sparse(P.v, bh, S, NG);
+  if constexpr (PAGED) {  // outer scales sit with the dense rows, in pages
+    for (SparseView* sv : {&ks, &vs}) {
+      sv->oscale = (sv == &ks ? P.k : P.v).oscale;
+      sv->pages = P.pages + (long long)b * (S >> P.pshift);
+      sv->pshift = P.pshift;
+      sv->hrow = kvh << P.pshift;
+      sv->prow = P.H << P.pshift;
+      sv->npages = P.npages;
+    }
+  }
   SoftState<QRows<QR>::GI> st;
   soft_init(st);
   if (n > 0) {
@@ -170,11 +188,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_oaken(AttnParams P) {
           });
     }
     __syncthreads();
-    const TokView kv{P.k.codes + bh * S * KI4::RB, P.k.scale + bh * S * NG, P.k.zero + bh * S * NG};
-    const TokView vv{P.v.codes + bh * S * VI4::RB, P.v.scale + bh * S * NG, P.v.zero + bh * S * NG};
+    TokView kv{P.k.codes + bh * S * KI4::RB, P.k.scale + bh * S * NG, P.k.zero + bh * S * NG};
+    TokView vv{P.v.codes + bh * S * VI4::RB, P.v.scale + bh * S * NG, P.v.zero + bh * S * NG};
+    if constexpr (PAGED) {  // the dense body lives in pages: the views start at the pool bases
+      const int pshift = P.pshift;
+      kv = TokView{P.k.codes, P.k.scale, P.k.zero, P.pages + (long long)b * (S >> pshift), pshift, kvh << pshift,
+                   P.H << pshift, P.npages, P.status};
+      vv = TokView{P.v.codes, P.v.scale, P.v.zero, kv.pages, pshift, kv.hrow, kv.prow, P.npages, P.status};
+    }
     const ChanView nc{nullptr, nullptr};
-    attend_wave<QR, NG, NG, KI4, VI4, false, true, 2>(P, L, st, kv, vv, nc, OL.sc, span, nq, t0, t1,
-                                                       wave, qop);
+    attend_wave<QR, NG, NG, KI4, VI4, false, true, 2, PAGED>(P, L, st, kv, vv, nc, OL.sc, span, nq, t0, t1,
+                                                              wave, qop);
   }
   wave_record<QR, NG>(L, st, wave, nq);
   __syncthreads();
@@ -203,15 +227,20 @@ __global__ __launch_bounds__(256, 2) void k_attn_oaken(AttnParams P) {
   finish_split(P, L, b, kvh, qt, split, nq, [&](int m, int d, float) { return osp[m][d]; });
 }
 
-template <int QR>
-hipError_t go(const AttnParams& P, int ng, dim3 grid, hipStream_t st) {
+template <int QR, bool PAGED>
+hipError_t go_pg(const AttnParams& P, int ng, dim3 grid, hipStream_t st) {
   switch (ng) {
-    case 1: hipLaunchKernelGGL((k_attn_oaken<QR, 1>), grid, dim3(kNW * 64), 0, st, P); break;
-    case 2: hipLaunchKernelGGL((k_attn_oaken<QR, 2>), grid, dim3(kNW * 64), 0, st, P); break;
-    case 4: hipLaunchKernelGGL((k_attn_oaken<QR, 4>), grid, dim3(kNW * 64), 0, st, P); break;
+    case 1: hipLaunchKernelGGL((k_attn_oaken<QR, 1, PAGED>), grid, dim3(kNW * 64), 0, st, P); break;
+    case 2: hipLaunchKernelGGL((k_attn_oaken<QR, 2, PAGED>), grid, dim3(kNW * 64), 0, st, P); break;
+    case 4: hipLaunchKernelGGL((k_attn_oaken<QR, 4, PAGED>), grid, dim3(kNW * 64), 0, st, P); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int QR>
+hipError_t go(const AttnParams& P, int ng, dim3 grid, hipStream_t st) {
+  return P.pages ? go_pg<QR, true>(P, ng, grid, st) : go_pg<QR, false>(P, ng, grid, st);
 }
 
 }  // namespace

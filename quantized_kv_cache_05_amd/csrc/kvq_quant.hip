@@ -594,7 +594,7 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
     const uint16_t* __restrict__ x, int t_new, int H, int S, const int* __restrict__ pos,
     float t_lo, float t_hi, long long cap, uint8_t* __restrict__ codes, float* __restrict__ scale,
     uint8_t* __restrict__ zero, float* __restrict__ oscale, uint32_t* __restrict__ rowptr,
-    uint16_t* __restrict__ sparse, unsigned* __restrict__ status) {
+    uint16_t* __restrict__ sparse, unsigned* __restrict__ status, PageMap pm) {
   constexpr int NG = kD / GE, LG = GE / 8;
   __shared__ uint16_t lrows[VL ? 16 : 1][128];
   const long long bh = blockIdx.x;
@@ -649,12 +649,24 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
       tile_tot += (unsigned)row_cnt[i];
     }
     if (active) {
-      const long long dst = bh * S + p + t;
-      store_row_codes<4, VL>(codes + dst * 64, li, plo, phi, lrow);
-      if (li % LG == 0) {
-        scale[dst * NG + li / LG] = s;
-        zero[dst * NG + li / LG] = (uint8_t)z;
-        oscale[dst * NG + li / LG] = so;
+      // the dense row: contiguous, or in its page (a table entry outside the
+      // pool skips the row and flags; the sparse list is per sequence)
+      long long dst = bh * S + p + t;
+      bool dense_ok = true;
+      if (pm.pages) {
+        const int tok = p + t;
+        const int pg = pm.pages[(long long)b * (S / pm.ptok) + tok / pm.ptok];
+        dense_ok = pg >= 0 && pg < pm.npages;
+        if (!dense_ok && li == 0) set_flag(status, kFlagPageRange);
+        dst = ((long long)pg * H + bh % H) * pm.ptok + tok % pm.ptok;
+      }
+      if (dense_ok) {
+        store_row_codes<4, VL>(codes + dst * 64, li, plo, phi, lrow);
+        if (li % LG == 0) {
+          scale[dst * NG + li / LG] = s;
+          zero[dst * NG + li / LG] = (uint8_t)z;
+          oscale[dst * NG + li / LG] = so;
+        }
       }
       unsigned long long e = rb + (unsigned)(incl - lc);
 #pragma unroll
@@ -690,7 +702,7 @@ __global__ __launch_bounds__(256) void k_quant_oaken_one(const uint16_t* __restr
                                                          const uint16_t* __restrict__ xv, int BH, int H,
                                                          int S, const int* __restrict__ pos,
                                                          TensorArgs tk, TensorArgs tv,
-                                                         unsigned* __restrict__ status) {
+                                                         unsigned* __restrict__ status, PageMap pm) {
   constexpr int NG = kD / GE, LG = GE / 8;
   __shared__ uint16_t lrows[16][128];
   const bool vl = blockIdx.y != 0;
@@ -732,13 +744,22 @@ __global__ __launch_bounds__(256) void k_quant_oaken_one(const uint16_t* __restr
     if (li >= m) incl += o;
   }
   const int rowtot = __shfl(incl, 15, 16);
-  const long long dst = bh * S + p;
-  if (vl) store_row_codes<4, true>(t.codes + dst * 64, li, plo, phi, lrows[rl]);
-  else store_row_codes<4, false>(t.codes + dst * 64, li, plo, phi, lrows[rl]);
-  if (li % LG == 0) {
-    t.scale[dst * NG + li / LG] = s;
-    t.zero[dst * NG + li / LG] = (uint8_t)z;
-    t.oscale[dst * NG + li / LG] = so;
+  long long dst = bh * S + p;
+  bool dense_ok = true;
+  if (pm.pages) {  // the dense row in its page; the sparse list is per sequence
+    const int pg = pm.pages[(long long)b * (S / pm.ptok) + p / pm.ptok];
+    dense_ok = pg >= 0 && pg < pm.npages;
+    if (!dense_ok && li == 0) set_flag(status, kFlagPageRange);
+    dst = ((long long)pg * H + bh % H) * pm.ptok + p % pm.ptok;
+  }
+  if (dense_ok) {
+    if (vl) store_row_codes<4, true>(t.codes + dst * 64, li, plo, phi, lrows[rl]);
+    else store_row_codes<4, false>(t.codes + dst * 64, li, plo, phi, lrows[rl]);
+    if (li % LG == 0) {
+      t.scale[dst * NG + li / LG] = s;
+      t.zero[dst * NG + li / LG] = (uint8_t)z;
+      t.oscale[dst * NG + li / LG] = so;
+    }
   }
   const unsigned long long cap = (unsigned long long)t.sparse_cap;
   unsigned long long e = base + (unsigned)(incl - lc);
@@ -1150,16 +1171,17 @@ hipError_t launch_chunk_append(const CacheArgs& c, const TensorArgs& t, bool vl,
 hipError_t launch_quant_oaken(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
                               int t_new, const int* pos, hipStream_t st) {
   const dim3 grid((unsigned)(c.B * c.H));
+  const PageMap pm{c.pages, c.ptok, c.npages};
 #define KVQ_OAK(GE)                                                                               \
   do {                                                                                            \
     if (vl)                                                                                       \
       hipLaunchKernelGGL((k_quant_oaken<GE, true>), grid, dim3(kThreads), 0, st, x, t_new, c.H,    \
                          c.S, pos, t.thr_lo, t.thr_hi, t.sparse_cap, t.codes, t.scale, t.zero,    \
-                         t.oscale, t.rowptr, t.sparse, c.status);                                 \
+                         t.oscale, t.rowptr, t.sparse, c.status, pm);                             \
     else                                                                                          \
       hipLaunchKernelGGL((k_quant_oaken<GE, false>), grid, dim3(kThreads), 0, st, x, t_new, c.H,   \
                          c.S, pos, t.thr_lo, t.thr_hi, t.sparse_cap, t.codes, t.scale, t.zero,    \
-                         t.oscale, t.rowptr, t.sparse, c.status);                                 \
+                         t.oscale, t.rowptr, t.sparse, c.status, pm);                             \
   } while (0)
   switch (t.group) {
     case 32: KVQ_OAK(32); break;
@@ -1174,11 +1196,12 @@ hipError_t launch_quant_oaken(const CacheArgs& c, const TensorArgs& t, bool vl, 
 hipError_t launch_quant_oaken_one(const CacheArgs& c, const uint16_t* xk, const uint16_t* xv,
                                  const int* pos, hipStream_t st) {
   const int BH = c.B * c.H;
+  const PageMap pm{c.pages, c.ptok, c.npages};
   const dim3 grid((unsigned)((BH + 15) / 16), 2);
   switch (c.k.group) {
-    case 32: hipLaunchKernelGGL((k_quant_oaken_one<32>), grid, dim3(kThreads), 0, st, xk, xv, BH, c.H, c.S, pos, c.k, c.v, c.status); break;
-    case 64: hipLaunchKernelGGL((k_quant_oaken_one<64>), grid, dim3(kThreads), 0, st, xk, xv, BH, c.H, c.S, pos, c.k, c.v, c.status); break;
-    case 128: hipLaunchKernelGGL((k_quant_oaken_one<128>), grid, dim3(kThreads), 0, st, xk, xv, BH, c.H, c.S, pos, c.k, c.v, c.status); break;
+    case 32: hipLaunchKernelGGL((k_quant_oaken_one<32>), grid, dim3(kThreads), 0, st, xk, xv, BH, c.H, c.S, pos, c.k, c.v, c.status, pm); break;
+    case 64: hipLaunchKernelGGL((k_quant_oaken_one<64>), grid, dim3(kThreads), 0, st, xk, xv, BH, c.H, c.S, pos, c.k, c.v, c.status, pm); break;
+    case 128: hipLaunchKernelGGL((k_quant_oaken_one<128>), grid, dim3(kThreads), 0, st, xk, xv, BH, c.H, c.S, pos, c.k, c.v, c.status, pm); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

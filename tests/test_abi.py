@@ -155,7 +155,13 @@ def test_paged_validation_and_sizes():
     assert status_of(K.kvq_cache_bytes, paged(P=128, S=320)) == K.KVQ_ERR_INVALID_ARG
     assert status_of(K.kvq_cache_bytes, paged(pages=0)) == K.KVQ_ERR_INVALID_ARG
     assert status_of(K.kvq_cache_bytes, paged(k_axis=1)) == K.KVQ_ERR_UNSUPPORTED
-    assert status_of(K.kvq_cache_bytes, paged(mode=K.KVQ_MODE_OAKEN)) == K.KVQ_ERR_UNSUPPORTED
+    # Oaken: the dense body in page pools, the sparse lists per (sequence, head) of max_seq rows
+    b = K.kvq_cache_bytes(paged(mode=K.KVQ_MODE_OAKEN, cap=1000))
+    assert (b.k.codes, b.k.scale, b.k.oscale) == (10 * H * 64 * 64, 10 * H * 64 * 2 * 4, 10 * H * 64 * 2 * 4)
+    assert (b.k.rowptr, b.k.sparse) == (2 * H * (256 + 1) * 4, 2 * H * 1000 * 2)
+    c = paged(mode=K.KVQ_MODE_DSQ)
+    c.dsq_sig = 13
+    assert status_of(K.kvq_cache_bytes, c) == K.KVQ_ERR_UNSUPPORTED
     assert status_of(K.kvq_cache_bytes, paged(mode=K.KVQ_MODE_CHUNK_MIXED, group=32)) == K.KVQ_ERR_UNSUPPORTED
 
 

@@ -1,4 +1,5 @@
-"""GPU parity of the paged cache layout (uniform mode, token-axis groups).
+"""GPU parity of the paged cache layout (uniform mode with token-axis groups, and
+Oaken's dense body with per-sequence sparse lists).
 
 Pages are handed out in a seeded random order from a pool larger than the
 sequences need.  Codes and scales gathered through the block table must equal
@@ -133,3 +134,62 @@ def test_paged_bad_page_is_flagged():
     assert cache.flags() == 0 and np.all(np.isfinite(out))
     decode(cache, q, H, [128, 128], 128, 0)  # now it reads through it: page 0 instead, flagged
     assert cache.flags() & K.KVQ_FLAG_PAGE_RANGE
+
+
+@pytest.mark.parametrize("P", [64, 128])
+@pytest.mark.parametrize("G", [1, 4])
+def test_paged_oaken(P, G):
+    """Oaken with its dense body in pages and its sparse lists per sequence: the sparse lists equal
+    the contiguous cache's byte for byte, every dense row gathered through the block table equals
+    the contiguous cache's row, decode equals the contiguous decode to rounding and meets the
+    attention bar against the oracle."""
+    from test_gpu_parity import oaken_thresholds
+    B, H, S, T = 2, 3, 512, 333
+    print("case paged oaken P=%d G=%d" % (P, G), flush=True)
+    w = synth.scaled(synth.WORKLOADS[5], batch=B, kv_heads=H, q_heads=H * G, seq=T, tokens=T)
+    wc = synth.scaled(synth.WORKLOADS[5], kv_heads=4, seq=256)
+    thr_k, thr_v = oaken_thresholds(wc, 0, 20), oaken_thresholds(wc, 1, 20)
+    k, v, q = w.kv(0), w.kv(1), w.q()
+    per_seq, used = S // P, -(-T // P)
+    pool = B * used + 2
+    ids = np.random.default_rng(77 + P).permutation(pool)[:B * used].reshape(B, used)
+    table = np.full((B, per_seq), -1, np.int32)
+    table[:, :used] = ids
+    cap = S * 24
+    # zero-filled, so that the unwritten tails of the sparse buffers compare equal too
+    kw = dict(k_bits=4, k_group=64, k_thr=thr_k, v_thr=thr_v, sparse_cap=cap, zero_fill=True)
+    paged = K.QuantKVCache(B, H, S, K.KVQ_MODE_OAKEN, page_tokens=P, num_pages=pool,
+                           block_table=i32_device(table.reshape(-1)), **kw)
+    flat = K.QuantKVCache(B, H, S, K.KVQ_MODE_OAKEN, **kw)
+    for cache in (paged, flat):  # bulk 300 rows, 32 more, then one row (the one-token kernel)
+        K.kvq_quant_append(cache.desc, to_device(k[:, :, :300]), to_device(v[:, :, :300]), 300, i32_device([0] * B))
+        K.kvq_quant_append(cache.desc, to_device(k[:, :, 300:332]), to_device(v[:, :, 300:332]), 32,
+                           i32_device([300] * B))
+        K.kvq_quant_append(cache.desc, to_device(k[:, :, 332:]), to_device(v[:, :, 332:]), 1, i32_device([332] * B))
+    torch.cuda.synchronize()
+    assert paged.flags() == 0 and flat.flags() == 0
+    for name in ("k", "v"):
+        for f in ("rowptr", "sparse"):
+            assert np.array_equal(host_bytes(paged.buf(name + "." + f)), host_bytes(flat.buf(name + "." + f))), (name, f)
+        for f, per in (("codes", 64), ("scale", 8), ("zero", 2), ("oscale", 8)):
+            pg = host_bytes(paged.buf(name + "." + f)).reshape(pool, H, P, per)
+            fl = host_bytes(flat.buf(name + "." + f)).reshape(B, H, S, per)
+            for b in range(B):
+                t = np.arange(T)
+                got = pg[table[b, t // P], :, t % P].transpose(1, 0, 2)
+                assert np.array_equal(got, fl[b, :, :T]), (name, f, b)
+    deq = {}
+    for name, x, thr in (("k", k, thr_k), ("v", v, thr_v)):
+        deq[name] = oracle.oaken_dequant_rows(*oracle.oaken_rows(x, thr, 64), thr, 64)
+    for lens in ([T, T], [T, 190]):
+        refs = np.stack([oracle.attention(q[b], deq["k"][b][:, :L], deq["v"][b][:, :L], SM)
+                         for b, L in enumerate(lens)])
+        for ns in (0, 1, 3):
+            out_p = decode(paged, q, H * G, lens, T, ns)
+            out_f = decode(flat, q, H * G, lens, T, ns)
+            # the Oaken V post-pass adds outer values with LDS float atomics, whose order varies
+            # between runs, so the two decodes agree to rounding rather than bit for bit
+            assert float(rel_err_rows(out_p, out_f).max()) <= 1e-6, (lens, ns)
+            err = float(rel_err_rows(out_p, refs).max())
+            print("paged oaken P%d G%d ns%d lens%s: max rel err %.3e" % (P, G, ns, lens, err), flush=True)
+            assert err <= ATTN_BAR and err <= ATTN_TIGHT
