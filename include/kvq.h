@@ -205,8 +205,12 @@ typedef struct kvq_cache {
   int32_t* perm;        /* CHUNK_MIXED: [B][C] original chunk id at each slot */
   int32_t* seg;         /* CHUNK_MIXED: [B][4] {n_fp16, n_int4, n_int2, n_chunks} */
   uint32_t* status;     /* device word for KVQ_FLAG_* bits (required) */
-  /* Paged layout (UNIFORM mode with TOKEN-axis K and V, and OAKEN;
-   * page_tokens 0 = contiguous).  Every per-token buffer (codes, scale, zero,
+  /* Paged layout (UNIFORM mode with TOKEN-axis K and V, OAKEN and DSQ;
+   * page_tokens 0 = contiguous).  DSQ pages hold page_tokens / 64 whole
+   * groups: every per-group buffer (codes, scale, codes2, scale2, zero2 and
+   * dsq_mask) is a pool [num_pages][H][page_tokens / 64][...] and group g of
+   * sequence b is group g % (page_tokens / 64) of page
+   * block_table[b][g * 64 / page_tokens]; the fp16 tails stay per sequence.  Every per-token buffer (codes, scale, zero,
    * and Oaken's oscale) is then a pool of num_pages pages
    * [num_pages][H][page_tokens][row], and token t of sequence b lives in page
    * block_table[b][t / page_tokens], row t % page_tokens of its head.  Oaken's

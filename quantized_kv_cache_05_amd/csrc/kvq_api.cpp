@@ -31,8 +31,10 @@ kvq_status check_config(const kvq_cache* c) {
   if (c->page_tokens != 0) {
     if (c->page_tokens != 64 && c->page_tokens != 128 && c->page_tokens != 256) return KVQ_ERR_INVALID_ARG;
     if (c->max_seq % c->page_tokens || c->num_pages < 1) return KVQ_ERR_INVALID_ARG;
-    // uniform token-axis caches, and Oaken's dense body (its sparse lists stay per sequence)
-    if (!((c->mode == KVQ_MODE_UNIFORM && k.axis == KVQ_AXIS_TOKEN) || c->mode == KVQ_MODE_OAKEN))
+    // uniform token-axis caches, Oaken's dense body (its sparse lists stay per
+    // sequence) and DSQ's groups (its fp16 tails stay per sequence)
+    if (!((c->mode == KVQ_MODE_UNIFORM && k.axis == KVQ_AXIS_TOKEN) || c->mode == KVQ_MODE_OAKEN ||
+          c->mode == KVQ_MODE_DSQ))
       return KVQ_ERR_UNSUPPORTED;
   }
   switch (c->mode) {
@@ -142,9 +144,10 @@ kvq_tensor_bytes tensor_bytes(const kvq_cache* c, const kvq_tensor& t, bool is_k
       r.codes2 = B * H * Q * 64 * D / 4;
       r.scale2 = B * H * Q * 64 * (D / 32) * 4;
       r.zero2 = B * H * Q * 64 * (D / 32);
-      // the group being appended: fp16 rows, and (K) the tokens' scores
-      r.codes16 = B * H * 64 * D * 2;
-      if (is_k) r.oscale = B * H * 64 * 4;
+      // the group being appended (per sequence, paged or not): fp16 rows, and
+      // (K) the tokens' scores
+      r.codes16 = B_seq * H * 64 * D * 2;
+      if (is_k) r.oscale = B_seq * H * 64 * 4;
       break;
     }
   }
@@ -314,8 +317,10 @@ kvq_status kvq_cache_bytes(const kvq_cache* c, kvq_cache_bytes_t* out) {
     out->perm = (size_t)c->batch * C * 4;
     out->seg = (size_t)c->batch * 4 * 4;
   }
-  if (c->mode == KVQ_MODE_DSQ)
-    out->dsq_mask = (size_t)c->batch * (size_t)c->kv_heads * (size_t)(c->max_seq / 64) * 8;
+  if (c->mode == KVQ_MODE_DSQ)  // one mask per group: [B][H][S / 64], or pooled with the pages
+    out->dsq_mask = c->page_tokens
+                        ? (size_t)c->num_pages * (size_t)c->kv_heads * (size_t)(c->page_tokens / 64) * 8
+                        : (size_t)c->batch * (size_t)c->kv_heads * (size_t)(c->max_seq / 64) * 8;
   out->status = 4;
   return KVQ_OK;
 }

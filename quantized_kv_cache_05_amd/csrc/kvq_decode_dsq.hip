@@ -30,7 +30,7 @@ __device__ __forceinline__ int arow_of_query(int m) {
   return QR == 1 ? 0 : (QR == 4 ? 4 * m : m);
 }
 
-template <int QR>
+template <int QR, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_dsq(AttnParams P) {
   using QRW = QRows<QR>;
   constexpr int R = QR, GI = QRW::GI;
@@ -90,7 +90,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   bool okO[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) okO[cb] = 16 * cb + n16 < noth;
+  // first slot of group grp in the per-group arrays: contiguous [B][H][S / 64],
+  // or, paged, group grp mod g of page pages[b][grp / g] in the pool
+  // [npages][H][g] (g = page_tokens / 64 groups per page; an entry outside
+  // the pool reads page 0 and flags)
+  auto group_base = [&](int grp) -> long long {
+    if constexpr (PAGED) {
+      const int gsh = P.pshift - 6;
+      int pg = P.pages[(long long)b * (P.S >> P.pshift) + (grp >> gsh)];
+      if (pg < 0 || pg >= P.npages) {
+        if (lane == 0) set_flag(P.status, kFlagPageRange);
+        pg = 0;
+      }
+      return ((long long)pg * P.H + kvh) * (1 << gsh) + (grp & ((1 << gsh) - 1));
+    } else {
+      return bh * Q + grp;
+    }
+  };
   struct KSide {
+    long long gb;               // the group's base (see group_base)
     float4 tsa[PER], tsb[PER];  // table channel scales, loaded first
     KI8<true> kS;
     KI2 kO[4];
@@ -98,7 +116,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     unsigned zkr[4];  // zero-points of the slot's 4 groups (bytes)
   };
   auto load_k = [&](int grp, KSide& d) {
-    const long long gb = bh * Q + grp;
+    const long long gb = group_base(grp);
+    d.gb = gb;
     const float* kss = P.k.scale + gb * kD;
     // lane l builds table entry (l + 64 k) mod NE (NE = 16, 64 or 256): with
     // one query four lanes build each entry and store the same values, which
@@ -127,7 +146,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   KSide kd;
   if (g0 + wave < g1) load_k(g0 + wave, kd);
   for (int grp = g0 + wave; grp < g1; grp += kNW) {
-    const long long gb = bh * Q + grp;
+    const long long gb = kd.gb;  // this group's base, found with its K side
     const uint8_t* vsig = P.v.codes + gb * kSigSlots * kD;
     const float* vss = P.v.scale + gb * kD;
     const TokView vo{P.v.codes2 + gb * kOthSlots * 32, P.v.scale2 + gb * kOthSlots * 4,
@@ -423,10 +442,21 @@ hipError_t launch_decode_dsq(const CacheArgs& c, const DecodeLaunch& d, hipStrea
   if (c.k.group != 32 || c.v.group != 32 || c.dsq_sig < 1 || c.dsq_sig > kSigSlots) return hipErrorInvalidValue;
   const AttnParams P = make_attn_params(c, d);
   const dim3 grid((unsigned)d.num_splits, (unsigned)(c.H * d.qtiles), (unsigned)c.B);
+  if (P.pages && P.pshift < 6) return hipErrorInvalidValue;  // pages hold whole groups
+  const bool pg = P.pages != nullptr;
   switch (d.qr) {
-    case 1: hipLaunchKernelGGL((k_attn_dsq<1>), grid, dim3(kNW * 64), 0, st, P); break;
-    case 4: hipLaunchKernelGGL((k_attn_dsq<4>), grid, dim3(kNW * 64), 0, st, P); break;
-    case 16: hipLaunchKernelGGL((k_attn_dsq<16>), grid, dim3(kNW * 64), 0, st, P); break;
+    case 1:
+      if (pg) hipLaunchKernelGGL((k_attn_dsq<1, true>), grid, dim3(kNW * 64), 0, st, P);
+      else hipLaunchKernelGGL((k_attn_dsq<1, false>), grid, dim3(kNW * 64), 0, st, P);
+      break;
+    case 4:
+      if (pg) hipLaunchKernelGGL((k_attn_dsq<4, true>), grid, dim3(kNW * 64), 0, st, P);
+      else hipLaunchKernelGGL((k_attn_dsq<4, false>), grid, dim3(kNW * 64), 0, st, P);
+      break;
+    case 16:
+      if (pg) hipLaunchKernelGGL((k_attn_dsq<16, true>), grid, dim3(kNW * 64), 0, st, P);
+      else hipLaunchKernelGGL((k_attn_dsq<16, false>), grid, dim3(kNW * 64), 0, st, P);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

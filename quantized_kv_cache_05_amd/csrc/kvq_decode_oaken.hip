@@ -142,7 +142,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_oaken(AttnParams P) {
   __shared__ float mwg[QR];
   constexpr int span = kOakSpan / QR;
   const int split = blockIdx.x, qt = blockIdx.y % P.qtiles, kvh = blockIdx.y / P.qtiles, b = blockIdx.z;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar addressing
+  // wave-uniform wave index (scalar addressing), except when paged (see the
+  // uniform decode kernel: the block-table entry must stay a vector load)
+  const int wave = PAGED ? (int)(threadIdx.x >> 6) : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nq = min(QR, P.G - qt * QR);
   u4_t qop[4];
   attn_prologue<QR, NG>(P, L, b, kvh, qt, nq, qop);

@@ -826,7 +826,7 @@ __global__ __launch_bounds__(256) void k_quant_dsq(const uint16_t* __restrict__ 
                                                    const float* __restrict__ score, int t_new, int H, int S,
                                                    int n_sig, const int* __restrict__ pos, TensorArgs kt,
                                                    TensorArgs vt, unsigned long long* __restrict__ mask_out,
-                                                   unsigned* __restrict__ status) {
+                                                   unsigned* __restrict__ status, PageMap pm) {
   __shared__ float gsc[64];  // the group's scores
   __shared__ int s_tok[kDsqSigSlots];
   __shared__ int o_tok[kDsqOthSlots];
@@ -843,8 +843,17 @@ __global__ __launch_bounds__(256) void k_quant_dsq(const uint16_t* __restrict__ 
   }
   const int k0 = (p & ~63) + 64 * gi;  // first token of the group
   if (k0 + 64 > p + t_new) return;     // still incomplete after this append
-  const long long Q = S / 64;
-  const long long gb = bh * Q + (k0 >> 6);  // destination group
+  // destination group: contiguous [B][H][S / 64], or group k0 mod ptok of
+  // page pages[b][k0 / ptok] in the pool [npages][H][ptok / 64]
+  long long gb = bh * (S / 64) + (k0 >> 6);
+  if (pm.pages) {
+    const int pg = pm.pages[(long long)b * (S / pm.ptok) + k0 / pm.ptok];
+    if (pg < 0 || pg >= pm.npages) {
+      if (threadIdx.x == 0) set_flag(status, kFlagPageRange);
+      return;
+    }
+    gb = ((long long)pg * H + bh % H) * (pm.ptok / 64) + (k0 % pm.ptok) / 64;
+  }
   const int n_oth = 64 - n_sig;
   // the group's tokens below p are read from the tails, the others from the input
   if (threadIdx.x < 64) {
@@ -1211,8 +1220,9 @@ hipError_t launch_quant_dsq(const CacheArgs& c, const uint16_t* xk, const uint16
                             int t_new, const int* pos, hipStream_t st) {
   // groups an append of t_new tokens can complete: floor((p mod 64 + t_new) / 64) <= (t_new + 63) / 64
   const dim3 grid((unsigned)((t_new + 63) / 64), (unsigned)(c.B * c.H));
+  const PageMap pm{c.pages, c.ptok, c.npages};
   hipLaunchKernelGGL(k_quant_dsq, grid, dim3(kThreads), 0, st, xk, xv, score, t_new, c.H, c.S, c.dsq_sig, pos,
-                     c.k, c.v, c.dsq_mask, c.status);
+                     c.k, c.v, c.dsq_mask, c.status, pm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_dsq_tail, dim3((unsigned)(c.B * c.H)), dim3(kThreads), 0, st, xk, xv, score, t_new, c.H,

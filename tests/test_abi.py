@@ -159,9 +159,12 @@ def test_paged_validation_and_sizes():
     b = K.kvq_cache_bytes(paged(mode=K.KVQ_MODE_OAKEN, cap=1000))
     assert (b.k.codes, b.k.scale, b.k.oscale) == (10 * H * 64 * 64, 10 * H * 64 * 2 * 4, 10 * H * 64 * 2 * 4)
     assert (b.k.rowptr, b.k.sparse) == (2 * H * (256 + 1) * 4, 2 * H * 1000 * 2)
-    c = paged(mode=K.KVQ_MODE_DSQ)
+    # DSQ: the groups (and their masks) in page pools, the fp16 tails per sequence
+    c = paged(mode=K.KVQ_MODE_DSQ, group=32)
     c.dsq_sig = 13
-    assert status_of(K.kvq_cache_bytes, c) == K.KVQ_ERR_UNSUPPORTED
+    b = K.kvq_cache_bytes(c)
+    assert (b.k.codes, b.k.codes2, b.dsq_mask) == (10 * H * 1 * 2048, 10 * H * 1 * 2048, 10 * H * 1 * 8)
+    assert (b.k.codes16, b.k.oscale) == (2 * H * 64 * 128 * 2, 2 * H * 64 * 4)
     assert status_of(K.kvq_cache_bytes, paged(mode=K.KVQ_MODE_CHUNK_MIXED, group=32)) == K.KVQ_ERR_UNSUPPORTED
 
 

@@ -1,5 +1,5 @@
-"""GPU parity of the paged cache layout (uniform mode with token-axis groups, and
-Oaken's dense body with per-sequence sparse lists).
+"""GPU parity of the paged cache layout (uniform mode with token-axis groups,
+Oaken's dense body with per-sequence sparse lists, and DSQ's 64-token groups).
 
 Pages are handed out in a seeded random order from a pool larger than the
 sequences need.  Codes and scales gathered through the block table must equal
@@ -192,4 +192,69 @@ def test_paged_oaken(P, G):
             assert float(rel_err_rows(out_p, out_f).max()) <= 1e-6, (lens, ns)
             err = float(rel_err_rows(out_p, refs).max())
             print("paged oaken P%d G%d ns%d lens%s: max rel err %.3e" % (P, G, ns, lens, err), flush=True)
+            assert err <= ATTN_BAR and err <= ATTN_TIGHT
+
+
+@pytest.mark.parametrize("P", [64, 128])
+@pytest.mark.parametrize("G", [1, 4])
+def test_paged_dsq(P, G):
+    """DSQ with its groups in pages: streamed appends into a paged and a contiguous cache give the
+    same groups (gathered through the block table) and tails byte for byte, decode equals the
+    contiguous decode bit for bit and meets the attention bar against the oracle."""
+    B, H, S = 2, 2, 512
+    sizes = [130, 1, 60, 64, 77]
+    T = sum(sizes)
+    print("case paged dsq P=%d G=%d" % (P, G), flush=True)
+    w = synth.scaled(synth.WORKLOADS[8], batch=B, kv_heads=H, q_heads=H * G, seq=T, tokens=T)
+    k, v, q, sc = w.kv(0), w.kv(1), w.q(), w.scores()
+    per_seq, used = S // P, -(-T // P)
+    pool = B * used + 2
+    ids = np.random.default_rng(99 + P).permutation(pool)[:B * used].reshape(B, used)
+    table = np.full((B, per_seq), -1, np.int32)
+    table[:, :used] = ids
+    kw = dict(k_group=32, v_group=32, dsq_sig=13, zero_fill=True)
+    paged = K.QuantKVCache(B, H, S, K.KVQ_MODE_DSQ, page_tokens=P, num_pages=pool,
+                           block_table=i32_device(table.reshape(-1)), **kw)
+    flat = K.QuantKVCache(B, H, S, K.KVQ_MODE_DSQ, **kw)
+    L = 0
+    for n in sizes:
+        for cache in (paged, flat):
+            K.kvq_dsq_append(cache.desc, to_device(np.ascontiguousarray(k[:, :, L:L + n])),
+                             to_device(np.ascontiguousarray(v[:, :, L:L + n])),
+                             torch.from_numpy(np.ascontiguousarray(sc[:, :, L:L + n])).cuda(), n, i32_device([L] * B))
+        L += n
+    torch.cuda.synchronize()
+    assert paged.flags() == 0 and flat.flags() == 0
+    gpp, Q = P // 64, S // 64
+    for name, per in (("k.codes", 2048), ("v.codes", 2048), ("k.scale", 512), ("v.scale", 512),
+                      ("k.codes2", 2048), ("v.codes2", 2048), ("k.scale2", 1024), ("v.scale2", 1024),
+                      ("k.zero2", 256), ("v.zero2", 256), ("dsq_mask", 8)):
+        pg = host_bytes(paged.buf(name)).view(np.uint8).reshape(pool, H, gpp, per)
+        fl = host_bytes(flat.buf(name)).view(np.uint8).reshape(B, H, Q, per)
+        for b in range(B):
+            g = np.arange(T // 64)
+            got = pg[table[b, g // gpp], :, g % gpp].transpose(1, 0, 2)
+            assert np.array_equal(got, fl[b, :, :T // 64]), (name, b)
+    for name in ("k.codes16", "v.codes16", "k.oscale"):
+        assert np.array_equal(host_bytes(paged.buf(name)), host_bytes(flat.buf(name))), name
+    n0 = T & ~63
+    deq = {}
+    for b in range(B):
+        for h in range(H):
+            kh = np.zeros((T, 128), np.float32)
+            vh = np.zeros((T, 128), np.float32)
+            kh[:n0], vh[:n0] = oracle.dsq_dequant(oracle.dsq_quant(k[b, h, :n0], v[b, h, :n0], sc[b, h, :n0]))
+            kh[n0:] = k[b, h, n0:].view(np.float16).astype(np.float32)
+            vh[n0:] = v[b, h, n0:].view(np.float16).astype(np.float32)
+            deq[b, h] = kh, vh
+    for lens in ([T, T], [T, n0 - 64]):
+        refs = np.stack([oracle.attention(q[b], np.stack([deq[b, h][0][:Lb] for h in range(H)]),
+                                          np.stack([deq[b, h][1][:Lb] for h in range(H)]), SM)
+                         for b, Lb in enumerate(lens)])
+        for ns in (0, 1, 3):
+            out_p = decode(paged, q, H * G, lens, T, ns)
+            out_f = decode(flat, q, H * G, lens, T, ns)
+            assert np.array_equal(out_p.view(np.uint32), out_f.view(np.uint32)), (lens, ns)
+            err = float(rel_err_rows(out_p, refs).max())
+            print("paged dsq P%d G%d ns%d lens%s: max rel err %.3e" % (P, G, ns, lens, err), flush=True)
             assert err <= ATTN_BAR and err <= ATTN_TIGHT
