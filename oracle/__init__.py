@@ -49,6 +49,10 @@ def lib():
                 "ora_e4m3_encode": ([ctypes.c_float], ctypes.c_uint8),
                 "ora_quant_rows_e4m3": ([vp, lg, i32, i32, vp, vp], None),
                 "ora_dequant_rows_e4m3": ([vp, vp, lg, i32, i32, vp], None),
+                "ora_e5m2_value": ([ctypes.c_uint8], dbl),
+                "ora_e5m2_encode": ([ctypes.c_float], ctypes.c_uint8),
+                "ora_quant_rows_e5m2": ([vp, lg, i32, i32, vp, vp], None),
+                "ora_dequant_rows_e5m2": ([vp, vp, lg, i32, i32, vp], None),
                 "ora_dequant_rows": ([vp, vp, vp, lg, i32, i32, i32, vp], None),
                 "ora_dequant_channel_blocks": ([vp, vp, vp, lg, lg, i32, i32, vp], None),
                 "ora_oaken_rows": ([vp, lg, i32, i32, vp, vp, vp, vp, vp, vp, vp], None),
@@ -145,6 +149,40 @@ def dequant_rows_e4m3(codes, scale, g):
     D = c.shape[-1]
     out = np.zeros(c.shape, np.float32)
     lib().ora_dequant_rows_e4m3(pc, ps, c.size // D, D, g, out.ctypes.data)
+    return out
+
+
+def e5m2_value(codes) -> np.ndarray:
+    """binary64 values of E5M2 codes (any shape)."""
+    L = lib()
+    flat = np.asarray(codes, dtype=np.uint8).reshape(-1)
+    return np.array([L.ora_e5m2_value(int(c)) for c in flat], dtype=np.float64).reshape(np.shape(codes))
+
+
+def e5m2_encode(y) -> np.ndarray:
+    """E5M2 codes of binary32 values (any shape)."""
+    L = lib()
+    flat = np.asarray(y, dtype=np.float32).reshape(-1)
+    return np.array([L.ora_e5m2_encode(float(v)) for v in flat], dtype=np.uint8).reshape(np.shape(y))
+
+
+def quant_rows_e5m2(x_bits, g):
+    """x [..., D] fp16 bits -> E5M2 codes [..., D] (uint8), scale [..., D/g]."""
+    x, px = _c(x_bits, np.uint16)
+    D = x.shape[-1]
+    rows = x.size // D
+    codes = np.zeros(x.shape, np.uint8)
+    scale = np.zeros(x.shape[:-1] + (D // g,), np.float32)
+    lib().ora_quant_rows_e5m2(px, rows, D, g, codes.ctypes.data, scale.ctypes.data)
+    return codes, scale
+
+
+def dequant_rows_e5m2(codes, scale, g):
+    c, pc = _c(codes, np.uint8)
+    s, ps = _c(scale, np.float32)
+    D = c.shape[-1]
+    out = np.zeros(c.shape, np.float32)
+    lib().ora_dequant_rows_e5m2(pc, ps, c.size // D, D, g, out.ctypes.data)
     return out
 
 

@@ -213,6 +213,79 @@ void ora_dequant_rows_e4m3(const uint8_t* codes, const float* scale, long rows, 
 }
 
 /*
+ * FP8 E5M2, the other format of [KVQ-Eng] §"主流KV Cache量化方案对比", item 1:
+ * 1 sign bit, 5 exponent bits with bias 15, 2 mantissa bits (the exponent
+ * of fp16); exponent field 0 holds the subnormals m * 2^-16, the all-ones
+ * exponent infinities (mantissa 0) and NaNs, so the largest finite
+ * magnitude is 1.75 * 2^15 = 57344.
+ *
+ * Readings (as for E4M3): one binary32 scale per token group,
+ * s = max|x| / 57344; the code of x / s is the nearest finite E5M2 value,
+ * ties to the even mantissa, magnitudes from 57344 up saturate to 57344
+ * (the cache never holds an infinity), sign bit of the quotient kept; an
+ * all-zero group has scale 0 and codes 0.
+ */
+double ora_e5m2_value(uint8_t c) {
+  int e = (c >> 2) & 31, m = c & 3;
+  double v;
+  if (e == 31)
+    v = m ? NAN : INFINITY;
+  else if (e == 0)
+    v = ldexp((double)m, -16);
+  else
+    v = ldexp((double)(4 + m), e - 17);
+  return (c & 0x80) ? -v : v;
+}
+
+/* E5M2 code of a binary32 value: the nearest of the 124 finite non-negative
+ * magnitudes (codes 0x00 .. 0x7B, increasing with the code), found by a
+ * plain search; on a tie the even code wins; 57344 and beyond give 57344. */
+uint8_t ora_e5m2_encode(float y) {
+  uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  double a = fabs((double)y);
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c <= 0x7B; ++c) {
+    double d = fabs(ora_e5m2_value((uint8_t)c) - a);
+    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+      bd = d;
+      best = c;
+    }
+  }
+  if (a >= 57344.0) best = 0x7B; /* saturation */
+  return (uint8_t)(sign | best);
+}
+
+/* One group of n elements: s = amax / 57344, codes E5M2(x / s). */
+void ora_quant_group_e5m2(const uint16_t* x, long n, float* s_out, uint8_t* q) {
+  float amax = 0.0f;
+  for (long i = 0; i < n; ++i) {
+    float v = fabsf(ora_f16_to_f32(x[i]));
+    if (v > amax) amax = v;
+  }
+  float s = amax / 57344.0f;
+  *s_out = s;
+  for (long i = 0; i < n; ++i) q[i] = s == 0.0f ? 0 : ora_e5m2_encode(ora_f16_to_f32(x[i]) / s);
+}
+
+/* Token-axis groups of g channels, E5M2 codes: codes rows x D, scale rows x (D / g). */
+void ora_quant_rows_e5m2(const uint16_t* x, long rows, int D, int g, uint8_t* codes, float* scale) {
+  int ng = D / g;
+  for (long r = 0; r < rows; ++r)
+    for (int j = 0; j < ng; ++j)
+      ora_quant_group_e5m2(x + r * D + (long)j * g, g, &scale[r * ng + j], codes + r * D + (long)j * g);
+}
+
+/* x_hat = value(code) * s in binary32. */
+void ora_dequant_rows_e5m2(const uint8_t* codes, const float* scale, long rows, int D, int g,
+                           float* out) {
+  int ng = D / g;
+  for (long r = 0; r < rows; ++r)
+    for (int d = 0; d < D; ++d)
+      out[r * D + d] = (float)ora_e5m2_value(codes[r * D + d]) * scale[r * ng + d / g];
+}
+
+/*
  * Channel-axis groups for K ([KVQ-Eng], advice to quantize K per channel):
  * x is `slices` slices of [T][D]; each channel of each block of gt
  * consecutive tokens is one group.  codes: slices x T x D,
