@@ -24,6 +24,8 @@ Workloads (seeded synthetic fp16 K/V, head_dim 128; ``--workload N``):
               (max|x| / 448) per token and head
   7 paged     workload 2 in a paged cache: pages of 64 tokens handed out in a
               seeded random order from one pool, read through a block table
+  9 e5m2      workload 2's shapes with FP8 E5M2 codes, one scale
+              (max|x| / 57344) per token and head
   8 dsq       batch 16, 32 MHA heads, 4096 tokens (workload 2's distribution)
               in KVO-LLM's differential significant-token cache: per 64-token
               group the 13 tokens with the largest seeded scores (exp N(0,1))
@@ -65,7 +67,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9])
     p.add_argument("--num-splits", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=16.0,
                    help="budget of the CPU-oracle leg (half single-threaded, half all threads)")
@@ -388,6 +390,8 @@ def build_workload(idx, torch, K, synth):
         return UniformToken(w, torch, K, bits=8, sym=True, group=128, append=True)
     if idx == 6:
         return UniformToken(w, torch, K, bits=8, sym=False, group=128, append=True, fmt=K.KVQ_FMT_E4M3)
+    if idx == 9:
+        return UniformToken(w, torch, K, bits=8, sym=False, group=128, append=True, fmt=K.KVQ_FMT_E5M2)
     if idx == 7:
         return UniformToken(w, torch, K, bits=8, sym=True, group=128, append=True, page=64)
     if idx == 3:
@@ -420,6 +424,9 @@ WORKLOAD_TEXT = {
     7: "llama2-7b-layer-int8-paged: workload 2 (batch 16, 32 MHA heads, 4096 cached + 1 appended "
        "token, INT8 symmetric per token and head) in a paged cache, 64-token pages in a seeded random "
        "order, block table read by decode; step = append 1 token per sequence + 1 decode query per head",
+    9: "llama2-7b-layer-e5m2: batch 16, 32 MHA heads, head_dim 128, 4096 cached + 1 appended token, "
+       "N(0,1) with 4 outlier channels x15 per head; FP8 E5M2 with one scale (max|x| / 57344) per token "
+       "and head; step = append 1 token per sequence + 1 decode query per head",
     8: "llama2-7b-layer-dsq: batch 16, 32 MHA heads, head_dim 128, 4096 tokens N(0,1) with 4 outlier "
        "channels x15 per head, seeded exp(N(0,1)) token scores; KVO-LLM differential significant-token "
        "quantization: per 64-token group the 13 top-scored tokens INT8 per channel, the other 51 INT2 "
@@ -443,12 +450,14 @@ def oracle_slice(w, idx, b, h, thr=None):
     q = w.q(b, b + 1)[0, h * G:(h + 1) * G]
     T = w.tokens
     t0 = time.perf_counter()
-    if idx == 6:
-        kc, ks = oracle.quant_rows_e4m3(k, 128)
-        vc, vs = oracle.quant_rows_e4m3(v, 128)
+    if idx in (6, 9):
+        q8, dq8 = ((oracle.quant_rows_e4m3, oracle.dequant_rows_e4m3) if idx == 6 else
+                   (oracle.quant_rows_e5m2, oracle.dequant_rows_e5m2))
+        kc, ks = q8(k, 128)
+        vc, vs = q8(v, 128)
         t1 = time.perf_counter()
-        kh = oracle.dequant_rows_e4m3(kc, ks, 128)
-        vh = oracle.dequant_rows_e4m3(vc, vs, 128)
+        kh = dq8(kc, ks, 128)
+        vh = dq8(vc, vs, 128)
         nbytes = 2 * T * (128 + 4)
     elif idx in (1, 2, 7):
         bits, sym, g = (4, False, 64) if idx == 1 else (8, True, 128)
@@ -808,7 +817,7 @@ def main():
     app_ms = step_ms - dec_ms
     w = wl.w
     app_tokens = w.batch * (1 if idx != 1 else w.tokens)
-    append_tok_s = app_tokens / (app_ms / 1e3) if (idx in (1, 2, 5, 6, 7) and app_ms > 0) else None
+    append_tok_s = app_tokens / (app_ms / 1e3) if (idx in (1, 2, 5, 6, 7, 9) and app_ms > 0) else None
     log("step %.4f ms, decode %.4f ms (median %.4f) -> %.1f GB/s (%.1f%% of peak)"
         % (step_ms, dec_ms, float(np.median(dec_times)), achieved, 100 * achieved / HBM_PEAK_GBS))
 

@@ -67,8 +67,9 @@ enum {
 /* Code format of a tensor. */
 enum {
   KVQ_FMT_INT = 0, /* integer codes as described below */
-  KVQ_FMT_E4M3 = 1 /* FP8 E4M3 codes ([KVQ-Eng] §"主流KV Cache量化方案对比", FP8 item);
-                      UNIFORM mode, bits 8, TOKEN axis, symmetric 0, K and V alike */
+  KVQ_FMT_E4M3 = 1, /* FP8 E4M3 codes ([KVQ-Eng] §"主流KV Cache量化方案对比", FP8 item);
+                       UNIFORM mode, bits 8, TOKEN axis, symmetric 0, K and V alike */
+  KVQ_FMT_E5M2 = 2   /* FP8 E5M2 codes (the same item's other format); same constraints */
 };
 
 /* Device status bits (OR-ed into *status by kernels). */
@@ -96,6 +97,11 @@ enum {
  *               the even mantissa, saturating at 448, sign bit of x / s;
  *               x_hat = value(q) * s.  Stored like symmetric INT8 (one
  *               byte per code, no zero buffer).
+ *   E5M2 (format KVQ_FMT_E5M2): s = max|x| / 57344, q = the OCP E5M2 value
+ *               (1 sign, 5 exponent bits with bias 15, 2 mantissa bits)
+ *               nearest to x / s, ties to the even mantissa, saturating at
+ *               57344 (no infinity is stored), sign bit of x / s; stored as
+ *               E4M3 is.
  *
  * Buffers by mode (B = batch, H = kv_heads, S = max_seq, D = 128,
  * RB = D * bits / 8 bytes per token row, NG = D / group):

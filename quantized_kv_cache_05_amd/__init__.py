@@ -34,6 +34,7 @@ KVQ_AXIS_TOKEN = 0
 KVQ_AXIS_CHANNEL = 1
 KVQ_FMT_INT = 0
 KVQ_FMT_E4M3 = 1
+KVQ_FMT_E5M2 = 2
 
 KVQ_FLAG_POS_RANGE = 1
 KVQ_FLAG_SPARSE_FULL = 2

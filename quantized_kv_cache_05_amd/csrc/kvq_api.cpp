@@ -42,8 +42,9 @@ kvq_status check_config(const kvq_cache* c) {
       for (const kvq_tensor* t : {&k, &v}) {
         if (t->bits != 8 && t->bits != 4 && t->bits != 2) return KVQ_ERR_INVALID_ARG;
         if (t->symmetric != 0 && t->symmetric != 1) return KVQ_ERR_INVALID_ARG;
-        if (t->format != KVQ_FMT_INT && t->format != KVQ_FMT_E4M3) return KVQ_ERR_INVALID_ARG;
-        if (t->format == KVQ_FMT_E4M3 && (t->bits != 8 || t->symmetric || t->axis != KVQ_AXIS_TOKEN))
+        if (t->format != KVQ_FMT_INT && t->format != KVQ_FMT_E4M3 && t->format != KVQ_FMT_E5M2)
+          return KVQ_ERR_INVALID_ARG;
+        if (t->format != KVQ_FMT_INT && (t->bits != 8 || t->symmetric || t->axis != KVQ_AXIS_TOKEN))
           return KVQ_ERR_UNSUPPORTED;
         if (t->symmetric && t->bits != 8) return KVQ_ERR_UNSUPPORTED;
         if (t->axis != KVQ_AXIS_TOKEN && t->axis != KVQ_AXIS_CHANNEL) return KVQ_ERR_INVALID_ARG;
@@ -112,7 +113,7 @@ kvq_tensor_bytes tensor_bytes(const kvq_cache* c, const kvq_tensor& t, bool is_k
         r.codes16 = B * H * 64 * D * 2;  // fp16 residual tail: the incomplete 64-token block
       } else {
         r.scale = B * H * S * ng * 4;
-        r.zero = (t.symmetric || t.format == KVQ_FMT_E4M3) ? 0 : B * H * S * ng;
+        r.zero = (t.symmetric || t.format != KVQ_FMT_INT) ? 0 : B * H * S * ng;
       }
       break;
     case KVQ_MODE_OAKEN:

@@ -193,6 +193,32 @@ struct KE4 {
   }
 };
 
+// FP8 E5M2 codes: an E5M2 byte is the high byte of the fp16 number of the
+// same value (same exponent field, two mantissa bits), so one byte permute
+// per pair builds the exact fp16 operands: byte i of the slot's two words to
+// bits 8-15 and 24-31 (channel offsets i and i + 4, as INT8).
+__host__ __device__ constexpr unsigned sel_high_bytes(int i) {
+  return ((4u + i) << 24) | (0x0Cu << 16) | ((unsigned)i << 8) | 0x0Cu;
+}
+
+struct KE5 {
+  static constexpr int RB = 128, OFF = 0, BITS = 8;
+  static constexpr bool SYM = true, F16 = false;
+  u4_t a, b;
+  __device__ __forceinline__ void load(const uint8_t* row, int q4) {
+    a = ld_nt<u4_t>(row + q4 * 32);
+    b = ld_nt<u4_t>(row + q4 * 32 + 16);
+  }
+  __device__ __forceinline__ u4_t slice(int s) const {
+    const unsigned lo = s < 2 ? a[2 * s] : b[2 * s - 4];
+    const unsigned hi = s < 2 ? a[2 * s + 1] : b[2 * s - 3];
+    u4_t o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = perm(hi, lo, sel_high_bytes(i));
+    return o;
+  }
+};
+
 struct KF16 {
   static constexpr int RB = 256, OFF = 0, BITS = 16;
   static constexpr bool SYM = false, F16 = true;
@@ -216,6 +242,7 @@ struct KF16 {
 // par = 1 for odd blocks when ZODD.
 
 struct VI4 {
+  static constexpr float WS = 1.0f;  // weight scale (see VE5)
   static constexpr int RB = 64, BITS = 4;
   static constexpr bool SYM = false, F16 = false, ZODD = true, ZP = true, MASK_ROWS = false;
   static constexpr unsigned ZMAGIC = 0xE400E400u;
@@ -238,6 +265,7 @@ struct VI4 {
 };
 
 struct VI2 {
+  static constexpr float WS = 1.0f;  // weight scale (see VE5)
   static constexpr int RB = 32, BITS = 2;
   static constexpr bool SYM = false, F16 = false, ZODD = false, ZP = true, MASK_ROWS = false;
   static constexpr unsigned ZMAGIC = 0xE400E400u;
@@ -265,6 +293,7 @@ struct VI2 {
 
 template <bool SYM_>
 struct VI8 {
+  static constexpr float WS = 1.0f;  // weight scale (see VE5)
   static constexpr int RB = 128, BITS = 8;
   static constexpr bool SYM = SYM_, F16 = false, ZODD = false, ZP = true, MASK_ROWS = false;
   static constexpr unsigned ZMAGIC = 0xE400E400u;
@@ -296,6 +325,7 @@ struct VI8 {
 // zero-point; rows past the valid range are cleared (a stray byte could be
 // the NaN pattern, and 0 * NaN would poison the product).
 struct VE4 {
+  static constexpr float WS = 1.0f;  // weight scale (see VE5)
   static constexpr int RB = 128, BITS = 8;
   static constexpr bool SYM = true, F16 = false, ZODD = false, ZP = false, MASK_ROWS = true;
   static constexpr float fac(int) { return 1.0f; }
@@ -324,7 +354,43 @@ struct VE4 {
   }
 };
 
+// E5M2 V codes: the B operand pair (rows 2p, 2p + 1) of column block j is
+// byte j mod 4 of the two rows' words moved to the high bytes.  No
+// zero-point; rows past the valid range are cleared (a stray byte could be
+// an infinity or NaN pattern).  The scale max|x| / 57344 is small, so the
+// weights p s would often be fp16 subnormals, which the matrix cores do not
+// multiply exactly: the weights enter as p (s 2^15) (exact scaling; s 2^15
+// stays below 37,450 for any fp16 input) and the output blocks carry the
+// factor 2^15, removed when the wave's state leaves the loop.
+struct VE5 {
+  static constexpr float WS = 32768.0f;
+  static constexpr int RB = 128, BITS = 8;
+  static constexpr bool SYM = true, F16 = false, ZODD = false, ZP = false, MASK_ROWS = true;
+  static constexpr float fac(int) { return WS; }
+  unsigned w0[8], w1[8];  // codes of channels n16 + 16 e, e = 0-3 and 4-7, per row
+  __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const u2_t v = ld_nt<u2_t>(row0 + k * RB + n16 * 8);
+      w0[k] = v[0];
+      w1[k] = v[1];
+    }
+  }
+  __device__ __forceinline__ void zero_row(int k) {
+    w0[k] = 0u;
+    w1[k] = 0u;
+  }
+  __device__ __forceinline__ u4_t block(int j) const {
+    const unsigned* w = (j >> 2) ? w1 : w0;
+    u4_t o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) o[p] = perm(w[2 * p + 1], w[2 * p], sel_high_bytes(j & 3));
+    return o;
+  }
+};
+
 struct VF16 {
+  static constexpr float WS = 1.0f;  // weight scale (see VE5)
   static constexpr int RB = 256, BITS = 16;
   static constexpr bool SYM = false, F16 = true, ZODD = false, ZP = false, MASK_ROWS = true;
   static constexpr float fac(int) { return 1.0f; }

@@ -390,8 +390,8 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
             w0 = p[0][i];
             w1 = p[1][i];
           } else {
-            w0 = ok[0] ? p[0][i] * sv[0][g] : 0.0f;
-            w1 = ok[1] ? p[1][i] * sv[1][g] : 0.0f;
+            w0 = ok[0] ? p[0][i] * (sv[0][g] * VC::WS) : 0.0f;
+            w1 = ok[1] ? p[1][i] * (sv[1][g] * VC::WS) : 0.0f;
           }
           unsigned hi, lo;
           split_pair(w0, w1, hi, lo);

@@ -119,6 +119,7 @@ hipError_t go_codec(const AttnParams& P, dim3 grid, hipStream_t st) {
   const bool chank = P.k.axis == 1;
   const int ng = kD / P.v.group;
   if (P.v.fmt == 1) return go_ng<QR, KE4, VE4, false>(P, grid, chank, ng, st);
+  if (P.v.fmt == 2) return go_ng<QR, KE5, VE5, false>(P, grid, chank, ng, st);
   if (P.v.sym) return go_ng<QR, KI8<true>, VI8<true>, false>(P, grid, chank, ng, st);
   switch (P.v.bits) {
     case 8: return go_ng<QR, KI8<false>, VI8<false>>(P, grid, chank, ng, st);
@@ -148,7 +149,7 @@ bool decode_uniform_supported(const TensorArgs& k, const TensorArgs& v) {
   if (v.axis != 0) return false;
   if (v.group != 32 && v.group != 64 && v.group != 128) return false;
   if (k.bits != v.bits || k.sym != v.sym || k.fmt != v.fmt) return false;
-  if (v.fmt == 1) return v.bits == 8 && !v.sym && k.axis == 0 && k.group == v.group;
+  if (v.fmt == 1 || v.fmt == 2) return v.bits == 8 && !v.sym && k.axis == 0 && k.group == v.group;
   if (v.sym && v.bits != 8) return false;
   if (v.bits != 8 && v.bits != 4 && v.bits != 2) return false;
   if (k.axis == 0) return k.group == v.group;

@@ -42,23 +42,43 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
   return sign | mag;
 }
 
-template <int BITS, bool SYM, int GE, bool F8 = false>
+// OCP E5M2 code of a binary32 value (5 exponent bits as fp16, largest finite
+// 1.75 * 2^15 = 57344; the cache never holds an infinity): the nearest
+// finite value, ties to the even mantissa, magnitudes from 57344 up give
+// 57344; the sign bit is kept.
+//  |y| < 2^-14: the subnormal codes m * 2^-16, m = rne(|y| * 2^16) (m = 4 is
+//               the smallest normal, code 0x04);
+//  otherwise  : exponent and mantissa bits rounded half to even at bit 21,
+//               then the exponent rebiased from 127 to 15.
+__device__ __forceinline__ uint32_t e5m2_code(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  const uint32_t normal = ((a + 0xFFFFFu + ((a >> 21) & 1u)) >> 21) - (112u << 2);
+  const uint32_t sub = (uint32_t)rintf(__uint_as_float(a) * 65536.0f);
+  const uint32_t mag = a >= 0x47600000u ? 0x7Bu : (a < 0x38800000u ? sub : normal);
+  return sign | mag;
+}
+
+// F8: 0 integer codes, 1 FP8 E4M3, 2 FP8 E5M2
+template <int BITS, bool SYM, int GE, int F8 = 0>
 __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint32_t& plo,
                                        uint32_t& phi, float& s, int& z) {
   constexpr int LG = GE / 8;
   plo = 0;
   phi = 0;
-  if constexpr (F8) {
-    static_assert(BITS == 8, "E4M3 codes are bytes");
+  if constexpr (F8 != 0) {
+    static_assert(BITS == 8, "FP8 codes are bytes");
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
     amax = max_lanes<1, LG>(amax);
-    s = amax / 448.0f;
+    s = amax / (F8 == 1 ? 448.0f : 57344.0f);
     z = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint32_t byte = s != 0.0f ? e4m3_code(x[k] / s) : 0u;
+      uint32_t byte = 0u;
+      if (s != 0.0f) byte = F8 == 1 ? e4m3_code(x[k] / s) : e5m2_code(x[k] / s);
       if (k < 4) plo |= byte << (8 * k);
       else phi |= byte << (8 * (k - 4));
     }
@@ -202,7 +222,7 @@ struct PageMap {
   int ptok, npages;
 };
 
-template <int BITS, bool SYM, int GE, bool VL, bool F8 = false>
+template <int BITS, bool SYM, int GE, bool VL, int F8 = 0>
 __device__ __forceinline__ void quant_token_row(long long row, const uint16_t* __restrict__ x, int t_new,
                                                 int H, int S, const int* __restrict__ pos, long long rows,
                                                 uint8_t* __restrict__ codes, float* __restrict__ scale,
@@ -242,7 +262,7 @@ __device__ __forceinline__ void quant_token_row(long long row, const uint16_t* _
   }
 }
 
-template <int BITS, bool SYM, int GE, bool VL, bool F8>
+template <int BITS, bool SYM, int GE, bool VL, int F8>
 __global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict__ x, int t_new, int H,
                                                      int S, const int* __restrict__ pos,
                                                      long long rows, uint8_t* __restrict__ codes,
@@ -258,7 +278,7 @@ __global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict_
 
 // K and V of the same token-axis format in one launch: blockIdx.y selects the
 // tensor (0: K rows, 1: V rows), so a decode-step append costs one launch.
-template <int BITS, bool SYM, int GE, bool F8>
+template <int BITS, bool SYM, int GE, int F8>
 __global__ __launch_bounds__(256) void k_quant_token_kv(const uint16_t* __restrict__ xk,
                                                         const uint16_t* __restrict__ xv, int t_new, int H,
                                                         int S, const int* __restrict__ pos, long long rows,
@@ -1029,18 +1049,22 @@ hipError_t launch_quant_token_kv(const CacheArgs& c, const uint16_t* xk, const u
     case 128: KVQ_TOK(BITS, SYM, 128, F8); break; \
     default: return hipErrorInvalidValue;         \
   }
-  if (t.fmt == 1) {
+  if (t.fmt == 1 || t.fmt == 2) {
     if (t.bits != 8 || t.sym) return hipErrorInvalidValue;
-    KVQ_TOK_G(8, false, true);
+    if (t.fmt == 1) {
+      KVQ_TOK_G(8, false, 1);
+    } else {
+      KVQ_TOK_G(8, false, 2);
+    }
   } else if (t.sym) {
     if (t.bits != 8) return hipErrorInvalidValue;
-    KVQ_TOK_G(8, true, false);
+    KVQ_TOK_G(8, true, 0);
   } else if (t.bits == 8) {
-    KVQ_TOK_G(8, false, false);
+    KVQ_TOK_G(8, false, 0);
   } else if (t.bits == 4) {
-    KVQ_TOK_G(4, false, false);
+    KVQ_TOK_G(4, false, 0);
   } else if (t.bits == 2) {
-    KVQ_TOK_G(2, false, false);
+    KVQ_TOK_G(2, false, 0);
   } else {
     return hipErrorInvalidValue;
   }
@@ -1070,18 +1094,22 @@ hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, bool vl, 
     case 128: KVQ_TOK(BITS, SYM, 128, F8); break; \
     default: return hipErrorInvalidValue;         \
   }
-  if (t.fmt == 1) {
+  if (t.fmt == 1 || t.fmt == 2) {
     if (t.bits != 8 || t.sym) return hipErrorInvalidValue;
-    KVQ_TOK_G(8, false, true);
+    if (t.fmt == 1) {
+      KVQ_TOK_G(8, false, 1);
+    } else {
+      KVQ_TOK_G(8, false, 2);
+    }
   } else if (t.sym) {
     if (t.bits != 8) return hipErrorInvalidValue;
-    KVQ_TOK_G(8, true, false);
+    KVQ_TOK_G(8, true, 0);
   } else if (t.bits == 8) {
-    KVQ_TOK_G(8, false, false);
+    KVQ_TOK_G(8, false, 0);
   } else if (t.bits == 4) {
-    KVQ_TOK_G(4, false, false);
+    KVQ_TOK_G(4, false, 0);
   } else if (t.bits == 2) {
-    KVQ_TOK_G(2, false, false);
+    KVQ_TOK_G(2, false, 0);
   } else {
     return hipErrorInvalidValue;
   }

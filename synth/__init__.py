@@ -213,6 +213,8 @@ WORKLOADS = {
                 outlier_mult=15.0, outlier_count=4),
     8: Workload(8, "llama2-7b-dsq", batch=16, kv_heads=32, q_heads=32, seq=4096, tokens=4096,
                 outlier_mult=15.0, outlier_count=4),
+    9: Workload(9, "llama2-7b-e5m2", batch=16, kv_heads=32, q_heads=32, seq=4097, tokens=4097,
+                outlier_mult=15.0, outlier_count=4),
 }
 
 

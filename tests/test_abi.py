@@ -116,12 +116,13 @@ def test_config_validation(mutate, expect):
     assert status_of(K.kvq_cache_bytes, c) == expect
 
 
-def test_e4m3_format_validation_and_sizes():
+@pytest.mark.parametrize("fmt", [1, 2])  # KVQ_FMT_E4M3, KVQ_FMT_E5M2
+def test_fp8_format_validation_and_sizes(fmt):
     B, H, S = 2, 3, 256
 
     def e4m3(**kw):
         c = make_desc(**kw)
-        c.k.format = c.v.format = K.KVQ_FMT_E4M3
+        c.k.format = c.v.format = fmt
         return c
 
     b = K.kvq_cache_bytes(e4m3(bits=8, group=64))
@@ -133,9 +134,9 @@ def test_e4m3_format_validation_and_sizes():
     assert status_of(K.kvq_cache_bytes, e4m3(mode=K.KVQ_MODE_OAKEN)) == K.KVQ_ERR_UNSUPPORTED
     assert status_of(K.kvq_cache_bytes, e4m3(mode=K.KVQ_MODE_CHUNK_MIXED, group=32)) == K.KVQ_ERR_UNSUPPORTED
     c = make_desc(bits=8)
-    c.k.format = K.KVQ_FMT_E4M3  # K and V formats must agree
+    c.k.format = fmt  # K and V formats must agree
     assert status_of(K.kvq_cache_bytes, c) == K.KVQ_ERR_UNSUPPORTED
-    c.k.format = 2
+    c.k.format = 3  # no such format
     assert status_of(K.kvq_cache_bytes, c) == K.KVQ_ERR_INVALID_ARG
 
 

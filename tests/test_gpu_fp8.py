@@ -1,9 +1,10 @@
-"""GPU parity of the FP8 E4M3 cache (uniform mode, token-axis groups).
+"""GPU parity of the FP8 caches, E4M3 and E5M2 (uniform mode, token-axis groups).
 
 Codes and scales must equal the oracle's bit for bit; attention within the
-bar.  The encoder is also checked exhaustively: groups whose largest
-magnitude is 448 have scale exactly 1, so every finite fp16 value up to 448
-in magnitude is encoded as itself and compared with the oracle's encoding.
+bar.  The encoders are also checked exhaustively: groups whose largest
+magnitude is the format's largest finite value (448, 57344) have scale
+exactly 1, so every finite fp16 value up to it in magnitude is encoded as
+itself and compared with the oracle's encoding.
 """
 import numpy as np
 import pytest
@@ -33,8 +34,15 @@ def f32bits(a):
     return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
 
 
-def e4m3_cache(B, H, S, group):
-    return K.QuantKVCache(B, H, S, K.KVQ_MODE_UNIFORM, k_bits=8, k_group=group, fmt=K.KVQ_FMT_E4M3)
+# format name -> (format id, oracle quantizer, oracle dequantizer, oracle encoder, largest finite value)
+FORMATS = {
+    "e4m3": (1, oracle.quant_rows_e4m3, oracle.dequant_rows_e4m3, oracle.e4m3_encode, 448.0),
+    "e5m2": (2, oracle.quant_rows_e5m2, oracle.dequant_rows_e5m2, oracle.e5m2_encode, 57344.0),
+}
+
+
+def fp8_cache(B, H, S, group, fmt="e4m3"):
+    return K.QuantKVCache(B, H, S, K.KVQ_MODE_UNIFORM, k_bits=8, k_group=group, fmt=FORMATS[fmt][0])
 
 
 def device_codes(cache, name, B, H, S, group):
@@ -43,24 +51,26 @@ def device_codes(cache, name, B, H, S, group):
     return codes, scale
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("group", [32, 64, 128])
 @pytest.mark.parametrize("G", [1, 4, 16])
-def test_e4m3_uniform(group, G):
+def test_fp8_uniform(group, G, fmt):
     B, H, T, S = 2, 3, 333, 384
-    print("case e4m3 group=%d G=%d" % (group, G), flush=True)
+    print("case %s group=%d G=%d" % (fmt, group, G), flush=True)
+    _, quant, dequant, _, _ = FORMATS[fmt]
     w = synth.scaled(synth.WORKLOADS[1], batch=B, kv_heads=H, q_heads=H * G, seq=T, tokens=T)
     k, v, q = w.kv(0), w.kv(1), w.q()
-    cache = e4m3_cache(B, H, S, group)
+    cache = fp8_cache(B, H, S, group, fmt)
     K.kvq_quant_append(cache.desc, to_device(k), to_device(v), T, i32_device([0] * B))
     torch.cuda.synchronize()
     assert cache.flags() == 0
     deq = {}
     for name, x in (("k", k), ("v", v)):
-        oc, os_ = oracle.quant_rows_e4m3(x, group)
+        oc, os_ = quant(x, group)
         gc, gs = device_codes(cache, name, B, H, S, group)
         assert np.array_equal(gc[:, :, :T], oc), name + " codes"
         assert np.array_equal(f32bits(gs[:, :, :T]), f32bits(os_)), name + " scales"
-        deq[name] = oracle.dequant_rows_e4m3(oc, os_, group)
+        deq[name] = dequant(oc, os_, group)
     seq_len = [T, T - 77]
     for ns in (0, 1, 3):
         out = torch.full((B, H * G, 128), float("nan"), dtype=torch.float32, device="cuda")
@@ -70,33 +80,36 @@ def test_e4m3_uniform(group, G):
         refs = np.stack([oracle.attention(q[b], deq["k"][b][:, :L], deq["v"][b][:, :L], SM)
                          for b, L in enumerate(seq_len)])
         err = float(rel_err_rows(out.cpu().numpy(), refs).max())
-        print("e4m3 g%d G%d ns%d: max rel err %.3e" % (group, G, ns, err), flush=True)
+        print("%s g%d G%d ns%d: max rel err %.3e" % (fmt, group, G, ns, err), flush=True)
         assert err <= ATTN_BAR and err <= ATTN_TIGHT
 
 
-def test_e4m3_encoder_every_f16_value():
-    """Every finite fp16 value of magnitude <= 448, in groups of 32 led by 448 (scale 1)."""
-    print("case e4m3 exhaustive encoder", flush=True)
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_encoder_every_f16_value(fmt):
+    """Every finite fp16 value of magnitude <= the format's largest, in groups of 32 led by it
+    (scale 1)."""
+    print("case %s exhaustive encoder" % fmt, flush=True)
+    _, _, _, encode, top = FORMATS[fmt]
     h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     f = h.view(np.float16).astype(np.float32)
-    vals = h[np.isfinite(f) & (np.abs(f) <= 448)]
+    vals = h[np.isfinite(f) & (np.abs(f) <= top)]
     per = 31
     n_groups = -(-vals.size // per)
     payload = np.zeros(n_groups * per, np.uint16)
     payload[:vals.size] = vals
-    groups = np.concatenate([np.full((n_groups, 1), np.float16(448.0).view(np.uint16), np.uint16),
+    groups = np.concatenate([np.full((n_groups, 1), np.float16(top).view(np.uint16), np.uint16),
                              payload.reshape(n_groups, per)], axis=1)
     rows = -(-n_groups // 4)
     x = np.zeros((rows * 4, 32), np.uint16)
     x[:n_groups] = groups
-    x[n_groups:, 0] = np.float16(448.0).view(np.uint16)
+    x[n_groups:, 0] = np.float16(top).view(np.uint16)
     x = x.reshape(1, 1, rows, 128)
     S = (rows + 63) // 64 * 64
-    cache = e4m3_cache(1, 1, S, 32)
+    cache = fp8_cache(1, 1, S, 32, fmt)
     K.kvq_quant_append(cache.desc, to_device(x), to_device(x), rows, i32_device([0]))
     torch.cuda.synchronize()
     assert cache.flags() == 0
-    want = oracle.e4m3_encode(x.view(np.float16).astype(np.float32))
+    want = encode(x.view(np.float16).astype(np.float32))
     for name in ("k", "v"):
         gc, gs = device_codes(cache, name, 1, 1, S, 32)
         assert np.all(gs[0, 0, :rows] == 1.0)

@@ -23,7 +23,7 @@ SM = 1.0 / np.sqrt(128.0)
 LAYOUT = {"k": "K", "v": "V"}
 
 # (bits, symmetric, group, format)
-CODECS = [(8, True, 128, 0), (4, False, 64, 0), (2, False, 32, 0), (8, False, 128, 1)]
+CODECS = [(8, True, 128, 0), (4, False, 64, 0), (2, False, 32, 0), (8, False, 128, 1), (8, False, 128, 2)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -57,8 +57,10 @@ def decode(cache, q, Hq, lens, max_len, ns):
 def oracle_rows(x, codec):
     bits, sym, group, fmt = codec
     if fmt:
-        c, s = oracle.quant_rows_e4m3(x, group)
-        return c, s, None, oracle.dequant_rows_e4m3(c, s, group)
+        q, dq = ((oracle.quant_rows_e4m3, oracle.dequant_rows_e4m3) if fmt == 1 else
+                 (oracle.quant_rows_e5m2, oracle.dequant_rows_e5m2))
+        c, s = q(x, group)
+        return c, s, None, dq(c, s, group)
     c, s, z = oracle.quant_rows(x, group, bits, sym)
     return c, s, z, oracle.dequant_rows(c, s, z, group, sym)
 
