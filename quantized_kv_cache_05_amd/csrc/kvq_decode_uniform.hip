@@ -159,73 +159,73 @@ bool decode_uniform_supported(const TensorArgs& k, const TensorArgs& v) {
 
 // Log-sum-exp merge of split partials: one workgroup of 1024 threads per
 // (b, query head): M = max m_j, L = sum l_j 2^(m_j - M), out = sum 2^(m_j - M) o_j / L.
-// Split weights are formed cooperatively in LDS, a chunk of splits at a time;
-// thread t owns output channel t mod 128 and the splits j = t / 128 (mod 8) of
-// the chunk, so each channel has eight threads with independent loads in
-// flight (a merge of 128 splits takes two rounds of loads per thread).
+// Thread t owns output channel t mod 128 and the splits j = t / 128 (mod 8);
+// it issues the loads of up to kMergeRun of its splits at once and folds them
+// into a running (max, sum, output) state, rescaled when the max grows, so a
+// merge of up to 128 splits waits on one round of loads.  The eight states of
+// each channel are then combined through LDS in a fixed order.
 constexpr int kMergeThreads = 1024;
-
-__device__ __forceinline__ float merge_block_reduce(float v, bool is_max, float* red) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const float o = __shfl_xor(v, m, 64);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int i = 1; i < kMergeThreads / 64; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
-  return r;
-}
+constexpr int kMergeRun = 16;
 
 __global__ __launch_bounds__(kMergeThreads) void k_merge(const float* __restrict__ ws, int NS,
                                                         float* __restrict__ out) {
   constexpr int NP = kMergeThreads / kD;  // threads per output channel
-  constexpr int CH = 2048;                // splits per LDS chunk
-  __shared__ float wgt[CH];
-  __shared__ float red[kMergeThreads / 64];
+  __shared__ float pm[NP], pl[NP];
   __shared__ float po[NP][kD];
   const long long bq = blockIdx.x;
   const int t = threadIdx.x, d = t & (kD - 1), part = t / kD;
   const float* rec0 = ws + bq * NS * kPartStride;
-  float M = -INFINITY;
-  for (int s = t; s < NS; s += kMergeThreads) M = fmaxf(M, rec0[(long long)s * kPartStride]);
-  M = merge_block_reduce(M, true, red);
-  float Lp = 0.0f, O = 0.0f;
-  if (M != -INFINITY) {
-    for (int c0 = 0; c0 < NS; c0 += CH) {
-      const int n = min(CH, NS - c0);
-      for (int s = t; s < n; s += kMergeThreads) {
-        const float* r = rec0 + (long long)(c0 + s) * kPartStride;
-        const float ms = r[0];
-        const float f = ms == -INFINITY ? 0.0f : fexp2(ms - M);
-        wgt[s] = f;
-        Lp = fmaf(f, r[1], Lp);
-      }
-      __syncthreads();
-      const float* r = rec0 + (long long)c0 * kPartStride + 4 + d;
-      int s = part;
-      for (; s + 7 * NP < n; s += 8 * NP) {
-        float v[8];
+  float M = -INFINITY, Ls = 0.0f, O = 0.0f;
+  for (int s0 = part; s0 < NS; s0 += kMergeRun * NP) {
+    float m[kMergeRun], l[kMergeRun], o[kMergeRun];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = r[(long long)(s + k * NP) * kPartStride];
+    for (int k = 0; k < kMergeRun; ++k) {
+      const int s = s0 + k * NP;
+      // past the last split, read split s0 again (in range) and drop it below
+      const float* r = rec0 + (long long)(s < NS ? s : s0) * kPartStride;
+      m[k] = r[0];
+      l[k] = r[1];
+      o[k] = r[4 + d];
+    }
+    float mx = M;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) O = fmaf(wgt[s + k * NP], v[k], O);
+    for (int k = 0; k < kMergeRun; ++k) {
+      if (s0 + k * NP >= NS) m[k] = -INFINITY;
+      mx = fmaxf(mx, m[k]);
+    }
+    if (mx != -INFINITY) {
+      const float c = fexp2(M - mx);  // 0 while M is still -inf
+      Ls *= c;
+      O *= c;
+#pragma unroll
+      for (int k = 0; k < kMergeRun; ++k) {
+        const float f = fexp2(m[k] - mx);  // 0 for an empty or dropped split
+        Ls = fmaf(f, l[k], Ls);
+        O = fmaf(f, o[k], O);
       }
-      for (; s < n; s += NP) O = fmaf(wgt[s], r[(long long)s * kPartStride], O);
-      __syncthreads();
+      M = mx;
     }
   }
-  const float L = merge_block_reduce(Lp, false, red);
+  if (d == 0) {
+    pm[part] = M;
+    pl[part] = Ls;
+  }
   po[part][d] = O;
   __syncthreads();
   if (t < kD) {
-    float o = 0.0f;
+    float Mx = -INFINITY;
 #pragma unroll
-    for (int p = 0; p < NP; ++p) o += po[p][t];
-    out[bq * kD + t] = L > 0.0f ? o / L : 0.0f;
+    for (int p = 0; p < NP; ++p) Mx = fmaxf(Mx, pm[p]);
+    float Lt = 0.0f, Ot = 0.0f;
+    if (Mx != -INFINITY) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const float f = fexp2(pm[p] - Mx);
+        Lt = fmaf(f, pl[p], Lt);
+        Ot = fmaf(f, po[p][t], Ot);
+      }
+    }
+    out[bq * kD + t] = Lt > 0.0f ? Ot / Lt : 0.0f;
   }
 }
 
