@@ -42,15 +42,17 @@ struct AttnLds {
   float q[R][128];       // query tile (fp16 values in binary32)
   float qg[R][4];        // sum of the query over each K channel group
   // channel-axis K: per wave, the block's scaled query as MFMA A-operand
-  // entries [hi / lo][k-step s][query m][lane group q4] (see attend_wave)
+  // entries [hi / lo][k-step s][query m][lane group q4] (see attend_wave);
+  // row R stays zero for the A-operand rows that hold no query
   struct __attribute__((aligned(16))) QTab {
-    u4_t e[2][4][R][4];
+    u4_t e[2][4][R + 1][4];
   };
   // (a placeholder of one entry's alignment when K has token-axis groups)
   struct Empty {};
   typename std::conditional<CHANK_, QTab[kNW], Empty>::type qtab;
   struct __attribute__((aligned(16))) Wave {
-    unsigned short w[NGV][2][R][kTile];  // softmax weights hi / lo, [V group][query][token]
+    // softmax weights hi / lo, [V group][query][token]; row R as in QTab
+    unsigned short w[NGV][2][R + 1][kTile];
   };
   struct Rec {
     float o[R][128 + 2];  // per query: output sum, then m, l
@@ -174,6 +176,16 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
   const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
   const int aq = QRW::arow_query(n16);  // query of this lane's A-operand row (-1: zero row)
   auto& W = L.u.wave[wave];
+  // A-operand rows that hold no query (4 query rows) read row R of the
+  // wave's LDS tables, kept zero here (read only after the LDS waits below)
+  const int ar = aq < 0 ? R : aq;
+  if constexpr (QRW::DIAG) {
+    if (lane < 8 * NGV)
+      *reinterpret_cast<u4_t*>(&W.w[lane >> 3][(lane >> 2) & 1][R][8 * (lane & 3)]) = u4_t{0u, 0u, 0u, 0u};
+    if constexpr (CHANK) {
+      if (lane < 32) L.qtab[wave].e[lane >> 4][(lane >> 2) & 3][R][lane & 3] = u4_t{0u, 0u, 0u, 0u};
+    }
+  }
   const int tb = t0 & ~(kTile * TPS - 1);
   // the running output is held in natural units between calls; inside, block
   // j accumulates with the codec's factor fac(j)
@@ -292,8 +304,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             const u4_t kb = kr[nb].slice(s);
-            u4_t qh = T.e[0][s][max(aq, 0)][q4], ql = T.e[1][s][max(aq, 0)][q4];
-            if (aq < 0) qh = ql = u4_t{0u, 0u, 0u, 0u};
+            const u4_t qh = T.e[0][s][ar][q4], ql = T.e[1][s][ar][q4];
             c = mfma(qh, kb, c);
             c = mfma(ql, kb, c);
           }
@@ -406,14 +417,10 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       wave_lds_sync();
       // ---- O += W V ----
       u4_t wa[NGV][2];
-      const int mr = max(aq, 0);
 #pragma unroll
       for (int g = 0; g < NGV; ++g)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          wa[g][h] = *reinterpret_cast<const u4_t*>(&W.w[g][h][mr][8 * q4]);
-          if (aq < 0) wa[g][h] = u4_t{0u, 0u, 0u, 0u};
-        }
+        for (int h = 0; h < 2; ++h) wa[g][h] = *reinterpret_cast<const u4_t*>(&W.w[g][h][ar][8 * q4]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         constexpr int JPG = 8 / NGV;
