@@ -528,6 +528,33 @@ def test_edges_empty_single_and_flags():
     assert np.array_equal(got[:, :, S - 1], oc_k[:, :, 0])
 
 
+def test_many_splits_merge():
+    """More splits than one round of the merge's loads (128): 313 splits of 64 tokens, the second
+    sequence shorter so that 172 of its splits are empty; against the oracle and the one-split result."""
+    B, H, T, S = 2, 2, 20000, 20032
+    print("case many splits T=%d" % T, flush=True)
+    w = synth.scaled(synth.WORKLOADS[2], batch=B, kv_heads=H, q_heads=H, seq=T, tokens=T)
+    k, v, q = w.kv(0), w.kv(1), w.q()
+    cache = K.QuantKVCache(B, H, S, K.KVQ_MODE_UNIFORM, k_bits=8, symmetric=True, k_group=128)
+    K.kvq_quant_append(cache.desc, to_device(k), to_device(v), T, i32_device([0] * B))
+    torch.cuda.synchronize()
+    assert cache.flags() == 0
+    deq = {}
+    for name, x in (("k", k), ("v", v)):
+        oc, os_, oz = oracle.quant_rows(x, 128, 8, True)
+        deq[name] = oracle.dequant_rows(oc, os_, oz, 128, True)
+    seq_len = [T, 9000]
+    refs = np.stack([oracle.attention(q[b], deq["k"][b][:, :L], deq["v"][b][:, :L], SM)
+                     for b, L in enumerate(seq_len)])
+    one = run_decode(cache, q, H, seq_len, T, 1)
+    many = run_decode(cache, q, H, seq_len, T, 1000)  # planned as 313 splits of 64 tokens
+    check_attention(one, refs, "one split")
+    check_attention(many, refs, "313 splits")
+    # the unsplit run sums 5000 tokens per wave in binary32 (the 313-split run 64), so the two
+    # agree to the implementation bar rather than to the 1e-5 of the short invariance test below
+    assert float(rel_err_rows(many, one).max()) <= ATTN_TIGHT
+
+
 def test_decode_deterministic_and_split_invariant():
     B, H, T, S = 2, 4, 1000, 1024
     w = synth.scaled(synth.WORKLOADS[2], batch=B, kv_heads=H, q_heads=H, seq=T, tokens=T)
