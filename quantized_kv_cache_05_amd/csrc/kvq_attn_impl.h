@@ -140,15 +140,33 @@ __device__ __forceinline__ void load_zsub(const TokView& vv, long long r0, u4_t 
   }
 }
 
-// Sum / max over the 16 lanes of a row group (lanes differing in bits 0-3).
+// Sum / max over the 16 lanes of a row group (lanes differing in bits 0-3),
+// with DPP lane exchanges inside the 16-lane rows (no LDS round trip):
+// quad_perm [1,0,3,2] and [2,3,0,1] pair the lanes of each quad,
+// row_half_mirror (lane i <-> 7 - i of each 8-lane half) the two quads of a
+// half, row_mirror (lane i <-> 15 - i) the two halves.  Each exchange pairs
+// every lane with the mirror lane of the other part, so after the four all
+// 16 lanes hold the same total (the operations are commutative, the order
+// of the partial sums is the same on every lane).  Callers run the whole
+// wave (a DPP read of an inactive lane would give 0).
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF,
+                                                               false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 __device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m, 64);
+  v += dpp_row<kDppXor1>(v);
+  v += dpp_row<kDppXor2>(v);
+  v += dpp_row<kDppHalfMirror>(v);
+  v += dpp_row<kDppMirror>(v);
   return v;
 }
 __device__ __forceinline__ float max16(float v) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  v = fmaxf(v, dpp_row<kDppXor1>(v));
+  v = fmaxf(v, dpp_row<kDppXor2>(v));
+  v = fmaxf(v, dpp_row<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_row<kDppMirror>(v));
   return v;
 }
 
