@@ -169,6 +169,16 @@ __device__ __forceinline__ float max16(float v) {
   v = fmaxf(v, dpp_row<kDppMirror>(v));
   return v;
 }
+// Sum over the 4 lanes of each quad (DPP), and lane 0's value as a
+// wave-uniform scalar (the whole wave active).
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp_row<kDppXor1>(v);
+  v += dpp_row<kDppXor2>(v);
+  return v;
+}
+__device__ __forceinline__ float lane0(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
 
 // ---------------------------------------------------------------------------
 // One wave's share of a token range [t0, t1) of one (b, kv head): tiles of 32
@@ -267,18 +277,19 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       }
       // sum the entries of each query: lanes of query m differ in q4e (bits 0-1)
       // and, for R <= 4, in the k-step (the bits above the query's)
-      part += __shfl_xor(part, 1, 64);
-      part += __shfl_xor(part, 2, 64);
       if constexpr (R == 1) {
-        part += __shfl_xor(part, 4, 64);
-        part += __shfl_xor(part, 8, 64);
-      } else if constexpr (R == 4) {
-        part += __shfl_xor(part, 16, 64);
-        part += __shfl_xor(part, 32, 64);
+        part = sum16(part);  // the entries sit in lanes 0-15
+      } else {
+        part = quad_sum(part);
+        if constexpr (R == 4) {
+          part += __shfl_xor(part, 16, 64);
+          part += __shfl_xor(part, 32, 64);
+        }
       }
       // the sum of query m sits in lane 4 m (R > 1) or lane 0 (R == 1)
 #pragma unroll
-      for (int i = 0; i < GI; ++i) cbias[i] = __shfl(part, R == 1 ? 0 : 4 * QRW::slot_query(q4, i), 64);
+      for (int i = 0; i < GI; ++i)
+        cbias[i] = R == 1 ? lane0(part) : __shfl(part, 4 * QRW::slot_query(q4, i), 64);
       wave_lds_sync();
     }
 #pragma unroll

@@ -214,19 +214,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       // the entries of query m differ in qe (bits 0-1) and, for R <= 4, in the
       // k-step (the bits above the query's); its sum ends in lane 4 m (lane 0
       // when R == 1)
-      part += __shfl_xor(part, 1, 64);
-      part += __shfl_xor(part, 2, 64);
       if constexpr (R == 1) {
-        part += __shfl_xor(part, 4, 64);
-        part += __shfl_xor(part, 8, 64);
-      } else if constexpr (R == 4) {
-        part += __shfl_xor(part, 16, 64);
-        part += __shfl_xor(part, 32, 64);
+        part = sum16(part);  // every 16-lane row holds all 16 entries
+      } else {
+        part = quad_sum(part);
+        if constexpr (R == 4) {
+          part += __shfl_xor(part, 16, 64);
+          part += __shfl_xor(part, 32, 64);
+        }
       }
     }
     float qs[GI];
 #pragma unroll
-    for (int i = 0; i < GI; ++i) qs[i] = __shfl(part, R == 1 ? 0 : 4 * QRW::slot_query(q4, i), 64);
+    for (int i = 0; i < GI; ++i) qs[i] = R == 1 ? lane0(part) : __shfl(part, 4 * QRW::slot_query(q4, i), 64);
     *reinterpret_cast<float2*>(&vscl[wave][2 * lane]) = vs2;
     wave_lds_sync();
     f4_t c = zero4;
