@@ -103,8 +103,10 @@ def test_paged_full():
     assert codes.numel() == pool * H * P * 128
 
 
-def test_e4m3_full():
-    wl, out = run_bench_step(6)
+@pytest.mark.parametrize("idx,fmt", [(6, "e4m3"), (9, "e5m2")])
+def test_fp8_full(idx, fmt):
+    quant_rows, dequant_rows = getattr(oracle, "quant_rows_" + fmt), getattr(oracle, "dequant_rows_" + fmt)
+    wl, out = run_bench_step(idx)
     w = wl.w
     B, H, T, G = w.batch, w.kv_heads, w.tokens, w.q_heads // w.kv_heads
     c = wl.caches[0]
@@ -113,14 +115,14 @@ def test_e4m3_full():
         deq = {}
         for name, tensor in (("k", 0), ("v", 1)):
             x = w.kv(tensor, b, b + 1, h, h + 1)[0, 0]
-            oc, os_ = oracle.quant_rows_e4m3(x, 128)
+            oc, os_ = quant_rows(x, 128)
             got = unpack_layout(bh(c.buf(name + ".codes"), B, H, b, h).reshape(S, 128)[:T], 8, name.upper())
             assert np.array_equal(got, oc), (name, b, h)
             gs = bh(c.buf(name + ".scale"), B, H, b, h, np.float32).reshape(S, 1)[:T]
             assert np.array_equal(f32bits(gs), f32bits(os_)), (name, b, h)
-            deq[name] = oracle.dequant_rows_e4m3(oc, os_, 128)
+            deq[name] = dequant_rows(oc, os_, 128)
         q = w.q(b, b + 1)[0]
-        check_rows(out, b, h, G, q, deq["k"], deq["v"], "workload 6")
+        check_rows(out, b, h, G, q, deq["k"], deq["v"], "workload %d" % idx)
 
 
 @pytest.mark.parametrize("idx", [1, 2])
