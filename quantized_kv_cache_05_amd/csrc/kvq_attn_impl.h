@@ -149,12 +149,6 @@ __device__ __forceinline__ void load_zsub(const TokView& vv, long long r0, u4_t 
 // 16 lanes hold the same total (the operations are commutative, the order
 // of the partial sums is the same on every lane).  Callers run the whole
 // wave (a DPP read of an inactive lane would give 0).
-template <int CTRL>
-__device__ __forceinline__ float dpp_row(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF,
-                                                               false));
-}
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 __device__ __forceinline__ float sum16(float v) {
   v += dpp_row<kDppXor1>(v);
   v += dpp_row<kDppXor2>(v);

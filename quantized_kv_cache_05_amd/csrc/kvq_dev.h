@@ -24,6 +24,22 @@ __device__ __forceinline__ float hi_h2f(uint32_t w) { return h2f((uint16_t)(w >>
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 __device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// DPP lane exchange inside 16-lane rows (no LDS round trip): lane i reads
+// lane i ^ 1 (quad_perm [1,0,3,2]), i ^ 2 (quad_perm [2,3,0,1]), 7 - i of its
+// 8-lane half (row_half_mirror) or 15 - i of its row (row_mirror).  A
+// reduction that applies them in this order pairs each lane with the mirror
+// of the part it has already combined, so it covers lanes differing in bits
+// 0-1, 0-2 or 0-3 like the xor exchanges 1, 2, 4, 8.  Callers keep every
+// lane of a 16-lane row active (a read of an inactive lane gives 0).
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF,
+                                                               false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int M>
+constexpr int dpp_step() { return M == 1 ? kDppXor1 : M == 2 ? kDppXor2 : M == 4 ? kDppHalfMirror : kDppMirror; }
+
 // Sum / max over the lanes that differ only in bits [lo_bit, hi_bit) of the lane id.
 template <int LO, int HI>
 __device__ __forceinline__ float sum_lanes(float v) {
@@ -31,16 +47,32 @@ __device__ __forceinline__ float sum_lanes(float v) {
   for (int m = LO; m < HI; m <<= 1) v += shfl_xor_f(v, m);
   return v;
 }
+// max / min are exact in any order: within a 16-lane row (LO = 1, HI <= 16)
+// through DPP, otherwise through lane permutes
 template <int LO, int HI>
 __device__ __forceinline__ float max_lanes(float v) {
+  if constexpr (LO == 1 && HI <= 16) {
+    if constexpr (HI > 1) v = fmaxf(v, dpp_row<dpp_step<1>()>(v));
+    if constexpr (HI > 2) v = fmaxf(v, dpp_row<dpp_step<2>()>(v));
+    if constexpr (HI > 4) v = fmaxf(v, dpp_row<dpp_step<4>()>(v));
+    if constexpr (HI > 8) v = fmaxf(v, dpp_row<dpp_step<8>()>(v));
+  } else {
 #pragma unroll
-  for (int m = LO; m < HI; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
+    for (int m = LO; m < HI; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  }
   return v;
 }
 template <int LO, int HI>
 __device__ __forceinline__ float min_lanes(float v) {
+  if constexpr (LO == 1 && HI <= 16) {
+    if constexpr (HI > 1) v = fminf(v, dpp_row<dpp_step<1>()>(v));
+    if constexpr (HI > 2) v = fminf(v, dpp_row<dpp_step<2>()>(v));
+    if constexpr (HI > 4) v = fminf(v, dpp_row<dpp_step<4>()>(v));
+    if constexpr (HI > 8) v = fminf(v, dpp_row<dpp_step<8>()>(v));
+  } else {
 #pragma unroll
-  for (int m = LO; m < HI; m <<= 1) v = fminf(v, shfl_xor_f(v, m));
+    for (int m = LO; m < HI; m <<= 1) v = fminf(v, shfl_xor_f(v, m));
+  }
   return v;
 }
 
