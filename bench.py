@@ -16,7 +16,7 @@ Workloads (seeded synthetic fp16 K/V, head_dim 128; ``--workload N``):
               FP16 / INT4 / INT2 (groups of 32) by query-chunk cosine
               similarity and reordered contiguous by class; step = 1 chunked
               decode query per head
-  5 oaken     batch 256, 40 heads, 2048 tokens of 0.5 * Student-t(3);
+  5 oaken     (default) batch 256, 40 heads, 2048 tokens of 0.5 * Student-t(3);
               thresholds from a 100-sequence calibration set; dense INT4 +
               sparse shifted outer values; step = append 1 token per
               sequence + 1 decode query per head
@@ -33,9 +33,12 @@ Workloads (seeded synthetic fp16 K/V, head_dim 128; ``--workload N``):
               difference from the significant mean); step = 1 decode query
               per head
 
-Prints one JSON line.  value = algorithmic bytes of a step (packed cache and
-metadata read by decode, query read, output written, appended tokens read
-and written) per second of step time, in GB/s.  roofline = the decode kernel
+Prints one JSON line for the headline workload (--workload, default 5, the
+largest configuration), with configurations 1-5 each measured in the same run
+and summarized under "configs" (--headline-only skips them).  value =
+algorithmic bytes of a step (packed cache and metadata read by decode, query
+read, output written, appended tokens read and written) per second of step
+time, in GB/s.  roofline = the decode kernel
 alone: its algorithmic bytes over its average duration (HIP events on the
 stream it runs on) against the 8 TB/s HBM peak.  Quantize throughput is in
 tokens/s, a token being one sequence position over all KV heads, K and V.
@@ -67,7 +70,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9])
+    p.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9],
+                   help="the workload of the headline value (default 5, the largest configuration)")
+    p.add_argument("--headline-only", action="store_true",
+                   help="measure the headline workload only (by default configurations 1-5 are all "
+                        "measured and reported under 'configs')")
     p.add_argument("--num-splits", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=16.0,
                    help="budget of the CPU-oracle leg (half single-threaded, half all threads)")
@@ -521,7 +528,8 @@ def _oracle_job(idx, b, h, thr):
 
 def cpu_baseline(w, idx, budget_s):
     """The oracle on (batch, kv head) slices: half the budget on one thread, half on worker
-    processes (one per available core, at most 16).  Runs before the GPU is initialised."""
+    processes (one per available core, at most 16: the host share of one GPU).  Runs before the
+    GPU is initialised.  Reports the workers used, the host's core count and CPU model."""
     import multiprocessing as mp
     from concurrent.futures import ProcessPoolExecutor, wait, FIRST_COMPLETED
 
@@ -580,10 +588,22 @@ def cpu_baseline(w, idx, budget_s):
     # their summed per-slice times; generation is not part of the oracle's rate
     wall_dec = wall * td_m / (tq_m + td_m + tg_m)
     wall_q = wall * tq_m / (tq_m + td_m + tg_m)
+    model = "?"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(nb_m / wall_dec / 1e9, 4),
         "unit": "GB/s",
         "cores": workers,
+        "host_cores": os.cpu_count(),
+        "cores_available": avail,
+        "cpu_model": model,
         "kind": "oracle",
         "sample": "%d of %d (batch, kv-head) slices of %d tokens on %d worker processes, %d slices on "
                   "one thread: oracle quantize + dequantize + binary64 attention%s" % (
@@ -724,51 +744,15 @@ def summarize_stats(stats_csv, bench_log):
 
 # ---------------------------------------------------------------------------
 
-def main():
-    global ARGS
-    ARGS = args = parse()
-    if args.summarize_stats:
-        summarize_stats(*args.summarize_stats)
-        return
-    if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, args.copy_probe_mib or 1024)
-        return
-    if args.gpus != 1:
-        print("bench.py measures one GPU (--gpus 1); runs on several GPUs are not part of this "
-              "library's scope", file=sys.stderr)
-        sys.exit(2)
+def measure(idx, steps, warmup, torch, K, synth, stream):
+    """Set up workload idx, time its bulk prefill quantize and `steps` steps (append + decode) after
+    `warmup` untimed ones; returns the per-workload figures.  Device memory is released on return."""
     import numpy as np
-
-    import synth
-
-    cpu = None
-    if not args.no_cpu:
-        t = time.perf_counter()
-        cpu = cpu_baseline(synth.WORKLOADS[args.workload], args.workload, args.cpu_seconds)
-        log("cpu oracle leg %.1fs: %s" % (time.perf_counter() - t, cpu))
-
-    import torch
-
-    import quantized_kv_cache_05_amd as K
-
-    torch.cuda.set_device(0)
-    stream = torch.cuda.current_stream()
-    idx = args.workload
     t = time.perf_counter()
     wl = build_workload(idx, torch, K, synth)
     torch.cuda.synchronize()
     log("workload %d set up in %.1fs (%d cache cop%s)" % (idx, time.perf_counter() - t, wl.rotate,
                                                         "y" if wl.rotate == 1 else "ies"))
-
-    if args.copy_probe_mib:
-        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
     # bulk prefill (quantize-append of the whole prompt); fills every cache copy
     for r in range(wl.rotate):
         wl.prefill(r)
@@ -793,13 +777,13 @@ def main():
         if ev_b is not None:
             ev_b.record(stream)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     flags = wl.flags()
     assert not any(flags), "device status flags %s" % flags
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+           for _ in range(steps)]
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     s0.record(stream)
@@ -807,7 +791,7 @@ def main():
         step(i, a, b)
     s1.record(stream)
     torch.cuda.synchronize()
-    step_ms = s0.elapsed_time(s1) / args.steps
+    step_ms = s0.elapsed_time(s1) / steps
     dec_times = [a.elapsed_time(b) for a, b in evs]
     dec_ms = float(np.mean(dec_times))
     dbytes = wl.decode_bytes()
@@ -820,42 +804,127 @@ def main():
     append_tok_s = app_tokens / (app_ms / 1e3) if (idx in (1, 2, 5, 6, 7, 9) and app_ms > 0) else None
     log("step %.4f ms, decode %.4f ms (median %.4f) -> %.1f GB/s (%.1f%% of peak)"
         % (step_ms, dec_ms, float(np.median(dec_times)), achieved, 100 * achieved / HBM_PEAK_GBS))
+    res = {
+        "workload": WORKLOAD_TEXT[idx],
+        "batch": w.batch, "kv_heads": w.kv_heads, "q_heads": w.q_heads, "seq_len": w.tokens,
+        "cache_copies": wl.rotate,
+        "steps": steps,
+        "value": value,
+        "ms_per_step": step_ms,
+        "decode_ms": dec_ms,
+        "decode_bytes": int(dbytes),
+        "decode_gbs": achieved,
+        "quant_prefill_tokens_per_s": bulk_tok_s,
+        "quant_prefill_ms": bulk_ms,
+        "quant_append_tokens_per_s": append_tok_s,
+    }
+    del wl
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
-    traffic = stored_traffic(idx)
+
+def config_summary(idx, r):
+    """The compact per-configuration record carried in the JSON line."""
+    return {
+        "workload": WORKLOAD_TEXT[idx].split(":")[0],
+        "decode_ms": round(r["decode_ms"], 5),
+        "decode_bytes": r["decode_bytes"],
+        "decode_gbs": round(r["decode_gbs"], 1),
+        "frac_hbm_peak": round(r["decode_gbs"] / HBM_PEAK_GBS, 4),
+        "quant_prefill_tokens_per_s": round(r["quant_prefill_tokens_per_s"], 1),
+        "quant_append_tokens_per_s": (round(r["quant_append_tokens_per_s"], 1)
+                                      if r["quant_append_tokens_per_s"] else None),
+        "traffic": stored_traffic(idx),
+    }
+
+
+def main():
+    global ARGS
+    ARGS = args = parse()
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.copy_probe_mib or 1024)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU (--gpus 1); runs on several GPUs are not part of this "
+              "library's scope", file=sys.stderr)
+        sys.exit(2)
+
+    import synth
+
+    cpu = None
+    if not args.no_cpu:
+        t = time.perf_counter()
+        cpu = cpu_baseline(synth.WORKLOADS[args.workload], args.workload, args.cpu_seconds)
+        log("cpu oracle leg %.1fs: %s" % (time.perf_counter() - t, cpu))
+
+    import torch
+
+    import quantized_kv_cache_05_amd as K
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    idx = args.workload
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    head = measure(idx, args.steps, args.warmup, torch, K, synth, stream)
+    configs = {}
+    if not args.headline_only:
+        # the other configurations of the metric, each set up, measured and released in turn
+        for j in (1, 2, 3, 4, 5):
+            if j == idx:
+                configs[str(j)] = config_summary(j, head)
+                continue
+            configs[str(j)] = config_summary(j, measure(j, min(args.steps, 20), min(args.warmup, 5),
+                                                        torch, K, synth, stream))
+    achieved = head["decode_gbs"]
     res = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(head["value"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 5),
+        "ms_per_step": round(head["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_TEXT[idx],
-            "batch": w.batch, "kv_heads": w.kv_heads, "q_heads": w.q_heads, "seq_len": w.tokens,
-            "num_splits": args.num_splits, "cache_copies": wl.rotate,
+            "workload": head["workload"],
+            "batch": head["batch"], "kv_heads": head["kv_heads"], "q_heads": head["q_heads"],
+            "seq_len": head["seq_len"], "num_splits": args.num_splits, "cache_copies": head["cache_copies"],
         },
-        "decode_ms": round(dec_ms, 5),
-        "decode_bytes": int(dbytes),
+        "decode_ms": round(head["decode_ms"], 5),
+        "decode_bytes": head["decode_bytes"],
         "decode_gbs": round(achieved, 1),
         "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
-        "quant_prefill_tokens_per_s": round(bulk_tok_s, 1),
-        "quant_prefill_ms": round(bulk_ms, 4),
-        "quant_append_tokens_per_s": round(append_tok_s, 1) if append_tok_s else None,
+        "quant_prefill_tokens_per_s": round(head["quant_prefill_tokens_per_s"], 1),
+        "quant_prefill_ms": round(head["quant_prefill_ms"], 4),
+        "quant_append_tokens_per_s": (round(head["quant_append_tokens_per_s"], 1)
+                                      if head["quant_append_tokens_per_s"] else None),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
+            "traffic": stored_traffic(idx),
         },
         "cpu_baseline": cpu,
+        "configs": configs or None,
     }
     print(json.dumps(res), flush=True)
 
