@@ -302,7 +302,7 @@ class Oaken(Workload):
         self.kx, self.vx = upload_kv(w, 0, torch), upload_kv(w, 1, torch)
         self.k_new = self.kx[:, :, T - 1:].contiguous()
         self.v_new = self.vx[:, :, T - 1:].contiguous()
-        cap = int(T * 128 * 0.08)  # outer share is ~5 % by construction of the thresholds
+        cap = int(T * 128 * 0.08) // 4 * 4  # outer share ~5 % by construction of the thresholds
         self.caches = [K.QuantKVCache(B, H, T, K.KVQ_MODE_OAKEN, k_bits=4, k_group=64, k_thr=self.thr[0],
                                       v_thr=self.thr[1], sparse_cap=cap)]
         self.q = torch.from_numpy(w.q().view("int16")).cuda()

@@ -45,7 +45,8 @@ typedef enum kvq_status {
   KVQ_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent field */
   KVQ_ERR_UNSUPPORTED = -2, /* valid but not implemented (head_dim != 128, ...) */
   KVQ_ERR_CAPACITY = -3,    /* t_new or max_len larger than the cache holds */
-  KVQ_ERR_ALIGNMENT = -4,   /* a device pointer is not aligned as required */
+  KVQ_ERR_ALIGNMENT = -4,   /* a device pointer is not aligned as required, or an OAKEN
+                               sparse_cap is not a multiple of 4 */
   KVQ_ERR_WORKSPACE = -5,   /* decode workspace missing or too small */
   KVQ_ERR_HIP = -6          /* a HIP launch failed */
 } kvq_status;
@@ -186,7 +187,9 @@ typedef struct kvq_tensor {
   int32_t format;     /* KVQ_FMT_INT or KVQ_FMT_E4M3 */
   float thr[4];       /* OAKEN: T_lo_outer, T_lo_inner, T_hi_inner, T_hi_outer (inner ones
                          are informational; [Oaken] §3.2.1) */
-  int64_t sparse_cap; /* OAKEN: capacity of `sparse` per (b, h), in entries */
+  int64_t sparse_cap; /* OAKEN: capacity of `sparse` per (b, h), in entries; a multiple
+                         of 4, so that every (b, h) list starts 8-byte aligned (decode
+                         reads four entries per load); else KVQ_ERR_ALIGNMENT */
   void* codes;
   float* scale;
   uint8_t* zero;

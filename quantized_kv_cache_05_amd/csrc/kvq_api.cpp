@@ -70,6 +70,8 @@ kvq_status check_config(const kvq_cache* c) {
         if (!std::isfinite(t->thr[0]) || !std::isfinite(t->thr[3]) || !(t->thr[0] < t->thr[3]))
           return KVQ_ERR_INVALID_ARG;
         if (t->sparse_cap < 0 || t->sparse_cap > 0xFFFFFFFFll) return KVQ_ERR_INVALID_ARG;
+        // lists start 8-byte aligned: decode reads them four entries per load
+        if (t->sparse_cap % 4) return KVQ_ERR_ALIGNMENT;
       }
       if (k.group != v.group) return KVQ_ERR_UNSUPPORTED;
       return KVQ_OK;
@@ -285,11 +287,6 @@ kvq_status plan_decode(const kvq_cache* c, int q_heads, int max_len, int num_spl
   if (ns > length) ns = length;
   long long piece = (length + ns - 1) / ns;
   piece = (piece + align - 1) / align * align;
-  if (c->mode == KVQ_MODE_OAKEN) {
-    // the Oaken kernel keeps one score slot per (query, token) of a split in LDS
-    const long long most = kvq::oaken_max_split(p->qr);
-    if (piece > most) piece = most;
-  }
   ns = (length + piece - 1) / piece;
   if (ns > 65535) return KVQ_ERR_UNSUPPORTED;
   p->num_splits = (int)ns;

@@ -443,6 +443,7 @@ struct TokView {
   int prow;              // rows of a page over all heads: H << pshift
   int npages;
   unsigned* status;
+  const float* oscale = nullptr;  // Oaken: outer scales [rows][ng], rows as `scale`
 };
 
 // Row offset that maps the tokens t of the page-aligned range starting at
@@ -463,6 +464,7 @@ __device__ __forceinline__ TokView at_rows(const TokView& v, long long off) {
   r.codes = v.codes + off * RB;
   r.scale = v.scale + off * NG;
   if (v.zero) r.zero = v.zero + off * NG;
+  if (v.oscale) r.oscale = v.oscale + off * NG;
   return r;
 }
 
@@ -470,20 +472,6 @@ __device__ __forceinline__ TokView at_rows(const TokView& v, long long off) {
 struct ChanView {
   const float* scale;   // [S/64][128]
   const uint8_t* zero;  // [S/64][128]
-};
-
-// Oaken sparse side list of one tensor for a (b, kv head).  The outer scales
-// are per token row of the dense body: contiguous rows of this (b, h), or,
-// paged, the pool base with token t in row
-// pages[t >> pshift] * prow + hrow + (t mod 2^pshift).
-struct SparseView {
-  const float* oscale;    // [rows][ng]
-  const uint32_t* rowptr; // [S + 1]
-  const uint16_t* sparse; // [cap]
-  unsigned cap;
-  float t_lo, t_hi;
-  const int* pages = nullptr;  // paged: this sequence's block-table row
-  int pshift = 0, hrow = 0, prow = 0, npages = 0;
 };
 
 // Running softmax state of a wave (lane-held, see the header comment).

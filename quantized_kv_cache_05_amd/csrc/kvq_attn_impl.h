@@ -175,6 +175,324 @@ __device__ __forceinline__ float lane0(float v) {
 }
 
 // ---------------------------------------------------------------------------
+// Oaken sparse side lists, consumed inside the tile loop.  Reconstruction
+// ([Oaken] §3.2.2): an outer value is T_hi + mag * s_out above the upper outer
+// threshold and T_lo - mag * s_out below the lower one; the dense code at an
+// outer position is the zero-point, so the dense part there is exactly 0 and
+// the outer values only add.  The row pointers of the next tile are loaded
+// one tile ahead, so the entry loads go out with the tile's code loads.  No
+// LDS atomics are used (they cost about as much as the rest of the tile), and
+// every sum is taken in a fixed order, so decode is deterministic.
+//
+// K (score part of each row).  The 32 rows of a tile own the contiguous
+// range [rp[tile], rp[tile + 32]) of the row-major entry list; a lane takes
+// 4 consecutive entries (one 8-byte load, 256 entries per round).  Per query,
+// each entry contributes u = q[idx] T_side and w = q[idx] (+-mag), the latter
+// kept per channel group g; exclusive prefix sums of u and of each w_g over
+// the round (inside the lane, then across the wave by DPP) go to LDS, and the
+// lane of row r forms its sum from two differences per array:
+//   sum_{e in row r} q[idx] x_hat = dU + sum_g s_out[r][g] dW_g,
+// so no entry needs to know its row.
+//
+// V (outer-value output).  The entries of rows 8k .. 8k + 7 (octet k) take
+// one lane each (one 2-byte load per octet).  The row of an entry comes from
+// one-hot row markers (bit r mod 8 at the slot of the row's first entry,
+// byte k for octet k) and a prefix OR across the wave: the highest bit set is
+// the last row started.  Within an octet two entries share an address of the
+// outer-value output only if they share row and channel, which a row's list
+// never does, so with one output copy per row mod 8 every octet updates its
+// copies by a plain read-modify-write with no conflicts; octets follow one
+// another in program order.  The copies are summed when the wave records its
+// result.  With 16 query rows a single copy is kept and each octet is applied
+// one row at a time.
+
+template <int QR>
+constexpr int kOakCopies = QR == 16 ? 1 : 8;
+
+template <int QR, int NG>
+struct __attribute__((aligned(16))) OakWave {
+  float ex[NG + 1][264];               // K: exclusive prefix sums over a round's entries, [256] = total
+  float so[kTile][NG];                 // V: outer scales of the tile's rows
+  float ksc[QR][kTile];                // outer-value part of each query's score, per row
+  float pr[QR][kTile];                 // softmax numerators, per query and row
+  unsigned mk[64];                     // V: one-hot row markers, byte k for octet k
+  float pad[64];                       // per-lane sink of masked updates
+  float osp[kOakCopies<QR>][QR][128];  // outer-value output per copy (row mod 8), wave frame
+};
+
+// One tensor's side list for a (b, kv head).
+struct OakList {
+  const uint32_t* rowptr;  // [S + 1]
+  const uint16_t* sparse;  // [cap]; cap a multiple of 4, so the list is 8-byte aligned
+  unsigned cap;            // 0: no list (sparse then points at 4 readable dummy entries)
+  float t_lo, t_hi;
+};
+
+template <int QR, int NG>
+struct OakCtx {
+  OakList l[2];            // K, V
+  OakWave<QR, NG>* w;      // this wave's LDS area
+};
+struct NoOak {};
+
+// Row pointers of one tile for a lane: lane l holds rp of rows l mod 32 and
+// l mod 32 + 1 (both halves of the wave the same rows), row indices clamped
+// to [t0, t1] so that rows outside the split own no entries.
+struct OakRp {
+  unsigned a[2], b[2];
+};
+
+__device__ __forceinline__ OakRp oak_rp_load(const OakList (&l)[2], int tile, int t0, int t1) {
+  const int r = (int)(threadIdx.x & 31);
+  const int ia = min(max(tile + r, t0), t1), ib = min(max(tile + r + 1, t0), t1);
+  OakRp p;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    p.a[x] = ld_nt<unsigned>(l[x].rowptr + ia);
+    p.b[x] = ld_nt<unsigned>(l[x].rowptr + ib);
+  }
+  return p;
+}
+
+// Entry loads through the global address space: the list pointer is one of
+// two globals, which the compiler would otherwise treat as a flat address
+// that might alias LDS, ordering every later LDS access behind the load.
+// Indices are clamped into the list (entries outside a range are masked by
+// the caller).
+__device__ __forceinline__ u2_t oak_words(const OakList& l, unsigned base, unsigned c) {
+  typedef const __attribute__((address_space(1))) u2_t gu2_t;
+  const unsigned wi = min((base >> 2) + 64u * c + (threadIdx.x & 63), max(l.cap >> 2, 1u) - 1u);
+  return __builtin_nontemporal_load((gu2_t*)(l.sparse + 4ull * wi));
+}
+__device__ __forceinline__ unsigned oak_entry(const OakList& l, unsigned e) {
+  typedef const __attribute__((address_space(1))) uint16_t gu16_t;
+  return __builtin_nontemporal_load((gu16_t*)(l.sparse + min(e, max(l.cap, 1u) - 1u)));
+}
+
+// 32-bit DPP move with old = 0 and bound_ctrl: lanes without a source read 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ unsigned dpp_u(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
+}
+// Inclusive prefix sum / OR in lane order over the wave: row_shr 1, 2, 4, 8
+// inside each 16-lane row, then row_bcast:15 (last lane of rows 0 and 2 into
+// rows 1 and 3) and row_bcast:31 (lane 31 into rows 2 and 3).  The sum's
+// order is fixed, so it is deterministic.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  auto f = [](unsigned x) { return __builtin_bit_cast(float, x); };
+  const auto u = [](float x) { return __builtin_bit_cast(unsigned, x); };
+  v += f(dpp_u<0x111>(u(v)));
+  v += f(dpp_u<0x112>(u(v)));
+  v += f(dpp_u<0x114>(u(v)));
+  v += f(dpp_u<0x118>(u(v)));
+  v += f(dpp_u<0x142, 0xA>(u(v)));
+  v += f(dpp_u<0x143, 0xC>(u(v)));
+  return v;
+}
+__device__ __forceinline__ unsigned wave_prefix_or(unsigned v) {
+  v |= dpp_u<0x111>(v);
+  v |= dpp_u<0x112>(v);
+  v |= dpp_u<0x114>(v);
+  v |= dpp_u<0x118>(v);
+  v |= dpp_u<0x142, 0xA>(v);
+  v |= dpp_u<0x143, 0xC>(v);
+  return v;
+}
+
+// x_hat of entry en (idx | side << 7 | mag << 8) with its row's outer scale,
+// one binary32 product and one sum as in the reconstruction rule.
+__device__ __forceinline__ float oak_value(unsigned en, float so, const OakList& l) {
+  const float step = __fmul_rn((float)((en >> 8) & 31u), so);
+  return (en & 128u) ? __fadd_rn(l.t_hi, step) : __fsub_rn(l.t_lo, step);
+}
+
+// K outer values of one tile: for each query m < nq, the sum over row r's
+// entries of q[m][idx] x_hat, into W.ksc[m][r].  rp: the tile's row pointers;
+// wd0: the lane's first round of entries (base = e0 rounded down to 4);
+// so_row: the outer scales of row lane & 31 (every lane computes a row; the
+// two halves of the wave write the same values).
+template <int QR, int NG, class LDS>
+__device__ __forceinline__ void oak_k_tile(const LDS& L, OakWave<QR, NG>& W, const OakList& l, const OakRp& rp,
+                                           u2_t wd0, unsigned e0, unsigned e1, unsigned base,
+                                           const float (&so_row)[NG], int nq) {
+  const unsigned lane = threadIdx.x & 63;
+  const unsigned ra = min(rp.a[0], l.cap), rb = min(rp.b[0], l.cap);
+  float acc[QR];
+#pragma unroll
+  for (int m = 0; m < QR; ++m) acc[m] = 0.0f;
+  for (unsigned c = 0; base + 256u * c < e1; ++c) {
+    const u2_t wd = c == 0 ? wd0 : oak_words(l, base, c);
+    const unsigned cb = base + 256u * c, e = cb + 4u * lane;
+    unsigned idx[4], grp[4];
+    float tv[4], sm[4];
+    bool ok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned word = wd[j >> 1];
+      const unsigned en = (j & 1) ? (word >> 16) : (word & 0xFFFFu);
+      idx[j] = en & 127u;
+      grp[j] = NG == 1 ? 0u : idx[j] / (128 / NG);
+      const bool hi = en & 128u;
+      const float mag = (float)((en >> 8) & 31u);
+      tv[j] = hi ? l.t_hi : l.t_lo;
+      sm[j] = hi ? mag : -mag;
+      ok[j] = e + j >= e0 && e + j < e1;
+    }
+    const unsigned s = min(max(ra, cb) - cb, 256u), t = min(max(rb, cb) - cb, 256u);
+#pragma unroll
+    for (int m = 0; m < QR; ++m) {
+      if (m < nq) {
+        float v[NG + 1][4];
+        float qr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qr[j] = L.q[m][idx[j]];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float qv = ok[j] ? qr[j] : 0.0f;
+          v[0][j] = qv * tv[j];
+          const float w = qv * sm[j];
+#pragma unroll
+          for (int g = 0; g < NG; ++g) v[1 + g][j] = grp[j] == (unsigned)g ? w : 0.0f;
+        }
+#pragma unroll
+        for (int a = 0; a <= NG; ++a) {
+          const float p1 = v[a][0], p2 = p1 + v[a][1], p3 = p2 + v[a][2], tot = p3 + v[a][3];
+          const float inc = wave_prefix_sum(tot), exc = inc - tot;
+          *reinterpret_cast<float4*>(&W.ex[a][4 * lane]) = float4{exc, exc + p1, exc + p2, exc + p3};
+          if (lane == 63) W.ex[a][256] = inc;
+        }
+        wave_lds_sync();
+        float d = W.ex[0][t] - W.ex[0][s];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) d = fmaf(so_row[g], W.ex[1 + g][t] - W.ex[1 + g][s], d);
+        acc[m] += d;
+        wave_lds_sync();  // the next pass rewrites ex
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < QR; ++m) W.ksc[m][lane & 31] = acc[m];
+}
+
+// V entries of one tile, before the softmax: the lane's entry of each octet
+// (k = 0..3), whether it lies in the octet's range, and its row in the tile.
+struct OakOct {
+  unsigned en[4];
+  unsigned row[4];
+  bool ok[4];
+  unsigned ro[5];   // octet boundaries in the list (wave-uniform)
+};
+
+template <int QR, int NG>
+__device__ __forceinline__ OakOct oak_v_prep(OakWave<QR, NG>& W, const OakList& l, const OakRp& rp) {
+  const unsigned lane = threadIdx.x & 63;
+  OakOct o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o.ro[k] = min((unsigned)__builtin_amdgcn_readlane((int)rp.a[1], 8 * k), l.cap);
+  o.ro[4] = min((unsigned)__builtin_amdgcn_readlane((int)rp.b[1], kTile - 1), l.cap);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o.en[k] = oak_entry(l, o.ro[k] + lane);
+    o.ok[k] = o.ro[k] + lane < o.ro[k + 1];
+  }
+  // one-hot markers: row lane r marks the slot of its first entry in octet r / 8
+  const unsigned ra = min(rp.a[1], l.cap), rb = min(rp.b[1], l.cap);
+  const unsigned oct = (lane >> 3) & 3;
+  W.mk[lane] = 0u;
+  unsigned ro_l = o.ro[0];
+#pragma unroll
+  for (int k = 1; k < 4; ++k)
+    if (oct == (unsigned)k) ro_l = o.ro[k];
+  const unsigned p = ra - ro_l;
+  if (lane < (unsigned)kTile && ra < rb && p < 64u)
+    reinterpret_cast<uint8_t*>(W.mk)[4 * p + oct] = (uint8_t)(1u << (lane & 7));
+  wave_lds_sync();
+  const unsigned orr = wave_prefix_or(W.mk[lane]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const unsigned byte = (orr >> (8 * k)) & 255u;
+    o.row[k] = 8u * k + (31u - (unsigned)__builtin_clz(byte | 1u));
+  }
+  return o;
+}
+
+// V entries after the softmax: p[m][row] x_hat into the wave's outer-value
+// output (copy row mod 8), octet by octet; entries past 64 in an octet take
+// further rounds (rare), with markers of their own.
+template <int QR, int NG>
+__device__ __forceinline__ void oak_v_apply_one(OakWave<QR, NG>& W, const OakList& l, unsigned en, unsigned row,
+                                                bool ok, int nq) {
+  const unsigned lane = threadIdx.x & 63, idx = en & 127u;
+  const float xh = oak_value(en, W.so[row][NG == 1 ? 0u : idx / (128 / NG)], l);
+  constexpr int NC = kOakCopies<QR>;
+#pragma unroll
+  for (int m = 0; m < QR; ++m) {
+    if (m < nq) {
+      const float val = W.pr[m][row] * xh;
+      if constexpr (NC == 8) {
+        float* a = ok ? &W.osp[row & 7][m][idx] : &W.pad[lane];
+        *a += ok ? val : 0.0f;
+      } else {  // one copy: one row of the octet at a time
+#pragma unroll
+        for (unsigned r = 0; r < 8; ++r) {
+          const bool mine = ok && (row & 7) == r;
+          float* a = mine ? &W.osp[0][m][idx] : &W.pad[lane];
+          *a += mine ? val : 0.0f;
+        }
+      }
+    }
+  }
+}
+
+template <int QR, int NG>
+__device__ __forceinline__ void oak_v_apply(OakWave<QR, NG>& W, const OakList& l, const OakRp& rp,
+                                            const OakOct& o, int nq) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) oak_v_apply_one<QR, NG>(W, l, o.en[k], o.row[k], o.ok[k], nq);
+  // octets with more than 64 entries (rare): further rounds of 64
+  const unsigned lane = threadIdx.x & 63;
+  const unsigned ra = min(rp.a[1], l.cap), rb = min(rp.b[1], l.cap);
+  for (int k = 0; k < 4; ++k) {
+    if (o.ro[k] + 64u >= o.ro[k + 1]) continue;
+    // the row of the round's last entry starts the next round
+    unsigned carry = 1u << (((unsigned)__builtin_amdgcn_readlane((int)o.row[k], 63)) & 7u);
+    for (unsigned c = 1; o.ro[k] + 64u * c < o.ro[k + 1]; ++c) {
+      const unsigned e = o.ro[k] + 64u * c + lane;
+      const unsigned en = oak_entry(l, e);
+      W.mk[lane] = 0u;
+      const unsigned p = ra - (o.ro[k] + 64u * c);
+      if (lane < (unsigned)kTile && (lane >> 3) == (unsigned)k && ra < rb && p < 64u)
+        reinterpret_cast<uint8_t*>(W.mk)[4 * p] = (uint8_t)(1u << (lane & 7));
+      wave_lds_sync();
+      const unsigned orr = wave_prefix_or(W.mk[lane] & 255u) | carry;
+      const unsigned row = 8u * k + (31u - (unsigned)__builtin_clz(orr));
+      oak_v_apply_one<QR, NG>(W, l, en, row, e < o.ro[k + 1], nq);
+      carry = 1u << (((unsigned)__builtin_amdgcn_readlane((int)row, 63)) & 7u);
+      wave_lds_sync();
+    }
+  }
+}
+
+template <int NG>
+__device__ __forceinline__ void load_f32s(const float* p, float (&v)[NG]) {
+  if constexpr (NG == 1) {
+    v[0] = ld_nt<float>(p);
+  } else if constexpr (NG == 2) {
+    const u2_t t = ld_nt<u2_t>(p);
+    const unsigned t0 = t[0], t1 = t[1];
+    v[0] = __builtin_bit_cast(float, t0);
+    v[1] = __builtin_bit_cast(float, t1);
+  } else {
+    const u4_t t = ld_nt<u4_t>(p);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const unsigned tg = t[g];
+      v[g] = __builtin_bit_cast(float, tg);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // One wave's share of a token range [t0, t1) of one (b, kv head): tiles of 32
 // tokens starting at tile-aligned offsets, taken round robin by the waves in
 // steps of TPS tiles.
@@ -182,15 +500,15 @@ __device__ __forceinline__ float lane0(float v) {
 //  KC / VC: codecs.  NGK / NGV: channel groups of K / V (token axis).
 //  CHANK: K has channel-axis groups of 64 tokens (scale folded into the query).
 //  PAGED: the views are paged (TokView), rebased for every tile.
-//  OAK: Oaken; oak_sc[m * oak_span + (t - t0)] holds the sparse outer-value
-//       part of query m's score for token t on entry and receives the final
-//       base-2 score (the V outer values are added after the loop).
+//  OAK: Oaken; oak holds the side lists and the wave's LDS area (OakCtx), the
+//       outer values enter the scores and the wave's outer-value output
+//       inside the loop (see OakWave).
 template <int QR, int NGK, int NGV, class KC, class VC, bool CHANK, bool OAK, int TPS, bool PAGED = false,
-          class LDS>
+          class LDS, class OK = NoOak>
 __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
                                             SoftState<QRows<QR>::GI>& st, const TokView& kv_,
-                                            const TokView& vv_, const ChanView& kc, float* oak_sc,
-                                            int oak_span, int nq, int t0, int t1, int wave,
+                                            const TokView& vv_, const ChanView& kc, const OK& oak,
+                                            int nq, int t0, int t1, int wave,
                                             const u4_t (&qop)[4]) {
   using QRW = QRows<QR>;
   constexpr int R = QR, GI = QRW::GI;
@@ -220,6 +538,9 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
   static_assert(!PAGED || kTile * TPS <= 64, "a step must stay inside one page");
   int pg_next = 0;
   if constexpr (PAGED) pg_next = kv_.pages[min(tb + wave * kTile * TPS, t1 - 1) >> kv_.pshift];
+  // Oaken: row pointers of the wave's next tile, one tile ahead
+  OakRp rp_next{};
+  if constexpr (OAK) rp_next = oak_rp_load(oak.l, tb + wave * kTile * TPS, t0, t1);
   for (int step = tb + wave * kTile * TPS; step < t1; step += kNW * kTile * TPS) {
     TokView kv = kv_, vv = vv_;
     if constexpr (PAGED) {
@@ -290,8 +611,33 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
     for (int tt = 0; tt < TPS; ++tt) {
       const int tile = step + tt * kTile;
       if (tile >= t1) break;
+      OakRp rpc{};
+      if constexpr (OAK) {
+        rpc = rp_next;
+        rp_next = oak_rp_load(oak.l, tt + 1 < TPS ? tile + kTile : step + kNW * kTile * TPS, t0, t1);
+      }
       if (tile + kTile <= t0) continue;
       // ---- loads ----
+      // Oaken: the tile's K entry range and first round of entries, its V
+      // entries (octets) and the rows' outer scales, issued ahead of the codes
+      unsigned ok_e0 = 0u, ok_e1 = 0u, ok_base = 0u;
+      u2_t ok_wd = u2_t{0u, 0u};
+      float oso[2][NGV];  // outer scales of row lane & 31, K and V
+      OakOct oct{};
+      if constexpr (OAK) {
+        const unsigned cap = oak.l[0].cap;
+        ok_e0 = min((unsigned)__builtin_amdgcn_readfirstlane((int)rpc.a[0]), cap);
+        ok_e1 = min((unsigned)__builtin_amdgcn_readlane((int)rpc.b[0], kTile - 1), cap);
+        ok_base = ok_e0 & ~3u;
+        ok_wd = oak_words(oak.l[0], ok_base, 0);
+        const long long t = tile + (lane & 31);
+        load_f32s<NGV>(kv.oscale + t * NGV, oso[0]);
+        load_f32s<NGV>(vv.oscale + t * NGV, oso[1]);
+        oct = oak_v_prep<QR, NGV>(*oak.w, oak.l[1], rpc);
+        // issued before the code loads, so that the entry work below waits on
+        // these alone (loads complete in order)
+        __builtin_amdgcn_sched_barrier(0);
+      }
       KC kr[2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) kr[nb].load(kv.codes + (long long)(tile + nb * 16 + n16) * KC::RB, q4);
@@ -317,6 +663,15 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       // -(OFF + z) of the B-operand rows as packed fp16 pairs, per V group
       u4_t zsub[2][NGV];
       if constexpr (VC::ZP) load_zsub<VC, NGV>(vv, tile + 8 * q4, zsub);
+      // ---- Oaken: the outer K values' share of each row's score ----
+      if constexpr (OAK) {
+        __builtin_amdgcn_sched_barrier(0);  // the code loads stay ahead of the entry work
+        auto& OW = *oak.w;
+#pragma unroll
+        for (int g = 0; g < NGV; ++g) OW.so[lane & 31][g] = oso[1][g];  // (both halves: same values)
+        oak_k_tile<QR, NGV>(L, OW, oak.l[0], rpc, ok_wd, ok_e0, ok_e1, ok_base, oso[0], nq);
+        wave_lds_sync();
+      }
       // ---- scores ----
       float sc[2][GI];
       if constexpr (CHANK) {
@@ -359,15 +714,14 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
           }
         }
       }
-      // ---- Oaken: the outer K values' share of the score (pre-pass) ----
+      // ---- Oaken: the outer K values' share of the score ----
       if constexpr (OAK) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
           for (int i = 0; i < GI; ++i) {
-            const int m = QRW::slot_query(q4, i);
-            const int t = tile + nb * 16 + n16;
-            if (ok[nb] && m < nq) sc[nb][i] = fmaf(oak_sc[m * oak_span + (t - t0)], P.qscale, sc[nb][i]);
+            const float o = oak.w->ksc[min(QRW::slot_query(q4, i), R - 1)][nb * 16 + n16];
+            sc[nb][i] = fmaf(o, P.qscale, sc[nb][i]);  // (rows outside the range are masked below)
           }
       }
       // ---- online softmax (base 2) ----
@@ -392,6 +746,21 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
 #pragma unroll
           for (int j = 0; j < 8; ++j) st.o[j][QRW::slot_elem(i)] *= a;
         }
+        if constexpr (OAK) {  // the outer-value output copies follow the same frame
+          auto& OW = *oak.w;
+#pragma unroll
+          for (int c = 0; c < kOakCopies<QR>; ++c) {
+            if constexpr (QR == 1) {
+              OW.osp[c][0][lane] *= alpha[0];
+              OW.osp[c][0][lane + 64] *= alpha[0];
+            } else {
+#pragma unroll
+              for (int i = 0; i < GI; ++i)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) OW.osp[c][QRW::slot_query(q4, i)][n16 + 16 * k] *= alpha[i];
+            }
+          }
+        }
       }
       float p[2][GI];
 #pragma unroll
@@ -401,16 +770,16 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
           p[nb][i] = ok[nb] ? fexp2(sc[nb][i] - st.m[i]) : 0.0f;
           st.l[i] += p[nb][i];
         }
-      // ---- Oaken: keep the final scores for the V outer values (post-pass) ----
+      // ---- Oaken: the softmax numerators of the rows, for the V entries ----
       if constexpr (OAK) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int i = 0; i < GI; ++i) {
-            const int m = QRW::slot_query(q4, i);
-            const int t = tile + nb * 16 + n16;
-            if (ok[nb] && m < nq && QRW::slot_owner(q4)) oak_sc[m * oak_span + (t - t0)] = sc[nb][i];
+        for (int i = 0; i < GI; ++i) {
+          const int m = QRW::slot_query(q4, i);
+          if (QRW::slot_owner(q4) && m < R) {
+            oak.w->pr[m][n16] = p[0][i];
+            oak.w->pr[m][16 + n16] = p[1][i];
           }
+        }
       }
       // ---- weights p * s_v (binary32) -> fp16 hi / lo in LDS ----
 #pragma unroll
@@ -438,6 +807,8 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
         }
       }
       wave_lds_sync();
+      // ---- Oaken: V entries into the outer-value output ----
+      if constexpr (OAK) oak_v_apply<QR, NGV>(*oak.w, oak.l[1], rpc, oct, nq);
       // ---- O += W V ----
       u4_t wa[NGV][2];
 #pragma unroll
@@ -471,8 +842,9 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
 
 // Fold the wave's state into its record (sum of l over the 16 token
 // columns).  Caller: all waves, after a barrier.
-template <int QR, int NGV, class LDS>
-__device__ __forceinline__ void wave_record(LDS& L, SoftState<QRows<QR>::GI>& st, int wave, int nq) {
+template <int QR, int NGV, class LDS, class Extra>
+__device__ __forceinline__ void wave_record(LDS& L, SoftState<QRows<QR>::GI>& st, int wave, int nq,
+                                            Extra&& extra) {
   constexpr int GI = QRows<QR>::GI;
   const int lane = threadIdx.x & 63, n16 = lane & 15, q4 = lane >> 4;
   float lt[GI];
@@ -488,13 +860,18 @@ __device__ __forceinline__ void wave_record(LDS& L, SoftState<QRows<QR>::GI>& st
     if (m >= nq) continue;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      rec.o[m][16 * j + n16] = st.o[j][QRW::slot_elem(i)];
+      rec.o[m][16 * j + n16] = st.o[j][QRW::slot_elem(i)] + extra(m, 16 * j + n16);
     }
     if (n16 == 0) {
       rec.o[m][128] = st.m[i];
       rec.o[m][129] = lt[i];
     }
   }
+}
+
+template <int QR, int NGV, class LDS>
+__device__ __forceinline__ void wave_record(LDS& L, SoftState<QRows<QR>::GI>& st, int wave, int nq) {
+  wave_record<QR, NGV>(L, st, wave, nq, [](int, int) { return 0.0f; });
 }
 
 // Merge the four wave records of each query and write the output (one

@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const ChanView nc{nullptr, nullptr};
       u4_t qop16[4];  // the plain query operand (qop was specialised above)
       build_qop<QR>(L, qop16);
-      attend_wave<QR, 1, 1, KF16, VF16, false, false, 1>(P, L, st, kt, vt, nc, nullptr, 0, nq, max(t0, lq), t1,
+      attend_wave<QR, 1, 1, KF16, VF16, false, false, 1>(P, L, st, kt, vt, nc, NoOak{}, nq, max(t0, lq), t1,
                                                          wave, qop16);
     }
   }

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mixed(AttnParams P) {
     if (a < e) {
       const TokView k16{P.k.codes16 + bh * S * KF16::RB, nullptr, nullptr};
       const TokView v16{P.v.codes16 + bh * S * VF16::RB, nullptr, nullptr};
-      attend_wave<QR, 1, 1, KF16, VF16, false, false, 1>(P, L, st, k16, v16, nc, nullptr, 0, nq,
+      attend_wave<QR, 1, 1, KF16, VF16, false, false, 1>(P, L, st, k16, v16, nc, NoOak{}, nq,
                                                           a * CT, e * CT, wave, qop);
     }
   }
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mixed(AttnParams P) {
     if (a < e) {
       const TokView k4{P.k.codes + bh * S * KI4::RB, P.k.scale + bh * S * NG, P.k.zero + bh * S * NG};
       const TokView v4{P.v.codes + bh * S * VI4::RB, P.v.scale + bh * S * NG, P.v.zero + bh * S * NG};
-      attend_wave<QR, NG, NG, KI4, VI4, false, false, 2>(P, L, st, k4, v4, nc, nullptr, 0, nq,
+      attend_wave<QR, NG, NG, KI4, VI4, false, false, 2>(P, L, st, k4, v4, nc, NoOak{}, nq,
                                                           (a - n16) * CT, (e - n16) * CT, wave, qop);
     }
   }
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mixed(AttnParams P) {
     if (a < e) {
       const TokView k2{P.k.codes2 + bh * S * KI2::RB, P.k.scale2 + bh * S * NG, P.k.zero2 + bh * S * NG};
       const TokView v2{P.v.codes2 + bh * S * VI2::RB, P.v.scale2 + bh * S * NG, P.v.zero2 + bh * S * NG};
-      attend_wave<QR, NG, NG, KI2, VI2, false, false, 2>(P, L, st, k2, v2, nc, nullptr, 0, nq,
+      attend_wave<QR, NG, NG, KI2, VI2, false, false, 2>(P, L, st, k2, v2, nc, NoOak{}, nq,
                                                           (a - n16 - n4) * CT, (e - n16 - n4) * CT,
                                                           wave, qop);
     }
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mixed(AttnParams P) {
       const long long wr = bh * S + (long long)(C - 1) * CT - w0;  // row of token t: wr + t
       const TokView kw{P.k.codes16 + wr * KF16::RB, nullptr, nullptr};
       const TokView vw{P.v.codes16 + wr * VF16::RB, nullptr, nullptr};
-      attend_wave<QR, 1, 1, KF16, VF16, false, false, 1>(P, L, st, kw, vw, nc, nullptr, 0, nq, w0, w1, wave,
+      attend_wave<QR, 1, 1, KF16, VF16, false, false, 1>(P, L, st, kw, vw, nc, NoOak{}, nq, w0, w1, wave,
                                                           qop);
     }
   }

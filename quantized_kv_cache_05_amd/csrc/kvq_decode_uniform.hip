@@ -59,7 +59,7 @@ void k_attn_uniform(AttnParams P) {
       vv = TokView{P.v.codes, P.v.scale, VC::SYM ? nullptr : P.v.zero, kv.pages, pshift, kv.hrow, kv.prow,
                    P.npages, P.status};
     }
-    attend_wave<QR, NGK, NGV, KC, VC, CHANK, false, 2, PAGED>(P, L, st, kv, vv, kc, nullptr, 0, nq, t0,
+    attend_wave<QR, NGK, NGV, KC, VC, CHANK, false, 2, PAGED>(P, L, st, kv, vv, kc, NoOak{}, nq, t0,
                                                                min(t1, lq), wave, qop);
   }
   if constexpr (CHANK) {
@@ -74,7 +74,7 @@ void k_attn_uniform(AttnParams P) {
       // the query operand is rebuilt here rather than kept live through the main loop
       u4_t qop16[4];
       build_qop<QR>(L, qop16);
-      attend_wave<QR, 1, NGV, KF16, VC, false, false, 1>(P, L, st, kt, vv, nc, nullptr, 0, nq,
+      attend_wave<QR, 1, NGV, KF16, VC, false, false, 1>(P, L, st, kt, vv, nc, NoOak{}, nq,
                                                          max(t0, lq), t1, wave, qop16);
     }
   }

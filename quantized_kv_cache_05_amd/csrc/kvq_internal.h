@@ -111,8 +111,6 @@ hipError_t launch_decode_uniform(const CacheArgs& c, const DecodeLaunch& d, hipS
 hipError_t launch_decode_oaken(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
 hipError_t launch_decode_mixed(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
 hipError_t launch_decode_dsq(const CacheArgs& c, const DecodeLaunch& d, hipStream_t st);
-// longest split (tokens) the Oaken decode kernel takes for qr query heads
-int oaken_max_split(int qr);
 // log-sum-exp merge of the split partials into the output
 hipError_t launch_merge(const DecodeLaunch& d, int B, hipStream_t st);
 

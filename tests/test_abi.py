@@ -174,6 +174,9 @@ def test_oaken_and_mixed_validation():
     assert status_of(K.kvq_cache_bytes, c) == K.KVQ_ERR_INVALID_ARG
     c = make_desc(mode=K.KVQ_MODE_OAKEN, bits=8)
     assert status_of(K.kvq_cache_bytes, c) == K.KVQ_ERR_UNSUPPORTED
+    # sparse lists start 8-byte aligned: a capacity that is not a multiple of 4 entries is refused
+    assert status_of(K.kvq_cache_bytes, make_desc(mode=K.KVQ_MODE_OAKEN, cap=1002)) == K.KVQ_ERR_ALIGNMENT
+    assert status_of(K.kvq_cache_bytes, make_desc(mode=K.KVQ_MODE_OAKEN, cap=1004)) == K.KVQ_OK
     c = make_desc(mode=K.KVQ_MODE_CHUNK_MIXED, ct=24)
     assert status_of(K.kvq_cache_bytes, c) == K.KVQ_ERR_INVALID_ARG
 
