@@ -70,13 +70,13 @@ struct AttnLds {
 template <int NG, bool SYM>
 __device__ __forceinline__ void load_tok_meta(const TokView& v, long long row, float (&s)[NG], float (&z)[NG]) {
   if constexpr (NG == 1) {
-    s[0] = ld_nt<float>(v.scale + row);
+    s[0] = ld_nt<float>(v.scale + (unsigned)row);
   } else if constexpr (NG == 2) {
-    const u2_t t = ld_nt<u2_t>(v.scale + (long long)row * 2);
+    const u2_t t = ld_nt<u2_t>(v.scale + (unsigned)(row * 2));
     const unsigned t0 = t[0], t1 = t[1];
     s[0] = __builtin_bit_cast(float, t0); s[1] = __builtin_bit_cast(float, t1);
   } else {
-    const u4_t t = ld_nt<u4_t>(v.scale + (long long)row * 4);
+    const u4_t t = ld_nt<u4_t>(v.scale + (unsigned)(row * 4));
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const unsigned tg = t[g];  // scalar copy before the bit cast (see the V product)
@@ -88,9 +88,9 @@ __device__ __forceinline__ void load_tok_meta(const TokView& v, long long row, f
     for (int g = 0; g < NG; ++g) z[g] = 0.0f;
   } else {
     unsigned zw;
-    if constexpr (NG == 1) zw = ld_nt<uint8_t>(v.zero + row);
-    else if constexpr (NG == 2) zw = ld_nt<uint16_t>(v.zero + (long long)row * 2);
-    else zw = ld_nt<unsigned>(v.zero + (long long)row * 4);
+    if constexpr (NG == 1) zw = ld_nt<uint8_t>(v.zero + (unsigned)row);
+    else if constexpr (NG == 2) zw = ld_nt<uint16_t>(v.zero + (unsigned)(row * 2));
+    else zw = ld_nt<unsigned>(v.zero + (unsigned)(row * 4));
 #pragma unroll
     for (int g = 0; g < NG; ++g) z[g] = (float)((zw >> (8 * g)) & 0xFFu);
   }
@@ -112,7 +112,7 @@ __device__ __forceinline__ void load_zsub(const TokView& vv, long long r0, u4_t 
       for (int p = 0; p < 4; ++p) zsub[0][g][p] = VC::ZMAGIC | 0x00800080u;  // z = 128
   } else {
     unsigned zw[2 * NGV];
-    const uint8_t* zp = vv.zero + (long long)r0 * NGV;
+    const uint8_t* zp = vv.zero + (unsigned)(r0 * NGV);
     if constexpr (NGV == 1) {
       const u2_t t = ld_nt<u2_t>(zp);
       zw[0] = t[0];
@@ -301,9 +301,13 @@ __device__ __forceinline__ unsigned wave_prefix_or(unsigned v) {
 
 // x_hat of entry en (idx | side << 7 | mag << 8) with its row's outer scale,
 // one binary32 product and one sum as in the reconstruction rule.
+// (contraction off: the product is rounded before the sum; T_lo - step is
+// formed as T_lo + (-step), the same binary32 result)
 __device__ __forceinline__ float oak_value(unsigned en, float so, const OakList& l) {
-  const float step = __fmul_rn((float)((en >> 8) & 31u), so);
-  return (en & 128u) ? __fadd_rn(l.t_hi, step) : __fsub_rn(l.t_lo, step);
+#pragma clang fp contract(off)
+  const bool hi = en & 128u;
+  const float step = (float)((en >> 8) & 31u) * so;
+  return (hi ? l.t_hi : l.t_lo) + (hi ? step : -step);
 }
 
 // K outer values of one tile: for each query m < nq, the sum over row r's
@@ -399,10 +403,7 @@ __device__ __forceinline__ OakOct oak_v_prep(OakWave<QR, NG>& W, const OakList& 
   const unsigned ra = min(rp.a[1], l.cap), rb = min(rp.b[1], l.cap);
   const unsigned oct = (lane >> 3) & 3;
   W.mk[lane] = 0u;
-  unsigned ro_l = o.ro[0];
-#pragma unroll
-  for (int k = 1; k < 4; ++k)
-    if (oct == (unsigned)k) ro_l = o.ro[k];
+  const unsigned ro_l = oct < 2 ? (oct ? o.ro[1] : o.ro[0]) : (oct == 2 ? o.ro[2] : o.ro[3]);
   const unsigned p = ra - ro_l;
   if (lane < (unsigned)kTile && ra < rb && p < 64u)
     reinterpret_cast<uint8_t*>(W.mk)[4 * p + oct] = (uint8_t)(1u << (lane & 7));
@@ -631,8 +632,8 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
         ok_base = ok_e0 & ~3u;
         ok_wd = oak_words(oak.l[0], ok_base, 0);
         const long long t = tile + (lane & 31);
-        load_f32s<NGV>(kv.oscale + t * NGV, oso[0]);
-        load_f32s<NGV>(vv.oscale + t * NGV, oso[1]);
+        load_f32s<NGV>(kv.oscale + (unsigned)(t * NGV), oso[0]);
+        load_f32s<NGV>(vv.oscale + (unsigned)(t * NGV), oso[1]);
         oct = oak_v_prep<QR, NGV>(*oak.w, oak.l[1], rpc);
         // issued before the code loads, so that the entry work below waits on
         // these alone (loads complete in order)
@@ -640,9 +641,9 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       }
       KC kr[2];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) kr[nb].load(kv.codes + (long long)(tile + nb * 16 + n16) * KC::RB, q4);
+      for (int nb = 0; nb < 2; ++nb) kr[nb].load(kv.codes + (unsigned)((tile + nb * 16 + n16) * KC::RB), q4);
       VC vr;
-      vr.load(vv.codes + (long long)(tile + 8 * q4) * VC::RB, n16);
+      vr.load(vv.codes + (unsigned)((tile + 8 * q4) * VC::RB), n16);
       float sk[2][NGK], zk[2][NGK], sv[2][NGV], zv[2][NGV];
       bool ok[2];
 #pragma unroll

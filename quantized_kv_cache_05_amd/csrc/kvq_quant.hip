@@ -60,6 +60,29 @@ __device__ __forceinline__ uint32_t e5m2_code(float y) {
   return sign | mag;
 }
 
+// Rounded quotients without a division per element.  Every code below is
+// rne(fl(x / s)) for one per-group s > 0: the correctly rounded binary32
+// quotient, then rounded to an integer (ties to even).  With r = 1/s to
+// within |r s - 1| <= 2^-22 (the hardware reciprocal, good to about 2^-23,
+// after one Newton step), y = fl(x r) differs from fl(x / s) by less than
+// |y| 2^-21 (the reciprocal's error plus the two roundings).  So where y lies
+// farther than |y| 2^-19 from every half-integer, rne(y) = rne(fl(x / s));
+// elsewhere (near-ties, exact ties, and anything not finite) `near` is set and
+// the caller divides.  Both tests are exact: y - rne(y) is exact (Sterbenz),
+// and the fused sum rounds monotonically against the representable 0.5.
+__device__ __forceinline__ float recip_refined(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  return s != 0.0f ? fmaf(fmaf(-s, r0, 1.0f), r0, r0) : 0.0f;  // s = 0: every y is 0
+}
+__device__ __forceinline__ float rne_quot(float x, float r, bool& near) {
+#pragma clang fp contract(off)
+  const float y = x * r;
+  const float n = rintf(y);
+  near |= !(fmaf(fabsf(y), 0x1p-19f, fabsf(y - n)) < 0.5f);
+  return n;
+}
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0ull; }
+
 // F8: 0 integer codes, 1 FP8 E4M3, 2 FP8 E5M2
 template <int BITS, bool SYM, int GE, int F8 = 0>
 __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint32_t& plo,
@@ -89,35 +112,53 @@ __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint
     amax = max_lanes<1, LG>(amax);
     s = amax / 127.0f;
     z = 0;
+    const float r = recip_refined(s);  // s = 0: all codes 0
+    bool near = false;
+    float n[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) n[k] = rne_quot(x[k], r, near);
+    if (wave_any(near) && near) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) n[k] = rintf(x[k] / s);
+    }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      int q = 0;
-      if (s != 0.0f) q = min(max((int)rintf(x[k] / s), -128), 127);
-      uint32_t byte = (uint32_t)(q & 0xFF);
+      const uint32_t byte = (uint32_t)((int)__builtin_amdgcn_fmed3f(n[k], -128.0f, 127.0f) & 0xFF);
       if (k < 4) plo |= byte << (8 * k);
       else phi |= byte << (8 * (k - 4));
     }
   } else {
-    constexpr int QMAX = (1 << BITS) - 1;
+    constexpr float QMAX = (float)((1 << BITS) - 1);
     float lo = 0.0f, hi = 0.0f;
+    float xm[8];  // invalid (excluded) values count as 0: they neither widen the range nor divide
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if ((valid >> k) & 1u) {
-        lo = fminf(lo, x[k]);
-        hi = fmaxf(hi, x[k]);
-      }
+    for (int k = 0; k < 8; ++k) {
+      xm[k] = ((valid >> k) & 1u) ? x[k] : 0.0f;
+      lo = fminf(lo, xm[k]);
+      hi = fmaxf(hi, xm[k]);
+    }
     lo = min_lanes<1, LG>(lo);
     hi = max_lanes<1, LG>(hi);
-    s = (hi - lo) / (float)QMAX;
-    z = 0;
-    if (s != 0.0f) z = min(max((int)rintf(-lo / s), 0), QMAX);
+    s = (hi - lo) / QMAX;
+    const float r = recip_refined(s);  // s = 0: z = 0 and all codes 0
+    bool near = false;
+    float zf = rne_quot(-lo, r, near);
+    float n[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) n[k] = rne_quot(xm[k], r, near);
+    if (wave_any(near) && near) {
+      zf = rintf(-lo / s);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) n[k] = rintf(xm[k] / s);
+    }
+    zf = __builtin_amdgcn_fmed3f(zf, 0.0f, QMAX);
+    z = (int)zf;
     uint64_t packed = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      int q = z;
-      if (s == 0.0f) q = 0;
-      else if ((valid >> k) & 1u) q = min(max((int)rintf(x[k] / s) + z, 0), QMAX);
-      packed |= (uint64_t)q << (BITS * k);
+      // an excluded value takes the zero-point (it decodes to 0)
+      const float q = ((valid >> k) & 1u) ? __builtin_amdgcn_fmed3f(n[k] + zf, 0.0f, QMAX) : zf;
+      packed |= (uint64_t)(uint32_t)q << (BITS * k);
     }
     plo = (uint32_t)packed;
     phi = (uint32_t)(packed >> 32);
@@ -604,19 +645,57 @@ __global__ __launch_bounds__(256) void k_chunk_wait(const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Outer values of an Oaken row (the Oaken page, §3.2.2): delta = x - T_hi
+// above the upper outer threshold, x - T_lo below the lower one; the group's
+// outer scale s_out = max |delta| / 31 and each value's 5-bit shifted
+// magnitude rne(|delta| / s_out).  d[k] = |delta| of an outer value, else 0.
+__device__ __forceinline__ void oak_deltas(const float (&v)[8], unsigned outer, float t_lo, float t_hi,
+                                           float (&d)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) d[k] = ((outer >> k) & 1u) ? fabsf(v[k] > t_hi ? v[k] - t_hi : v[k] - t_lo) : 0.0f;
+}
+// The sparse entries of a lane's outer values (channel | side << 7 | mag << 8)
+// to entries e, e + 1, ... of a list of capacity cap; `dropped` on overflow.
+__device__ __forceinline__ void oak_store_entries(const float (&v)[8], unsigned outer, float t_hi, float so,
+                                                  int li, uint16_t* sp, unsigned long long e,
+                                                  unsigned long long cap, float t_lo, bool& dropped) {
+  float d[8], m[8];
+  oak_deltas(v, outer, t_lo, t_hi, d);
+  const float r = recip_refined(so);  // s_out = 0: magnitudes 0
+  bool near = false;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m[k] = rne_quot(d[k], r, near);
+  if (wave_any(near) && near) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m[k] = rintf(d[k] / so);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if ((outer >> k) & 1u) {
+      const unsigned mag = (unsigned)__builtin_amdgcn_fmed3f(m[k], 0.0f, 31.0f);
+      if (e < cap) sp[e] = (uint16_t)((unsigned)(li * 8 + k) | (unsigned)(v[k] > t_hi) << 7 | mag << 8);
+      else dropped = true;
+      ++e;
+    }
+}
+
 // Oaken (the Oaken page, §3.1 online stage, §3.2.1-3.2.2): per row, outer
 // values (x > T_hi_outer or x < T_lo_outer) leave the dense INT4 body (coded
 // z) and go to the row's sparse list as shifted deltas with a per-group
-// 5-bit scale.  One workgroup per (b, h) walks the new rows in tiles of 16,
-// keeping the running entry offset so rowptr stays a prefix sum.
+// 5-bit scale.  One workgroup per (b, h) walks the new rows in tiles of 64
+// (four rows per 16-lane row group), the next tile's rows loaded while the
+// current one is coded.  The rows' outer counts meet in LDS once per tile;
+// every wave scans all 64 of them itself, so the running entry offset (and
+// with it rowptr, a prefix sum of the counts) needs one barrier per tile.
 template <int GE, bool VL>
 __global__ __launch_bounds__(256) void k_quant_oaken(
     const uint16_t* __restrict__ x, int t_new, int H, int S, const int* __restrict__ pos,
     float t_lo, float t_hi, long long cap, uint8_t* __restrict__ codes, float* __restrict__ scale,
     uint8_t* __restrict__ zero, float* __restrict__ oscale, uint32_t* __restrict__ rowptr,
     uint16_t* __restrict__ sparse, unsigned* __restrict__ status, PageMap pm) {
-  constexpr int NG = kD / GE, LG = GE / 8;
+  constexpr int NG = kD / GE, LG = GE / 8, U = 4, TR = 16 * U;
   __shared__ uint16_t lrows[VL ? 16 : 1][128];
+  __shared__ unsigned row_cnt[2][TR];  // alternate tiles: one barrier per tile
   const long long bh = blockIdx.x;
   const int b = (int)(bh / H);
   const int p = pos[b];
@@ -626,49 +705,80 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
   }
   uint32_t* rp = rowptr + bh * (S + 1);
   uint16_t* sp = sparse + bh * cap;
-  __shared__ int row_cnt[16];
   unsigned long long base = p == 0 ? 0ull : (unsigned long long)rp[p];
   if (p == 0 && threadIdx.x == 0) rp[0] = 0u;
-  const int rl = threadIdx.x >> 4, li = threadIdx.x & 15;
+  const int rl = threadIdx.x >> 4, li = threadIdx.x & 15, lane = threadIdx.x & 63;
   uint16_t* lrow = lrows[VL ? rl : 0];
+  const uint16_t* xr = x + (bh * t_new + rl) * kD + li * 8;
+  uint4 nxt[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    nxt[u] = 16 * u + rl < t_new ? ld_row8(xr + (long long)(16 * u) * kD) : make_uint4(0u, 0u, 0u, 0u);
   bool dropped = false;
-  for (int t0 = 0; t0 < t_new; t0 += 16) {
-    const int t = t0 + rl;
-    const bool active = t < t_new;
-    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    unsigned outer = 0;
-    if (active) {
-      unpack8(ld_row8(x + (bh * t_new + t) * kD + li * 8), v);
+  for (int t0 = 0, it = 0; t0 < t_new; t0 += TR, it ^= 1) {
+    uint4 raw[U];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) outer |= (unsigned)((v[k] > t_hi) || (v[k] < t_lo)) << k;
+    for (int u = 0; u < U; ++u) raw[u] = nxt[u];
+    if (t0 + TR < t_new) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + TR + 16 * u + rl;
+        nxt[u] = t < t_new ? ld_row8(xr + (long long)(t - rl) * kD) : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
-    uint32_t plo, phi;
-    float s;
-    int z;
-    quant8<4, false, GE>(v, ~outer & 0xFFu, plo, phi, s, z);
-    float dmax = 0.0f;
+    // pass 1: the rows' outer masks and counts (a lane's first entry within
+    // its row in bits 8 and up)
+    unsigned meta[U];
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if ((outer >> k) & 1u) dmax = fmaxf(dmax, fabsf(v[k] > t_hi ? v[k] - t_hi : v[k] - t_lo));
-    dmax = max_lanes<1, LG>(dmax);
-    const float so = dmax / 31.0f;
-    const int lc = __popc(outer);
-    int incl = lc;
+    for (int u = 0; u < U; ++u) {
+      float v[8];
+      unpack8(raw[u], v);
+      unsigned outer = 0;
+      if (t0 + 16 * u + rl < t_new) {
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      const int o = __shfl_up(incl, m, 16);
-      if (li >= m) incl += o;
+        for (int k = 0; k < 8; ++k) outer |= (unsigned)((v[k] > t_hi) || (v[k] < t_lo)) << k;
+      }
+      const int lc = __popc(outer);
+      int incl = lc;
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        const int o = __shfl_up(incl, m, 16);
+        if (li >= m) incl += o;
+      }
+      if (li == 15) row_cnt[it][16 * u + rl] = (unsigned)incl;  // 0 for an inactive row
+      meta[u] = outer | (unsigned)(incl - lc) << 8;
     }
-    const int rowtot = __shfl(incl, 15, 16);
-    if (li == 0) row_cnt[rl] = active ? rowtot : 0;
     __syncthreads();
-    unsigned long long rb = base, tile_tot = 0;
+    // each wave: inclusive scan of the tile's 64 row counts, lane r = row r
+    const unsigned cnt = row_cnt[it][lane];
+    unsigned scan = cnt;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < rl) rb += (unsigned)row_cnt[i];
-      tile_tot += (unsigned)row_cnt[i];
+    for (int m = 1; m < 64; m <<= 1) {
+      const unsigned o = __shfl_up(scan, m, 64);
+      if (lane >= m) scan += o;
     }
-    if (active) {
+    const unsigned excl_row = scan - cnt;
+    const unsigned tile_tot = __shfl(scan, 63, 64);
+    // pass 2: per row, the dense INT4 body, the outer scales and the entries
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + 16 * u + rl;
+      const unsigned long long rb = base + __shfl(excl_row, 16 * u + rl, 64);
+      const unsigned rcnt = __shfl(cnt, 16 * u + rl, 64);
+      if (t >= t_new) continue;
+      const unsigned outer = meta[u] & 0xFFu;
+      float v[8];
+      unpack8(raw[u], v);
+      uint32_t plo, phi;
+      float s;
+      int z;
+      quant8<4, false, GE>(v, ~outer & 0xFFu, plo, phi, s, z);
+      float d[8], dmax = 0.0f;
+      oak_deltas(v, outer, t_lo, t_hi, d);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) dmax = fmaxf(dmax, d[k]);
+      dmax = max_lanes<1, LG>(dmax);
+      const float so = dmax / 31.0f;
       // the dense row: contiguous, or in its page (a table entry outside the
       // pool skips the row and flags; the sparse list is per sequence)
       long long dst = bh * S + p + t;
@@ -688,27 +798,14 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
           oscale[dst * NG + li / LG] = so;
         }
       }
-      unsigned long long e = rb + (unsigned)(incl - lc);
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if ((outer >> k) & 1u) {
-          const bool above = v[k] > t_hi;
-          const float delta = above ? v[k] - t_hi : v[k] - t_lo;
-          int mag = 0;
-          if (so != 0.0f) mag = min(max((int)rintf(fabsf(delta) / so), 0), 31);
-          if (e < (unsigned long long)cap)
-            sp[e] = (uint16_t)((li * 8 + k) | ((int)above << 7) | (mag << 8));
-          else
-            dropped = true;
-          ++e;
-        }
+      oak_store_entries(v, outer, t_hi, so, li, sp, rb + (meta[u] >> 8), (unsigned long long)cap, t_lo, dropped);
       if (li == 0) {
-        unsigned long long end = rb + (unsigned)rowtot;
+        const unsigned long long end = rb + rcnt;
         rp[p + t + 1] = (uint32_t)(end < (unsigned long long)cap ? end : (unsigned long long)cap);
       }
+      __builtin_amdgcn_sched_barrier(0);  // rows one after another: bounded register use
     }
     base += tile_tot;
-    __syncthreads();
   }
   if (dropped) set_flag(status, kFlagSparseFull);
 }
@@ -750,10 +847,10 @@ __global__ __launch_bounds__(256) void k_quant_oaken_one(const uint16_t* __restr
   float s;
   int z;
   quant8<4, false, GE>(v, ~outer & 0xFFu, plo, phi, s, z);
-  float dmax = 0.0f;
+  float d[8], dmax = 0.0f;
+  oak_deltas(v, outer, t.thr_lo, t.thr_hi, d);
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
-    if ((outer >> k) & 1u) dmax = fmaxf(dmax, fabsf(v[k] > t.thr_hi ? v[k] - t.thr_hi : v[k] - t.thr_lo));
+  for (int k = 0; k < 8; ++k) dmax = fmaxf(dmax, d[k]);
   dmax = max_lanes<1, LG>(dmax);
   const float so = dmax / 31.0f;
   const int lc = __popc(outer);
@@ -784,17 +881,7 @@ __global__ __launch_bounds__(256) void k_quant_oaken_one(const uint16_t* __restr
   const unsigned long long cap = (unsigned long long)t.sparse_cap;
   unsigned long long e = base + (unsigned)(incl - lc);
   bool dropped = false;
-#pragma unroll
-  for (int k = 0; k < 8; ++k)
-    if ((outer >> k) & 1u) {
-      const bool above = v[k] > t.thr_hi;
-      const float delta = above ? v[k] - t.thr_hi : v[k] - t.thr_lo;
-      int mag = 0;
-      if (so != 0.0f) mag = min(max((int)rintf(fabsf(delta) / so), 0), 31);
-      if (e < cap) sp[e] = (uint16_t)((li * 8 + k) | ((int)above << 7) | (mag << 8));
-      else dropped = true;
-      ++e;
-    }
+  oak_store_entries(v, outer, t.thr_hi, so, li, sp, e, cap, t.thr_lo, dropped);
   if (li == 0) {
     const unsigned long long end = base + (unsigned)rowtot;
     rp[p + 1] = (uint32_t)(end < cap ? end : cap);
