@@ -15,8 +15,9 @@
  *    ("KV Cache的显存瓶颈" section): [batch][kv_heads][seq][head_dim], fp16,
  *    row-major, head_dim == 128.
  *  - Ownership: the caller allocates and frees every buffer (sizes from
- *    kvq_cache_bytes / kvq_decode_workspace_bytes).  The library keeps no
- *    state, never allocates, frees or synchronizes; all work is enqueued on
+ *    kvq_cache_bytes / kvq_decode_workspace_bytes).  The library never
+ *    allocates, frees or synchronizes, and keeps no state beyond the fixed
+ *    per-device array of kvq_decode_attn_noalloc; all work is enqueued on
  *    `stream` (a hipStream_t; NULL = the default stream) and buffers must
  *    stay alive until that work has completed.  Pre-allocating the cache is
  *    the practice [Cocktail] §5.2 recommends.
@@ -387,6 +388,27 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t q_heads,
                            const int32_t* seq_len, int32_t max_len, float sm_scale, float* out,
                            void* workspace, size_t workspace_bytes, int32_t num_splits,
                            void* stream);
+
+/*
+ * kvq_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops that forbid hipMalloc): the same
+ * arguments without the workspace, and the same kernels; the split partials
+ * go to a fixed array of KVQ_STATIC_SCRATCH_BYTES in the library's device
+ * image, one per device, held until the process ends.  The array's device
+ * address is looked up on the first call on each device (the current
+ * device), after which no call allocates or frees anything.
+ *  Returns KVQ_ERR_WORKSPACE, before any launch, when the chosen split plan
+ *  needs more than KVQ_STATIC_SCRATCH_BYTES (kvq_decode_workspace_bytes
+ *  gives the need), else as kvq_decode_attn.
+ *  Every call on a device shares that device's array: calls that overlap on
+ *  one device (two streams, two threads) race and must be ordered by the
+ *  caller.  Each call writes every partial it reads, so the array needs no
+ *  clearing between calls.
+ */
+#define KVQ_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+kvq_status kvq_decode_attn_noalloc(const kvq_cache* c, const void* q, int32_t q_heads,
+                                   const int32_t* seq_len, int32_t max_len, float sm_scale, float* out,
+                                   int32_t num_splits, void* stream);
 
 /*
  * [Cocktail] §3.1.1 chunk precision search: for every sequence b, the

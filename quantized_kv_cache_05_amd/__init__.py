@@ -43,6 +43,7 @@ KVQ_FLAG_BAD_CHUNK_BITS = 8
 KVQ_FLAG_PAGE_RANGE = 16
 
 PART_STRIDE = 132  # floats per split partial in the decode workspace
+STATIC_SCRATCH_BYTES = 32 << 20  # KVQ_STATIC_SCRATCH_BYTES: split partials of kvq_decode_attn_noalloc
 
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -81,7 +82,7 @@ _lib = None
 
 EXPORTS = ("kvq_cache_bytes", "kvq_quant_append", "kvq_reorder_chunks", "kvq_append_chunks",
            "kvq_dsq_append", "kvq_decode_workspace_bytes",
-           "kvq_decode_attn", "kvq_chunk_bits", "kvq_hist_f16", "kvq_hist_percentiles",
+           "kvq_decode_attn", "kvq_decode_attn_noalloc", "kvq_chunk_bits", "kvq_hist_f16", "kvq_hist_percentiles",
            "kvq_status_string")
 
 
@@ -100,6 +101,7 @@ def lib():
         L.kvq_dsq_append.argtypes = [P(kvq_cache), _vp, _vp, _vp, _i32, _vp, _vp]
         L.kvq_decode_workspace_bytes.argtypes = [P(kvq_cache), _i32, _i32, _i32, P(_sz)]
         L.kvq_decode_attn.argtypes = [P(kvq_cache), _vp, _i32, _vp, _i32, _f32, _vp, _vp, _sz, _i32, _vp]
+        L.kvq_decode_attn_noalloc.argtypes = [P(kvq_cache), _vp, _i32, _vp, _i32, _f32, _vp, _i32, _vp]
         L.kvq_chunk_bits.argtypes = [_vp, _vp, _i32, _i32, _i32, ctypes.c_double, ctypes.c_double, _vp,
                                      _vp, _vp]
         L.kvq_hist_f16.argtypes = [_vp, _i64, _vp, _vp]
@@ -183,6 +185,14 @@ def kvq_decode_attn(cache: kvq_cache, q, q_heads: int, seq_len, max_len: int, sm
                                         int(max_len), float(sm_scale), _ptr(out), _ptr(workspace),
                                         int(workspace_bytes), int(num_splits), _stream(stream)),
                   "kvq_decode_attn")
+
+
+def kvq_decode_attn_noalloc(cache: kvq_cache, q, q_heads: int, seq_len, max_len: int, sm_scale: float, out,
+                            num_splits: int = 0, stream=None) -> int:
+    return _check(lib().kvq_decode_attn_noalloc(ctypes.byref(cache), _ptr(q), int(q_heads), _ptr(seq_len),
+                                                int(max_len), float(sm_scale), _ptr(out), int(num_splits),
+                                                _stream(stream)),
+                  "kvq_decode_attn_noalloc")
 
 
 def kvq_chunk_bits(q_emb, chunk_emb, batch: int, n_chunks: int, dim: int, alpha: float, beta: float,

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "kvq.h"
 #include "kvq_internal.h"
@@ -299,6 +300,89 @@ size_t workspace_for(const kvq_cache* c, int q_heads, const Plan& p) {
   return (size_t)c->batch * (size_t)q_heads * (size_t)p.num_splits * kvq::kPartStride * sizeof(float);
 }
 
+// Split partials of kvq_decode_attn_noalloc: a fixed array in the device
+// image (each device holds its own copy).  Host code never passes the
+// array's name to a kernel: it is a host-side stand-in, and the device
+// address comes from hipGetSymbolAddress, looked up once per device with
+// that device current.
+__device__ __align__(256) float scratch[KVQ_STATIC_SCRATCH_BYTES / sizeof(float)];
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices] = {};
+
+kvq_status static_scratch(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KVQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return KVQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVQ_ERR_HIP;
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return KVQ_OK;
+}
+
+// kvq_decode_attn with the caller's workspace, or (use_static) with the
+// library's fixed per-device array; every argument check precedes the first
+// HIP call.
+kvq_status decode_attn(const kvq_cache* c, const void* q, int32_t q_heads, const int32_t* seq_len,
+                       int32_t max_len, float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                       int32_t num_splits, void* stream, bool use_static) {
+  kvq_status s = check_config(c);
+  if (s != KVQ_OK) return s;
+  if (!q || !out) return KVQ_ERR_INVALID_ARG;
+  if (c->mode != KVQ_MODE_CHUNK_MIXED && !seq_len) return KVQ_ERR_INVALID_ARG;
+  if (!std::isfinite(sm_scale)) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || (seq_len && !aligned(seq_len, 4)))
+    return KVQ_ERR_ALIGNMENT;
+  Plan p;
+  s = plan_decode(c, q_heads, max_len, num_splits, &p);
+  if (s != KVQ_OK) return s;
+  const size_t need = workspace_for(c, q_heads, p);
+  if (use_static) {
+    if (need > KVQ_STATIC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
+  } else if (need) {
+    if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return KVQ_ERR_ALIGNMENT;
+  }
+  s = check_buffers(c);
+  if (s != KVQ_OK) return s;
+  if (use_static && need) {
+    float* ws = nullptr;
+    s = static_scratch(&ws);
+    if (s != KVQ_OK) return s;
+    workspace = ws;
+  }
+  const CacheArgs a = cache_args(c);
+  kvq::DecodeLaunch d;
+  d.q = static_cast<const uint16_t*>(q);
+  d.Hq = q_heads;
+  d.G = p.G;
+  d.qr = p.qr;
+  d.qtiles = p.qtiles;
+  d.seq_len = seq_len;
+  d.max_len = c->mode == KVQ_MODE_CHUNK_MIXED ? c->max_seq : max_len;
+  d.num_splits = p.num_splits;
+  d.split_len = p.split_len;
+  d.qscale = sm_scale * 1.4426950408889634f;
+  d.out = out;
+  d.ws = static_cast<float*>(need ? workspace : nullptr);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (c->mode) {
+    case KVQ_MODE_UNIFORM: e = kvq::launch_decode_uniform(a, d, st); break;
+    case KVQ_MODE_OAKEN: e = kvq::launch_decode_oaken(a, d, st); break;
+    case KVQ_MODE_DSQ: e = kvq::launch_decode_dsq(a, d, st); break;
+    default: e = kvq::launch_decode_mixed(a, d, st); break;
+  }
+  if (e == hipErrorInvalidValue) return KVQ_ERR_UNSUPPORTED;
+  if (e != hipSuccess) return KVQ_ERR_HIP;
+  if (p.num_splits > 1) e = kvq::launch_merge(d, c->batch, st);
+  return from_hip(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -439,50 +523,16 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32
 kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t q_heads, const int32_t* seq_len,
                            int32_t max_len, float sm_scale, float* out, void* workspace,
                            size_t workspace_bytes, int32_t num_splits, void* stream) {
-  kvq_status s = check_config(c);
-  if (s != KVQ_OK) return s;
-  if (!q || !out) return KVQ_ERR_INVALID_ARG;
-  if (c->mode != KVQ_MODE_CHUNK_MIXED && !seq_len) return KVQ_ERR_INVALID_ARG;
-  if (!std::isfinite(sm_scale)) return KVQ_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(out, 16) || (seq_len && !aligned(seq_len, 4)))
-    return KVQ_ERR_ALIGNMENT;
-  Plan p;
-  s = plan_decode(c, q_heads, max_len, num_splits, &p);
-  if (s != KVQ_OK) return s;
-  const size_t need = workspace_for(c, q_heads, p);
-  if (need) {
-    if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return KVQ_ERR_ALIGNMENT;
-  }
-  s = check_buffers(c);
-  if (s != KVQ_OK) return s;
-  const CacheArgs a = cache_args(c);
-  kvq::DecodeLaunch d;
-  d.q = static_cast<const uint16_t*>(q);
-  d.Hq = q_heads;
-  d.G = p.G;
-  d.qr = p.qr;
-  d.qtiles = p.qtiles;
-  d.seq_len = seq_len;
-  d.max_len = c->mode == KVQ_MODE_CHUNK_MIXED ? c->max_seq : max_len;
-  d.num_splits = p.num_splits;
-  d.split_len = p.split_len;
-  d.qscale = sm_scale * 1.4426950408889634f;
-  d.out = out;
-  d.ws = static_cast<float*>(need ? workspace : nullptr);
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  switch (c->mode) {
-    case KVQ_MODE_UNIFORM: e = kvq::launch_decode_uniform(a, d, st); break;
-    case KVQ_MODE_OAKEN: e = kvq::launch_decode_oaken(a, d, st); break;
-    case KVQ_MODE_DSQ: e = kvq::launch_decode_dsq(a, d, st); break;
-    default: e = kvq::launch_decode_mixed(a, d, st); break;
-  }
-  if (e == hipErrorInvalidValue) return KVQ_ERR_UNSUPPORTED;
-  if (e != hipSuccess) return KVQ_ERR_HIP;
-  if (p.num_splits > 1) e = kvq::launch_merge(d, c->batch, st);
-  return from_hip(e);
+  return decode_attn(c, q, q_heads, seq_len, max_len, sm_scale, out, workspace, workspace_bytes, num_splits,
+                     stream, false);
 }
+
+kvq_status kvq_decode_attn_noalloc(const kvq_cache* c, const void* q, int32_t q_heads,
+                                   const int32_t* seq_len, int32_t max_len, float sm_scale, float* out,
+                                   int32_t num_splits, void* stream) {
+  return decode_attn(c, q, q_heads, seq_len, max_len, sm_scale, out, nullptr, 0, num_splits, stream, true);
+}
+
 
 kvq_status kvq_chunk_bits(const double* q_emb, const double* chunk_emb, int32_t batch,
                           int32_t n_chunks, int32_t dim, double alpha, double beta, double* sims,
