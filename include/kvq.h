@@ -215,23 +215,39 @@ typedef struct kvq_cache {
   int32_t* perm;        /* CHUNK_MIXED: [B][C] original chunk id at each slot */
   int32_t* seg;         /* CHUNK_MIXED: [B][4] {n_fp16, n_int4, n_int2, n_chunks} */
   uint32_t* status;     /* device word for KVQ_FLAG_* bits (required) */
-  /* Paged layout (UNIFORM mode with TOKEN-axis K and V, OAKEN and DSQ;
-   * page_tokens 0 = contiguous).  DSQ pages hold page_tokens / 64 whole
-   * groups: every per-group buffer (codes, scale, codes2, scale2, zero2 and
-   * dsq_mask) is a pool [num_pages][H][page_tokens / 64][...] and group g of
-   * sequence b is group g % (page_tokens / 64) of page
-   * block_table[b][g * 64 / page_tokens]; the fp16 tails stay per sequence.  Every per-token buffer (codes, scale, zero,
-   * and Oaken's oscale) is then a pool of num_pages pages
-   * [num_pages][H][page_tokens][row], and token t of sequence b lives in page
-   * block_table[b][t / page_tokens], row t % page_tokens of its head.  Oaken's
-   * sparse lists (rowptr, sparse) stay per (sequence, head) as without pages:
-   * a dense page table plus per-sequence sparse lists, after the dual
-   * dense / sparse page management of [Oaken] §3.2.3.  Pages are owned by the caller, who may map
-   * any page to any (b, logical page); a page shared by two sequences is
-   * written by both. */
+  /* Paged layout (every mode; page_tokens 0 = contiguous).  Every per-token
+   * buffer (codes, scale, zero, and Oaken's oscale) is then a pool of
+   * num_pages pages [num_pages][H][page_tokens][row], and token t of
+   * sequence b lives in page block_table[b][t / page_tokens], row
+   * t % page_tokens of its head.
+   *  - UNIFORM with a CHANNEL-axis K: K's per-block scale and zero are pools
+   *    [num_pages][H][page_tokens / 64][128] (a 64-token block never
+   *    straddles a page); the fp16 tail (codes16) stays per sequence.
+   *  - OAKEN: the sparse lists (rowptr, sparse) stay per (sequence, head) as
+   *    without pages: a dense page table plus per-sequence sparse lists,
+   *    after the dual dense / sparse page management of [Oaken] §3.2.3.
+   *  - CHUNK_MIXED: each class pool (FP16: codes16; INT4: codes, scale,
+   *    zero; INT2: codes2, scale2, zero2) is a pool of num_pages pages, and
+   *    block_table holds one table per class, int32
+   *    [3][batch][max_seq / page_tokens] (FP16, INT4, INT2): class-local row
+   *    r of sequence b (class-local chunk k holds rows k * chunk_tokens ..)
+   *    lives in page block_table[cls][b][r / page_tokens].  The waiting
+   *    chunk of streaming appends is the FP16 class's last chunk, so the
+   *    last entry of each sequence's FP16 table must be mapped when
+   *    kvq_append_chunks is used.
+   *  - DSQ: pages hold page_tokens / 64 whole groups: every per-group buffer
+   *    (codes, scale, codes2, scale2, zero2 and dsq_mask) is a pool
+   *    [num_pages][H][page_tokens / 64][...] and group g of sequence b is
+   *    group g % (page_tokens / 64) of page block_table[b][g * 64 /
+   *    page_tokens]; the fp16 tails stay per sequence.
+   * Pages are owned by the caller, who may map any page to any (b, logical
+   * page); a page shared by two sequences is written by both.  An append
+   * row or chunk whose table entry lies outside [0, num_pages) is skipped
+   * and raises KVQ_FLAG_PAGE_RANGE. */
   int32_t page_tokens;          /* 0, 64, 128 or 256; max_seq a multiple of it */
   int32_t num_pages;            /* pages in each pool (paged: >= 1) */
-  const int32_t* block_table;   /* paged: device int32 [batch][max_seq / page_tokens] */
+  const int32_t* block_table;   /* paged: device int32 [batch][max_seq / page_tokens]
+                                   (CHUNK_MIXED: [3][batch][max_seq / page_tokens]) */
   /* DSQ mode ([KVO-LLM] §3.1): significant tokens per 64-token group (1 .. 16;
    * the page's top 20 % of 64 is 12.8, so 13) and the significance mask. */
   int32_t dsq_sig;

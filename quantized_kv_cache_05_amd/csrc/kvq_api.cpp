@@ -32,11 +32,11 @@ kvq_status check_config(const kvq_cache* c) {
   if (c->page_tokens != 0) {
     if (c->page_tokens != 64 && c->page_tokens != 128 && c->page_tokens != 256) return KVQ_ERR_INVALID_ARG;
     if (c->max_seq % c->page_tokens || c->num_pages < 1) return KVQ_ERR_INVALID_ARG;
-    // uniform token-axis caches, Oaken's dense body (its sparse lists stay per
-    // sequence) and DSQ's groups (its fp16 tails stay per sequence)
-    if (!((c->mode == KVQ_MODE_UNIFORM && k.axis == KVQ_AXIS_TOKEN) || c->mode == KVQ_MODE_OAKEN ||
-          c->mode == KVQ_MODE_DSQ))
-      return KVQ_ERR_UNSUPPORTED;
+    // every mode: uniform caches (a channel-axis K's fp16 tail stays per
+    // sequence), Oaken's dense body (its sparse lists stay per sequence),
+    // chunk-mixed class pools (one block-table row per class and sequence;
+    // page_tokens is a multiple of chunk_tokens) and DSQ's groups (its fp16
+    // tails stay per sequence)
   }
   switch (c->mode) {
     case KVQ_MODE_UNIFORM: {
@@ -113,7 +113,8 @@ kvq_tensor_bytes tensor_bytes(const kvq_cache* c, const kvq_tensor& t, bool is_k
       if (is_k && t.axis == KVQ_AXIS_CHANNEL) {
         r.scale = B * H * (S / 64) * D * 4;
         r.zero = B * H * (S / 64) * D;
-        r.codes16 = B * H * 64 * D * 2;  // fp16 residual tail: the incomplete 64-token block
+        // fp16 residual tail: the incomplete 64-token block (per sequence, paged or not)
+        r.codes16 = B_seq * H * 64 * D * 2;
       } else {
         r.scale = B * H * S * ng * 4;
         r.zero = (t.symmetric || t.format != KVQ_FMT_INT) ? 0 : B * H * S * ng;

@@ -500,12 +500,15 @@ __device__ __forceinline__ void load_f32s(const float* p, float (&v)[NG]) {
 //
 //  KC / VC: codecs.  NGK / NGV: channel groups of K / V (token axis).
 //  CHANK: K has channel-axis groups of 64 tokens (scale folded into the query).
-//  PAGED: the views are paged (TokView), rebased for every tile.
+//  PAGED: the views are paged (TokView), rebased for every tile; PK: K is
+//         paged too (false: K is a per-sequence view, e.g. an fp16 tail).
+//         With CHANK, the block scales (kc) are pool bases, indexed by the
+//         page row of the block.
 //  OAK: Oaken; oak holds the side lists and the wave's LDS area (OakCtx), the
 //       outer values enter the scores and the wave's outer-value output
 //       inside the loop (see OakWave).
 template <int QR, int NGK, int NGV, class KC, class VC, bool CHANK, bool OAK, int TPS, bool PAGED = false,
-          class LDS, class OK = NoOak>
+          bool PK = PAGED, class LDS, class OK = NoOak>
 __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
                                             SoftState<QRows<QR>::GI>& st, const TokView& kv_,
                                             const TokView& vv_, const ChanView& kc, const OK& oak,
@@ -538,17 +541,19 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
   // multiple of 64 tokens and steps start 64-aligned)
   static_assert(!PAGED || kTile * TPS <= 64, "a step must stay inside one page");
   int pg_next = 0;
-  if constexpr (PAGED) pg_next = kv_.pages[min(tb + wave * kTile * TPS, t1 - 1) >> kv_.pshift];
+  if constexpr (PAGED) pg_next = vv_.pages[min(tb + wave * kTile * TPS, t1 - 1) >> vv_.pshift];
   // Oaken: row pointers of the wave's next tile, one tile ahead
   OakRp rp_next{};
   if constexpr (OAK) rp_next = oak_rp_load(oak.l, tb + wave * kTile * TPS, t0, t1);
   for (int step = tb + wave * kTile * TPS; step < t1; step += kNW * kTile * TPS) {
     TokView kv = kv_, vv = vv_;
+    long long ro = 0;  // paged: pool row of token t = t + ro (this step's page)
     if constexpr (PAGED) {
-      const long long ro = page_row_offset(kv_, pg_next, step);
-      kv = at_rows<KC::RB, NGK>(kv_, ro);
+      ro = page_row_offset(vv_, pg_next, step);
+      if constexpr (PK && CHANK) kv.codes = kv_.codes + ro * KC::RB;
+      else if constexpr (PK) kv = at_rows<KC::RB, NGK>(kv_, ro);
       vv = at_rows<VC::RB, NGV>(vv_, ro);
-      pg_next = kv_.pages[min(step + kNW * kTile * TPS, t1 - 1) >> kv_.pshift];
+      pg_next = vv_.pages[min(step + kNW * kTile * TPS, t1 - 1) >> vv_.pshift];
     }
     // ---- channel-axis K: fold the block's scales into the query ----
     // The R x 128 products q[m][d] * s[d] are spread over the wave: entry
@@ -558,9 +563,9 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
     // sum_d q[m][d] s[d] (OFF + z[d]) is reduced over its entries.
     float cbias[GI];
     if constexpr (CHANK) {
-      const int blk = step >> 6;
-      const float* sp = kc.scale + (long long)blk * 128;
-      const uint8_t* zp = kc.zero + (long long)blk * 128;
+      const long long blk = (step + ro) >> 6;  // a 64-token block never straddles a page
+      const float* sp = kc.scale + blk * 128;
+      const uint8_t* zp = kc.zero + blk * 128;
       auto& T = L.qtab[wave];
       constexpr int NE = 16 * R, PER = (NE + 63) / 64;
       float part = 0.0f;

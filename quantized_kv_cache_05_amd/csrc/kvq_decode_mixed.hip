@@ -4,12 +4,30 @@
 // contiguous row range of that class's pool, attended with that class's
 // codecs into the same running softmax state, so the split emits one partial.
 // The tokens of a chunk still being appended are attended by the last split.
+// Paged, each class pool is a pool of pages with its own block-table row per
+// sequence; steps of 32 or 64 class-local rows never straddle a page.
 #include "kvq_attn_impl.h"
 
 namespace kvq {
 namespace {
 
-template <int QR, int NG>
+// View of class cls's pool for (b, kvh) (row t of the view = class-local row
+// t): contiguous, or paged through class cls's block-table row.
+template <bool PAGED, int RB, int NGC>
+__device__ __forceinline__ TokView class_view(const AttnParams& P, int cls, int b, int kvh, const uint8_t* codes,
+                                              const float* scale, const uint8_t* zero) {
+  const long long S = P.S, bh = (long long)b * P.H + kvh;
+  if constexpr (PAGED) {
+    const int pshift = P.pshift;
+    return TokView{codes, scale, zero, P.pages + ((long long)cls * P.B + b) * (S >> pshift), pshift,
+                   kvh << pshift, P.H << pshift, P.npages, P.status};
+  } else {
+    return TokView{codes + bh * S * RB, scale ? scale + bh * S * NGC : nullptr,
+                   zero ? zero + bh * S * NGC : nullptr};
+  }
+}
+
+template <int QR, int NG, bool PAGED>
 __global__ __launch_bounds__(256, 2) void k_attn_mixed(AttnParams P) {
   __shared__ AttnLds<QR, NG> L;
   const int split = blockIdx.x, qt = blockIdx.y % P.qtiles, kvh = blockIdx.y / P.qtiles, b = blockIdx.z;
@@ -24,66 +42,69 @@ __global__ __launch_bounds__(256, 2) void k_attn_mixed(AttnParams P) {
   if (n16 < 0 || n4 < 0 || n > C || n16 + n4 > n) n = n16 = n4 = 0;
   const int j0 = split * P.split_len;
   const int j1 = min(n, j0 + P.split_len);
-  const long long bh = (long long)b * P.H + kvh;
-  const long long S = P.S;
   SoftState<QRows<QR>::GI> st;
   soft_init(st);
   const ChanView nc{nullptr, nullptr};
   {
     const int a = max(j0, 0), e = min(j1, n16);
     if (a < e) {
-      const TokView k16{P.k.codes16 + bh * S * KF16::RB, nullptr, nullptr};
-      const TokView v16{P.v.codes16 + bh * S * VF16::RB, nullptr, nullptr};
-      attend_wave<QR, 1, 1, KF16, VF16, false, false, 1>(P, L, st, k16, v16, nc, NoOak{}, nq,
-                                                          a * CT, e * CT, wave, qop);
+      const TokView k16 = class_view<PAGED, KF16::RB, 1>(P, 0, b, kvh, P.k.codes16, nullptr, nullptr);
+      const TokView v16 = class_view<PAGED, VF16::RB, 1>(P, 0, b, kvh, P.v.codes16, nullptr, nullptr);
+      attend_wave<QR, 1, 1, KF16, VF16, false, false, 1, PAGED>(P, L, st, k16, v16, nc, NoOak{}, nq, a * CT,
+                                                                 e * CT, wave, qop);
     }
   }
   {
     const int a = max(j0, n16), e = min(j1, n16 + n4);
     if (a < e) {
-      const TokView k4{P.k.codes + bh * S * KI4::RB, P.k.scale + bh * S * NG, P.k.zero + bh * S * NG};
-      const TokView v4{P.v.codes + bh * S * VI4::RB, P.v.scale + bh * S * NG, P.v.zero + bh * S * NG};
-      attend_wave<QR, NG, NG, KI4, VI4, false, false, 2>(P, L, st, k4, v4, nc, NoOak{}, nq,
-                                                          (a - n16) * CT, (e - n16) * CT, wave, qop);
+      const TokView k4 = class_view<PAGED, KI4::RB, NG>(P, 1, b, kvh, P.k.codes, P.k.scale, P.k.zero);
+      const TokView v4 = class_view<PAGED, VI4::RB, NG>(P, 1, b, kvh, P.v.codes, P.v.scale, P.v.zero);
+      attend_wave<QR, NG, NG, KI4, VI4, false, false, 2, PAGED>(P, L, st, k4, v4, nc, NoOak{}, nq,
+                                                                 (a - n16) * CT, (e - n16) * CT, wave, qop);
     }
   }
   {
     const int a = max(j0, n16 + n4), e = min(j1, n);
     if (a < e) {
-      const TokView k2{P.k.codes2 + bh * S * KI2::RB, P.k.scale2 + bh * S * NG, P.k.zero2 + bh * S * NG};
-      const TokView v2{P.v.codes2 + bh * S * VI2::RB, P.v.scale2 + bh * S * NG, P.v.zero2 + bh * S * NG};
-      attend_wave<QR, NG, NG, KI2, VI2, false, false, 2>(P, L, st, k2, v2, nc, NoOak{}, nq,
-                                                          (a - n16 - n4) * CT, (e - n16 - n4) * CT,
-                                                          wave, qop);
+      const TokView k2 = class_view<PAGED, KI2::RB, NG>(P, 2, b, kvh, P.k.codes2, P.k.scale2, P.k.zero2);
+      const TokView v2 = class_view<PAGED, VI2::RB, NG>(P, 2, b, kvh, P.v.codes2, P.v.scale2, P.v.zero2);
+      attend_wave<QR, NG, NG, KI2, VI2, false, false, 2, PAGED>(P, L, st, k2, v2, nc, NoOak{}, nq,
+                                                                 (a - n16 - n4) * CT, (e - n16 - n4) * CT,
+                                                                 wave, qop);
     }
   }
   // tokens of the chunk not yet complete (streaming appends) wait as fp16 in
-  // the FP16 pool's last chunk: the last split attends seg[b][3] * CT ..
-  // seq_len[b] - 1 of them
+  // the FP16 pool's last chunk, class-local rows (C - 1) CT on: the last
+  // split attends seg[b][3] * CT .. seq_len[b] - 1 of them
   if (P.seq_len && split == P.num_splits - 1 && n < C) {
     const int len = clamp_seq_len(P, b, blockIdx.y == 0 && threadIdx.x == 0);
     const int w0 = n * CT, w1 = min(len, w0 + CT - 1);
     if (w0 < w1) {
-      const long long wr = bh * S + (long long)(C - 1) * CT - w0;  // row of token t: wr + t
-      const TokView kw{P.k.codes16 + wr * KF16::RB, nullptr, nullptr};
-      const TokView vw{P.v.codes16 + wr * VF16::RB, nullptr, nullptr};
-      attend_wave<QR, 1, 1, KF16, VF16, false, false, 1>(P, L, st, kw, vw, nc, NoOak{}, nq, w0, w1, wave,
-                                                          qop);
+      const TokView kw = class_view<PAGED, KF16::RB, 1>(P, 0, b, kvh, P.k.codes16, nullptr, nullptr);
+      const TokView vw = class_view<PAGED, VF16::RB, 1>(P, 0, b, kvh, P.v.codes16, nullptr, nullptr);
+      const int r0 = (C - 1) * CT;
+      attend_wave<QR, 1, 1, KF16, VF16, false, false, 1, PAGED>(P, L, st, kw, vw, nc, NoOak{}, nq, r0,
+                                                                 r0 + (w1 - w0), wave, qop);
     }
   }
   wave_record<QR, NG>(L, st, wave, nq);
   finish_split(P, L, b, kvh, qt, split, nq);
 }
 
-template <int QR>
-hipError_t go(const AttnParams& P, int ng, dim3 grid, hipStream_t st) {
+template <int QR, bool PAGED>
+hipError_t go_pg(const AttnParams& P, int ng, dim3 grid, hipStream_t st) {
   switch (ng) {
-    case 1: hipLaunchKernelGGL((k_attn_mixed<QR, 1>), grid, dim3(kNW * 64), 0, st, P); break;
-    case 2: hipLaunchKernelGGL((k_attn_mixed<QR, 2>), grid, dim3(kNW * 64), 0, st, P); break;
-    case 4: hipLaunchKernelGGL((k_attn_mixed<QR, 4>), grid, dim3(kNW * 64), 0, st, P); break;
+    case 1: hipLaunchKernelGGL((k_attn_mixed<QR, 1, PAGED>), grid, dim3(kNW * 64), 0, st, P); break;
+    case 2: hipLaunchKernelGGL((k_attn_mixed<QR, 2, PAGED>), grid, dim3(kNW * 64), 0, st, P); break;
+    case 4: hipLaunchKernelGGL((k_attn_mixed<QR, 4, PAGED>), grid, dim3(kNW * 64), 0, st, P); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int QR>
+hipError_t go(const AttnParams& P, int ng, dim3 grid, hipStream_t st) {
+  return P.pages ? go_pg<QR, true>(P, ng, grid, st) : go_pg<QR, false>(P, ng, grid, st);
 }
 
 }  // namespace

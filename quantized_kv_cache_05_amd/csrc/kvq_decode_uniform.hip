@@ -5,16 +5,25 @@
 namespace kvq {
 namespace {
 
-// Occupancy target (waves per SIMD): two in general; four for the 4-query
-// per-channel-K kernels with 4- or 2-bit codes and two V groups, and for the
-// paged one-query kernels with at most two groups other than asymmetric
-// INT8, which fit in 128 registers without spilling (the contiguous
-// one-query kernels land there by themselves).
+// Occupancy target (waves per SIMD): two in general; four for the
+// contiguous 4-query per-channel-K kernels with 4- or 2-bit codes and two V
+// groups, and for the paged token-axis one-query kernels with at most two
+// groups other than asymmetric INT8, which fit in 128 registers without
+// spilling (the contiguous one-query kernels land there by themselves).
 template <int QR, class KC, int NGV, bool CHANK, bool PAGED>
-constexpr int kUniformWaves = ((CHANK && QR == 4 && NGV == 2 && KC::BITS <= 4) ||
-                               (PAGED && QR == 1 && NGV <= 2 && !(KC::BITS == 8 && !KC::SYM)))
+constexpr int kUniformWaves = ((CHANK && !PAGED && QR == 4 && NGV == 2 && KC::BITS <= 4) ||
+                               (!CHANK && PAGED && QR == 1 && NGV <= 2 && !(KC::BITS == 8 && !KC::SYM)))
                                   ? 4
                                   : 2;
+
+// Paged V view of (b, kvh): the pool bases and this sequence's block-table row.
+template <class VC, int NGV>
+__device__ __forceinline__ TokView paged_v(const AttnParams& P, int b, int kvh) {
+  const int pshift = P.pshift;
+  return TokView{P.v.codes, P.v.scale, VC::SYM ? nullptr : P.v.zero,
+                 P.pages + (long long)b * (P.S >> pshift), pshift, kvh << pshift, P.H << pshift,
+                 P.npages, P.status};
+}
 
 template <int QR, class KC, class VC, int NGK, int NGV, bool CHANK, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kUniformWaves<QR, KC, NGV, CHANK, PAGED>)))
@@ -52,12 +61,10 @@ void k_attn_uniform(AttnParams P) {
     TokView vv{P.v.codes + bh * S * VC::RB, P.v.scale + bh * S * NGV,
                VC::SYM ? nullptr : P.v.zero + bh * S * NGV};
     if constexpr (PAGED) {  // pools of pages: the views start at the pool bases
-      const int pshift = P.pshift;
-      kv = TokView{P.k.codes, P.k.scale, KC::SYM ? nullptr : P.k.zero,
-                   P.pages + (long long)b * (S >> pshift), pshift, kvh << pshift, P.H << pshift,
-                   P.npages, P.status};
-      vv = TokView{P.v.codes, P.v.scale, VC::SYM ? nullptr : P.v.zero, kv.pages, pshift, kv.hrow, kv.prow,
-                   P.npages, P.status};
+      vv = paged_v<VC, NGV>(P, b, kvh);
+      kv = TokView{P.k.codes, CHANK ? nullptr : P.k.scale, (CHANK || KC::SYM) ? nullptr : P.k.zero, vv.pages,
+                   vv.pshift, vv.hrow, vv.prow, P.npages, P.status};
+      if constexpr (CHANK) kc = ChanView{P.k.scale, P.k.zero};  // blocks indexed by pool row / 64
     }
     attend_wave<QR, NGK, NGV, KC, VC, CHANK, false, 2, PAGED>(P, L, st, kv, vv, kc, NoOak{}, nq, t0,
                                                                min(t1, lq), wave, qop);
@@ -67,15 +74,17 @@ void k_attn_uniform(AttnParams P) {
       const long long bh = (long long)b * P.H + kvh;
       const long long S = P.S;
       // row t of the view is tail row t - lq
+      // (the tail is per sequence, paged or not)
       const TokView kt{P.k.codes16 + (bh * 64 - lq) * KF16::RB, nullptr, nullptr};
-      const TokView vv{P.v.codes + bh * S * VC::RB, P.v.scale + bh * S * NGV,
-                       VC::SYM ? nullptr : P.v.zero + bh * S * NGV};
+      TokView vv{P.v.codes + bh * S * VC::RB, P.v.scale + bh * S * NGV,
+                 VC::SYM ? nullptr : P.v.zero + bh * S * NGV};
+      if constexpr (PAGED) vv = paged_v<VC, NGV>(P, b, kvh);
       const ChanView nc{nullptr, nullptr};
       // the query operand is rebuilt here rather than kept live through the main loop
       u4_t qop16[4];
       build_qop<QR>(L, qop16);
-      attend_wave<QR, 1, NGV, KF16, VC, false, false, 1>(P, L, st, kt, vv, nc, NoOak{}, nq,
-                                                         max(t0, lq), t1, wave, qop16);
+      attend_wave<QR, 1, NGV, KF16, VC, false, false, 1, PAGED, false>(P, L, st, kt, vv, nc, NoOak{}, nq,
+                                                                      max(t0, lq), t1, wave, qop16);
     }
   }
   wave_record<QR, NGV>(L, st, wave, nq);
@@ -84,13 +93,10 @@ void k_attn_uniform(AttnParams P) {
 
 template <int QR, class KC, class VC, int NGK, int NGV, bool CHANK>
 hipError_t go(const AttnParams& P, dim3 grid, hipStream_t st) {
-  if constexpr (!CHANK) {
-    if (P.pages) {
-      hipLaunchKernelGGL((k_attn_uniform<QR, KC, VC, NGK, NGV, false, true>), grid, dim3(kNW * 64), 0, st, P);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((k_attn_uniform<QR, KC, VC, NGK, NGV, CHANK, false>), grid, dim3(kNW * 64), 0, st, P);
+  if (P.pages)
+    hipLaunchKernelGGL((k_attn_uniform<QR, KC, VC, NGK, NGV, CHANK, true>), grid, dim3(kNW * 64), 0, st, P);
+  else
+    hipLaunchKernelGGL((k_attn_uniform<QR, KC, VC, NGK, NGV, CHANK, false>), grid, dim3(kNW * 64), 0, st, P);
   return hipGetLastError();
 }
 

@@ -372,7 +372,7 @@ __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restric
                                                        float* __restrict__ scale,
                                                        uint8_t* __restrict__ zero,
                                                        const uint8_t* __restrict__ tail,
-                                                       unsigned* __restrict__ status) {
+                                                       unsigned* __restrict__ status, PageMap pm) {
   constexpr int QMAX = (1 << BITS) - 1, RB = kD * BITS / 8;
   const long long bh = blockIdx.y;
   const int b = (int)(bh / H);
@@ -383,6 +383,18 @@ __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restric
   }
   const int k0 = (p & ~63) + 64 * (int)blockIdx.x;
   if (k0 + 64 > p + t_new) return;  // incomplete after this append (or past it)
+  // the block's first code row (its scales: row / 64): contiguous, or in its
+  // page (a block never straddles a page; an entry outside the pool skips
+  // the block and flags; the fp16 tail is per sequence)
+  long long row0 = bh * S + k0;
+  if (pm.pages) {
+    const int pg = pm.pages[(long long)b * (S / pm.ptok) + k0 / pm.ptok];
+    if (pg < 0 || pg >= pm.npages) {
+      if (threadIdx.x == 0) set_flag(status, kFlagPageRange);
+      return;
+    }
+    row0 = ((long long)pg * H + bh % H) * pm.ptok + k0 % pm.ptok;
+  }
   __shared__ float tile[64][kD + 1];
   __shared__ float lo_sh[2][kD], hi_sh[2][kD], s_sh[kD];
   __shared__ int z_sh[kD];
@@ -419,14 +431,14 @@ __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restric
     if (s != 0.0f) z = min(max((int)rintf(-lo / s), 0), QMAX);
     s_sh[c] = s;
     z_sh[c] = z;
-    const long long m = (bh * (S / 64) + k0 / 64) * kD + c;
+    const long long m = (row0 / 64) * kD + c;
     scale[m] = s;
     zero[m] = (uint8_t)z;
   }
   __syncthreads();
   // thread (row r, 32-channel block pc): slices q = 0..3 of k-step pc
   const int r = threadIdx.x >> 2, pc = threadIdx.x & 3;
-  uint8_t* dst = codes + (bh * S + k0 + r) * RB;
+  uint8_t* dst = codes + (row0 + r) * RB;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     uint64_t w = 0;
@@ -462,6 +474,27 @@ __global__ __launch_bounds__(256) void k_channel_tail(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Class pools of a chunk-mixed cache: contiguous [B][H][C][CT] rows per
+// class, or pages: class cls of sequence b maps its class-local rows through
+// its own block-table row pages[cls][b][.] (a chunk never straddles a page:
+// chunk_tokens divides page_tokens).
+struct ClassPages {
+  const int* pages;  // null: contiguous; else int32 [3][B][S / ptok]
+  int ptok, npages, B;
+};
+
+// First pool row of class-local chunk k of (b, h) in class cls's pool; -1
+// for a block-table entry outside the pool.
+__device__ __forceinline__ long long chunk_row0(const ClassPages& cp, int cls, long long bh, int H, int S,
+                                                int CT, int k) {
+  const long long lrow = (long long)k * CT;
+  if (!cp.pages) return bh * S + lrow;
+  const int b = (int)(bh / H);
+  const int pg = cp.pages[((long long)cls * cp.B + b) * (S / cp.ptok) + lrow / cp.ptok];
+  if (pg < 0 || pg >= cp.npages) return -1;
+  return ((long long)pg * H + bh % H) * cp.ptok + lrow % cp.ptok;
+}
+
 // Chunk-mixed cache (the Cocktail page's reorder, §3.1.2, then quantization
 // of the reordered chunks): one workgroup per (slot, b, h); the slot's source
 // chunk is perm[b][slot], its class follows from seg[b].  FP16 chunks are
@@ -472,7 +505,7 @@ __global__ __launch_bounds__(256) void k_quant_mixed(
     const int* __restrict__ perm, const int* __restrict__ seg, uint8_t* __restrict__ c16,
     uint8_t* __restrict__ c4, float* __restrict__ s4, uint8_t* __restrict__ z4,
     uint8_t* __restrict__ c2, float* __restrict__ s2, uint8_t* __restrict__ z2,
-    unsigned* __restrict__ status) {
+    unsigned* __restrict__ status, ClassPages cp) {
   constexpr int NG = kD / GE, LG = GE / 8;
   __shared__ uint16_t lrows[VL ? 16 : 1][128];
   const int j = blockIdx.x;
@@ -489,7 +522,11 @@ __global__ __launch_bounds__(256) void k_quant_mixed(
   const int cls = j < n16 ? 0 : (j < n16 + n4 ? 1 : 2);
   const int k = cls == 0 ? j : (cls == 1 ? j - n16 : j - n16 - n4);
   const uint16_t* xs = x + (bh * S + (long long)src * CT) * kD;
-  const long long drow0 = (bh * C + k) * CT;
+  const long long drow0 = chunk_row0(cp, cls, bh, H, S, CT, k);
+  if (drow0 < 0) {
+    if (threadIdx.x == 0) set_flag(status, kFlagPageRange);
+    return;
+  }
   const int li = threadIdx.x & 15;
   uint16_t* lrow = lrows[VL ? (threadIdx.x >> 4) : 0];
   for (int r = threadIdx.x >> 4; r < CT; r += 16) {
@@ -568,7 +605,7 @@ __global__ __launch_bounds__(256) void k_chunk_append(
     int i0, const uint16_t* __restrict__ x, int t_new, int H, int S, int CT, int C, const int* __restrict__ pos,
     const uint8_t* __restrict__ bits, int n_new, const int* __restrict__ seg, uint8_t* __restrict__ c16,
     uint8_t* __restrict__ c4, float* __restrict__ s4, uint8_t* __restrict__ z4, uint8_t* __restrict__ c2,
-    float* __restrict__ s2, uint8_t* __restrict__ z2, unsigned* __restrict__ status) {
+    float* __restrict__ s2, uint8_t* __restrict__ z2, unsigned* __restrict__ status, ClassPages cp) {
   constexpr int NG = kD / GE, LG = GE / 8;
   __shared__ uint16_t lrows[VL ? 16 : 1][128];
   const int i = i0 + (int)blockIdx.x;
@@ -586,8 +623,12 @@ __global__ __launch_bounds__(256) void k_chunk_append(
   int k = seg[b * 4 + cls];
   for (int i2 = 0; i2 < i; ++i2) k += chunk_cls(bb[i2]) == cls;
   if (k >= C) return;
-  const long long wrow0 = (bh * C + (C - 1)) * CT;  // waiting chunk
-  const long long drow0 = (bh * C + k) * CT;
+  const long long wrow0 = chunk_row0(cp, 0, bh, H, S, CT, C - 1);  // waiting chunk
+  const long long drow0 = chunk_row0(cp, cls, bh, H, S, CT, k);
+  if (wrow0 < 0 || drow0 < 0) {
+    if (threadIdx.x == 0) set_flag(status, kFlagPageRange);
+    return;
+  }
   const int li = threadIdx.x & 15;
   uint16_t* lrow = lrows[VL ? (threadIdx.x >> 4) : 0];
   for (int r = threadIdx.x >> 4; r < CT; r += 16) {
@@ -628,19 +669,25 @@ __global__ __launch_bounds__(256) void k_chunk_append(
 template <bool VL>
 __global__ __launch_bounds__(256) void k_chunk_wait(const uint16_t* __restrict__ x, int t_new, int H, int S,
                                                     int CT, int C, const int* __restrict__ pos,
-                                                    const int* __restrict__ seg, uint8_t* __restrict__ c16) {
+                                                    const int* __restrict__ seg, uint8_t* __restrict__ c16,
+                                                    unsigned* __restrict__ status, ClassPages cp) {
   __shared__ uint16_t lrows[VL ? 16 : 1][128];
   const long long bh = blockIdx.x;
   const int b = (int)(bh / H);
   const int p = pos[b];
   if (p < 0 || p + t_new > S || p / CT != seg[b * 4 + 3]) return;  // flagged by k_chunk_append
+  const long long wrow0 = chunk_row0(cp, 0, bh, H, S, CT, C - 1);  // the waiting chunk
+  if (wrow0 < 0) {
+    if (threadIdx.x == 0) set_flag(status, kFlagPageRange);
+    return;
+  }
   const int e = p + t_new, j0 = (e / CT) * CT;
   const int r0 = max(p, j0) - j0, r1 = e - j0;
   const int li = threadIdx.x & 15;
   uint16_t* lrow = lrows[VL ? (threadIdx.x >> 4) : 0];
   for (int r = r0 + (threadIdx.x >> 4); r < r1; r += 16) {
     const uint4 raw = ld_row8(x + (bh * t_new + (j0 + r - p)) * kD + li * 8);
-    store_row_f16<VL>(c16 + ((bh * C + (C - 1)) * CT + r) * kD * 2, li, raw, lrow);
+    store_row_f16<VL>(c16 + (wrow0 + r) * kD * 2, li, raw, lrow);
   }
 }
 
@@ -1210,15 +1257,16 @@ hipError_t launch_quant_channel(const CacheArgs& c, const TensorArgs& t, const u
   if (t.group != 64 || t_new < 1) return hipErrorInvalidValue;
   // blocks an append of t_new tokens can complete: floor((p mod 64 + t_new) / 64) <= (t_new + 63) / 64
   const dim3 grid((unsigned)((t_new + 63) / 64), (unsigned)(c.B * c.H));
+  const PageMap pm{c.pages, c.ptok, c.npages};
   if (t.bits == 8)
     hipLaunchKernelGGL(k_quant_channel<8>, grid, dim3(kThreads), 0, st, x, t_new, c.H, c.S, pos,
-                       t.codes, t.scale, t.zero, t.codes16, c.status);
+                       t.codes, t.scale, t.zero, t.codes16, c.status, pm);
   else if (t.bits == 4)
     hipLaunchKernelGGL(k_quant_channel<4>, grid, dim3(kThreads), 0, st, x, t_new, c.H, c.S, pos,
-                       t.codes, t.scale, t.zero, t.codes16, c.status);
+                       t.codes, t.scale, t.zero, t.codes16, c.status, pm);
   else if (t.bits == 2)
     hipLaunchKernelGGL(k_quant_channel<2>, grid, dim3(kThreads), 0, st, x, t_new, c.H, c.S, pos,
-                       t.codes, t.scale, t.zero, t.codes16, c.status);
+                       t.codes, t.scale, t.zero, t.codes16, c.status, pm);
   else
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
@@ -1232,16 +1280,17 @@ hipError_t launch_quant_mixed(const CacheArgs& c, const TensorArgs& t, bool vl, 
                               const int* pos, hipStream_t st) {
   const int C = c.S / c.chunk_tokens;
   const dim3 grid((unsigned)C, (unsigned)(c.B * c.H));
+  const ClassPages cp{c.pages, c.ptok, c.npages, c.B};
 #define KVQ_MIX(GE)                                                                                \
   do {                                                                                             \
     if (vl)                                                                                        \
       hipLaunchKernelGGL((k_quant_mixed<GE, true>), grid, dim3(kThreads), 0, st, x, c.H, c.S,      \
                          c.chunk_tokens, C, pos, c.perm, c.seg, t.codes16, t.codes, t.scale,       \
-                         t.zero, t.codes2, t.scale2, t.zero2, c.status);                           \
+                         t.zero, t.codes2, t.scale2, t.zero2, c.status, cp);                       \
     else                                                                                           \
       hipLaunchKernelGGL((k_quant_mixed<GE, false>), grid, dim3(kThreads), 0, st, x, c.H, c.S,     \
                          c.chunk_tokens, C, pos, c.perm, c.seg, t.codes16, t.codes, t.scale,       \
-                         t.zero, t.codes2, t.scale2, t.zero2, c.status);                           \
+                         t.zero, t.codes2, t.scale2, t.zero2, c.status, cp);                       \
   } while (0)
   switch (t.group) {
     case 32: KVQ_MIX(32); break;
@@ -1256,6 +1305,7 @@ hipError_t launch_quant_mixed(const CacheArgs& c, const TensorArgs& t, bool vl, 
 hipError_t launch_chunk_append(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
                                int t_new, const int* pos, const uint8_t* bits, int n_new, hipStream_t st) {
   const int C = c.S / c.chunk_tokens, CT = c.chunk_tokens;
+  const ClassPages cp{c.pages, c.ptok, c.npages, c.B};
   hipError_t e = hipSuccess;
   // chunk 0 first, then the others (see k_chunk_append)
   for (int part = 0; part < 2 && e == hipSuccess; ++part) {
@@ -1267,11 +1317,11 @@ hipError_t launch_chunk_append(const CacheArgs& c, const TensorArgs& t, bool vl,
     if (vl)                                                                                          \
       hipLaunchKernelGGL((k_chunk_append<GE, true>), grid, dim3(kThreads), 0, st, i0, x, t_new, c.H, \
                          c.S, CT, C, pos, bits, n_new, c.seg, t.codes16, t.codes, t.scale, t.zero,   \
-                         t.codes2, t.scale2, t.zero2, c.status);                                    \
+                         t.codes2, t.scale2, t.zero2, c.status, cp);                                \
     else                                                                                             \
       hipLaunchKernelGGL((k_chunk_append<GE, false>), grid, dim3(kThreads), 0, st, i0, x, t_new,     \
                          c.H, c.S, CT, C, pos, bits, n_new, c.seg, t.codes16, t.codes, t.scale,      \
-                         t.zero, t.codes2, t.scale2, t.zero2, c.status);                            \
+                         t.zero, t.codes2, t.scale2, t.zero2, c.status, cp);                        \
   } while (0)
     switch (t.group) {
       case 32: KVQ_CA(32); break;
@@ -1285,10 +1335,10 @@ hipError_t launch_chunk_append(const CacheArgs& c, const TensorArgs& t, bool vl,
   if (e != hipSuccess) return e;
   if (vl)
     hipLaunchKernelGGL((k_chunk_wait<true>), dim3((unsigned)(c.B * c.H)), dim3(kThreads), 0, st, x, t_new,
-                       c.H, c.S, CT, C, pos, c.seg, t.codes16);
+                       c.H, c.S, CT, C, pos, c.seg, t.codes16, c.status, cp);
   else
     hipLaunchKernelGGL((k_chunk_wait<false>), dim3((unsigned)(c.B * c.H)), dim3(kThreads), 0, st, x,
-                       t_new, c.H, c.S, CT, C, pos, c.seg, t.codes16);
+                       t_new, c.H, c.S, CT, C, pos, c.seg, t.codes16, c.status, cp);
   return hipGetLastError();
 }
 

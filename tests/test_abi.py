@@ -155,7 +155,11 @@ def test_paged_validation_and_sizes():
     assert status_of(K.kvq_cache_bytes, paged(P=32)) == K.KVQ_ERR_INVALID_ARG
     assert status_of(K.kvq_cache_bytes, paged(P=128, S=320)) == K.KVQ_ERR_INVALID_ARG
     assert status_of(K.kvq_cache_bytes, paged(pages=0)) == K.KVQ_ERR_INVALID_ARG
-    assert status_of(K.kvq_cache_bytes, paged(k_axis=1)) == K.KVQ_ERR_UNSUPPORTED
+    # channel-axis K: codes and per-block scales in the pools, the fp16 tail per sequence
+    b = K.kvq_cache_bytes(paged(P=128, pages=5, bits=4, k_axis=1, group=64))
+    assert (b.k.codes, b.k.scale, b.k.zero) == (5 * H * 128 * 64, 5 * H * 2 * 128 * 4, 5 * H * 2 * 128)
+    assert b.k.codes16 == 2 * H * 64 * 128 * 2
+    assert (b.v.codes, b.v.scale, b.v.zero) == (5 * H * 128 * 64, 5 * H * 128 * 2 * 4, 5 * H * 128 * 2)
     # Oaken: the dense body in page pools, the sparse lists per (sequence, head) of max_seq rows
     b = K.kvq_cache_bytes(paged(mode=K.KVQ_MODE_OAKEN, cap=1000))
     assert (b.k.codes, b.k.scale, b.k.oscale) == (10 * H * 64 * 64, 10 * H * 64 * 2 * 4, 10 * H * 64 * 2 * 4)
@@ -166,7 +170,11 @@ def test_paged_validation_and_sizes():
     b = K.kvq_cache_bytes(c)
     assert (b.k.codes, b.k.codes2, b.dsq_mask) == (10 * H * 1 * 2048, 10 * H * 1 * 2048, 10 * H * 1 * 8)
     assert (b.k.codes16, b.k.oscale) == (2 * H * 64 * 128 * 2, 2 * H * 64 * 4)
-    assert status_of(K.kvq_cache_bytes, paged(mode=K.KVQ_MODE_CHUNK_MIXED, group=32)) == K.KVQ_ERR_UNSUPPORTED
+    # chunk-mixed: three class pools of num_pages pages each
+    b = K.kvq_cache_bytes(paged(mode=K.KVQ_MODE_CHUNK_MIXED, group=32))
+    rows = 10 * H * 64
+    assert (b.k.codes16, b.k.codes, b.k.scale, b.k.zero) == ((rows + 64) * 256, rows * 64, rows * 4 * 4, rows * 4)
+    assert (b.v.codes2, b.v.scale2, b.v.zero2) == (rows * 32, rows * 4 * 4, rows * 4)
 
 
 def test_oaken_and_mixed_validation():
