@@ -76,6 +76,8 @@ def parse():
                    help="measure the headline workload only (by default configurations 1-5 are all "
                         "measured and reported under 'configs')")
     p.add_argument("--num-splits", type=int, default=0)
+    p.add_argument("--page-tokens", type=int, default=0, choices=[0, 64, 128, 256],
+                   help="workloads 3 and 4: the same cache in the paged layout (tokens per page)")
     p.add_argument("--cpu-seconds", type=float, default=16.0,
                    help="budget of the CPU-oracle leg (half single-threaded, half all threads)")
     p.add_argument("--no-cpu", action="store_true")
@@ -150,6 +152,22 @@ class Workload:
         return [c.flags() for c in self.caches]
 
 
+def page_tables(torch, w, page, tables):
+    """Paged layout for a workload: `tables` block tables (one per precision class of a chunk-mixed
+    cache) mapping every logical page of every sequence to a page of a pool of batch * pages-per-
+    sequence pages, in a seeded random order.  Returns the cache keywords and the table bytes the
+    decode workgroups read (an upper bound for chunk-mixed caches, whose classes share the rows)."""
+    if not page:
+        return {}, 0
+    import numpy as np
+    B, H, T = w.batch, w.kv_heads, w.tokens
+    n = -(-T // page)
+    rng = np.random.default_rng(w.seed + page)
+    order = np.stack([rng.permutation(B * n).astype(np.int32) for _ in range(tables)])
+    kw = dict(page_tokens=page, num_pages=B * n, block_table=torch.from_numpy(order.reshape(-1)).cuda())
+    return kw, B * H * n * 4
+
+
 class UniformToken(Workload):
     """Workloads 1, 2, 6 and 7: token-axis groups, optional 1-token append per step."""
 
@@ -213,15 +231,16 @@ class UniformToken(Workload):
 class ChannelK(Workload):
     """Workload 3: K per channel over 64-token blocks, V token groups of 64, GQA."""
 
-    def __init__(self, w, torch, K):
+    def __init__(self, w, torch, K, page=0):
         super().__init__(w, torch, K)
         B, H, T = w.batch, w.kv_heads, w.tokens
         self.kx, self.vx = upload_kv(w, 0, torch), upload_kv(w, 1, torch)
+        paging, self.table_bytes = page_tables(torch, w, page, 1)
         one = K.QuantKVCache(B, H, T, K.KVQ_MODE_UNIFORM, k_bits=4, k_axis=K.KVQ_AXIS_CHANNEL,
-                             k_group=64, v_group=64)
+                             k_group=64, v_group=64, **paging)
         self.rotate = max(1, min(8, -(-2 * MALL_BYTES // one.total_bytes)))
         self.caches = [one] + [K.QuantKVCache(B, H, T, K.KVQ_MODE_UNIFORM, k_bits=4,
-                                              k_axis=K.KVQ_AXIS_CHANNEL, k_group=64, v_group=64)
+                                              k_axis=K.KVQ_AXIS_CHANNEL, k_group=64, v_group=64, **paging)
                                for _ in range(self.rotate - 1)]
         self.q = torch.from_numpy(w.q().view("int16")).cuda()
         self.pos0 = i32(torch, [0] * B)
@@ -238,13 +257,13 @@ class ChannelK(Workload):
         rows = w.batch * w.kv_heads * w.tokens
         k = rows * 64 + (rows // 64) * 128 * 5
         v = rows * (64 + 2 * 5)
-        return k + v + w.batch * w.q_heads * 128 * (2 + 4)
+        return k + v + w.batch * w.q_heads * 128 * (2 + 4) + self.table_bytes
 
 
 class Cocktail(Workload):
     """Workload 4: chunk precision search, reorder, class pools, chunked decode."""
 
-    def __init__(self, w, torch, K):
+    def __init__(self, w, torch, K, page=0):
         super().__init__(w, torch, K)
         import numpy as np
         B, H, T, CT = w.batch, w.kv_heads, w.tokens, w.chunk_tokens
@@ -254,7 +273,8 @@ class Cocktail(Workload):
         self.c_emb = torch.from_numpy(np.stack([e[1] for e in embs])).cuda()
         self.bits = torch.zeros((B, self.C), dtype=torch.uint8, device="cuda")
         self.kx, self.vx = upload_kv(w, 0, torch), upload_kv(w, 1, torch)
-        self.caches = [K.QuantKVCache(B, H, T, K.KVQ_MODE_CHUNK_MIXED, k_group=32, chunk_tokens=CT)]
+        paging, self.table_bytes = page_tables(torch, w, page, 3)
+        self.caches = [K.QuantKVCache(B, H, T, K.KVQ_MODE_CHUNK_MIXED, k_group=32, chunk_tokens=CT, **paging)]
         self.q = torch.from_numpy(w.q().view("int16")).cuda()
         self.pos0 = i32(torch, [0] * B)
         self.seq_len = None
@@ -286,7 +306,7 @@ class Cocktail(Workload):
             rows16, rows4, rows2 = n16 * CT, n4 * CT, n2 * CT
             total += 2 * H * (rows16 * 256 + rows4 * (64 + ng * 5) + rows2 * (32 + ng * 5))
             total += 16  # the sequence's segment counts
-        return total + w.batch * w.q_heads * 128 * (2 + 4)
+        return total + w.batch * w.q_heads * 128 * (2 + 4) + self.table_bytes
 
 
 class Oaken(Workload):
@@ -389,8 +409,10 @@ class Dsq(Workload):
         return 2 * groups * dsq_group_bytes() + w.batch * w.q_heads * 128 * (2 + 4)
 
 
-def build_workload(idx, torch, K, synth):
+def build_workload(idx, torch, K, synth, page=0):
     w = synth.WORKLOADS[idx]
+    if page and idx not in (3, 4):
+        raise SystemExit("--page-tokens applies to workloads 3 and 4 (workload 7 is the paged INT8 one)")
     if idx == 1:
         return UniformToken(w, torch, K, bits=4, sym=False, group=64, append=False)
     if idx == 2:
@@ -402,9 +424,9 @@ def build_workload(idx, torch, K, synth):
     if idx == 7:
         return UniformToken(w, torch, K, bits=8, sym=True, group=128, append=True, page=64)
     if idx == 3:
-        return ChannelK(w, torch, K)
+        return ChannelK(w, torch, K, page)
     if idx == 4:
-        return Cocktail(w, torch, K)
+        return Cocktail(w, torch, K, page)
     if idx == 8:
         return Dsq(w, torch, K)
     return Oaken(w, torch, K)
@@ -744,12 +766,12 @@ def summarize_stats(stats_csv, bench_log):
 
 # ---------------------------------------------------------------------------
 
-def measure(idx, steps, warmup, torch, K, synth, stream):
+def measure(idx, steps, warmup, torch, K, synth, stream, page=0):
     """Set up workload idx, time its bulk prefill quantize and `steps` steps (append + decode) after
     `warmup` untimed ones; returns the per-workload figures.  Device memory is released on return."""
     import numpy as np
     t = time.perf_counter()
-    wl = build_workload(idx, torch, K, synth)
+    wl = build_workload(idx, torch, K, synth, page)
     torch.cuda.synchronize()
     log("workload %d set up in %.1fs (%d cache cop%s)" % (idx, time.perf_counter() - t, wl.rotate,
                                                         "y" if wl.rotate == 1 else "ies"))
@@ -878,7 +900,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    head = measure(idx, args.steps, args.warmup, torch, K, synth, stream)
+    head = measure(idx, args.steps, args.warmup, torch, K, synth, stream, args.page_tokens)
     configs = {}
     if not args.headline_only:
         # the other configurations of the metric, each set up, measured and released in turn
@@ -906,6 +928,7 @@ def main():
             "workload": head["workload"],
             "batch": head["batch"], "kv_heads": head["kv_heads"], "q_heads": head["q_heads"],
             "seq_len": head["seq_len"], "num_splits": args.num_splits, "cache_copies": head["cache_copies"],
+            "page_tokens": args.page_tokens,
         },
         "decode_ms": round(head["decode_ms"], 5),
         "decode_bytes": head["decode_bytes"],
@@ -921,7 +944,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic(idx),
+            "traffic": None if args.page_tokens else stored_traffic(idx),
         },
         "cpu_baseline": cpu,
         "configs": configs or None,

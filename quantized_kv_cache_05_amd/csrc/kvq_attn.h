@@ -446,6 +446,17 @@ struct TokView {
   const float* oscale = nullptr;  // Oaken: outer scales [rows][ng], rows as `scale`
 };
 
+// Block-table entry i, loaded on the vector path: a scalar load would share
+// its wait counter with the LDS operations, so every LDS wait of the tile
+// loop would also wait for it.  The opaque zero keeps the address
+// non-uniform; callers make the value wave-uniform (readfirstlane) where
+// they use it, one step later, so the page arithmetic stays scalar.
+__device__ __forceinline__ int page_entry_v(const int* pages, int i) {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return pages[i + z];
+}
+
 // Row offset that maps the tokens t of the page-aligned range starting at
 // `tok` (within one page) to their pool rows: row = t + offset.  pg is the
 // block-table entry of that page; one outside the pool reads page 0 and

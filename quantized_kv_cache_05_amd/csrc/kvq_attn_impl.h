@@ -541,7 +541,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
   // multiple of 64 tokens and steps start 64-aligned)
   static_assert(!PAGED || kTile * TPS <= 64, "a step must stay inside one page");
   int pg_next = 0;
-  if constexpr (PAGED) pg_next = vv_.pages[min(tb + wave * kTile * TPS, t1 - 1) >> vv_.pshift];
+  if constexpr (PAGED) pg_next = page_entry_v(vv_.pages, min(tb + wave * kTile * TPS, t1 - 1) >> vv_.pshift);
   // Oaken: row pointers of the wave's next tile, one tile ahead
   OakRp rp_next{};
   if constexpr (OAK) rp_next = oak_rp_load(oak.l, tb + wave * kTile * TPS, t0, t1);
@@ -549,11 +549,11 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
     TokView kv = kv_, vv = vv_;
     long long ro = 0;  // paged: pool row of token t = t + ro (this step's page)
     if constexpr (PAGED) {
-      ro = page_row_offset(vv_, pg_next, step);
+      ro = page_row_offset(vv_, __builtin_amdgcn_readfirstlane(pg_next), step);
       if constexpr (PK && CHANK) kv.codes = kv_.codes + ro * KC::RB;
       else if constexpr (PK) kv = at_rows<KC::RB, NGK>(kv_, ro);
       vv = at_rows<VC::RB, NGV>(vv_, ro);
-      pg_next = vv_.pages[min(step + kNW * kTile * TPS, t1 - 1) >> vv_.pshift];
+      pg_next = page_entry_v(vv_.pages, min(step + kNW * kTile * TPS, t1 - 1) >> vv_.pshift);
     }
     // ---- channel-axis K: fold the block's scales into the query ----
     // The R x 128 products q[m][d] * s[d] are spread over the wave: entry

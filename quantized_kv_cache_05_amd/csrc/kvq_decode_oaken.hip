@@ -28,9 +28,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_oaken(AttnParams P) {
   __shared__ AttnLds<QR, NG> L;
   __shared__ OakWave<QR, NG> OW[kNW];
   const int split = blockIdx.x, qt = blockIdx.y % P.qtiles, kvh = blockIdx.y / P.qtiles, b = blockIdx.z;
-  // wave-uniform wave index (scalar addressing), except when paged (see the
-  // uniform decode kernel: the block-table entry must stay a vector load)
-  const int wave = PAGED ? (int)(threadIdx.x >> 6) : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar addressing
   const int nq = min(QR, P.G - qt * QR);
   for (int i = threadIdx.x; i < (int)(sizeof(OW) / 4); i += blockDim.x) reinterpret_cast<float*>(OW)[i] = 0.0f;
   u4_t qop[4];

@@ -30,10 +30,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kUniformWav
 void k_attn_uniform(AttnParams P) {
   __shared__ AttnLds<QR, NGV, CHANK> L;
   const int split = blockIdx.x, qt = blockIdx.y % P.qtiles, kvh = blockIdx.y / P.qtiles, b = blockIdx.z;
-  // wave-uniform wave index (scalar addressing), except in the paged kernels:
-  // there it would make the next step's block-table entry a scalar load,
-  // counted with the LDS operations, so every LDS wait would also wait for it
-  const int wave = PAGED ? (int)(threadIdx.x >> 6) : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar addressing
   const int nq = min(QR, P.G - qt * QR);
   u4_t qop[4];
   attn_prologue<QR, NGK>(P, L, b, kvh, qt, nq, qop);
