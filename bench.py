@@ -88,6 +88,8 @@ def parse():
                    help="no GPU work: turn the counter CSVs of two rocprofv3 --pmc runs of this "
                         "script (FETCH_SIZE, then WRITE_SIZE, both with --copy-probe-mib) and the "
                         "bench line printed by one of them into a traffic summary on stdout")
+    p.add_argument("--summarize-busy", nargs=3, metavar=("COUNTER_CSV", "AGENT_CSV", "BENCH_LOG"),
+                   help="print VALU / MFMA busy fractions from a rocprofv3 --pmc run of BUSY_COUNTERS")
     p.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "BENCH_LOG"),
                    help="no GPU work: summarize a rocprofv3 --kernel-trace --stats run of this "
                         "script (its kernel_stats.csv and the output it printed) on stdout")
@@ -640,8 +642,13 @@ def cpu_baseline(w, idx, budget_s):
 # stored HBM counters of the decode kernel (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)
 
 def source_hash():
+    """Hash of the sources the decode kernels are built from (their headers, the decode
+    translation units and the host code that plans their launches)."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "quantized_kv_cache_05_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "quantized_kv_cache_05_amd", "csrc")
+    files = set(glob.glob(os.path.join(csrc, "*.h")) + glob.glob(os.path.join(csrc, "kvq_decode_*.hip")) +
+                [os.path.join(csrc, "kvq_api.cpp")])
+    for f in sorted(files):
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
             h.update(fh.read())
@@ -729,6 +736,55 @@ def short_kernel_name(name):
         return name.split("<")[0] + "<...>"
     cut = name.find("(")
     return name[:cut] if cut > 0 else name
+
+
+BUSY_COUNTERS = ("SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES "
+                 "SQ_WAVE_CYCLES SQ_INSTS_LDS GRBM_GUI_ACTIVE")
+
+
+def summarize_busy(counter_csv, agent_csv, bench_log):
+    """VALU and MFMA busy fractions of the decode kernels from one rocprofv3 --pmc run of
+    BUSY_COUNTERS, averaged over each kernel's dispatches.  GRBM_GUI_ACTIVE is summed over the
+    XCDs, so the active cycles of one XCD are GRBM_GUI_ACTIVE / Num_Xcc; a wave64 VALU instruction
+    occupies its SIMD for 4 cycles and SQ_ACTIVE_INST_VALU counts those in units of 4 cycles:
+      VALU busy = 4 SQ_ACTIVE_INST_VALU / (SIMDs x cycles)
+      MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x cycles)
+    and the MFMA rate counts 16 x 16 x 32 x 2 flops per instruction (v_mfma_f32_16x16x32_f16)."""
+    import csv
+    import collections
+    with open(agent_csv) as fh:
+        gpu = [r for r in csv.DictReader(fh) if r["Agent_Type"] == "GPU"][0]
+    simds, xcc = int(gpu["Simd_Count"]), int(gpu["Num_Xcc"])
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    with open(counter_csv) as fh:
+        for r in csv.DictReader(fh):
+            if "k_attn_" not in r["Kernel_Name"] and "k_merge" not in r["Kernel_Name"]:
+                continue
+            name = short_kernel_name(r["Kernel_Name"])
+            agg[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            dur[name][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    bench = None
+    with open(bench_log) as fh:
+        for line in fh:
+            if line.startswith("{"):
+                bench = json.loads(line)
+    lines = []
+    if bench:
+        lines += ["workload: %s" % bench["config"]["workload"], ""]
+    lines.append("SIMDs: %d, XCDs: %d" % (simds, xcc))
+    for name, d in agg.items():
+        avg = {c: sum(v) / len(v) for c, v in d.items()}
+        cyc = avg["GRBM_GUI_ACTIVE"] / xcc
+        ns = sum(dur[name].values()) / len(dur[name])
+        lines += ["", "kernel: %s (%d dispatches, %.2f us each under the profiler)" % (name, len(dur[name]), ns / 1e3)]
+        lines += ["  %s: %.6g" % (c, avg[c]) for c in sorted(avg)]
+        lines.append("  VALU busy: %.1f %%" % (100 * 4 * avg["SQ_ACTIVE_INST_VALU"] / (simds * cyc)))
+        lines.append("  MFMA busy: %.1f %%" % (100 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cyc)))
+        lines.append("  MFMA rate: %.1f TFLOP/s (dense f16 peak 2500)" % (avg["SQ_INSTS_MFMA"] * 16384 / ns / 1e3))
+        lines.append("  VALU instructions per wave: %.0f" % (avg["SQ_INSTS_VALU"] / avg["SQ_WAVES"]))
+    lines.append("source_hash: %s" % source_hash())
+    print("\n".join(lines))
 
 
 def summarize_stats(stats_csv, bench_log):
@@ -866,6 +922,9 @@ def main():
     ARGS = args = parse()
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_busy:
+        summarize_busy(*args.summarize_busy)
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.copy_probe_mib or 1024)
