@@ -394,11 +394,12 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32
  *  out:      device fp32 [batch][q_heads][128]; a sequence with no tokens
  *            gets zeros.
  *  num_splits: sequence splits per (b, kv head); 0 picks one from the shape.
- *            OAKEN caches split into pieces of at most 2048 / r tokens
- *            (r = 1, 4 or 16 query heads per workgroup: 1 when q_heads ==
- *            kv_heads, 4 up to 4 query heads per KV head, else 16), so they
- *            may use more splits than requested;
- *            kvq_decode_workspace_bytes applies the same rule.
+ *            Pieces are rounded up to whole 64-token steps (chunk-mixed:
+ *            whole chunks), so a split count that does not divide the
+ *            length evenly may come out lower; kvq_decode_workspace_bytes
+ *            applies the same rule.  The result does not depend on the
+ *            split count beyond binary32 rounding, and two calls with the
+ *            same arguments give the same bits.
  */
 kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t q_heads,
                            const int32_t* seq_len, int32_t max_len, float sm_scale, float* out,
