@@ -386,6 +386,23 @@ kvq_status decode_attn(const kvq_cache* c, const void* q, int32_t q_heads, const
 
 }  // namespace
 
+namespace kvq {
+
+// The (K, V) pairs go_codec in kvq_decode_uniform.hip dispatches to a kernel.
+bool decode_uniform_supported(const TensorArgs& k, const TensorArgs& v) {
+  if (v.axis != 0) return false;
+  if (v.group != 32 && v.group != 64 && v.group != 128) return false;
+  if (k.bits != v.bits || k.sym != v.sym || k.fmt != v.fmt) return false;
+  if (v.fmt == 1 || v.fmt == 2) return v.bits == 8 && !v.sym && k.axis == 0 && k.group == v.group;
+  if (v.sym && v.bits != 8) return false;
+  if (v.bits != 8 && v.bits != 4 && v.bits != 2) return false;
+  if (k.axis == 0) return k.group == v.group;
+  if (k.axis == 1) return k.group == 64 && !k.sym && (k.bits == 8 || k.bits == 4);
+  return false;
+}
+
+}  // namespace kvq
+
 extern "C" {
 
 kvq_status kvq_cache_bytes(const kvq_cache* c, kvq_cache_bytes_t* out) {

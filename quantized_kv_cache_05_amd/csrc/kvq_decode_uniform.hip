@@ -148,17 +148,6 @@ AttnParams make_attn_params(const CacheArgs& c, const DecodeLaunch& d) {
   return P;
 }
 
-bool decode_uniform_supported(const TensorArgs& k, const TensorArgs& v) {
-  if (v.axis != 0) return false;
-  if (v.group != 32 && v.group != 64 && v.group != 128) return false;
-  if (k.bits != v.bits || k.sym != v.sym || k.fmt != v.fmt) return false;
-  if (v.fmt == 1 || v.fmt == 2) return v.bits == 8 && !v.sym && k.axis == 0 && k.group == v.group;
-  if (v.sym && v.bits != 8) return false;
-  if (v.bits != 8 && v.bits != 4 && v.bits != 2) return false;
-  if (k.axis == 0) return k.group == v.group;
-  if (k.axis == 1) return k.group == 64 && !k.sym && (k.bits == 8 || k.bits == 4);
-  return false;
-}
 
 // Log-sum-exp merge of split partials: one workgroup of 1024 threads per
 // (b, query head): M = max m_j, L = sum l_j 2^(m_j - M), out = sum 2^(m_j - M) o_j / L.

@@ -1,16 +1,22 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 bench times (its own workload builders, automatic split count).
 
-The whole cache is built and decoded on the GPU; the oracle then recomputes
-a few sampled (batch, KV head) slices one by one from the same seeded
-inputs: codes, scales, zero-points, sparse entries, row pointers, perm and
-seg of the slice bit for bit, and the decode output rows of that slice's
-query heads within the attention bar.  Inputs of the oracle are regenerated
-on the host and never read back from the GPU (the Oaken thresholds are
-recomputed by the oracle from the calibration set and must equal the
-device's).
+The whole cache is built and decoded on the GPU and copied to the host once;
+the oracle then recomputes (batch, KV head) slices one by one from the same
+seeded inputs: codes, scales, zero-points, sparse entries, row pointers,
+perm and seg of the slice bit for bit, and the decode output rows of that
+slice's query heads within the attention bar.  Every slice is checked where
+the workload has at most FULL_LIMIT of them (all but workload 5's 10,240:
+there a seeded sample of SAMPLE_5 slices, with the first and last); the
+slices run on a pool of host threads (the oracle and the generator are C
+code that releases the interpreter lock).  Host RAM is printed with each
+test.  Inputs of the oracle are regenerated on the host and never read back
+from the GPU (the Oaken thresholds are recomputed by the oracle from the
+calibration set and must equal the device's).
 """
 import argparse
+import os
+from concurrent.futures import ThreadPoolExecutor, as_completed
 
 import numpy as np
 import pytest
@@ -26,6 +32,9 @@ torch = pytest.importorskip("torch")
 K = pytest.importorskip("quantized_kv_cache_05_amd")
 
 SM = bench.SM_SCALE
+FULL_LIMIT = 1024
+SAMPLE_5 = 2048
+WORKERS = min(16, os.cpu_count() or 1)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -37,23 +46,57 @@ def _gpu():
     yield
 
 
-def bh(t, B, H, b, h, dtype=np.uint8, per=None):
-    """Bytes of slice (b, h) of a [B][H][...] device buffer -> numpy of dtype (per: bytes per
-    slice, for buffers with spare bytes at the end)."""
+def host_ram_gib():
+    try:
+        with open("/proc/meminfo") as fh:
+            for line in fh:
+                if line.startswith("MemTotal:"):
+                    return int(line.split()[1]) / 2.0 ** 20
+    except OSError:
+        pass
+    return float("nan")
+
+
+def host(t, shape=None, dtype=np.uint8, nbytes=None):
+    """A device buffer copied to the host as numpy of dtype (the first nbytes bytes, for buffers
+    with spare bytes at the end), optionally reshaped."""
     flat = t.view(torch.uint8)
-    if per is not None:
-        flat = flat[:B * H * per]
-    return flat.view(B, H, -1)[b, h].cpu().numpy().view(dtype)
+    if nbytes is not None:
+        flat = flat[:nbytes]
+    a = flat.cpu().numpy().view(dtype)
+    return a.reshape(shape) if shape is not None else a
 
 
 def f32bits(a):
     return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
 
 
-def sampled_slices(B, H, seed):
+def slices_to_check(B, H, seed, limit=FULL_LIMIT):
+    every = [(b, h) for b in range(B) for h in range(H)]
+    if len(every) <= limit:
+        return every
     rng = np.random.default_rng(seed)
-    picks = {(0, 0), (B - 1, H - 1), (int(rng.integers(B)), int(rng.integers(H)))}
+    picks = {(0, 0), (B - 1, H - 1)}
+    for i in rng.choice(len(every), size=limit - 2, replace=False):
+        picks.add(every[int(i)])
     return sorted(picks)
+
+
+def run_slices(label, B, H, slices, fn):
+    """fn(b, h) -> max relative attention error of the slice's query rows; raises on a mismatch."""
+    print("%s: host RAM %.0f GiB, checking %d of %d (batch, KV head) slices on %d threads"
+          % (label, host_ram_gib(), len(slices), B * H, WORKERS), flush=True)
+    worst, done = 0.0, 0
+    step = max(1, len(slices) // 8)
+    with ThreadPoolExecutor(WORKERS) as ex:
+        futs = {ex.submit(fn, b, h): (b, h) for b, h in slices}
+        for f in as_completed(futs):
+            worst = max(worst, f.result())
+            done += 1
+            if done % step == 0 or done == len(slices):
+                print("  %s: %d / %d slices, max rel err so far %.3e" % (label, done, len(slices), worst),
+                      flush=True)
+    assert worst <= ATTN_BAR and worst <= ATTN_TIGHT, (label, worst)
 
 
 def run_bench_step(idx):
@@ -70,11 +113,9 @@ def run_bench_step(idx):
     return wl, wl.out.cpu().numpy()
 
 
-def check_rows(out, b, h, G, q, kh, vh, label):
+def rows_err(out, b, h, G, q, kh, vh):
     ref = oracle.attention(q[h * G:(h + 1) * G], kh[None], vh[None], SM)
-    err = float(rel_err_rows(out[b, h * G:(h + 1) * G], ref).max())
-    print("%s b%d h%d: max rel err %.3e" % (label, b, h, err), flush=True)
-    assert err <= ATTN_BAR and err <= ATTN_TIGHT, (label, b, h, err)
+    return float(rel_err_rows(out[b, h * G:(h + 1) * G], ref).max())
 
 
 def test_paged_full():
@@ -84,23 +125,24 @@ def test_paged_full():
     c = wl.caches[0]
     P, pool = c.desc.page_tokens, c.desc.num_pages
     table = c.block_table.cpu().numpy()
-    codes = c.buf("k.codes")
-    for b, h in sampled_slices(B, H, 107):
+    hb = {name: (host(c.buf(name + ".codes"), (pool, H, P, 128)),
+                 host(c.buf(name + ".scale"), (pool, H, P), np.uint32)) for name in ("k", "v")}
+    Q = w.q()
+
+    def one(b, h):
         t = np.arange(T)
         pg, r = table[b, t // P], t % P
         deq = {}
         for name, tensor in (("k", 0), ("v", 1)):
             x = w.kv(tensor, b, b + 1, h, h + 1)[0, 0]
             oc, os_, oz = oracle.quant_rows(x, 128, 8, True)
-            allc = c.buf(name + ".codes").view(torch.uint8).view(pool, H, P, 128)[:, h].cpu().numpy()
-            got = unpack_layout(allc[pg, r], 8, name.upper(), True)
-            assert np.array_equal(got, oc), (name, b, h)
-            alls = c.buf(name + ".scale").view(torch.uint8).view(pool, H, P, 4)[:, h].cpu().numpy()
-            assert np.array_equal(alls[pg, r].view(np.uint32)[:, 0], f32bits(os_)[:, 0]), (name, b, h)
+            codes, scale = hb[name]
+            assert np.array_equal(unpack_layout(codes[pg, h, r], 8, name.upper(), True), oc), (name, b, h)
+            assert np.array_equal(scale[pg, h, r], f32bits(os_)[:, 0]), (name, b, h)
             deq[name] = oracle.dequant_rows(oc, os_, oz, 128, True)
-        q = w.q(b, b + 1)[0]
-        check_rows(out, b, h, G, q, deq["k"], deq["v"], "workload 7")
-    assert codes.numel() == pool * H * P * 128
+        return rows_err(out, b, h, G, Q[b], deq["k"], deq["v"])
+
+    run_slices("workload 7", B, H, slices_to_check(B, H, 107), one)
 
 
 @pytest.mark.parametrize("idx,fmt", [(6, "e4m3"), (9, "e5m2")])
@@ -111,18 +153,22 @@ def test_fp8_full(idx, fmt):
     B, H, T, G = w.batch, w.kv_heads, w.tokens, w.q_heads // w.kv_heads
     c = wl.caches[0]
     S = c.desc.max_seq
-    for b, h in sampled_slices(B, H, 106):
+    hb = {name: (host(c.buf(name + ".codes"), (B, H, S, 128)), host(c.buf(name + ".scale"), (B, H, S), np.uint32))
+          for name in ("k", "v")}
+    Q = w.q()
+
+    def one(b, h):
         deq = {}
         for name, tensor in (("k", 0), ("v", 1)):
             x = w.kv(tensor, b, b + 1, h, h + 1)[0, 0]
             oc, os_ = quant_rows(x, 128)
-            got = unpack_layout(bh(c.buf(name + ".codes"), B, H, b, h).reshape(S, 128)[:T], 8, name.upper())
-            assert np.array_equal(got, oc), (name, b, h)
-            gs = bh(c.buf(name + ".scale"), B, H, b, h, np.float32).reshape(S, 1)[:T]
-            assert np.array_equal(f32bits(gs), f32bits(os_)), (name, b, h)
+            codes, scale = hb[name]
+            assert np.array_equal(unpack_layout(codes[b, h, :T], 8, name.upper()), oc), (name, b, h)
+            assert np.array_equal(scale[b, h, :T], f32bits(os_)[:, 0]), (name, b, h)
             deq[name] = dequant_rows(oc, os_, 128)
-        q = w.q(b, b + 1)[0]
-        check_rows(out, b, h, G, q, deq["k"], deq["v"], "workload %d" % idx)
+        return rows_err(out, b, h, G, Q[b], deq["k"], deq["v"])
+
+    run_slices("workload %d" % idx, B, H, slices_to_check(B, H, 100 + idx), one)
 
 
 @pytest.mark.parametrize("idx", [1, 2])
@@ -133,22 +179,24 @@ def test_uniform_token_full(idx):
     bits, sym, g = wl.bits, bool(wl.sym), wl.group
     c = wl.caches[0]
     S, RB, NG = c.desc.max_seq, 128 * bits // 8, 128 // g
-    for b, h in sampled_slices(B, H, 100 + idx):
+    hb = {name: (host(c.buf(name + ".codes"), (B, H, S, RB)), host(c.buf(name + ".scale"), (B, H, S, NG), np.uint32),
+                 None if sym else host(c.buf(name + ".zero"), (B, H, S, NG))) for name in ("k", "v")}
+    Q = w.q()
+
+    def one(b, h):
         deq = {}
         for name, tensor in (("k", 0), ("v", 1)):
             x = w.kv(tensor, b, b + 1, h, h + 1)[0, 0]
             oc, os_, oz = oracle.quant_rows(x, g, bits, sym)
-            got = unpack_layout(bh(c.buf(name + ".codes"), B, H, b, h).reshape(S, RB)[:T], bits,
-                                name.upper(), sym)
-            assert np.array_equal(got, oc), (name, b, h)
-            gs = bh(c.buf(name + ".scale"), B, H, b, h, np.float32).reshape(S, NG)[:T]
-            assert np.array_equal(f32bits(gs), f32bits(os_)), (name, b, h)
+            codes, scale, zero = hb[name]
+            assert np.array_equal(unpack_layout(codes[b, h, :T], bits, name.upper(), sym), oc), (name, b, h)
+            assert np.array_equal(scale[b, h, :T], f32bits(os_)), (name, b, h)
             if not sym:
-                gz = bh(c.buf(name + ".zero"), B, H, b, h).reshape(S, NG)[:T]
-                assert np.array_equal(gz, oz), (name, b, h)
+                assert np.array_equal(zero[b, h, :T], oz), (name, b, h)
             deq[name] = oracle.dequant_rows(oc, os_, oz, g, sym)
-        q = w.q(b, b + 1)[0]
-        check_rows(out, b, h, G, q, deq["k"], deq["v"], "workload %d" % idx)
+        return rows_err(out, b, h, G, Q[b], deq["k"], deq["v"])
+
+    run_slices("workload %d" % idx, B, H, slices_to_check(B, H, 100 + idx), one)
 
 
 def test_channel_k_gqa_full():
@@ -157,25 +205,28 @@ def test_channel_k_gqa_full():
     B, H, T, G = w.batch, w.kv_heads, w.tokens, w.q_heads // w.kv_heads
     c = wl.caches[0]
     S = c.desc.max_seq
-    for b, h in sampled_slices(B, H, 103):
+    kcodes = host(c.buf("k.codes"), (B, H, S, 64))
+    kscale = host(c.buf("k.scale"), (B, H, S // 64, 128), np.uint32)
+    kzero = host(c.buf("k.zero"), (B, H, S // 64, 128))
+    vcodes = host(c.buf("v.codes"), (B, H, S, 64))
+    vscale = host(c.buf("v.scale"), (B, H, S, 2), np.uint32)
+    vzero = host(c.buf("v.zero"), (B, H, S, 2))
+    Q = w.q()
+
+    def one(b, h):
         k = w.kv(0, b, b + 1, h, h + 1)[0, 0]
         v = w.kv(1, b, b + 1, h, h + 1)[0, 0]
         kc, ks, kz = oracle.quant_channel_blocks(k, 64, 4)
-        got = unpack_layout(bh(c.buf("k.codes"), B, H, b, h).reshape(S, 64)[:T], 4, "K")
-        assert np.array_equal(got, kc), (b, h)
-        gs = bh(c.buf("k.scale"), B, H, b, h, np.float32).reshape(S // 64, 128)[:T // 64]
-        gz = bh(c.buf("k.zero"), B, H, b, h).reshape(S // 64, 128)[:T // 64]
-        assert np.array_equal(f32bits(gs), f32bits(ks)) and np.array_equal(gz, kz), (b, h)
+        assert np.array_equal(unpack_layout(kcodes[b, h, :T], 4, "K"), kc), (b, h)
+        assert np.array_equal(kscale[b, h, :T // 64], f32bits(ks)) and np.array_equal(kzero[b, h, :T // 64], kz)
         vc, vs, vz = oracle.quant_rows(v, 64, 4)
-        gotv = unpack_layout(bh(c.buf("v.codes"), B, H, b, h).reshape(S, 64)[:T], 4, "V")
-        assert np.array_equal(gotv, vc), (b, h)
-        gvs = bh(c.buf("v.scale"), B, H, b, h, np.float32).reshape(S, 2)[:T]
-        gvz = bh(c.buf("v.zero"), B, H, b, h).reshape(S, 2)[:T]
-        assert np.array_equal(f32bits(gvs), f32bits(vs)) and np.array_equal(gvz, vz), (b, h)
+        assert np.array_equal(unpack_layout(vcodes[b, h, :T], 4, "V"), vc), (b, h)
+        assert np.array_equal(vscale[b, h, :T], f32bits(vs)) and np.array_equal(vzero[b, h, :T], vz), (b, h)
         kh = oracle.dequant_channel_blocks(kc, ks, kz, 64)
         vh = oracle.dequant_rows(vc, vs, vz, 64)
-        q = w.q(b, b + 1)[0]
-        check_rows(out, b, h, G, q, kh, vh, "workload 3")
+        return rows_err(out, b, h, G, Q[b], kh, vh)
+
+    run_slices("workload 3", B, H, slices_to_check(B, H, 103), one)
 
 
 def test_chunk_mixed_full():
@@ -187,30 +238,36 @@ def test_chunk_mixed_full():
     dev_bits = wl.bits.cpu().numpy()
     dev_perm = c.buf("perm").view(torch.int32).view(B, C).cpu().numpy()
     dev_seg = c.buf("seg").view(torch.int32).view(B, 4).cpu().numpy()
-    checked = set()
-    for b, h in sampled_slices(B, H, 104):
+    per_b = {}
+    for b in range(B):  # the chunk search and the reorder are per sequence
         bits_c, _ = oracle.chunk_bits(*w.chunk_embeddings(b))
-        if b not in checked:
-            assert np.array_equal(dev_bits[b], bits_c), b
-            checked.add(b)
+        assert np.array_equal(dev_bits[b], bits_c), b
         perm_o, seg_o = oracle.reorder(bits_c[None])
         assert np.array_equal(dev_perm[b], perm_o[0]) and np.array_equal(dev_seg[b], seg_o[0]), b
-        n16, n4, n2, n = seg_o[0]
+        per_b[b] = perm_o[0], seg_o[0]
+    hb = {}
+    for name in ("k", "v"):
+        hb[name] = dict(
+            p16=host(c.buf(name + ".codes16"), (B, H, C, CT, 128), np.uint16, nbytes=B * H * C * CT * 256),
+            p4=host(c.buf(name + ".codes"), (B, H, C, CT, 64)),
+            s4=host(c.buf(name + ".scale"), (B, H, C, CT, 4), np.uint32),
+            z4=host(c.buf(name + ".zero"), (B, H, C, CT, 4)),
+            p2=host(c.buf(name + ".codes2"), (B, H, C, CT, 32)),
+            s2=host(c.buf(name + ".scale2"), (B, H, C, CT, 4), np.uint32),
+            z2=host(c.buf(name + ".zero2"), (B, H, C, CT, 4)))
+    Q = w.q()
+
+    def one(b, h):
+        perm_o, (n16, n4, n2, n) = per_b[b]
         deq = {}
         for name, tensor in (("k", 0), ("v", 1)):
             x = w.kv(tensor, b, b + 1, h, h + 1)[0, 0]
             lay = name.upper()
-            p16 = f16_layout(bh(c.buf(name + ".codes16"), B, H, b, h, np.uint16, per=C * CT * 256)
-                             .reshape(C, CT, 128), lay)
-            p4 = unpack_layout(bh(c.buf(name + ".codes"), B, H, b, h).reshape(C, CT, 64), 4, lay)
-            s4 = bh(c.buf(name + ".scale"), B, H, b, h, np.float32).reshape(C, CT, 4)
-            z4 = bh(c.buf(name + ".zero"), B, H, b, h).reshape(C, CT, 4)
-            p2 = unpack_layout(bh(c.buf(name + ".codes2"), B, H, b, h).reshape(C, CT, 32), 2, lay)
-            s2 = bh(c.buf(name + ".scale2"), B, H, b, h, np.float32).reshape(C, CT, 4)
-            z2 = bh(c.buf(name + ".zero2"), B, H, b, h).reshape(C, CT, 4)
+            pools = hb[name]
+            p16 = f16_layout(pools["p16"][b, h], lay)
             xh = np.zeros((T, 128), np.float32)
             for j in range(n):
-                src = perm_o[0, j]
+                src = perm_o[j]
                 rows = x[src * CT:(src + 1) * CT]
                 if j < n16:
                     assert np.array_equal(p16[j], rows), (name, b, h, j)
@@ -218,14 +275,16 @@ def test_chunk_mixed_full():
                     continue
                 nb, kk = (4, j - n16) if j < n16 + n4 else (2, j - n16 - n4)
                 oc, os_, oz = oracle.quant_rows(rows, 32, nb)
-                pc, ps, pz = (p4, s4, z4) if nb == 4 else (p2, s2, z2)
-                assert np.array_equal(pc[kk], oc), (name, b, h, j)
-                assert np.array_equal(f32bits(ps[kk]), f32bits(os_)), (name, b, h, j)
-                assert np.array_equal(pz[kk], oz), (name, b, h, j)
+                pc, ps, pz = ((pools["p4"], pools["s4"], pools["z4"]) if nb == 4 else
+                              (pools["p2"], pools["s2"], pools["z2"]))
+                assert np.array_equal(unpack_layout(pc[b, h, kk], nb, lay), oc), (name, b, h, j)
+                assert np.array_equal(ps[b, h, kk], f32bits(os_)), (name, b, h, j)
+                assert np.array_equal(pz[b, h, kk], oz), (name, b, h, j)
                 xh[src * CT:(src + 1) * CT] = oracle.dequant_rows(oc, os_, oz, 32)
             deq[name] = xh
-        q = w.q(b, b + 1)[0]
-        check_rows(out, b, h, G, q, deq["k"], deq["v"], "workload 4")
+        return rows_err(out, b, h, G, Q[b], deq["k"], deq["v"])
+
+    run_slices("workload 4", B, H, slices_to_check(B, H, 104), one)
 
 
 def test_oaken_full():
@@ -241,24 +300,32 @@ def test_oaken_full():
             oracle.hist_f16(w.calibration(tensor, s), hist)
         thr.append(oracle.thresholds_from_hist(hist))
         assert np.array_equal(f32bits(thr[-1]), f32bits(np.array(wl.thr[tensor], np.float32))), tensor
-    for b, h in sampled_slices(B, H, 105):
+    hb = {}
+    for name in ("k", "v"):
+        hb[name] = dict(codes=host(c.buf(name + ".codes"), (B, H, S, 64)),
+                        scale=host(c.buf(name + ".scale"), (B, H, S, 2), np.uint32),
+                        oscale=host(c.buf(name + ".oscale"), (B, H, S, 2), np.uint32),
+                        zero=host(c.buf(name + ".zero"), (B, H, S, 2)),
+                        rowptr=host(c.buf(name + ".rowptr"), (B, H, S + 1), np.uint32),
+                        sparse=host(c.buf(name + ".sparse"), (B, H, cap), np.uint16))
+    Q = w.q()
+
+    def one(b, h):
         deq = {}
         for name, tensor in (("k", 0), ("v", 1)):
             x = w.kv(tensor, b, b + 1, h, h + 1)[0, 0]
             t = thr[tensor]
             oc, os_, oz, oo, oe, on = oracle.oaken_rows(x, t, 64)
-            got = unpack_layout(bh(c.buf(name + ".codes"), B, H, b, h).reshape(S, 64)[:T], 4, name.upper())
-            assert np.array_equal(got, oc), (name, b, h)
-            for buf, ref, dt in (("scale", os_, np.float32), ("oscale", oo, np.float32)):
-                g = bh(c.buf(name + "." + buf), B, H, b, h, dt).reshape(S, 2)[:T]
-                assert np.array_equal(f32bits(g), f32bits(ref)), (name, buf, b, h)
-            gz = bh(c.buf(name + ".zero"), B, H, b, h).reshape(S, 2)[:T]
-            assert np.array_equal(gz, oz), (name, b, h)
-            rp = bh(c.buf(name + ".rowptr"), B, H, b, h, np.uint32)[:T + 1].astype(np.int64)
+            d = hb[name]
+            assert np.array_equal(unpack_layout(d["codes"][b, h, :T], 4, name.upper()), oc), (name, b, h)
+            assert np.array_equal(d["scale"][b, h, :T], f32bits(os_)), (name, b, h)
+            assert np.array_equal(d["oscale"][b, h, :T], f32bits(oo)), (name, b, h)
+            assert np.array_equal(d["zero"][b, h, :T], oz), (name, b, h)
+            rp = d["rowptr"][b, h, :T + 1].astype(np.int64)
             assert rp[0] == 0 and np.array_equal(np.diff(rp), on), (name, b, h)
-            sp = bh(c.buf(name + ".sparse"), B, H, b, h, np.uint16)[:cap]
             flat = np.concatenate([oe[i, :on[i]] for i in range(T)])
-            assert np.array_equal(sp[:rp[T]], flat), (name, b, h)
+            assert np.array_equal(d["sparse"][b, h, :rp[T]], flat), (name, b, h)
             deq[name] = oracle.oaken_dequant_rows(oc, os_, oz, oo, oe, on, t, 64)
-        q = w.q(b, b + 1)[0]
-        check_rows(out, b, h, G, q, deq["k"], deq["v"], "workload 5")
+        return rows_err(out, b, h, G, Q[b], deq["k"], deq["v"])
+
+    run_slices("workload 5", B, H, slices_to_check(B, H, 105, SAMPLE_5), one)
