@@ -14,8 +14,9 @@
 //           B = V codes, one k-step of 32 tokens, 8 column blocks of 16
 //           channels.
 // Codes enter the matrix cores as exact small fp16 integers OFF + c, built
-// with a magic-exponent OR (OFF = 16 for 4-bit, 4 for 2-bit, 256 / 384 for
-// 8-bit codes).  Group scales and zero-points stay in binary32 outside the
+// with a magic-exponent OR (OFF = 16 for 4-bit, 4 for 2-bit; 8-bit codes
+// subtract their offset of 256 / 384 with one exact packed fp16 add, OFF =
+// 0).  Group scales and zero-points stay in binary32 outside the
 // products: per token t and channel group g
 //   score = sum_g s[t][g] * (C_g[t] - (OFF + z[t][g]) * Q_g),  Q_g = sum_{d in g} q_d,
 // which equals sum_d q_d s (c_td - z) up to binary32 rounding.  On the V side
@@ -94,7 +95,12 @@ __device__ __forceinline__ void split_pair(float a, float b, unsigned& hi, unsig
 
 // ---------------------------------------------------------------------------
 // K codecs: load a token row's 4 slices for lane group q4, and form k-step s
-// as 4 fp16 pairs (channels v, v + 4 of the slice), value OFF + code.
+// as 4 fp16 pairs (channels v, v + 4 of the slice), value OFF + code.  The
+// widening leaves an offset under the code (the exponent's implicit bit);
+// the per-group bias (OFF + z) sum q removes it after the product.  A large
+// offset inflates the binary32 partial sums of the matrix cores and costs
+// absolute precision in the scores, so the 8-bit codecs subtract theirs
+// exactly in fp16 first (OFF = 0).
 
 struct KI4 {
   static constexpr int RB = 64, OFF = 16, BITS = 4;
@@ -136,8 +142,11 @@ struct KI2 {
 
 template <bool SYM_>
 struct KI8 {
-  static constexpr int RB = 128, OFF = SYM_ ? 384 : 256, BITS = 8;
+  static constexpr int RB = 128, OFF = 0, BITS = 8;
   static constexpr bool SYM = SYM_, F16 = false;
+  // 256 + byte (offset binary for the signed codes: 384 + c) minus that
+  // offset, as an exact fp16 pair: the code itself
+  static constexpr unsigned kUnoffset = SYM_ ? 0xDE00DE00u : 0xDC00DC00u;  // -(384, 384) or -(256, 256)
   u4_t a, b;
   __device__ __forceinline__ void load(const uint8_t* row, int q4) {
     a = ld_nt<u4_t>(row + q4 * 32);
@@ -152,7 +161,10 @@ struct KI8 {
     }
     u4_t o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = (perm(hi, lo, sel_bytes(i)) << 2) | 0x5C005C00u;
+    for (int i = 0; i < 4; ++i) {
+      const unsigned w = (perm(hi, lo, sel_bytes(i)) << 2) | 0x5C005C00u;
+      o[i] = __builtin_bit_cast(unsigned, __builtin_bit_cast(h2_t, w) + __builtin_bit_cast(h2_t, kUnoffset));
+    }
     return o;
   }
 };
@@ -241,14 +253,24 @@ struct KF16 {
 // are built from the rows' z bytes as ((z << ZSH[par]) & ZMASK[par]) | ZMAGIC,
 // par = 1 for odd blocks when ZODD.
 
+// kWeightScaleNote.  The V weights w = p s (p <= 1 the softmax numerator, s
+// the token group's V scale; p alone for fp16 rows) enter the matrix cores as
+// fp16 hi + lo pairs.  Most p of a long sequence are far below 1, so w would
+// often be an fp16 subnormal, and the matrix cores do not multiply
+// subnormal operands exactly (a row of 4097 E4M3 tokens lost 1.3e-4 of its
+// norm that way).  Each codec therefore scales its weights by WS, a power of
+// two as large as keeps s WS (the largest weight) below the fp16 maximum for
+// any fp16 input (the bound is noted at each WS), so that only weights far
+// too small to matter stay subnormal; WS is exact, and the output blocks
+// carry it (fac) until the wave's state leaves the loop.
 struct VI4 {
-  static constexpr float WS = 1.0f;  // weight scale (see VE5)
+  static constexpr float WS = 4.0f;  // weight scale (see kWeightScaleNote): s 4 <= 34,935
   static constexpr int RB = 64, BITS = 4;
   static constexpr bool SYM = false, F16 = false, ZODD = true, ZP = true, MASK_ROWS = false;
   static constexpr unsigned ZMAGIC = 0xE400E400u;
   static constexpr unsigned ZMASK[2] = {0x000F000Fu, 0x00F000F0u};
   static constexpr int ZSH[2] = {0, 4};
-  static constexpr float fac(int j) { return (j & 1) ? 16.0f : 1.0f; }
+  static constexpr float fac(int j) { return (j & 1) ? 16.0f * WS : WS; }
   unsigned r[8];
   __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
 #pragma unroll
@@ -265,7 +287,7 @@ struct VI4 {
 };
 
 struct VI2 {
-  static constexpr float WS = 1.0f;  // weight scale (see VE5)
+  static constexpr float WS = 1.0f;  // weight scale (see kWeightScaleNote): s <= 43,669
   static constexpr int RB = 32, BITS = 2;
   static constexpr bool SYM = false, F16 = false, ZODD = false, ZP = true, MASK_ROWS = false;
   static constexpr unsigned ZMAGIC = 0xE400E400u;
@@ -293,13 +315,13 @@ struct VI2 {
 
 template <bool SYM_>
 struct VI8 {
-  static constexpr float WS = 1.0f;  // weight scale (see VE5)
+  static constexpr float WS = 64.0f;  // weight scale (see kWeightScaleNote): s 64 <= 33,011
   static constexpr int RB = 128, BITS = 8;
   static constexpr bool SYM = SYM_, F16 = false, ZODD = false, ZP = true, MASK_ROWS = false;
   static constexpr unsigned ZMAGIC = 0xE400E400u;
   static constexpr unsigned ZMASK[2] = {0x00FF00FFu, 0x00FF00FFu};
   static constexpr int ZSH[2] = {0, 0};
-  static constexpr float fac(int) { return 1.0f; }
+  static constexpr float fac(int) { return WS; }
   unsigned w0[8], w1[8];  // codes 0-3 and 4-7 of the column word, per row (offset binary)
   __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
 #pragma unroll
@@ -325,10 +347,10 @@ struct VI8 {
 // zero-point; rows past the valid range are cleared (a stray byte could be
 // the NaN pattern, and 0 * NaN would poison the product).
 struct VE4 {
-  static constexpr float WS = 1.0f;  // weight scale (see VE5)
+  static constexpr float WS = 256.0f;  // weight scale (see kWeightScaleNote): s 256 <= 37,431
   static constexpr int RB = 128, BITS = 8;
   static constexpr bool SYM = true, F16 = false, ZODD = false, ZP = false, MASK_ROWS = true;
-  static constexpr float fac(int) { return 1.0f; }
+  static constexpr float fac(int) { return WS; }
   unsigned w0[8], w1[8];  // codes of channels n16 + 16 e, e = 0-3 and 4-7, per row
   __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
 #pragma unroll
@@ -357,13 +379,9 @@ struct VE4 {
 // E5M2 V codes: the B operand pair (rows 2p, 2p + 1) of column block j is
 // byte j mod 4 of the two rows' words moved to the high bytes.  No
 // zero-point; rows past the valid range are cleared (a stray byte could be
-// an infinity or NaN pattern).  The scale max|x| / 57344 is small, so the
-// weights p s would often be fp16 subnormals, which the matrix cores do not
-// multiply exactly: the weights enter as p (s 2^15) (exact scaling; s 2^15
-// stays below 37,450 for any fp16 input) and the output blocks carry the
-// factor 2^15, removed when the wave's state leaves the loop.
+// an infinity or NaN pattern).
 struct VE5 {
-  static constexpr float WS = 32768.0f;
+  static constexpr float WS = 32768.0f;  // weight scale (see kWeightScaleNote): s 2^15 <= 37,450
   static constexpr int RB = 128, BITS = 8;
   static constexpr bool SYM = true, F16 = false, ZODD = false, ZP = false, MASK_ROWS = true;
   static constexpr float fac(int) { return WS; }
@@ -390,10 +408,10 @@ struct VE5 {
 };
 
 struct VF16 {
-  static constexpr float WS = 1.0f;  // weight scale (see VE5)
+  static constexpr float WS = 32768.0f;  // weight scale (see kWeightScaleNote): the weight is p <= 1
   static constexpr int RB = 256, BITS = 16;
   static constexpr bool SYM = false, F16 = true, ZODD = false, ZP = false, MASK_ROWS = true;
-  static constexpr float fac(int) { return 1.0f; }
+  static constexpr float fac(int) { return WS; }
   u4_t r[8];
   __device__ __forceinline__ void load(const uint8_t* row0, int n16) {
 #pragma unroll

@@ -796,8 +796,8 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
         for (int g = 0; g < NGV; ++g) {
           float w0, w1;
           if constexpr (VC::F16) {
-            w0 = p[0][i];
-            w1 = p[1][i];
+            w0 = p[0][i] * VC::WS;
+            w1 = p[1][i] * VC::WS;
           } else {
             w0 = ok[0] ? p[0][i] * (sv[0][g] * VC::WS) : 0.0f;
             w1 = ok[1] ? p[1][i] * (sv[1][g] * VC::WS) : 0.0f;

@@ -5,8 +5,8 @@
 // not depend on token order, so the two classes are attended slot by slot.
 // A wave takes whole groups (operand layouts as in kvq_attn.h):
 //  significant K  the channel scales are folded into the query, A = q_d s_d
-//                 split into fp16 hi + lo, B = codes as 384 + c, so
-//                 score = C - 384 sum_d q_d s_d;
+//                 split into fp16 hi + lo, B = the signed codes c (widened
+//                 exactly, the offset subtracted in fp16), so score = C;
 //  base           base is the mean of the dequantized significant rows, so
 //                 q . base is the mean of their scores: base is never read;
 //  other K        score = q . base + sum_g s_g (C_g - (4 + z_g) Q_g), as for
@@ -19,6 +19,11 @@
 
 namespace kvq {
 namespace {
+
+// Weight scale of the significant V rows: the weights are p <= 1, so p 2^15
+// stays finite in fp16.
+constexpr float kSigWS = 32768.0f;
+
 
 constexpr int kSigSlots = 16;  // significant-row slots per group
 constexpr int kOthSlots = 64;  // other-row slots per group
@@ -227,7 +232,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     float qs[GI];
 #pragma unroll
     for (int i = 0; i < GI; ++i) qs[i] = R == 1 ? lane0(part) : __shfl(part, 4 * QRW::slot_query(q4, i), 64);
-    *reinterpret_cast<float2*>(&vscl[wave][2 * lane]) = vs2;
+    // the significant-V weights enter the matrix cores scaled by kSigWS (kept
+    // clear of fp16 subnormals, see kWeightScaleNote); the channel scales in
+    // the table carry its inverse (both exact powers of two)
+    *reinterpret_cast<float2*>(&vscl[wave][2 * lane]) = float2{vs2.x * (1.0f / kSigWS), vs2.y * (1.0f / kSigWS)};
     wave_lds_sync();
     f4_t c = zero4;
 #pragma unroll
@@ -324,7 +332,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int i = 0; i < GI; ++i) {
       const int m = QRW::slot_query(q4, i);
       unsigned hi, lo;
-      split_pair(pS[i], 0.0f, hi, lo);
+      split_pair(pS[i] * kSigWS, 0.0f, hi, lo);
       if (QRW::slot_owner(q4) && m < R) {
         W.w[0][0][m][n16] = (unsigned short)(hi & 0xFFFFu);
         W.w[0][0][m][16 + n16] = (unsigned short)(hi >> 16);
