@@ -188,9 +188,10 @@ typedef struct kvq_tensor {
   int32_t format;     /* KVQ_FMT_INT or KVQ_FMT_E4M3 */
   float thr[4];       /* OAKEN: T_lo_outer, T_lo_inner, T_hi_inner, T_hi_outer (inner ones
                          are informational; [Oaken] §3.2.1) */
-  int64_t sparse_cap; /* OAKEN: capacity of `sparse` per (b, h), in entries; a multiple
-                         of 4, so that every (b, h) list starts 8-byte aligned (decode
-                         reads four entries per load); else KVQ_ERR_ALIGNMENT */
+  int64_t sparse_cap; /* OAKEN: capacity of `sparse` per (b, h), in entries, at most
+                         2^31 - 4 (else KVQ_ERR_INVALID_ARG); a multiple of 4, so that
+                         every (b, h) list starts 8-byte aligned (decode reads four
+                         entries per load); else KVQ_ERR_ALIGNMENT */
   void* codes;
   float* scale;
   uint8_t* zero;

@@ -70,7 +70,8 @@ kvq_status check_config(const kvq_cache* c) {
         if (!is_pow2_group(t->group)) return KVQ_ERR_INVALID_ARG;
         if (!std::isfinite(t->thr[0]) || !std::isfinite(t->thr[3]) || !(t->thr[0] < t->thr[3]))
           return KVQ_ERR_INVALID_ARG;
-        if (t->sparse_cap < 0 || t->sparse_cap > 0xFFFFFFFFll) return KVQ_ERR_INVALID_ARG;
+        // below 2^31 entries: entry byte offsets within a list fit 32 bits
+        if (t->sparse_cap < 0 || t->sparse_cap > 0x7FFFFFFCll) return KVQ_ERR_INVALID_ARG;
         // lists start 8-byte aligned: decode reads them four entries per load
         if (t->sparse_cap % 4) return KVQ_ERR_ALIGNMENT;
       }

@@ -31,10 +31,11 @@ __device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v
 // of the part it has already combined, so it covers lanes differing in bits
 // 0-1, 0-2 or 0-3 like the xor exchanges 1, 2, 4, 8.  Callers keep every
 // lane of a 16-lane row active (a read of an inactive lane gives 0).
+// (The moved value has no "old" operand, so the compiler can fold the move
+// into the instruction that consumes it, e.g. v_max_f32 with a DPP operand.)
 template <int CTRL>
 __device__ __forceinline__ float dpp_row(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF,
-                                                               false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 template <int M>

@@ -68,17 +68,21 @@ __device__ __forceinline__ uint32_t e5m2_code(float y) {
 // |y| 2^-21 (the reciprocal's error plus the two roundings).  So where y lies
 // farther than |y| 2^-19 from every half-integer, rne(y) = rne(fl(x / s));
 // elsewhere (near-ties, exact ties, and anything not finite) `near` is set and
-// the caller divides.  Both tests are exact: y - rne(y) is exact (Sterbenz),
-// and the fused sum rounds monotonically against the representable 0.5.
+// the caller divides.  Every caller knows a power of two M >= |y| (M = 2^bits
+// for the codes: |x / s| <= 2^bits - 1 up to rounding; 32 for the Oaken
+// magnitudes), so the test is |y - rne(y)| < 0.5 - M 2^-19, exact (y - rne(y)
+// is exact by Sterbenz, and both sides are representable).
 __device__ __forceinline__ float recip_refined(float s) {
   const float r0 = __builtin_amdgcn_rcpf(s);
   return s != 0.0f ? fmaf(fmaf(-s, r0, 1.0f), r0, r0) : 0.0f;  // s = 0: every y is 0
 }
+template <int M>
 __device__ __forceinline__ float rne_quot(float x, float r, bool& near) {
 #pragma clang fp contract(off)
+  constexpr float kAccept = 0.5f - (float)M * 0x1p-19f;
   const float y = x * r;
   const float n = rintf(y);
-  near |= !(fmaf(fabsf(y), 0x1p-19f, fabsf(y - n)) < 0.5f);
+  near |= !(fabsf(y - n) < kAccept);
   return n;
 }
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0ull; }
@@ -116,7 +120,7 @@ __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint
     bool near = false;
     float n[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) n[k] = rne_quot(x[k], r, near);
+    for (int k = 0; k < 8; ++k) n[k] = rne_quot<128>(x[k], r, near);
     if (wave_any(near) && near) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) n[k] = rintf(x[k] / s);
@@ -142,10 +146,10 @@ __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint
     s = (hi - lo) / QMAX;
     const float r = recip_refined(s);  // s = 0: z = 0 and all codes 0
     bool near = false;
-    float zf = rne_quot(-lo, r, near);
+    float zf = rne_quot<(1 << BITS)>(-lo, r, near);
     float n[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) n[k] = rne_quot(xm[k], r, near);
+    for (int k = 0; k < 8; ++k) n[k] = rne_quot<(1 << BITS)>(xm[k], r, near);
     if (wave_any(near) && near) {
       zf = rintf(-lo / s);
 #pragma unroll
@@ -156,8 +160,8 @@ __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint
     uint64_t packed = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      // an excluded value takes the zero-point (it decodes to 0)
-      const float q = ((valid >> k) & 1u) ? __builtin_amdgcn_fmed3f(n[k] + zf, 0.0f, QMAX) : zf;
+      // an excluded value (xm = 0, so n = 0) takes the zero-point: it decodes to 0
+      const float q = __builtin_amdgcn_fmed3f(n[k] + zf, 0.0f, QMAX);
       packed |= (uint64_t)(uint32_t)q << (BITS * k);
     }
     plo = (uint32_t)packed;
@@ -695,35 +699,54 @@ __global__ __launch_bounds__(256) void k_chunk_wait(const uint16_t* __restrict__
 // Outer values of an Oaken row (the Oaken page, §3.2.2): delta = x - T_hi
 // above the upper outer threshold, x - T_lo below the lower one; the group's
 // outer scale s_out = max |delta| / 31 and each value's 5-bit shifted
-// magnitude rne(|delta| / s_out).  d[k] = |delta| of an outer value, else 0.
-__device__ __forceinline__ void oak_deltas(const float (&v)[8], unsigned outer, float t_lo, float t_hi,
-                                           float (&d)[8]) {
+// magnitude rne(|delta| / s_out).
+//
+// s_out without visiting the outer values: binary32 subtraction is monotone,
+// so the largest fl(x - T_hi) over the values above T_hi is fl(max x - T_hi),
+// and the largest fl(T_lo - x) (= |fl(x - T_lo)|) over the values below T_lo
+// is fl(T_lo - min x); a group without such values gives a non-positive
+// difference.  Hence max |delta| = max(fl(max x - T_hi), fl(T_lo - min x), 0)
+// over all of the group's values, exactly.
+template <int LG>
+__device__ __forceinline__ float oak_outer_scale(const float (&v)[8], float t_lo, float t_hi) {
+  float mx = v[0], mn = v[0];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) d[k] = ((outer >> k) & 1u) ? fabsf(v[k] > t_hi ? v[k] - t_hi : v[k] - t_lo) : 0.0f;
-}
-// The sparse entries of a lane's outer values (channel | side << 7 | mag << 8)
-// to entries e, e + 1, ... of a list of capacity cap; `dropped` on overflow.
-__device__ __forceinline__ void oak_store_entries(const float (&v)[8], unsigned outer, float t_hi, float so,
-                                                  int li, uint16_t* sp, unsigned long long e,
-                                                  unsigned long long cap, float t_lo, bool& dropped) {
-  float d[8], m[8];
-  oak_deltas(v, outer, t_lo, t_hi, d);
-  const float r = recip_refined(so);  // s_out = 0: magnitudes 0
-  bool near = false;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) m[k] = rne_quot(d[k], r, near);
-  if (wave_any(near) && near) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) m[k] = rintf(d[k] / so);
+  for (int k = 1; k < 8; ++k) {
+    mx = fmaxf(mx, v[k]);
+    mn = fminf(mn, v[k]);
   }
-#pragma unroll
-  for (int k = 0; k < 8; ++k)
-    if ((outer >> k) & 1u) {
-      const unsigned mag = (unsigned)__builtin_amdgcn_fmed3f(m[k], 0.0f, 31.0f);
-      if (e < cap) sp[e] = (uint16_t)((unsigned)(li * 8 + k) | (unsigned)(v[k] > t_hi) << 7 | mag << 8);
-      else dropped = true;
-      ++e;
-    }
+  mx = max_lanes<1, LG>(mx);
+  mn = min_lanes<1, LG>(mn);
+  return fmaxf(fmaxf(mx - t_hi, t_lo - mn), 0.0f) / 31.0f;
+}
+
+// A lane's entries (channel | side << 7 | mag << 8) for its outer values, one
+// iteration per set bit of `outer` in ascending channel order (about 5 % of
+// the values are outer, so a wave runs two or three iterations, not eight),
+// to entries e, e + 1, ... of a list of capacity cap (< 2^31, so byte offsets
+// fit 32 bits); `dropped` on overflow.  raw: the lane's 8 fp16 values.
+__device__ __forceinline__ void oak_lane_entries(const uint4 raw, unsigned outer, float t_lo, float t_hi,
+                                                 float so, int li, uint16_t* sp, unsigned e, unsigned cap,
+                                                 bool& dropped) {
+  const float r = recip_refined(so);  // s_out = 0: magnitudes 0
+  while (outer) {
+    const int k = __builtin_ctz(outer);
+    outer &= outer - 1u;
+    const unsigned w = (k & 4) ? ((k & 2) ? raw.w : raw.z) : ((k & 2) ? raw.y : raw.x);
+    const float v = h2f((uint16_t)(w >> (16 * (k & 1))));
+    const bool above = v > t_hi;
+    const float d = above ? v - t_hi : t_lo - v;
+    bool near = false;
+    float m = rne_quot<32>(d, r, near);
+    if (wave_any(near) && near) m = rintf(d / so);
+    const unsigned mag = (unsigned)__builtin_amdgcn_fmed3f(m, 0.0f, 31.0f);
+    if (e < cap)
+      *reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(sp) + (e << 1)) =
+          (uint16_t)((unsigned)(li * 8 + k) | (unsigned)above << 7 | mag << 8);
+    else
+      dropped = true;
+    ++e;
+  }
 }
 
 // Oaken (the Oaken page, §3.1 online stage, §3.2.1-3.2.2): per row, outer
@@ -752,15 +775,18 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
   }
   uint32_t* rp = rowptr + bh * (S + 1);
   uint16_t* sp = sparse + bh * cap;
-  unsigned long long base = p == 0 ? 0ull : (unsigned long long)rp[p];
+  const unsigned capu = (unsigned)cap;  // < 2^31 (validated)
+  // running entry count: at most cap + 128 t_new < 2^32
+  unsigned base = p == 0 ? 0u : rp[p];
   if (p == 0 && threadIdx.x == 0) rp[0] = 0u;
   const int rl = threadIdx.x >> 4, li = threadIdx.x & 15, lane = threadIdx.x & 63;
   uint16_t* lrow = lrows[VL ? rl : 0];
-  const uint16_t* xr = x + (bh * t_new + rl) * kD + li * 8;
+  // rows past the last one load the last row (always readable); such rows
+  // are neither counted nor stored
+  const uint16_t* xr = x + bh * t_new * kD + li * 8;
   uint4 nxt[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-    nxt[u] = 16 * u + rl < t_new ? ld_row8(xr + (long long)(16 * u) * kD) : make_uint4(0u, 0u, 0u, 0u);
+  for (int u = 0; u < U; ++u) nxt[u] = ld_row8(xr + (long long)min(16 * u + rl, t_new - 1) * kD);
   bool dropped = false;
   for (int t0 = 0, it = 0; t0 < t_new; t0 += TR, it ^= 1) {
     uint4 raw[U];
@@ -768,23 +794,29 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
     for (int u = 0; u < U; ++u) raw[u] = nxt[u];
     if (t0 + TR < t_new) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = t0 + TR + 16 * u + rl;
-        nxt[u] = t < t_new ? ld_row8(xr + (long long)(t - rl) * kD) : make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int u = 0; u < U; ++u) nxt[u] = ld_row8(xr + (long long)min(t0 + TR + 16 * u + rl, t_new - 1) * kD);
     }
-    // pass 1: the rows' outer masks and counts (a lane's first entry within
-    // its row in bits 8 and up)
+    // pass 1: per row, the dense INT4 body, the scales and the outer mask;
+    // the row's outer count (a lane's first entry within its row in bits 8
+    // and up of meta)
     unsigned meta[U];
+    float sos[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const int t = t0 + 16 * u + rl;
+      const bool active = t < t_new;
       float v[8];
       unpack8(raw[u], v);
       unsigned outer = 0;
-      if (t0 + 16 * u + rl < t_new) {
+      if (active) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) outer |= (unsigned)((v[k] > t_hi) || (v[k] < t_lo)) << k;
       }
+      uint32_t plo, phi;
+      float s;
+      int z;
+      quant8<4, false, GE>(v, ~outer & 0xFFu, plo, phi, s, z);
+      const float so = oak_outer_scale<LG>(v, t_lo, t_hi);
       const int lc = __popc(outer);
       int incl = lc;
 #pragma unroll
@@ -794,6 +826,28 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
       }
       if (li == 15) row_cnt[it][16 * u + rl] = (unsigned)incl;  // 0 for an inactive row
       meta[u] = outer | (unsigned)(incl - lc) << 8;
+      sos[u] = so;
+      if (active) {
+        // the dense row: contiguous, or in its page (a table entry outside
+        // the pool skips the row and flags; the sparse list is per sequence)
+        long long dst = bh * S + p + t;
+        bool dense_ok = true;
+        if (pm.pages) {
+          const int tok = p + t;
+          const int pg = pm.pages[(long long)b * (S / pm.ptok) + tok / pm.ptok];
+          dense_ok = pg >= 0 && pg < pm.npages;
+          if (!dense_ok && li == 0) set_flag(status, kFlagPageRange);
+          dst = ((long long)pg * H + bh % H) * pm.ptok + tok % pm.ptok;
+        }
+        if (dense_ok) {
+          store_row_codes<4, VL>(codes + dst * 64, li, plo, phi, lrow);
+          if (li % LG == 0) {
+            scale[dst * NG + li / LG] = s;
+            zero[dst * NG + li / LG] = (uint8_t)z;
+            oscale[dst * NG + li / LG] = so;
+          }
+        }
+      }
     }
     __syncthreads();
     // each wave: inclusive scan of the tile's 64 row counts, lane r = row r
@@ -806,51 +860,15 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
     }
     const unsigned excl_row = scan - cnt;
     const unsigned tile_tot = __shfl(scan, 63, 64);
-    // pass 2: per row, the dense INT4 body, the outer scales and the entries
+    // pass 2: the entries (only where there are outer values) and rowptr
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + 16 * u + rl;
-      const unsigned long long rb = base + __shfl(excl_row, 16 * u + rl, 64);
+      const unsigned rb = base + __shfl(excl_row, 16 * u + rl, 64);
       const unsigned rcnt = __shfl(cnt, 16 * u + rl, 64);
       if (t >= t_new) continue;
-      const unsigned outer = meta[u] & 0xFFu;
-      float v[8];
-      unpack8(raw[u], v);
-      uint32_t plo, phi;
-      float s;
-      int z;
-      quant8<4, false, GE>(v, ~outer & 0xFFu, plo, phi, s, z);
-      float d[8], dmax = 0.0f;
-      oak_deltas(v, outer, t_lo, t_hi, d);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) dmax = fmaxf(dmax, d[k]);
-      dmax = max_lanes<1, LG>(dmax);
-      const float so = dmax / 31.0f;
-      // the dense row: contiguous, or in its page (a table entry outside the
-      // pool skips the row and flags; the sparse list is per sequence)
-      long long dst = bh * S + p + t;
-      bool dense_ok = true;
-      if (pm.pages) {
-        const int tok = p + t;
-        const int pg = pm.pages[(long long)b * (S / pm.ptok) + tok / pm.ptok];
-        dense_ok = pg >= 0 && pg < pm.npages;
-        if (!dense_ok && li == 0) set_flag(status, kFlagPageRange);
-        dst = ((long long)pg * H + bh % H) * pm.ptok + tok % pm.ptok;
-      }
-      if (dense_ok) {
-        store_row_codes<4, VL>(codes + dst * 64, li, plo, phi, lrow);
-        if (li % LG == 0) {
-          scale[dst * NG + li / LG] = s;
-          zero[dst * NG + li / LG] = (uint8_t)z;
-          oscale[dst * NG + li / LG] = so;
-        }
-      }
-      oak_store_entries(v, outer, t_hi, so, li, sp, rb + (meta[u] >> 8), (unsigned long long)cap, t_lo, dropped);
-      if (li == 0) {
-        const unsigned long long end = rb + rcnt;
-        rp[p + t + 1] = (uint32_t)(end < (unsigned long long)cap ? end : (unsigned long long)cap);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // rows one after another: bounded register use
+      oak_lane_entries(raw[u], meta[u] & 0xFFu, t_lo, t_hi, sos[u], li, sp, rb + (meta[u] >> 8), capu, dropped);
+      if (li == 0) rp[(unsigned)(p + t + 1)] = min(rb + rcnt, capu);
     }
     base += tile_tot;
   }
@@ -883,10 +901,11 @@ __global__ __launch_bounds__(256) void k_quant_oaken_one(const uint16_t* __restr
   }
   uint32_t* rp = t.rowptr + bh * (S + 1);
   uint16_t* sp = t.sparse + bh * t.sparse_cap;
-  const unsigned long long base = p == 0 ? 0ull : (unsigned long long)rp[p];
+  const unsigned base = p == 0 ? 0u : rp[p];
   if (p == 0 && li == 0) rp[0] = 0u;
   float v[8];
-  unpack8(ld_row8(x + bh * kD + li * 8), v);
+  const uint4 raw = ld_row8(x + bh * kD + li * 8);
+  unpack8(raw, v);
   unsigned outer = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) outer |= (unsigned)((v[k] > t.thr_hi) || (v[k] < t.thr_lo)) << k;
@@ -894,12 +913,7 @@ __global__ __launch_bounds__(256) void k_quant_oaken_one(const uint16_t* __restr
   float s;
   int z;
   quant8<4, false, GE>(v, ~outer & 0xFFu, plo, phi, s, z);
-  float d[8], dmax = 0.0f;
-  oak_deltas(v, outer, t.thr_lo, t.thr_hi, d);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) dmax = fmaxf(dmax, d[k]);
-  dmax = max_lanes<1, LG>(dmax);
-  const float so = dmax / 31.0f;
+  const float so = oak_outer_scale<LG>(v, t.thr_lo, t.thr_hi);
   const int lc = __popc(outer);
   int incl = lc;
 #pragma unroll
@@ -925,13 +939,12 @@ __global__ __launch_bounds__(256) void k_quant_oaken_one(const uint16_t* __restr
       t.oscale[dst * NG + li / LG] = so;
     }
   }
-  const unsigned long long cap = (unsigned long long)t.sparse_cap;
-  unsigned long long e = base + (unsigned)(incl - lc);
+  const unsigned cap = (unsigned)t.sparse_cap;  // < 2^31 (validated)
+  const unsigned e = base + (unsigned)(incl - lc);
   bool dropped = false;
-  oak_store_entries(v, outer, t.thr_hi, so, li, sp, e, cap, t.thr_lo, dropped);
+  oak_lane_entries(raw, outer, t.thr_lo, t.thr_hi, so, li, sp, e, cap, dropped);
   if (li == 0) {
-    const unsigned long long end = base + (unsigned)rowtot;
-    rp[p + 1] = (uint32_t)(end < cap ? end : cap);
+    rp[p + 1] = min(base + (unsigned)rowtot, cap);
   }
   if (dropped) set_flag(status, kFlagSparseFull);
 }

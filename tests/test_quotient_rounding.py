@@ -1,8 +1,9 @@
 """Host check of the argument behind the quantizers' division-free integer codes.
 
 The kernels round y = fl(x * r), r a refined reciprocal of the group scale s,
-and keep rne(y) only where |y - rne(y)| + |y| 2^-19 < 0.5; elsewhere they
-divide.  The claim: every accepted rne(y) equals rne(fl(x / s)), the code the
+and keep rne(y) only where |y - rne(y)| < 0.5 - M 2^-19, M a power of two
+above every |x / s| the caller can form (2^bits for the codes, 32 for the
+Oaken magnitudes); elsewhere they divide.  The claim: every accepted rne(y) equals rne(fl(x / s)), the code the
 binary32 definition gives.  This test replays the acceptance rule in numpy
 (binary64 products rounded once to binary32 stand in for the fused
 multiply-adds) with reciprocals deliberately perturbed by up to 3 ulp before
@@ -24,14 +25,15 @@ def _nudge(r, k):
     return out
 
 
-def _accepted_and_codes(x, s, rng):
+def _accepted_and_codes(x, s, rng, M):
     r0 = (f32(1) / s).astype(f32)
     r0 = _nudge(r0, rng.integers(-3, 4, s.size))
     e = (f32(1) - s.astype(np.float64) * r0).astype(f32)       # fma(-s, r0, 1)
     r = (e.astype(np.float64) * r0 + r0).astype(f32)            # fma(e, r0, r0)
     y = (x * r).astype(f32)
     n = np.rint(y).astype(f32)
-    ok = (np.abs(y).astype(np.float64) * 2.0 ** -19 + np.abs(y - n)).astype(f32) < f32(0.5)
+    assert np.all(np.abs(y) < M)  # the premise of the bound
+    ok = np.abs(y - n) < f32(0.5 - M * 2.0 ** -19)
     return ok, n
 
 
@@ -50,7 +52,7 @@ def test_accepted_fast_codes_equal_the_divided_codes():
             else:
                 k = rng.integers(-qmax, qmax + 1, s.size).astype(f32)
                 x = ((k + (f32(0.5) if case == "half-integers" else f32(0))) * s).astype(f32)
-            ok, n = _accepted_and_codes(x, s, rng)
+            ok, n = _accepted_and_codes(x, s, rng, qmax + 1)
             ref = np.rint((x / s).astype(f32))
             assert not np.any(ok & (n != ref)), (case, qmax)
             if case == "random":
