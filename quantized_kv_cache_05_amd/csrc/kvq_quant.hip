@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restric
     row0 = ((long long)pg * H + bh % H) * pm.ptok + k0 % pm.ptok;
   }
   __shared__ float tile[64][kD + 1];
-  __shared__ float lo_sh[2][kD], hi_sh[2][kD], s_sh[kD];
+  __shared__ float lo_sh[2][kD], hi_sh[2][kD], s_sh[kD], r_sh[kD];
   __shared__ int z_sh[kD];
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
@@ -434,6 +434,7 @@ __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restric
     int z = 0;
     if (s != 0.0f) z = min(max((int)rintf(-lo / s), 0), QMAX);
     s_sh[c] = s;
+    r_sh[c] = recip_refined(s);
     z_sh[c] = z;
     const long long m = (row0 / 64) * kD + c;
     scale[m] = s;
@@ -445,13 +446,26 @@ __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restric
   uint8_t* dst = codes + (row0 + r) * RB;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
+    // rne(x / s) without a divide per value (rne_quot; s = 0: r = 0, z = 0, code 0)
+    float n[8];
+    bool near = false;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int ch = pc * 32 + q * 8 + v;
+      n[v] = rne_quot<(1 << BITS)>(tile[r][ch], r_sh[ch], near);
+    }
+    if (wave_any(near) && near) {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int ch = pc * 32 + q * 8 + v;
+        n[v] = rintf(tile[r][ch] / s_sh[ch]);
+      }
+    }
     uint64_t w = 0;
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
       const int ch = pc * 32 + q * 8 + v;
-      const float s = s_sh[ch];
-      int c = 0;
-      if (s != 0.0f) c = min(max((int)rintf(tile[r][ch] / s) + z_sh[ch], 0), QMAX);
+      const int c = (int)__builtin_amdgcn_fmed3f(n[v] + (float)z_sh[ch], 0.0f, (float)QMAX);
       w |= (uint64_t)c << (BITS * v);
     }
     store_codes8<BITS>(dst, 4 * q + pc, (uint32_t)w, (uint32_t)(w >> 32));
@@ -1067,11 +1081,21 @@ __global__ __launch_bounds__(256) void k_quant_dsq(const uint16_t* __restrict__ 
       amax = fmaxf(amax, fabsf(xv_[i]));
     }
     const float s = amax / 127.0f;
+    // rne(x / s) without a divide per value (rne_quot; slots past n_sig hold
+    // 0 and code 0; s = 0 gives r = 0 and codes 0)
+    const float r = recip_refined(s);
+    bool near = false;
+    float n[kDsqSigSlots];
+#pragma unroll
+    for (int i = 0; i < kDsqSigSlots; ++i) n[i] = rne_quot<128>(xv_[i], r, near);
+    if (wave_any(near) && near) {
+#pragma unroll
+      for (int i = 0; i < kDsqSigSlots; ++i) n[i] = rintf(xv_[i] / s);
+    }
     float acc = 0.0f;  // K base: sum in slot order, one rounding per operation
 #pragma unroll
     for (int i = 0; i < kDsqSigSlots; ++i) {
-      int q = 0;
-      if (i < n_sig && s != 0.0f) q = min(max((int)rintf(xv_[i] / s), -128), 127);
+      const int q = (int)__builtin_amdgcn_fmed3f(n[i], -128.0f, 127.0f);
       sig[tsr][i][d] = (int8_t)q;
       if (i < n_sig) acc = acc + s * (float)q;
     }
