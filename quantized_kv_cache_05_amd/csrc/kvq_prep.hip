@@ -14,65 +14,103 @@
 namespace kvq {
 namespace {
 
-// Binary64 arithmetic in program order, one rounding per operation: the
-// functions below forbid the compiler to fuse a product and a sum into one
-// fused multiply-add (HIP's default allows it).
-__device__ __forceinline__ double cosine(const double* __restrict__ qe, double qn,
-                                         const double* __restrict__ ce, int dim) {
-#pragma clang fp contract(off)
-  double dot = 0.0, cc = 0.0;
-  for (int d = 0; d < dim; ++d) {
-    const double c = ce[d];
-    dot = dot + qe[d] * c;
-    cc = cc + c * c;
-  }
-  return dot / (qn * sqrt(cc));
-}
+// Binary64 arithmetic in program order, one rounding per operation (the
+// kernel below forbids the compiler to fuse a product and a sum into one
+// fused multiply-add, which HIP's default allows): each similarity is one
+// thread's sequential sums over d, so rows cannot be split across lanes.
+// The rows are read in slices of kSliceD values staged through LDS, loaded
+// cooperatively so that a wave's load instruction covers 8 rows' 64-byte
+// slices (not 64 rows' 8 bytes).  Each thread also forms the query's sum of
+// squares in the same order, next to its chunk's two sums, so every thread
+// has the same |q| without a separate pass.
+constexpr int kChunkThreads = 1024;
+constexpr int kSliceD = 8;
+constexpr int kSimLds = 4096;  // similarities kept in LDS for the class pass (32 KiB)
 
-// One workgroup per sequence.  Pass 1: similarities, their minimum and
-// maximum; pass 2: classes (similarities recomputed bit-identically when no
-// output array is given).
-__global__ __launch_bounds__(256) void k_chunk_bits(const double* __restrict__ q_emb,
-                                                    const double* __restrict__ c_emb, int n,
-                                                    int dim, double alpha, double beta,
-                                                    double* __restrict__ sims,
-                                                    uint8_t* __restrict__ bits) {
+// One workgroup of 1024 threads per sequence, 1024 chunks at a time, one
+// chunk per thread.  Pass 1: similarities, their minimum and maximum; pass
+// 2: classes, from LDS, from the output array, or recomputed bit-identically
+// (beyond kSimLds chunks without an output array).
+__global__ __launch_bounds__(kChunkThreads) void k_chunk_bits(const double* __restrict__ q_emb,
+                                                              const double* __restrict__ c_emb, int n,
+                                                              int dim, double alpha, double beta,
+                                                              double* __restrict__ sims,
+                                                              uint8_t* __restrict__ bits) {
 #pragma clang fp contract(off)
   const int b = blockIdx.x;
   const double* qe = q_emb + (long long)b * dim;
   const double* ce = c_emb + (long long)b * n * dim;
-  __shared__ double qn_sh, red_min[256], red_max[256];
-  if (threadIdx.x == 0) {
-    double qq = 0.0;
-    for (int d = 0; d < dim; ++d) qq = qq + qe[d] * qe[d];
-    qn_sh = sqrt(qq);
-  }
-  __syncthreads();
-  const double qn = qn_sh;
-  double lo = INFINITY, hi = -INFINITY;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const double s = cosine(qe, qn, ce + (long long)i * dim, dim);
-    if (sims) sims[(long long)b * n + i] = s;
-    lo = fmin(lo, s);
-    hi = fmax(hi, s);
-  }
-  red_min[threadIdx.x] = lo;
-  red_max[threadIdx.x] = hi;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) {
-      red_min[threadIdx.x] = fmin(red_min[threadIdx.x], red_min[threadIdx.x + w]);
-      red_max[threadIdx.x] = fmax(red_max[threadIdx.x], red_max[threadIdx.x + w]);
+  __shared__ double tile[kChunkThreads][kSliceD + 1];  // +1: conflict-free row reads
+  __shared__ double sim_sh[kSimLds];
+  __shared__ double wave_min[kChunkThreads / 64], wave_max[kChunkThreads / 64];
+  const int t = threadIdx.x;
+  // the similarities of chunks c0 .. c0 + 1023 (thread t: chunk c0 + t)
+  // element j = t mod 8 of the slice at d0 of rows c0 + t / 8 + 128 m
+  auto load_slice = [&](int c0, int d0, double (&v)[kSliceD]) {
+#pragma unroll
+    for (int m = 0; m < kSliceD; ++m) {
+      const int c = c0 + (t >> 3) + 128 * m, d = d0 + (t & 7);
+      v[m] = (c < n && d < dim) ? ce[(long long)c * dim + d] : 0.0;
     }
-    __syncthreads();
+  };
+  auto similarity_block = [&](int c0) -> double {
+    double dot = 0.0, cc = 0.0, qq = 0.0;
+    double nxt[kSliceD];
+    load_slice(c0, 0, nxt);
+    for (int d0 = 0; d0 < dim; d0 += kSliceD) {
+      __syncthreads();  // the previous slice has been read
+#pragma unroll
+      for (int m = 0; m < kSliceD; ++m) tile[(t >> 3) + 128 * m][t & 7] = nxt[m];
+      __syncthreads();
+      if (d0 + kSliceD < dim) load_slice(c0, d0 + kSliceD, nxt);  // in flight during the sums
+      const int dn = min(kSliceD, dim - d0);
+      for (int j = 0; j < dn; ++j) {
+        const double q = qe[d0 + j], c = tile[t][j];
+        dot = dot + q * c;
+        cc = cc + c * c;
+        qq = qq + q * q;
+      }
+    }
+    return dot / (sqrt(qq) * sqrt(cc));
+  };
+  double lo = INFINITY, hi = -INFINITY;
+  for (int c0 = 0; c0 < n; c0 += kChunkThreads) {
+    const double s = similarity_block(c0);
+    const int i = c0 + t;
+    if (i < n) {
+      if (sims) sims[(long long)b * n + i] = s;
+      if (i < kSimLds) sim_sh[i] = s;
+      lo = fmin(lo, s);
+      hi = fmax(hi, s);
+    }
   }
-  const double smin = red_min[0], smax = red_max[0];
+  // minimum and maximum (exact in any order): across the wave, then the waves
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    lo = fmin(lo, __shfl_xor(lo, m, 64));
+    hi = fmax(hi, __shfl_xor(hi, m, 64));
+  }
+  if ((t & 63) == 0) {
+    wave_min[t >> 6] = lo;
+    wave_max[t >> 6] = hi;
+  }
+  __syncthreads();
+  double smin = wave_min[0], smax = wave_max[0];
+#pragma unroll
+  for (int w = 1; w < kChunkThreads / 64; ++w) {
+    smin = fmin(smin, wave_min[w]);
+    smax = fmax(smax, wave_max[w]);
+  }
   const double range = smax - smin;
   const double t_low = smin + range * alpha;
   const double t_high = smax - range * beta;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const double s = sims ? sims[(long long)b * n + i] : cosine(qe, qn, ce + (long long)i * dim, dim);
-    bits[(long long)b * n + i] = s > t_high ? 16 : (s > t_low ? 4 : 2);
+  for (int c0 = 0; c0 < n; c0 += kChunkThreads) {
+    const int i = c0 + t;
+    double s = 0.0;
+    if (c0 + kChunkThreads <= kSimLds) s = sim_sh[min(i, kSimLds - 1)];
+    else if (sims) s = sims[(long long)b * n + min(i, n - 1)];
+    else s = similarity_block(c0);  // every thread takes part (barriers inside)
+    if (i < n) bits[(long long)b * n + i] = s > t_high ? 16 : (s > t_low ? 4 : 2);
   }
 }
 
@@ -169,7 +207,7 @@ __global__ __launch_bounds__(1024) void k_percentiles(const unsigned long long* 
 
 hipError_t launch_chunk_bits(const double* q_emb, const double* c_emb, int batch, int n, int dim,
                              double alpha, double beta, double* sims, uint8_t* bits, hipStream_t st) {
-  hipLaunchKernelGGL(k_chunk_bits, dim3((unsigned)batch), dim3(256), 0, st, q_emb, c_emb, n, dim,
+  hipLaunchKernelGGL(k_chunk_bits, dim3((unsigned)batch), dim3(kChunkThreads), 0, st, q_emb, c_emb, n, dim,
                      alpha, beta, sims, bits);
   return hipGetLastError();
 }
