@@ -102,16 +102,11 @@ __device__ __forceinline__ void load_tok_meta(const TokView& v, long long row, f
 // contiguous (NGV per row); the row offset is a multiple of 8, so the loads
 // are aligned.  Rows past the valid range multiply zero weights; the mask
 // keeps their (arbitrary) bytes inside the mantissa, so the pairs stay finite.
+// (load_zraw issues the loads of the zero-point words, zsub_from_raw forms
+// the pairs, so that the loads can be issued well before any use.)
 template <class VC, int NGV>
-__device__ __forceinline__ void load_zsub(const TokView& vv, long long r0, u4_t (&zsub)[2][NGV]) {
-  constexpr int NP = VC::ZODD ? 2 : 1;
-  if constexpr (VC::SYM) {
-#pragma unroll
-    for (int g = 0; g < NGV; ++g)
-#pragma unroll
-      for (int p = 0; p < 4; ++p) zsub[0][g][p] = VC::ZMAGIC | 0x00800080u;  // z = 128
-  } else {
-    unsigned zw[2 * NGV];
+__device__ __forceinline__ void load_zraw(const TokView& vv, long long r0, unsigned (&zw)[2 * NGV]) {
+  if constexpr (!VC::SYM) {
     const uint8_t* zp = vv.zero + (unsigned)(r0 * NGV);
     if constexpr (NGV == 1) {
       const u2_t t = ld_nt<u2_t>(zp);
@@ -125,6 +120,17 @@ __device__ __forceinline__ void load_zsub(const TokView& vv, long long r0, u4_t 
         for (int e = 0; e < 4; ++e) zw[4 * k + e] = t[e];
       }
     }
+  }
+}
+template <class VC, int NGV>
+__device__ __forceinline__ void zsub_from_raw(const unsigned (&zw)[2 * NGV], u4_t (&zsub)[2][NGV]) {
+  constexpr int NP = VC::ZODD ? 2 : 1;
+  if constexpr (VC::SYM) {
+#pragma unroll
+    for (int g = 0; g < NGV; ++g)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) zsub[0][g][p] = VC::ZMAGIC | 0x00800080u;  // z = 128
+  } else {
 #pragma unroll
     for (int g = 0; g < NGV; ++g)
 #pragma unroll
@@ -195,10 +201,9 @@ __device__ __forceinline__ float lane0(float v) {
 // so no entry needs to know its row.
 //
 // V (outer-value output).  The entries of rows 8k .. 8k + 7 (octet k) take
-// one lane each (one 2-byte load per octet).  The row of an entry comes from
-// one-hot row markers (bit r mod 8 at the slot of the row's first entry,
-// byte k for octet k) and a prefix OR across the wave: the highest bit set is
-// the last row started.  Within an octet two entries share an address of the
+// one lane each (one 2-byte load per octet).  The row of an entry is 8k plus
+// the row tag the quantizer stores in the entry (bits 13-15: the token index
+// mod 8; tiles start at multiples of 32).  Within an octet two entries share an address of the
 // outer-value output only if they share row and channel, which a row's list
 // never does, so with one output copy per row mod 8 every octet updates its
 // copies by a plain read-modify-write with no conflicts; octets follow one
@@ -214,8 +219,10 @@ struct __attribute__((aligned(16))) OakWave {
   float ex[NG + 1][264];               // K: exclusive prefix sums over a round's entries, [256] = total
   float so[kTile][NG];                 // V: outer scales of the tile's rows
   float ksc[QR][kTile];                // outer-value part of each query's score, per row
-  float pr[QR][kTile];                 // softmax numerators, per query and row
-  unsigned mk[64];                     // V: one-hot row markers, byte k for octet k
+  float pr[QR][kTile];                 // softmax numerators, per query and row (QR > 1)
+  // one query row: per row, the numerator p times T_lo, T_hi and each group's
+  // outer scale, so that an entry's share is one fma (p x_hat = p T + mag p s)
+  float pv[QR == 1 ? kTile : 1][NG <= 2 ? 4 : 8];
   float pad[64];                       // per-lane sink of masked updates
   float osp[kOakCopies<QR>][QR][128];  // outer-value output per copy (row mod 8), wave frame
 };
@@ -274,7 +281,7 @@ template <int CTRL, int ROWS = 0xF>
 __device__ __forceinline__ unsigned dpp_u(unsigned v) {
   return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
 }
-// Inclusive prefix sum / OR in lane order over the wave: row_shr 1, 2, 4, 8
+// Inclusive prefix sum in lane order over the wave: row_shr 1, 2, 4, 8
 // inside each 16-lane row, then row_bcast:15 (last lane of rows 0 and 2 into
 // rows 1 and 3) and row_bcast:31 (lane 31 into rows 2 and 3).  The sum's
 // order is fixed, so it is deterministic.
@@ -289,17 +296,8 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
   v += f(dpp_u<0x143, 0xC>(u(v)));
   return v;
 }
-__device__ __forceinline__ unsigned wave_prefix_or(unsigned v) {
-  v |= dpp_u<0x111>(v);
-  v |= dpp_u<0x112>(v);
-  v |= dpp_u<0x114>(v);
-  v |= dpp_u<0x118>(v);
-  v |= dpp_u<0x142, 0xA>(v);
-  v |= dpp_u<0x143, 0xC>(v);
-  return v;
-}
 
-// x_hat of entry en (idx | side << 7 | mag << 8) with its row's outer scale,
+// x_hat of entry en (idx | side << 7 | mag << 8 | tag << 13) with its row's outer scale,
 // one binary32 product and one sum as in the reconstruction rule.
 // (contraction off: the product is rounded before the sum; T_lo - step is
 // formed as T_lo + (-step), the same binary32 result)
@@ -379,16 +377,14 @@ __device__ __forceinline__ void oak_k_tile(const LDS& L, OakWave<QR, NG>& W, con
 }
 
 // V entries of one tile, before the softmax: the lane's entry of each octet
-// (k = 0..3), whether it lies in the octet's range, and its row in the tile.
+// (k = 0..3) and whether it lies in the octet's range.
 struct OakOct {
   unsigned en[4];
-  unsigned row[4];
   bool ok[4];
   unsigned ro[5];   // octet boundaries in the list (wave-uniform)
 };
 
-template <int QR, int NG>
-__device__ __forceinline__ OakOct oak_v_prep(OakWave<QR, NG>& W, const OakList& l, const OakRp& rp) {
+__device__ __forceinline__ OakOct oak_v_prep(const OakList& l, const OakRp& rp) {
   const unsigned lane = threadIdx.x & 63;
   OakOct o;
 #pragma unroll
@@ -399,31 +395,25 @@ __device__ __forceinline__ OakOct oak_v_prep(OakWave<QR, NG>& W, const OakList& 
     o.en[k] = oak_entry(l, o.ro[k] + lane);
     o.ok[k] = o.ro[k] + lane < o.ro[k + 1];
   }
-  // one-hot markers: row lane r marks the slot of its first entry in octet r / 8
-  const unsigned ra = min(rp.a[1], l.cap), rb = min(rp.b[1], l.cap);
-  const unsigned oct = (lane >> 3) & 3;
-  W.mk[lane] = 0u;
-  const unsigned ro_l = oct < 2 ? (oct ? o.ro[1] : o.ro[0]) : (oct == 2 ? o.ro[2] : o.ro[3]);
-  const unsigned p = ra - ro_l;
-  if (lane < (unsigned)kTile && ra < rb && p < 64u)
-    reinterpret_cast<uint8_t*>(W.mk)[4 * p + oct] = (uint8_t)(1u << (lane & 7));
-  wave_lds_sync();
-  const unsigned orr = wave_prefix_or(W.mk[lane]);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const unsigned byte = (orr >> (8 * k)) & 255u;
-    o.row[k] = 8u * k + (31u - (unsigned)__builtin_clz(byte | 1u));
-  }
   return o;
 }
 
 // V entries after the softmax: p[m][row] x_hat into the wave's outer-value
-// output (copy row mod 8), octet by octet; entries past 64 in an octet take
-// further rounds (rare), with markers of their own.
+// output (copy row mod 8), octet k by octet; entries past 64 in an octet take
+// further rounds (rare).  The row is 8k + the entry's tag.
 template <int QR, int NG>
-__device__ __forceinline__ void oak_v_apply_one(OakWave<QR, NG>& W, const OakList& l, unsigned en, unsigned row,
+__device__ __forceinline__ void oak_v_apply_one(OakWave<QR, NG>& W, const OakList& l, unsigned en, unsigned k,
                                                 bool ok, int nq) {
-  const unsigned lane = threadIdx.x & 63, idx = en & 127u;
+  const unsigned lane = threadIdx.x & 63, idx = en & 127u, tag = en >> 13, row = 8u * k + tag;
+  if constexpr (QR == 1) {
+    const bool hi = en & 128u;
+    const float mag = (float)((en >> 8) & 31u);
+    const float* pv = W.pv[row];
+    const float val = fmaf(hi ? mag : -mag, pv[2 + (NG == 1 ? 0u : idx / (128 / NG))], hi ? pv[1] : pv[0]);
+    float* a = ok ? &W.osp[tag][0][idx] : &W.pad[lane];
+    *a += ok ? val : 0.0f;
+    return;
+  }
   const float xh = oak_value(en, W.so[row][NG == 1 ? 0u : idx / (128 / NG)], l);
   constexpr int NC = kOakCopies<QR>;
 #pragma unroll
@@ -431,12 +421,12 @@ __device__ __forceinline__ void oak_v_apply_one(OakWave<QR, NG>& W, const OakLis
     if (m < nq) {
       const float val = W.pr[m][row] * xh;
       if constexpr (NC == 8) {
-        float* a = ok ? &W.osp[row & 7][m][idx] : &W.pad[lane];
+        float* a = ok ? &W.osp[tag][m][idx] : &W.pad[lane];
         *a += ok ? val : 0.0f;
       } else {  // one copy: one row of the octet at a time
 #pragma unroll
         for (unsigned r = 0; r < 8; ++r) {
-          const bool mine = ok && (row & 7) == r;
+          const bool mine = ok && tag == r;
           float* a = mine ? &W.osp[0][m][idx] : &W.pad[lane];
           *a += mine ? val : 0.0f;
         }
@@ -446,30 +436,15 @@ __device__ __forceinline__ void oak_v_apply_one(OakWave<QR, NG>& W, const OakLis
 }
 
 template <int QR, int NG>
-__device__ __forceinline__ void oak_v_apply(OakWave<QR, NG>& W, const OakList& l, const OakRp& rp,
-                                            const OakOct& o, int nq) {
+__device__ __forceinline__ void oak_v_apply(OakWave<QR, NG>& W, const OakList& l, const OakOct& o, int nq) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) oak_v_apply_one<QR, NG>(W, l, o.en[k], o.row[k], o.ok[k], nq);
+  for (int k = 0; k < 4; ++k) oak_v_apply_one<QR, NG>(W, l, o.en[k], (unsigned)k, o.ok[k], nq);
   // octets with more than 64 entries (rare): further rounds of 64
   const unsigned lane = threadIdx.x & 63;
-  const unsigned ra = min(rp.a[1], l.cap), rb = min(rp.b[1], l.cap);
   for (int k = 0; k < 4; ++k) {
-    if (o.ro[k] + 64u >= o.ro[k + 1]) continue;
-    // the row of the round's last entry starts the next round
-    unsigned carry = 1u << (((unsigned)__builtin_amdgcn_readlane((int)o.row[k], 63)) & 7u);
     for (unsigned c = 1; o.ro[k] + 64u * c < o.ro[k + 1]; ++c) {
       const unsigned e = o.ro[k] + 64u * c + lane;
-      const unsigned en = oak_entry(l, e);
-      W.mk[lane] = 0u;
-      const unsigned p = ra - (o.ro[k] + 64u * c);
-      if (lane < (unsigned)kTile && (lane >> 3) == (unsigned)k && ra < rb && p < 64u)
-        reinterpret_cast<uint8_t*>(W.mk)[4 * p] = (uint8_t)(1u << (lane & 7));
-      wave_lds_sync();
-      const unsigned orr = wave_prefix_or(W.mk[lane] & 255u) | carry;
-      const unsigned row = 8u * k + (31u - (unsigned)__builtin_clz(orr));
-      oak_v_apply_one<QR, NG>(W, l, en, row, e < o.ro[k + 1], nq);
-      carry = 1u << (((unsigned)__builtin_amdgcn_readlane((int)row, 63)) & 7u);
-      wave_lds_sync();
+      oak_v_apply_one<QR, NG>(W, l, oak_entry(l, e), (unsigned)k, e < o.ro[k + 1], nq);
     }
   }
 }
@@ -492,6 +467,16 @@ __device__ __forceinline__ void load_f32s(const float* p, float (&v)[NG]) {
     }
   }
 }
+
+// The loaded inputs of one tile: K and V codes, token metadata, V zero-point
+// words (no arithmetic on them yet, so issuing the loads waits for nothing).
+template <class KC, class VC, int NGK, int NGV>
+struct TileIn {
+  KC kr[2];
+  VC vr;
+  float sk[2][NGK], zk[2][NGK], sv[2][NGV], zv[2][NGV];
+  unsigned zraw[2 * NGV];
+};
 
 // ---------------------------------------------------------------------------
 // One wave's share of a token range [t0, t1) of one (b, kv head): tiles of 32
@@ -555,6 +540,25 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       vv = at_rows<VC::RB, NGV>(vv_, ro);
       pg_next = page_entry_v(vv_.pages, min(step + kNW * kTile * TPS, t1 - 1) >> vv_.pshift);
     }
+    // the tile inputs; with channel-axis K the first tile's loads are issued
+    // before the block scales are folded, so that both memory round trips
+    // overlap instead of following one another
+    using In = TileIn<KC, VC, NGK, NGV>;
+    auto load_in = [&](In& in, int tile) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) in.kr[nb].load(kv.codes + (unsigned)((tile + nb * 16 + n16) * KC::RB), q4);
+      in.vr.load(vv.codes + (unsigned)((tile + 8 * q4) * VC::RB), n16);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int t = tile + nb * 16 + n16;
+        if constexpr (!CHANK && !KC::F16) load_tok_meta<NGK, KC::SYM>(kv, t, in.sk[nb], in.zk[nb]);
+        // V zero-points enter through zsub below; only the scales are needed here
+        if constexpr (!VC::F16) load_tok_meta<NGV, true>(vv, t, in.sv[nb], in.zv[nb]);
+      }
+      if constexpr (VC::ZP) load_zraw<VC, NGV>(vv, tile + 8 * q4, in.zraw);
+    };
+    In pre;
+    if constexpr (CHANK) load_in(pre, step);
     // ---- channel-axis K: fold the block's scales into the query ----
     // The R x 128 products q[m][d] * s[d] are spread over the wave: entry
     // (s, m, q4e) covers channels 32 s + 8 q4e + (v, v + 4), v < 4; it is
@@ -639,25 +643,28 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
         const long long t = tile + (lane & 31);
         load_f32s<NGV>(kv.oscale + (unsigned)(t * NGV), oso[0]);
         load_f32s<NGV>(vv.oscale + (unsigned)(t * NGV), oso[1]);
-        oct = oak_v_prep<QR, NGV>(*oak.w, oak.l[1], rpc);
+        oct = oak_v_prep(oak.l[1], rpc);
         // issued before the code loads, so that the entry work below waits on
         // these alone (loads complete in order)
         __builtin_amdgcn_sched_barrier(0);
       }
-      KC kr[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) kr[nb].load(kv.codes + (unsigned)((tile + nb * 16 + n16) * KC::RB), q4);
-      VC vr;
-      vr.load(vv.codes + (unsigned)((tile + 8 * q4) * VC::RB), n16);
-      float sk[2][NGK], zk[2][NGK], sv[2][NGV], zv[2][NGV];
+      In in;
+      if constexpr (CHANK) {
+        if (tt == 0) in = pre;
+        else load_in(in, tile);
+      } else {
+        load_in(in, tile);
+      }
+      KC (&kr)[2] = in.kr;
+      VC& vr = in.vr;
+      auto& sk = in.sk;
+      auto& zk = in.zk;
+      auto& sv = in.sv;
       bool ok[2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int t = tile + nb * 16 + n16;
         ok[nb] = t >= t0 && t < t1;
-        if constexpr (!CHANK && !KC::F16) load_tok_meta<NGK, KC::SYM>(kv, t, sk[nb], zk[nb]);
-        // V zero-points enter through zsub below; only the scales are needed here
-        if constexpr (!VC::F16) load_tok_meta<NGV, true>(vv, t, sv[nb], zv[nb]);
       }
       if constexpr (VC::MASK_ROWS) {
 #pragma unroll
@@ -668,7 +675,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       }
       // -(OFF + z) of the B-operand rows as packed fp16 pairs, per V group
       u4_t zsub[2][NGV];
-      if constexpr (VC::ZP) load_zsub<VC, NGV>(vv, tile + 8 * q4, zsub);
+      if constexpr (VC::ZP) zsub_from_raw<VC, NGV>(in.zraw, zsub);
       // ---- Oaken: the outer K values' share of each row's score ----
       if constexpr (OAK) {
         __builtin_amdgcn_sched_barrier(0);  // the code loads stay ahead of the entry work
@@ -777,7 +784,27 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
           st.l[i] += p[nb][i];
         }
       // ---- Oaken: the softmax numerators of the rows, for the V entries ----
-      if constexpr (OAK) {
+      if constexpr (OAK && QR == 1) {
+        if (q4 == 0) {  // lanes 0-15 hold rows n16 and 16 + n16
+          const OakList& lv = oak.l[1];
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const int row = nb * 16 + n16;
+            const float pn = p[nb][0];
+            float v[NGV <= 2 ? 4 : 8];
+            v[0] = pn * lv.t_lo;
+            v[1] = pn * lv.t_hi;
+#pragma unroll
+            for (int g = 0; g < NGV; ++g) v[2 + g] = pn * oak.w->so[row][g];
+#pragma unroll
+            for (int g = NGV + 2; g < (NGV <= 2 ? 4 : 8); ++g) v[g] = 0.0f;
+            float* d = oak.w->pv[row];
+#pragma unroll
+            for (int g = 0; g < (NGV <= 2 ? 4 : 8); g += 4)
+              *reinterpret_cast<float4*>(d + g) = float4{v[g], v[g + 1], v[g + 2], v[g + 3]};
+          }
+        }
+      } else if constexpr (OAK) {
 #pragma unroll
         for (int i = 0; i < GI; ++i) {
           const int m = QRW::slot_query(q4, i);
@@ -814,7 +841,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       }
       wave_lds_sync();
       // ---- Oaken: V entries into the outer-value output ----
-      if constexpr (OAK) oak_v_apply<QR, NGV>(*oak.w, oak.l[1], rpc, oct, nq);
+      if constexpr (OAK) oak_v_apply<QR, NGV>(*oak.w, oak.l[1], oct, nq);
       // ---- O += W V ----
       u4_t wa[NGV][2];
 #pragma unroll

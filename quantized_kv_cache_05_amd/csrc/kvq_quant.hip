@@ -734,14 +734,16 @@ __device__ __forceinline__ float oak_outer_scale(const float (&v)[8], float t_lo
   return fmaxf(fmaxf(mx - t_hi, t_lo - mn), 0.0f) / 31.0f;
 }
 
-// A lane's entries (channel | side << 7 | mag << 8) for its outer values, one
-// iteration per set bit of `outer` in ascending channel order (about 5 % of
-// the values are outer, so a wave runs two or three iterations, not eight),
-// to entries e, e + 1, ... of a list of capacity cap (< 2^31, so byte offsets
-// fit 32 bits); `dropped` on overflow.  raw: the lane's 8 fp16 values.
+// A lane's entries (channel | side << 7 | mag << 8 | tag << 13) for its
+// outer values, one iteration per set bit of `outer` in ascending channel
+// order (about 5 % of the values are outer, so a wave runs two or three
+// iterations, not eight), to entries e, e + 1, ... of a list of capacity cap
+// (< 2^31, so byte offsets fit 32 bits); `dropped` on overflow.  raw: the
+// lane's 8 fp16 values; tag: the row's token index mod 8, which decode reads
+// in place of a search of the row pointers.
 __device__ __forceinline__ void oak_lane_entries(const uint4 raw, unsigned outer, float t_lo, float t_hi,
-                                                 float so, int li, uint16_t* sp, unsigned e, unsigned cap,
-                                                 bool& dropped) {
+                                                 float so, int li, unsigned tag, uint16_t* sp, unsigned e,
+                                                 unsigned cap, bool& dropped) {
   const float r = recip_refined(so);  // s_out = 0: magnitudes 0
   while (outer) {
     const int k = __builtin_ctz(outer);
@@ -756,7 +758,7 @@ __device__ __forceinline__ void oak_lane_entries(const uint4 raw, unsigned outer
     const unsigned mag = (unsigned)__builtin_amdgcn_fmed3f(m, 0.0f, 31.0f);
     if (e < cap)
       *reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(sp) + (e << 1)) =
-          (uint16_t)((unsigned)(li * 8 + k) | (unsigned)above << 7 | mag << 8);
+          (uint16_t)((unsigned)(li * 8 + k) | (unsigned)above << 7 | mag << 8 | tag << 13);
     else
       dropped = true;
     ++e;
@@ -881,7 +883,8 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
       const unsigned rb = base + __shfl(excl_row, 16 * u + rl, 64);
       const unsigned rcnt = __shfl(cnt, 16 * u + rl, 64);
       if (t >= t_new) continue;
-      oak_lane_entries(raw[u], meta[u] & 0xFFu, t_lo, t_hi, sos[u], li, sp, rb + (meta[u] >> 8), capu, dropped);
+      oak_lane_entries(raw[u], meta[u] & 0xFFu, t_lo, t_hi, sos[u], li, (unsigned)(p + t) & 7u, sp,
+                       rb + (meta[u] >> 8), capu, dropped);
       if (li == 0) rp[(unsigned)(p + t + 1)] = min(rb + rcnt, capu);
     }
     base += tile_tot;
@@ -956,7 +959,7 @@ __global__ __launch_bounds__(256) void k_quant_oaken_one(const uint16_t* __restr
   const unsigned cap = (unsigned)t.sparse_cap;  // < 2^31 (validated)
   const unsigned e = base + (unsigned)(incl - lc);
   bool dropped = false;
-  oak_lane_entries(raw, outer, t.thr_lo, t.thr_hi, so, li, sp, e, cap, dropped);
+  oak_lane_entries(raw, outer, t.thr_lo, t.thr_hi, so, li, (unsigned)p & 7u, sp, e, cap, dropped);
   if (li == 0) {
     rp[p + 1] = min(base + (unsigned)rowtot, cap);
   }

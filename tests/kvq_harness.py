@@ -62,6 +62,20 @@ def f16_layout(rows_u16: np.ndarray, layout: str) -> np.ndarray:
     return rows_u16[..., K16_PERM if layout == "K" else V_PERM]
 
 
+def oaken_untag(entries: np.ndarray, rowptr: np.ndarray) -> np.ndarray:
+    """One (b, h) Oaken side list as stored by the library -> the entries
+    without their row tags (channel | side << 7 | mag << 8).  The stored
+    entry carries the token index of its row mod 8 in bits 13-15; this checks
+    the tag of every listed entry (rows 0 .. len(rowptr) - 2) against its row
+    and strips it."""
+    rp = np.asarray(rowptr, np.int64)
+    n = int(rp[-1])
+    e = np.asarray(entries[:n], np.uint16)
+    rows = np.repeat(np.arange(len(rp) - 1), np.diff(rp))
+    assert np.array_equal(e >> 13, (rows & 7).astype(np.uint16)), "Oaken entry row tags"
+    return e & np.uint16(0x1FFF)
+
+
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     """Inverse of unpack_codes (used only to test the unpacker itself)."""
     c = np.ascontiguousarray(codes).astype(np.uint8)

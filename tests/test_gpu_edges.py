@@ -27,8 +27,8 @@ import numpy as np
 import pytest
 
 import oracle
-from kvq_harness import (ATTN_BAR, ATTN_TIGHT, f16_layout, host_bytes, i32_device, rel_err_rows, to_device,
-                         unpack_layout)
+from kvq_harness import (ATTN_BAR, ATTN_TIGHT, f16_layout, host_bytes, i32_device, oaken_untag, rel_err_rows,
+                         to_device, unpack_layout)
 
 pytestmark = pytest.mark.gpu
 
@@ -449,9 +449,8 @@ def test_edges_oaken(G):
         assert np.array_equal(np.diff(rp[:, :, :T + 1].astype(np.int64), axis=-1), on), name + " counts"
         for b in range(B):
             for hh in range(H):
-                n = int(rp[b, hh, T])
                 ref = np.concatenate([oe[b, hh, t, :on[b, hh, t]] for t in range(T)])
-                assert np.array_equal(sp[b, hh, :n], ref), (name, b, hh)
+                assert np.array_equal(oaken_untag(sp[b, hh], rp[b, hh, :T + 1]), ref), (name, b, hh)
         assert (os_ == 0).any() and (oo == 0).any() and (on == 128).any()
         deq[name] = oracle.oaken_dequant_rows(oc, os_, oz, oo, oe, on, OAK_THR, 64)
     q = queries(B, H * G, 19 + G)

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from kvq_harness import (ATTN_BAR, ATTN_TIGHT, f16_layout, host_bytes, i32_device, rel_err_rows,
+from kvq_harness import (ATTN_BAR, ATTN_TIGHT, f16_layout, host_bytes, i32_device, oaken_untag, rel_err_rows,
                          to_device, unpack_layout)
 
 LAYOUT = {"k": "K", "v": "V"}
@@ -445,9 +445,10 @@ def check_oaken_tensor(cache, name, x, thr, B, H, S, lens, group=64):
         assert rp[b, :, 0].max() == 0
         assert np.array_equal(np.diff(rp[b, :, :L + 1].astype(np.int64), axis=-1), on[b, :, :L])
         for h in range(H):
+            ent = oaken_untag(sp[b, h], rp[b, h, :L + 1])
             for t in range(L):
                 n = on[b, h, t]
-                assert np.array_equal(sp[b, h, rp[b, h, t]:rp[b, h, t] + n], oe[b, h, t, :n]), (b, h, t)
+                assert np.array_equal(ent[rp[b, h, t]:rp[b, h, t] + n], oe[b, h, t, :n]), (b, h, t)
     return oracle.oaken_dequant_rows(oc, os_, oz, oo, oe, on, thr, group)
 
 
