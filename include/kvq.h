@@ -124,10 +124,13 @@ enum {
  *    oscale [B][H][S][NG]  float outer scale max|delta| / 31 per group
  *    rowptr [B][H][S+1]    uint32: entries of token t are
  *                          sparse[rowptr[t] .. rowptr[t+1]) of that (b, h)
- *    sparse [B][H][sparse_cap] uint16 entries idx | side << 7 | mag << 8:
+ *    sparse [B][H][sparse_cap] uint16 entries
+ *                          idx | side << 7 | mag << 8 | tag << 13:
  *                          idx the channel, side 1 above T_hi_outer,
  *                          x_hat = T_hi_outer + mag * oscale (side 1) or
- *                          T_lo_outer - mag * oscale (side 0)
+ *                          T_lo_outer - mag * oscale (side 0); tag the
+ *                          entry's token index mod 8 (a row tag for
+ *                          decode, redundant with rowptr)
  *  CHUNK_MIXED ([Cocktail] §3.1.2; C = S / chunk_tokens chunk slots, each
  *  class pool holds up to C chunks per (b, h) in reordered slot order):
  *    codes16 [B][H][C][chunk_tokens][D] fp16, the FP16 chunks, plus 64
