@@ -102,8 +102,9 @@ __device__ __forceinline__ void load_tok_meta(const TokView& v, long long row, f
 // contiguous (NGV per row); the row offset is a multiple of 8, so the loads
 // are aligned.  Rows past the valid range multiply zero weights; the mask
 // keeps their (arbitrary) bytes inside the mantissa, so the pairs stay finite.
-// (load_zraw issues the loads of the zero-point words, zsub_from_raw forms
-// the pairs, so that the loads can be issued well before any use.)
+// (load_zraw issues the loads of the zero-point words, zsub_one forms the
+// pairs of one group and block parity, so that the loads can be issued well
+// before any use and each set of pairs is formed just before its blocks.)
 template <class VC, int NGV>
 __device__ __forceinline__ void load_zraw(const TokView& vv, long long r0, unsigned (&zw)[2 * NGV]) {
   if constexpr (!VC::SYM) {
@@ -123,27 +124,22 @@ __device__ __forceinline__ void load_zraw(const TokView& vv, long long r0, unsig
   }
 }
 template <class VC, int NGV>
-__device__ __forceinline__ void zsub_from_raw(const unsigned (&zw)[2 * NGV], u4_t (&zsub)[2][NGV]) {
-  constexpr int NP = VC::ZODD ? 2 : 1;
+__device__ __forceinline__ u4_t zsub_one(const unsigned (&zw)[2 * NGV], int g, int par) {
+  u4_t z;
   if constexpr (VC::SYM) {
 #pragma unroll
-    for (int g = 0; g < NGV; ++g)
-#pragma unroll
-      for (int p = 0; p < 4; ++p) zsub[0][g][p] = VC::ZMAGIC | 0x00800080u;  // z = 128
+    for (int p = 0; p < 4; ++p) z[p] = VC::ZMAGIC | 0x00800080u;  // z = 128
   } else {
 #pragma unroll
-    for (int g = 0; g < NGV; ++g)
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int ia = 2 * p * NGV + g, ib = (2 * p + 1) * NGV + g;
-        // byte ia of the row bytes -> bits 0-7, byte ib -> bits 16-23
-        const unsigned sel = (0x0Cu << 24) | ((4u + (ib & 3)) << 16) | (0x0Cu << 8) | (unsigned)(ia & 3);
-        const unsigned x = perm(zw[ib >> 2], zw[ia >> 2], sel);
-#pragma unroll
-        for (int par = 0; par < NP; ++par)
-          zsub[par][g][p] = and_or(x << VC::ZSH[par], VC::ZMASK[par], VC::ZMAGIC);
-      }
+    for (int p = 0; p < 4; ++p) {
+      const int ia = 2 * p * NGV + g, ib = (2 * p + 1) * NGV + g;
+      // byte ia of the row bytes -> bits 0-7, byte ib -> bits 16-23
+      const unsigned sel = (0x0Cu << 24) | ((4u + (ib & 3)) << 16) | (0x0Cu << 8) | (unsigned)(ia & 3);
+      const unsigned x = perm(zw[ib >> 2], zw[ia >> 2], sel);
+      z[p] = and_or(x << VC::ZSH[par], VC::ZMASK[par], VC::ZMAGIC);
+    }
   }
+  return z;
 }
 
 // Sum / max over the 16 lanes of a row group (lanes differing in bits 0-3),
@@ -674,8 +670,6 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
         }
       }
       // -(OFF + z) of the B-operand rows as packed fp16 pairs, per V group
-      u4_t zsub[2][NGV];
-      if constexpr (VC::ZP) zsub_from_raw<VC, NGV>(in.zraw, zsub);
       // ---- Oaken: the outer K values' share of each row's score ----
       if constexpr (OAK) {
         __builtin_amdgcn_sched_barrier(0);  // the code loads stay ahead of the entry work
@@ -843,27 +837,37 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       // ---- Oaken: V entries into the outer-value output ----
       if constexpr (OAK) oak_v_apply<QR, NGV>(*oak.w, oak.l[1], oct, nq);
       // ---- O += W V ----
-      u4_t wa[NGV][2];
+      // blocks by V group and parity: each group's weights and -(OFF + z)
+      // pairs are read / formed just before its blocks
+      constexpr int JPG = 8 / NGV, NP = VC::ZODD ? 2 : 1;
 #pragma unroll
-      for (int g = 0; g < NGV; ++g)
+      for (int g = 0; g < NGV; ++g) {
+        u4_t wa[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) wa[g][h] = *reinterpret_cast<const u4_t*>(&W.w[g][h][ar][8 * q4]);
+        for (int h = 0; h < 2; ++h) wa[h] = *reinterpret_cast<const u4_t*>(&W.w[g][h][ar][8 * q4]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        constexpr int JPG = 8 / NGV;
-        u4_t b = vr.block(j);
-        if constexpr (VC::ZP) {
+        for (int par = 0; par < NP; ++par) {
+          u4_t zs{};
+          if constexpr (VC::ZP) zs = zsub_one<VC, NGV>(in.zraw, g, par);
 #pragma unroll
-          for (int p2 = 0; p2 < 4; ++p2) {
-            // copy vector elements to scalars before bit casts: clang miscompiles a bit cast
-            // applied directly to an ext-vector element
-            const unsigned bv = b[p2], zv = zsub[VC::ZODD ? (j & 1) : 0][j / JPG][p2];
-            const h2_t x = __builtin_bit_cast(h2_t, bv) + __builtin_bit_cast(h2_t, zv);
-            b[p2] = __builtin_bit_cast(unsigned, x);
+          for (int jj = 0; jj < JPG; ++jj) {
+            const int j = g * JPG + jj;
+            if (VC::ZODD && (j & 1) != par) continue;
+            u4_t b = vr.block(j);
+            if constexpr (VC::ZP) {
+#pragma unroll
+              for (int p2 = 0; p2 < 4; ++p2) {
+                // copy vector elements to scalars before bit casts: clang miscompiles a bit cast
+                // applied directly to an ext-vector element
+                const unsigned bv = b[p2], zv = zs[p2];
+                const h2_t x = __builtin_bit_cast(h2_t, bv) + __builtin_bit_cast(h2_t, zv);
+                b[p2] = __builtin_bit_cast(unsigned, x);
+              }
+            }
+            st.o[j] = mfma(wa[0], b, st.o[j]);
+            st.o[j] = mfma(wa[1], b, st.o[j]);
           }
         }
-        st.o[j] = mfma(wa[j / JPG][0], b, st.o[j]);
-        st.o[j] = mfma(wa[j / JPG][1], b, st.o[j]);
       }
       wave_lds_sync();
     }
