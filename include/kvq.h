@@ -368,9 +368,12 @@ kvq_status kvq_dsq_append(const kvq_cache* c, const void* k_new, const void* v_n
 
 /*
  * Workspace needed by kvq_decode_attn for the same (c, q_heads, max_len,
- * num_splits); 0 when the chosen split count is 1.  Host only.  The
- * workspace holds the split partials (m, l, unnormalized output per batch,
- * query head and split); one workspace serves one call at a time.
+ * num_splits).  Host only.  The workspace holds the split partials (m, l,
+ * unnormalized output per batch, query head and split; none when the chosen
+ * split count is 1) and, for OAKEN, each token's share of the scores from
+ * the K outer values ([batch][q_heads][max_len] binary32, from a 256-byte
+ * aligned offset), formed by a first kernel of the same call.  Other modes
+ * with one split need 0 bytes.  One workspace serves one call at a time.
  */
 kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32_t max_len,
                                       int32_t num_splits, size_t* bytes);
@@ -413,20 +416,21 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t q_heads,
 /*
  * kvq_decode_attn for callers that cannot allocate device memory (code under
  * HIP graph capture, serving loops that forbid hipMalloc): the same
- * arguments without the workspace, and the same kernels; the split partials
- * go to a fixed array of KVQ_STATIC_SCRATCH_BYTES in the library's device
- * image, one per device, held until the process ends.  The array's device
+ * arguments without the workspace, and the same kernels; what the workspace
+ * would hold (split partials, OAKEN's score shares) goes to a fixed array of
+ * KVQ_STATIC_SCRATCH_BYTES in the library's device image, one per device,
+ * held until the process ends.  The array's device
  * address is looked up on the first call on each device (the current
  * device), after which no call allocates or frees anything.
- *  Returns KVQ_ERR_WORKSPACE, before any launch, when the chosen split plan
- *  needs more than KVQ_STATIC_SCRATCH_BYTES (kvq_decode_workspace_bytes
- *  gives the need), else as kvq_decode_attn.
+ *  Returns KVQ_ERR_WORKSPACE, before any launch, when the call needs more
+ *  than KVQ_STATIC_SCRATCH_BYTES (kvq_decode_workspace_bytes gives the
+ *  need), else as kvq_decode_attn.
  *  Every call on a device shares that device's array: calls that overlap on
  *  one device (two streams, two threads) race and must be ordered by the
- *  caller.  Each call writes every partial it reads, so the array needs no
- *  clearing between calls.
+ *  caller.  Each call writes every value of the array that enters its
+ *  result before reading it, so the array needs no clearing between calls.
  */
-#define KVQ_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+#define KVQ_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
 kvq_status kvq_decode_attn_noalloc(const kvq_cache* c, const void* q, int32_t q_heads,
                                    const int32_t* seq_len, int32_t max_len, float sm_scale, float* out,
                                    int32_t num_splits, void* stream);

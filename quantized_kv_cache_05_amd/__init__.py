@@ -43,7 +43,7 @@ KVQ_FLAG_BAD_CHUNK_BITS = 8
 KVQ_FLAG_PAGE_RANGE = 16
 
 PART_STRIDE = 132  # floats per split partial in the decode workspace
-STATIC_SCRATCH_BYTES = 32 << 20  # KVQ_STATIC_SCRATCH_BYTES: split partials of kvq_decode_attn_noalloc
+STATIC_SCRATCH_BYTES = 128 << 20  # KVQ_STATIC_SCRATCH_BYTES: the workspace of kvq_decode_attn_noalloc
 
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 

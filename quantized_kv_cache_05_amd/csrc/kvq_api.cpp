@@ -297,12 +297,22 @@ kvq_status plan_decode(const kvq_cache* c, int q_heads, int max_len, int num_spl
   return KVQ_OK;
 }
 
-size_t workspace_for(const kvq_cache* c, int q_heads, const Plan& p) {
+// Decode workspace: the split partials (when the plan splits), then for
+// OAKEN the K outer-value score shares [batch][q_heads][max_len], from a
+// 256-byte aligned offset.
+size_t partials_bytes(const kvq_cache* c, int q_heads, const Plan& p) {
   if (p.num_splits <= 1) return 0;
   return (size_t)c->batch * (size_t)q_heads * (size_t)p.num_splits * kvq::kPartStride * sizeof(float);
 }
+size_t oak_ksc_offset(const kvq_cache* c, int q_heads, const Plan& p) {
+  return (partials_bytes(c, q_heads, p) + 255) & ~(size_t)255;
+}
+size_t workspace_for(const kvq_cache* c, int q_heads, int max_len, const Plan& p) {
+  if (c->mode != KVQ_MODE_OAKEN || max_len <= 0) return partials_bytes(c, q_heads, p);
+  return oak_ksc_offset(c, q_heads, p) + (size_t)c->batch * (size_t)q_heads * (size_t)max_len * sizeof(float);
+}
 
-// Split partials of kvq_decode_attn_noalloc: a fixed array in the device
+// Workspace of kvq_decode_attn_noalloc: a fixed array in the device
 // image (each device holds its own copy).  Host code never passes the
 // array's name to a kernel: it is a host-side stand-in, and the device
 // address comes from hipGetSymbolAddress, looked up once per device with
@@ -342,7 +352,7 @@ kvq_status decode_attn(const kvq_cache* c, const void* q, int32_t q_heads, const
   Plan p;
   s = plan_decode(c, q_heads, max_len, num_splits, &p);
   if (s != KVQ_OK) return s;
-  const size_t need = workspace_for(c, q_heads, p);
+  const size_t need = workspace_for(c, q_heads, max_len, p);
   if (use_static) {
     if (need > KVQ_STATIC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
   } else if (need) {
@@ -370,7 +380,10 @@ kvq_status decode_attn(const kvq_cache* c, const void* q, int32_t q_heads, const
   d.split_len = p.split_len;
   d.qscale = sm_scale * 1.4426950408889634f;
   d.out = out;
-  d.ws = static_cast<float*>(need ? workspace : nullptr);
+  d.ws = p.num_splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  d.oak_ksc = c->mode == KVQ_MODE_OAKEN && max_len > 0
+                  ? reinterpret_cast<float*>(static_cast<char*>(workspace) + oak_ksc_offset(c, q_heads, p))
+                  : nullptr;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (c->mode) {
@@ -535,7 +548,7 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32
   Plan p;
   s = plan_decode(c, q_heads, max_len, num_splits, &p);
   if (s != KVQ_OK) return s;
-  *bytes = workspace_for(c, q_heads, p);
+  *bytes = workspace_for(c, q_heads, max_len, p);
   return KVQ_OK;
 }
 

@@ -437,6 +437,7 @@ struct AttnParams {
   const int* seq_len;
   float* out;
   float* ws;           // split partials [B][Hq][num_splits][kPartStride]
+  float* oak_ksc;      // OAKEN: K outer-value score shares [B][Hq][max_len]
   const int* seg;
   unsigned* status;
   TensorArgs k, v;

@@ -181,20 +181,16 @@ __device__ __forceinline__ float lane0(float v) {
 // ([Oaken] §3.2.2): an outer value is T_hi + mag * s_out above the upper outer
 // threshold and T_lo - mag * s_out below the lower one; the dense code at an
 // outer position is the zero-point, so the dense part there is exactly 0 and
-// the outer values only add.  The row pointers of the next tile are loaded
+// the outer values only add.  The V row pointers of the next tile are loaded
 // one tile ahead, so the entry loads go out with the tile's code loads.  No
 // LDS atomics are used (they cost about as much as the rest of the tile), and
 // every sum is taken in a fixed order, so decode is deterministic.
 //
-// K (score part of each row).  The 32 rows of a tile own the contiguous
-// range [rp[tile], rp[tile + 32]) of the row-major entry list; a lane takes
-// 4 consecutive entries (one 8-byte load, 256 entries per round).  Per query,
-// each entry contributes u = q[idx] T_side and w = q[idx] (+-mag), the latter
-// kept per channel group g; exclusive prefix sums of u and of each w_g over
-// the round (inside the lane, then across the wave by DPP) go to LDS, and the
-// lane of row r forms its sum from two differences per array:
-//   sum_{e in row r} q[idx] x_hat = dU + sum_g s_out[r][g] dW_g,
-// so no entry needs to know its row.
+// K (score part of each row).  sum_{e in row t} q[idx] x_hat depends on
+// the query and the entries only, not on the softmax, so a separate kernel
+// (k_oak_kscore) forms it for every token beforehand, one thread per row
+// summing its entries in order, into the decode workspace; the tile loop adds
+// one float per token and query to the scores.
 //
 // V (outer-value output).  The entries of rows 8k .. 8k + 7 (octet k) take
 // one lane each (one 2-byte load per octet).  The row of an entry is 8k plus
@@ -212,9 +208,7 @@ constexpr int kOakCopies = QR == 16 ? 1 : 8;
 
 template <int QR, int NG>
 struct __attribute__((aligned(16))) OakWave {
-  float ex[NG + 1][264];               // K: exclusive prefix sums over a round's entries, [256] = total
   float so[kTile][NG];                 // V: outer scales of the tile's rows
-  float ksc[QR][kTile];                // outer-value part of each query's score, per row
   float pr[QR][kTile];                 // softmax numerators, per query and row (QR > 1)
   // one query row: per row, the numerator p times T_lo, T_hi and each group's
   // outer scale, so that an entry's share is one fma (p x_hat = p T + mag p s)
@@ -233,64 +227,33 @@ struct OakList {
 
 template <int QR, int NG>
 struct OakCtx {
-  OakList l[2];            // K, V
+  OakList v;               // the V side list
+  const float* ksc;        // K outer-value score shares of query row m, token t: ksc[m * ld + t]
+  int ld;                  // row stride of ksc (tokens)
   OakWave<QR, NG>* w;      // this wave's LDS area
 };
 struct NoOak {};
 
-// Row pointers of one tile for a lane: lane l holds rp of rows l mod 32 and
-// l mod 32 + 1 (both halves of the wave the same rows), row indices clamped
-// to [t0, t1] so that rows outside the split own no entries.
+// V row pointers of one tile for a lane: lane l holds rp of rows l mod 32
+// and l mod 32 + 1 (both halves of the wave the same rows), row indices
+// clamped to [t0, t1] so that rows outside the split own no entries.
 struct OakRp {
-  unsigned a[2], b[2];
+  unsigned a, b;
 };
 
-__device__ __forceinline__ OakRp oak_rp_load(const OakList (&l)[2], int tile, int t0, int t1) {
+__device__ __forceinline__ OakRp oak_rp_load(const OakList& l, int tile, int t0, int t1) {
   const int r = (int)(threadIdx.x & 31);
   const int ia = min(max(tile + r, t0), t1), ib = min(max(tile + r + 1, t0), t1);
-  OakRp p;
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    p.a[x] = ld_nt<unsigned>(l[x].rowptr + ia);
-    p.b[x] = ld_nt<unsigned>(l[x].rowptr + ib);
-  }
-  return p;
+  return OakRp{ld_nt<unsigned>(l.rowptr + ia), ld_nt<unsigned>(l.rowptr + ib)};
 }
 
-// Entry loads through the global address space: the list pointer is one of
-// two globals, which the compiler would otherwise treat as a flat address
-// that might alias LDS, ordering every later LDS access behind the load.
-// Indices are clamped into the list (entries outside a range are masked by
-// the caller).
-__device__ __forceinline__ u2_t oak_words(const OakList& l, unsigned base, unsigned c) {
-  typedef const __attribute__((address_space(1))) u2_t gu2_t;
-  const unsigned wi = min((base >> 2) + 64u * c + (threadIdx.x & 63), max(l.cap >> 2, 1u) - 1u);
-  return __builtin_nontemporal_load((gu2_t*)(l.sparse + 4ull * wi));
-}
+// Entry loads through the global address space: the list pointer would
+// otherwise be taken as a flat address that might alias LDS, ordering every
+// later LDS access behind the load.  The index is clamped into the list
+// (entries outside a range are masked by the caller).
 __device__ __forceinline__ unsigned oak_entry(const OakList& l, unsigned e) {
   typedef const __attribute__((address_space(1))) uint16_t gu16_t;
   return __builtin_nontemporal_load((gu16_t*)(l.sparse + min(e, max(l.cap, 1u) - 1u)));
-}
-
-// 32-bit DPP move with old = 0 and bound_ctrl: lanes without a source read 0.
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ unsigned dpp_u(unsigned v) {
-  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
-}
-// Inclusive prefix sum in lane order over the wave: row_shr 1, 2, 4, 8
-// inside each 16-lane row, then row_bcast:15 (last lane of rows 0 and 2 into
-// rows 1 and 3) and row_bcast:31 (lane 31 into rows 2 and 3).  The sum's
-// order is fixed, so it is deterministic.
-__device__ __forceinline__ float wave_prefix_sum(float v) {
-  auto f = [](unsigned x) { return __builtin_bit_cast(float, x); };
-  const auto u = [](float x) { return __builtin_bit_cast(unsigned, x); };
-  v += f(dpp_u<0x111>(u(v)));
-  v += f(dpp_u<0x112>(u(v)));
-  v += f(dpp_u<0x114>(u(v)));
-  v += f(dpp_u<0x118>(u(v)));
-  v += f(dpp_u<0x142, 0xA>(u(v)));
-  v += f(dpp_u<0x143, 0xC>(u(v)));
-  return v;
 }
 
 // x_hat of entry en (idx | side << 7 | mag << 8 | tag << 13) with its row's outer scale,
@@ -302,74 +265,6 @@ __device__ __forceinline__ float oak_value(unsigned en, float so, const OakList&
   const bool hi = en & 128u;
   const float step = (float)((en >> 8) & 31u) * so;
   return (hi ? l.t_hi : l.t_lo) + (hi ? step : -step);
-}
-
-// K outer values of one tile: for each query m < nq, the sum over row r's
-// entries of q[m][idx] x_hat, into W.ksc[m][r].  rp: the tile's row pointers;
-// wd0: the lane's first round of entries (base = e0 rounded down to 4);
-// so_row: the outer scales of row lane & 31 (every lane computes a row; the
-// two halves of the wave write the same values).
-template <int QR, int NG, class LDS>
-__device__ __forceinline__ void oak_k_tile(const LDS& L, OakWave<QR, NG>& W, const OakList& l, const OakRp& rp,
-                                           u2_t wd0, unsigned e0, unsigned e1, unsigned base,
-                                           const float (&so_row)[NG], int nq) {
-  const unsigned lane = threadIdx.x & 63;
-  const unsigned ra = min(rp.a[0], l.cap), rb = min(rp.b[0], l.cap);
-  float acc[QR];
-#pragma unroll
-  for (int m = 0; m < QR; ++m) acc[m] = 0.0f;
-  for (unsigned c = 0; base + 256u * c < e1; ++c) {
-    const u2_t wd = c == 0 ? wd0 : oak_words(l, base, c);
-    const unsigned cb = base + 256u * c, e = cb + 4u * lane;
-    unsigned idx[4], grp[4];
-    float tv[4], sm[4];
-    bool ok[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const unsigned word = wd[j >> 1];
-      const unsigned en = (j & 1) ? (word >> 16) : (word & 0xFFFFu);
-      idx[j] = en & 127u;
-      grp[j] = NG == 1 ? 0u : idx[j] / (128 / NG);
-      const bool hi = en & 128u;
-      const float mag = (float)((en >> 8) & 31u);
-      tv[j] = hi ? l.t_hi : l.t_lo;
-      sm[j] = hi ? mag : -mag;
-      ok[j] = e + j >= e0 && e + j < e1;
-    }
-    const unsigned s = min(max(ra, cb) - cb, 256u), t = min(max(rb, cb) - cb, 256u);
-#pragma unroll
-    for (int m = 0; m < QR; ++m) {
-      if (m < nq) {
-        float v[NG + 1][4];
-        float qr[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) qr[j] = L.q[m][idx[j]];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float qv = ok[j] ? qr[j] : 0.0f;
-          v[0][j] = qv * tv[j];
-          const float w = qv * sm[j];
-#pragma unroll
-          for (int g = 0; g < NG; ++g) v[1 + g][j] = grp[j] == (unsigned)g ? w : 0.0f;
-        }
-#pragma unroll
-        for (int a = 0; a <= NG; ++a) {
-          const float p1 = v[a][0], p2 = p1 + v[a][1], p3 = p2 + v[a][2], tot = p3 + v[a][3];
-          const float inc = wave_prefix_sum(tot), exc = inc - tot;
-          *reinterpret_cast<float4*>(&W.ex[a][4 * lane]) = float4{exc, exc + p1, exc + p2, exc + p3};
-          if (lane == 63) W.ex[a][256] = inc;
-        }
-        wave_lds_sync();
-        float d = W.ex[0][t] - W.ex[0][s];
-#pragma unroll
-        for (int g = 0; g < NG; ++g) d = fmaf(so_row[g], W.ex[1 + g][t] - W.ex[1 + g][s], d);
-        acc[m] += d;
-        wave_lds_sync();  // the next pass rewrites ex
-      }
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < QR; ++m) W.ksc[m][lane & 31] = acc[m];
 }
 
 // V entries of one tile, before the softmax: the lane's entry of each octet
@@ -384,8 +279,8 @@ __device__ __forceinline__ OakOct oak_v_prep(const OakList& l, const OakRp& rp) 
   const unsigned lane = threadIdx.x & 63;
   OakOct o;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) o.ro[k] = min((unsigned)__builtin_amdgcn_readlane((int)rp.a[1], 8 * k), l.cap);
-  o.ro[4] = min((unsigned)__builtin_amdgcn_readlane((int)rp.b[1], kTile - 1), l.cap);
+  for (int k = 0; k < 4; ++k) o.ro[k] = min((unsigned)__builtin_amdgcn_readlane((int)rp.a, 8 * k), l.cap);
+  o.ro[4] = min((unsigned)__builtin_amdgcn_readlane((int)rp.b, kTile - 1), l.cap);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     o.en[k] = oak_entry(l, o.ro[k] + lane);
@@ -485,8 +380,9 @@ struct TileIn {
 //         paged too (false: K is a per-sequence view, e.g. an fp16 tail).
 //         With CHANK, the block scales (kc) are pool bases, indexed by the
 //         page row of the block.
-//  OAK: Oaken; oak holds the side lists and the wave's LDS area (OakCtx), the
-//       outer values enter the scores and the wave's outer-value output
+//  OAK: Oaken; oak holds the V side list, the K outer-value score shares
+//       and the wave's LDS area (OakCtx); the score shares are added to the
+//       scores and the V outer values enter the wave's outer-value output
 //       inside the loop (see OakWave).
 template <int QR, int NGK, int NGV, class KC, class VC, bool CHANK, bool OAK, int TPS, bool PAGED = false,
           bool PK = PAGED, class LDS, class OK = NoOak>
@@ -525,7 +421,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
   if constexpr (PAGED) pg_next = page_entry_v(vv_.pages, min(tb + wave * kTile * TPS, t1 - 1) >> vv_.pshift);
   // Oaken: row pointers of the wave's next tile, one tile ahead
   OakRp rp_next{};
-  if constexpr (OAK) rp_next = oak_rp_load(oak.l, tb + wave * kTile * TPS, t0, t1);
+  if constexpr (OAK) rp_next = oak_rp_load(oak.v, tb + wave * kTile * TPS, t0, t1);
   for (int step = tb + wave * kTile * TPS; step < t1; step += kNW * kTile * TPS) {
     TokView kv = kv_, vv = vv_;
     long long ro = 0;  // paged: pool row of token t = t + ro (this step's page)
@@ -620,26 +516,28 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       OakRp rpc{};
       if constexpr (OAK) {
         rpc = rp_next;
-        rp_next = oak_rp_load(oak.l, tt + 1 < TPS ? tile + kTile : step + kNW * kTile * TPS, t0, t1);
+        rp_next = oak_rp_load(oak.v, tt + 1 < TPS ? tile + kTile : step + kNW * kTile * TPS, t0, t1);
       }
       if (tile + kTile <= t0) continue;
       // ---- loads ----
-      // Oaken: the tile's K entry range and first round of entries, its V
-      // entries (octets) and the rows' outer scales, issued ahead of the codes
-      unsigned ok_e0 = 0u, ok_e1 = 0u, ok_base = 0u;
-      u2_t ok_wd = u2_t{0u, 0u};
-      float oso[2][NGV];  // outer scales of row lane & 31, K and V
+      // Oaken: the tile's V entries (octets), the rows' V outer scales and
+      // the K score shares of the lane's score slots, issued ahead of the codes
+      float oso[NGV];  // V outer scales of row lane & 31
+      float oks[2][GI];
       OakOct oct{};
       if constexpr (OAK) {
-        const unsigned cap = oak.l[0].cap;
-        ok_e0 = min((unsigned)__builtin_amdgcn_readfirstlane((int)rpc.a[0]), cap);
-        ok_e1 = min((unsigned)__builtin_amdgcn_readlane((int)rpc.b[0], kTile - 1), cap);
-        ok_base = ok_e0 & ~3u;
-        ok_wd = oak_words(oak.l[0], ok_base, 0);
         const long long t = tile + (lane & 31);
-        load_f32s<NGV>(kv.oscale + (unsigned)(t * NGV), oso[0]);
-        load_f32s<NGV>(vv.oscale + (unsigned)(t * NGV), oso[1]);
-        oct = oak_v_prep(oak.l[1], rpc);
+        load_f32s<NGV>(vv.oscale + (unsigned)(t * NGV), oso);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const unsigned tk = (unsigned)min(tile + nb * 16 + n16, oak.ld - 1);
+#pragma unroll
+          for (int i = 0; i < GI; ++i) {
+            const unsigned m = (unsigned)min(QRW::slot_query(q4, i), nq - 1);
+            oks[nb][i] = ld_nt<float>(oak.ksc + (m * (unsigned)oak.ld + tk));
+          }
+        }
+        oct = oak_v_prep(oak.v, rpc);
         // issued before the code loads, so that the entry work below waits on
         // these alone (loads complete in order)
         __builtin_amdgcn_sched_barrier(0);
@@ -670,14 +568,11 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
         }
       }
       // -(OFF + z) of the B-operand rows as packed fp16 pairs, per V group
-      // ---- Oaken: the outer K values' share of each row's score ----
+      // ---- Oaken: the rows' V outer scales into LDS ----
       if constexpr (OAK) {
         __builtin_amdgcn_sched_barrier(0);  // the code loads stay ahead of the entry work
-        auto& OW = *oak.w;
 #pragma unroll
-        for (int g = 0; g < NGV; ++g) OW.so[lane & 31][g] = oso[1][g];  // (both halves: same values)
-        oak_k_tile<QR, NGV>(L, OW, oak.l[0], rpc, ok_wd, ok_e0, ok_e1, ok_base, oso[0], nq);
-        wave_lds_sync();
+        for (int g = 0; g < NGV; ++g) oak.w->so[lane & 31][g] = oso[g];  // (both halves: same values)
       }
       // ---- scores ----
       float sc[2][GI];
@@ -726,10 +621,8 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-          for (int i = 0; i < GI; ++i) {
-            const float o = oak.w->ksc[min(QRW::slot_query(q4, i), R - 1)][nb * 16 + n16];
-            sc[nb][i] = fmaf(o, P.qscale, sc[nb][i]);  // (rows outside the range are masked below)
-          }
+          for (int i = 0; i < GI; ++i)
+            sc[nb][i] = fmaf(oks[nb][i], P.qscale, sc[nb][i]);  // (rows outside the range are masked below)
       }
       // ---- online softmax (base 2) ----
       float alpha[GI];
@@ -779,8 +672,9 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
         }
       // ---- Oaken: the softmax numerators of the rows, for the V entries ----
       if constexpr (OAK && QR == 1) {
+        wave_lds_sync();  // the rows' outer scales, written by other lanes
         if (q4 == 0) {  // lanes 0-15 hold rows n16 and 16 + n16
-          const OakList& lv = oak.l[1];
+          const OakList& lv = oak.v;
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb) {
             const int row = nb * 16 + n16;
@@ -835,7 +729,7 @@ __device__ __forceinline__ void attend_wave(const AttnParams& P, LDS& L,
       }
       wave_lds_sync();
       // ---- Oaken: V entries into the outer-value output ----
-      if constexpr (OAK) oak_v_apply<QR, NGV>(*oak.w, oak.l[1], oct, nq);
+      if constexpr (OAK) oak_v_apply<QR, NGV>(*oak.w, oak.v, oct, nq);
       // ---- O += W V ----
       // blocks by V group and parity: each group's weights and -(OFF + z)
       // pairs are read / formed just before its blocks

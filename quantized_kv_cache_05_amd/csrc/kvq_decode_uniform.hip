@@ -139,7 +139,7 @@ AttnParams make_attn_params(const CacheArgs& c, const DecodeLaunch& d) {
   P.B = c.B; P.H = c.H; P.S = c.S; P.Hq = d.Hq; P.G = d.G; P.qtiles = d.qtiles;
   P.max_len = d.max_len; P.num_splits = d.num_splits; P.split_len = d.split_len;
   P.chunk_tokens = c.chunk_tokens; P.qscale = d.qscale; P.q = d.q; P.seq_len = d.seq_len;
-  P.out = d.out; P.ws = d.ws; P.seg = c.seg; P.status = c.status;
+  P.out = d.out; P.ws = d.ws; P.oak_ksc = d.oak_ksc; P.seg = c.seg; P.status = c.status;
   P.k = c.k; P.v = c.v;
   P.pages = c.pages;
   P.pshift = c.ptok ? __builtin_ctz((unsigned)c.ptok) : 0;

@@ -60,6 +60,7 @@ struct DecodeLaunch {
   float qscale;  // sm_scale * log2(e)
   float* out;
   float* ws;     // split partials, null when num_splits == 1
+  float* oak_ksc;  // OAKEN: K outer-value score shares [B][Hq][max_len] (null otherwise)
 };
 
 // vl: write the V row layout (else the K row layout), see kvq.h.

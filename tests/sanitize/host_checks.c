@@ -102,8 +102,8 @@ static void api_checks(void) {
   c.batch = 16;
   c.kv_heads = 32;
   c.max_seq = 65536;
-  CHECK(kvq_decode_workspace_bytes(&c, 32, 65536, 256, &n) == KVQ_OK && n > KVQ_STATIC_SCRATCH_BYTES);
-  CHECK(kvq_decode_attn_noalloc(&c, DEV(1), 32, DEV(2), 65536, 0.1f, DEV(3), 256, NULL) == KVQ_ERR_WORKSPACE);
+  CHECK(kvq_decode_workspace_bytes(&c, 32, 65536, 1024, &n) == KVQ_OK && n > KVQ_STATIC_SCRATCH_BYTES);
+  CHECK(kvq_decode_attn_noalloc(&c, DEV(1), 32, DEV(2), 65536, 0.1f, DEV(3), 1024, NULL) == KVQ_ERR_WORKSPACE);
   CHECK(kvq_decode_attn_noalloc(&c, DEV(1), 32, DEV(2), 65536, 0.1f, DEV(3), 4, NULL) == KVQ_ERR_INVALID_ARG);
   /* preparation entry points */
   CHECK(kvq_chunk_bits(DEV(1), DEV(2), 0, 8, 16, 0.6, 0.1, NULL, DEV(3), NULL) == KVQ_OK);
