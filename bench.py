@@ -656,7 +656,7 @@ def source_hash():
 
 
 def stored_traffic(idx):
-    """HBM bytes per decode launch from profiles/decode_traffic_w<idx>.txt, if it was taken on the
+    """HBM bytes per decode call from profiles/decode_traffic_w<idx>.txt, if it was taken on the
     current kernel sources; None otherwise."""
     path = os.path.join(ROOT, "profiles", "decode_traffic_w%d.txt" % idx)
     if not os.path.exists(path):
@@ -670,15 +670,22 @@ def stored_traffic(idx):
     if kv.get("source_hash") != source_hash():
         return None
     try:
-        return int(float(kv["hbm_bytes_per_launch"]))
+        return int(float(kv["hbm_bytes_per_call"]))
     except (KeyError, ValueError):
         return None
 
 
+def decode_kernel(name):
+    """The kernels that read the cache in a decode call: the attention kernel and, for Oaken,
+    the K outer-value score kernel that runs before it (the split merge reads only partials)."""
+    return "k_attn_" in name or "k_oak_kscore" in name
+
+
 def summarize_pmc(fetch_csv, write_csv, bench_log, copy_mib):
-    """Per-launch HBM bytes of the attention kernel from FETCH_SIZE / WRITE_SIZE (KiB per
-    dispatch).  Each counter is scaled by what it reads for the plain copy of copy_mib MiB that
-    the same run made (the largest copy dispatch): bytes moved / counter KiB."""
+    """Per-call HBM bytes of the decode kernels (decode_kernel) from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), summed over the kernels of one call.  Each counter is scaled by what it
+    reads for the plain copy of copy_mib MiB that the same run made (the largest copy
+    dispatch): bytes moved / counter KiB."""
     import csv
 
     def per_dispatch(path):
@@ -699,9 +706,11 @@ def summarize_pmc(fetch_csv, write_csv, bench_log, copy_mib):
         attn = [r for r in rows if "k_attn_" in r[0]]
         if not attn:
             raise SystemExit("%s: no attention kernel dispatch" % path)
-        kib = sum(r[2] for r in attn) / len(attn)
+        dec = [r for r in rows if decode_kernel(r[0])]
+        kib = sum(r[2] for r in dec) / len(attn)  # per call: one attention dispatch per call
         factor = copy_bytes / (probe[2] * 1024.0)
-        res[name] = (kib, probe[2], factor, len(attn), attn[0][0])
+        names = sorted({short_kernel_name(r[0]) for r in dec})
+        res[name] = (kib, probe[2], factor, len(attn), " + ".join(names))
     bench = None
     with open(bench_log) as fh:
         for line in fh:
@@ -709,20 +718,20 @@ def summarize_pmc(fetch_csv, write_csv, bench_log, copy_mib):
                 bench = json.loads(line)
     hbm = sum(kib * 1024.0 * f for kib, _, f, _, _ in res.values())
     lines = [
-        "kernel: %s" % res["fetch"][4],
+        "kernels (per decode call): %s" % res["fetch"][4],
         "workload: %s" % (bench["config"]["workload"] if bench else "?"),
-        "dispatches: %d (FETCH_SIZE run), %d (WRITE_SIZE run)" % (res["fetch"][3], res["write"][3]),
+        "decode calls: %d (FETCH_SIZE run), %d (WRITE_SIZE run)" % (res["fetch"][3], res["write"][3]),
         "copy_probe_bytes: %d" % copy_bytes,
         "copy_probe_fetch_kib: %.1f" % res["fetch"][1],
         "copy_probe_write_kib: %.1f" % res["write"][1],
         "fetch_factor: %.5f" % res["fetch"][2],
         "write_factor: %.5f" % res["write"][2],
-        "fetch_kib_per_launch: %.1f" % res["fetch"][0],
-        "write_kib_per_launch: %.1f" % res["write"][0],
-        "hbm_bytes_per_launch: %d" % round(hbm),
+        "fetch_kib_per_call: %.1f" % res["fetch"][0],
+        "write_kib_per_call: %.1f" % res["write"][0],
+        "hbm_bytes_per_call: %d" % round(hbm),
     ]
     if bench:
-        lines += ["algorithmic_bytes_per_launch: %d" % bench["decode_bytes"],
+        lines += ["algorithmic_bytes_per_call: %d" % bench["decode_bytes"],
                   "traffic_over_algorithmic: %.4f" % (hbm / bench["decode_bytes"])]
     lines.append("source_hash: %s" % source_hash())
     print("\n".join(lines))
@@ -759,7 +768,7 @@ def summarize_busy(counter_csv, agent_csv, bench_log):
     dur = collections.defaultdict(dict)
     with open(counter_csv) as fh:
         for r in csv.DictReader(fh):
-            if "k_attn_" not in r["Kernel_Name"] and "k_merge" not in r["Kernel_Name"]:
+            if not decode_kernel(r["Kernel_Name"]) and "k_merge" not in r["Kernel_Name"]:
                 continue
             name = short_kernel_name(r["Kernel_Name"])
             agg[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
@@ -810,12 +819,12 @@ def summarize_stats(stats_csv, bench_log):
         lines.append("%-58s %6s %12.2f %12.2f %12.2f %7.2f" % (
             short_kernel_name(r["Name"])[:58], r["Calls"], float(r["AverageNs"]) / 1e3,
             float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
-    attn = [r for r in rows if "k_attn_" in r["Name"]]
-    if attn and bench:
-        a = attn[0]
-        lines += ["", "attention kernel: %s" % short_kernel_name(a["Name"]),
-                  "attention avg_us: %.2f -> %.1f GB/s on the decode algorithmic bytes" % (
-                      float(a["AverageNs"]) / 1e3, bench["decode_bytes"] / float(a["AverageNs"]))]
+    dec = [r for r in rows if decode_kernel(r["Name"])]
+    if dec and bench:
+        ns = sum(float(r["AverageNs"]) for r in dec)
+        lines += ["", "decode kernels: %s" % " + ".join(short_kernel_name(r["Name"]) for r in dec),
+                  "decode kernels avg_us (sum): %.2f -> %.1f GB/s on the decode algorithmic bytes" % (
+                      ns / 1e3, bench["decode_bytes"] / ns)]
     lines.append("source_hash: %s" % source_hash())
     print("\n".join(lines))
 
