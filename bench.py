@@ -641,17 +641,43 @@ def cpu_baseline(w, idx, budget_s):
 # ---------------------------------------------------------------------------
 # stored HBM counters of the decode kernel (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)
 
+def code_text(src):
+    """C/C++ source without comments and with whitespace collapsed, so that a change to
+    comments or layout alone leaves source_hash unchanged (string literals are kept whole)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash():
-    """Hash of the sources the decode kernels are built from (their headers, the decode
-    translation units and the host code that plans their launches)."""
+    """Hash of the code the decode kernels are built from (their headers, the decode
+    translation units and the host code that plans their launches), comments and layout
+    excluded."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_kv_cache_05_amd", "csrc")
     files = set(glob.glob(os.path.join(csrc, "*.h")) + glob.glob(os.path.join(csrc, "kvq_decode_*.hip")) +
                 [os.path.join(csrc, "kvq_api.cpp")])
     for f in sorted(files):
-        with open(f, "rb") as fh:
+        with open(f, encoding="utf-8") as fh:
             h.update(os.path.basename(f).encode())
-            h.update(fh.read())
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -177,7 +177,7 @@ __device__ __forceinline__ float lane0(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Oaken sparse side lists, consumed inside the tile loop.  Reconstruction
+// Oaken sparse side lists in the tile loop.  Reconstruction
 // ([Oaken] §3.2.2): an outer value is T_hi + mag * s_out above the upper outer
 // threshold and T_lo - mag * s_out below the lower one; the dense code at an
 // outer position is the zero-point, so the dense part there is exactly 0 and
@@ -195,13 +195,13 @@ __device__ __forceinline__ float lane0(float v) {
 // V (outer-value output).  The entries of rows 8k .. 8k + 7 (octet k) take
 // one lane each (one 2-byte load per octet).  The row of an entry is 8k plus
 // the row tag the quantizer stores in the entry (bits 13-15: the token index
-// mod 8; tiles start at multiples of 32).  Within an octet two entries share an address of the
-// outer-value output only if they share row and channel, which a row's list
-// never does, so with one output copy per row mod 8 every octet updates its
-// copies by a plain read-modify-write with no conflicts; octets follow one
-// another in program order.  The copies are summed when the wave records its
-// result.  With 16 query rows a single copy is kept and each octet is applied
-// one row at a time.
+// mod 8; tiles start at multiples of 32).  Within an octet two entries share
+// an address of the outer-value output only if they share row and channel,
+// which a row's list never does, so with one output copy per row mod 8 every
+// octet updates its copies by a plain read-modify-write with no conflicts;
+// octets follow one another in program order.  The copies are summed when the
+// wave records its result.  With 16 query rows a single copy is kept and each
+// octet is applied one row at a time.
 
 template <int QR>
 constexpr int kOakCopies = QR == 16 ? 1 : 8;
