@@ -231,6 +231,28 @@ def test_workspace_plan():
     assert K.kvq_decode_workspace_bytes(g2, 64, 1024, 3) == 3 * per_split(2, 64)
 
 
+def test_oaken_workspace_holds_k_shares():
+    """Oaken decode keeps each token's K outer-value score share (binary32 per batch row, query
+    head and token up to max_len) in the workspace, after the split partials from a 256-byte
+    aligned offset; with max_len 0 no share is needed."""
+    per_split = lambda B, Hq: B * Hq * K.PART_STRIDE * 4
+    c = make_desc(B=16, H=40, S=2048, mode=K.KVQ_MODE_OAKEN, bits=4, group=64, cap=1004)
+    shares = lambda B, Hq, L: B * Hq * L * 4
+    assert K.kvq_decode_workspace_bytes(c, 40, 2048, 1) == shares(16, 40, 2048)
+    assert K.kvq_decode_workspace_bytes(c, 40, 777, 1) == shares(16, 40, 777)
+    assert K.kvq_decode_workspace_bytes(c, 40, 0, 1) == 0
+    for ns in (2, 3, 8):
+        n = K.kvq_decode_workspace_bytes(c, 40, 2048, ns)
+        parts = n - shares(16, 40, 2048)
+        assert parts > 0 and parts % 256 == 0
+        k = round(parts / per_split(16, 40))  # split count actually planned (pieces are whole steps)
+        assert 2 <= k <= ns and (k * per_split(16, 40) + 255) // 256 * 256 == parts
+    g = make_desc(B=1, H=2, S=2048, mode=K.KVQ_MODE_OAKEN, bits=4, group=64, cap=1004)
+    assert K.kvq_decode_workspace_bytes(g, 8, 2048, 1) == shares(1, 8, 2048)  # G = 4
+    # the no-alloc array holds a batch-256, 40-head, 2048-token cache's shares
+    assert shares(256, 40, 2048) <= K.STATIC_SCRATCH_BYTES
+
+
 def test_status_strings():
     for s in range(-6, 1):
         assert K.kvq_status_string(s) and K.kvq_status_string(s) != "unknown status"
