@@ -479,6 +479,44 @@ def test_oaken(G):
             check_attention(out, refs, "oaken G%d ns%d lens%s" % (G, ns, lens_d))
 
 
+@pytest.mark.parametrize("G", [1, 4, 16])
+def test_oaken_k_score_shares(G):
+    """The first Oaken decode kernel's output, read back from the workspace: each token's share
+    of the score from its K outer values, sum over the row's entries of q[idx] x_hat, against
+    the oracle's reconstruction of the outer values alone (the dense codes set to their
+    zero-points, so the dense part is 0) contracted with the query in binary64."""
+    B, H, T, S = 2, 3, 333, 384
+    print("case oaken K shares G=%d" % G, flush=True)
+    w = synth.scaled(synth.WORKLOADS[5], batch=B, kv_heads=H, q_heads=H * G, seq=T, tokens=T,
+                     index=synth.WORKLOADS[5].index + 3)
+    wc = synth.scaled(synth.WORKLOADS[5], kv_heads=4, seq=256)
+    thr_k, thr_v = oaken_thresholds(wc, 0, 20), oaken_thresholds(wc, 1, 20)
+    k, v, q = w.kv(0), w.kv(1), w.q()
+    cache = K.QuantKVCache(B, H, S, K.KVQ_MODE_OAKEN, k_bits=4, k_group=64, k_thr=thr_k, v_thr=thr_v,
+                           sparse_cap=S * 24)
+    K.kvq_quant_append(cache.desc, to_device(k), to_device(v), T, i32_device([0] * B))
+    lens = [T, 190]
+    Hq = H * G
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+    ws, n = cache.workspace(Hq, T, 1)
+    assert n == B * Hq * T * 4  # one split: the shares alone
+    K.kvq_decode_attn(cache.desc, to_device(q), Hq, i32_device(lens), T, SM, out, ws, n, 1)
+    torch.cuda.synchronize()
+    assert cache.flags() == 0
+    got = ws[:n].view(torch.float32).cpu().numpy().reshape(B, Hq, T).astype(np.float64)
+    oc, os_, oz, oo, oe, on = oracle.oaken_rows(k, thr_k, 64)
+    dense_zero = np.repeat(oz, 64, axis=-1)  # every code at its zero-point
+    outer = oracle.oaken_dequant_rows(dense_zero, os_, oz, oo, oe, on, thr_k, 64).astype(np.float64)
+    qf = q.view(np.float16).astype(np.float64)  # [B, Hq, 128]
+    for b in range(B):
+        for hq in range(Hq):
+            x = outer[b, hq // G, :lens[b]]                 # [L, 128]
+            want = x @ qf[b, hq]
+            bound = 1e-5 * (np.abs(x) @ np.abs(qf[b, hq])) + 1e-30
+            err = np.abs(got[b, hq, :lens[b]] - want)
+            assert np.all(err <= bound), (b, hq, float((err / bound).max()))
+
+
 def test_oaken_sparse_capacity_flag():
     B, H, T, S = 1, 1, 64, 64
     w = synth.scaled(synth.WORKLOADS[5], batch=B, kv_heads=H, q_heads=H, seq=T, tokens=T)
