@@ -452,16 +452,17 @@ def check_oaken_tensor(cache, name, x, thr, B, H, S, lens, group=64):
     return oracle.oaken_dequant_rows(oc, os_, oz, oo, oe, on, thr, group)
 
 
+@pytest.mark.parametrize("group", [64, 32])
 @pytest.mark.parametrize("G", [1, 4, 16])
-def test_oaken(G):
+def test_oaken(G, group):
     B, H, T, S = 2, 3, 333, 384
-    print("case oaken G=%d" % G, flush=True)
+    print("case oaken G=%d group=%d" % (G, group), flush=True)
     w = synth.scaled(synth.WORKLOADS[5], batch=B, kv_heads=H, q_heads=H * G, seq=T, tokens=T)
     wc = synth.scaled(synth.WORKLOADS[5], kv_heads=4, seq=256)
     thr_k, thr_v = oaken_thresholds(wc, 0, 20), oaken_thresholds(wc, 1, 20)
     k, v, q = w.kv(0), w.kv(1), w.q()
     cap = S * 24
-    cache = K.QuantKVCache(B, H, S, K.KVQ_MODE_OAKEN, k_bits=4, k_group=64, k_thr=thr_k, v_thr=thr_v,
+    cache = K.QuantKVCache(B, H, S, K.KVQ_MODE_OAKEN, k_bits=4, k_group=group, k_thr=thr_k, v_thr=thr_v,
                            sparse_cap=cap)
     # bulk 300 rows, then a 32-row append, then one more row
     K.kvq_quant_append(cache.desc, to_device(k[:, :, :300]), to_device(v[:, :, :300]), 300, i32_device([0] * B))
@@ -470,29 +471,30 @@ def test_oaken(G):
     torch.cuda.synchronize()
     assert cache.flags() == 0
     lens = [T, T]
-    kh = check_oaken_tensor(cache, "k", k, thr_k, B, H, S, lens)
-    vh = check_oaken_tensor(cache, "v", v, thr_v, B, H, S, lens)
+    kh = check_oaken_tensor(cache, "k", k, thr_k, B, H, S, lens, group)
+    vh = check_oaken_tensor(cache, "v", v, thr_v, B, H, S, lens, group)
     for lens_d in ([T, T], [T, 190]):
         refs = np.stack([oracle.attention(q[b], kh[b][:, :L], vh[b][:, :L], SM) for b, L in enumerate(lens_d)])
         for ns in (0, 1, 3):
             out = run_decode(cache, q, H * G, lens_d, T, ns)
-            check_attention(out, refs, "oaken G%d ns%d lens%s" % (G, ns, lens_d))
+            check_attention(out, refs, "oaken G%d g%d ns%d lens%s" % (G, group, ns, lens_d))
 
 
+@pytest.mark.parametrize("group", [64, 32])
 @pytest.mark.parametrize("G", [1, 4, 16])
-def test_oaken_k_score_shares(G):
+def test_oaken_k_score_shares(G, group):
     """The first Oaken decode kernel's output, read back from the workspace: each token's share
     of the score from its K outer values, sum over the row's entries of q[idx] x_hat, against
     the oracle's reconstruction of the outer values alone (the dense codes set to their
     zero-points, so the dense part is 0) contracted with the query in binary64."""
     B, H, T, S = 2, 3, 333, 384
-    print("case oaken K shares G=%d" % G, flush=True)
+    print("case oaken K shares G=%d group=%d" % (G, group), flush=True)
     w = synth.scaled(synth.WORKLOADS[5], batch=B, kv_heads=H, q_heads=H * G, seq=T, tokens=T,
                      index=synth.WORKLOADS[5].index + 3)
     wc = synth.scaled(synth.WORKLOADS[5], kv_heads=4, seq=256)
     thr_k, thr_v = oaken_thresholds(wc, 0, 20), oaken_thresholds(wc, 1, 20)
     k, v, q = w.kv(0), w.kv(1), w.q()
-    cache = K.QuantKVCache(B, H, S, K.KVQ_MODE_OAKEN, k_bits=4, k_group=64, k_thr=thr_k, v_thr=thr_v,
+    cache = K.QuantKVCache(B, H, S, K.KVQ_MODE_OAKEN, k_bits=4, k_group=group, k_thr=thr_k, v_thr=thr_v,
                            sparse_cap=S * 24)
     K.kvq_quant_append(cache.desc, to_device(k), to_device(v), T, i32_device([0] * B))
     lens = [T, 190]
@@ -504,9 +506,9 @@ def test_oaken_k_score_shares(G):
     torch.cuda.synchronize()
     assert cache.flags() == 0
     got = ws[:n].view(torch.float32).cpu().numpy().reshape(B, Hq, T).astype(np.float64)
-    oc, os_, oz, oo, oe, on = oracle.oaken_rows(k, thr_k, 64)
-    dense_zero = np.repeat(oz, 64, axis=-1)  # every code at its zero-point
-    outer = oracle.oaken_dequant_rows(dense_zero, os_, oz, oo, oe, on, thr_k, 64).astype(np.float64)
+    oc, os_, oz, oo, oe, on = oracle.oaken_rows(k, thr_k, group)
+    dense_zero = np.repeat(oz, group, axis=-1)  # every code at its zero-point
+    outer = oracle.oaken_dequant_rows(dense_zero, os_, oz, oo, oe, on, thr_k, group).astype(np.float64)
     qf = q.view(np.float16).astype(np.float64)  # [B, Hq, 128]
     for b in range(B):
         for hq in range(Hq):
