@@ -139,15 +139,18 @@ def test_uniform_append_positions():
 # ---------------------------------------------------------------------------
 # channel-axis K (per channel over 64-token blocks), token-axis V, GQA
 
-@pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("G", [1, 4, 16])
-def test_channel_k(bits, G):
+CHANNEL_CASES = [(4, 1, 64), (4, 4, 64), (4, 16, 64), (8, 1, 64), (8, 4, 64), (8, 16, 64),
+                 (4, 1, 32), (4, 4, 128), (8, 4, 32), (8, 1, 128)]
+
+
+@pytest.mark.parametrize("bits,G,vg", CHANNEL_CASES)
+def test_channel_k(bits, G, vg):
     B, H, T, S = 1, 2, 640, 704
-    print("case channel bits=%d G=%d" % (bits, G), flush=True)
+    print("case channel bits=%d G=%d v_group=%d" % (bits, G, vg), flush=True)
     w = synth.scaled(synth.WORKLOADS[3], batch=B, kv_heads=H, q_heads=H * G, seq=T, tokens=T)
     k, v, q = w.kv(0), w.kv(1), w.q()
     cache = K.QuantKVCache(B, H, S, K.KVQ_MODE_UNIFORM, k_bits=bits, k_axis=K.KVQ_AXIS_CHANNEL,
-                           k_group=64, v_group=64)
+                           k_group=64, v_group=vg)
     K.kvq_quant_append(cache.desc, to_device(k), to_device(v), T, i32_device([0]))
     torch.cuda.synchronize()
     assert cache.flags() == 0
@@ -158,16 +161,17 @@ def test_channel_k(bits, G):
     gs = dev_f32(cache.buf("k.scale"), (B, H, S // 64, 128))[:, :, :T // 64]
     gz = dev_u8(cache.buf("k.zero"), (B, H, S // 64, 128))[:, :, :T // 64]
     assert np.array_equal(f32bits(gs), f32bits(ks)) and np.array_equal(gz, kz)
-    vc, vs, vz = oracle.quant_rows(v, 64, bits)
+    vc, vs, vz = oracle.quant_rows(v, vg, bits)
     gotv = unpack_layout(dev_u8(cache.buf("v.codes"), (B, H, S, RB))[:, :, :T], bits, "V")
     assert np.array_equal(gotv, vc)
+    assert np.array_equal(f32bits(dev_f32(cache.buf("v.scale"), (B, H, S, 128 // vg))[:, :, :T]), f32bits(vs))
     kh = oracle.dequant_channel_blocks(kc, ks, kz, 64)
-    vh = oracle.dequant_rows(vc, vs, vz, 64)
+    vh = oracle.dequant_rows(vc, vs, vz, vg)
     for L in (640, 576):
         for ns in (0, 1, 5):
             out = run_decode(cache, q, H * G, [L], T, ns)
             refs = oracle.attention(q[0], kh[0][:, :L], vh[0][:, :L], SM)[None]
-            check_attention(out, refs, "channel b%d G%d L%d ns%d" % (bits, G, L, ns))
+            check_attention(out, refs, "channel b%d G%d vg%d L%d ns%d" % (bits, G, vg, L, ns))
 
 
 def k16_rows(raw_u16):
