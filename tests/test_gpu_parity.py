@@ -246,12 +246,12 @@ def mixed_reference(x, perm, seg, bits_of_chunk, group, CT):
     return out
 
 
-@pytest.mark.parametrize("G", [1, 4])
-@pytest.mark.parametrize("source", ["random", "cosine"])
-def test_chunk_mixed(G, source):
-    B, H, S, CT, group = 2, 3, 1024, 32, 32
+@pytest.mark.parametrize("G,source,group", [(1, "random", 32), (4, "random", 32), (1, "cosine", 32),
+                                             (4, "cosine", 32), (1, "random", 64), (4, "random", 128)])
+def test_chunk_mixed(G, source, group):
+    B, H, S, CT = 2, 3, 1024, 32
     C = S // CT
-    print("case mixed G=%d source=%s" % (G, source), flush=True)
+    print("case mixed G=%d source=%s group=%d" % (G, source, group), flush=True)
     w = synth.scaled(synth.WORKLOADS[4], batch=B, kv_heads=H, q_heads=H * G, seq=S, tokens=S, emb_dim=64)
     k, v, q = w.kv(0), w.kv(1), w.q()
     if source == "random":
@@ -275,11 +275,12 @@ def test_chunk_mixed(G, source):
                          .reshape(B, H, C, CT, 128),
                          LAYOUT[name])
         p4 = unpack_layout(dev_u8(cache.buf(name + ".codes"), (B, H, C, CT, 64)), 4, LAYOUT[name])
-        s4 = dev_f32(cache.buf(name + ".scale"), (B, H, C, CT, 4))
-        z4 = dev_u8(cache.buf(name + ".zero"), (B, H, C, CT, 4))
+        ng = 128 // group
+        s4 = dev_f32(cache.buf(name + ".scale"), (B, H, C, CT, ng))
+        z4 = dev_u8(cache.buf(name + ".zero"), (B, H, C, CT, ng))
         p2 = unpack_layout(dev_u8(cache.buf(name + ".codes2"), (B, H, C, CT, 32)), 2, LAYOUT[name])
-        s2 = dev_f32(cache.buf(name + ".scale2"), (B, H, C, CT, 4))
-        z2 = dev_u8(cache.buf(name + ".zero2"), (B, H, C, CT, 4))
+        s2 = dev_f32(cache.buf(name + ".scale2"), (B, H, C, CT, ng))
+        z2 = dev_u8(cache.buf(name + ".zero2"), (B, H, C, CT, ng))
         for b in range(B):
             n16, n4, n2, n = seg_o[b]
             for j in range(n):
