@@ -69,7 +69,7 @@ def oracle_rows(x, codec):
 
 @pytest.mark.parametrize("codec", CODECS)
 @pytest.mark.parametrize("P", [64, 256])
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 4, 16])
 def test_paged_matches_contiguous(codec, P, G):
     bits, sym, group, fmt = codec
     B, H, S, T = 3, 2, 512, 333
@@ -141,7 +141,7 @@ def test_paged_bad_page_is_flagged():
 
 
 @pytest.mark.parametrize("P", [64, 128])
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 4, 16])
 def test_paged_oaken(P, G):
     """Oaken with its dense body in pages and its sparse lists per sequence: the sparse lists equal
     the contiguous cache's byte for byte, every dense row gathered through the block table equals
@@ -199,7 +199,7 @@ def test_paged_oaken(P, G):
 
 
 @pytest.mark.parametrize("P", [64, 128])
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 4, 16])
 def test_paged_dsq(P, G):
     """DSQ with its groups in pages: streamed appends into a paged and a contiguous cache give the
     same groups (gathered through the block table) and tails byte for byte, decode equals the
@@ -265,7 +265,7 @@ def test_paged_dsq(P, G):
 
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("P", [64, 256])
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 4, 16])
 def test_paged_channel_k(bits, P, G):
     """K per channel over 64-token blocks with its codes and block scales in pages (a block never
     straddles a page), the fp16 tail per sequence: streamed appends into a paged and a contiguous
@@ -363,7 +363,7 @@ def gather_class_rows(cache, name, field, per, pool, H, P, table_cb, rows):
 
 
 @pytest.mark.parametrize("P,CT", [(64, 16), (64, 32), (128, 32)])
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 4, 16])
 def test_paged_chunk_mixed(P, CT, G):
     """Cocktail class pools in pages, one block table per class: the bulk path (reorder, then
     quantize) and streamed appends (the waiting chunk in the FP16 class's last page) into paged and

@@ -247,7 +247,8 @@ def mixed_reference(x, perm, seg, bits_of_chunk, group, CT):
 
 
 @pytest.mark.parametrize("G,source,group", [(1, "random", 32), (4, "random", 32), (1, "cosine", 32),
-                                             (4, "cosine", 32), (1, "random", 64), (4, "random", 128)])
+                                             (4, "cosine", 32), (1, "random", 64), (4, "random", 128),
+                                             (16, "random", 32)])
 def test_chunk_mixed(G, source, group):
     B, H, S, CT = 2, 3, 1024, 32
     C = S // CT
