@@ -78,7 +78,7 @@ def _compare_groups(dev, ref, b, h, q0, q1, n_sig):
         assert not d[:, n:].any(), name + " pad slots"
 
 
-CASES = [(13, 1), (13, 4), (13, 16), (1, 1), (16, 4), (7, 16)]
+CASES = [(13, 1), (13, 4), (13, 16), (1, 1), (16, 4), (7, 16), (13, 20), (5, 32)]
 
 
 @pytest.mark.parametrize("n_sig,G", CASES)

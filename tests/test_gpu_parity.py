@@ -71,8 +71,12 @@ UNIFORM_CASES = [(8, 1, 128), (8, 1, 64), (8, 0, 128), (8, 0, 32), (4, 0, 64), (
                  (2, 0, 32), (2, 0, 64), (2, 0, 128)]
 
 
-@pytest.mark.parametrize("bits,sym,group", UNIFORM_CASES)
-@pytest.mark.parametrize("G", [1, 4, 16])
+# more than 16 query heads per KV head: two query tiles per KV head, the
+# second partly filled (20 = 16 + 4) or full (32)
+MANY_HEADS = [(8, 1, 128, 20), (4, 0, 64, 20), (2, 0, 32, 32), (8, 0, 64, 32)]
+
+
+@pytest.mark.parametrize("bits,sym,group,G", [c + (G,) for c in UNIFORM_CASES for G in (1, 4, 16)] + MANY_HEADS)
 def test_uniform_token(bits, sym, group, G):
     B, H, T, S = 2, 3, 333, 384
     print("case uniform bits=%d sym=%d group=%d G=%d" % (bits, sym, group, G), flush=True)
@@ -140,7 +144,7 @@ def test_uniform_append_positions():
 # channel-axis K (per channel over 64-token blocks), token-axis V, GQA
 
 CHANNEL_CASES = [(4, 1, 64), (4, 4, 64), (4, 16, 64), (8, 1, 64), (8, 4, 64), (8, 16, 64),
-                 (4, 1, 32), (4, 4, 128), (8, 4, 32), (8, 1, 128)]
+                 (4, 1, 32), (4, 4, 128), (8, 4, 32), (8, 1, 128), (4, 20, 64), (8, 32, 64)]
 
 
 @pytest.mark.parametrize("bits,G,vg", CHANNEL_CASES)
@@ -248,7 +252,7 @@ def mixed_reference(x, perm, seg, bits_of_chunk, group, CT):
 
 @pytest.mark.parametrize("G,source,group", [(1, "random", 32), (4, "random", 32), (1, "cosine", 32),
                                              (4, "cosine", 32), (1, "random", 64), (4, "random", 128),
-                                             (16, "random", 32)])
+                                             (16, "random", 32), (20, "random", 32)])
 def test_chunk_mixed(G, source, group):
     B, H, S, CT = 2, 3, 1024, 32
     C = S // CT
@@ -458,8 +462,8 @@ def check_oaken_tensor(cache, name, x, thr, B, H, S, lens, group=64):
     return oracle.oaken_dequant_rows(oc, os_, oz, oo, oe, on, thr, group)
 
 
-@pytest.mark.parametrize("group", [64, 32])
-@pytest.mark.parametrize("G", [1, 4, 16])
+@pytest.mark.parametrize("G,group", [(1, 64), (1, 32), (4, 64), (4, 32), (16, 64), (16, 32), (20, 64),
+                                     (32, 32)])
 def test_oaken(G, group):
     B, H, T, S = 2, 3, 333, 384
     print("case oaken G=%d group=%d" % (G, group), flush=True)
@@ -486,8 +490,8 @@ def test_oaken(G, group):
             check_attention(out, refs, "oaken G%d g%d ns%d lens%s" % (G, group, ns, lens_d))
 
 
-@pytest.mark.parametrize("group", [64, 32])
-@pytest.mark.parametrize("G", [1, 4, 16])
+@pytest.mark.parametrize("G,group", [(1, 64), (1, 32), (4, 64), (4, 32), (16, 64), (16, 32), (20, 64),
+                                     (32, 32)])
 def test_oaken_k_score_shares(G, group):
     """The first Oaken decode kernel's output, read back from the workspace: each token's share
     of the score from its K outer values, sum over the row's entries of q[idx] x_hat, against
