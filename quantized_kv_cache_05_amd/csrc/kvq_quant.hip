@@ -721,11 +721,11 @@ __global__ __launch_bounds__(256) void k_chunk_wait(const uint16_t* __restrict__
 // is fl(T_lo - min x); a group without such values gives a non-positive
 // difference.  Hence max |delta| = max(fl(max x - T_hi), fl(T_lo - min x), 0)
 // over all of the group's values, exactly.
-template <int LG>
-__device__ __forceinline__ float oak_outer_scale(const float (&v)[8], float t_lo, float t_hi) {
+template <int LG, int N>
+__device__ __forceinline__ float oak_outer_scale(const float (&v)[N], float t_lo, float t_hi) {
   float mx = v[0], mn = v[0];
 #pragma unroll
-  for (int k = 1; k < 8; ++k) {
+  for (int k = 1; k < N; ++k) {
     mx = fmaxf(mx, v[k]);
     mn = fminf(mn, v[k]);
   }
@@ -734,54 +734,112 @@ __device__ __forceinline__ float oak_outer_scale(const float (&v)[8], float t_lo
   return fmaxf(fmaxf(mx - t_hi, t_lo - mn), 0.0f) / 31.0f;
 }
 
-// A lane's entries (channel | side << 7 | mag << 8 | tag << 13) for its
-// outer values, one iteration per set bit of `outer` in ascending channel
-// order (about 5 % of the values are outer, so a wave runs two or three
-// iterations, not eight), to entries e, e + 1, ... of a list of capacity cap
-// (< 2^31, so byte offsets fit 32 bits); `dropped` on overflow.  raw: the
-// lane's 8 fp16 values; tag: the row's token index mod 8, which decode reads
-// in place of a search of the row pointers.
+// One sparse entry (channel | side << 7 | mag << 8 | tag << 13) for the
+// outer value v of a group with outer scale so (r = recip_refined(so); s_out
+// = 0: magnitude 0).  tag: the row's token index mod 8, which decode reads in
+// place of a search of the row pointers.
+__device__ __forceinline__ uint16_t oak_entry_word(float v, float t_lo, float t_hi, float so, float r,
+                                                   unsigned ch, unsigned tag) {
+  const bool above = v > t_hi;
+  const float d = above ? v - t_hi : t_lo - v;
+  bool near = false;
+  float m = rne_quot<32>(d, r, near);
+  if (wave_any(near) && near) m = rintf(d / so);
+  const unsigned mag = (unsigned)__builtin_amdgcn_fmed3f(m, 0.0f, 31.0f);
+  return (uint16_t)(ch | (unsigned)above << 7 | mag << 8 | tag << 13);
+}
+__device__ __forceinline__ void store_entry(uint16_t* sp, unsigned e, unsigned cap, uint16_t w,
+                                            bool& dropped) {
+  if (e < cap)
+    *reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(sp) + (e << 1)) = w;
+  else
+    dropped = true;
+}
+
+// A lane's entries for its outer values (bit k of `outer`: value k of the
+// lane's 8 fp16 values in raw), one iteration per set bit in ascending
+// channel order, to entries e, e + 1, ... of a list of capacity cap (< 2^31,
+// so byte offsets fit 32 bits); `dropped` on overflow.
 __device__ __forceinline__ void oak_lane_entries(const uint4 raw, unsigned outer, float t_lo, float t_hi,
                                                  float so, int li, unsigned tag, uint16_t* sp, unsigned e,
                                                  unsigned cap, bool& dropped) {
-  const float r = recip_refined(so);  // s_out = 0: magnitudes 0
+  const float r = recip_refined(so);
   while (outer) {
     const int k = __builtin_ctz(outer);
     outer &= outer - 1u;
     const unsigned w = (k & 4) ? ((k & 2) ? raw.w : raw.z) : ((k & 2) ? raw.y : raw.x);
     const float v = h2f((uint16_t)(w >> (16 * (k & 1))));
-    const bool above = v > t_hi;
-    const float d = above ? v - t_hi : t_lo - v;
-    bool near = false;
-    float m = rne_quot<32>(d, r, near);
-    if (wave_any(near) && near) m = rintf(d / so);
-    const unsigned mag = (unsigned)__builtin_amdgcn_fmed3f(m, 0.0f, 31.0f);
-    if (e < cap)
-      *reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(sp) + (e << 1)) =
-          (uint16_t)((unsigned)(li * 8 + k) | (unsigned)above << 7 | mag << 8 | tag << 13);
-    else
-      dropped = true;
-    ++e;
+    store_entry(sp, e++, cap, oak_entry_word(v, t_lo, t_hi, so, r, (unsigned)(li * 8 + k), tag), dropped);
   }
+}
+
+// The dense INT4 body of one lane's 16 values of an Oaken row (outer values
+// enter as 0, so they neither widen the range nor divide), in groups of 16 LG
+// channels over LG lanes: s = (hi - lo) / 15, z = rne(-lo / s) and code
+// clamp(rne(x / s) + z, 0, 15), the asymmetric quantizer of the token rows,
+// returned as exact small floats.
+template <int LG>
+__device__ __forceinline__ void oak_dense16(const float (&xm)[16], float (&q)[16], float& s, int& z) {
+  constexpr float QMAX = 15.0f;
+  float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    lo = fminf(lo, xm[k]);
+    hi = fmaxf(hi, xm[k]);
+  }
+  lo = min_lanes<1, LG>(lo);
+  hi = max_lanes<1, LG>(hi);
+  s = (hi - lo) / QMAX;
+  const float r = recip_refined(s);  // s = 0: z = 0 and all codes 0
+  bool near = false;
+  float zf = rne_quot<16>(-lo, r, near);
+  float n[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) n[k] = rne_quot<16>(xm[k], r, near);
+  if (wave_any(near) && near) {
+    zf = rintf(-lo / s);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) n[k] = rintf(xm[k] / s);
+  }
+  zf = __builtin_amdgcn_fmed3f(zf, 0.0f, QMAX);
+  z = (int)zf;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) q[k] = __builtin_amdgcn_fmed3f(n[k] + zf, 0.0f, QMAX);
+}
+
+// Eight 4-bit codes (exact floats 0..15) as one word, code k in bits 4k..4k+3:
+// pairs joined exactly in float, each pair converted into its byte.
+__device__ __forceinline__ uint32_t pack_nibbles8(const float* q) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[2 * b + 1], 16.0f, q[2 * b]), b, w);
+  return w;
 }
 
 // Oaken (the Oaken page, §3.1 online stage, §3.2.1-3.2.2): per row, outer
 // values (x > T_hi_outer or x < T_lo_outer) leave the dense INT4 body (coded
 // z) and go to the row's sparse list as shifted deltas with a per-group
 // 5-bit scale.  One workgroup per (b, h) walks the new rows in tiles of 64
-// (four rows per 16-lane row group), the next tile's rows loaded while the
-// current one is coded.  The rows' outer counts meet in LDS once per tile;
-// every wave scans all 64 of them itself, so the running entry offset (and
-// with it rowptr, a prefix sum of the counts) needs one barrier per tile.
+// (eight lanes per row, 16 channels per lane, 32 rows at a time), the next
+// tile's rows loaded while the current one is coded.  The rows' outer counts
+// meet in LDS once per tile; every wave scans all 64 of them itself, so the
+// running entry offset (and with it rowptr, a prefix sum of the counts)
+// needs one barrier per tile.
 template <int GE, bool VL>
 __global__ __launch_bounds__(256) void k_quant_oaken(
     const uint16_t* __restrict__ x, int t_new, int H, int S, const int* __restrict__ pos,
     float t_lo, float t_hi, long long cap, uint8_t* __restrict__ codes, float* __restrict__ scale,
     uint8_t* __restrict__ zero, float* __restrict__ oscale, uint32_t* __restrict__ rowptr,
     uint16_t* __restrict__ sparse, unsigned* __restrict__ status, PageMap pm) {
-  constexpr int NG = kD / GE, LG = GE / 8, U = 4, TR = 16 * U;
-  __shared__ uint16_t lrows[VL ? 16 : 1][128];
+  constexpr int NG = kD / GE, LG = GE / 16, U = 2, TR = 32 * U;
+  static_assert(GE >= 16, "a group spans whole lanes");
+  // V layout: code k of lane li goes to byte 8 k + li of its row's slot, so
+  // that word n (channels n + 16 j) is bytes 8 n .. 8 n + 7
+  __shared__ __align__(16) uint8_t lcode[VL ? 32 : 1][128];
   __shared__ unsigned row_cnt[2][TR];  // alternate tiles: one barrier per tile
+  // the tile's rows as each thread loaded them, word-major (conflict-free):
+  // pass 2 reads its outer values back from here
+  __shared__ uint32_t lraw[8 * U][256];
   const long long bh = blockIdx.x;
   const int b = (int)(bh / H);
   const int p = pos[b];
@@ -795,54 +853,99 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
   // running entry count: at most cap + 128 t_new < 2^32
   unsigned base = p == 0 ? 0u : rp[p];
   if (p == 0 && threadIdx.x == 0) rp[0] = 0u;
-  const int rl = threadIdx.x >> 4, li = threadIdx.x & 15, lane = threadIdx.x & 63;
-  uint16_t* lrow = lrows[VL ? rl : 0];
+  const int rl = threadIdx.x >> 3, li = threadIdx.x & 7, lane = threadIdx.x & 63;
+  uint8_t* lc = lcode[VL ? rl : 0];
   // rows past the last one load the last row (always readable); such rows
   // are neither counted nor stored
-  const uint16_t* xr = x + bh * t_new * kD + li * 8;
-  uint4 nxt[U];
+  const uint16_t* xr = x + bh * t_new * kD + li * 16;
+  uint4 nxt[U][2];
 #pragma unroll
-  for (int u = 0; u < U; ++u) nxt[u] = ld_row8(xr + (long long)min(16 * u + rl, t_new - 1) * kD);
+  for (int u = 0; u < U; ++u) {
+    const uint16_t* r = xr + (long long)min(32 * u + rl, t_new - 1) * kD;
+    nxt[u][0] = ld_row8(r);
+    nxt[u][1] = ld_row8(r + 8);
+  }
   bool dropped = false;
   for (int t0 = 0, it = 0; t0 < t_new; t0 += TR, it ^= 1) {
-    uint4 raw[U];
+    uint4 raw[U][2];
 #pragma unroll
-    for (int u = 0; u < U; ++u) raw[u] = nxt[u];
+    for (int u = 0; u < U; ++u) {
+      raw[u][0] = nxt[u][0];
+      raw[u][1] = nxt[u][1];
+    }
     if (t0 + TR < t_new) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) nxt[u] = ld_row8(xr + (long long)min(t0 + TR + 16 * u + rl, t_new - 1) * kD);
+      for (int u = 0; u < U; ++u) {
+        const uint16_t* r = xr + (long long)min(t0 + TR + 32 * u + rl, t_new - 1) * kD;
+        nxt[u][0] = ld_row8(r);
+        nxt[u][1] = ld_row8(r + 8);
+      }
     }
     // pass 1: per row, the dense INT4 body, the scales and the outer mask;
-    // the row's outer count (a lane's first entry within its row in bits 8
+    // the row's outer count (a lane's first entry within its row in bits 16
     // and up of meta)
     unsigned meta[U];
     float sos[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = t0 + 16 * u + rl;
+      const int t = t0 + 32 * u + rl;
       const bool active = t < t_new;
-      float v[8];
-      unpack8(raw[u], v);
-      unsigned outer = 0;
-      if (active) {
+      float v[16], xm[16];
+      {
+        float h[8];
+        unpack8(raw[u][0], h);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) outer |= (unsigned)((v[k] > t_hi) || (v[k] < t_lo)) << k;
+        for (int k = 0; k < 8; ++k) v[k] = h[k];
+        unpack8(raw[u][1], h);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[8 + k] = h[k];
       }
-      uint32_t plo, phi;
-      float s;
-      int z;
-      quant8<4, false, GE>(v, ~outer & 0xFFu, plo, phi, s, z);
-      const float so = oak_outer_scale<LG>(v, t_lo, t_hi);
-      const int lc = __popc(outer);
-      int incl = lc;
+      unsigned outer = 0;
 #pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        const int o = __shfl_up(incl, m, 16);
+      for (int k = 0; k < 16; ++k) {
+        const bool o = ((v[k] > t_hi) | (v[k] < t_lo)) & active;
+        outer |= (unsigned)o << k;
+        xm[k] = o ? 0.0f : v[k];
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        lraw[8 * u + c][threadIdx.x] = (&raw[u][0].x)[c];
+        lraw[8 * u + 4 + c][threadIdx.x] = (&raw[u][1].x)[c];
+      }
+      float q[16], s;
+      int z;
+      oak_dense16<LG>(xm, q, s, z);
+      const float so = oak_outer_scale<LG>(v, t_lo, t_hi);
+      const int lcnt = __popc(outer);
+      int incl = lcnt;
+#pragma unroll
+      for (int m = 1; m < 8; m <<= 1) {
+        const int o = __shfl_up(incl, m, 8);
         if (li >= m) incl += o;
       }
-      if (li == 15) row_cnt[it][16 * u + rl] = (unsigned)incl;  // 0 for an inactive row
-      meta[u] = outer | (unsigned)(incl - lc) << 8;
+      if (li == 7) row_cnt[it][32 * u + rl] = (unsigned)incl;  // 0 for an inactive row
+      meta[u] = outer | (unsigned)(incl - lcnt) << 16;
       sos[u] = so;
+      // codes: K layout, slots of channels 16 li .. +7 and 16 li + 8 .. +15;
+      // V layout, words 2 li and 2 li + 1 through the row's LDS slot
+      uint32_t w0, w1;
+      if constexpr (!VL) {
+        w0 = pack_nibbles8(q);
+        w1 = pack_nibbles8(q + 8);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) lc[8 * k + li] = (uint8_t)(unsigned)q[k];
+        wave_lds_sync();
+        const uint4 by = *reinterpret_cast<const uint4*>(lc + 16 * li);
+        wave_lds_sync();
+        // bytes b0..b3 (each < 16) of a word -> nibbles b0 | b1 << 4 | b2 << 8 | b3 << 12
+        auto nib4 = [](uint32_t d) {
+          const uint32_t t = d | (d >> 4);
+          return (t & 0xFFu) | ((t >> 8) & 0xFF00u);
+        };
+        w0 = nib4(by.x) | nib4(by.y) << 16;
+        w1 = nib4(by.z) | nib4(by.w) << 16;
+      }
       if (active) {
         // the dense row: contiguous, or in its page (a table entry outside
         // the pool skips the row and flags; the sparse list is per sequence)
@@ -856,7 +959,13 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
           dst = ((long long)pg * H + bh % H) * pm.ptok + tok % pm.ptok;
         }
         if (dense_ok) {
-          store_row_codes<4, VL>(codes + dst * 64, li, plo, phi, lrow);
+          uint8_t* row = codes + dst * 64;
+          if constexpr (!VL) {
+            st_nt<uint32_t>(row + 4 * k_slot(2 * li), w0);
+            st_nt<uint32_t>(row + 4 * k_slot(2 * li + 1), w1);
+          } else {
+            st_nt<u2q_t>(row + 8 * li, u2q_t{w0, w1});
+          }
           if (li % LG == 0) {
             scale[dst * NG + li / LG] = s;
             zero[dst * NG + li / LG] = (uint8_t)z;
@@ -876,16 +985,37 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
     }
     const unsigned excl_row = scan - cnt;
     const unsigned tile_tot = __shfl(scan, 63, 64);
-    // pass 2: the entries (only where there are outer values) and rowptr
+    // pass 2: rowptr, then the entries.  A lane's outer bits of the tile's
+    // two rows form one mask (bit 16 u + k: value k of row u), walked in one
+    // loop with the values read back from LDS, so a wave runs as many
+    // iterations as its busiest lane has outer values in the whole tile
+    // (about four at a 5 % outer rate), not that many per row.  Bits come in
+    // ascending (row, channel) order: the lane's c-th entry of the tile is
+    // its (c - before_u)-th of row u.
+    unsigned mask = 0, before = 0, off[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = t0 + 16 * u + rl;
-      const unsigned rb = base + __shfl(excl_row, 16 * u + rl, 64);
-      const unsigned rcnt = __shfl(cnt, 16 * u + rl, 64);
-      if (t >= t_new) continue;
-      oak_lane_entries(raw[u], meta[u] & 0xFFu, t_lo, t_hi, sos[u], li, (unsigned)(p + t) & 7u, sp,
-                       rb + (meta[u] >> 8), capu, dropped);
-      if (li == 0) rp[(unsigned)(p + t + 1)] = min(rb + rcnt, capu);
+      const int t = t0 + 32 * u + rl;
+      const unsigned rb = base + __shfl(excl_row, 32 * u + rl, 64);
+      const unsigned rcnt = __shfl(cnt, 32 * u + rl, 64);
+      const unsigned outer = meta[u] & 0xFFFFu;  // 0 for a row past the last
+      off[u] = rb + (meta[u] >> 16) - before;    // mod 2^32
+      before += __popc(outer);
+      mask |= outer << (16 * u);
+      if (t < t_new && li == 0) rp[(unsigned)(p + t + 1)] = min(rb + rcnt, capu);
+    }
+    const unsigned tag = (unsigned)(p + t0 + rl) & 7u;  // (p + t0 + 32 u + rl) mod 8
+    const float so0 = sos[0], so1 = sos[1];
+    const unsigned of0 = off[0], of1 = off[1];
+    for (unsigned c = 0; mask; ++c) {
+      const int j = __builtin_ctz(mask);
+      mask &= mask - 1u;
+      const bool r1 = (j & 16) != 0;
+      const float so = r1 ? so1 : so0;
+      const float v = h2f(reinterpret_cast<const uint16_t*>(&lraw[j >> 1][threadIdx.x])[j & 1]);
+      store_entry(sp, (r1 ? of1 : of0) + c, capu,
+                  oak_entry_word(v, t_lo, t_hi, so, recip_refined(so), (unsigned)(li * 16 + (j & 15)), tag),
+                  dropped);
     }
     base += tile_tot;
   }
