@@ -87,6 +87,22 @@ __device__ __forceinline__ float rne_quot(float x, float r, bool& near) {
 }
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0ull; }
 
+// The IEEE quotient fl(x / D) for x >= 0 and a constant D without a division:
+// q0 = fl(x c) with c = fl(1/D), the residual x - q0 D exact by a fused
+// multiply-add, then q0 + r c rounded once (Markstein's correction step with
+// a correctly rounded reciprocal).  Checked on the CPU over every binade
+// where a step can leave the normal range and one where none does (the rest
+// are scaled copies), for the divisors used below.  x infinite or NaN is
+// passed through, as the division would give.
+template <int D>
+__device__ __forceinline__ float div_const(float x) {
+#pragma clang fp contract(off)
+  constexpr float c = 1.0f / (float)D;
+  const float q0 = x * c;
+  const float q = fmaf(fmaf(-q0, (float)D, x), c, q0);
+  return __builtin_isfinite(x) ? q : q0;
+}
+
 // F8: 0 integer codes, 1 FP8 E4M3, 2 FP8 E5M2
 template <int BITS, bool SYM, int GE, int F8 = 0>
 __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint32_t& plo,
@@ -731,7 +747,7 @@ __device__ __forceinline__ float oak_outer_scale(const float (&v)[N], float t_lo
   }
   mx = max_lanes<1, LG>(mx);
   mn = min_lanes<1, LG>(mn);
-  return fmaxf(fmaxf(mx - t_hi, t_lo - mn), 0.0f) / 31.0f;
+  return div_const<31>(fmaxf(fmaxf(mx - t_hi, t_lo - mn), 0.0f));
 }
 
 // One sparse entry (channel | side << 7 | mag << 8 | tag << 13) for the
@@ -789,13 +805,22 @@ __device__ __forceinline__ void oak_dense16(const float (&xm)[16], float (&q)[16
   }
   lo = min_lanes<1, LG>(lo);
   hi = max_lanes<1, LG>(hi);
-  s = (hi - lo) / QMAX;
+  s = div_const<15>(hi - lo);
   const float r = recip_refined(s);  // s = 0: z = 0 and all codes 0
   bool near = false;
   float zf = rne_quot<16>(-lo, r, near);
-  float n[16];
+  // rne_quot's test on the largest |y - rne(y)| of the lane's values: a lane
+  // with any near value divides all of them (a NaN y gives NaN either way)
+  constexpr float kAccept = 0.5f - 16.0f * 0x1p-19f;
+  float n[16], dev = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) n[k] = rne_quot<16>(xm[k], r, near);
+  for (int k = 0; k < 16; ++k) {
+#pragma clang fp contract(off)
+    const float y = xm[k] * r;
+    n[k] = rintf(y);
+    dev = fmaxf(dev, fabsf(y - n[k]));
+  }
+  near |= !(dev < kAccept);
   if (wave_any(near) && near) {
     zf = rintf(-lo / s);
 #pragma unroll
@@ -1006,15 +1031,16 @@ __global__ __launch_bounds__(256) void k_quant_oaken(
     }
     const unsigned tag = (unsigned)(p + t0 + rl) & 7u;  // (p + t0 + 32 u + rl) mod 8
     const float so0 = sos[0], so1 = sos[1];
+    const float rc0 = recip_refined(so0), rc1 = recip_refined(so1);
     const unsigned of0 = off[0], of1 = off[1];
     for (unsigned c = 0; mask; ++c) {
       const int j = __builtin_ctz(mask);
       mask &= mask - 1u;
       const bool r1 = (j & 16) != 0;
-      const float so = r1 ? so1 : so0;
       const float v = h2f(reinterpret_cast<const uint16_t*>(&lraw[j >> 1][threadIdx.x])[j & 1]);
       store_entry(sp, (r1 ? of1 : of0) + c, capu,
-                  oak_entry_word(v, t_lo, t_hi, so, recip_refined(so), (unsigned)(li * 16 + (j & 15)), tag),
+                  oak_entry_word(v, t_lo, t_hi, r1 ? so1 : so0, r1 ? rc1 : rc0, (unsigned)(li * 16 + (j & 15)),
+                                 tag),
                   dropped);
     }
     base += tile_tot;
