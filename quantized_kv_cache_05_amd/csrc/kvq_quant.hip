@@ -103,6 +103,24 @@ __device__ __forceinline__ float div_const(float x) {
   return __builtin_isfinite(x) ? q : q0;
 }
 
+// rne_quot over a lane's N values with one test: the largest |y - rne(y)|
+// against the same bound, so a lane with any near value divides all of them
+// (each division gives the code the fast path would where that one is not
+// near; a NaN y gives NaN either way).
+template <int M, int N>
+__device__ __forceinline__ bool rne_quot_lane(const float (&x)[N], float r, float (&n)[N]) {
+  constexpr float kAccept = 0.5f - (float)M * 0x1p-19f;
+  float dev = 0.0f;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+#pragma clang fp contract(off)
+    const float y = x[k] * r;
+    n[k] = rintf(y);
+    dev = fmaxf(dev, fabsf(y - n[k]));
+  }
+  return !(dev < kAccept);
+}
+
 // F8: 0 integer codes, 1 FP8 E4M3, 2 FP8 E5M2
 template <int BITS, bool SYM, int GE, int F8 = 0>
 __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint32_t& plo,
@@ -116,7 +134,7 @@ __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint
 #pragma unroll
     for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
     amax = max_lanes<1, LG>(amax);
-    s = amax / (F8 == 1 ? 448.0f : 57344.0f);
+    s = amax / (F8 == 1 ? 448.0f : 57344.0f);  // (the corrected step misrounds some of these quotients)
     z = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -130,13 +148,11 @@ __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint
 #pragma unroll
     for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
     amax = max_lanes<1, LG>(amax);
-    s = amax / 127.0f;
+    s = div_const<127>(amax);
     z = 0;
     const float r = recip_refined(s);  // s = 0: all codes 0
-    bool near = false;
     float n[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) n[k] = rne_quot<128>(x[k], r, near);
+    const bool near = rne_quot_lane<128>(x, r, n);
     if (wave_any(near) && near) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) n[k] = rintf(x[k] / s);
@@ -159,13 +175,11 @@ __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint
     }
     lo = min_lanes<1, LG>(lo);
     hi = max_lanes<1, LG>(hi);
-    s = (hi - lo) / QMAX;
+    s = div_const<(1 << BITS) - 1>(hi - lo);
     const float r = recip_refined(s);  // s = 0: z = 0 and all codes 0
-    bool near = false;
-    float zf = rne_quot<(1 << BITS)>(-lo, r, near);
     float n[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) n[k] = rne_quot<(1 << BITS)>(xm[k], r, near);
+    bool near = rne_quot_lane<(1 << BITS)>(xm, r, n);
+    float zf = rne_quot<(1 << BITS)>(-lo, r, near);
     if (wave_any(near) && near) {
       zf = rintf(-lo / s);
 #pragma unroll
@@ -807,20 +821,9 @@ __device__ __forceinline__ void oak_dense16(const float (&xm)[16], float (&q)[16
   hi = max_lanes<1, LG>(hi);
   s = div_const<15>(hi - lo);
   const float r = recip_refined(s);  // s = 0: z = 0 and all codes 0
-  bool near = false;
+  float n[16];
+  bool near = rne_quot_lane<16>(xm, r, n);
   float zf = rne_quot<16>(-lo, r, near);
-  // rne_quot's test on the largest |y - rne(y)| of the lane's values: a lane
-  // with any near value divides all of them (a NaN y gives NaN either way)
-  constexpr float kAccept = 0.5f - 16.0f * 0x1p-19f;
-  float n[16], dev = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-#pragma clang fp contract(off)
-    const float y = xm[k] * r;
-    n[k] = rintf(y);
-    dev = fmaxf(dev, fabsf(y - n[k]));
-  }
-  near |= !(dev < kAccept);
   if (wave_any(near) && near) {
     zf = rintf(-lo / s);
 #pragma unroll
