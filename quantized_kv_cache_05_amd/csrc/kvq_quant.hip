@@ -383,7 +383,10 @@ __global__ __launch_bounds__(256) void k_quant_token_kv(const uint16_t* __restri
 // k_quant_channel: one workgroup per (block touched by the append, b h);
 // block k0 = 64 floor(p / 64) + 64 blockIdx.x is quantized when it is
 // complete after the append, its rows below p read from the tail, the others
-// from the input.  Codes in the K row layout.  k_channel_tail (launched after
+// from the input.  The block's rows are staged in LDS as fp16; each
+// channel's range is reduced over four 16-row quarters, then each thread
+// codes 8 channels of 4 rows (their scales read once).  Codes in the K row
+// layout.  k_channel_tail (launched after
 // it on the same stream, so the tail is read before it is overwritten) then
 // moves the new tokens of the block left incomplete into the tail.
 
@@ -429,76 +432,87 @@ __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restric
     }
     row0 = ((long long)pg * H + bh % H) * pm.ptok + k0 % pm.ptok;
   }
-  __shared__ float tile[64][kD + 1];
-  __shared__ float lo_sh[2][kD], hi_sh[2][kD], s_sh[kD], r_sh[kD];
-  __shared__ int z_sh[kD];
+  // the block's 64 fp16 rows (16-byte aligned rows: 16-byte writes and reads)
+  __shared__ __align__(16) uint16_t tile[64][kD + 8];
+  __shared__ float lo_sh[4][kD], hi_sh[4][kD];
+  __shared__ __align__(16) float s_sh[kD], r_sh[kD], z_sh[kD];
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int r = pass * 16 + (threadIdx.x >> 4), li = threadIdx.x & 15;
     const int t = k0 + r;
     const uint4 raw = t < p ? ld_row8_k16(tail + (bh * 64 + r) * 256, li)
                             : ld_row8(x + (bh * t_new + (t - p)) * kD + li * 8);
-    float v[8];
-    unpack8(raw, v);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) tile[r][li * 8 + k] = v[k];
+    *reinterpret_cast<uint4*>(&tile[r][li * 8]) = raw;
   }
   __syncthreads();
   {
-    const int c = threadIdx.x & 127, half = threadIdx.x >> 7;
-    float lo = 0.0f, hi = 0.0f;
-    for (int r = half * 32; r < half * 32 + 32; ++r) {
-      const float v = tile[r][c];
-      lo = fminf(lo, v);
-      hi = fmaxf(hi, v);
+    // channels 2 cp and 2 cp + 1 over rows 16 qr .. 16 qr + 15
+    const int cp = threadIdx.x & 63, qr = threadIdx.x >> 6;
+    float lo0 = 0.0f, hi0 = 0.0f, lo1 = 0.0f, hi1 = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile[16 * qr + r][2 * cp]);
+      const float v0 = lo_h2f(w), v1 = hi_h2f(w);
+      lo0 = fminf(lo0, v0);
+      hi0 = fmaxf(hi0, v0);
+      lo1 = fminf(lo1, v1);
+      hi1 = fmaxf(hi1, v1);
     }
-    lo_sh[half][c] = lo;
-    hi_sh[half][c] = hi;
+    lo_sh[qr][2 * cp] = lo0;
+    hi_sh[qr][2 * cp] = hi0;
+    lo_sh[qr][2 * cp + 1] = lo1;
+    hi_sh[qr][2 * cp + 1] = hi1;
   }
   __syncthreads();
   if (threadIdx.x < kD) {
     const int c = threadIdx.x;
-    const float lo = fminf(lo_sh[0][c], lo_sh[1][c]);
-    const float hi = fmaxf(hi_sh[0][c], hi_sh[1][c]);
-    const float s = (hi - lo) / (float)QMAX;
+    const float lo = fminf(fminf(lo_sh[0][c], lo_sh[1][c]), fminf(lo_sh[2][c], lo_sh[3][c]));
+    const float hi = fmaxf(fmaxf(hi_sh[0][c], hi_sh[1][c]), fmaxf(hi_sh[2][c], hi_sh[3][c]));
+    const float s = div_const<QMAX>(hi - lo);
     int z = 0;
     if (s != 0.0f) z = min(max((int)rintf(-lo / s), 0), QMAX);
     s_sh[c] = s;
     r_sh[c] = recip_refined(s);
-    z_sh[c] = z;
+    z_sh[c] = (float)z;
     const long long m = (row0 / 64) * kD + c;
     scale[m] = s;
     zero[m] = (uint8_t)z;
   }
   __syncthreads();
-  // thread (row r, 32-channel block pc): slices q = 0..3 of k-step pc
-  const int r = threadIdx.x >> 2, pc = threadIdx.x & 3;
-  uint8_t* dst = codes + (row0 + r) * RB;
+  // thread (rows 4 rg .. 4 rg + 3, channels 8 cg .. 8 cg + 7): the channels'
+  // scales read once for four rows; the 8 codes of a row form slot k_slot(cg)
+  const int rg = threadIdx.x >> 4, cg = threadIdx.x & 15;
+  float sv[8], rv[8], zv[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int h = 0; h < 2; ++h) {
+    const float4 a = *reinterpret_cast<const float4*>(&s_sh[8 * cg + 4 * h]);
+    const float4 b2 = *reinterpret_cast<const float4*>(&r_sh[8 * cg + 4 * h]);
+    const float4 c2 = *reinterpret_cast<const float4*>(&z_sh[8 * cg + 4 * h]);
+    sv[4 * h] = a.x; sv[4 * h + 1] = a.y; sv[4 * h + 2] = a.z; sv[4 * h + 3] = a.w;
+    rv[4 * h] = b2.x; rv[4 * h + 1] = b2.y; rv[4 * h + 2] = b2.z; rv[4 * h + 3] = b2.w;
+    zv[4 * h] = c2.x; zv[4 * h + 1] = c2.y; zv[4 * h + 2] = c2.z; zv[4 * h + 3] = c2.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * rg + i;
+    float v[8];
+    unpack8(*reinterpret_cast<const uint4*>(&tile[r][8 * cg]), v);
     // rne(x / s) without a divide per value (rne_quot; s = 0: r = 0, z = 0, code 0)
     float n[8];
     bool near = false;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int ch = pc * 32 + q * 8 + v;
-      n[v] = rne_quot<(1 << BITS)>(tile[r][ch], r_sh[ch], near);
-    }
+    for (int k = 0; k < 8; ++k) n[k] = rne_quot<(1 << BITS)>(v[k], rv[k], near);
     if (wave_any(near) && near) {
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const int ch = pc * 32 + q * 8 + v;
-        n[v] = rintf(tile[r][ch] / s_sh[ch]);
-      }
+      for (int k = 0; k < 8; ++k) n[k] = rintf(v[k] / sv[k]);
     }
     uint64_t w = 0;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int ch = pc * 32 + q * 8 + v;
-      const int c = (int)__builtin_amdgcn_fmed3f(n[v] + (float)z_sh[ch], 0.0f, (float)QMAX);
-      w |= (uint64_t)c << (BITS * v);
+    for (int k = 0; k < 8; ++k) {
+      const int c = (int)__builtin_amdgcn_fmed3f(n[k] + zv[k], 0.0f, (float)QMAX);
+      w |= (uint64_t)c << (BITS * k);
     }
-    store_codes8<BITS>(dst, 4 * q + pc, (uint32_t)w, (uint32_t)(w >> 32));
+    store_codes8<BITS>(codes + (row0 + r) * RB, k_slot(cg), (uint32_t)w, (uint32_t)(w >> 32));
   }
 }
 
