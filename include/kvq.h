@@ -282,6 +282,7 @@ kvq_status kvq_cache_bytes(const kvq_cache* c, kvq_cache_bytes_t* out);
  *  k_new, v_new: device fp16 [batch][kv_heads][t_new][128].
  *  pos:          device int32 [batch]; token t of sequence b goes to cache
  *                position pos[b] + t.
+ *  batch * kv_heads * t_new must be below 2^31 (UNSUPPORTED otherwise).
  *  UNIFORM/TOKEN: any pos, t_new >= 1.
  *  UNIFORM/CHANNEL: any t_new >= 1, appended as a stream: pos[b] must be
  *                the sequence's current length.  K blocks of 64 tokens that

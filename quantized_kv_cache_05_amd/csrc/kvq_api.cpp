@@ -446,6 +446,7 @@ kvq_status kvq_quant_append(const kvq_cache* c, const void* k_new, const void* v
   if (t_new < 0) return KVQ_ERR_INVALID_ARG;
   if (t_new > c->max_seq) return KVQ_ERR_CAPACITY;
   if (t_new == 0) return KVQ_OK;
+  if ((long long)c->batch * c->kv_heads * t_new >= (1ll << 31)) return KVQ_ERR_UNSUPPORTED;  // 32-bit row index
   if (!k_new || !v_new || !pos) return KVQ_ERR_INVALID_ARG;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos, 4)) return KVQ_ERR_ALIGNMENT;
   s = check_buffers(c);

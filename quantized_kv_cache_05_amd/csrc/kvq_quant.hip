@@ -297,18 +297,43 @@ struct PageMap {
   int ptok, npages;
 };
 
+// Unsigned division by a divisor fixed for a launch, n < 2^32, as one high
+// multiply, an add and shifts (the round-up multiplier construction of
+// Granlund and Montgomery): s = ceil(log2 d), m = floor(2^32 (2^s - d) / d)
+// + 1, q = (t + ((n - t) >> 1)) >> (s - 1) with t = mulhi(n, m); d = 1: q = n.
+// It replaces the 64-bit divides of the row index, which the compiler
+// expands into some 80 instructions per lane.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, s};
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  if (f.s == 0) return n;
+  const uint32_t t = __umulhi(n, f.m);
+  return (t + ((n - t) >> 1)) >> (f.s - 1);
+}
+
+// rows = batch * H * t_new < 2^31 (checked by the caller), so the grid-strided
+// row index never wraps
 template <int BITS, bool SYM, int GE, bool VL, int F8 = 0>
-__device__ __forceinline__ void quant_token_row(long long row, const uint16_t* __restrict__ x, int t_new,
-                                                int H, int S, const int* __restrict__ pos, long long rows,
+__device__ __forceinline__ void quant_token_row(uint32_t row, const uint16_t* __restrict__ x, FastDiv ft,
+                                                FastDiv fh, int S, const int* __restrict__ pos, uint32_t rows,
                                                 uint8_t* __restrict__ codes, float* __restrict__ scale,
                                                 uint8_t* __restrict__ zero, unsigned* __restrict__ status,
                                                 uint16_t* lrow, const PageMap& pm) {
   constexpr int NG = kD / GE, LG = GE / 8, RB = kD * BITS / 8;
   const int li = threadIdx.x & 15;
   if (row >= rows) return;  // all 16 lanes of a row leave together
-  const int t = (int)(row % t_new);
-  const long long bh = row / t_new;
-  const int b = (int)(bh / H);
+  const uint32_t bh32 = fdiv(row, ft);
+  const int t = (int)(row - bh32 * ft.d);
+  const long long bh = bh32;
+  const uint32_t b32 = fdiv(bh32, fh);
+  const int b = (int)b32, H = (int)fh.d;
   const int p = pos[b];
   if (p < 0 || p + t >= S) {
     if (li == 0) set_flag(status, kFlagPosRange);
@@ -322,10 +347,10 @@ __device__ __forceinline__ void quant_token_row(long long row, const uint16_t* _
       if (li == 0) set_flag(status, kFlagPageRange);
       return;
     }
-    dst = ((long long)pg * H + bh % H) * pm.ptok + tok % pm.ptok;
+    dst = ((long long)pg * H + (bh32 - b32 * fh.d)) * pm.ptok + tok % pm.ptok;
   }
   float v[8];
-  unpack8(ld_row8(x + row * kD + li * 8), v);
+  unpack8(ld_row8(x + (long long)row * kD + li * 8), v);
   uint32_t plo, phi;
   float s;
   int z;
@@ -338,36 +363,36 @@ __device__ __forceinline__ void quant_token_row(long long row, const uint16_t* _
 }
 
 template <int BITS, bool SYM, int GE, bool VL, int F8>
-__global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict__ x, int t_new, int H,
+__global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict__ x, FastDiv ft, FastDiv fh,
                                                      int S, const int* __restrict__ pos,
-                                                     long long rows, uint8_t* __restrict__ codes,
+                                                     uint32_t rows, uint8_t* __restrict__ codes,
                                                      float* __restrict__ scale,
                                                      uint8_t* __restrict__ zero,
                                                      unsigned* __restrict__ status, PageMap pm) {
   __shared__ uint16_t lrows[VL ? 16 : 1][128];
   // blocks of 16 rows, grid-strided: a bounded grid keeps the dispatch cost low
-  for (long long r0 = (long long)blockIdx.x * 16; r0 < rows; r0 += (long long)gridDim.x * 16)
-    quant_token_row<BITS, SYM, GE, VL, F8>(r0 + (threadIdx.x >> 4), x, t_new, H, S, pos, rows, codes,
-                                           scale, zero, status, lrows[VL ? (threadIdx.x >> 4) : 0], pm);
+  for (uint32_t r0 = blockIdx.x * 16u; r0 < rows; r0 += gridDim.x * 16u)
+    quant_token_row<BITS, SYM, GE, VL, F8>(r0 + (threadIdx.x >> 4), x, ft, fh, S, pos, rows, codes, scale,
+                                           zero, status, lrows[VL ? (threadIdx.x >> 4) : 0], pm);
 }
 
 // K and V of the same token-axis format in one launch: blockIdx.y selects the
 // tensor (0: K rows, 1: V rows), so a decode-step append costs one launch.
 template <int BITS, bool SYM, int GE, int F8>
 __global__ __launch_bounds__(256) void k_quant_token_kv(const uint16_t* __restrict__ xk,
-                                                        const uint16_t* __restrict__ xv, int t_new, int H,
-                                                        int S, const int* __restrict__ pos, long long rows,
+                                                        const uint16_t* __restrict__ xv, FastDiv ft, FastDiv fh,
+                                                        int S, const int* __restrict__ pos, uint32_t rows,
                                                         TensorArgs tk, TensorArgs tv,
                                                         unsigned* __restrict__ status, PageMap pm) {
   __shared__ uint16_t lrows[16][128];
-  for (long long r0 = (long long)blockIdx.x * 16; r0 < rows; r0 += (long long)gridDim.x * 16) {
-    const long long row = r0 + (threadIdx.x >> 4);
+  for (uint32_t r0 = blockIdx.x * 16u; r0 < rows; r0 += gridDim.x * 16u) {
+    const uint32_t row = r0 + (threadIdx.x >> 4);
     if (blockIdx.y == 0)
-      quant_token_row<BITS, SYM, GE, false, F8>(row, xk, t_new, H, S, pos, rows, tk.codes, tk.scale,
-                                                tk.zero, status, lrows[0], pm);
+      quant_token_row<BITS, SYM, GE, false, F8>(row, xk, ft, fh, S, pos, rows, tk.codes, tk.scale, tk.zero,
+                                                status, lrows[0], pm);
     else
-      quant_token_row<BITS, SYM, GE, true, F8>(row, xv, t_new, H, S, pos, rows, tv.codes, tv.scale,
-                                               tv.zero, status, lrows[threadIdx.x >> 4], pm);
+      quant_token_row<BITS, SYM, GE, true, F8>(row, xv, ft, fh, S, pos, rows, tv.codes, tv.scale, tv.zero,
+                                               status, lrows[threadIdx.x >> 4], pm);
   }
 }
 
@@ -1083,7 +1108,7 @@ __global__ __launch_bounds__(256) void k_quant_oaken_one(const uint16_t* __restr
   const int rl = threadIdx.x >> 4, li = threadIdx.x & 15;
   const long long bh = (long long)blockIdx.x * 16 + rl;
   if (bh >= BH) return;  // all 16 lanes of a row leave together
-  const int b = (int)(bh / H);
+  const int b = (int)((uint32_t)bh / (uint32_t)H);  // (bh < BH < 2^31: a 32-bit divide)
   const int p = pos[b];
   if (p < 0 || p + 1 > S) {
     if (li == 0) set_flag(status, kFlagPosRange);
@@ -1385,10 +1410,12 @@ hipError_t launch_quant_token_kv(const CacheArgs& c, const uint16_t* xk, const u
   const TensorArgs& t = c.k;
   const PageMap pm{c.pages, c.ptok, c.npages};
   const long long rows = (long long)c.B * c.H * t_new;
+  if (rows >= (1ll << 31)) return hipErrorInvalidValue;  // (rejected by kvq_quant_append)
+  const FastDiv ft = make_fastdiv((uint32_t)t_new), fh = make_fastdiv((uint32_t)c.H);
   const dim3 grid((unsigned)std::min<long long>((rows + 15) / 16, kRowBlocks), 2);
-#define KVQ_TOK(BITS, SYM, GE, F8)                                                                      \
-  hipLaunchKernelGGL((k_quant_token_kv<BITS, SYM, GE, F8>), grid, dim3(kThreads), 0, st, xk, xv, t_new, \
-                     c.H, c.S, pos, rows, c.k, c.v, c.status, pm)
+#define KVQ_TOK(BITS, SYM, GE, F8)                                                                       \
+  hipLaunchKernelGGL((k_quant_token_kv<BITS, SYM, GE, F8>), grid, dim3(kThreads), 0, st, xk, xv, ft, fh, \
+                     c.S, pos, (uint32_t)rows, c.k, c.v, c.status, pm)
 #define KVQ_TOK_G(BITS, SYM, F8)                  \
   switch (t.group) {                              \
     case 32: KVQ_TOK(BITS, SYM, 32, F8); break;   \
@@ -1424,15 +1451,18 @@ hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, bool vl, 
                               int t_new, const int* pos, hipStream_t st) {
   const PageMap pm{c.pages, c.ptok, c.npages};
   const long long rows = (long long)c.B * c.H * t_new;
+  if (rows >= (1ll << 31)) return hipErrorInvalidValue;  // (rejected by kvq_quant_append)
+  const FastDiv ft = make_fastdiv((uint32_t)t_new), fh = make_fastdiv((uint32_t)c.H);
+  const uint32_t nr = (uint32_t)rows;
   const dim3 grid((unsigned)std::min<long long>((rows + 15) / 16, kRowBlocks));
 #define KVQ_TOK(BITS, SYM, GE, F8)                                                                  \
   do {                                                                                              \
     if (vl)                                                                                         \
       hipLaunchKernelGGL((k_quant_token<BITS, SYM, GE, true, F8>), grid, dim3(kThreads), 0, st, x,  \
-                         t_new, c.H, c.S, pos, rows, t.codes, t.scale, t.zero, c.status, pm);       \
+                         ft, fh, c.S, pos, nr, t.codes, t.scale, t.zero, c.status, pm);             \
     else                                                                                            \
       hipLaunchKernelGGL((k_quant_token<BITS, SYM, GE, false, F8>), grid, dim3(kThreads), 0, st, x, \
-                         t_new, c.H, c.S, pos, rows, t.codes, t.scale, t.zero, c.status, pm);       \
+                         ft, fh, c.S, pos, nr, t.codes, t.scale, t.zero, c.status, pm);             \
   } while (0)
 #define KVQ_TOK_G(BITS, SYM, F8)                  \
   switch (t.group) {                              \
