@@ -583,9 +583,14 @@ __device__ __forceinline__ long long chunk_row0(const ClassPages& cp, int cls, l
 }
 
 // Chunk-mixed cache (the Cocktail page's reorder, §3.1.2, then quantization
-// of the reordered chunks): one workgroup per (slot, b, h); the slot's source
-// chunk is perm[b][slot], its class follows from seg[b].  FP16 chunks are
-// copied (in the row layout of the FP16 pool).
+// of the reordered chunks): one workgroup per (kMixSlots consecutive slots,
+// b, h); a slot's source chunk is perm[b][slot], its class follows from
+// seg[b].  FP16 chunks are copied (in the row layout of the FP16 pool).  A
+// chunk is only chunk_tokens rows, so a workgroup takes several: the
+// sequence's class counts and the slots' sources are read once, and the
+// workgroups' per-slot prologue no longer dominates.
+constexpr int kMixSlots = 8;
+
 template <int GE, bool VL>
 __global__ __launch_bounds__(256) void k_quant_mixed(
     const uint16_t* __restrict__ x, int H, int S, int CT, int C, const int* __restrict__ pos,
@@ -595,52 +600,62 @@ __global__ __launch_bounds__(256) void k_quant_mixed(
     unsigned* __restrict__ status, ClassPages cp) {
   constexpr int NG = kD / GE, LG = GE / 8;
   __shared__ uint16_t lrows[VL ? 16 : 1][128];
-  const int j = blockIdx.x;
+  __shared__ int lsrc[kMixSlots];
+  const int j0 = blockIdx.x * kMixSlots;
   const long long bh = blockIdx.y;
   const int b = (int)(bh / H);
   if (pos[b] != 0) {
-    if (threadIdx.x == 0 && j == 0) set_flag(status, kFlagPosRange);
+    if (threadIdx.x == 0 && j0 == 0) set_flag(status, kFlagPosRange);
     return;
   }
   const int n16 = seg[b * 4], n4 = seg[b * 4 + 1], n = seg[b * 4 + 3];
-  if (j >= n || n > C) return;
-  const int src = perm[(long long)b * C + j];
-  if (src < 0 || src >= C) return;
-  const int cls = j < n16 ? 0 : (j < n16 + n4 ? 1 : 2);
-  const int k = cls == 0 ? j : (cls == 1 ? j - n16 : j - n16 - n4);
-  const uint16_t* xs = x + (bh * S + (long long)src * CT) * kD;
-  const long long drow0 = chunk_row0(cp, cls, bh, H, S, CT, k);
-  if (drow0 < 0) {
-    if (threadIdx.x == 0) set_flag(status, kFlagPageRange);
-    return;
+  if (j0 >= n || n > C) return;
+  if (threadIdx.x < kMixSlots) {
+    const int j = j0 + (int)threadIdx.x;
+    lsrc[threadIdx.x] = j < n ? perm[(long long)b * C + j] : -1;
   }
+  __syncthreads();
   const int li = threadIdx.x & 15;
   uint16_t* lrow = lrows[VL ? (threadIdx.x >> 4) : 0];
-  for (int r = threadIdx.x >> 4; r < CT; r += 16) {
-    const uint4 raw = ld_row8(xs + (long long)r * kD + li * 8);
-    const long long drow = drow0 + r;
-    if (cls == 0) {
-      store_row_f16<VL>(c16 + drow * kD * 2, li, raw, lrow);
+  for (int sl = 0; sl < kMixSlots; ++sl) {
+    const int j = j0 + sl;
+    if (j >= n) break;  // (uniform over the workgroup)
+    const int src = lsrc[sl];
+    if (src < 0 || src >= C) continue;
+    const int cls = j < n16 ? 0 : (j < n16 + n4 ? 1 : 2);
+    const int k = cls == 0 ? j : (cls == 1 ? j - n16 : j - n16 - n4);
+    const uint16_t* xs = x + (bh * S + (long long)src * CT) * kD;
+    const long long drow0 = chunk_row0(cp, cls, bh, H, S, CT, k);
+    if (drow0 < 0) {
+      if (threadIdx.x == 0) set_flag(status, kFlagPageRange);
       continue;
     }
-    float v[8];
-    unpack8(raw, v);
-    uint32_t plo, phi;
-    float s;
-    int z;
-    if (cls == 1) {
-      quant8<4, false, GE>(v, 0xFFu, plo, phi, s, z);
-      store_row_codes<4, VL>(c4 + drow * 64, li, plo, phi, lrow);
-      if (li % LG == 0) {
-        s4[drow * NG + li / LG] = s;
-        z4[drow * NG + li / LG] = (uint8_t)z;
+    for (int r = threadIdx.x >> 4; r < CT; r += 16) {
+      const uint4 raw = ld_row8(xs + (long long)r * kD + li * 8);
+      const long long drow = drow0 + r;
+      if (cls == 0) {
+        store_row_f16<VL>(c16 + drow * kD * 2, li, raw, lrow);
+        continue;
       }
-    } else {
-      quant8<2, false, GE>(v, 0xFFu, plo, phi, s, z);
-      store_row_codes<2, VL>(c2 + drow * 32, li, plo, phi, lrow);
-      if (li % LG == 0) {
-        s2[drow * NG + li / LG] = s;
-        z2[drow * NG + li / LG] = (uint8_t)z;
+      float v[8];
+      unpack8(raw, v);
+      uint32_t plo, phi;
+      float s;
+      int z;
+      if (cls == 1) {
+        quant8<4, false, GE>(v, 0xFFu, plo, phi, s, z);
+        store_row_codes<4, VL>(c4 + drow * 64, li, plo, phi, lrow);
+        if (li % LG == 0) {
+          s4[drow * NG + li / LG] = s;
+          z4[drow * NG + li / LG] = (uint8_t)z;
+        }
+      } else {
+        quant8<2, false, GE>(v, 0xFFu, plo, phi, s, z);
+        store_row_codes<2, VL>(c2 + drow * 32, li, plo, phi, lrow);
+        if (li % LG == 0) {
+          s2[drow * NG + li / LG] = s;
+          z2[drow * NG + li / LG] = (uint8_t)z;
+        }
       }
     }
   }
@@ -1522,7 +1537,7 @@ hipError_t launch_quant_channel(const CacheArgs& c, const TensorArgs& t, const u
 hipError_t launch_quant_mixed(const CacheArgs& c, const TensorArgs& t, bool vl, const uint16_t* x,
                               const int* pos, hipStream_t st) {
   const int C = c.S / c.chunk_tokens;
-  const dim3 grid((unsigned)C, (unsigned)(c.B * c.H));
+  const dim3 grid((unsigned)((C + kMixSlots - 1) / kMixSlots), (unsigned)(c.B * c.H));
   const ClassPages cp{c.pages, c.ptok, c.npages, c.B};
 #define KVQ_MIX(GE)                                                                                \
   do {                                                                                             \
