@@ -318,17 +318,129 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
   return (t + ((n - t) >> 1)) >> (f.s - 1);
 }
 
+// Codes of one lane's 16 values (channels 16 li .. 16 li + 15) of a token
+// row, groups of GE channels over GE / 16 lanes: the quantizer of quant8 on
+// twice the values per lane (the same groups, so the same scales and codes),
+// codes returned as integers (two's complement bytes for symmetric INT8).
+template <int BITS, bool SYM, int GE, int F8 = 0>
+__device__ __forceinline__ void quant16(const float (&x)[16], unsigned (&c)[16], float& s, int& z) {
+  constexpr int LG = GE / 16;
+  if constexpr (F8 != 0) {
+    static_assert(BITS == 8, "FP8 codes are bytes");
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(x[k]));
+    amax = max_lanes<1, LG>(amax);
+    s = amax / (F8 == 1 ? 448.0f : 57344.0f);  // (the corrected step misrounds some of these quotients)
+    z = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) c[k] = s != 0.0f ? (F8 == 1 ? e4m3_code(x[k] / s) : e5m2_code(x[k] / s)) : 0u;
+  } else if constexpr (SYM) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(x[k]));
+    amax = max_lanes<1, LG>(amax);
+    s = div_const<127>(amax);
+    z = 0;
+    const float r = recip_refined(s);  // s = 0: all codes 0
+    float n[16];
+    const bool near = rne_quot_lane<128>(x, r, n);
+    if (wave_any(near) && near) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) n[k] = rintf(x[k] / s);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) c[k] = (unsigned)((int)__builtin_amdgcn_fmed3f(n[k], -128.0f, 127.0f) & 0xFF);
+  } else {
+    constexpr float QMAX = (float)((1 << BITS) - 1);
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      lo = fminf(lo, x[k]);
+      hi = fmaxf(hi, x[k]);
+    }
+    lo = min_lanes<1, LG>(lo);
+    hi = max_lanes<1, LG>(hi);
+    s = div_const<(1 << BITS) - 1>(hi - lo);
+    const float r = recip_refined(s);  // s = 0: z = 0 and all codes 0
+    float n[16];
+    bool near = rne_quot_lane<(1 << BITS)>(x, r, n);
+    float zf = rne_quot<(1 << BITS)>(-lo, r, near);
+    if (wave_any(near) && near) {
+      zf = rintf(-lo / s);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) n[k] = rintf(x[k] / s);
+    }
+    zf = __builtin_amdgcn_fmed3f(zf, 0.0f, QMAX);
+    z = (int)zf;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) c[k] = (unsigned)__builtin_amdgcn_fmed3f(n[k] + zf, 0.0f, QMAX);
+  }
+}
+
+// Eight codes of BITS bits, code k at bits BITS k (lo: the first 32 bits).
+template <int BITS>
+__device__ __forceinline__ void pack8(const unsigned* c, uint32_t& lo, uint32_t& hi) {
+  lo = 0;
+  hi = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (BITS * k < 32) lo |= c[k] << (BITS * k);
+    else hi |= c[k] << (BITS * k - 32);
+  }
+}
+
+// Store a lane's 16 codes (channels 16 li + k) into a packed row.
+//  K layout: the lane's two 8-channel slots, k_slot(2 li) and k_slot(2 li + 1).
+//  V layout: word n holds channels n + 16 j, so the lane's code k is code j
+//  = li of word k; the row's 8 lanes exchange codes through `lc` (128 bytes
+//  of this row, wave-local): code k to byte 8 k + li, then lane li reads
+//  bytes 16 li .. 16 li + 15, words 2 li and 2 li + 1.
+template <int BITS, bool VL>
+__device__ __forceinline__ void store_row_codes16(uint8_t* row, int li, const unsigned (&c)[16], uint8_t* lc) {
+  if constexpr (!VL) {
+    uint32_t lo, hi;
+    pack8<BITS>(c, lo, hi);
+    store_codes8<BITS>(row, k_slot(2 * li), lo, hi);
+    pack8<BITS>(c + 8, lo, hi);
+    store_codes8<BITS>(row, k_slot(2 * li + 1), lo, hi);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) lc[8 * k + li] = (uint8_t)c[k];
+    wave_lds_sync();
+    const uint4 by = *reinterpret_cast<const uint4*>(lc + 16 * li);
+    wave_lds_sync();
+    if constexpr (BITS == 8) {
+      st_u4(row + 16 * li, by);
+    } else if constexpr (BITS == 4) {
+      // bytes b0..b3 (each < 16) -> b0 | b1 << 4 | b2 << 8 | b3 << 12
+      auto nib4 = [](uint32_t d) {
+        const uint32_t t = d | (d >> 4);
+        return (t & 0xFFu) | ((t >> 8) & 0xFF00u);
+      };
+      st_nt<u2q_t>(row + 8 * li, u2q_t{nib4(by.x) | nib4(by.y) << 16, nib4(by.z) | nib4(by.w) << 16});
+    } else {
+      // bytes b0..b3 (each < 4) -> b0 | b1 << 2 | b2 << 4 | b3 << 6
+      auto crumb4 = [](uint32_t d) {
+        const uint32_t t = d | (d >> 6);
+        return (t & 0xFu) | ((t >> 12) & 0xF0u);
+      };
+      st_nt<uint32_t>(row + 4 * li, crumb4(by.x) | crumb4(by.y) << 8 | crumb4(by.z) << 16 | crumb4(by.w) << 24);
+    }
+  }
+}
+
 // rows = batch * H * t_new < 2^31 (checked by the caller), so the grid-strided
-// row index never wraps
+// row index never wraps.  Eight lanes per row, 16 channels per lane.
 template <int BITS, bool SYM, int GE, bool VL, int F8 = 0>
 __device__ __forceinline__ void quant_token_row(uint32_t row, const uint16_t* __restrict__ x, FastDiv ft,
                                                 FastDiv fh, int S, const int* __restrict__ pos, uint32_t rows,
                                                 uint8_t* __restrict__ codes, float* __restrict__ scale,
                                                 uint8_t* __restrict__ zero, unsigned* __restrict__ status,
-                                                uint16_t* lrow, const PageMap& pm) {
-  constexpr int NG = kD / GE, LG = GE / 8, RB = kD * BITS / 8;
-  const int li = threadIdx.x & 15;
-  if (row >= rows) return;  // all 16 lanes of a row leave together
+                                                uint8_t* lc, const PageMap& pm) {
+  constexpr int NG = kD / GE, LG = GE / 16, RB = kD * BITS / 8;
+  const int li = threadIdx.x & 7;
+  if (row >= rows) return;  // all 8 lanes of a row leave together
   const uint32_t bh32 = fdiv(row, ft);
   const int t = (int)(row - bh32 * ft.d);
   const long long bh = bh32;
@@ -349,13 +461,22 @@ __device__ __forceinline__ void quant_token_row(uint32_t row, const uint16_t* __
     }
     dst = ((long long)pg * H + (bh32 - b32 * fh.d)) * pm.ptok + tok % pm.ptok;
   }
-  float v[8];
-  unpack8(ld_row8(x + (long long)row * kD + li * 8), v);
-  uint32_t plo, phi;
+  const uint16_t* src = x + (long long)row * kD + li * 16;
+  float v[16];
+  {
+    float h[8];
+    unpack8(ld_row8(src), h);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = h[k];
+    unpack8(ld_row8(src + 8), h);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[8 + k] = h[k];
+  }
+  unsigned c[16];
   float s;
   int z;
-  quant8<BITS, SYM, GE, F8>(v, 0xFFu, plo, phi, s, z);
-  store_row_codes<BITS, VL>(codes + dst * RB, li, plo, phi, lrow);
+  quant16<BITS, SYM, GE, F8>(v, c, s, z);
+  store_row_codes16<BITS, VL>(codes + dst * RB, li, c, lc);
   if (li % LG == 0) {
     scale[dst * NG + li / LG] = s;
     if constexpr (!SYM && !F8) zero[dst * NG + li / LG] = (uint8_t)z;
@@ -369,11 +490,11 @@ __global__ __launch_bounds__(256) void k_quant_token(const uint16_t* __restrict_
                                                      float* __restrict__ scale,
                                                      uint8_t* __restrict__ zero,
                                                      unsigned* __restrict__ status, PageMap pm) {
-  __shared__ uint16_t lrows[VL ? 16 : 1][128];
-  // blocks of 16 rows, grid-strided: a bounded grid keeps the dispatch cost low
-  for (uint32_t r0 = blockIdx.x * 16u; r0 < rows; r0 += gridDim.x * 16u)
-    quant_token_row<BITS, SYM, GE, VL, F8>(r0 + (threadIdx.x >> 4), x, ft, fh, S, pos, rows, codes, scale,
-                                           zero, status, lrows[VL ? (threadIdx.x >> 4) : 0], pm);
+  __shared__ __align__(16) uint8_t lcode[VL ? 32 : 1][128];
+  // blocks of 32 rows, grid-strided: a bounded grid keeps the dispatch cost low
+  for (uint32_t r0 = blockIdx.x * 32u; r0 < rows; r0 += gridDim.x * 32u)
+    quant_token_row<BITS, SYM, GE, VL, F8>(r0 + (threadIdx.x >> 3), x, ft, fh, S, pos, rows, codes, scale,
+                                           zero, status, lcode[VL ? (threadIdx.x >> 3) : 0], pm);
 }
 
 // K and V of the same token-axis format in one launch: blockIdx.y selects the
@@ -384,15 +505,15 @@ __global__ __launch_bounds__(256) void k_quant_token_kv(const uint16_t* __restri
                                                         int S, const int* __restrict__ pos, uint32_t rows,
                                                         TensorArgs tk, TensorArgs tv,
                                                         unsigned* __restrict__ status, PageMap pm) {
-  __shared__ uint16_t lrows[16][128];
-  for (uint32_t r0 = blockIdx.x * 16u; r0 < rows; r0 += gridDim.x * 16u) {
-    const uint32_t row = r0 + (threadIdx.x >> 4);
+  __shared__ __align__(16) uint8_t lcode[32][128];
+  for (uint32_t r0 = blockIdx.x * 32u; r0 < rows; r0 += gridDim.x * 32u) {
+    const uint32_t row = r0 + (threadIdx.x >> 3);
     if (blockIdx.y == 0)
       quant_token_row<BITS, SYM, GE, false, F8>(row, xk, ft, fh, S, pos, rows, tk.codes, tk.scale, tk.zero,
-                                                status, lrows[0], pm);
+                                                status, lcode[0], pm);
     else
       quant_token_row<BITS, SYM, GE, true, F8>(row, xv, ft, fh, S, pos, rows, tv.codes, tv.scale, tv.zero,
-                                               status, lrows[threadIdx.x >> 4], pm);
+                                               status, lcode[threadIdx.x >> 3], pm);
   }
 }
 
@@ -1413,7 +1534,7 @@ __global__ __launch_bounds__(256) void k_dsq_tail(const uint16_t* __restrict__ x
 }
 
 constexpr int kThreads = 256;
-constexpr long long kRowBlocks = 4096;  // grid bound of the row kernels (blocks of 16 rows)
+constexpr long long kRowBlocks = 4096;  // grid bound of the row kernels (blocks of 32 rows)
 
 }  // namespace
 
@@ -1427,7 +1548,7 @@ hipError_t launch_quant_token_kv(const CacheArgs& c, const uint16_t* xk, const u
   const long long rows = (long long)c.B * c.H * t_new;
   if (rows >= (1ll << 31)) return hipErrorInvalidValue;  // (rejected by kvq_quant_append)
   const FastDiv ft = make_fastdiv((uint32_t)t_new), fh = make_fastdiv((uint32_t)c.H);
-  const dim3 grid((unsigned)std::min<long long>((rows + 15) / 16, kRowBlocks), 2);
+  const dim3 grid((unsigned)std::min<long long>((rows + 31) / 32, kRowBlocks), 2);
 #define KVQ_TOK(BITS, SYM, GE, F8)                                                                       \
   hipLaunchKernelGGL((k_quant_token_kv<BITS, SYM, GE, F8>), grid, dim3(kThreads), 0, st, xk, xv, ft, fh, \
                      c.S, pos, (uint32_t)rows, c.k, c.v, c.status, pm)
@@ -1469,7 +1590,7 @@ hipError_t launch_quant_token(const CacheArgs& c, const TensorArgs& t, bool vl, 
   if (rows >= (1ll << 31)) return hipErrorInvalidValue;  // (rejected by kvq_quant_append)
   const FastDiv ft = make_fastdiv((uint32_t)t_new), fh = make_fastdiv((uint32_t)c.H);
   const uint32_t nr = (uint32_t)rows;
-  const dim3 grid((unsigned)std::min<long long>((rows + 15) / 16, kRowBlocks));
+  const dim3 grid((unsigned)std::min<long long>((rows + 31) / 32, kRowBlocks));
 #define KVQ_TOK(BITS, SYM, GE, F8)                                                                  \
   do {                                                                                              \
     if (vl)                                                                                         \
