@@ -719,8 +719,9 @@ __global__ __launch_bounds__(256) void k_quant_mixed(
     uint8_t* __restrict__ c4, float* __restrict__ s4, uint8_t* __restrict__ z4,
     uint8_t* __restrict__ c2, float* __restrict__ s2, uint8_t* __restrict__ z2,
     unsigned* __restrict__ status, ClassPages cp) {
-  constexpr int NG = kD / GE, LG = GE / 8;
+  constexpr int NG = kD / GE, LG = GE / 16;
   __shared__ uint16_t lrows[VL ? 16 : 1][128];
+  __shared__ __align__(16) uint8_t lcode[VL ? 32 : 1][128];
   __shared__ int lsrc[kMixSlots];
   const int j0 = blockIdx.x * kMixSlots;
   const long long bh = blockIdx.y;
@@ -751,31 +752,43 @@ __global__ __launch_bounds__(256) void k_quant_mixed(
       if (threadIdx.x == 0) set_flag(status, kFlagPageRange);
       continue;
     }
-    for (int r = threadIdx.x >> 4; r < CT; r += 16) {
-      const uint4 raw = ld_row8(xs + (long long)r * kD + li * 8);
+    if (cls == 0) {  // FP16: copied, 16 lanes per row
+      for (int r = threadIdx.x >> 4; r < CT; r += 16)
+        store_row_f16<VL>(c16 + (drow0 + r) * kD * 2, li, ld_row8(xs + (long long)r * kD + li * 8), lrow);
+      continue;
+    }
+    // INT4 / INT2: eight lanes per row, 16 channels per lane
+    const int l8 = threadIdx.x & 7;
+    uint8_t* lc = lcode[VL ? (threadIdx.x >> 3) : 0];
+    for (int r = threadIdx.x >> 3; r < CT; r += 32) {
+      const uint16_t* src = xs + (long long)r * kD + l8 * 16;
       const long long drow = drow0 + r;
-      if (cls == 0) {
-        store_row_f16<VL>(c16 + drow * kD * 2, li, raw, lrow);
-        continue;
+      float v[16];
+      {
+        float h[8];
+        unpack8(ld_row8(src), h);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = h[k];
+        unpack8(ld_row8(src + 8), h);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[8 + k] = h[k];
       }
-      float v[8];
-      unpack8(raw, v);
-      uint32_t plo, phi;
+      unsigned c[16];
       float s;
       int z;
       if (cls == 1) {
-        quant8<4, false, GE>(v, 0xFFu, plo, phi, s, z);
-        store_row_codes<4, VL>(c4 + drow * 64, li, plo, phi, lrow);
-        if (li % LG == 0) {
-          s4[drow * NG + li / LG] = s;
-          z4[drow * NG + li / LG] = (uint8_t)z;
+        quant16<4, false, GE>(v, c, s, z);
+        store_row_codes16<4, VL>(c4 + drow * 64, l8, c, lc);
+        if (l8 % LG == 0) {
+          s4[drow * NG + l8 / LG] = s;
+          z4[drow * NG + l8 / LG] = (uint8_t)z;
         }
       } else {
-        quant8<2, false, GE>(v, 0xFFu, plo, phi, s, z);
-        store_row_codes<2, VL>(c2 + drow * 32, li, plo, phi, lrow);
-        if (li % LG == 0) {
-          s2[drow * NG + li / LG] = s;
-          z2[drow * NG + li / LG] = (uint8_t)z;
+        quant16<2, false, GE>(v, c, s, z);
+        store_row_codes16<2, VL>(c2 + drow * 32, l8, c, lc);
+        if (l8 % LG == 0) {
+          s2[drow * NG + l8 / LG] = s;
+          z2[drow * NG + l8 / LG] = (uint8_t)z;
         }
       }
     }
