@@ -1430,7 +1430,7 @@ __global__ __launch_bounds__(256) void k_quant_dsq(const uint16_t* __restrict__ 
       xv_[i] = i < n_sig ? h2f(h) : 0.0f;
       amax = fmaxf(amax, fabsf(xv_[i]));
     }
-    const float s = amax / 127.0f;
+    const float s = div_const<127>(amax);
     // rne(x / s) without a divide per value (rne_quot; slots past n_sig hold
     // 0 and code 0; s = 0 gives r = 0 and codes 0)
     const float r = recip_refined(s);
