@@ -299,10 +299,18 @@ __device__ __forceinline__ void oak_v_apply_one(OakWave<QR, NG>& W, const OakLis
   if constexpr (QR == 1) {
     const bool hi = en & 128u;
     const float mag = (float)((en >> 8) & 31u);
-    const float* pv = W.pv[row];
-    const float val = fmaf(hi ? mag : -mag, pv[2 + (NG == 1 ? 0u : idx / (128 / NG))], hi ? pv[1] : pv[0]);
-    float* a = ok ? &W.osp[tag][0][idx] : &W.pad[lane];
-    *a += ok ? val : 0.0f;
+    float sg, tv;
+    if constexpr (NG <= 2) {  // the row's four products in one 16-byte read
+      const float4 pv = *reinterpret_cast<const float4*>(W.pv[row]);
+      sg = (NG == 2 && idx >= 64u) ? pv.w : pv.z;
+      tv = hi ? pv.y : pv.x;
+    } else {
+      const float* pv = W.pv[row];
+      sg = pv[2 + idx / (128 / NG)];
+      tv = hi ? pv[1] : pv[0];
+    }
+    const float val = fmaf(hi ? mag : -mag, sg, tv);
+    if (ok) W.osp[tag][0][idx] += val;
     return;
   }
   const float xh = oak_value(en, W.so[row][NG == 1 ? 0u : idx / (128 / NG)], l);
