@@ -9,13 +9,18 @@
 //     s = max|x| / 127, q = clamp(rne(x / s), -128, 127)
 //   FP8 E4M3 (the same page's FP8 item): s = max|x| / 448, q = E4M3 code of
 //     x / s (nearest, ties to even, saturating at 448; see e4m3_code)
-// The divisions are true IEEE divisions (the build keeps correctly rounded
-// fp32 division and denormals), so codes, scales and zero-points are
-// bit-identical to any other binary32 evaluation of these formulas.
+// Every quotient is the IEEE binary32 one (the build keeps correctly rounded
+// fp32 division and denormals; where a kernel avoids the divide, by the
+// corrected constant division or the rounding check below, it reaches the
+// same value), so codes, scales and zero-points are bit-identical to any
+// other binary32 evaluation of these formulas.
 //
-// Thread layout of the token-axis kernels: 16 lanes per 128-channel row, each
-// lane holds 8 consecutive channels (one 16-byte load); a group of GE
-// channels is GE / 8 adjacent lanes, reduced with lane shuffles.
+// Thread layout of the token-axis, Oaken prefill and chunk-mixed INT4/INT2
+// kernels: 8 lanes per 128-channel row, each lane holds 16 consecutive
+// channels (two 16-byte loads); a group of GE channels is GE / 16 adjacent
+// lanes, reduced with lane exchanges.  The one-token Oaken append, the
+// streaming chunk kernels, the DSQ rows and the FP16 copies keep 16 lanes
+// of 8 channels (quant8).
 #include <algorithm>
 
 #include "kvq_dev.h"
