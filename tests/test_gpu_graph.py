@@ -8,7 +8,9 @@ same token at the same position is idempotent, so each replay recomputes the
 same cache and output.  Modes: uniform INT4 (one attention kernel and the
 merge), channel-axis K (the streaming tail, the token V rows, attention,
 merge), Oaken (the one-token Oaken append, the K score-share kernel,
-attention), and the no-alloc decode entry point."""
+attention), paged INT8 and paged Oaken, DSQ (its one-token append into the
+tails, then decode), the chunk-mixed cache (decode alone: its cache is
+full), and the no-alloc decode entry point."""
 import numpy as np
 import pytest
 
@@ -31,7 +33,8 @@ def _gpu():
 
 
 @pytest.mark.parametrize("mode,noalloc", [("uniform_4_a_64", False), ("uniform_4_a_64", True),
-                                          ("channel4", False), ("oaken", False)])
+                                          ("channel4", False), ("oaken", False), ("paged8", False),
+                                          ("paged_oaken", False), ("dsq", False), ("mixed", False)])
 @pytest.mark.parametrize("G", [1, 4])
 def test_graph_replay_matches_eager_step(mode, noalloc, G):
     print("case graph %s noalloc=%d G=%d" % (mode, noalloc, G), flush=True)
@@ -39,22 +42,29 @@ def test_graph_replay_matches_eager_step(mode, noalloc, G):
     torch.cuda.synchronize()
     assert cache.flags() == 0
     B, H = q.shape[0], Hq // G
-    wl = {"oaken": 5, "channel4": 3}.get(mode, 2)
+    wl = {"oaken": 5, "paged_oaken": 5, "channel4": 3, "dsq": 8}.get(mode, 2)
     w = synth.scaled(synth.WORKLOADS[wl], batch=B, kv_heads=H, q_heads=Hq, seq=T + 1, tokens=T + 1)
     k1 = to_device(np.ascontiguousarray(w.kv(0)[:, :, T:T + 1]))
     v1 = to_device(np.ascontiguousarray(w.kv(1)[:, :, T:T + 1]))
     qd = to_device(q)
     pos = i32_device([T] * B)
-    lens = i32_device([T + 1, T - 57])
+    append = mode != "mixed"  # (the chunk-mixed cache is full: decode alone)
+    max_len = T + 1 if append else T
+    lens = i32_device([max_len, T - 57])
     out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
-    ws, n = cache.workspace(Hq, T + 1, 0)
+    ws, n = cache.workspace(Hq, max_len, 0)
+    if mode == "dsq":
+        score1 = torch.from_numpy(np.ascontiguousarray(w.scores()[:, :, T:T + 1])).cuda()
 
     def step():
-        K.kvq_quant_append(cache.desc, k1, v1, 1, pos)
+        if mode == "dsq":
+            K.kvq_dsq_append(cache.desc, k1, v1, score1, 1, pos)
+        elif append:
+            K.kvq_quant_append(cache.desc, k1, v1, 1, pos)
         if noalloc:
-            K.kvq_decode_attn_noalloc(cache.desc, qd, Hq, lens, T + 1, SM, out, 0)
+            K.kvq_decode_attn_noalloc(cache.desc, qd, Hq, lens, max_len, SM, out, 0)
         else:
-            K.kvq_decode_attn(cache.desc, qd, Hq, lens, T + 1, SM, out, ws, n, 0)
+            K.kvq_decode_attn(cache.desc, qd, Hq, lens, max_len, SM, out, ws, n, 0)
 
     step()
     torch.cuda.synchronize()
