@@ -8,7 +8,7 @@
 //   symmetric INT8 ([KV-cache quantization engineering page, INT8 listing]):
 //     s = max|x| / 127, q = clamp(rne(x / s), -128, 127)
 //   FP8 E4M3 (the same page's FP8 item): s = max|x| / 448, q = E4M3 code of
-//     x / s (nearest, ties to even, saturating at 448; see e4m3_code)
+//     x / s (nearest, ties to even, saturating at 448; see f8_pair)
 // Every quotient is the IEEE binary32 one (the build keeps correctly rounded
 // fp32 division and denormals; where a kernel avoids the divide, by the
 // corrected constant division or the rounding check below, it reaches the
@@ -28,41 +28,20 @@
 namespace kvq {
 namespace {
 
-// OCP E4M3 code (no infinities, largest finite 1.75 * 2^8 = 448) of a
-// binary32 value, from its bits: the nearest finite value, ties to the even
-// mantissa, magnitudes from 448 up give 448; the sign bit is kept.
-//  |y| < 2^-6: the subnormal codes m * 2^-9, m = rne(|y| * 2^9) (exact
-//              scaling; m = 8 is the smallest normal, code 0x08);
-//  otherwise : exponent and mantissa bits rounded half to even at bit 20
-//              (a carry out of the mantissa steps the exponent), then the
-//              exponent rebiased from 127 to 7.
-// All three candidates are formed and one selected, so a wave never splits.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  const uint32_t normal = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-  const uint32_t sub = (uint32_t)rintf(__uint_as_float(a) * 512.0f);
-  const uint32_t mag = a >= 0x43E00000u ? 0x7Eu : (a < 0x3C800000u ? sub : normal);
-  return sign | mag;
-}
-
-// OCP E5M2 code of a binary32 value (5 exponent bits as fp16, largest finite
-// 1.75 * 2^15 = 57344; the cache never holds an infinity): the nearest
-// finite value, ties to the even mantissa, magnitudes from 57344 up give
-// 57344; the sign bit is kept.
-//  |y| < 2^-14: the subnormal codes m * 2^-16, m = rne(|y| * 2^16) (m = 4 is
-//               the smallest normal, code 0x04);
-//  otherwise  : exponent and mantissa bits rounded half to even at bit 21,
-//               then the exponent rebiased from 127 to 15.
-__device__ __forceinline__ uint32_t e5m2_code(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  const uint32_t normal = ((a + 0xFFFFFu + ((a >> 21) & 1u)) >> 21) - (112u << 2);
-  const uint32_t sub = (uint32_t)rintf(__uint_as_float(a) * 65536.0f);
-  const uint32_t mag = a >= 0x47600000u ? 0x7Bu : (a < 0x38800000u ? sub : normal);
-  return sign | mag;
+// FP8 codes of two binary32 quotients, by the hardware conversion to the
+// OCP formats (E4M3: no infinities, largest finite 448; E5M2: largest finite
+// 57344): the nearest value, ties to the even mantissa, sign kept.  Each
+// quotient is first clamped to the largest finite magnitude, so anything at
+// or beyond it gives that magnitude (saturation) whatever the conversion does
+// with overflows.  The cache never holds an infinity or NaN, so the codes of
+// non-finite inputs are left unspecified.  Returns the two bytes in bits 0-15.
+template <int F8>
+__device__ __forceinline__ uint32_t f8_pair(float y0, float y1) {
+  constexpr float kTop = F8 == 1 ? 448.0f : 57344.0f;
+  y0 = __builtin_amdgcn_fmed3f(y0, -kTop, kTop);
+  y1 = __builtin_amdgcn_fmed3f(y1, -kTop, kTop);
+  if constexpr (F8 == 1) return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false) & 0xFFFFu;
+  else return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(y0, y1, 0, false) & 0xFFFFu;
 }
 
 // Rounded quotients without a division per element.  Every code below is
@@ -126,29 +105,13 @@ __device__ __forceinline__ bool rne_quot_lane(const float (&x)[N], float r, floa
   return !(dev < kAccept);
 }
 
-// F8: 0 integer codes, 1 FP8 E4M3, 2 FP8 E5M2
-template <int BITS, bool SYM, int GE, int F8 = 0>
+template <int BITS, bool SYM, int GE>
 __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint32_t& plo,
                                        uint32_t& phi, float& s, int& z) {
   constexpr int LG = GE / 8;
   plo = 0;
   phi = 0;
-  if constexpr (F8 != 0) {
-    static_assert(BITS == 8, "FP8 codes are bytes");
-    float amax = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
-    amax = max_lanes<1, LG>(amax);
-    s = amax / (F8 == 1 ? 448.0f : 57344.0f);  // (the corrected step misrounds some of these quotients)
-    z = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      uint32_t byte = 0u;
-      if (s != 0.0f) byte = F8 == 1 ? e4m3_code(x[k] / s) : e5m2_code(x[k] / s);
-      if (k < 4) plo |= byte << (8 * k);
-      else phi |= byte << (8 * (k - 4));
-    }
-  } else if constexpr (SYM) {
+  if constexpr (SYM) {
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
@@ -327,6 +290,7 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
 // row, groups of GE channels over GE / 16 lanes: the quantizer of quant8 on
 // twice the values per lane (the same groups, so the same scales and codes),
 // codes returned as integers (two's complement bytes for symmetric INT8).
+// F8: 0 integer codes, 1 FP8 E4M3, 2 FP8 E5M2.
 template <int BITS, bool SYM, int GE, int F8 = 0>
 __device__ __forceinline__ void quant16(const float (&x)[16], unsigned (&c)[16], float& s, int& z) {
   constexpr int LG = GE / 16;
@@ -339,7 +303,11 @@ __device__ __forceinline__ void quant16(const float (&x)[16], unsigned (&c)[16],
     s = amax / (F8 == 1 ? 448.0f : 57344.0f);  // (the corrected step misrounds some of these quotients)
     z = 0;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) c[k] = s != 0.0f ? (F8 == 1 ? e4m3_code(x[k] / s) : e5m2_code(x[k] / s)) : 0u;
+    for (int k = 0; k < 16; k += 2) {
+      const uint32_t w = f8_pair<F8>(x[k] / s, x[k + 1] / s);
+      c[k] = s != 0.0f ? (w & 0xFFu) : 0u;
+      c[k + 1] = s != 0.0f ? (w >> 8) : 0u;
+    }
   } else if constexpr (SYM) {
     float amax = 0.0f;
 #pragma unroll
