@@ -105,6 +105,35 @@ __device__ __forceinline__ bool rne_quot_lane(const float (&x)[N], float r, floa
   return !(dev < kAccept);
 }
 
+// Asymmetric codes clamp(rne(fl(x / s)) + z, 0, M - 1) of a lane's N values
+// (M = 2^bits), z = clamp(rne(fl(-lo / s)), 0, M - 1) already formed as the
+// exact float zf.  Each code comes from t = fl(x r + zf), one rounding: with
+// |x / s| < M and 0 <= zf < M, t differs from fl(x / s) + zf by less than
+// M 2^-21 (the reciprocal's error, the quotient's rounding and the sum's), so
+// where every |t - rne(t)| of the lane (exact, by Sterbenz) stays below
+// 0.5 - M 2^-19, rne(t) is the integer nearest fl(x / s) + zf, which is
+// rne(fl(x / s)) + zf (zf an integer, and no tie).  Otherwise (near-ties,
+// exact ties, anything not finite) the lane divides.  A NaN t gives NaN
+// either way.
+template <int M, int N>
+__device__ __forceinline__ void asym_codes(const float (&x)[N], float s, float r, float zf, float (&q)[N]) {
+  constexpr float kAccept = 0.5f - (float)M * 0x1p-19f;
+  float dev = 0.0f;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const float t = fmaf(x[k], r, zf);
+    q[k] = rintf(t);
+    dev = fmaxf(dev, fabsf(t - q[k]));
+  }
+  const bool near = !(dev < kAccept);
+  if (wave_any(near) && near) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) q[k] = rintf(x[k] / s) + zf;
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) q[k] = __builtin_amdgcn_fmed3f(q[k], 0.0f, (float)(M - 1));
+}
+
 template <int BITS, bool SYM, int GE>
 __device__ __forceinline__ void quant8(const float (&x)[8], unsigned valid, uint32_t& plo,
                                        uint32_t& phi, float& s, int& z) {
@@ -336,18 +365,15 @@ __device__ __forceinline__ void quant16(const float (&x)[16], unsigned (&c)[16],
     hi = max_lanes<1, LG>(hi);
     s = div_const<(1 << BITS) - 1>(hi - lo);
     const float r = recip_refined(s);  // s = 0: z = 0 and all codes 0
-    float n[16];
-    bool near = rne_quot_lane<(1 << BITS)>(x, r, n);
+    bool near = false;
     float zf = rne_quot<(1 << BITS)>(-lo, r, near);
-    if (wave_any(near) && near) {
-      zf = rintf(-lo / s);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) n[k] = rintf(x[k] / s);
-    }
+    if (wave_any(near) && near) zf = rintf(-lo / s);
     zf = __builtin_amdgcn_fmed3f(zf, 0.0f, QMAX);
     z = (int)zf;
+    float q[16];
+    asym_codes<(1 << BITS)>(x, s, r, zf, q);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) c[k] = (unsigned)__builtin_amdgcn_fmed3f(n[k] + zf, 0.0f, QMAX);
+    for (int k = 0; k < 16; ++k) c[k] = (unsigned)q[k];
   }
 }
 
@@ -982,18 +1008,12 @@ __device__ __forceinline__ void oak_dense16(const float (&xm)[16], float (&q)[16
   hi = max_lanes<1, LG>(hi);
   s = div_const<15>(hi - lo);
   const float r = recip_refined(s);  // s = 0: z = 0 and all codes 0
-  float n[16];
-  bool near = rne_quot_lane<16>(xm, r, n);
+  bool near = false;
   float zf = rne_quot<16>(-lo, r, near);
-  if (wave_any(near) && near) {
-    zf = rintf(-lo / s);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) n[k] = rintf(xm[k] / s);
-  }
+  if (wave_any(near) && near) zf = rintf(-lo / s);
   zf = __builtin_amdgcn_fmed3f(zf, 0.0f, QMAX);
   z = (int)zf;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) q[k] = __builtin_amdgcn_fmed3f(n[k] + zf, 0.0f, QMAX);
+  asym_codes<16>(xm, s, r, zf, q);
 }
 
 // Eight 4-bit codes (exact floats 0..15) as one word, code k in bits 4k..4k+3:

@@ -61,3 +61,38 @@ def test_accepted_fast_codes_equal_the_divided_codes():
                 # an exact tie is never accepted: such quotients take the divide
                 tie = (np.abs((x / s).astype(f32) - ref) == f32(0.5))
                 assert not np.any(ok & tie)
+
+
+def test_accepted_codes_with_the_zero_point_folded_in():
+    """The asymmetric codes round t = fl(x r + z) (one fused multiply-add) and
+    accept rne(t) under the same rule; the claim is rne(t) = rne(fl(x / s)) + z
+    with z = clamp(rne(fl(-lo / s)), 0, qmax), before the final clamp."""
+    rng = np.random.default_rng(2027)
+    N = 400_000
+    for case in ("random", "integers", "half-integers"):
+        for qmax in (3, 15):
+            hi = np.abs(rng.standard_normal(N) * 4).astype(np.float16).astype(f32)
+            lo = -np.abs(rng.standard_normal(N) * 4).astype(np.float16).astype(f32)
+            s = ((hi - lo) / f32(qmax)).astype(f32)
+            keep = s > 0
+            hi, lo, s = hi[keep], lo[keep], s[keep]
+            z = np.clip(np.rint((-lo / s).astype(f32)), 0, qmax).astype(f32)
+            if case == "random":
+                x = (lo + (hi - lo) * rng.random(s.size).astype(f32)).astype(np.float16).astype(f32)
+            else:
+                k = rng.integers(-qmax, qmax + 1, s.size).astype(f32)
+                x = ((k + (f32(0.5) if case == "half-integers" else f32(0))) * s).astype(f32)
+                x = np.clip(x, lo, hi)
+            r0 = (f32(1) / s).astype(f32)
+            r0 = _nudge(r0, rng.integers(-3, 4, s.size))
+            e = (f32(1) - s.astype(np.float64) * r0).astype(f32)
+            r = (e.astype(np.float64) * r0 + r0).astype(f32)
+            t = (x.astype(np.float64) * r + z).astype(f32)           # fma(x, r, z)
+            M = qmax + 1
+            assert np.all(np.abs(t) < M)
+            n = np.rint(t).astype(f32)
+            ok = np.abs(t - n) < f32(0.5 - M * 2.0 ** -19)
+            ref = np.rint((x / s).astype(f32)) + z
+            assert not np.any(ok & (n != ref)), (case, qmax)
+            if case == "random":
+                assert ok.mean() > 0.99
