@@ -1331,6 +1331,7 @@ __device__ __forceinline__ unsigned dsq_key(float x) {
 
 constexpr int kDsqSigSlots = 16;  // significant-row slots per group
 constexpr int kDsqOthSlots = 64;  // other-row slots per group
+constexpr int kDsqPre = 4;        // other rows loaded ahead per row group
 
 // 8 channels 8 li .. 8 li + 7 of an fp16 V-layout row (word n holds
 // channels n + 16 j), in channel order (inverse of store_row_f16's V order).
@@ -1463,23 +1464,37 @@ __global__ __launch_bounds__(256) void k_quant_dsq(const uint16_t* __restrict__ 
   // 4. the other tokens: INT2 rows in groups of 32 channels; 16 lanes per row
   const int li = threadIdx.x & 15, rg = threadIdx.x >> 4;
   uint16_t* lrow = lrows[rg];
+  // The input rows of kDsqPre slots are loaded before any of them is coded
+  // (slots past n_oth load a row of the group, unused); rows still in the
+  // tails (tokens below p) are read from there in place of theirs.
 #pragma unroll
   for (int tsr = 0; tsr < 2; ++tsr) {
     const TensorArgs& t = tsr ? vt : kt;
-    for (int slot = rg; slot < kDsqOthSlots; slot += 16) {
+    const uint16_t* xin = tsr ? xv : xk;
+#pragma unroll
+    for (int s0 = 0; s0 < kDsqOthSlots; s0 += 16 * kDsqPre) {
+    uint4 raws[kDsqPre];
+    int toks[kDsqPre];
+#pragma unroll
+    for (int j = 0; j < kDsqPre; ++j) {
+      const int slot = s0 + rg + 16 * j;
+      toks[j] = slot < n_oth ? k0 + o_tok[slot] : max(k0, p);
+      raws[j] = ld_row8(xin + (bh * t_new + (max(toks[j], p) - p)) * kD + li * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < kDsqPre; ++j) {
+      const int slot = s0 + rg + 16 * j;
       const long long dst = gb * kDsqOthSlots + slot;
       uint32_t plo = 0, phi = 0;
       float s = 0.0f;
       int z = 0;
       if (slot < n_oth) {
         float v[8];
-        const int tok = k0 + o_tok[slot];
-        uint4 raw;
+        const int tok = toks[j];
+        uint4 raw = raws[j];
         if (tok < p) {
-          const uint8_t* trow = (tsr ? vt : kt).codes16 + (bh * 64 + (tok - k0)) * 256;
+          const uint8_t* trow = t.codes16 + (bh * 64 + (tok - k0)) * 256;
           raw = tsr ? ld_row8_v16(trow, li) : ld_row8_k16(trow, li);
-        } else {
-          raw = ld_row8((tsr ? xv : xk) + (bh * t_new + (tok - p)) * kD + li * 8);
         }
         unpack8(raw, v);
         if (tsr == 0) {
@@ -1507,6 +1522,7 @@ __global__ __launch_bounds__(256) void k_quant_dsq(const uint16_t* __restrict__ 
         t.scale2[dst * 4 + (li >> 2)] = s;
         t.zero2[dst * 4 + (li >> 2)] = (uint8_t)z;
       }
+    }
     }
   }
 }
