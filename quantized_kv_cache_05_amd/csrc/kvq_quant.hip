@@ -1419,8 +1419,11 @@ __global__ __launch_bounds__(256) void k_quant_dsq(const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < kDsqSigSlots; ++i) {
       const int tok = k0 + (i < n_sig ? s_tok[i] : 0);
-      // both addresses stay valid whichever side is taken (input row >= p, tail row < 64)
-      const uint16_t h = tok < p ? tail[(tok - k0) * kD + toff] : x[(long long)max(tok, p) * kD];
+      // the input row is always read (row max(tok, p) exists), so the
+      // slots' loads issue together; a token still in the tails (rare)
+      // replaces it from there
+      uint16_t h = x[(long long)max(tok, p) * kD];
+      if (tok < p) h = tail[(tok - k0) * kD + toff];
       xv_[i] = i < n_sig ? h2f(h) : 0.0f;
       amax = fmaxf(amax, fabsf(xv_[i]));
     }
