@@ -585,8 +585,10 @@ __global__ __launch_bounds__(256) void k_quant_channel(const uint16_t* __restric
   for (int pass = 0; pass < 4; ++pass) {
     const int r = pass * 16 + (threadIdx.x >> 4), li = threadIdx.x & 15;
     const int t = k0 + r;
-    const uint4 raw = t < p ? ld_row8_k16(tail + (bh * 64 + r) * 256, li)
-                            : ld_row8(x + (bh * t_new + (t - p)) * kD + li * 8);
+    // the input row is always read (row max(t, p) is in the input), so the
+    // passes' loads issue together; a row still in the tail replaces it
+    uint4 raw = ld_row8(x + (bh * t_new + (max(t, p) - p)) * kD + li * 8);
+    if (t < p) raw = ld_row8_k16(tail + (bh * 64 + r) * 256, li);
     *reinterpret_cast<uint4*>(&tile[r][li * 8]) = raw;
   }
   __syncthreads();
